@@ -1,0 +1,226 @@
+/*
+ * Plain fp64 CPU oracle for the selective state-space (SSD) layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path links, loads or calls
+ * this file; it is used by the tests, by the smoke check and by the benchmark's
+ * CPU-baseline leg. It shares no code with the HIP library.
+ *
+ * What it computes is the token-by-token recurrence, written out directly:
+ *
+ *   per head h (B/C group g = h / (H/G)), state hs in R^{P x N}, for t = 0..L-1:
+ *     a        = exp(dt_t * A_h)                       decay of the step
+ *     hs[p][n] = a * hs[p][n] + dt_t * x_t[p] * B_t[n] input enters the state
+ *     y_t[p]   = sum_n C_t[n] * hs[p][n] + D_h * x_t[p] output read after update
+ *
+ * Sources (titles and sections of the pages):
+ *   - "从Transformer到Mamba" tutorial, section 2.2 (discretisation): the
+ *     discrete recurrence x_k = Abar x_{k-1} + Bbar u_k, y_k = C x_k with
+ *     Abar = exp(dt A); the output is taken from the updated state.
+ *   - same page, section 2.1, and "深挖-Mamba", core concept 1 (SSM): the
+ *     D x feed-through term.
+ *   - "深挖-Mamba", core concept 3 (selective scan), and the tutorial's
+ *     section 3.2: dt, B and C are per token, A is shared (one scalar per
+ *     head here, as in the Mamba-2 "Draft:Mamba2" page's SSD section).
+ *   - The input is scaled by dt (Bbar = dt * B), the Euler form the layer is
+ *     defined with; the tutorial's zero-order-hold Bbar is not used.
+ * The state is stored transposed to the usual N x P: hs[p][n], n fastest.
+ *
+ * All token inputs arrive as float32 arrays holding the exact values the GPU
+ * reads (bf16 values are exact in float32) and are promoted to double; the
+ * optional initial state is double.
+ *
+ * Work is split over independent (batch, head) units with POSIX threads; each
+ * unit runs its tokens strictly in order.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdatomic.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    const float *x, *dt, *A, *B, *C, *D;
+    const double *init;
+    int batch, seqlen, nheads, headdim, ngroups, dstate;
+    const int *units;
+    int nunits;
+    double *y;      /* [nunits][seqlen][headdim] */
+    double *state;  /* [nunits][headdim][dstate] final state (may be NULL) */
+    double *snaps;  /* [nunits][seqlen/snap_every][headdim][dstate] (may be NULL) */
+    int snap_every;
+    atomic_int next;
+} fwd_job;
+
+static void fwd_unit(fwd_job *j, int u, double *hs)
+{
+    const int H = j->nheads, P = j->headdim, N = j->dstate, L = j->seqlen;
+    const int G = j->ngroups;
+    const int bh = j->units ? j->units[u] : u;
+    const int b = bh / H, h = bh % H;
+    const int g = h / (H / G);
+    const double A = j->A[h];
+    const double D = j->D ? j->D[h] : 0.0;
+    const size_t PN = (size_t)P * N;
+
+    if (j->init) {
+        const double *s0 = j->init + (size_t)bh * PN;
+        for (size_t k = 0; k < PN; ++k) hs[k] = s0[k];
+    } else {
+        memset(hs, 0, PN * sizeof(double));
+    }
+    double *yu = j->y ? j->y + (size_t)u * L * P : NULL;
+    int nsnap = 0;
+    for (int t = 0; t < L; ++t) {
+        const size_t tok = (size_t)b * L + t;
+        const double d = j->dt[tok * H + h];
+        const double a = exp(d * A);
+        const float *xt = j->x + (tok * H + h) * P;
+        const float *Bt = j->B + (tok * G + g) * N;
+        const float *Ct = j->C + (tok * G + g) * N;
+        for (int p = 0; p < P; ++p) {
+            double *row = hs + (size_t)p * N;
+            const double dx = d * (double)xt[p];
+            double acc = 0.0;
+            for (int n = 0; n < N; ++n) {
+                row[n] = a * row[n] + dx * (double)Bt[n];
+                acc += (double)Ct[n] * row[n];
+            }
+            if (yu) yu[(size_t)t * P + p] = acc + D * (double)xt[p];
+        }
+        if (j->snaps && j->snap_every > 0 && (t + 1) % j->snap_every == 0) {
+            const int per = L / j->snap_every;
+            memcpy(j->snaps + ((size_t)u * per + nsnap) * PN, hs, PN * sizeof(double));
+            ++nsnap;
+        }
+    }
+    if (j->state) memcpy(j->state + (size_t)u * PN, hs, PN * sizeof(double));
+}
+
+static void *fwd_worker(void *arg)
+{
+    fwd_job *j = (fwd_job *)arg;
+    double *hs = (double *)malloc((size_t)j->headdim * j->dstate * sizeof(double));
+    if (!hs) return (void *)1;
+    for (;;) {
+        int u = atomic_fetch_add(&j->next, 1);
+        if (u >= j->nunits) break;
+        fwd_unit(j, u, hs);
+    }
+    free(hs);
+    return NULL;
+}
+
+static int run_threads(void *(*fn)(void *), void *job, int nthreads, int nunits)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > nunits) nthreads = nunits;
+    if (nthreads <= 1) return fn(job) == NULL ? 0 : -3;
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!tid) return -3;
+    int started = 0, rc = 0;
+    for (; started < nthreads; ++started)
+        if (pthread_create(&tid[started], NULL, fn, job) != 0) break;
+    if (started == 0) rc = (fn(job) == NULL) ? 0 : -3;
+    for (int i = 0; i < started; ++i) {
+        void *r = NULL;
+        pthread_join(tid[i], &r);
+        if (r != NULL) rc = -3;
+    }
+    free(tid);
+    return rc;
+}
+
+/*
+ * Forward over whole sequences.
+ *   x [batch][seqlen][nheads][headdim], dt [batch][seqlen][nheads],
+ *   B, C [batch][seqlen][ngroups][dstate], A, D [nheads] (D may be NULL: 0),
+ *   init [batch][nheads][headdim][dstate] (may be NULL: zero state).
+ *   units: flat (b*nheads + h) indices to compute, or NULL for all of them.
+ *   y [nunits][seqlen][headdim]; state [nunits][headdim][dstate] (may be NULL);
+ *   snaps: the state after every snap_every-th token (may be NULL).
+ * Returns 0, or a negative value on bad arguments / allocation failure.
+ */
+int ssd_oracle_forward(const float *x, const float *dt, const float *A, const float *B,
+                       const float *C, const float *D, const double *init,
+                       int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate,
+                       const int *units, int nunits, double *y, double *state,
+                       double *snaps, int snap_every, int nthreads)
+{
+    if (!x || !dt || !A || !B || !C) return -1;
+    if (batch < 1 || seqlen < 0 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1) return -2;
+    if (nheads % ngroups) return -2;
+    if (!units) nunits = batch * nheads;
+    if (nunits < 0) return -2;
+    for (int u = 0; units && u < nunits; ++u)
+        if (units[u] < 0 || units[u] >= batch * nheads) return -2;
+    if (nunits == 0) return 0;
+    fwd_job j = {x, dt, A, B, C, D, init, batch, seqlen, nheads, headdim, ngroups, dstate,
+                 units, nunits, y, state, snaps, snap_every, 0};
+    atomic_init(&j.next, 0);
+    return run_threads(fwd_worker, &j, nthreads, nunits);
+}
+
+typedef struct {
+    double *state;  /* [nunits][headdim][dstate] */
+    const float *x, *dt, *A, *B, *C, *D;
+    int batch, nheads, headdim, ngroups, dstate;
+    const int *units;
+    int nunits;
+    double *y;      /* [nunits][headdim] */
+    atomic_int next;
+} step_job;
+
+static void *step_worker(void *arg)
+{
+    step_job *j = (step_job *)arg;
+    const int H = j->nheads, P = j->headdim, N = j->dstate, G = j->ngroups;
+    for (;;) {
+        int u = atomic_fetch_add(&j->next, 1);
+        if (u >= j->nunits) break;
+        const int bh = j->units ? j->units[u] : u;
+        const int b = bh / H, h = bh % H, g = h / (H / G);
+        const double d = j->dt[bh];
+        const double a = exp(d * (double)j->A[h]);
+        const double D = j->D ? j->D[h] : 0.0;
+        const float *xt = j->x + (size_t)bh * P;
+        const float *Bt = j->B + ((size_t)b * G + g) * N;
+        const float *Ct = j->C + ((size_t)b * G + g) * N;
+        double *hs = j->state + (size_t)u * P * N;
+        for (int p = 0; p < P; ++p) {
+            double *row = hs + (size_t)p * N;
+            const double dx = d * (double)xt[p];
+            double acc = 0.0;
+            for (int n = 0; n < N; ++n) {
+                row[n] = a * row[n] + dx * (double)Bt[n];
+                acc += (double)Ct[n] * row[n];
+            }
+            j->y[(size_t)u * P + p] = acc + D * (double)xt[p];
+        }
+    }
+    return NULL;
+}
+
+/*
+ * One recurrent step for every selected (b, h) unit: the loop body above for a
+ * single token.
+ *   state [nunits][headdim][dstate] (in/out, double),
+ *   x [batch][nheads][headdim], dt [batch][nheads], B, C [batch][ngroups][dstate],
+ *   y [nunits][headdim].
+ */
+int ssd_oracle_step(double *state, const float *x, const float *dt, const float *A,
+                    const float *B, const float *C, const float *D,
+                    int batch, int nheads, int headdim, int ngroups, int dstate,
+                    const int *units, int nunits, double *y, int nthreads)
+{
+    if (!state || !x || !dt || !A || !B || !C || !y) return -1;
+    if (batch < 1 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1) return -2;
+    if (nheads % ngroups) return -2;
+    if (!units) nunits = batch * nheads;
+    for (int u = 0; units && u < nunits; ++u)
+        if (units[u] < 0 || units[u] >= batch * nheads) return -2;
+    if (nunits <= 0) return 0;
+    step_job j = {state, x, dt, A, B, C, D, batch, nheads, headdim, ngroups, dstate,
+                  units, nunits, y, 0};
+    atomic_init(&j.next, 0);
+    return run_threads(step_worker, &j, nthreads, nunits);
+}

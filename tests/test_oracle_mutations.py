@@ -1,0 +1,51 @@
+"""Plant plausible mistakes in the oracle source (on the CPU) and check that at
+least one pin catches each. This is what makes the pins trustworthy: an oracle
+with a dropped term, a wrong sign, a wrong index or a transposed operand does
+not pass them."""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+MUTATIONS = {
+    "dropped_D": ("acc + D * (double)xt[p]", "acc"),
+    "sign_of_A": ("const double a = exp(d * A);", "const double a = exp(-d * A);"),
+    "no_decay": ("row[n] = a * row[n] + dx * (double)Bt[n];", "row[n] = row[n] + dx * (double)Bt[n];"),
+    "no_dt_on_input": ("const double dx = d * (double)xt[p];\n            double acc = 0.0;\n            for (int n = 0; n < N; ++n) {\n                row[n] = a * row[n]",
+                       "const double dx = (double)xt[p];\n            double acc = 0.0;\n            for (int n = 0; n < N; ++n) {\n                row[n] = a * row[n]"),
+    "B_C_swapped": ("acc += (double)Ct[n] * row[n];\n            }\n            if (yu)", "acc += (double)Bt[n] * row[n];\n            }\n            if (yu)"),
+    "output_before_update": ("row[n] = a * row[n] + dx * (double)Bt[n];\n                acc += (double)Ct[n] * row[n];",
+                             "acc += (double)Ct[n] * row[n];\n                row[n] = a * row[n] + dx * (double)Bt[n];"),
+    "group_index": ("const int g = h / (H / G);\n    const double A", "const int g = h % G;\n    const double A"),
+    "transposed_state_read": ("acc += (double)Ct[n] * row[n];\n            }\n            if (yu)",
+                              "acc += (double)Ct[n] * hs[(size_t)(n % P) * N + (p % N)];\n            }\n            if (yu)"),
+    "init_ignored": ("for (size_t k = 0; k < PN; ++k) hs[k] = s0[k];", "(void)s0; memset(hs, 0, PN * sizeof(double));"),
+    "previous_token_dt_for_decay": ("const double a = exp(d * A);", "const double a = exp((t ? (double)j->dt[(tok - 1) * H + h] : d) * A);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    before, after = MUTATIONS[name]
+    src = open(oracle.SRC_PATH).read()
+    # the first occurrence is in the forward recurrence (the step follows it)
+    assert before in src, f"mutation anchor for {name} not present"
+    mut_src = tmp_path / "mut.c"
+    mut_src.write_text(src.replace(before, after, 1))
+    lib = oracle.build(force=True, src=str(mut_src), out=str(tmp_path / f"libmut_{name}.so"))
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib=lib)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught planted mistake {name}"
+
+
+def test_unmutated_source_passes_all_pins(tmp_path):
+    lib = oracle.build(force=True, out=str(tmp_path / "libclean.so"))
+    for pin in ALL_PINS:
+        pin(lib=lib)
+    assert os.path.exists(lib)
