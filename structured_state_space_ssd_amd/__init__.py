@@ -1,0 +1,168 @@
+"""MI355X-native Mamba-2 SSD layer: chunked forward pass and recurrent decode.
+
+Thin Python front end over libssd.so (include/ssd.h). Tensors are torch tensors
+on the GPU; work is enqueued on torch's current stream. Nothing here computes:
+the functions check tensor metadata, allocate outputs / workspace with torch,
+and call the C ABI.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _native
+from ._native import SSDError, check, dtype_code, ptr, stream_handle
+
+__all__ = ["forward", "step", "workspace_size", "chunk_cumsum", "chunk_state",
+           "state_passing", "chunk_scan", "SSDError", "stages"]
+
+HEADDIM = 64
+
+
+def _req(t, name, dtype=None, device=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _opt(t, name, dtype=torch.float32):
+    return None if t is None else _req(t, name, dtype)
+
+
+def workspace_size(batch, seqlen, nheads, headdim, dstate, chunk) -> int:
+    return int(_native.lib.ssd_forward_workspace_size(batch, seqlen, nheads, headdim, dstate, chunk))
+
+
+def forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, return_final_state=False,
+            workspace=None):
+    """y = SSD(x, dt, A, B, C, D) over whole sequences.
+
+    x [Bt,L,H,P], dt [Bt,L,H], B, C [Bt,L,G,N] (all float32 or all bfloat16),
+    A, D [H] float32, init_state [Bt,H,P,N] float32 or None.
+    Returns y (and the final state [Bt,H,P,N] float32 if requested).
+    """
+    _req(x, "x")
+    dt_ = dtype_code(x.dtype)
+    Bt, L, H, P = x.shape
+    _req(dt, "dt", x.dtype)
+    _req(B, "B", x.dtype)
+    _req(C, "C", x.dtype)
+    _req(A, "A", torch.float32)
+    _opt(D, "D")
+    _opt(init_state, "init_state")
+    G, N = B.shape[2], B.shape[3]
+    if tuple(dt.shape) != (Bt, L, H) or tuple(B.shape) != (Bt, L, G, N) or C.shape != B.shape:
+        raise ValueError("shape mismatch among x, dt, B, C")
+    y = torch.empty_like(x)
+    fs = torch.empty((Bt, H, P, N), dtype=torch.float32, device=x.device) if return_final_state else None
+    need = workspace_size(Bt, L, H, P, N, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    rc = _native.lib.ssd_forward(
+        ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), Bt, L, H, P, G, N, chunk, dt_,
+        ptr(init_state), ptr(y), ptr(fs), ptr(workspace), workspace.numel(), stream_handle(x.device))
+    check(rc, "ssd_forward")
+    return (y, fs) if return_final_state else y
+
+
+def step(state, x, dt, A, B, C, D=None, y=None):
+    """One decode step; updates state [Bt,H,P,N] float32 in place, returns y [Bt,H,P].
+
+    x [Bt,H,P], dt [Bt,H], B, C [Bt,G,N] (float32 or bfloat16), A, D [H] float32.
+    """
+    _req(state, "state", torch.float32)
+    _req(x, "x")
+    dt_ = dtype_code(x.dtype)
+    Bt, H, P = x.shape
+    _req(dt, "dt", x.dtype)
+    _req(B, "B", x.dtype)
+    _req(C, "C", x.dtype)
+    _req(A, "A", torch.float32)
+    _opt(D, "D")
+    G, N = B.shape[1], B.shape[2]
+    if tuple(state.shape) != (Bt, H, P, N) or tuple(dt.shape) != (Bt, H) or C.shape != B.shape:
+        raise ValueError("shape mismatch among state, x, dt, B, C")
+    if y is None:
+        y = torch.empty_like(x)
+    rc = _native.lib.ssd_step(ptr(state), ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D),
+                              Bt, H, P, G, N, dt_, ptr(y), stream_handle(x.device))
+    check(rc, "ssd_step")
+    return y
+
+
+# ---- stage-by-stage entry points (what forward enqueues) --------------------
+
+def _nc(L, Q):
+    return (L + Q - 1) // Q
+
+
+def chunk_cumsum(dt, A, chunk, out=None):
+    """dA_cumsum [Bt,H,nC*Q] float32: within-chunk prefix sums of dt*A."""
+    _req(dt, "dt")
+    Bt, L, H = dt.shape
+    if out is None:
+        out = torch.empty((Bt, H, _nc(L, chunk) * chunk), dtype=torch.float32, device=dt.device)
+    rc = _native.lib.ssd_chunk_cumsum(ptr(dt), ptr(_req(A, "A", torch.float32)), Bt, L, H, chunk,
+                                      dtype_code(dt.dtype), ptr(out), stream_handle(dt.device))
+    check(rc, "ssd_chunk_cumsum")
+    return out
+
+
+def chunk_state(x, B, dt, dA_cumsum, chunk, out=None):
+    """states [Bt,nC,H,P,N] float32: each chunk's contribution from a zero state."""
+    Bt, L, H, P = _req(x, "x").shape
+    G, N = B.shape[2], B.shape[3]
+    if out is None:
+        out = torch.empty((Bt, _nc(L, chunk), H, P, N), dtype=torch.float32, device=x.device)
+    rc = _native.lib.ssd_chunk_state(ptr(x), ptr(_req(B, "B", x.dtype)), ptr(_req(dt, "dt", x.dtype)),
+                                     ptr(_req(dA_cumsum, "dA_cumsum", torch.float32)), Bt, L, H, P, G,
+                                     N, chunk, dtype_code(x.dtype), ptr(out), stream_handle(x.device))
+    check(rc, "ssd_chunk_state")
+    return out
+
+
+def state_passing(states, dA_cumsum, seqlen, chunk, init_state=None, out=None, final_state=None):
+    """chunk_init [Bt,nC,H,P,N] float32 (state entering each chunk); optional final state."""
+    Bt, nC, H, P, N = _req(states, "states", torch.float32).shape
+    if out is None:
+        out = torch.empty_like(states)
+    rc = _native.lib.ssd_state_passing(ptr(states), ptr(_req(dA_cumsum, "dA_cumsum", torch.float32)),
+                                       ptr(_opt(init_state, "init_state")), Bt, seqlen, H, P, N, chunk,
+                                       ptr(out), ptr(_opt(final_state, "final_state")),
+                                       stream_handle(states.device))
+    check(rc, "ssd_state_passing")
+    return out
+
+
+def chunk_scan(x, dt, dA_cumsum, B, C, D, chunk_init, chunk, y=None):
+    """y [Bt,L,H,P]: intra-chunk product + state-to-output + D x."""
+    Bt, L, H, P = _req(x, "x").shape
+    G, N = B.shape[2], B.shape[3]
+    if y is None:
+        y = torch.empty_like(x)
+    rc = _native.lib.ssd_chunk_scan(ptr(x), ptr(_req(dt, "dt", x.dtype)),
+                                    ptr(_req(dA_cumsum, "dA_cumsum", torch.float32)),
+                                    ptr(_req(B, "B", x.dtype)), ptr(_req(C, "C", x.dtype)),
+                                    ptr(_opt(D, "D")), ptr(_req(chunk_init, "chunk_init", torch.float32)),
+                                    Bt, L, H, P, G, N, chunk, dtype_code(x.dtype), ptr(y),
+                                    stream_handle(x.device))
+    check(rc, "ssd_chunk_scan")
+    return y
+
+
+def stages(x, dt, A, B, C, D=None, chunk=256, init_state=None):
+    """Run the four forward stages one call at a time; returns a dict with every
+    intermediate (dA_cumsum, states, chunk_init, final_state) and y."""
+    Bt, L, H, P = x.shape
+    N = B.shape[3]
+    s = chunk_cumsum(dt, A, chunk)
+    st = chunk_state(x, B, dt, s, chunk)
+    fs = torch.empty((Bt, H, P, N), dtype=torch.float32, device=x.device)
+    ci = state_passing(st, s, L, chunk, init_state=init_state, final_state=fs)
+    y = chunk_scan(x, dt, s, B, C, D, ci, chunk)
+    return {"dA_cumsum": s, "states": st, "chunk_init": ci, "final_state": fs, "y": y}

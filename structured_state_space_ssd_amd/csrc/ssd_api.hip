@@ -1,0 +1,172 @@
+// C ABI of libssd.so: argument checks, workspace layout and launch order.
+// Every declaration and its contract is in include/ssd.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssd.h"
+#include "ssd_launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kHeaddim = 64;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool supported_dstate(int n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
+bool supported_chunk(int q) { return q == 64 || q == 128 || q == 256; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_dtype(int d) { return d == SSD_F32 || d == SSD_BF16; }
+
+struct Workspace {
+    size_t cumsum_off, states_off, init_off, total;
+};
+
+Workspace layout(int batch, int seqlen, int nheads, int headdim, int dstate, int chunk) {
+    const size_t nC = (static_cast<size_t>(seqlen) + chunk - 1) / chunk;
+    const size_t cumsum = static_cast<size_t>(batch) * nheads * nC * chunk * sizeof(float);
+    const size_t st = static_cast<size_t>(batch) * nC * nheads * headdim * dstate * sizeof(float);
+    Workspace w;
+    w.cumsum_off = 0;
+    w.states_off = align_up(cumsum);
+    w.init_off = w.states_off + align_up(st);
+    w.total = w.init_off + align_up(st);
+    return w;
+}
+
+int check_dims(int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate) {
+    if (batch < 1 || seqlen < 1 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1)
+        return SSD_ERR_SHAPE;
+    if (nheads % ngroups != 0) return SSD_ERR_SHAPE;
+    if (headdim != kHeaddim || !supported_dstate(dstate)) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *ssd_strerror(int status) {
+    switch (status) {
+        case SSD_OK: return "ok";
+        case SSD_ERR_NULL: return "a required pointer is NULL";
+        case SSD_ERR_SHAPE: return "invalid sizes (non-positive, or nheads not a multiple of ngroups)";
+        case SSD_ERR_UNSUPPORTED:
+            return "unsupported configuration (need headdim 64, dstate in {16,32,64,128,256}, "
+                   "chunk in {64,128,256}, dtype SSD_F32/SSD_BF16, 16-byte aligned buffers)";
+        case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+        case SSD_ERR_HIP: return "HIP runtime error at kernel launch";
+        default: return "unknown status";
+    }
+}
+
+size_t ssd_forward_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
+                                  int chunk) {
+    if (batch < 1 || seqlen < 1 || nheads < 1 || headdim < 1 || dstate < 1 || chunk < 1) return 0;
+    return layout(batch, seqlen, nheads, headdim, dstate, chunk).total;
+}
+
+int ssd_chunk_cumsum(const void *dt, const float *A, int batch, int seqlen, int nheads, int chunk,
+                     int dtype, float *dA_cumsum, void *stream) {
+    if (!dt || !A || !dA_cumsum) return SSD_ERR_NULL;
+    if (batch < 1 || seqlen < 1 || nheads < 1) return SSD_ERR_SHAPE;
+    if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    return status_of(ssd::launch_chunk_cumsum(dt, A, batch, seqlen, nheads, chunk,
+                                              dtype == SSD_BF16, dA_cumsum,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int ssd_chunk_state(const void *x, const void *B, const void *dt, const float *dA_cumsum, int batch,
+                    int seqlen, int nheads, int headdim, int ngroups, int dstate, int chunk,
+                    int dtype, float *states, void *stream) {
+    if (!x || !B || !dt || !dA_cumsum || !states) return SSD_ERR_NULL;
+    int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
+    if (rc != SSD_OK) return rc;
+    if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(B) || !aligned16(states)) return SSD_ERR_UNSUPPORTED;
+    return status_of(ssd::launch_chunk_state(x, B, dt, dA_cumsum, batch, seqlen, nheads, ngroups,
+                                             dstate, chunk, dtype == SSD_BF16, states,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int ssd_state_passing(const float *states, const float *dA_cumsum, const float *init_state,
+                      int batch, int seqlen, int nheads, int headdim, int dstate, int chunk,
+                      float *chunk_init, float *final_state, void *stream) {
+    if (!states || !dA_cumsum || !chunk_init) return SSD_ERR_NULL;
+    int rc = check_dims(batch, seqlen, nheads, headdim, 1, dstate);
+    if (rc != SSD_OK) return rc;
+    if (!supported_chunk(chunk)) return SSD_ERR_UNSUPPORTED;
+    if (!aligned16(states) || !aligned16(chunk_init) || (init_state && !aligned16(init_state)) ||
+        (final_state && !aligned16(final_state)))
+        return SSD_ERR_UNSUPPORTED;
+    return status_of(ssd::launch_state_passing(states, dA_cumsum, init_state, batch, seqlen, nheads,
+                                               dstate, chunk, chunk_init, final_state,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int ssd_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *B,
+                   const void *C, const float *D, const float *chunk_init, int batch, int seqlen,
+                   int nheads, int headdim, int ngroups, int dstate, int chunk, int dtype, void *y,
+                   void *stream) {
+    if (!x || !dt || !dA_cumsum || !B || !C || !chunk_init || !y) return SSD_ERR_NULL;
+    int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
+    if (rc != SSD_OK) return rc;
+    if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(chunk_init) || !aligned16(y))
+        return SSD_ERR_UNSUPPORTED;
+    return status_of(ssd::launch_chunk_scan(x, dt, dA_cumsum, B, C, D, chunk_init, batch, seqlen,
+                                            nheads, ngroups, dstate, chunk, dtype == SSD_BF16, y,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int ssd_forward(const void *x, const void *dt, const float *A, const void *B, const void *C,
+                const float *D, int batch, int seqlen, int nheads, int headdim, int ngroups,
+                int dstate, int chunk, int dtype, const float *init_state, void *y,
+                float *final_state, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
+    int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
+    if (rc != SSD_OK) return rc;
+    if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) ||
+        (init_state && !aligned16(init_state)) || (final_state && !aligned16(final_state)))
+        return SSD_ERR_UNSUPPORTED;
+    const Workspace ws = layout(batch, seqlen, nheads, headdim, dstate, chunk);
+    if (!workspace || workspace_bytes < ws.total) return SSD_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return SSD_ERR_WORKSPACE;
+
+    char *base = static_cast<char *>(workspace);
+    float *cumsum = reinterpret_cast<float *>(base + ws.cumsum_off);
+    float *states = reinterpret_cast<float *>(base + ws.states_off);
+    float *cinit = reinterpret_cast<float *>(base + ws.init_off);
+    const bool bf16 = dtype == SSD_BF16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    hipError_t e = ssd::launch_chunk_cumsum(dt, A, batch, seqlen, nheads, chunk, bf16, cumsum, s);
+    if (e == hipSuccess)
+        e = ssd::launch_chunk_state(x, B, dt, cumsum, batch, seqlen, nheads, ngroups, dstate, chunk,
+                                    bf16, states, s);
+    if (e == hipSuccess)
+        e = ssd::launch_state_passing(states, cumsum, init_state, batch, seqlen, nheads, dstate,
+                                      chunk, cinit, final_state, s);
+    if (e == hipSuccess)
+        e = ssd::launch_chunk_scan(x, dt, cumsum, B, C, D, cinit, batch, seqlen, nheads, ngroups,
+                                   dstate, chunk, bf16, y, s);
+    return status_of(e);
+}
+
+int ssd_step(float *state, const void *x, const void *dt, const float *A, const void *B,
+             const void *C, const float *D, int batch, int nheads, int headdim, int ngroups,
+             int dstate, int dtype, void *y, void *stream) {
+    if (!state || !x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
+    int rc = check_dims(batch, 1, nheads, headdim, ngroups, dstate);
+    if (rc != SSD_OK) return rc;
+    if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    if (!aligned16(state)) return SSD_ERR_UNSUPPORTED;
+    return status_of(ssd::launch_decode_step(state, x, dt, A, B, C, D, batch, nheads, ngroups,
+                                             dstate, dtype == SSD_BF16, y,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// Device-side helpers shared by the SSD kernels (gfx950 / CDNA4 only).
+//
+// Matrix products use the 16x16 MFMA family with a common fragment format:
+// for a 16-row operand tile and a 32-wide slice of the contraction index k,
+// lane l = 16*g + r (g = 0..3, r = 0..15) holds 8 elements of row r, at k
+// positions kmap(g, e), e = 0..7, where kmap is any bijection onto the 32
+// positions that both operands of one product share. One bf16 fragment pair
+// is a single v_mfma_f32_16x16x32_bf16; one fp32 pair is eight
+// v_mfma_f32_16x16x4_f32 (element e of every lane per instruction), so both
+// dtypes sum exactly the same 32 products. The 16x16 float32 result lives in
+// 4 registers per lane: lane 16*g + c holds rows 4*g + 0..3 of column c.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;  // bf16 storage in global memory
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+    return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// Input element -> float.
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+
+// float -> output element (bf16: round to nearest even in hardware).
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
+    __bf16 b = static_cast<__bf16>(v);
+    return __builtin_bit_cast(bf16_t, b);
+}
+
+// ---- MFMA operand fragments ------------------------------------------------
+//
+// Frag<T>: the 8 elements one lane contributes to a 16x16x32 product, in the
+// MFMA operand type for input dtype T (bf16 -> __bf16, float -> float).
+template <typename T> struct Frag;
+
+template <> struct Frag<bf16_t> {
+    bf16x8 v;
+    __device__ __forceinline__ void zero() {
+        for (int e = 0; e < 8; ++e) v[e] = static_cast<__bf16>(0.0f);
+    }
+    __device__ __forceinline__ void set(int e, float f) { v[e] = static_cast<__bf16>(f); }
+    __device__ __forceinline__ float get(int e) const { return static_cast<float>(v[e]); }
+};
+
+template <> struct Frag<float> {
+    float v[8];
+    __device__ __forceinline__ void zero() {
+        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+    }
+    __device__ __forceinline__ void set(int e, float f) { v[e] = f; }
+    __device__ __forceinline__ float get(int e) const { return v[e]; }
+};
+
+// acc += A * B over one 32-wide k slice (A rows and B columns each one lane's
+// row index r; see the header comment).
+__device__ __forceinline__ void mma(floatx4 &acc, const Frag<bf16_t> &a, const Frag<bf16_t> &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(floatx4 &acc, const Frag<float> &a, const Frag<float> &b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+
+// Load 8 consecutive elements (k = k0 .. k0+7) of one row from LDS, where the
+// LDS copy is stored in the MFMA operand type. Requires 16-byte (bf16) or
+// 32-byte (float) alignment of the address.
+__device__ __forceinline__ void lds_frag8(Frag<bf16_t> &f, const __bf16 *p) {
+    f.v = *reinterpret_cast<const bf16x8 *>(p);
+}
+__device__ __forceinline__ void lds_frag8(Frag<float> &f, const float *p) {
+    const floatx4 a = *reinterpret_cast<const floatx4 *>(p);
+    const floatx4 b = *reinterpret_cast<const floatx4 *>(p + 4);
+    f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
+    f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
+}
+
+// Load two runs of 4 consecutive elements (elements 0..3 from p0, 4..7 from p1).
+__device__ __forceinline__ void lds_frag4x2(Frag<bf16_t> &f, const __bf16 *p0, const __bf16 *p1) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(p0);
+    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p1);
+    f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
+    f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
+}
+__device__ __forceinline__ void lds_frag4x2(Frag<float> &f, const float *p0, const float *p1) {
+    const floatx4 a = *reinterpret_cast<const floatx4 *>(p0);
+    const floatx4 b = *reinterpret_cast<const floatx4 *>(p1);
+    f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
+    f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
+}
+
+// MFMA operand type held in LDS for input dtype T.
+template <typename T> struct LdsT;
+template <> struct LdsT<bf16_t> { using type = __bf16; };
+template <> struct LdsT<float> { using type = float; };
+
+__device__ __forceinline__ __bf16 to_lds(float v, __bf16 *) { return static_cast<__bf16>(v); }
+__device__ __forceinline__ float to_lds(float v, float *) { return v; }
+
+// 16-byte global load of 8 bf16 or 2x16 bytes of 8 floats, as floats.
+__device__ __forceinline__ void load8(const bf16_t *p, float out[8]) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        out[2 * i] = __uint_as_float(w[i] << 16);
+        out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8(const float *p, float out[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+}  // namespace ssd

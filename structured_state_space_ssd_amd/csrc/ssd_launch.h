@@ -1,0 +1,30 @@
+// Host-side launchers of the SSD kernels (one per kernel source file). They
+// assume arguments were validated by the C-ABI layer (ssd_api.hip) and return
+// the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace ssd {
+
+hipError_t launch_chunk_cumsum(const void *dt, const float *A, int batch, int seqlen, int nheads,
+                               int chunk, bool bf16, float *dA_cumsum, hipStream_t stream);
+
+hipError_t launch_chunk_state(const void *x, const void *B, const void *dt, const float *dA_cumsum,
+                              int batch, int seqlen, int nheads, int ngroups, int dstate, int chunk,
+                              bool bf16, float *states, hipStream_t stream);
+
+hipError_t launch_state_passing(const float *states, const float *dA_cumsum, const float *init,
+                                int batch, int seqlen, int nheads, int dstate, int chunk,
+                                float *chunk_init, float *final_state, hipStream_t stream);
+
+hipError_t launch_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *B,
+                             const void *C, const float *D, const float *chunk_init, int batch,
+                             int seqlen, int nheads, int ngroups, int dstate, int chunk, bool bf16,
+                             void *y, hipStream_t stream);
+
+hipError_t launch_decode_step(float *state, const void *x, const void *dt, const float *A,
+                              const void *B, const void *C, const float *D, int batch, int nheads,
+                              int ngroups, int dstate, bool bf16, void *y, hipStream_t stream);
+
+}  // namespace ssd

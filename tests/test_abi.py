@@ -1,0 +1,122 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, sizes
+its workspace as documented, and rejects bad arguments before touching the GPU
+(every call here fails validation, so no HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+LIB = os.path.join(ROOT, "structured_state_space_ssd_amd", "libssd.so")
+
+SSD_OK, SSD_ERR_NULL, SSD_ERR_SHAPE, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = 0, -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|size_t|int)\s*(ssd_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libssd.so is not built (run __graft_entry__.build())")
+    import torch  # noqa: F401  (binds the HIP runtime the way the package does)
+    from structured_state_space_ssd_amd import _native
+    return _native.lib
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("ssd_forward", "ssd_step", "ssd_forward_workspace_size", "ssd_strerror",
+                     "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(raw, name), f"{name} declared in ssd.h but not exported"
+
+
+def test_strerror(lib):
+    for code in (SSD_OK, SSD_ERR_NULL, SSD_ERR_SHAPE, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP, 42):
+        s = lib.ssd_strerror(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.ssd_strerror(42) == b"unknown status"
+
+
+def _ws_expected(Bt, L, H, P, N, Q):
+    al = lambda v: (v + 255) // 256 * 256
+    nC = -(-L // Q)
+    cs = Bt * H * nC * Q * 4
+    st = Bt * nC * H * P * N * 4
+    return al(cs) + 2 * al(st)
+
+
+@pytest.mark.parametrize("dims", [(8, 2048, 80, 64, 64, 256), (1, 65536, 80, 64, 128, 256),
+                                  (1, 1, 1, 64, 16, 64), (3, 77, 5, 64, 32, 128)])
+def test_workspace_size(lib, dims):
+    assert lib.ssd_forward_workspace_size(*dims) == _ws_expected(*dims)
+
+
+def test_workspace_size_invalid(lib):
+    assert lib.ssd_forward_workspace_size(0, 10, 1, 64, 16, 64) == 0
+    assert lib.ssd_forward_workspace_size(1, 10, 1, 64, 16, 0) == 0
+
+
+FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: every call below fails its checks first
+
+
+def _fwd(lib, **kw):
+    a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, batch=1, seqlen=128, nheads=4,
+             headdim=64, ngroups=1, dstate=64, chunk=64, dtype=1, init=None, y=FAKE, fs=None,
+             ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.ssd_forward(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["batch"], a["seqlen"],
+                           a["nheads"], a["headdim"], a["ngroups"], a["dstate"], a["chunk"], a["dtype"],
+                           a["init"], a["y"], a["fs"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), SSD_ERR_NULL),
+    (dict(y=None), SSD_ERR_NULL),
+    (dict(A=None), SSD_ERR_NULL),
+    (dict(batch=0), SSD_ERR_SHAPE),
+    (dict(seqlen=0), SSD_ERR_SHAPE),
+    (dict(nheads=6, ngroups=4), SSD_ERR_SHAPE),
+    (dict(headdim=32), SSD_ERR_UNSUPPORTED),
+    (dict(dstate=48), SSD_ERR_UNSUPPORTED),
+    (dict(chunk=96), SSD_ERR_UNSUPPORTED),
+    (dict(dtype=7), SSD_ERR_UNSUPPORTED),
+    (dict(x=ctypes.c_void_p(0x100002)), SSD_ERR_UNSUPPORTED),
+    (dict(ws=None), SSD_ERR_WORKSPACE),
+    (dict(wsb=1024), SSD_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x100010)), SSD_ERR_WORKSPACE),
+])
+def test_forward_rejects(lib, kw, code):
+    assert _fwd(lib, **kw) == code
+
+
+def test_step_rejects(lib):
+    args = [FAKE] * 7 + [4, 8, 64, 2, 128, 1, FAKE, None]
+    ok = list(args)
+    bad = list(ok); bad[0] = None
+    assert lib.ssd_step(*bad) == SSD_ERR_NULL
+    bad = list(ok); bad[8] = 6; bad[10] = 4  # nheads 6, ngroups 4
+    assert lib.ssd_step(*bad) == SSD_ERR_SHAPE
+    bad = list(ok); bad[11] = 100
+    assert lib.ssd_step(*bad) == SSD_ERR_UNSUPPORTED
+    bad = list(ok); bad[9] = 128
+    assert lib.ssd_step(*bad) == SSD_ERR_UNSUPPORTED
+
+
+def test_stage_entry_points_reject(lib):
+    assert lib.ssd_chunk_cumsum(None, FAKE, 1, 10, 2, 64, 1, FAKE, None) == SSD_ERR_NULL
+    assert lib.ssd_chunk_cumsum(FAKE, FAKE, 1, 10, 2, 100, 1, FAKE, None) == SSD_ERR_UNSUPPORTED
+    assert lib.ssd_chunk_state(FAKE, FAKE, FAKE, FAKE, 1, 10, 3, 64, 2, 64, 64, 1, FAKE, None) == SSD_ERR_SHAPE
+    assert lib.ssd_state_passing(FAKE, FAKE, None, 1, 10, 2, 64, 64, 64, None, None, None) == SSD_ERR_NULL
+    assert lib.ssd_chunk_scan(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 10, 2, 64, 1, 64, 256, 9,
+                              FAKE, None) == SSD_ERR_UNSUPPORTED

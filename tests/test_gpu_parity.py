@@ -1,0 +1,144 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case runs the same seeded inputs through the library and the oracle and
+compares relative L2 at the stated tolerances (1e-4 float32, 2e-2 bf16, 1e-3
+for the decode state). Each forward case is also run with D = 0, because the
+D x term dominates y and would otherwise hide errors in the SSM part.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import ssd_workloads as W
+from gpu_util import down, print_case, rel_l2, tol, units_view, up
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _ssd():
+    import structured_state_space_ssd_amd as ssd
+    return ssd
+
+
+def run_forward(w, d, D, init, units=None):
+    ssd = _ssd()
+    y, fs = ssd.forward(up(d["x"]), up(d["dt"]), up(d["A"]), up(d["B"]), up(d["C"]),
+                        None if D is None else up(D), chunk=w.chunk, init_state=up(init),
+                        return_final_state=True)
+    torch.cuda.synchronize()
+    return y, fs
+
+
+def check_forward(w, units=None, init=None, both_D=True):
+    """Compare y and the final state with the oracle (all units or a sample)."""
+    print_case(f"[forward] {w.name} Bt={w.batch} L={w.seqlen} H={w.nheads} G={w.ngroups} "
+               f"N={w.dstate} Q={w.chunk} {w.dtype} units={'all' if units is None else len(units)}")
+    d = W.generate(w)
+    if init is None:
+        init = d["init"]
+    H = w.nheads
+    uu = np.arange(w.batch * H) if units is None else np.asarray(units)
+    # oracle without D; the D x term is added exactly in float64 (y is linear in it)
+    y0, s0, _ = oracle.forward(d["x"].val, d["dt"].val, d["A"], d["B"].val, d["C"].val, None,
+                               init, units=None if units is None else uu)
+    xv = units_view(d["x"].val, uu, H).astype(np.float64)
+    Dv = d["D"].astype(np.float64)[uu % H][:, None, None]
+    errs = {}
+    for with_D in ([True, False] if both_D else [True]):
+        y, fs = run_forward(w, d, d["D"] if with_D else None, init)
+        yg = units_view(down(y), uu, H)
+        yref = y0 + Dv * xv if with_D else y0
+        errs[f"y{'_D' if with_D else '_noD'}"] = rel_l2(yg, yref)
+        fsg = down(fs).reshape(-1, w.headdim, w.dstate)[uu]
+        errs["state"] = rel_l2(fsg, s0)
+        del y, fs
+    print_case(f"   errors {errs}")
+    t = tol(w.dtype)
+    for k, e in errs.items():
+        assert e < t, (w.name, k, e)
+    return errs
+
+
+# ---------------------------------------------------------------- named workloads
+
+def test_tiny_f32():
+    check_forward(W.WORKLOADS["tiny_f32"])
+
+
+def test_mamba2_2p7b_full():
+    check_forward(W.WORKLOADS["mamba2_2.7b"])
+
+
+def test_large_state_full():
+    check_forward(W.WORKLOADS["large_state"])
+
+
+def test_long_seq_sampled():
+    w = W.WORKLOADS["long_seq"]
+    # heads from every other group, first / last head of a group
+    check_forward(w, units=[0, 9, 10, 37, 44, 79])
+
+
+def test_decode_64_steps():
+    _decode(W.WORKLOADS["decode"], zero_init=False)
+
+
+def test_decode_64_steps_zero_init():
+    _decode(W.WORKLOADS["decode"], zero_init=True)
+
+
+def _decode(w, zero_init, nunits=512):
+    ssd = _ssd()
+    print_case(f"[decode] Bt={w.batch} H={w.nheads} N={w.dstate} steps={w.seqlen} zero_init={zero_init}")
+    d = W.generate(w)
+    H, P, N = w.nheads, w.headdim, w.dstate
+    rng = np.random.default_rng(123)
+    units = np.sort(rng.choice(w.batch * H, size=nunits, replace=False))
+    init = np.zeros_like(d["init"]) if zero_init else d["init"]
+    state = up(init)
+    st_o = np.ascontiguousarray(init.reshape(-1, P, N)[units].astype(np.float64))
+    X, DT, Bv, Cv = up(d["x"]), up(d["dt"]), up(d["B"]), up(d["C"])
+    A, D = up(d["A"]), up(d["D"])
+    ys, yos = [], []
+    for t in range(w.seqlen):
+        y = ssd.step(state, X[t], DT[t], A, Bv[t], Cv[t], D)
+        ys.append(down(y).reshape(-1, P)[units])
+        yos.append(oracle.step(st_o, d["x"].val[t], d["dt"].val[t], d["A"], d["B"].val[t],
+                               d["C"].val[t], d["D"], units=units))
+    torch.cuda.synchronize()
+    ey = rel_l2(np.stack(ys), np.stack(yos))
+    es = rel_l2(down(state).reshape(-1, P, N)[units], st_o)
+    print_case(f"   rel_l2 y={ey:.3e} state={es:.3e}")
+    assert ey < tol(w.dtype) and es < 1e-3
+
+
+# ---------------------------------------------------------------- sweeps and edge cases
+
+SWEEP = [(n, q, dt) for dt in ("f32", "bf16") for n in (16, 32, 64, 128, 256) for q in (64, 128, 256)]
+
+
+@pytest.mark.parametrize("N,Q,dtype", SWEEP, ids=[f"N{n}-Q{q}-{d}" for n, q, d in SWEEP])
+def test_sweep_shapes(N, Q, dtype):
+    # several chunks plus a ragged tail; 2 groups; non-zero initial state
+    w = W.small(f"sweep_N{N}_Q{Q}_{dtype}", 2, 2 * Q + 37, 4, 64, 2, N, Q, dtype,
+                seed=100 + N + Q, init_std=0.2)
+    check_forward(w)
+
+
+@pytest.mark.parametrize("L,Q", [(1, 64), (50, 64), (64, 64), (65, 64), (127, 128), (300, 256)])
+def test_short_and_ragged(L, Q):
+    check_forward(W.small(f"ragged_L{L}_Q{Q}", 3, L, 2, 64, 1, 64, Q, "bf16", seed=200 + L))
+
+
+def test_groups_8():
+    check_forward(W.small("groups8", 1, 600, 16, 64, 8, 128, 256, "bf16", seed=301, init_std=0.1))
+
+
+def test_strong_decay_and_large_dt():
+    # dt up to 2 with A down to -16: within-chunk log-decay far below fp32 exp range
+    check_forward(W.small("strong", 2, 512, 4, 64, 1, 64, 256, "f32", seed=302, dt_lo=0.5, dt_hi=2.0))
+
+
+def test_slow_decay_long():
+    check_forward(W.small("slow", 1, 4096, 4, 64, 1, 64, 128, "f32", seed=303, dt_lo=1e-5, dt_hi=1e-4))
