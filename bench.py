@@ -1,0 +1,333 @@
+"""SSD layer benchmark on one MI355X.
+
+One step = one full SSD forward (chunk_cumsum, chunk_state, state_passing,
+chunk_cb, chunk_scan) over the Mamba-2 2.7B-shaped layer: batch 8, L 2048, 80 heads x
+P 64, N 64, one B/C group, chunk 256, bf16 inputs, fp32 accumulation, inputs
+already resident in HBM. Prints ONE JSON line.
+
+Per-stage GPU times come from HIP events the library records between its
+launches (ssd_forward_timed) on the launch stream, inside the timed region.
+Roofline figures use algorithmic bytes / flops (what the method must read,
+write and compute), not executed ones. The decode step (256 x 80 heads,
+P 64, N 128, fp32 state, 64 consecutive tokens) is reported alongside.
+The CPU baseline is the fp64 oracle (test infrastructure) on the same
+workload, timed on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSD layer fwd tokens/s + MFMA util (2.7B-shape, L=2048); decode step GB/s"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (no sparsity)
+FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix
+STAGES = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_cb", "chunk_scan"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+# ---------------------------------------------------------------- accounting
+
+def accounting(w):
+    """Algorithmic bytes and flops per launch of each forward stage.
+
+    Bytes: every input read once and every output written once, at its storage
+    width (bf16 2 B for x, dt, B, C, y and, in bf16 runs, chunk_init; float32
+    4 B for A, D, dA_cumsum and the chunk states). B and C are counted once per
+    group, not per head.
+    The C B^T tiles (chunk_cb output, chunk_scan input) are counted once each
+    way. Flops (multiply + add = 2): chunk_state 2PN per token-head;
+    chunk_scan (Q+1)P (causal masked product: Q(Q+1)/2 pairs x 2P per
+    chunk-head) + 2NP (state to output) + 2P (skip) per token-head; chunk_cb
+    (Q+1)N per token per group (causal C B^T); state_passing 2PN per
+    chunk-head element pair.
+    """
+    Bt, L, H, P, G, N, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk
+    e = 2 if w.dtype == "bf16" else 4
+    nC = -(-L // Q)
+    tok = Bt * L
+    x = tok * H * P * e
+    dt = tok * H * e
+    bc = tok * G * N * e
+    s = Bt * H * nC * Q * 4
+    st = Bt * nC * H * P * N * 4
+    ci = Bt * nC * H * P * N * e  # chunk_init, stored in the operand type
+    send = Bt * H * nC * 4
+    nt = Q // 16
+    cb = Bt * nC * G * (nt // 2) * (nt // 2 + 1) * 512 * e  # causal C B^T tiles
+    acc = {
+        "chunk_cumsum": {"bytes": dt + H * 4 + s, "flops": tok * H * 2},
+        "chunk_state": {"bytes": x + bc + dt + s + st, "flops": tok * H * 2 * P * N},
+        "state_passing": {"bytes": st + ci + send, "flops": Bt * nC * H * P * N * 2},
+        "chunk_cb": {"bytes": 2 * bc + cb, "flops": tok * G * (Q + 1) * N},
+        "chunk_scan": {"bytes": x + x + dt + s + bc + cb + ci + H * 4,
+                       "flops": tok * H * ((Q + 1) * P + 2 * N * P + 2 * P)},
+    }
+    return acc
+
+
+def decode_accounting(w):
+    Bt, H, P, G, N = w.batch, w.nheads, w.headdim, w.ngroups, w.dstate
+    e = 2 if w.dtype == "bf16" else 4
+    state = Bt * H * P * N * 4
+    inputs = Bt * H * P * e + Bt * H * e + 2 * Bt * G * N * e + 2 * H * 4
+    return {"bytes": 2 * state + inputs + Bt * H * P * e, "flops": Bt * H * P * N * 5}
+
+
+def kernel_source_digest(name):
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "structured_state_space_ssd_amd", "csrc")
+    for f in (f"{name}.hip", "ssd_common.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current source of the kernel; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(kernel)
+    if not rec or rec.get("source_digest") != kernel_source_digest(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------- GPU timing
+
+def upload(d):
+    import numpy as np
+    import torch
+    import ssd_workloads as W
+    out = {}
+    for k, t in d.items():
+        if t is None:
+            out[k] = None
+        elif isinstance(t, W.Tensor):
+            if t.dtype == "bf16":
+                out[k] = torch.from_numpy(t.dev.view(np.int16)).view(torch.bfloat16).cuda()
+            else:
+                out[k] = torch.from_numpy(t.dev).cuda()
+        else:
+            out[k] = torch.from_numpy(np.ascontiguousarray(t)).cuda()
+    return out
+
+
+def time_forward(w, steps, warmup):
+    import torch
+    import ssd_workloads as W
+    import structured_state_space_ssd_amd as ssd
+
+    d = W.generate(w)
+    g = upload(d)
+    x, dt, A, B, C, D = (g[k] for k in ("x", "dt", "A", "B", "C", "D"))
+    ws = torch.empty(ssd.workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate,
+                                        w.chunk, x.dtype), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    ns = len(STAGES)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)] for _ in range(steps)]
+    for evs in events:  # create the underlying HIP events
+        for e in evs:
+            e.record()
+    for _ in range(warmup):
+        ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y, events=events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_stage = [0.0] * ns
+    for evs in events:
+        for i in range(ns):
+            per_stage[i] += evs[i].elapsed_time(evs[i + 1])
+    per_stage = [v / steps for v in per_stage]  # ms
+    gpu_ms = sum(events[k][0].elapsed_time(events[k][ns]) for k in range(steps)) / steps
+    span_ms = events[0][0].elapsed_time(events[-1][ns]) / steps
+    return {"wall_ms": wall * 1e3 / steps, "gpu_ms": gpu_ms, "span_ms": span_ms,
+            "stage_ms": dict(zip(STAGES, per_stage))}
+
+
+def time_decode(w, warmup=3):
+    import torch
+    import ssd_workloads as W
+    import structured_state_space_ssd_amd as ssd
+
+    d = W.generate(w)
+    g = upload(d)
+    state = g["init"]
+    x, dt, A, B, C, D = (g[k] for k in ("x", "dt", "A", "B", "C", "D"))
+    y = torch.empty_like(x[0])
+    for t in range(warmup):
+        ssd.step(state, x[t], dt[t], A, B[t], C[t], D, y=y)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(w.seqlen + 1)]
+    ev[0].record()
+    for t in range(w.seqlen):
+        ssd.step(state, x[t], dt[t], A, B[t], C[t], D, y=y)
+        ev[t + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[t].elapsed_time(ev[t + 1]) for t in range(w.seqlen)]
+    return {"mean_ms": sum(per) / len(per), "min_ms": min(per), "max_ms": max(per)}
+
+
+def cpu_baseline(w):
+    """The fp64 oracle (as it stands) on the same workload, on this host."""
+    import oracle
+    import ssd_workloads as W
+    d = W.generate(w)
+    n = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.forward(d["x"].val, d["dt"].val, d["A"], d["B"].val, d["C"].val, d["D"], None,
+                   want_state=True, nthreads=n)
+    sec = time.perf_counter() - t0
+    return {"value": w.tokens / sec, "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"the whole {w.name} forward (batch {w.batch} x L {w.seqlen}, all {w.batch * w.nheads} "
+                      f"(batch, head) units), one pass, fp64 recurrence, {sec:.2f} s wall"}
+
+
+def counters_run(w):
+    """A short, fixed sequence of launches for counter collection."""
+    import torch
+    copy_bytes = 1 << 30
+    src = torch.empty(copy_bytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        dst.copy_(src)  # reads and writes exactly copy_bytes each
+    torch.cuda.synchronize()
+    print(f"[counters] copy of {copy_bytes} bytes x2 done", file=sys.stderr, flush=True)
+    del src, dst
+    time_forward(w, steps=3, warmup=1)
+    print("[counters] forward x4 done", file=sys.stderr, flush=True)
+    time_decode(W_decode(), warmup=0)
+    print("[counters] decode done", file=sys.stderr, flush=True)
+
+
+def W_decode():
+    import ssd_workloads as W
+    return W.WORKLOADS["decode"]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mamba2_2.7b")
+    ap.add_argument("--all", action="store_true", help="also time the other forward workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--counters", action="store_true",
+                    help="short run for rocprofv3 counter collection: a few forwards, a few decode "
+                         "steps and a plain 1 GiB device copy that calibrates the byte counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this SSD build has no multi-GPU path "
+              "(batch/head sharding needs no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ssd_workloads as W
+    import structured_state_space_ssd_amd  # noqa: F401  (fails loudly if libssd.so is missing)
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w = W.WORKLOADS[args.workload]
+    if args.counters:
+        counters_run(w)
+        return
+    print(f"[bench] {w.name}: timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
+    fwd = time_forward(w, args.steps, args.warmup)
+    ms = fwd["wall_ms"]
+    acc = accounting(w)
+    kernels = {}
+    for name in STAGES:
+        t = fwd["stage_ms"][name] * 1e-3
+        a = acc[name]
+        gbs = a["bytes"] / t / 1e9
+        tfl = a["flops"] / t / 1e12
+        peak_f = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+        intensity = a["flops"] / a["bytes"]
+        applicable = min(peak_f, intensity * HBM_PEAK_GBS / 1e3)  # TFLOP/s roof at this intensity
+        kernels[name] = {"us": round(t * 1e6, 2), "alg_bytes": a["bytes"], "alg_flops": a["flops"],
+                         "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "TFLOP_s": round(tfl, 2), "mfma_frac": round(tfl / peak_f, 4),
+                         "roofline_frac": round(tfl / applicable, 4)}
+    dom = max(STAGES, key=lambda k: fwd["stage_ms"][k])
+    dk = kernels[dom]
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": dk["GB_s"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(dk["GB_s"] / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dom)}
+    print(f"[bench] forward {ms * 1e3:.1f} us/step; stages " +
+          ", ".join(f"{k} {v['us']:.1f} us" for k, v in kernels.items()), file=sys.stderr, flush=True)
+
+    extra = {}
+    if args.all:
+        for name in ("tiny_f32", "large_state", "long_seq"):
+            wl = W.WORKLOADS[name]
+            r = time_forward(wl, 10, 3)
+            extra[name] = {"us_per_forward": round(r["wall_ms"] * 1e3, 1),
+                           "tokens_per_s": round(wl.tokens / (r["wall_ms"] * 1e-3)),
+                           "stage_us": {k: round(v * 1e3, 1) for k, v in r["stage_ms"].items()}}
+            print(f"[bench] {name}: {r['wall_ms'] * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    wd = W.WORKLOADS["decode"]
+    dec = time_decode(wd)
+    da = decode_accounting(wd)
+    dec_gbs = da["bytes"] / (dec["mean_ms"] * 1e-3) / 1e9
+    decode = {"workload": "decode: batch 256, 80 heads x P 64, N 128, fp32 state, bf16 inputs, 64 steps",
+              "us_per_step": round(dec["mean_ms"] * 1e3, 2), "GB_s": round(dec_gbs, 1),
+              "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4), "alg_bytes_per_step": da["bytes"],
+              "tokens_per_s": round(wd.batch / (dec["mean_ms"] * 1e-3))}
+    print(f"[bench] decode {decode['us_per_step']} us/step, {decode['GB_s']} GB/s", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] cpu baseline (fp64 oracle)...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w)
+
+    out = {
+        "metric": METRIC,
+        "value": round(w.tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; shapes and distributions of the named workload)",
+        "config": {"workload": "SSD layer forward, Mamba-2 2.7B shape", "batch": w.batch,
+                   "seq_len": w.seqlen, "nheads": w.nheads, "headdim": w.headdim,
+                   "dstate": w.dstate, "ngroups": w.ngroups, "chunk": w.chunk,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "gpu_us_per_step": round(fwd["gpu_ms"] * 1e3, 2),
+        "kernels": kernels,
+        "decode": decode,
+    }
+    if extra:
+        out["other_workloads"] = extra
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -71,16 +71,18 @@ const char *ssd_strerror(int status);
  * holds, at 256-byte aligned offsets in this order:
  *   dA_cumsum   float32 [Bt][H][nC*Q]      within-chunk prefix sums of dt*A
  *   states      float32 [Bt][nC][H][P][N]  each chunk's own state contribution
- *   chunk_init  float32 [Bt][nC][H][P][N]  state entering each chunk
+ *   chunk_init  [Bt][nC][H][P][N]          state entering each chunk, in the MFMA
+ *                                          operand type (bf16 for SSD_BF16, else float32)
+ *   cb          ssd_chunk_cb_size(...) bytes: C B^T tiles of every chunk
  * After the forward pass has run, these hold the intermediate results of the
- * four stages below (a caller may read them, e.g. to test a stage).
+ * stages below (a caller may read them, e.g. to test a stage).
  */
 size_t ssd_forward_workspace_size(int batch, int seqlen, int nheads, int headdim,
-                                  int dstate, int chunk);
+                                  int ngroups, int dstate, int chunk, int dtype);
 
 /*
  * Full SSD layer forward: enqueues ssd_chunk_cumsum, ssd_chunk_state,
- * ssd_state_passing and ssd_chunk_scan on `stream`.
+ * ssd_state_passing, ssd_chunk_cb and ssd_chunk_scan on `stream`.
  *   D           nullable: no feed-through term.
  *   init_state  nullable: the state before token 0 is zero.
  *   y           output, [Bt][L][H][P] in dtype.
@@ -92,6 +94,21 @@ int ssd_forward(const void *x, const void *dt, const float *A, const void *B,
                 int headdim, int ngroups, int dstate, int chunk, int dtype,
                 const float *init_state, void *y, float *final_state,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ssd_forward with per-stage timing hooks for profilers and benchmarks.
+ * `events` is NULL (then this is exactly ssd_forward) or an array of 6
+ * hipEvent_t owned by the caller: events[k] is recorded on `stream` right
+ * before stage k+1 is enqueued and events[5] after the last stage, so the
+ * elapsed time between consecutive events is each stage's GPU time (stages in
+ * the order listed for ssd_forward).
+ */
+int ssd_forward_timed(const void *x, const void *dt, const float *A, const void *B,
+                      const void *C, const float *D, int batch, int seqlen, int nheads,
+                      int headdim, int ngroups, int dstate, int chunk, int dtype,
+                      const float *init_state, void *y, float *final_state,
+                      void *workspace, size_t workspace_bytes, void *stream,
+                      void *const *events);
 
 /*
  * One recurrent (decode) step for every (batch, head): updates `state`
@@ -125,24 +142,38 @@ int ssd_chunk_state(const void *x, const void *B, const void *dt, const float *d
                     int chunk, int dtype, float *states, void *stream);
 
 /*
- * Stage 3: the sequential pass over chunks,
+ * Stage 3: the sequential pass over chunks, in float32,
  *   H_0 = init_state (NULL: zero),  H_{c+1} = exp(s_end(c)) * H_c + states_c,
- * writing chunk_init[b][c] = H_c (float32 [Bt][nC][H][P][N]) and, if
- * final_state is not NULL, final_state = H_nC ([Bt][H][P][N]).
+ * writing chunk_init[b][c] = H_c ([Bt][nC][H][P][N] in the operand type of
+ * dtype: bf16 for SSD_BF16, the precision ssd_chunk_scan multiplies it in;
+ * float32 for SSD_F32) and, if final_state is not NULL, final_state = H_nC
+ * (float32 [Bt][H][P][N]).
  */
 int ssd_state_passing(const float *states, const float *dA_cumsum, const float *init_state,
                       int batch, int seqlen, int nheads, int headdim, int dstate, int chunk,
-                      float *chunk_init, float *final_state, void *stream);
+                      int dtype, void *chunk_init, float *final_state, void *stream);
 
 /*
- * Stage 4: outputs of every chunk,
+ * Stage 4a: C_i . B_j for every pair of tokens j <= i (in 32-token slices) of
+ * every chunk, once per B/C group; this does not depend on the head. `cb` is
+ * scratch of ssd_chunk_cb_size(...) bytes (32-byte aligned) in the layout
+ * ssd_chunk_scan reads (MFMA operand fragments, in dtype's operand type: bf16
+ * or float32). The content is only meant for ssd_chunk_scan.
+ */
+size_t ssd_chunk_cb_size(int batch, int seqlen, int ngroups, int chunk, int dtype);
+int ssd_chunk_cb(const void *B, const void *C, int batch, int seqlen, int ngroups, int dstate,
+                 int chunk, int dtype, void *cb, void *stream);
+
+/*
+ * Stage 4b: outputs of every chunk,
  *   y_i = sum_{j in c, j <= i} (C_i . B_j) exp(s_i - s_j) dt_j x_j   (diagonal block)
  *       + exp(s_i) H_c C_i                                           (off-diagonal blocks)
  *       + D_h x_i,
- * writing y [Bt][L][H][P] in dtype. D is nullable.
+ * with C_i . B_j read from `cb` (stage 4a), writing y [Bt][L][H][P] in dtype.
+ * D is nullable.
  */
-int ssd_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *B,
-                   const void *C, const float *D, const float *chunk_init, int batch,
+int ssd_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *C,
+                   const void *cb, const float *D, const void *chunk_init, int batch,
                    int seqlen, int nheads, int headdim, int ngroups, int dstate, int chunk,
                    int dtype, void *y, void *stream);
 

@@ -7,13 +7,15 @@ and call the C ABI.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import _native
 from ._native import SSDError, check, dtype_code, ptr, stream_handle
 
 __all__ = ["forward", "step", "workspace_size", "chunk_cumsum", "chunk_state",
-           "state_passing", "chunk_scan", "SSDError", "stages"]
+           "state_passing", "chunk_cb", "chunk_scan", "SSDError", "stages"]
 
 HEADDIM = 64
 
@@ -34,17 +36,20 @@ def _opt(t, name, dtype=torch.float32):
     return None if t is None else _req(t, name, dtype)
 
 
-def workspace_size(batch, seqlen, nheads, headdim, dstate, chunk) -> int:
-    return int(_native.lib.ssd_forward_workspace_size(batch, seqlen, nheads, headdim, dstate, chunk))
+def workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, dtype=torch.bfloat16) -> int:
+    return int(_native.lib.ssd_forward_workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate,
+                                                      chunk, dtype_code(dtype)))
 
 
 def forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, return_final_state=False,
-            workspace=None):
+            workspace=None, y=None, events=None):
     """y = SSD(x, dt, A, B, C, D) over whole sequences.
 
     x [Bt,L,H,P], dt [Bt,L,H], B, C [Bt,L,G,N] (all float32 or all bfloat16),
     A, D [H] float32, init_state [Bt,H,P,N] float32 or None.
     Returns y (and the final state [Bt,H,P,N] float32 if requested).
+    ``events``: optional sequence of 6 recorded-once torch.cuda.Event(enable_timing=True);
+    the library records them around its five stages (see ssd_forward_timed).
     """
     _req(x, "x")
     dt_ = dtype_code(x.dtype)
@@ -58,14 +63,21 @@ def forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, return_final_sta
     G, N = B.shape[2], B.shape[3]
     if tuple(dt.shape) != (Bt, L, H) or tuple(B.shape) != (Bt, L, G, N) or C.shape != B.shape:
         raise ValueError("shape mismatch among x, dt, B, C")
-    y = torch.empty_like(x)
+    if y is None:
+        y = torch.empty_like(x)
     fs = torch.empty((Bt, H, P, N), dtype=torch.float32, device=x.device) if return_final_state else None
-    need = workspace_size(Bt, L, H, P, N, chunk)
+    need = workspace_size(Bt, L, H, P, G, N, chunk, x.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    rc = _native.lib.ssd_forward(
+    ev = None
+    if events is not None:
+        if len(events) != 6:
+            raise ValueError("events must hold 6 torch.cuda.Event objects")
+        ev = (ctypes.c_void_p * 6)(*[e.cuda_event for e in events])
+    rc = _native.lib.ssd_forward_timed(
         ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), Bt, L, H, P, G, N, chunk, dt_,
-        ptr(init_state), ptr(y), ptr(fs), ptr(workspace), workspace.numel(), stream_handle(x.device))
+        ptr(init_state), ptr(y), ptr(fs), ptr(workspace), workspace.numel(), stream_handle(x.device),
+        ev)
     check(rc, "ssd_forward")
     return (y, fs) if return_final_state else y
 
@@ -126,29 +138,44 @@ def chunk_state(x, B, dt, dA_cumsum, chunk, out=None):
     return out
 
 
-def state_passing(states, dA_cumsum, seqlen, chunk, init_state=None, out=None, final_state=None):
-    """chunk_init [Bt,nC,H,P,N] float32 (state entering each chunk); optional final state."""
+def state_passing(states, dA_cumsum, seqlen, chunk, init_state=None, out=None, final_state=None,
+                  dtype=torch.float32):
+    """chunk_init [Bt,nC,H,P,N] (state entering each chunk) in ``dtype`` (the
+    forward's input dtype: bf16 or float32); optional float32 final state."""
     Bt, nC, H, P, N = _req(states, "states", torch.float32).shape
     if out is None:
-        out = torch.empty_like(states)
+        out = torch.empty(states.shape, dtype=dtype, device=states.device)
     rc = _native.lib.ssd_state_passing(ptr(states), ptr(_req(dA_cumsum, "dA_cumsum", torch.float32)),
                                        ptr(_opt(init_state, "init_state")), Bt, seqlen, H, P, N, chunk,
-                                       ptr(out), ptr(_opt(final_state, "final_state")),
+                                       dtype_code(out.dtype), ptr(out),
+                                       ptr(_opt(final_state, "final_state")),
                                        stream_handle(states.device))
     check(rc, "ssd_state_passing")
     return out
 
 
-def chunk_scan(x, dt, dA_cumsum, B, C, D, chunk_init, chunk, y=None):
+def chunk_cb(B, C, chunk, out=None):
+    """C B^T tiles of every chunk (opaque layout, read by chunk_scan)."""
+    Bt, L, G, N = _req(B, "B").shape
+    n = int(_native.lib.ssd_chunk_cb_size(Bt, L, G, chunk, dtype_code(B.dtype)))
+    if out is None:
+        out = torch.empty(max(n, 1), dtype=torch.uint8, device=B.device)
+    rc = _native.lib.ssd_chunk_cb(ptr(B), ptr(_req(C, "C", B.dtype)), Bt, L, G, N, chunk,
+                                  dtype_code(B.dtype), ptr(out), stream_handle(B.device))
+    check(rc, "ssd_chunk_cb")
+    return out
+
+
+def chunk_scan(x, dt, dA_cumsum, C, cb, D, chunk_init, chunk, y=None):
     """y [Bt,L,H,P]: intra-chunk product + state-to-output + D x."""
     Bt, L, H, P = _req(x, "x").shape
-    G, N = B.shape[2], B.shape[3]
+    G, N = C.shape[2], C.shape[3]
     if y is None:
         y = torch.empty_like(x)
     rc = _native.lib.ssd_chunk_scan(ptr(x), ptr(_req(dt, "dt", x.dtype)),
                                     ptr(_req(dA_cumsum, "dA_cumsum", torch.float32)),
-                                    ptr(_req(B, "B", x.dtype)), ptr(_req(C, "C", x.dtype)),
-                                    ptr(_opt(D, "D")), ptr(_req(chunk_init, "chunk_init", torch.float32)),
+                                    ptr(_req(C, "C", x.dtype)), ptr(_req(cb, "cb")),
+                                    ptr(_opt(D, "D")), ptr(_req(chunk_init, "chunk_init", x.dtype)),
                                     Bt, L, H, P, G, N, chunk, dtype_code(x.dtype), ptr(y),
                                     stream_handle(x.device))
     check(rc, "ssd_chunk_scan")
@@ -156,13 +183,14 @@ def chunk_scan(x, dt, dA_cumsum, B, C, D, chunk_init, chunk, y=None):
 
 
 def stages(x, dt, A, B, C, D=None, chunk=256, init_state=None):
-    """Run the four forward stages one call at a time; returns a dict with every
-    intermediate (dA_cumsum, states, chunk_init, final_state) and y."""
+    """Run the forward stages one call at a time; returns a dict with every
+    intermediate (dA_cumsum, states, chunk_init, final_state, cb) and y."""
     Bt, L, H, P = x.shape
     N = B.shape[3]
     s = chunk_cumsum(dt, A, chunk)
     st = chunk_state(x, B, dt, s, chunk)
     fs = torch.empty((Bt, H, P, N), dtype=torch.float32, device=x.device)
-    ci = state_passing(st, s, L, chunk, init_state=init_state, final_state=fs)
-    y = chunk_scan(x, dt, s, B, C, D, ci, chunk)
-    return {"dA_cumsum": s, "states": st, "chunk_init": ci, "final_state": fs, "y": y}
+    ci = state_passing(st, s, L, chunk, init_state=init_state, final_state=fs, dtype=x.dtype)
+    cb = chunk_cb(B, C, chunk)
+    y = chunk_scan(x, dt, s, C, cb, D, ci, chunk)
+    return {"dA_cumsum": s, "states": st, "chunk_init": ci, "final_state": fs, "cb": cb, "y": y}

@@ -23,12 +23,15 @@ _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 # name -> (restype, argtypes); mirrors include/ssd.h
 SIGNATURES = {
     "ssd_strerror": (ctypes.c_char_p, [_i]),
-    "ssd_forward_workspace_size": (_sz, [_i] * 6),
+    "ssd_forward_workspace_size": (_sz, [_i] * 8),
+    "ssd_chunk_cb_size": (_sz, [_i] * 5),
+    "ssd_chunk_cb": (_i, [_vp, _vp] + [_i] * 6 + [_vp, _vp]),
     "ssd_forward": (_i, [_vp] * 6 + [_i] * 8 + [_vp, _vp, _vp, _vp, _sz, _vp]),
+    "ssd_forward_timed": (_i, [_vp] * 6 + [_i] * 8 + [_vp, _vp, _vp, _vp, _sz, _vp, _vp]),
     "ssd_step": (_i, [_vp] * 7 + [_i] * 6 + [_vp, _vp]),
     "ssd_chunk_cumsum": (_i, [_vp, _vp] + [_i] * 5 + [_vp, _vp]),
     "ssd_chunk_state": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _vp]),
-    "ssd_state_passing": (_i, [_vp] * 3 + [_i] * 6 + [_vp, _vp, _vp]),
+    "ssd_state_passing": (_i, [_vp] * 3 + [_i] * 7 + [_vp, _vp, _vp]),
     "ssd_chunk_scan": (_i, [_vp] * 7 + [_i] * 8 + [_vp, _vp]),
 }
 
@@ -36,7 +39,7 @@ SIGNATURES = {
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m structured_state_space_ssd_amd.build` "
+            f"{LIB_PATH} is not built; run `python structured_state_space_ssd_amd/build.py` "
             "(there is no fallback implementation)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():

@@ -1,7 +1,8 @@
 """Compile the HIP sources in csrc/ into libssd.so (gfx950 only), in-tree.
 
 Each .hip file is compiled to an object in parallel, then linked into one
-shared library next to this file. Run ``python -m structured_state_space_ssd_amd.build``.
+shared library next to this file. Run ``python structured_state_space_ssd_amd/build.py``
+(by path: importing the package loads the library being built).
 """
 from __future__ import annotations
 

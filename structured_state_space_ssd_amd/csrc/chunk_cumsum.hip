@@ -2,67 +2,94 @@
 // of a_t = dt_t * A_h ("Mamba 模型", section 4.1: the decay between tokens j <= i
 // of one chunk is exp(s_i - s_j), the segment sum of a over (j, i]).
 //
-// One workgroup per (chunk, batch, block of 32 heads). The Q x 32 tile of a is
-// read with row-contiguous (head-fastest) loads into LDS, then each wavefront
-// scans one head at a time: every lane sums Q/64 consecutive tokens, a
-// wavefront-wide inclusive scan of the lane totals gives each lane its
-// offset, and the chunk row s[b][h][cQ .. cQ+Q) is written contiguously.
+// Two-level scan with an LDS transpose. A workgroup of 1024 threads covers one
+// (chunk, batch, block of 64 heads). Thread (k, hh) owns the k-th of 16 runs of
+// Q/16 consecutive tokens of head hh. Its loads are unconditional (the token
+// and head indices are clamped into range and out-of-range values replaced by
+// zero with a select), so all of them are in flight together; one load
+// instruction reads 64 consecutive heads of one token (128 contiguous bytes of
+// bf16 dt). Each thread forms its run's prefix sums in registers and writes
+// them, and the run total, to LDS; one wavefront per head then turns the 16
+// run totals into run offsets. The outputs are written token-fastest: lanes
+// take consecutive tokens of one head, so each store instruction writes 256
+// contiguous bytes of s[b][h][.].
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 
-constexpr int kCumsumHeads = 32;
+constexpr int kCumsumHeads = 64;
+constexpr int kCumsumRuns = 16;
 
-template <typename T>
-__global__ __launch_bounds__(256) void chunk_cumsum_kernel(const T *__restrict__ dt,
-                                                           const float *__restrict__ A, int L,
-                                                           int H, int Q, int nC,
-                                                           float *__restrict__ out) {
-    __shared__ float tile[256][kCumsumHeads + 1];
+template <typename T, int Q>
+__global__ __launch_bounds__(1024) void chunk_cumsum_kernel(const T *__restrict__ dt,
+                                                            const float *__restrict__ A, int L,
+                                                            int H, int nC,
+                                                            float *__restrict__ out) {
+    constexpr int R = Q / kCumsumRuns;  // tokens per run: 4, 8 or 16
+    __shared__ float tile[Q][kCumsumHeads + 1];
+    __shared__ float off[kCumsumRuns][kCumsumHeads];
     const int c = blockIdx.x, b = blockIdx.y, h0 = blockIdx.z * kCumsumHeads;
+    const int tid = threadIdx.x;
+    const int hh = tid & 63, k = tid >> 6, h = h0 + hh;
+    const int hc = min(h, H - 1);
     const int t0 = c * Q;
-    const int len = min(Q, L - t0);
-    for (int idx = threadIdx.x; idx < Q * kCumsumHeads; idx += blockDim.x) {
-        const int t = idx / kCumsumHeads, hh = idx % kCumsumHeads, h = h0 + hh;
-        float a = 0.0f;
-        if (t < len && h < H) a = to_f32(dt[((size_t)b * L + t0 + t) * H + h]) * A[h];
-        tile[t][hh] = a;
+    const float a = h < H ? A[hc] : 0.0f;
+    float v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int t = t0 + k * R + r;
+        const float d = to_f32(dt[((size_t)b * L + min(t, L - 1)) * H + hc]);
+        v[r] = (h < H && t < L) ? d * a : 0.0f;
+    }
+#pragma unroll
+    for (int r = 1; r < R; ++r) v[r] += v[r - 1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) tile[k * R + r][hh] = v[r];
+    off[k][hh] = v[R - 1];
+    __syncthreads();
+    if (tid < kCumsumHeads) {  // exclusive prefix of the run totals, one head per thread
+        float run = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < kCumsumRuns; ++kk) {
+            const float t = off[kk][tid];
+            off[kk][tid] = run;
+            run += t;
+        }
     }
     __syncthreads();
-    const int w = wave_id(), l = lane_id();
-    const int per = Q >> 6;  // tokens per lane: 1, 2 or 4
-    for (int hh = w; hh < kCumsumHeads; hh += 4) {
-        const int h = h0 + hh;
-        if (h >= H) break;  // uniform across the wavefront
-        float v[4];
-        float run = 0.0f;
-        for (int k = 0; k < per; ++k) {
-            run += tile[l * per + k][hh];
-            v[k] = run;
-        }
-        float incl = run;
+    const int tt = tid & 63, hq = tid >> 6;
+    for (int hl = hq; hl < kCumsumHeads; hl += 16) {
+        const int hg = h0 + hl;
+        if (hg >= H) break;  // uniform across the wavefront
+        float *dst = out + ((size_t)b * H + hg) * ((size_t)nC * Q) + t0;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float o = __shfl_up(incl, off);
-            if (l >= off) incl += o;
+        for (int tb = 0; tb < Q; tb += 64) {
+            const int t = tb + tt;
+            dst[t] = tile[t][hl] + off[t / R][hl];
         }
-        const float excl = incl - run;
-        float *dst = out + ((size_t)b * H + h) * ((size_t)nC * Q) + t0 + l * per;
-        for (int k = 0; k < per; ++k) dst[k] = excl + v[k];
     }
 }
 
 hipError_t launch_chunk_cumsum(const void *dt, const float *A, int batch, int seqlen, int nheads,
                                int chunk, bool bf16, float *dA_cumsum, hipStream_t stream) {
     const int nC = (seqlen + chunk - 1) / chunk;
-    dim3 grid(nC, batch, (nheads + kCumsumHeads - 1) / kCumsumHeads);
-    if (bf16)
-        chunk_cumsum_kernel<bf16_t><<<grid, 256, 0, stream>>>(
-            static_cast<const bf16_t *>(dt), A, seqlen, nheads, chunk, nC, dA_cumsum);
-    else
-        chunk_cumsum_kernel<float><<<grid, 256, 0, stream>>>(
-            static_cast<const float *>(dt), A, seqlen, nheads, chunk, nC, dA_cumsum);
+    const dim3 grid(nC, batch, (nheads + kCumsumHeads - 1) / kCumsumHeads);
+#define SSD_CUMSUM(T, Q)                                                                       \
+    chunk_cumsum_kernel<T, Q><<<grid, 1024, 0, stream>>>(static_cast<const T *>(dt), A, seqlen, \
+                                                        nheads, nC, dA_cumsum)
+    if (bf16) {
+        if (chunk == 64) SSD_CUMSUM(bf16_t, 64);
+        else if (chunk == 128) SSD_CUMSUM(bf16_t, 128);
+        else if (chunk == 256) SSD_CUMSUM(bf16_t, 256);
+        else return hipErrorInvalidValue;
+    } else {
+        if (chunk == 64) SSD_CUMSUM(float, 64);
+        else if (chunk == 128) SSD_CUMSUM(float, 128);
+        else if (chunk == 256) SSD_CUMSUM(float, 256);
+        else return hipErrorInvalidValue;
+    }
+#undef SSD_CUMSUM
     return hipGetLastError();
 }
 

@@ -3,161 +3,173 @@
 // factor through which the off-diagonal blocks act):
 //   S_c[p][n] = sum_{j in c} w_j * x_j[p] * B_j[n],  w_j = exp(s_end - s_j) * dt_j.
 //
-// One workgroup (4 wavefronts) per (chunk, head, batch). S_c = X^T (w o B) is a
-// [P x Q] x [Q x N] product whose contraction index is the token, which is the
-// slow (row) index of both x and B in memory, so both operands are staged
-// through LDS transposed: XT[p][j] and BT[n][j] (w folded into B in fp32
-// before rounding to the operand type). Tokens go through LDS 64 at a time:
-// global loads are 16-byte row segments; each thread packs two tokens into
-// 4-byte LDS writes. The MFMA phase reads 16-byte fragments (8 consecutive
-// tokens) for both operands. Wavefront w owns output column tiles w, w+4, ...
-// over all four 16-row tiles of P = 64.
+// One workgroup (8 wavefronts) per (chunk, head, batch). S_c = X^T (w o B) is a
+// [P x Q] x [Q x N] product whose contraction index, the token, is the row of
+// both x and B in memory. Both are kept in LDS in their natural row layout:
+// every global load is a piece of 8 elements of a token row (16 bytes for
+// bf16) with consecutive lanes on consecutive pieces, and every LDS write is
+// that same piece (w folded
+// into B in fp32 before rounding to the operand type). The MFMA operands, which
+// need 4 consecutive tokens per lane, come from the transposing LDS read
+// (lds_colfrag). All global loads of the chunk are issued at the start; LDS
+// holds half of the chunk at a time (two phases; four for the largest float
+// tiles). Wavefront w owns the output
+// tiles of P-rows 16*(w%4) .. +15 and N-column tiles w/4, w/4+2, ...
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 
-template <typename E>
-__device__ __forceinline__ void lds_store2(E *dst, float a, float b);
-template <>
-__device__ __forceinline__ void lds_store2<__bf16>(__bf16 *dst, float a, float b) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    bf16x2 v;
-    v[0] = static_cast<__bf16>(a);
-    v[1] = static_cast<__bf16>(b);
-    *reinterpret_cast<bf16x2 *>(dst) = v;
-}
-template <>
-__device__ __forceinline__ void lds_store2<float>(float *dst, float a, float b) {
-    *reinterpret_cast<float2 *>(dst) = make_float2(a, b);
-}
-
-template <typename T, int N>
-__global__ __launch_bounds__(256) void chunk_state_kernel(
+template <typename T, int N, int Q>
+__global__ __launch_bounds__(512) void chunk_state_kernel(
     const T *__restrict__ x, const T *__restrict__ B, const T *__restrict__ dt,
-    const float *__restrict__ dA_cumsum, int L, int H, int G, int Q, int nC,
+    const float *__restrict__ dA_cumsum, int L, int H, int G, int nC,
     float *__restrict__ states) {
     using E = typename LdsT<T>::type;
-    constexpr int P = 64, JB = 64, LD = JB + 8;
-    constexpr int NT = N / 16;              // 16-wide column tiles of S
-    constexpr int NTW = (NT + 3) / 4;       // tiles per wavefront
-    __shared__ __attribute__((aligned(16))) E xt[P * LD];
-    __shared__ __attribute__((aligned(16))) E bt[N * LD];
-    __shared__ float wj[256];
+    constexpr int P = 64, NTHR = 512;
+    constexpr int LDX = colfrag_stride(P, sizeof(E));
+    constexpr int LDB = colfrag_stride(N, sizeof(E));
+    // LDS holds Q / NPH tokens at a time: two phases, or four if that is too big
+    constexpr int NPH = (Q / 2) * (LDX + LDB) * (int)sizeof(E) > 96 * 1024 ? 4 : 2;
+    constexpr int QH = Q / NPH;
+    constexpr int SEG = 8;                            // elements per piece (one Raw8)
+    constexpr int XPR = P / SEG, BPR = N / SEG;       // pieces per token row
+    constexpr int XP = Q * XPR / NTHR;                // x pieces per thread (whole chunk)
+    constexpr int BP = (Q * BPR + NTHR - 1) / NTHR;   // B pieces per thread
+    constexpr int NTW = (N / 16 + 1) / 2;             // N-column tiles per wavefront
+    __shared__ __attribute__((aligned(16))) E xs[QH * LDX];
+    __shared__ __attribute__((aligned(16))) E bs[QH * LDB];
+    __shared__ float wj[Q];
 
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int g = h / (H / G);
     const int t0 = c * Q, len = min(Q, L - t0);
+    const int tid = threadIdx.x;
+    const T *xh = x + (((size_t)b * L + t0) * H + h) * P;
+    const T *bg = B + (((size_t)b * L + t0) * G + g) * N;
+    const size_t xstride = (size_t)H * P, bstride = (size_t)G * N;
+
+    // ---- all global loads of the chunk, issued up front
+    Raw8<T> xv[XP], bv[BP];
+#pragma unroll
+    for (int k = 0; k < XP; ++k) {
+        const int idx = tid + k * NTHR, j = idx / XPR, q = idx % XPR;
+        if (j < len) xv[k].load(xh + (size_t)j * xstride + q * SEG);
+        else xv[k].zero();
+    }
+#pragma unroll
+    for (int k = 0; k < BP; ++k) {
+        const int idx = tid + k * NTHR, j = idx / BPR, q = idx % BPR;
+        if (idx < Q * BPR && j < len) bv[k].load(bg + (size_t)j * bstride + q * SEG);
+        else bv[k].zero();
+    }
     const float *s = dA_cumsum + ((size_t)b * H + h) * (size_t)nC * Q + (size_t)c * Q;
     const float s_end = s[len - 1];
-    for (int j = threadIdx.x; j < Q; j += 256) {
+    for (int j = tid; j < Q; j += NTHR) {
         float wv = 0.0f;
         if (j < len)
-            wv = exp2f((s_end - s[j]) * kLog2e) * to_f32(dt[((size_t)b * L + t0 + j) * H + h]);
+            wv = __builtin_amdgcn_exp2f((s_end - s[j]) * kLog2e) * to_f32(dt[((size_t)b * L + t0 + j) * H + h]);
         wj[j] = wv;
     }
 
-    const int w = wave_id(), l = lane_id(), g4 = l >> 4, r16 = l & 15;
-    floatx4 acc[4][NTW];
+    const int w = wave_id(), l = lane_id(), g4 = l >> 4;
+    const int pt = w % 4;
+    floatx4 acc[NTW];
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-        for (int i = 0; i < NTW; ++i) acc[pt][i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < NTW; ++i) acc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const T *xh = x + (((size_t)b * L + t0) * H + h) * P;     // token stride H*P
-    const T *bg = B + (((size_t)b * L + t0) * G + g) * N;     // token stride G*N
-    const size_t xs = (size_t)H * P, bs = (size_t)G * N;
-
-    for (int jb = 0; jb < len; jb += JB) {
-        __syncthreads();  // previous block consumed (first pass: wj written)
-        {   // x block -> XT[p][j]; thread = (8-wide p slice, token pair)
-            const int pb = threadIdx.x >> 5, jp = threadIdx.x & 31;
-            const int j0 = jb + 2 * jp;
-            float v0[8], v1[8];
-            if (j0 < len) load8(xh + (size_t)j0 * xs + pb * 8, v0);
-            else for (int e = 0; e < 8; ++e) v0[e] = 0.0f;
-            if (j0 + 1 < len) load8(xh + (size_t)(j0 + 1) * xs + pb * 8, v1);
-            else for (int e = 0; e < 8; ++e) v1[e] = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) lds_store2<E>(xt + (pb * 8 + e) * LD + 2 * jp, v0[e], v1[e]);
+    for (int ph = 0; ph < NPH; ++ph) {
+        __syncthreads();  // wj ready (phase 0) / previous phase consumed (phase 1)
+#pragma unroll
+        for (int k = 0; k < XP; ++k) {
+            const int idx = tid + k * NTHR, j = idx / XPR, q = idx % XPR;
+            if (j / QH == ph) {
+                E *d = xs + (j - ph * QH) * LDX + q * SEG;
+                Frag<T> f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f.set(e, xv[k].get(e));
+                store_frag8(d, f);
+            }
         }
-        // B block scaled by w -> BT[n][j]
-        for (int idx = threadIdx.x; idx < 32 * (N / 8); idx += 256) {
-            const int nb = idx >> 5, jp = idx & 31;
-            const int j0 = jb + 2 * jp;
-            float v0[8], v1[8];
-            if (j0 < len) {
-                load8(bg + (size_t)j0 * bs + nb * 8, v0);
-                const float w0 = wj[j0];
-                for (int e = 0; e < 8; ++e) v0[e] *= w0;
-            } else {
-                for (int e = 0; e < 8; ++e) v0[e] = 0.0f;
-            }
-            if (j0 + 1 < len) {
-                load8(bg + (size_t)(j0 + 1) * bs + nb * 8, v1);
-                const float w1 = wj[j0 + 1];
-                for (int e = 0; e < 8; ++e) v1[e] *= w1;
-            } else {
-                for (int e = 0; e < 8; ++e) v1[e] = 0.0f;
-            }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) lds_store2<E>(bt + (nb * 8 + e) * LD + 2 * jp, v0[e], v1[e]);
+        for (int k = 0; k < BP; ++k) {
+            const int idx = tid + k * NTHR, j = idx / BPR, q = idx % BPR;
+            if (idx < Q * BPR && j / QH == ph) {
+                const float wv = wj[j];
+                E *d = bs + (j - ph * QH) * LDB + q * SEG;
+                Frag<T> f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f.set(e, bv[k].get(e) * wv);
+                store_frag8(d, f);
+            }
         }
         __syncthreads();
-        const int kend = min(JB, len - jb);
-        for (int kk = 0; kk < kend; kk += 32) {
-            Frag<T> a[4];
-#pragma unroll
-            for (int pt = 0; pt < 4; ++pt) lds_frag8(a[pt], xt + (pt * 16 + r16) * LD + kk + 8 * g4);
+        const int kend = min(QH, len - ph * QH);  // tokens of this phase (<= 0: none)
+        for (int kb = 0; kb < kend; kb += 32) {
+            const int jb = kb + 4 * g4;
+            Frag<T> xf;
+            lds_colfrag(xf, xs, LDX, jb, jb + 16, pt * 16);
 #pragma unroll
             for (int i = 0; i < NTW; ++i) {
-                const int nt = w + 4 * i;
-                if (nt < NT) {
+                const int nt = w / 4 + 2 * i;
+                if (nt < N / 16) {
                     Frag<T> bf;
-                    lds_frag8(bf, bt + (nt * 16 + r16) * LD + kk + 8 * g4);
-#pragma unroll
-                    for (int pt = 0; pt < 4; ++pt) mma(acc[pt][i], a[pt], bf);
+                    lds_colfrag(bf, bs, LDB, jb, jb + 16, nt * 16);
+                    mma(acc[i], xf, bf);
                 }
             }
         }
     }
 
     float *dst = states + (((size_t)b * nC + c) * H + h) * (size_t)P * N;
+    const int cc = l & 15;
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
-        const int nt = w + 4 * i;
-        if (nt < NT) {
+        const int nt = w / 4 + 2 * i;
+        if (nt < N / 16) {
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    dst[(size_t)(pt * 16 + 4 * g4 + r) * N + nt * 16 + r16] = acc[pt][i][r];
+            for (int r = 0; r < 4; ++r)
+                dst[(size_t)(pt * 16 + 4 * g4 + r) * N + nt * 16 + cc] = acc[i][r];
         }
     }
 }
 
-template <typename T, int N>
+template <typename T, int N, int Q>
 static void launch_cs(const void *x, const void *B, const void *dt, const float *dA, int batch,
-                      int L, int H, int G, int Q, float *states, hipStream_t stream) {
+                      int L, int H, int G, float *states, hipStream_t stream) {
     const int nC = (L + Q - 1) / Q;
-    dim3 grid(nC, H, batch);
-    chunk_state_kernel<T, N><<<grid, 256, 0, stream>>>(
+    const dim3 grid(nC, H, batch);
+    chunk_state_kernel<T, N, Q><<<grid, 512, 0, stream>>>(
         static_cast<const T *>(x), static_cast<const T *>(B), static_cast<const T *>(dt), dA, L, H,
-        G, Q, nC, states);
+        G, nC, states);
+}
+
+template <typename T, int N>
+static bool cs_q(int Q, const void *x, const void *B, const void *dt, const float *dA, int batch,
+                 int L, int H, int G, float *states, hipStream_t s) {
+    switch (Q) {
+        case 64: launch_cs<T, N, 64>(x, B, dt, dA, batch, L, H, G, states, s); return true;
+        case 128: launch_cs<T, N, 128>(x, B, dt, dA, batch, L, H, G, states, s); return true;
+        case 256: launch_cs<T, N, 256>(x, B, dt, dA, batch, L, H, G, states, s); return true;
+        default: return false;
+    }
 }
 
 template <typename T>
 static hipError_t dispatch_cs(const void *x, const void *B, const void *dt, const float *dA,
                               int batch, int L, int H, int G, int N, int Q, float *states,
-                              hipStream_t stream) {
+                              hipStream_t s) {
+    bool ok = false;
     switch (N) {
-        case 16: launch_cs<T, 16>(x, B, dt, dA, batch, L, H, G, Q, states, stream); break;
-        case 32: launch_cs<T, 32>(x, B, dt, dA, batch, L, H, G, Q, states, stream); break;
-        case 64: launch_cs<T, 64>(x, B, dt, dA, batch, L, H, G, Q, states, stream); break;
-        case 128: launch_cs<T, 128>(x, B, dt, dA, batch, L, H, G, Q, states, stream); break;
-        case 256: launch_cs<T, 256>(x, B, dt, dA, batch, L, H, G, Q, states, stream); break;
-        default: return hipErrorInvalidValue;
+        case 16: ok = cs_q<T, 16>(Q, x, B, dt, dA, batch, L, H, G, states, s); break;
+        case 32: ok = cs_q<T, 32>(Q, x, B, dt, dA, batch, L, H, G, states, s); break;
+        case 64: ok = cs_q<T, 64>(Q, x, B, dt, dA, batch, L, H, G, states, s); break;
+        case 128: ok = cs_q<T, 128>(Q, x, B, dt, dA, batch, L, H, G, states, s); break;
+        case 256: ok = cs_q<T, 256>(Q, x, B, dt, dA, batch, L, H, G, states, s); break;
+        default: break;
     }
+    if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

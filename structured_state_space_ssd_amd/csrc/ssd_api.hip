@@ -19,18 +19,22 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool valid_dtype(int d) { return d == SSD_F32 || d == SSD_BF16; }
 
 struct Workspace {
-    size_t cumsum_off, states_off, init_off, total;
+    size_t cumsum_off, states_off, init_off, cb_off, total;
 };
 
-Workspace layout(int batch, int seqlen, int nheads, int headdim, int dstate, int chunk) {
+Workspace layout(int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate, int chunk,
+                 bool bf16) {
     const size_t nC = (static_cast<size_t>(seqlen) + chunk - 1) / chunk;
     const size_t cumsum = static_cast<size_t>(batch) * nheads * nC * chunk * sizeof(float);
-    const size_t st = static_cast<size_t>(batch) * nC * nheads * headdim * dstate * sizeof(float);
+    const size_t elems = static_cast<size_t>(batch) * nC * nheads * headdim * dstate;
+    const size_t st = elems * sizeof(float);
+    const size_t ci = elems * (bf16 ? 2 : 4);
     Workspace w;
     w.cumsum_off = 0;
     w.states_off = align_up(cumsum);
     w.init_off = w.states_off + align_up(st);
-    w.total = w.init_off + align_up(st);
+    w.cb_off = w.init_off + align_up(ci);
+    w.total = w.cb_off + align_up(ssd::chunk_cb_bytes(batch, seqlen, ngroups, chunk, bf16));
     return w;
 }
 
@@ -62,10 +66,30 @@ const char *ssd_strerror(int status) {
     }
 }
 
-size_t ssd_forward_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
-                                  int chunk) {
-    if (batch < 1 || seqlen < 1 || nheads < 1 || headdim < 1 || dstate < 1 || chunk < 1) return 0;
-    return layout(batch, seqlen, nheads, headdim, dstate, chunk).total;
+size_t ssd_forward_workspace_size(int batch, int seqlen, int nheads, int headdim, int ngroups,
+                                  int dstate, int chunk, int dtype) {
+    if (batch < 1 || seqlen < 1 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1 ||
+        !supported_chunk(chunk) || !valid_dtype(dtype))
+        return 0;
+    return layout(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, dtype == SSD_BF16).total;
+}
+
+size_t ssd_chunk_cb_size(int batch, int seqlen, int ngroups, int chunk, int dtype) {
+    if (batch < 1 || seqlen < 1 || ngroups < 1 || !supported_chunk(chunk) || !valid_dtype(dtype))
+        return 0;
+    return ssd::chunk_cb_bytes(batch, seqlen, ngroups, chunk, dtype == SSD_BF16);
+}
+
+int ssd_chunk_cb(const void *B, const void *C, int batch, int seqlen, int ngroups, int dstate,
+                 int chunk, int dtype, void *cb, void *stream) {
+    if (!B || !C || !cb) return SSD_ERR_NULL;
+    if (batch < 1 || seqlen < 1 || ngroups < 1 || dstate < 1) return SSD_ERR_SHAPE;
+    if (!supported_dstate(dstate) || !supported_chunk(chunk) || !valid_dtype(dtype))
+        return SSD_ERR_UNSUPPORTED;
+    if (!aligned16(B) || !aligned16(C) || (reinterpret_cast<uintptr_t>(cb) % 32) != 0)
+        return SSD_ERR_UNSUPPORTED;
+    return status_of(ssd::launch_chunk_cb(B, C, batch, seqlen, ngroups, dstate, chunk,
+                                          dtype == SSD_BF16, cb, static_cast<hipStream_t>(stream)));
 }
 
 int ssd_chunk_cumsum(const void *dt, const float *A, int batch, int seqlen, int nheads, int chunk,
@@ -93,38 +117,40 @@ int ssd_chunk_state(const void *x, const void *B, const void *dt, const float *d
 
 int ssd_state_passing(const float *states, const float *dA_cumsum, const float *init_state,
                       int batch, int seqlen, int nheads, int headdim, int dstate, int chunk,
-                      float *chunk_init, float *final_state, void *stream) {
+                      int dtype, void *chunk_init, float *final_state, void *stream) {
     if (!states || !dA_cumsum || !chunk_init) return SSD_ERR_NULL;
     int rc = check_dims(batch, seqlen, nheads, headdim, 1, dstate);
     if (rc != SSD_OK) return rc;
-    if (!supported_chunk(chunk)) return SSD_ERR_UNSUPPORTED;
+    if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
     if (!aligned16(states) || !aligned16(chunk_init) || (init_state && !aligned16(init_state)) ||
         (final_state && !aligned16(final_state)))
         return SSD_ERR_UNSUPPORTED;
     return status_of(ssd::launch_state_passing(states, dA_cumsum, init_state, batch, seqlen, nheads,
-                                               dstate, chunk, chunk_init, final_state,
-                                               static_cast<hipStream_t>(stream)));
+                                               dstate, chunk, dtype == SSD_BF16, chunk_init,
+                                               final_state, static_cast<hipStream_t>(stream)));
 }
 
-int ssd_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *B,
-                   const void *C, const float *D, const float *chunk_init, int batch, int seqlen,
+int ssd_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *C,
+                   const void *cb, const float *D, const void *chunk_init, int batch, int seqlen,
                    int nheads, int headdim, int ngroups, int dstate, int chunk, int dtype, void *y,
                    void *stream) {
-    if (!x || !dt || !dA_cumsum || !B || !C || !chunk_init || !y) return SSD_ERR_NULL;
+    if (!x || !dt || !dA_cumsum || !C || !cb || !chunk_init || !y) return SSD_ERR_NULL;
     int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
     if (rc != SSD_OK) return rc;
     if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
-    if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(chunk_init) || !aligned16(y))
+    if (!aligned16(x) || !aligned16(C) || !aligned16(chunk_init) || !aligned16(y) ||
+        !aligned16(dA_cumsum) || (reinterpret_cast<uintptr_t>(cb) % 32) != 0)
         return SSD_ERR_UNSUPPORTED;
-    return status_of(ssd::launch_chunk_scan(x, dt, dA_cumsum, B, C, D, chunk_init, batch, seqlen,
+    return status_of(ssd::launch_chunk_scan(x, dt, dA_cumsum, C, cb, D, chunk_init, batch, seqlen,
                                             nheads, ngroups, dstate, chunk, dtype == SSD_BF16, y,
                                             static_cast<hipStream_t>(stream)));
 }
 
-int ssd_forward(const void *x, const void *dt, const float *A, const void *B, const void *C,
-                const float *D, int batch, int seqlen, int nheads, int headdim, int ngroups,
-                int dstate, int chunk, int dtype, const float *init_state, void *y,
-                float *final_state, void *workspace, size_t workspace_bytes, void *stream) {
+int ssd_forward_timed(const void *x, const void *dt, const float *A, const void *B,
+                      const void *C, const float *D, int batch, int seqlen, int nheads,
+                      int headdim, int ngroups, int dstate, int chunk, int dtype,
+                      const float *init_state, void *y, float *final_state, void *workspace,
+                      size_t workspace_bytes, void *stream, void *const *events) {
     if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
     int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
     if (rc != SSD_OK) return rc;
@@ -132,28 +158,52 @@ int ssd_forward(const void *x, const void *dt, const float *A, const void *B, co
     if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) ||
         (init_state && !aligned16(init_state)) || (final_state && !aligned16(final_state)))
         return SSD_ERR_UNSUPPORTED;
-    const Workspace ws = layout(batch, seqlen, nheads, headdim, dstate, chunk);
+    const Workspace ws = layout(batch, seqlen, nheads, headdim, ngroups, dstate, chunk,
+                                dtype == SSD_BF16);
     if (!workspace || workspace_bytes < ws.total) return SSD_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return SSD_ERR_WORKSPACE;
 
     char *base = static_cast<char *>(workspace);
     float *cumsum = reinterpret_cast<float *>(base + ws.cumsum_off);
     float *states = reinterpret_cast<float *>(base + ws.states_off);
-    float *cinit = reinterpret_cast<float *>(base + ws.init_off);
+    void *cinit = base + ws.init_off;
+    void *cb = base + ws.cb_off;
     const bool bf16 = dtype == SSD_BF16;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
-    hipError_t e = ssd::launch_chunk_cumsum(dt, A, batch, seqlen, nheads, chunk, bf16, cumsum, s);
+    auto mark = [&](int k) -> hipError_t {
+        return events ? hipEventRecord(static_cast<hipEvent_t>(events[k]), s) : hipSuccess;
+    };
+
+    hipError_t e = mark(0);
+    if (e == hipSuccess)
+        e = ssd::launch_chunk_cumsum(dt, A, batch, seqlen, nheads, chunk, bf16, cumsum, s);
+    if (e == hipSuccess) e = mark(1);
     if (e == hipSuccess)
         e = ssd::launch_chunk_state(x, B, dt, cumsum, batch, seqlen, nheads, ngroups, dstate, chunk,
                                     bf16, states, s);
+    if (e == hipSuccess) e = mark(2);
     if (e == hipSuccess)
         e = ssd::launch_state_passing(states, cumsum, init_state, batch, seqlen, nheads, dstate,
-                                      chunk, cinit, final_state, s);
+                                      chunk, bf16, cinit, final_state, s);
+    if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess)
-        e = ssd::launch_chunk_scan(x, dt, cumsum, B, C, D, cinit, batch, seqlen, nheads, ngroups,
+        e = ssd::launch_chunk_cb(B, C, batch, seqlen, ngroups, dstate, chunk, bf16, cb, s);
+    if (e == hipSuccess) e = mark(4);
+    if (e == hipSuccess)
+        e = ssd::launch_chunk_scan(x, dt, cumsum, C, cb, D, cinit, batch, seqlen, nheads, ngroups,
                                    dstate, chunk, bf16, y, s);
+    if (e == hipSuccess) e = mark(5);
     return status_of(e);
+}
+
+int ssd_forward(const void *x, const void *dt, const float *A, const void *B, const void *C,
+                const float *D, int batch, int seqlen, int nheads, int headdim, int ngroups,
+                int dstate, int chunk, int dtype, const float *init_state, void *y,
+                float *final_state, void *workspace, size_t workspace_bytes, void *stream) {
+    return ssd_forward_timed(x, dt, A, B, C, D, batch, seqlen, nheads, headdim, ngroups, dstate,
+                             chunk, dtype, init_state, y, final_state, workspace, workspace_bytes,
+                             stream, nullptr);
 }
 
 int ssd_step(float *state, const void *x, const void *dt, const float *A, const void *B,

@@ -101,6 +101,25 @@ __device__ __forceinline__ void lds_frag4x2(Frag<float> &f, const float *p0, con
     f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
 }
 
+// Store / load one lane's 8 fragment elements to / from memory (16 bytes for
+// bf16, 32 bytes for float; the address must be aligned to that size).
+__device__ __forceinline__ void store_frag8(__bf16 *p, const Frag<bf16_t> &f) {
+    *reinterpret_cast<bf16x8 *>(p) = f.v;
+}
+__device__ __forceinline__ void store_frag8(float *p, const Frag<float> &f) {
+    reinterpret_cast<floatx4 *>(p)[0] = floatx4{f.v[0], f.v[1], f.v[2], f.v[3]};
+    reinterpret_cast<floatx4 *>(p)[1] = floatx4{f.v[4], f.v[5], f.v[6], f.v[7]};
+}
+__device__ __forceinline__ void load_frag8(Frag<bf16_t> &f, const __bf16 *p) {
+    f.v = *reinterpret_cast<const bf16x8 *>(p);
+}
+__device__ __forceinline__ void load_frag8(Frag<float> &f, const float *p) {
+    const floatx4 a = reinterpret_cast<const floatx4 *>(p)[0];
+    const floatx4 b = reinterpret_cast<const floatx4 *>(p)[1];
+    f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
+    f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
+}
+
 // MFMA operand type held in LDS for input dtype T.
 template <typename T> struct LdsT;
 template <> struct LdsT<bf16_t> { using type = __bf16; };
@@ -126,7 +145,82 @@ __device__ __forceinline__ void load8(const float *p, float out[8]) {
     out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
+// Eight input elements as loaded from memory, still packed (bf16: one 16-byte
+// load, 4 registers; float: two 16-byte loads, 8 registers).
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+    uint4 u;
+    __device__ __forceinline__ void load(const bf16_t *p) { u = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void zero() { u = make_uint4(0, 0, 0, 0); }
+    __device__ __forceinline__ float get(int e) const {
+        const uint32_t w = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+template <> struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = reinterpret_cast<const float4 *>(p)[0];
+        b = reinterpret_cast<const float4 *>(p)[1];
+    }
+    __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ __forceinline__ float get(int e) const {
+        const float4 &q = e < 4 ? a : b;
+        const int k = e & 3;
+        return k == 0 ? q.x : k == 1 ? q.y : k == 2 ? q.z : q.w;
+    }
+};
+
+// Copy 16 bytes.
+__device__ __forceinline__ void copy16(void *dst, const void *src) {
+    *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+}
+
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ---- operand fragments whose contraction index is the ROW of an LDS matrix
+//
+// For a row-major LDS matrix M (row stride `stride` elements), lane 16*g + c
+// receives column cb + c at rows r1 + 0..3 (elements 0..3) and r2 + 0..3
+// (elements 4..7), where r1 and r2 are the values of the lane's own group g.
+// bf16 uses the gfx950 transposing LDS read ds_read_b64_tr_b16: within each
+// 16-lane group, lane j's element e comes from element j%4 of the 8 bytes
+// read by lane 4e + j/4, so lane s of a group reads row r + s/4 at columns
+// cb + 4*(s%4) .. +3. float reads the eight values one by one.
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+__device__ __forceinline__ void lds_colfrag(Frag<bf16_t> &f, const __bf16 *m, int stride, int r1,
+                                            int r2, int cb) {
+    const int s = lane_id() & 15;
+    const int off = (s >> 2) * stride + cb + 4 * (s & 3);
+    const shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_shortx4 *)(m + r1 * stride + off));
+    const shortx4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_shortx4 *)(m + r2 * stride + off));
+    const bf16x4 ab = __builtin_bit_cast(bf16x4, a);
+    const bf16x4 bb = __builtin_bit_cast(bf16x4, b);
+    f.v = bf16x8{ab[0], ab[1], ab[2], ab[3], bb[0], bb[1], bb[2], bb[3]};
+}
+__device__ __forceinline__ void lds_colfrag(Frag<float> &f, const float *m, int stride, int r1,
+                                            int r2, int cb) {
+    const int c = lane_id() & 15;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f.v[e] = m[(r1 + e) * stride + cb + c];
+        f.v[4 + e] = m[(r2 + e) * stride + cb + c];
+    }
+}
+
+// LDS row stride (in elements of `bytes` each) for a matrix with `cols`
+// columns read through lds_colfrag: the stride in 4-byte words is the
+// smallest value >= the row length that is 8 mod 16, which spreads the 8
+// rows one half-wavefront reads over distinct banks.
+__host__ __device__ constexpr int colfrag_stride(int cols, int bytes) {
+    int w = (cols * bytes + 3) / 4;
+    while (w % 16 != 8) ++w;
+    return w * 4 / bytes;
+}
 
 }  // namespace ssd

@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 
 namespace ssd {
 
@@ -14,12 +15,20 @@ hipError_t launch_chunk_state(const void *x, const void *B, const void *dt, cons
                               int batch, int seqlen, int nheads, int ngroups, int dstate, int chunk,
                               bool bf16, float *states, hipStream_t stream);
 
+// chunk_init is written in the MFMA operand type of the forward's dtype
+// (bf16 when bf16 is true, else float32).
 hipError_t launch_state_passing(const float *states, const float *dA_cumsum, const float *init,
                                 int batch, int seqlen, int nheads, int dstate, int chunk,
-                                float *chunk_init, float *final_state, hipStream_t stream);
+                                bool bf16, void *chunk_init, float *final_state,
+                                hipStream_t stream);
 
-hipError_t launch_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *B,
-                             const void *C, const float *D, const float *chunk_init, int batch,
+size_t chunk_cb_bytes(int batch, int seqlen, int ngroups, int chunk, bool bf16);
+
+hipError_t launch_chunk_cb(const void *B, const void *C, int batch, int seqlen, int ngroups,
+                           int dstate, int chunk, bool bf16, void *cb, hipStream_t stream);
+
+hipError_t launch_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *C,
+                             const void *cb, const float *D, const void *chunk_init, int batch,
                              int seqlen, int nheads, int ngroups, int dstate, int chunk, bool bf16,
                              void *y, hipStream_t stream);
 

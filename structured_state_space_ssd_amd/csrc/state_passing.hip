@@ -7,16 +7,29 @@
 // Sequential over chunks, parallel over (batch, head, P*N/4): each thread owns
 // one float4 of a head's P x N state. The chunk loop is unrolled by 8 so that
 // the loads of 8 chunks' S are in flight before the dependent updates run; a
-// wavefront reads and writes 1 KiB contiguous per chunk. Pure HBM streaming.
+// wavefront reads 1 KiB contiguous per chunk. chunk_init is written in the
+// operand type chunk_scan multiplies it in (bf16 for bf16 inputs: the same
+// rounding chunk_scan would apply), which halves its bytes. Pure HBM streaming.
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 
+__device__ __forceinline__ void store4(float *p, const floatx4 &v) {
+    *reinterpret_cast<floatx4 *>(p) = v;
+}
+__device__ __forceinline__ void store4(__bf16 *p, const floatx4 &v) {
+    *reinterpret_cast<bf16x4 *>(p) = bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]),
+                                            static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
+}
+
+// OutT: element type of chunk_init (float, or __bf16 = the bf16 MFMA operand
+// type chunk_scan reads; the recurrence itself always runs in float32).
+template <typename OutT>
 __global__ __launch_bounds__(256) void state_passing_kernel(
     const float *__restrict__ states, const float *__restrict__ dA_cumsum,
     const float *__restrict__ init, int L, int H, int PN, int Q, int nC,
-    float *__restrict__ chunk_init, float *__restrict__ final_state) {
+    OutT *__restrict__ chunk_init, float *__restrict__ final_state) {
     const int h = blockIdx.y, b = blockIdx.z;
     const int e4 = blockIdx.x * 256 + threadIdx.x;
     if (e4 * 4 >= PN) return;
@@ -26,7 +39,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
     if (init) hc = reinterpret_cast<const floatx4 *>(init + head * PN)[e4];
     const size_t cstride = (size_t)H * PN;
     const float *sp = states + ((size_t)b * nC * H + h) * PN + (size_t)e4 * 4;
-    float *cp = chunk_init + ((size_t)b * nC * H + h) * PN + (size_t)e4 * 4;
+    OutT *cp = chunk_init + ((size_t)b * nC * H + h) * PN + (size_t)e4 * 4;
     constexpr int U = 8;
     for (int c0 = 0; c0 < nC; c0 += U) {
         floatx4 sv[U];
@@ -44,7 +57,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
         for (int u = 0; u < U; ++u) {
             const int c = c0 + u;
             if (c < nC) {
-                *reinterpret_cast<floatx4 *>(cp + c * cstride) = hc;
+                store4(cp + c * cstride, hc);
                 hc = dec[u] * hc + sv[u];
             }
         }
@@ -54,12 +67,19 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
 
 hipError_t launch_state_passing(const float *states, const float *dA_cumsum, const float *init,
                                 int batch, int seqlen, int nheads, int dstate, int chunk,
-                                float *chunk_init, float *final_state, hipStream_t stream) {
+                                bool bf16, void *chunk_init, float *final_state,
+                                hipStream_t stream) {
     const int nC = (seqlen + chunk - 1) / chunk;
     const int PN = 64 * dstate;
-    dim3 grid((PN / 4 + 255) / 256, nheads, batch);
-    state_passing_kernel<<<grid, 256, 0, stream>>>(states, dA_cumsum, init, seqlen, nheads, PN,
-                                                   chunk, nC, chunk_init, final_state);
+    const dim3 grid((PN / 4 + 255) / 256, nheads, batch);
+    if (bf16)
+        state_passing_kernel<__bf16><<<grid, 256, 0, stream>>>(
+            states, dA_cumsum, init, seqlen, nheads, PN, chunk, nC,
+            static_cast<__bf16 *>(chunk_init), final_state);
+    else
+        state_passing_kernel<float><<<grid, 256, 0, stream>>>(
+            states, dA_cumsum, init, seqlen, nheads, PN, chunk, nC,
+            static_cast<float *>(chunk_init), final_state);
     return hipGetLastError();
 }
 

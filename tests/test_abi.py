@@ -31,7 +31,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("ssd_forward", "ssd_step", "ssd_forward_workspace_size", "ssd_strerror",
-                     "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan"):
+                     "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_cb",
+                     "ssd_chunk_scan", "ssd_forward_timed", "ssd_chunk_cb_size"):
         assert required in names
 
 
@@ -48,23 +49,34 @@ def test_strerror(lib):
     assert lib.ssd_strerror(42) == b"unknown status"
 
 
-def _ws_expected(Bt, L, H, P, N, Q):
+def _cb_expected(Bt, L, G, Q, dtype):
+    nC = -(-L // Q)
+    nt = Q // 16
+    return Bt * nC * G * (nt // 2) * (nt // 2 + 1) * 64 * 8 * (2 if dtype == 1 else 4)
+
+
+def _ws_expected(Bt, L, H, P, G, N, Q, dtype):
     al = lambda v: (v + 255) // 256 * 256
     nC = -(-L // Q)
     cs = Bt * H * nC * Q * 4
     st = Bt * nC * H * P * N * 4
-    return al(cs) + 2 * al(st)
+    ci = Bt * nC * H * P * N * (2 if dtype == 1 else 4)
+    return al(cs) + al(st) + al(ci) + al(_cb_expected(Bt, L, G, Q, dtype))
 
 
-@pytest.mark.parametrize("dims", [(8, 2048, 80, 64, 64, 256), (1, 65536, 80, 64, 128, 256),
-                                  (1, 1, 1, 64, 16, 64), (3, 77, 5, 64, 32, 128)])
+@pytest.mark.parametrize("dims", [(8, 2048, 80, 64, 1, 64, 256, 1), (1, 65536, 80, 64, 8, 128, 256, 1),
+                                  (1, 1, 1, 64, 1, 16, 64, 0), (3, 77, 5, 64, 5, 32, 128, 0)])
 def test_workspace_size(lib, dims):
     assert lib.ssd_forward_workspace_size(*dims) == _ws_expected(*dims)
+    Bt, L, H, P, G, N, Q, dt = dims
+    assert lib.ssd_chunk_cb_size(Bt, L, G, Q, dt) == _cb_expected(Bt, L, G, Q, dt)
 
 
 def test_workspace_size_invalid(lib):
-    assert lib.ssd_forward_workspace_size(0, 10, 1, 64, 16, 64) == 0
-    assert lib.ssd_forward_workspace_size(1, 10, 1, 64, 16, 0) == 0
+    assert lib.ssd_forward_workspace_size(0, 10, 1, 64, 1, 16, 64, 1) == 0
+    assert lib.ssd_forward_workspace_size(1, 10, 1, 64, 1, 16, 0, 1) == 0
+    assert lib.ssd_forward_workspace_size(1, 10, 1, 64, 1, 16, 64, 5) == 0
+    assert lib.ssd_chunk_cb_size(1, 10, 1, 96, 1) == 0
 
 
 FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: every call below fails its checks first
@@ -117,6 +129,11 @@ def test_stage_entry_points_reject(lib):
     assert lib.ssd_chunk_cumsum(None, FAKE, 1, 10, 2, 64, 1, FAKE, None) == SSD_ERR_NULL
     assert lib.ssd_chunk_cumsum(FAKE, FAKE, 1, 10, 2, 100, 1, FAKE, None) == SSD_ERR_UNSUPPORTED
     assert lib.ssd_chunk_state(FAKE, FAKE, FAKE, FAKE, 1, 10, 3, 64, 2, 64, 64, 1, FAKE, None) == SSD_ERR_SHAPE
-    assert lib.ssd_state_passing(FAKE, FAKE, None, 1, 10, 2, 64, 64, 64, None, None, None) == SSD_ERR_NULL
+    assert lib.ssd_state_passing(FAKE, FAKE, None, 1, 10, 2, 64, 64, 64, 1, None, None, None) == SSD_ERR_NULL
+    assert lib.ssd_state_passing(FAKE, FAKE, None, 1, 10, 2, 64, 64, 64, 4, FAKE, None, None) == SSD_ERR_UNSUPPORTED
     assert lib.ssd_chunk_scan(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 10, 2, 64, 1, 64, 256, 9,
                               FAKE, None) == SSD_ERR_UNSUPPORTED
+    assert lib.ssd_chunk_scan(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1, 10, 2, 64, 1, 64, 256, 1,
+                              FAKE, None) == SSD_ERR_NULL
+    assert lib.ssd_chunk_cb(FAKE, None, 1, 10, 1, 64, 64, 1, FAKE, None) == SSD_ERR_NULL
+    assert lib.ssd_chunk_cb(FAKE, FAKE, 1, 10, 1, 48, 64, 1, FAKE, None) == SSD_ERR_UNSUPPORTED
