@@ -184,19 +184,28 @@ def time_decode(w, warmup=3):
     return {"mean_ms": sum(per) / len(per), "min_ms": min(per), "max_ms": max(per)}
 
 
-def cpu_baseline(w):
-    """The fp64 oracle (as it stands) on the same workload, on this host."""
+def cpu_baseline(w, min_seconds=1.5):
+    """The fp64 oracle (as it stands) on the same workload, on this host.
+
+    A bounded sample: whole forward passes over the workload, repeated until
+    at least ``min_seconds`` of wall time (about 10-30 s of CPU work on the
+    threads it uses)."""
     import oracle
     import ssd_workloads as W
     d = W.generate(w)
     n = oracle.default_threads()
-    t0 = time.perf_counter()
-    oracle.forward(d["x"].val, d["dt"].val, d["A"], d["B"].val, d["C"].val, d["D"], None,
-                   want_state=True, nthreads=n)
-    sec = time.perf_counter() - t0
-    return {"value": w.tokens / sec, "unit": "tokens/s", "cores": n, "kind": "oracle",
-            "sample": f"the whole {w.name} forward (batch {w.batch} x L {w.seqlen}, all {w.batch * w.nheads} "
-                      f"(batch, head) units), one pass, fp64 recurrence, {sec:.2f} s wall"}
+    passes, sec = 0, 0.0
+    while passes == 0 or sec < min_seconds:
+        t0 = time.perf_counter()
+        oracle.forward(d["x"].val, d["dt"].val, d["A"], d["B"].val, d["C"].val, d["D"], None,
+                       want_state=True, nthreads=n)
+        sec += time.perf_counter() - t0
+        passes += 1
+    return {"value": round(passes * w.tokens / sec, 1), "unit": "tokens/s", "cores": n,
+            "kind": "oracle",
+            "sample": f"{passes} pass(es) of the whole {w.name} forward (batch {w.batch} x L "
+                      f"{w.seqlen}, all {w.batch * w.nheads} (batch, head) units, y and final "
+                      f"state), fp64 recurrence on {n} threads, {sec:.2f} s wall"}
 
 
 def counters_run(w):
@@ -217,6 +226,116 @@ def counters_run(w):
     print("[counters] decode done", file=sys.stderr, flush=True)
 
 
+# ---------------------------------------------------------------- profile summaries
+#
+# The rocprofv3 runs these read (OUT is any scratch directory):
+TRACE_CMD = ('rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/trace" -o trace '
+             '-- python bench.py --steps 20 --warmup 5 > "$OUT/bench_trace.log"')
+FETCH_CMD = ('rocprofv3 --pmc FETCH_SIZE --output-format csv -d "$OUT/fetch" -o fetch '
+             '-- python bench.py --counters')
+WRITE_CMD = ('rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/write" -o write '
+             '-- python bench.py --counters')
+KERNEL_OF = {"chunk_cumsum_kernel": "chunk_cumsum", "chunk_state_kernel": "chunk_state",
+             "state_passing_kernel": "state_passing", "chunk_cb_kernel": "chunk_cb",
+             "chunk_scan_kernel": "chunk_scan", "decode_step_kernel": "decode_step"}
+CALIBRATION_KERNEL = "__amd_rocclr_copyBuffer"  # the 1 GiB device copy of --counters
+COPY_BYTES = 1 << 30
+
+
+def _stage_of(kernel_name):
+    for k, v in KERNEL_OF.items():
+        if k in kernel_name:
+            return v
+    return None
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(stats_csv, bench_log):
+    """Markdown table of a --kernel-trace --stats run, with the bench line's own
+    event timings of the same run beside the profiler's averages."""
+    rows = _read_csv(stats_csv)
+    bench = None
+    with open(bench_log) as f:
+        for line in f:
+            if line.startswith("{"):
+                bench = json.loads(line)
+    out = ["# Kernel trace: SSD forward stages (Mamba-2 2.7B-shaped layer) and decode step", "",
+           "Commands, from the repository root on one MI355X:", "", "```",
+           "cd /tmp && export TMPDIR=/tmp && cd -", TRACE_CMD,
+           f'python bench.py --summarize-trace "$OUT/trace/trace_kernel_stats.csv" "$OUT/bench_trace.log"',
+           "```", "",
+           "| kernel | stage | calls | avg us | min us | max us | bench event avg us |",
+           "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        stage = _stage_of(r["Name"])
+        ev = ""
+        if bench and stage in bench.get("kernels", {}):
+            ev = f"{bench['kernels'][stage]['us']:.2f}"
+        elif bench and stage == "decode_step":
+            ev = f"{bench['decode']['us_per_step']:.2f}"
+        name = r["Name"].split("(")[0].replace("void ", "")
+        out.append(f"| `{name}` | {stage or '-'} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {ev} |")
+    if bench:
+        out += ["", f"Bench line of the same run: value {bench['value']:.4g} tokens/s, "
+                    f"{bench['ms_per_step'] * 1e3:.1f} us per forward, roofline "
+                    f"{json.dumps(bench['roofline'])}."]
+    return "\n".join(out)
+
+
+def summarize_traffic(fetch_csv, write_csv, workload="mamba2_2.7b"):
+    """HBM bytes per launch of each kernel from FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for the
+    plain 1 GiB device copy of the same run. Returns (markdown, json dict)."""
+    import ssd_workloads as W
+    per = {}
+    for tag, path in (("fetch", fetch_csv), ("write", write_csv)):
+        for r in _read_csv(path):
+            name = r["Kernel_Name"]
+            key = CALIBRATION_KERNEL if name == CALIBRATION_KERNEL else _stage_of(name)
+            if key is None:
+                continue
+            per.setdefault(key, {}).setdefault(tag, []).append(float(r["Counter_Value"]))
+    cal = per[CALIBRATION_KERNEL]
+    f_scale = COPY_BYTES / 1024 / max(cal["fetch"])
+    w_scale = COPY_BYTES / 1024 / max(cal["write"])
+    acc = accounting(W.WORKLOADS[workload])
+    acc["decode_step"] = decode_accounting(W_decode())
+    rec = {"_calibration": {"kernel": CALIBRATION_KERNEL, "copy_bytes": COPY_BYTES,
+                            "fetch_kib": max(cal["fetch"]), "write_kib": max(cal["write"]),
+                            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+                            "commands": [FETCH_CMD, WRITE_CMD]}}
+    out = ["# HBM traffic per launch: SSD forward stages (Mamba-2 2.7B-shaped layer) and decode step",
+           "", "Commands, from the repository root on one MI355X:", "", "```",
+           "cd /tmp && export TMPDIR=/tmp && cd -", f"timeout -s KILL 60 {FETCH_CMD}",
+           f"timeout -s KILL 60 {WRITE_CMD}",
+           'python bench.py --summarize-traffic "$OUT/fetch/fetch_counter_collection.csv" '
+           '"$OUT/write/write_counter_collection.csv"', "```", "",
+           f"Calibration: the 1 GiB device copy reads FETCH_SIZE {max(cal['fetch']):.0f} KiB and "
+           f"WRITE_SIZE {max(cal['write']):.0f} KiB, so FETCH_SIZE is scaled by {f_scale:.3f} and "
+           f"WRITE_SIZE by {w_scale:.3f}.", "",
+           "| kernel | dispatches | fetch MB | write MB | HBM MB / launch | algorithmic MB | ratio |",
+           "|---|---|---|---|---|---|---|"]
+    for k in ("chunk_cumsum", "chunk_state", "state_passing", "chunk_cb", "chunk_scan", "decode_step"):
+        if k not in per or "fetch" not in per[k] or "write" not in per[k]:
+            continue
+        fk = sum(per[k]["fetch"]) / len(per[k]["fetch"])
+        wk = sum(per[k]["write"]) / len(per[k]["write"])
+        b = fk * 1024 * f_scale + wk * 1024 * w_scale
+        alg = acc[k]["bytes"]
+        rec[k] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                  "bytes_per_launch": round(b), "alg_bytes": alg,
+                  "source_digest": kernel_source_digest(k)}
+        out.append(f"| {k} | {len(per[k]['fetch'])} | {fk * 1024 * f_scale / 1e6:.1f} | "
+                   f"{wk * 1024 * w_scale / 1e6:.1f} | {b / 1e6:.1f} | {alg / 1e6:.1f} | {b / alg:.2f} |")
+    return "\n".join(out), rec
+
+
 def W_decode():
     import ssd_workloads as W
     return W.WORKLOADS["decode"]
@@ -233,7 +352,22 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 counter collection: a few forwards, a few decode "
                          "steps and a plain 1 GiB device copy that calibrates the byte counters")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "BENCH_LOG"),
+                    help="print the markdown summary of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM-traffic summary of two rocprofv3 --pmc runs and write "
+                         "profiles/hbm_traffic.json")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(*args.summarize_trace))
+        return
+    if args.summarize_traffic:
+        md, rec = summarize_traffic(*args.summarize_traffic)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(md)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this SSD build has no multi-GPU path "
               "(batch/head sharding needs no communication; see the design notes). "

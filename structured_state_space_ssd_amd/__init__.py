@@ -73,6 +73,9 @@ def forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, return_final_sta
     if events is not None:
         if len(events) != 6:
             raise ValueError("events must hold 6 torch.cuda.Event objects")
+        for e in events:
+            if not e.cuda_event:
+                e.record()  # torch creates the HIP event on its first record
         ev = (ctypes.c_void_p * 6)(*[e.cuda_event for e in events])
     rc = _native.lib.ssd_forward_timed(
         ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), Bt, L, H, P, G, N, chunk, dt_,
