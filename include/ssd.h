@@ -73,7 +73,8 @@ const char *ssd_strerror(int status);
  *   states      float32 [Bt][nC][H][P][N]  each chunk's own state contribution
  *   chunk_init  [Bt][nC][H][P][N]          state entering each chunk, in the MFMA
  *                                          operand type (bf16 for SSD_BF16, else float32)
- *   cb          ssd_chunk_cb_size(...) bytes: C B^T tiles of every chunk
+ *   cb          SSD_F32 only: ssd_chunk_cb_size(...) bytes, C B^T tiles of every
+ *               chunk (the SSD_BF16 chunk scan forms them itself; no space)
  * After the forward pass has run, these hold the intermediate results of the
  * stages below (a caller may read them, e.g. to test a stage).
  */
@@ -82,7 +83,8 @@ size_t ssd_forward_workspace_size(int batch, int seqlen, int nheads, int headdim
 
 /*
  * Full SSD layer forward: enqueues ssd_chunk_cumsum, ssd_chunk_state,
- * ssd_state_passing, ssd_chunk_cb and ssd_chunk_scan on `stream`.
+ * ssd_state_passing, ssd_chunk_cb (SSD_F32 only) and ssd_chunk_scan on
+ * `stream`.
  *   D           nullable: no feed-through term.
  *   init_state  nullable: the state before token 0 is zero.
  *   y           output, [Bt][L][H][P] in dtype.
@@ -101,7 +103,8 @@ int ssd_forward(const void *x, const void *dt, const float *A, const void *B,
  * hipEvent_t owned by the caller: events[k] is recorded on `stream` right
  * before stage k+1 is enqueued and events[5] after the last stage, so the
  * elapsed time between consecutive events is each stage's GPU time (stages in
- * the order listed for ssd_forward).
+ * the order listed for ssd_forward; for SSD_BF16 the ssd_chunk_cb interval is
+ * empty, that work being part of ssd_chunk_scan).
  */
 int ssd_forward_timed(const void *x, const void *dt, const float *A, const void *B,
                       const void *C, const float *D, int batch, int seqlen, int nheads,
@@ -169,13 +172,16 @@ int ssd_chunk_cb(const void *B, const void *C, int batch, int seqlen, int ngroup
  *   y_i = sum_{j in c, j <= i} (C_i . B_j) exp(s_i - s_j) dt_j x_j   (diagonal block)
  *       + exp(s_i) H_c C_i                                           (off-diagonal blocks)
  *       + D_h x_i,
- * with C_i . B_j read from `cb` (stage 4a), writing y [Bt][L][H][P] in dtype.
- * D is nullable.
+ * writing y [Bt][L][H][P] in dtype. D is nullable. C_i . B_j comes from
+ *   SSD_BF16: B itself ([Bt][L][G][N], 16-byte aligned): the kernel forms the
+ *             C B^T tiles of each chunk on chip; `cb` is not read (may be NULL);
+ *   SSD_F32:  `cb`, the output of ssd_chunk_cb (stage 4a); `B` is not read
+ *             (may be NULL).
  */
-int ssd_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *C,
-                   const void *cb, const float *D, const void *chunk_init, int batch,
-                   int seqlen, int nheads, int headdim, int ngroups, int dstate, int chunk,
-                   int dtype, void *y, void *stream);
+int ssd_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *B,
+                   const void *C, const void *cb, const float *D, const void *chunk_init,
+                   int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate,
+                   int chunk, int dtype, void *y, void *stream);
 
 #ifdef __cplusplus
 }

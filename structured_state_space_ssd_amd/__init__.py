@@ -169,15 +169,20 @@ def chunk_cb(B, C, chunk, out=None):
     return out
 
 
-def chunk_scan(x, dt, dA_cumsum, C, cb, D, chunk_init, chunk, y=None):
-    """y [Bt,L,H,P]: intra-chunk product + state-to-output + D x."""
+def chunk_scan(x, dt, dA_cumsum, B, C, cb, D, chunk_init, chunk, y=None):
+    """y [Bt,L,H,P]: intra-chunk product + state-to-output + D x.
+
+    bfloat16 forms C B^T on chip from B (cb may be None); float32 reads the
+    C B^T tiles of chunk_cb (B may be None)."""
     Bt, L, H, P = _req(x, "x").shape
     G, N = C.shape[2], C.shape[3]
     if y is None:
         y = torch.empty_like(x)
+    bf16 = x.dtype == torch.bfloat16
     rc = _native.lib.ssd_chunk_scan(ptr(x), ptr(_req(dt, "dt", x.dtype)),
                                     ptr(_req(dA_cumsum, "dA_cumsum", torch.float32)),
-                                    ptr(_req(C, "C", x.dtype)), ptr(_req(cb, "cb")),
+                                    ptr(_req(B, "B", x.dtype) if bf16 else B),
+                                    ptr(_req(C, "C", x.dtype)), ptr(cb if bf16 else _req(cb, "cb")),
                                     ptr(_opt(D, "D")), ptr(_req(chunk_init, "chunk_init", x.dtype)),
                                     Bt, L, H, P, G, N, chunk, dtype_code(x.dtype), ptr(y),
                                     stream_handle(x.device))
@@ -195,5 +200,5 @@ def stages(x, dt, A, B, C, D=None, chunk=256, init_state=None):
     fs = torch.empty((Bt, H, P, N), dtype=torch.float32, device=x.device)
     ci = state_passing(st, s, L, chunk, init_state=init_state, final_state=fs, dtype=x.dtype)
     cb = chunk_cb(B, C, chunk)
-    y = chunk_scan(x, dt, s, C, cb, D, ci, chunk)
+    y = chunk_scan(x, dt, s, B, C, cb, D, ci, chunk)
     return {"dA_cumsum": s, "states": st, "chunk_init": ci, "final_state": fs, "cb": cb, "y": y}

@@ -275,56 +275,540 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_kernel(
     }
 }
 
-template <typename T, int N, int Q>
-static void launch_scan(const void *x, const void *dt, const float *dA, const void *C,
-                        const void *cb, const float *D, const void *Hc, int batch, int L, int H,
-                        int G, void *y, hipStream_t stream) {
-    using E = typename LdsT<T>::type;
+// ============================================================================
+// bf16 inputs: persistent head blocks fed by global-to-LDS loads
+// ============================================================================
+//
+// A workgroup owns one (batch, chunk, B/C group) and a run of consecutive heads
+// of that group, which it processes one after another; in the main
+// configurations it fills a compute unit's LDS, one workgroup per compute unit.
+//   - Head-independent data is prepared once: the causal C B^T tiles of the
+//     chunk are computed on MFMA straight into LDS (in the fragment layout of
+//     chunk_cb.hip, which this path therefore does not need), and the C rows of
+//     the wavefront's two tiles stay in registers.
+//   - Per head, x and H_c reach LDS through direct global-to-LDS loads (16
+//     bytes per lane, no registers involved). x has two buffers: the next
+//     head's x streams in during the whole of this head. H_c, read only by the
+//     state-to-output product at the start of a head, is refilled right after
+//     that product. The next head's decay tables are formed meanwhile.
+//   - Inside a head no value is waited for from global memory: every operand
+//     comes from LDS or registers. (Memory operations complete in issue order
+//     for the wait counter, so a wait on any global load issued after the
+//     prefetch would also wait for the prefetch.)
+//   - Outputs are staged through the head's x buffer and leave as whole
+//     128-byte token rows; the next head's first wait leaves those stores in
+//     flight.
+// The products are those of the float kernel above, except that the
+// state-to-output product takes raw C rows and scales its result by exp(s_i)
+// per token, and every wavefront's slice sequence is fixed at compile time
+// (one code path per tile pair). LDS rows are 128 bytes (x) or 2N bytes (H_c)
+// with their 16-byte pieces XOR-swizzled so that the transposing reads of x
+// and the row reads of H_c touch distinct banks.
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte-per-lane global-to-LDS load: lane l's 16 bytes from `src` land
+// at byte lds_base + 16*l (lds_base is the same for the whole wavefront). In
+// inline assembly so that the compiler does not hold later reads of other LDS
+// buffers behind it; completion is awaited explicitly (wait_barrier).
+__device__ __forceinline__ void dma16(const void *src, const void *lds_base) {
+    const uint32_t a =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(a)
+                 : "memory", "m0");
+}
+
+// This wavefront's LDS operations complete and at most VM of its global
+// memory operations (the most recently issued ones) remain outstanding; then
+// the workgroup meets.
+template <int VM>
+__device__ __forceinline__ void wait_barrier() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// LDS operations complete, global ones stay in flight; then the workgroup meets.
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// x tile: token rows of 64 bf16 (eight 16-byte pieces); piece q of row r is
+// stored at piece q ^ (r & 7). A half-wavefront's transposing read covers 8
+// consecutive rows x 2 pieces, which this puts on 16 distinct bank groups.
+__device__ __forceinline__ int x_at(int r, int col) {
+    return r * 64 + ((((col >> 3) ^ r) & 7) << 3) + (col & 7);
+}
+
+// H_c rows of N bf16 (N/8 pieces); piece q of row p is stored at q ^ f(p), f
+// chosen so that one fragment read (16 consecutive rows, one piece) touches
+// distinct bank groups.
+template <int N>
+__device__ __forceinline__ int h_swz(int p) {
+    constexpr int PPR = N / 8;
+    constexpr int RPW = PPR >= 16 ? 1 : 16 / PPR;  // rows per 256-byte bank window
+    constexpr int MSK = (PPR >= 16 ? 16 : PPR) - 1;
+    return (p / RPW) & MSK;
+}
+
+// Transposing reads of the swizzled x tile. Lane 16*g + s of a fragment for
+// head-dim columns 16*pt + 0..15 reads row 32*jp + 4*g + s/4 (+16 for the
+// second half) at column 16*pt + 4*(s%4); since 32*jp and 16 are multiples of
+// 8, the swizzle term r & 7 = (4*g + s/4) & 7 is the same for every slice, and
+// the element offset splits into a per-lane part, 16 * (pt ^ zt) with a
+// per-lane zt, and compile-time multiples of 2048 (jp) and 1024 (second half).
+__device__ __forceinline__ void x_colfrag_offsets(int (&xo)[4], int l) {
+    const int s = l & 15, g = l >> 4;
+    const int r = 4 * g + (s >> 2);
+    const int z = r & 7;
+    const int base = r * 64 + 8 * (((s >> 1) & 1) ^ (z & 1)) + 4 * (s & 1);
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) xo[pt] = base + 16 * (pt ^ (z >> 1));
+}
+
+// x^T operand fragment: lane 16*g + c receives x[32*jp + 4*g + 0..3][16*pt + c]
+// (elements 0..3) and x[32*jp + 16 + 4*g + 0..3][16*pt + c] (elements 4..7).
+template <int JP>
+__device__ __forceinline__ void x_colfrag(Frag<bf16_t> &f, const __bf16 *xs, int xo) {
+    const shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(xs + xo + JP * 2048));
+    const shortx4 b =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(xs + xo + JP * 2048 + 1024));
+    const bf16x4 ab = __builtin_bit_cast(bf16x4, a);
+    const bf16x4 bb = __builtin_bit_cast(bf16x4, b);
+    f.v = bf16x8{ab[0], ab[1], ab[2], ab[3], bb[0], bb[1], bb[2], bb[3]};
+}
+
+// Per-head decay tables (as in the float kernel).
+template <int Q>
+struct ScanTables {
+    float sl[Q];    // s * log2(e)
+    float dtl[Q];   // s * log2(e) - log2(dt) (+inf past the end)
+    float colf[Q];  // exp2(s_end(slice of j) - s_j) * dt_j
+};
+
+// Entry of causal tile (it, jp) in a unit's C B^T tile list: tiles are stored
+// row-tile-major, row tile it holding jp = 0..it/2.
+__device__ __forceinline__ int cb_tile_start(int it) {
+    const int m0 = it / 2;
+    return (it % 2 == 0) ? m0 * (m0 + 1) : (m0 + 1) * (m0 + 1);
+}
+
+// Slice K (of NT/2 + 1) of wavefront pair index MM: tile 2*MM + (w&1) takes
+// slices 0..MM, tile NT-1-2*MM-(w&1) slices 0..NT/2-1-MM; the last slice of
+// each holds its diagonal. cbl0 / cbl1: this lane's C B^T fragment of slice 0
+// of the two tiles in LDS (the slices of a tile are consecutive entries).
+template <int Q, int MM, int K>
+__device__ __forceinline__ void scan_slice(floatx4 (&acc)[2][4], const __bf16 *cbl0,
+                                           const __bf16 *cbl1, const __bf16 *xs,
+                                           const int (&xo)[4], const ScanTables<Q> &tb,
+                                           const float (&si)[2], int il0, int il1, int g4) {
+    constexpr int NT = Q / 16;
+    constexpr int TI = K <= MM ? 0 : 1;
+    constexpr int JP = TI ? K - MM - 1 : K;
+    constexpr bool DIAG = TI ? (JP == NT / 2 - 1 - MM) : (JP == MM);
+    const int il = TI ? il1 : il0;
+    const float s_i = si[TI];
+    const int jb = JP * 32 + 4 * g4;
+    Frag<bf16_t> cbk, mf;
+    cbk.v = *reinterpret_cast<const bf16x8 *>((TI ? cbl1 : cbl0) + JP * 512);
+    if constexpr (!DIAG) {
+        // strictly below the diagonal: exp2(s_i - s_j) dt_j =
+        // exp2(s_i - s_end(slice)) * colf[j], both factors <= 1; no mask
+        const float rowf = __builtin_amdgcn_exp2f(s_i - tb.sl[JP * 32 + 31]);
+        const floatx4 c0 = *reinterpret_cast<const floatx4 *>(tb.colf + jb);
+        const floatx4 c1 = *reinterpret_cast<const floatx4 *>(tb.colf + jb + 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            mf.set(r, cbk.get(r) * (c0[r] * rowf));
+            mf.set(4 + r, cbk.get(4 + r) * (c1[r] * rowf));
+        }
+    } else {
+        // the slice holding the diagonal: exp2(s_i - (s_j - log2 dt_j)) and the causal mask
+        const floatx4 d0 = *reinterpret_cast<const floatx4 *>(tb.dtl + jb);
+        const floatx4 d1 = *reinterpret_cast<const floatx4 *>(tb.dtl + jb + 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float v0 = cbk.get(r) * __builtin_amdgcn_exp2f(s_i - d0[r]);
+            const float v1 = cbk.get(4 + r) * __builtin_amdgcn_exp2f(s_i - d1[r]);
+            mf.set(r, jb + r <= il ? v0 : 0.0f);
+            mf.set(4 + r, jb + 16 + r <= il ? v1 : 0.0f);
+        }
+    }
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+        Frag<bf16_t> xf;
+        x_colfrag<JP>(xf, xs, xo[pt]);
+        mma(acc[TI][pt], xf, mf);
+    }
+}
+
+template <int Q, int MM, int K>
+__device__ __forceinline__ void scan_slices(floatx4 (&acc)[2][4], const __bf16 *cbl0,
+                                            const __bf16 *cbl1, const __bf16 *xs,
+                                            const int (&xo)[4], const ScanTables<Q> &tb,
+                                            const float (&si)[2], int il0, int il1, int g4) {
+    if constexpr (K < Q / 32 + 1) {
+        scan_slice<Q, MM, K>(acc, cbl0, cbl1, xs, xo, tb, si, il0, il1, g4);
+        scan_slices<Q, MM, K + 1>(acc, cbl0, cbl1, xs, xo, tb, si, il0, il1, g4);
+    }
+}
+
+template <int Q, int MM>
+__device__ __forceinline__ void scan_slices_of(int M, floatx4 (&acc)[2][4], const __bf16 *cbl0,
+                                               const __bf16 *cbl1, const __bf16 *xs,
+                                               const int (&xo)[4], const ScanTables<Q> &tb,
+                                               const float (&si)[2], int il0, int il1, int g4) {
+    if constexpr (MM < Q / 64) {
+        if (M == MM) scan_slices<Q, MM, 0>(acc, cbl0, cbl1, xs, xo, tb, si, il0, il1, g4);
+        else scan_slices_of<Q, MM + 1>(M, acc, cbl0, cbl1, xs, xo, tb, si, il0, il1, g4);
+    }
+}
+
+// LDS of the bf16 kernel and whether x is double-buffered.
+template <int N, int Q>
+struct ScanBf16Lds {
+    static constexpr int ENTRIES = (Q / 32) * (Q / 32 + 1);
+    static constexpr size_t kSingle = (size_t)Q * 64 * 2 + 64 * N * 2 + 2 * sizeof(ScanTables<Q>) +
+                                      (size_t)ENTRIES * 1024;
+    static constexpr bool kDbuf = kSingle + (size_t)Q * 64 * 2 <= 160 * 1024;
+    static constexpr size_t kBytes = kSingle + (kDbuf ? (size_t)Q * 64 * 2 : 0);
+};
+
+}  // namespace
+
+template <int N, int Q>
+__global__ __launch_bounds__(Q * 2) void chunk_scan_bf16_kernel(
+    const bf16_t *__restrict__ x, const bf16_t *__restrict__ dt,
+    const float *__restrict__ dA_cumsum, const bf16_t *__restrict__ B,
+    const bf16_t *__restrict__ C, const float *__restrict__ D,
+    const __bf16 *__restrict__ chunk_init, int L, int H, int G, int nC, int nU, int nblk, int hbh,
+    bf16_t *__restrict__ y) {
+    constexpr int P = 64, NW = Q / 32, NT = Q / 16;
+    constexpr int NK = (N + 31) / 32;
+    constexpr int ENTRIES = ScanBf16Lds<N, Q>::ENTRIES;
+    constexpr bool DBUF = ScanBf16Lds<N, Q>::kDbuf;
+    constexpr int PPR = N / 8;           // 16-byte pieces per H_c row
+    constexpr int XI = Q * 8 / 64 / NW;  // x loads (and y stores) per wavefront per head
+    __shared__ __attribute__((aligned(16))) __bf16 xb0[Q * P];
+    __shared__ __attribute__((aligned(16))) __bf16 xb1[DBUF ? Q * P : 8];
+    __shared__ __attribute__((aligned(16))) __bf16 hbuf[P * N];
+    __shared__ __attribute__((aligned(16))) __bf16 cbs[ENTRIES * 512];
+    __shared__ __attribute__((aligned(16))) ScanTables<Q> tab0;
+    __shared__ __attribute__((aligned(16))) ScanTables<Q> tab1;
+
+    // workgroup -> (unit u = c + nC*(g + G*b), head block kb); the nblk blocks
+    // of one unit get ids with the same id % 8, i.e. the same XCD, which then
+    // reads that unit's B and C once
+    const int id = blockIdx.x;
+    const int q8 = id / (8 * nblk), rem = id - q8 * 8 * nblk;
+    const int kb = rem / 8, u = q8 * 8 + rem % 8;
+    if (u >= nU) return;  // whole workgroup
+    const int hpg = H / G;
+    const int c = u % nC, g = (u / nC) % G, b = u / (nC * G);
+    const int hfirst = g * hpg + kb * hbh;
+    const int nh = min(hbh, hpg - kb * hbh);
+    if (nh <= 0) return;  // whole workgroup
+
+    const int t0 = c * Q, len = min(Q, L - t0);
+    const bool full = len == Q;
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = l >> 4, r16 = l & 15;
+    const int M = w >> 1;
+    const int tile0 = 2 * M + (w & 1), tile1 = NT - 1 - tile0;
+    const int il0 = tile0 * 16 + r16, il1 = tile1 * 16 + r16;
+    const size_t xrow = (size_t)H * P;  // token stride of x and y
+    const bf16_t *xbase = x + ((size_t)b * L + t0) * xrow;
+    bf16_t *ybase = y + ((size_t)b * L + t0) * xrow;
+    const __bf16 *hbase = chunk_init + ((size_t)b * nC + c) * H * (size_t)(P * N);
+    const float *sbase = dA_cumsum + (size_t)b * H * nC * Q + (size_t)c * Q;
+    const size_t bcrow = (size_t)G * N;  // token stride of B and C
+    const bf16_t *Bc = B + ((size_t)b * L + t0) * bcrow + (size_t)g * N;
+    const bf16_t *Cc = C + ((size_t)b * L + t0) * bcrow + (size_t)g * N;
+
+    auto issue_x = [&](int h, const __bf16 *buf) {
+        const bf16_t *xh = xbase + (size_t)h * P;
+#pragma unroll
+        for (int k = 0; k < XI; ++k) {
+            const int i = k * NW + w;  // 8 token rows per load
+            const int s = i * 64 + l;
+            const int r = s >> 3, q = (s & 7) ^ (r & 7);
+            dma16(xh + (size_t)min(r, len - 1) * xrow + q * 8, buf + i * 512);
+        }
+    };
+    auto issue_h = [&](int h) {
+        const __bf16 *hc = hbase + (size_t)h * (P * N);
+#pragma unroll
+        for (int i = w; i < PPR; i += NW) {  // 64 pieces per load, PPR loads in all
+            const int s = i * 64 + l;
+            const int p = s / PPR, q = (s % PPR) ^ h_swz<N>(p);
+            dma16(hc + (size_t)p * N + q * 8, hbuf + i * 512);
+        }
+    };
+    // table inputs are loaded raw (s, s at the slice end, dt's bf16 bits) and
+    // only turned into table entries by tab_store
+    auto tab_load = [&](int h, float &sv, float &se, float &d) {
+        if (tid < Q) {
+            const float *s = sbase + (size_t)h * nC * Q;
+            sv = s[tid];
+            se = s[tid | 31];
+            d = __uint_as_float(dt[((size_t)b * L + t0 + min(tid, len - 1)) * H + h]);
+        }
+    };
+    auto tab_store = [&](ScanTables<Q> &t, float sv, float se, float draw) {
+        if (tid < Q) {
+            const float d = tid < len ? bf16_to_f32((bf16_t)__float_as_uint(draw)) : 0.0f;
+            const float si_ = sv * kLog2e;
+            t.sl[tid] = si_;
+            t.dtl[tid] = si_ - __log2f(d);
+            t.colf[tid] = __builtin_amdgcn_exp2f(se * kLog2e - si_) * d;
+        }
+    };
+
+    // ---- prologue. The first head's x and H_c on their way ...
+    issue_x(hfirst, xb0);
+    issue_h(hfirst);
+    // ... the unit's causal C B^T tiles into LDS: tile e = (it, jp) by
+    // wavefront e % NW, two 16x16 products of B rows against C rows over N
+    // (fragment layout: lane 16*g + r holds row 16*it + r at tokens
+    // 32*jp + 4*g + 0..3 and 32*jp + 16 + 4*g + 0..3; past the end: zero)
+#pragma unroll 3
+    for (int e = w; e < ENTRIES; e += NW) {
+        int it = 0;
+        while (cb_tile_start(it + 1) <= e) ++it;
+        const int jp = e - cb_tile_start(it);
+        const int i = it * 16 + r16;
+        floatx4 m[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+            const int n0 = kk * 32 + 8 * g4;
+            const bool kin = n0 < N;
+            uint4 cr = *reinterpret_cast<const uint4 *>(Cc + (size_t)min(i, len - 1) * bcrow +
+                                                        min(n0, N - 8));
+            if (!(kin && i < len)) cr = make_uint4(0, 0, 0, 0);
+            Frag<bf16_t> cf;
+            cf.v = __builtin_bit_cast(bf16x8, cr);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int j = jp * 32 + half * 16 + r16;
+                uint4 br = *reinterpret_cast<const uint4 *>(Bc + (size_t)min(j, len - 1) * bcrow +
+                                                            min(n0, N - 8));
+                if (!(kin && j < len)) br = make_uint4(0, 0, 0, 0);
+                Frag<bf16_t> bf;
+                bf.v = __builtin_bit_cast(bf16x8, br);
+                mma(m[half], bf, cf);
+            }
+        }
+        Frag<bf16_t> out;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            out.set(r, m[0][r]);
+            out.set(4 + r, m[1][r]);
+        }
+        *reinterpret_cast<bf16x8 *>(cbs + e * 512 + l * 8) = out.v;
+    }
+    // ... the first head's tables, and the C rows of both tiles (state-to-output
+    // B operand), kept in registers for all heads
+    {
+        float sv = 0.0f, se = 0.0f, d = 0.0f;
+        tab_load(hfirst, sv, se, d);
+        tab_store(tab0, sv, se, d);
+    }
+    Frag<bf16_t> cf[2][NK];
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+        const int il = ti ? il1 : il0;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+            const int n0 = kk * 32 + 8 * g4;
+            uint4 raw = *reinterpret_cast<const uint4 *>(Cc + (size_t)min(il, len - 1) * bcrow +
+                                                         min(n0, N - 8));
+            if (!(il < len && n0 < N)) raw = make_uint4(0, 0, 0, 0);
+            cf[ti][kk].v = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+    const __bf16 *cbl0 = cbs + cb_tile_start(tile0) * 512 + l * 8;
+    const __bf16 *cbl1 = cbs + cb_tile_start(tile1) * 512 + l * 8;
+    int xo[4];
+    x_colfrag_offsets(xo, l);
+
+    for (int k = 0; k < nh; ++k) {
+        const int h = hfirst + k;
+        const bool more = k + 1 < nh;
+        const bool odd = DBUF && (k & 1);
+        __bf16 *xs = odd ? xb1 : xb0;
+        const ScanTables<Q> &tb = (k & 1) ? tab1 : tab0;
+        // x(h), H_c(h) and tables(h) are in LDS, head h-1 is done with its
+        // buffers; head h-1's XI output stores (the most recent global
+        // operations, full chunks only) may stay in flight
+        if (DBUF && full && k > 0) wait_barrier<XI>();
+        else wait_barrier<0>();
+        float nsv = 0.0f, nse = 0.0f, nd = 0.0f;
+        if (more) tab_load(h + 1, nsv, nse, nd);  // before the prefetch: waited for at the end
+        if (DBUF && more) issue_x(h + 1, odd ? xb0 : xb1);
+
+        // ---- state to output: Y^T[p][i] = sum_n H_c[p][n] C_i[n], scaled by exp(s_i) below
+        floatx4 acc[2][4];
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) acc[ti][pt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+            const int n0 = kk * 32 + 8 * g4;
+            const int q = min(n0, N - 8) >> 3;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const int p = pt * 16 + r16;
+                Frag<bf16_t> hf;
+                hf.v = *reinterpret_cast<const bf16x8 *>(hbuf + p * N + ((q ^ h_swz<N>(p)) << 3));
+                if (n0 >= N) hf.zero();  // only N = 16
+#pragma unroll
+                for (int ti = 0; ti < 2; ++ti) mma(acc[ti][pt], hf, cf[ti][kk]);
+            }
+        }
+        barrier_lds();  // every wavefront has read H_c(h)
+        if (more) issue_h(h + 1);
+
+        float si[2];
+        const float Dh = D ? D[h] : 0.0f;
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) {
+            const int il = ti ? il1 : il0;
+            si[ti] = tb.sl[il];
+            const float sc = __builtin_amdgcn_exp2f(si[ti]);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xs + x_at(il, pt * 16 + 4 * g4));
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[ti][pt][r] = acc[ti][pt][r] * sc + Dh * static_cast<float>(xv[r]);
+            }
+        }
+        // ---- diagonal blocks
+        scan_slices_of<Q, 0>(M, acc, cbl0, cbl1, xs, xo, tb, si, il0, il1, g4);
+
+        // ---- next head's tables. Their inputs are consumed only here: the
+        // empty asm keeps the compiler from waiting for their loads early
+        // (which, memory operations completing in issue order, would also
+        // wait for the prefetch issued after them); here that wait costs
+        // nothing, and it precedes this head's output stores.
+        asm volatile("" : "+v"(nsv), "+v"(nse), "+v"(nd));
+        if (more) tab_store((k & 1) ? tab0 : tab1, nsv, nse, nd);
+
+        // ---- outputs, staged in this head's x buffer and stored as whole rows
+        barrier_lds();  // every wavefront is done reading x(h)
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) {
+            const int il = ti ? il1 : il0;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const bf16x4 v{static_cast<__bf16>(acc[ti][pt][0]), static_cast<__bf16>(acc[ti][pt][1]),
+                               static_cast<__bf16>(acc[ti][pt][2]), static_cast<__bf16>(acc[ti][pt][3])};
+                *reinterpret_cast<bf16x4 *>(xs + x_at(il, pt * 16 + 4 * g4)) = v;
+            }
+        }
+        barrier_lds();
+        bf16_t *yh = ybase + (size_t)h * P;
+#pragma unroll
+        for (int kq = 0; kq < XI; ++kq) {
+            const int i = kq * NW + w;
+            const int s = i * 64 + l;
+            const int r = s >> 3, q = (s & 7) ^ (r & 7);
+            const uint4 v = *reinterpret_cast<const uint4 *>(xs + s * 8);
+            if (r < len) *reinterpret_cast<uint4 *>(yh + (size_t)r * xrow + q * 8) = v;
+        }
+        if (!DBUF && more) {
+            barrier_lds();  // every wavefront has read its outputs out of x(h)
+            issue_x(h + 1, xb0);
+        }
+    }
+}
+
+template <int N, int Q>
+static void launch_scan_bf16(const void *x, const void *dt, const float *dA, const void *B,
+                             const void *C, const float *D, const void *Hc, int batch, int L,
+                             int H, int G, void *y, hipStream_t stream) {
     const int nC = (L + Q - 1) / Q;
-    const dim3 grid(nC, H, batch);
-    chunk_scan_kernel<T, N, Q><<<grid, Q * 2, 0, stream>>>(
-        static_cast<const T *>(x), static_cast<const T *>(dt), dA, static_cast<const T *>(C),
-        static_cast<const E *>(cb), D, static_cast<const E *>(Hc), L, H, G, nC,
-        static_cast<T *>(y));
+    const int hpg = H / G;
+    const int nU = batch * nC * G;
+    // resident workgroups per compute unit (LDS-bound), 256 compute units
+    const int per_cu = (int)((160 * 1024) / ScanBf16Lds<N, Q>::kBytes);
+    const int target = 256 * (per_cu < 1 ? 1 : per_cu);
+    int nblk = (target + nU - 1) / nU;
+    nblk = nblk < 1 ? 1 : (nblk > hpg ? hpg : nblk);
+    const int hbh = (hpg + nblk - 1) / nblk;
+    nblk = (hpg + hbh - 1) / hbh;
+    const dim3 grid((unsigned)(8 * nblk) * (unsigned)((nU + 7) / 8));
+    chunk_scan_bf16_kernel<N, Q><<<grid, Q * 2, 0, stream>>>(
+        static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(dt), dA,
+        static_cast<const bf16_t *>(B), static_cast<const bf16_t *>(C), D,
+        static_cast<const __bf16 *>(Hc), L, H, G, nC, nU, nblk, hbh, static_cast<bf16_t *>(y));
+}
+
+template <typename T, int N, int Q>
+static void launch_scan(const void *x, const void *dt, const float *dA, const void *B,
+                        const void *C, const void *cb, const float *D, const void *Hc, int batch,
+                        int L, int H, int G, void *y, hipStream_t stream) {
+    if constexpr (sizeof(T) == 2) {
+        launch_scan_bf16<N, Q>(x, dt, dA, B, C, D, Hc, batch, L, H, G, y, stream);
+    } else {
+        using E = typename LdsT<T>::type;
+        const int nC = (L + Q - 1) / Q;
+        const dim3 grid(nC, H, batch);
+        chunk_scan_kernel<T, N, Q><<<grid, Q * 2, 0, stream>>>(
+            static_cast<const T *>(x), static_cast<const T *>(dt), dA, static_cast<const T *>(C),
+            static_cast<const E *>(cb), D, static_cast<const E *>(Hc), L, H, G, nC,
+            static_cast<T *>(y));
+    }
 }
 
 template <typename T, int N>
-static bool scan_q(int Q, const void *x, const void *dt, const float *dA, const void *C,
-                   const void *cb, const float *D, const void *Hc, int batch, int L, int H, int G,
-                   void *y, hipStream_t s) {
+static bool scan_q(int Q, const void *x, const void *dt, const float *dA, const void *B,
+                   const void *C, const void *cb, const float *D, const void *Hc, int batch, int L,
+                   int H, int G, void *y, hipStream_t s) {
     switch (Q) {
-        case 64: launch_scan<T, N, 64>(x, dt, dA, C, cb, D, Hc, batch, L, H, G, y, s); return true;
-        case 128: launch_scan<T, N, 128>(x, dt, dA, C, cb, D, Hc, batch, L, H, G, y, s); return true;
-        case 256: launch_scan<T, N, 256>(x, dt, dA, C, cb, D, Hc, batch, L, H, G, y, s); return true;
+        case 64: launch_scan<T, N, 64>(x, dt, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); return true;
+        case 128: launch_scan<T, N, 128>(x, dt, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); return true;
+        case 256: launch_scan<T, N, 256>(x, dt, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); return true;
         default: return false;
     }
 }
 
 template <typename T>
 static hipError_t scan_dispatch(int N, int Q, const void *x, const void *dt, const float *dA,
-                                const void *C, const void *cb, const float *D, const void *Hc,
-                                int batch, int L, int H, int G, void *y, hipStream_t s) {
+                                const void *B, const void *C, const void *cb, const float *D,
+                                const void *Hc, int batch, int L, int H, int G, void *y,
+                                hipStream_t s) {
     bool ok = false;
     switch (N) {
-        case 16: ok = scan_q<T, 16>(Q, x, dt, dA, C, cb, D, Hc, batch, L, H, G, y, s); break;
-        case 32: ok = scan_q<T, 32>(Q, x, dt, dA, C, cb, D, Hc, batch, L, H, G, y, s); break;
-        case 64: ok = scan_q<T, 64>(Q, x, dt, dA, C, cb, D, Hc, batch, L, H, G, y, s); break;
-        case 128: ok = scan_q<T, 128>(Q, x, dt, dA, C, cb, D, Hc, batch, L, H, G, y, s); break;
-        case 256: ok = scan_q<T, 256>(Q, x, dt, dA, C, cb, D, Hc, batch, L, H, G, y, s); break;
+        case 16: ok = scan_q<T, 16>(Q, x, dt, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
+        case 32: ok = scan_q<T, 32>(Q, x, dt, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
+        case 64: ok = scan_q<T, 64>(Q, x, dt, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
+        case 128: ok = scan_q<T, 128>(Q, x, dt, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
+        case 256: ok = scan_q<T, 256>(Q, x, dt, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
         default: break;
     }
     if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
-hipError_t launch_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *C,
-                             const void *cb, const float *D, const void *chunk_init, int batch,
-                             int seqlen, int nheads, int ngroups, int dstate, int chunk, bool bf16,
-                             void *y, hipStream_t stream) {
+bool chunk_scan_reads_cb(bool bf16) { return !bf16; }
+
+hipError_t launch_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *B,
+                             const void *C, const void *cb, const float *D, const void *chunk_init,
+                             int batch, int seqlen, int nheads, int ngroups, int dstate, int chunk,
+                             bool bf16, void *y, hipStream_t stream) {
     if (bf16)
-        return scan_dispatch<bf16_t>(dstate, chunk, x, dt, dA_cumsum, C, cb, D, chunk_init, batch,
-                                     seqlen, nheads, ngroups, y, stream);
-    return scan_dispatch<float>(dstate, chunk, x, dt, dA_cumsum, C, cb, D, chunk_init, batch,
+        return scan_dispatch<bf16_t>(dstate, chunk, x, dt, dA_cumsum, B, C, cb, D, chunk_init,
+                                     batch, seqlen, nheads, ngroups, y, stream);
+    return scan_dispatch<float>(dstate, chunk, x, dt, dA_cumsum, B, C, cb, D, chunk_init, batch,
                                 seqlen, nheads, ngroups, y, stream);
 }
 

@@ -34,7 +34,9 @@ Workspace layout(int batch, int seqlen, int nheads, int headdim, int ngroups, in
     w.states_off = align_up(cumsum);
     w.init_off = w.states_off + align_up(st);
     w.cb_off = w.init_off + align_up(ci);
-    w.total = w.cb_off + align_up(ssd::chunk_cb_bytes(batch, seqlen, ngroups, chunk, bf16));
+    w.total = w.cb_off;
+    if (ssd::chunk_scan_reads_cb(bf16))
+        w.total += align_up(ssd::chunk_cb_bytes(batch, seqlen, ngroups, chunk, bf16));
     return w;
 }
 
@@ -130,19 +132,23 @@ int ssd_state_passing(const float *states, const float *dA_cumsum, const float *
                                                final_state, static_cast<hipStream_t>(stream)));
 }
 
-int ssd_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *C,
-                   const void *cb, const float *D, const void *chunk_init, int batch, int seqlen,
-                   int nheads, int headdim, int ngroups, int dstate, int chunk, int dtype, void *y,
-                   void *stream) {
-    if (!x || !dt || !dA_cumsum || !C || !cb || !chunk_init || !y) return SSD_ERR_NULL;
+int ssd_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *B,
+                   const void *C, const void *cb, const float *D, const void *chunk_init,
+                   int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate,
+                   int chunk, int dtype, void *y, void *stream) {
+    if (!x || !dt || !dA_cumsum || !C || !chunk_init || !y) return SSD_ERR_NULL;
     int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
     if (rc != SSD_OK) return rc;
     if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    const bool bf16 = dtype == SSD_BF16;
+    const bool reads_cb = ssd::chunk_scan_reads_cb(bf16);
+    if (reads_cb ? !cb : !B) return SSD_ERR_NULL;
     if (!aligned16(x) || !aligned16(C) || !aligned16(chunk_init) || !aligned16(y) ||
-        !aligned16(dA_cumsum) || (reinterpret_cast<uintptr_t>(cb) % 32) != 0)
+        !aligned16(dA_cumsum) || (reads_cb ? (reinterpret_cast<uintptr_t>(cb) % 32) != 0
+                                           : !aligned16(B)))
         return SSD_ERR_UNSUPPORTED;
-    return status_of(ssd::launch_chunk_scan(x, dt, dA_cumsum, C, cb, D, chunk_init, batch, seqlen,
-                                            nheads, ngroups, dstate, chunk, dtype == SSD_BF16, y,
+    return status_of(ssd::launch_chunk_scan(x, dt, dA_cumsum, B, C, cb, D, chunk_init, batch,
+                                            seqlen, nheads, ngroups, dstate, chunk, bf16, y,
                                             static_cast<hipStream_t>(stream)));
 }
 
@@ -187,12 +193,12 @@ int ssd_forward_timed(const void *x, const void *dt, const float *A, const void 
         e = ssd::launch_state_passing(states, cumsum, init_state, batch, seqlen, nheads, dstate,
                                       chunk, bf16, cinit, final_state, s);
     if (e == hipSuccess) e = mark(3);
-    if (e == hipSuccess)
+    if (e == hipSuccess && ssd::chunk_scan_reads_cb(bf16))
         e = ssd::launch_chunk_cb(B, C, batch, seqlen, ngroups, dstate, chunk, bf16, cb, s);
     if (e == hipSuccess) e = mark(4);
     if (e == hipSuccess)
-        e = ssd::launch_chunk_scan(x, dt, cumsum, C, cb, D, cinit, batch, seqlen, nheads, ngroups,
-                                   dstate, chunk, bf16, y, s);
+        e = ssd::launch_chunk_scan(x, dt, cumsum, B, C, cb, D, cinit, batch, seqlen, nheads,
+                                   ngroups, dstate, chunk, bf16, y, s);
     if (e == hipSuccess) e = mark(5);
     return status_of(e);
 }

@@ -27,10 +27,14 @@ size_t chunk_cb_bytes(int batch, int seqlen, int ngroups, int chunk, bool bf16);
 hipError_t launch_chunk_cb(const void *B, const void *C, int batch, int seqlen, int ngroups,
                            int dstate, int chunk, bool bf16, void *cb, hipStream_t stream);
 
-hipError_t launch_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *C,
-                             const void *cb, const float *D, const void *chunk_init, int batch,
-                             int seqlen, int nheads, int ngroups, int dstate, int chunk, bool bf16,
-                             void *y, hipStream_t stream);
+// The bf16 path forms C B^T itself (reads B, ignores cb); the float path reads
+// the C B^T tiles of launch_chunk_cb (reads cb, ignores B).
+bool chunk_scan_reads_cb(bool bf16);
+
+hipError_t launch_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *B,
+                             const void *C, const void *cb, const float *D, const void *chunk_init,
+                             int batch, int seqlen, int nheads, int ngroups, int dstate, int chunk,
+                             bool bf16, void *y, hipStream_t stream);
 
 hipError_t launch_decode_step(float *state, const void *x, const void *dt, const float *A,
                               const void *B, const void *C, const float *D, int batch, int nheads,

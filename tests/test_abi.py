@@ -61,7 +61,9 @@ def _ws_expected(Bt, L, H, P, G, N, Q, dtype):
     cs = Bt * H * nC * Q * 4
     st = Bt * nC * H * P * N * 4
     ci = Bt * nC * H * P * N * (2 if dtype == 1 else 4)
-    return al(cs) + al(st) + al(ci) + al(_cb_expected(Bt, L, G, Q, dtype))
+    # the C B^T scratch is needed by the float path only (bf16 forms the tiles on chip)
+    cb = al(_cb_expected(Bt, L, G, Q, dtype)) if dtype == 0 else 0
+    return al(cs) + al(st) + al(ci) + cb
 
 
 @pytest.mark.parametrize("dims", [(8, 2048, 80, 64, 1, 64, 256, 1), (1, 65536, 80, 64, 8, 128, 256, 1),
@@ -131,9 +133,17 @@ def test_stage_entry_points_reject(lib):
     assert lib.ssd_chunk_state(FAKE, FAKE, FAKE, FAKE, 1, 10, 3, 64, 2, 64, 64, 1, FAKE, None) == SSD_ERR_SHAPE
     assert lib.ssd_state_passing(FAKE, FAKE, None, 1, 10, 2, 64, 64, 64, 1, None, None, None) == SSD_ERR_NULL
     assert lib.ssd_state_passing(FAKE, FAKE, None, 1, 10, 2, 64, 64, 64, 4, FAKE, None, None) == SSD_ERR_UNSUPPORTED
-    assert lib.ssd_chunk_scan(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 10, 2, 64, 1, 64, 256, 9,
+    # ssd_chunk_scan(x, dt, dA, B, C, cb, D, chunk_init, Bt, L, H, P, G, N, Q, dtype, y, stream)
+    assert lib.ssd_chunk_scan(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 10, 2, 64, 1, 64, 256, 9,
                               FAKE, None) == SSD_ERR_UNSUPPORTED
-    assert lib.ssd_chunk_scan(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1, 10, 2, 64, 1, 64, 256, 1,
+    assert lib.ssd_chunk_scan(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 1, 10, 2, 64, 1, 64, 256, 1,
                               FAKE, None) == SSD_ERR_NULL
+    # bf16 reads B (not cb), float reads cb (not B)
+    assert lib.ssd_chunk_scan(FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, 1, 10, 2, 64, 1, 64, 256, 1,
+                              FAKE, None) == SSD_ERR_NULL
+    assert lib.ssd_chunk_scan(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1, 10, 2, 64, 1, 64, 256, 0,
+                              FAKE, None) == SSD_ERR_NULL
+    assert lib.ssd_chunk_scan(FAKE, FAKE, FAKE, ctypes.c_void_p(0x100008), FAKE, None, None, FAKE, 1, 10,
+                              2, 64, 1, 64, 256, 1, FAKE, None) == SSD_ERR_UNSUPPORTED
     assert lib.ssd_chunk_cb(FAKE, None, 1, 10, 1, 64, 64, 1, FAKE, None) == SSD_ERR_NULL
     assert lib.ssd_chunk_cb(FAKE, FAKE, 1, 10, 1, 48, 64, 1, FAKE, None) == SSD_ERR_UNSUPPORTED
