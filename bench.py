@@ -237,7 +237,7 @@ WRITE_CMD = ('rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/write" -o 
              '-- python bench.py --counters')
 KERNEL_OF = {"chunk_cumsum_kernel": "chunk_cumsum", "chunk_state_kernel": "chunk_state",
              "state_passing_kernel": "state_passing", "chunk_cb_kernel": "chunk_cb",
-             "chunk_scan_kernel": "chunk_scan", "decode_step_kernel": "decode_step"}
+             "chunk_scan": "chunk_scan", "decode_step_kernel": "decode_step"}
 CALIBRATION_KERNEL = "__amd_rocclr_copyBuffer"  # the 1 GiB device copy of --counters
 COPY_BYTES = 1 << 30
 

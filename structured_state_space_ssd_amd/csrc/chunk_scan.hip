@@ -401,24 +401,17 @@ __device__ __forceinline__ int cb_tile_start(int it) {
     return (it % 2 == 0) ? m0 * (m0 + 1) : (m0 + 1) * (m0 + 1);
 }
 
-// Slice K (of NT/2 + 1) of wavefront pair index MM: tile 2*MM + (w&1) takes
-// slices 0..MM, tile NT-1-2*MM-(w&1) slices 0..NT/2-1-MM; the last slice of
-// each holds its diagonal. cbl0 / cbl1: this lane's C B^T fragment of slice 0
-// of the two tiles in LDS (the slices of a tile are consecutive entries).
-template <int Q, int MM, int K>
-__device__ __forceinline__ void scan_slice(floatx4 (&acc)[2][4], const __bf16 *cbl0,
-                                           const __bf16 *cbl1, const __bf16 *xs,
-                                           const int (&xo)[4], const ScanTables<Q> &tb,
-                                           const float (&si)[2], int il0, int il1, int g4) {
-    constexpr int NT = Q / 16;
-    constexpr int TI = K <= MM ? 0 : 1;
-    constexpr int JP = TI ? K - MM - 1 : K;
-    constexpr bool DIAG = TI ? (JP == NT / 2 - 1 - MM) : (JP == MM);
-    const int il = TI ? il1 : il0;
-    const float s_i = si[TI];
+// Slice JP (0..JMAX) of this wavefront's row tile it (JMAX = it/2; slice
+// JMAX holds the diagonal). cbl: this lane's C B^T fragment of slice 0 of the
+// tile in LDS (the slices of a tile are consecutive entries).
+template <int Q, int JMAX, int JP>
+__device__ __forceinline__ void scan_slice(floatx4 (&acc)[4], const __bf16 *cbl,
+                                           const __bf16 *xs, const int (&xo)[4],
+                                           const ScanTables<Q> &tb, float s_i, int il, int g4) {
+    constexpr bool DIAG = JP == JMAX;
     const int jb = JP * 32 + 4 * g4;
     Frag<bf16_t> cbk, mf;
-    cbk.v = *reinterpret_cast<const bf16x8 *>((TI ? cbl1 : cbl0) + JP * 512);
+    cbk.v = *reinterpret_cast<const bf16x8 *>(cbl + JP * 512);
     if constexpr (!DIAG) {
         // strictly below the diagonal: exp2(s_i - s_j) dt_j =
         // exp2(s_i - s_end(slice)) * colf[j], both factors <= 1; no mask
@@ -446,30 +439,37 @@ __device__ __forceinline__ void scan_slice(floatx4 (&acc)[2][4], const __bf16 *c
     for (int pt = 0; pt < 4; ++pt) {
         Frag<bf16_t> xf;
         x_colfrag<JP>(xf, xs, xo[pt]);
-        mma(acc[TI][pt], xf, mf);
+        mma(acc[pt], xf, mf);
     }
 }
 
-template <int Q, int MM, int K>
-__device__ __forceinline__ void scan_slices(floatx4 (&acc)[2][4], const __bf16 *cbl0,
-                                            const __bf16 *cbl1, const __bf16 *xs,
-                                            const int (&xo)[4], const ScanTables<Q> &tb,
-                                            const float (&si)[2], int il0, int il1, int g4) {
-    if constexpr (K < Q / 32 + 1) {
-        scan_slice<Q, MM, K>(acc, cbl0, cbl1, xs, xo, tb, si, il0, il1, g4);
-        scan_slices<Q, MM, K + 1>(acc, cbl0, cbl1, xs, xo, tb, si, il0, il1, g4);
+template <int Q, int JMAX, int JP>
+__device__ __forceinline__ void scan_slices(floatx4 (&acc)[4], const __bf16 *cbl,
+                                            const __bf16 *xs, const int (&xo)[4],
+                                            const ScanTables<Q> &tb, float s_i, int il, int g4) {
+    if constexpr (JP <= JMAX) {
+        scan_slice<Q, JMAX, JP>(acc, cbl, xs, xo, tb, s_i, il, g4);
+        scan_slices<Q, JMAX, JP + 1>(acc, cbl, xs, xo, tb, s_i, il, g4);
     }
 }
 
-template <int Q, int MM>
-__device__ __forceinline__ void scan_slices_of(int M, floatx4 (&acc)[2][4], const __bf16 *cbl0,
-                                               const __bf16 *cbl1, const __bf16 *xs,
-                                               const int (&xo)[4], const ScanTables<Q> &tb,
-                                               const float (&si)[2], int il0, int il1, int g4) {
-    if constexpr (MM < Q / 64) {
-        if (M == MM) scan_slices<Q, MM, 0>(acc, cbl0, cbl1, xs, xo, tb, si, il0, il1, g4);
-        else scan_slices_of<Q, MM + 1>(M, acc, cbl0, cbl1, xs, xo, tb, si, il0, il1, g4);
+// Dispatch on the (wavefront-uniform) tile's last slice index jmax.
+template <int Q, int JMAX>
+__device__ __forceinline__ void scan_tile(int jmax, floatx4 (&acc)[4], const __bf16 *cbl,
+                                          const __bf16 *xs, const int (&xo)[4],
+                                          const ScanTables<Q> &tb, float s_i, int il, int g4) {
+    if constexpr (JMAX < Q / 32) {
+        if (jmax == JMAX) scan_slices<Q, JMAX, 0>(acc, cbl, xs, xo, tb, s_i, il, g4);
+        else scan_tile<Q, JMAX + 1>(jmax, acc, cbl, xs, xo, tb, s_i, il, g4);
     }
+}
+
+// Row tile of wavefront w (one per wavefront). Wavefronts w and w + 4k share a
+// SIMD; the assignment gives every SIMD the same number of 32-token slices:
+// SIMD s takes tiles s, 7-s, 8+s, 15-s (Q = 256), s, 7-s (Q = 128), s (Q = 64).
+__device__ __forceinline__ int scan_tile_of(int w) {
+    const int s = w & 3, k = w >> 2;
+    return (k >> 1) * 8 + ((k & 1) ? 7 - s : s);
 }
 
 // LDS of the bf16 kernel and whether x is double-buffered.
@@ -485,13 +485,13 @@ struct ScanBf16Lds {
 }  // namespace
 
 template <int N, int Q>
-__global__ __launch_bounds__(Q * 2) void chunk_scan_bf16_kernel(
+__global__ __launch_bounds__(Q * 4) void chunk_scan_bf16_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ dt,
     const float *__restrict__ dA_cumsum, const bf16_t *__restrict__ B,
     const bf16_t *__restrict__ C, const float *__restrict__ D,
-    const __bf16 *__restrict__ chunk_init, int L, int H, int G, int nC, int nU, int nblk, int hbh,
+    const __bf16 *__restrict__ chunk_init, int L, int H, int G, int nC, int nU, int nblk,
     bf16_t *__restrict__ y) {
-    constexpr int P = 64, NW = Q / 32, NT = Q / 16;
+    constexpr int P = 64, NW = Q / 16;  // one wavefront per 16-row tile
     constexpr int NK = (N + 31) / 32;
     constexpr int ENTRIES = ScanBf16Lds<N, Q>::ENTRIES;
     constexpr bool DBUF = ScanBf16Lds<N, Q>::kDbuf;
@@ -513,16 +513,18 @@ __global__ __launch_bounds__(Q * 2) void chunk_scan_bf16_kernel(
     if (u >= nU) return;  // whole workgroup
     const int hpg = H / G;
     const int c = u % nC, g = (u / nC) % G, b = u / (nC * G);
-    const int hfirst = g * hpg + kb * hbh;
-    const int nh = min(hbh, hpg - kb * hbh);
+    // the block's heads are g*hpg + kb + k*nblk, k = 0..nh-1: the nblk blocks
+    // of a unit work on adjacent heads at the same time, so their x and y
+    // rows are neighbouring 128-byte pieces of the same token rows
+    const int hfirst = g * hpg + kb;
+    const int nh = (hpg - kb + nblk - 1) / nblk;
     if (nh <= 0) return;  // whole workgroup
 
     const int t0 = c * Q, len = min(Q, L - t0);
     const bool full = len == Q;
     const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = l >> 4, r16 = l & 15;
-    const int M = w >> 1;
-    const int tile0 = 2 * M + (w & 1), tile1 = NT - 1 - tile0;
-    const int il0 = tile0 * 16 + r16, il1 = tile1 * 16 + r16;
+    const int tile = scan_tile_of(w), jmax = tile / 2;
+    const int il = tile * 16 + r16;
     const size_t xrow = (size_t)H * P;  // token stride of x and y
     const bf16_t *xbase = x + ((size_t)b * L + t0) * xrow;
     bf16_t *ybase = y + ((size_t)b * L + t0) * xrow;
@@ -532,48 +534,59 @@ __global__ __launch_bounds__(Q * 2) void chunk_scan_bf16_kernel(
     const bf16_t *Bc = B + ((size_t)b * L + t0) * bcrow + (size_t)g * N;
     const bf16_t *Cc = C + ((size_t)b * L + t0) * bcrow + (size_t)g * N;
 
-    auto issue_x = [&](int h, const __bf16 *buf) {
+    // Per-head address arithmetic takes the lane index from opaque_tid(),
+    // which the compiler cannot see through: otherwise it keeps the
+    // loop-invariant 64-bit addresses of every load and store alive across the
+    // head loop, runs out of registers and spills them, and every reload of a
+    // spill waits for all outstanding memory operations, the prefetch
+    // included.
+    auto opaque_tid = []() {
+        int t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        return t;
+    };
+    auto issue_x = [&](int h, const __bf16 *buf, int ln) {
         const bf16_t *xh = xbase + (size_t)h * P;
 #pragma unroll
         for (int k = 0; k < XI; ++k) {
             const int i = k * NW + w;  // 8 token rows per load
-            const int s = i * 64 + l;
+            const int s = i * 64 + ln;
             const int r = s >> 3, q = (s & 7) ^ (r & 7);
             dma16(xh + (size_t)min(r, len - 1) * xrow + q * 8, buf + i * 512);
         }
     };
-    auto issue_h = [&](int h) {
+    auto issue_h = [&](int h, int ln) {
         const __bf16 *hc = hbase + (size_t)h * (P * N);
 #pragma unroll
         for (int i = w; i < PPR; i += NW) {  // 64 pieces per load, PPR loads in all
-            const int s = i * 64 + l;
+            const int s = i * 64 + ln;
             const int p = s / PPR, q = (s % PPR) ^ h_swz<N>(p);
             dma16(hc + (size_t)p * N + q * 8, hbuf + i * 512);
         }
     };
     // table inputs are loaded raw (s, s at the slice end, dt's bf16 bits) and
     // only turned into table entries by tab_store
-    auto tab_load = [&](int h, float &sv, float &se, float &d) {
-        if (tid < Q) {
+    auto tab_load = [&](int h, int td, float &sv, float &se, float &d) {
+        if (td < Q) {
             const float *s = sbase + (size_t)h * nC * Q;
-            sv = s[tid];
-            se = s[tid | 31];
-            d = __uint_as_float(dt[((size_t)b * L + t0 + min(tid, len - 1)) * H + h]);
+            sv = s[td];
+            se = s[td | 31];
+            d = __uint_as_float(dt[((size_t)b * L + t0 + min(td, len - 1)) * H + h]);
         }
     };
-    auto tab_store = [&](ScanTables<Q> &t, float sv, float se, float draw) {
-        if (tid < Q) {
-            const float d = tid < len ? bf16_to_f32((bf16_t)__float_as_uint(draw)) : 0.0f;
+    auto tab_store = [&](ScanTables<Q> &t, int td, float sv, float se, float draw) {
+        if (td < Q) {
+            const float d = td < len ? bf16_to_f32((bf16_t)__float_as_uint(draw)) : 0.0f;
             const float si_ = sv * kLog2e;
-            t.sl[tid] = si_;
-            t.dtl[tid] = si_ - __log2f(d);
-            t.colf[tid] = __builtin_amdgcn_exp2f(se * kLog2e - si_) * d;
+            t.sl[td] = si_;
+            t.dtl[td] = si_ - __log2f(d);
+            t.colf[td] = __builtin_amdgcn_exp2f(se * kLog2e - si_) * d;
         }
     };
 
     // ---- prologue. The first head's x and H_c on their way ...
-    issue_x(hfirst, xb0);
-    issue_h(hfirst);
+    issue_x(hfirst, xb0, l);
+    issue_h(hfirst, l);
     // ... the unit's causal C B^T tiles into LDS: tile e = (it, jp) by
     // wavefront e % NW, two 16x16 products of B rows against C rows over N
     // (fragment layout: lane 16*g + r holds row 16*it + r at tokens
@@ -613,12 +626,332 @@ __global__ __launch_bounds__(Q * 2) void chunk_scan_bf16_kernel(
         }
         *reinterpret_cast<bf16x8 *>(cbs + e * 512 + l * 8) = out.v;
     }
-    // ... the first head's tables, and the C rows of both tiles (state-to-output
-    // B operand), kept in registers for all heads
+    // ... the first head's tables, and the C rows of the wavefront's tile
+    // (state-to-output B operand), kept in registers for all heads
     {
         float sv = 0.0f, se = 0.0f, d = 0.0f;
-        tab_load(hfirst, sv, se, d);
-        tab_store(tab0, sv, se, d);
+        tab_load(hfirst, tid, sv, se, d);
+        tab_store(tab0, tid, sv, se, d);
+    }
+    Frag<bf16_t> cf[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+        const int n0 = kk * 32 + 8 * g4;
+        uint4 raw = *reinterpret_cast<const uint4 *>(Cc + (size_t)min(il, len - 1) * bcrow +
+                                                     min(n0, N - 8));
+        if (!(il < len && n0 < N)) raw = make_uint4(0, 0, 0, 0);
+        cf[kk].v = __builtin_bit_cast(bf16x8, raw);
+    }
+    const __bf16 *cbl = cbs + cb_tile_start(tile) * 512 + l * 8;
+    int xo[4];
+    x_colfrag_offsets(xo, l);
+
+    for (int k = 0; k < nh; ++k) {
+        const int h = hfirst + k * nblk, hn = h + nblk;
+        const bool more = k + 1 < nh;
+        const bool odd = DBUF && (k & 1);
+        __bf16 *xs = odd ? xb1 : xb0;
+        const ScanTables<Q> &tb = (k & 1) ? tab1 : tab0;
+        // x(h), H_c(h) and tables(h) are in LDS, head h-1 is done with its
+        // buffers; head h-1's XI output stores (the most recent global
+        // operations, full chunks only) may stay in flight
+        if (DBUF && full && k > 0) wait_barrier<XI>();
+        else wait_barrier<0>();
+        const int td = opaque_tid(), ln = td & 63;
+        float nsv = 0.0f, nse = 0.0f, nd = 0.0f;
+        if (more) tab_load(hn, td, nsv, nse, nd);  // before the prefetch: waited for at the end
+        if (DBUF && more) issue_x(hn, odd ? xb0 : xb1, ln);
+
+        // ---- state to output: Y^T[p][i] = sum_n H_c[p][n] C_i[n], scaled by exp(s_i) below
+        floatx4 acc[4];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[pt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+            const int n0 = kk * 32 + 8 * g4;
+            const int q = min(n0, N - 8) >> 3;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const int p = pt * 16 + r16;
+                Frag<bf16_t> hf;
+                hf.v = *reinterpret_cast<const bf16x8 *>(hbuf + p * N + ((q ^ h_swz<N>(p)) << 3));
+                if (n0 >= N) hf.zero();  // only N = 16
+                mma(acc[pt], hf, cf[kk]);
+            }
+        }
+        barrier_lds();  // every wavefront has read H_c(h)
+        if (more) issue_h(hn, ln);
+
+        const float Dh = D ? D[h] : 0.0f;
+        const float si = tb.sl[il];
+        {
+            const float sc = __builtin_amdgcn_exp2f(si);
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xs + x_at(il, pt * 16 + 4 * g4));
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[pt][r] = acc[pt][r] * sc + Dh * static_cast<float>(xv[r]);
+            }
+        }
+        // ---- diagonal blocks
+        scan_tile<Q, 0>(jmax, acc, cbl, xs, xo, tb, si, il, g4);
+
+        // ---- next head's tables. Their inputs are consumed only here: the
+        // empty asm keeps the compiler from waiting for their loads early
+        // (which, memory operations completing in issue order, would also
+        // wait for the prefetch issued after them); here that wait costs
+        // nothing, and it precedes this head's output stores.
+        asm volatile("" : "+v"(nsv), "+v"(nse), "+v"(nd));
+        if (more) tab_store((k & 1) ? tab0 : tab1, td, nsv, nse, nd);
+
+        // ---- outputs, staged in this head's x buffer and stored as whole rows
+        barrier_lds();  // every wavefront is done reading x(h)
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+            const bf16x4 v{static_cast<__bf16>(acc[pt][0]), static_cast<__bf16>(acc[pt][1]),
+                           static_cast<__bf16>(acc[pt][2]), static_cast<__bf16>(acc[pt][3])};
+            *reinterpret_cast<bf16x4 *>(xs + x_at(il, pt * 16 + 4 * g4)) = v;
+        }
+        barrier_lds();
+        bf16_t *yh = ybase + (size_t)h * P;
+#pragma unroll
+        for (int kq = 0; kq < XI; ++kq) {
+            const int i = kq * NW + w;
+            const int s = i * 64 + ln;
+            const int r = s >> 3, q = (s & 7) ^ (r & 7);
+            const uint4 v = *reinterpret_cast<const uint4 *>(xs + s * 8);
+            if (r < len) *reinterpret_cast<uint4 *>(yh + (size_t)r * xrow + q * 8) = v;
+        }
+        if (!DBUF && more) {
+            barrier_lds();  // every wavefront has read its outputs out of x(h)
+            issue_x(hn, xb0, ln);
+        }
+    }
+}
+
+// ---- small states (N <= 64 at chunk 256): two workgroups per compute unit
+//
+// For small N the chunk's B rows fit in LDS next to x and H_c, so the C B^T
+// values of a slice are formed right where they are needed (two 16x16 MFMA
+// products of B rows from LDS against the wavefront's C rows in registers),
+// in float32, and the decay multiplies them before the single rounding to
+// bf16. A workgroup then needs under half of the LDS, two of them share a
+// compute unit, and each wavefront owns a pair of row tiles with equal
+// causal work (tiles 2*MM + (w&1) and NT-1-2*MM-(w&1): NT/2 + 1 slices of 32
+// tokens). x is single-buffered: the next head's x is loaded once this head's
+// outputs have left its buffer, while the other workgroup computes.
+
+namespace {
+
+// Slice K of wavefront pair index MM (see scan_slice for the decay).
+template <int N, int Q, int MM, int K>
+__device__ __forceinline__ void pair_slice(floatx4 (&acc)[2][4], const Frag<bf16_t> (&cf)[2][(N + 31) / 32],
+                                           const __bf16 *bsm, const int (&bo)[(N + 31) / 32],
+                                           const __bf16 *xs, const int (&xo)[4],
+                                           const ScanTables<Q> &tb, const float (&si)[2], int il0,
+                                           int il1, int g4, int r16) {
+    constexpr int NT = Q / 16, NK = (N + 31) / 32;
+    constexpr int TI = K <= MM ? 0 : 1;
+    constexpr int JP = TI ? K - MM - 1 : K;
+    constexpr bool DIAG = TI ? (JP == NT / 2 - 1 - MM) : (JP == MM);
+    const int il = TI ? il1 : il0;
+    const float s_i = si[TI];
+    const int jb = JP * 32 + 4 * g4;
+    // the slice's x^T fragments first: their LDS latency overlaps the C B^T
+    // products and the decay arithmetic below
+    Frag<bf16_t> xf[4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) x_colfrag<JP>(xf[pt], xs, xo[pt]);
+    // C B^T of the slice: lane 16*g + r gets rows (tokens) i = 16*tile + r at
+    // tokens jb + 0..3 (m[0]) and jb + 16 + 0..3 (m[1])
+    floatx4 m[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            Frag<bf16_t> bfr;
+            bfr.v = *reinterpret_cast<const bf16x8 *>(bsm + bo[kk] + (JP * 32 + half * 16) * N);
+            if (kk * 32 + 8 * g4 >= N) bfr.zero();  // only N = 16
+            mma(m[half], bfr, cf[TI][kk]);
+        }
+    }
+    Frag<bf16_t> mf;
+    if constexpr (!DIAG) {
+        const float rowf = __builtin_amdgcn_exp2f(s_i - tb.sl[JP * 32 + 31]);
+        const floatx4 c0 = *reinterpret_cast<const floatx4 *>(tb.colf + jb);
+        const floatx4 c1 = *reinterpret_cast<const floatx4 *>(tb.colf + jb + 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            mf.set(r, m[0][r] * (c0[r] * rowf));
+            mf.set(4 + r, m[1][r] * (c1[r] * rowf));
+        }
+    } else {
+        const floatx4 d0 = *reinterpret_cast<const floatx4 *>(tb.dtl + jb);
+        const floatx4 d1 = *reinterpret_cast<const floatx4 *>(tb.dtl + jb + 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float v0 = m[0][r] * __builtin_amdgcn_exp2f(s_i - d0[r]);
+            const float v1 = m[1][r] * __builtin_amdgcn_exp2f(s_i - d1[r]);
+            mf.set(r, jb + r <= il ? v0 : 0.0f);
+            mf.set(4 + r, jb + 16 + r <= il ? v1 : 0.0f);
+        }
+    }
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) mma(acc[TI][pt], xf[pt], mf);
+}
+
+template <int N, int Q, int MM, int K>
+__device__ __forceinline__ void pair_slices(floatx4 (&acc)[2][4], const Frag<bf16_t> (&cf)[2][(N + 31) / 32],
+                                            const __bf16 *bsm, const int (&bo)[(N + 31) / 32],
+                                            const __bf16 *xs, const int (&xo)[4],
+                                            const ScanTables<Q> &tb, const float (&si)[2], int il0,
+                                            int il1, int g4, int r16) {
+    if constexpr (K < Q / 32 + 1) {
+        pair_slice<N, Q, MM, K>(acc, cf, bsm, bo, xs, xo, tb, si, il0, il1, g4, r16);
+        __builtin_amdgcn_sched_barrier(0);  // keep slices apart: bounded register use
+        pair_slices<N, Q, MM, K + 1>(acc, cf, bsm, bo, xs, xo, tb, si, il0, il1, g4, r16);
+    }
+}
+
+template <int N, int Q, int MM>
+__device__ __forceinline__ void pair_slices_of(int M, floatx4 (&acc)[2][4],
+                                               const Frag<bf16_t> (&cf)[2][(N + 31) / 32],
+                                               const __bf16 *bsm, const int (&bo)[(N + 31) / 32],
+                                               const __bf16 *xs, const int (&xo)[4],
+                                               const ScanTables<Q> &tb, const float (&si)[2],
+                                               int il0, int il1, int g4, int r16) {
+    if constexpr (MM < Q / 64) {
+        if (M == MM) pair_slices<N, Q, MM, 0>(acc, cf, bsm, bo, xs, xo, tb, si, il0, il1, g4, r16);
+        else pair_slices_of<N, Q, MM + 1>(M, acc, cf, bsm, bo, xs, xo, tb, si, il0, il1, g4, r16);
+    }
+}
+
+// Element offset, within a row-major LDS matrix of N-element rows stored with
+// the h_swz piece swizzle, of the 8 elements one lane reads for an MFMA
+// operand: row r16 (+ any multiple of 16 rows, which leaves the swizzle
+// unchanged) at columns 32*kk + 8*g (clamped into the row for N = 16).
+template <int N>
+__device__ __forceinline__ void swz_row_offsets(int (&o)[(N + 31) / 32], int l) {
+    const int g4 = l >> 4, r16 = l & 15;
+#pragma unroll
+    for (int kk = 0; kk < (N + 31) / 32; ++kk) {
+        const int q = min(kk * 32 + 8 * g4, N - 8) >> 3;
+        o[kk] = r16 * N + ((q ^ h_swz<N>(r16)) << 3);
+    }
+}
+
+template <int N, int Q>
+struct PairLds {
+    static constexpr size_t kBytes = (size_t)Q * 64 * 2 + 64 * N * 2 + (size_t)Q * N * 2 +
+                                     2 * sizeof(ScanTables<Q>);
+    static constexpr bool kFits = kBytes <= 80 * 1024;  // two per compute unit
+};
+
+}  // namespace
+
+template <int N, int Q>
+__global__ __launch_bounds__(Q * 2, 4) void chunk_scan_bf16_pair_kernel(
+    const bf16_t *__restrict__ x, const bf16_t *__restrict__ dt,
+    const float *__restrict__ dA_cumsum, const bf16_t *__restrict__ B,
+    const bf16_t *__restrict__ C, const float *__restrict__ D,
+    const __bf16 *__restrict__ chunk_init, int L, int H, int G, int nC, int nU, int nblk,
+    bf16_t *__restrict__ y) {
+    constexpr int P = 64, NW = Q / 32, NT = Q / 16;
+    constexpr int NK = (N + 31) / 32;
+    constexpr int PPR = N / 8;            // 16-byte pieces per H_c / B row
+    constexpr int XI = Q * 8 / 64 / NW;   // x loads (and y stores) per wavefront per head
+    constexpr int BI = Q * PPR / 64;      // B loads per workgroup
+    __shared__ __attribute__((aligned(16))) __bf16 xs[Q * P];
+    __shared__ __attribute__((aligned(16))) __bf16 hbuf[P * N];
+    __shared__ __attribute__((aligned(16))) __bf16 bsm[Q * N];
+    __shared__ __attribute__((aligned(16))) ScanTables<Q> tab0;
+    __shared__ __attribute__((aligned(16))) ScanTables<Q> tab1;
+
+    // workgroup -> (unit u = c + nC*(g + G*b), head block kb), XCD-aware as above
+    const int id = blockIdx.x;
+    const int q8 = id / (8 * nblk), rem = id - q8 * 8 * nblk;
+    const int kb = rem / 8, u = q8 * 8 + rem % 8;
+    if (u >= nU) return;  // whole workgroup
+    const int hpg = H / G;
+    const int c = u % nC, g = (u / nC) % G, b = u / (nC * G);
+    // the block's heads are g*hpg + kb + k*nblk, k = 0..nh-1: the nblk blocks
+    // of a unit work on adjacent heads at the same time, so their x and y
+    // rows are neighbouring 128-byte pieces of the same token rows
+    const int hfirst = g * hpg + kb;
+    const int nh = (hpg - kb + nblk - 1) / nblk;
+    if (nh <= 0) return;  // whole workgroup
+
+    const int t0 = c * Q, len = min(Q, L - t0);
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = l >> 4, r16 = l & 15;
+    const int M = w >> 1;
+    const int tile0 = 2 * M + (w & 1), tile1 = NT - 1 - tile0;
+    const int il0 = tile0 * 16 + r16, il1 = tile1 * 16 + r16;
+    const size_t xrow = (size_t)H * P;
+    const bf16_t *xbase = x + ((size_t)b * L + t0) * xrow;
+    bf16_t *ybase = y + ((size_t)b * L + t0) * xrow;
+    const __bf16 *hbase = chunk_init + ((size_t)b * nC + c) * H * (size_t)(P * N);
+    const float *sbase = dA_cumsum + (size_t)b * H * nC * Q + (size_t)c * Q;
+    const size_t bcrow = (size_t)G * N;
+    const bf16_t *Bc = B + ((size_t)b * L + t0) * bcrow + (size_t)g * N;
+    const bf16_t *Cc = C + ((size_t)b * L + t0) * bcrow + (size_t)g * N;
+
+    auto opaque_tid = []() {  // see chunk_scan_bf16_kernel
+        int t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        return t;
+    };
+    auto issue_x = [&](int h, int ln) {
+        const bf16_t *xh = xbase + (size_t)h * P;
+#pragma unroll
+        for (int k = 0; k < XI; ++k) {
+            const int i = k * NW + w;
+            const int s = i * 64 + ln;
+            const int r = s >> 3, q = (s & 7) ^ (r & 7);
+            dma16(xh + (size_t)min(r, len - 1) * xrow + q * 8, xs + i * 512);
+        }
+    };
+    auto issue_h = [&](int h, int ln) {
+        const __bf16 *hc = hbase + (size_t)h * (P * N);
+#pragma unroll
+        for (int i = w; i < PPR; i += NW) {
+            const int s = i * 64 + ln;
+            const int p = s / PPR, q = (s % PPR) ^ h_swz<N>(p);
+            dma16(hc + (size_t)p * N + q * 8, hbuf + i * 512);
+        }
+    };
+    auto tab_load = [&](int h, int td, float &sv, float &se, float &d) {
+        if (td < Q) {
+            const float *s = sbase + (size_t)h * nC * Q;
+            sv = s[td];
+            se = s[td | 31];
+            d = __uint_as_float(dt[((size_t)b * L + t0 + min(td, len - 1)) * H + h]);
+        }
+    };
+    auto tab_store = [&](ScanTables<Q> &t, int td, float sv, float se, float draw) {
+        if (td < Q) {
+            const float d = td < len ? bf16_to_f32((bf16_t)__float_as_uint(draw)) : 0.0f;
+            const float si_ = sv * kLog2e;
+            t.sl[td] = si_;
+            t.dtl[td] = si_ - __log2f(d);
+            t.colf[td] = __builtin_amdgcn_exp2f(se * kLog2e - si_) * d;
+        }
+    };
+
+    // ---- prologue: the chunk's B rows (token rows past the end repeat the
+    // last one; their products are multiplied by zero decay), the first
+    // head's x and H_c, its tables, and the C rows of both tiles in registers
+    for (int i = w; i < BI; i += NW) {
+        const int s = i * 64 + l;
+        const int j = s / PPR, q = (s % PPR) ^ h_swz<N>(j);
+        dma16(Bc + (size_t)min(j, len - 1) * bcrow + q * 8, bsm + i * 512);
+    }
+    issue_x(hfirst, l);
+    issue_h(hfirst, l);
+    {
+        float sv = 0.0f, se = 0.0f, d = 0.0f;
+        tab_load(hfirst, tid, sv, se, d);
+        tab_store(tab0, tid, sv, se, d);
     }
     Frag<bf16_t> cf[2][NK];
 #pragma unroll
@@ -633,27 +966,21 @@ __global__ __launch_bounds__(Q * 2) void chunk_scan_bf16_kernel(
             cf[ti][kk].v = __builtin_bit_cast(bf16x8, raw);
         }
     }
-    const __bf16 *cbl0 = cbs + cb_tile_start(tile0) * 512 + l * 8;
-    const __bf16 *cbl1 = cbs + cb_tile_start(tile1) * 512 + l * 8;
     int xo[4];
     x_colfrag_offsets(xo, l);
+    int so[NK];  // this lane's H_c / B fragment offsets
+    swz_row_offsets<N>(so, l);
 
     for (int k = 0; k < nh; ++k) {
-        const int h = hfirst + k;
+        const int h = hfirst + k * nblk, hn = h + nblk;
         const bool more = k + 1 < nh;
-        const bool odd = DBUF && (k & 1);
-        __bf16 *xs = odd ? xb1 : xb0;
         const ScanTables<Q> &tb = (k & 1) ? tab1 : tab0;
-        // x(h), H_c(h) and tables(h) are in LDS, head h-1 is done with its
-        // buffers; head h-1's XI output stores (the most recent global
-        // operations, full chunks only) may stay in flight
-        if (DBUF && full && k > 0) wait_barrier<XI>();
-        else wait_barrier<0>();
+        wait_barrier<0>();  // x(h), H_c(h), tables(h) (and B) in LDS
+        const int td = opaque_tid(), ln = td & 63;
         float nsv = 0.0f, nse = 0.0f, nd = 0.0f;
-        if (more) tab_load(h + 1, nsv, nse, nd);  // before the prefetch: waited for at the end
-        if (DBUF && more) issue_x(h + 1, odd ? xb0 : xb1);
+        if (more) tab_load(hn, td, nsv, nse, nd);
 
-        // ---- state to output: Y^T[p][i] = sum_n H_c[p][n] C_i[n], scaled by exp(s_i) below
+        // ---- state to output, scaled by exp(s_i) below
         floatx4 acc[2][4];
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti)
@@ -661,20 +988,17 @@ __global__ __launch_bounds__(Q * 2) void chunk_scan_bf16_kernel(
             for (int pt = 0; pt < 4; ++pt) acc[ti][pt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
-            const int n0 = kk * 32 + 8 * g4;
-            const int q = min(n0, N - 8) >> 3;
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
-                const int p = pt * 16 + r16;
                 Frag<bf16_t> hf;
-                hf.v = *reinterpret_cast<const bf16x8 *>(hbuf + p * N + ((q ^ h_swz<N>(p)) << 3));
-                if (n0 >= N) hf.zero();  // only N = 16
+                hf.v = *reinterpret_cast<const bf16x8 *>(hbuf + so[kk] + pt * 16 * N);
+                if (kk * 32 + 8 * g4 >= N) hf.zero();  // only N = 16
 #pragma unroll
                 for (int ti = 0; ti < 2; ++ti) mma(acc[ti][pt], hf, cf[ti][kk]);
             }
         }
         barrier_lds();  // every wavefront has read H_c(h)
-        if (more) issue_h(h + 1);
+        if (more) issue_h(hn, ln);
 
         float si[2];
         const float Dh = D ? D[h] : 0.0f;
@@ -692,18 +1016,14 @@ __global__ __launch_bounds__(Q * 2) void chunk_scan_bf16_kernel(
             }
         }
         // ---- diagonal blocks
-        scan_slices_of<Q, 0>(M, acc, cbl0, cbl1, xs, xo, tb, si, il0, il1, g4);
+        pair_slices_of<N, Q, 0>(M, acc, cf, bsm, so, xs, xo, tb, si, il0, il1, g4, r16);
 
-        // ---- next head's tables. Their inputs are consumed only here: the
-        // empty asm keeps the compiler from waiting for their loads early
-        // (which, memory operations completing in issue order, would also
-        // wait for the prefetch issued after them); here that wait costs
-        // nothing, and it precedes this head's output stores.
+        // ---- next head's tables (see chunk_scan_bf16_kernel)
         asm volatile("" : "+v"(nsv), "+v"(nse), "+v"(nd));
-        if (more) tab_store((k & 1) ? tab0 : tab1, nsv, nse, nd);
+        if (more) tab_store((k & 1) ? tab0 : tab1, td, nsv, nse, nd);
 
-        // ---- outputs, staged in this head's x buffer and stored as whole rows
-        barrier_lds();  // every wavefront is done reading x(h)
+        // ---- outputs through the x buffer, stored as whole rows
+        barrier_lds();
 #pragma unroll
         for (int ti = 0; ti < 2; ++ti) {
             const int il = ti ? il1 : il0;
@@ -719,14 +1039,14 @@ __global__ __launch_bounds__(Q * 2) void chunk_scan_bf16_kernel(
 #pragma unroll
         for (int kq = 0; kq < XI; ++kq) {
             const int i = kq * NW + w;
-            const int s = i * 64 + l;
+            const int s = i * 64 + ln;
             const int r = s >> 3, q = (s & 7) ^ (r & 7);
             const uint4 v = *reinterpret_cast<const uint4 *>(xs + s * 8);
             if (r < len) *reinterpret_cast<uint4 *>(yh + (size_t)r * xrow + q * 8) = v;
         }
-        if (!DBUF && more) {
-            barrier_lds();  // every wavefront has read its outputs out of x(h)
-            issue_x(h + 1, xb0);
+        if (more) {
+            barrier_lds();  // the outputs have left the x buffer
+            issue_x(hn, ln);
         }
     }
 }
@@ -738,18 +1058,25 @@ static void launch_scan_bf16(const void *x, const void *dt, const float *dA, con
     const int nC = (L + Q - 1) / Q;
     const int hpg = H / G;
     const int nU = batch * nC * G;
+    constexpr bool kPair = PairLds<N, Q>::kFits;
     // resident workgroups per compute unit (LDS-bound), 256 compute units
-    const int per_cu = (int)((160 * 1024) / ScanBf16Lds<N, Q>::kBytes);
+    const size_t lds = kPair ? PairLds<N, Q>::kBytes : ScanBf16Lds<N, Q>::kBytes;
+    const int per_cu = (int)((160 * 1024) / lds);
     const int target = 256 * (per_cu < 1 ? 1 : per_cu);
     int nblk = (target + nU - 1) / nU;
     nblk = nblk < 1 ? 1 : (nblk > hpg ? hpg : nblk);
-    const int hbh = (hpg + nblk - 1) / nblk;
-    nblk = (hpg + hbh - 1) / hbh;
     const dim3 grid((unsigned)(8 * nblk) * (unsigned)((nU + 7) / 8));
-    chunk_scan_bf16_kernel<N, Q><<<grid, Q * 2, 0, stream>>>(
-        static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(dt), dA,
-        static_cast<const bf16_t *>(B), static_cast<const bf16_t *>(C), D,
-        static_cast<const __bf16 *>(Hc), L, H, G, nC, nU, nblk, hbh, static_cast<bf16_t *>(y));
+    if constexpr (kPair) {
+        chunk_scan_bf16_pair_kernel<N, Q><<<grid, Q * 2, 0, stream>>>(
+            static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(dt), dA,
+            static_cast<const bf16_t *>(B), static_cast<const bf16_t *>(C), D,
+            static_cast<const __bf16 *>(Hc), L, H, G, nC, nU, nblk, static_cast<bf16_t *>(y));
+    } else {
+        chunk_scan_bf16_kernel<N, Q><<<grid, Q * 4, 0, stream>>>(
+            static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(dt), dA,
+            static_cast<const bf16_t *>(B), static_cast<const bf16_t *>(C), D,
+            static_cast<const __bf16 *>(Hc), L, H, G, nC, nU, nblk, static_cast<bf16_t *>(y));
+    }
 }
 
 template <typename T, int N, int Q>
