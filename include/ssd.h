@@ -100,8 +100,9 @@ int ssd_forward(const void *x, const void *dt, const float *A, const void *B,
 /*
  * ssd_forward with per-stage timing hooks for profilers and benchmarks.
  * `events` is NULL (then this is exactly ssd_forward) or an array of 6
- * hipEvent_t owned by the caller: events[k] is recorded on `stream` right
- * before stage k+1 is enqueued and events[5] after the last stage, so the
+ * hipEvent_t owned by the caller, any of which may be NULL (not recorded):
+ * events[k] is recorded on `stream` right before stage k+1 is enqueued and
+ * events[5] after the last stage, so the
  * elapsed time between consecutive events is each stage's GPU time (stages in
  * the order listed for ssd_forward; for SSD_BF16 the ssd_chunk_cb interval is
  * empty, that work being part of ssd_chunk_scan).

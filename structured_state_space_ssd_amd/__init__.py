@@ -48,8 +48,9 @@ def forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, return_final_sta
     x [Bt,L,H,P], dt [Bt,L,H], B, C [Bt,L,G,N] (all float32 or all bfloat16),
     A, D [H] float32, init_state [Bt,H,P,N] float32 or None.
     Returns y (and the final state [Bt,H,P,N] float32 if requested).
-    ``events``: optional sequence of 6 recorded-once torch.cuda.Event(enable_timing=True);
-    the library records them around its five stages (see ssd_forward_timed).
+    ``events``: optional sequence of 6 torch.cuda.Event(enable_timing=True) or None;
+    the library records them around its five stages (see ssd_forward_timed),
+    skipping the None entries.
     """
     _req(x, "x")
     dt_ = dtype_code(x.dtype)
@@ -72,11 +73,11 @@ def forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, return_final_sta
     ev = None
     if events is not None:
         if len(events) != 6:
-            raise ValueError("events must hold 6 torch.cuda.Event objects")
+            raise ValueError("events must hold 6 entries (torch.cuda.Event or None)")
         for e in events:
-            if not e.cuda_event:
+            if e is not None and not e.cuda_event:
                 e.record()  # torch creates the HIP event on its first record
-        ev = (ctypes.c_void_p * 6)(*[e.cuda_event for e in events])
+        ev = (ctypes.c_void_p * 6)(*[e.cuda_event if e is not None else None for e in events])
     rc = _native.lib.ssd_forward_timed(
         ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), Bt, L, H, P, G, N, chunk, dt_,
         ptr(init_state), ptr(y), ptr(fs), ptr(workspace), workspace.numel(), stream_handle(x.device),

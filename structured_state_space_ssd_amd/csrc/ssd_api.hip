@@ -178,7 +178,8 @@ int ssd_forward_timed(const void *x, const void *dt, const float *A, const void 
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     auto mark = [&](int k) -> hipError_t {
-        return events ? hipEventRecord(static_cast<hipEvent_t>(events[k]), s) : hipSuccess;
+        return events && events[k] ? hipEventRecord(static_cast<hipEvent_t>(events[k]), s)
+                                   : hipSuccess;
     };
 
     hipError_t e = mark(0);
