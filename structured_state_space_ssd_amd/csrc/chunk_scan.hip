@@ -307,47 +307,6 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_kernel(
 
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// One 16-byte-per-lane global-to-LDS load: lane l's 16 bytes from `src` land
-// at byte lds_base + 16*l (lds_base is the same for the whole wavefront). In
-// inline assembly so that the compiler does not hold later reads of other LDS
-// buffers behind it; completion is awaited explicitly (wait_barrier).
-__device__ __forceinline__ void dma16(const void *src, const void *lds_base) {
-    const uint32_t a =
-        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)lds_base);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(a)
-                 : "memory", "m0");
-}
-
-// This wavefront's LDS operations complete and at most VM of its global
-// memory operations (the most recently issued ones) remain outstanding; then
-// the workgroup meets.
-template <int VM>
-__device__ __forceinline__ void wait_barrier() {
-    static_assert(VM >= 0 && VM < 64, "vmcnt range");
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-// LDS operations complete, global ones stay in flight; then the workgroup meets.
-__device__ __forceinline__ void barrier_lds() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// x tile: token rows of 64 bf16 (eight 16-byte pieces); piece q of row r is
-// stored at piece q ^ (r & 7). A half-wavefront's transposing read covers 8
-// consecutive rows x 2 pieces, which this puts on 16 distinct bank groups.
-__device__ __forceinline__ int x_at(int r, int col) {
-    return r * 64 + ((((col >> 3) ^ r) & 7) << 3) + (col & 7);
-}
-
 // H_c rows of N bf16 (N/8 pieces); piece q of row p is stored at q ^ f(p), f
 // chosen so that one fragment read (16 consecutive rows, one piece) touches
 // distinct bank groups.

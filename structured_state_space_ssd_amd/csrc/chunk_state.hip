@@ -135,14 +135,148 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(
     }
 }
 
+// ---- bf16: a pipeline of global-to-LDS loads over phases of TP tokens ------
+//
+// The same product, S_c = (w o X)^T B over the chunk's tokens, with the chunk
+// streamed through LDS in phases of TP tokens (64, or 32 for N >= 128): while
+// phase k is multiplied, phase k+1's x and B rows are already on their way by
+// direct global-to-LDS loads, so a workgroup keeps memory busy instead of
+// loading everything and then computing. The token weights w_j are applied to
+// the x^T operand fragments (8 multiplies per fragment, shared by the
+// wavefront's N tiles), so x and B land in LDS exactly as stored. Both tiles
+// are read with the transposing LDS read (contraction index = token = row).
+template <int PPR>
+__device__ __forceinline__ void colfrag_swz(Frag<bf16_t> &f, const __bf16 *m, int r1, int r2,
+                                            int cb) {
+    const int s = lane_id() & 15;
+    const int col = cb + 4 * (s & 3);
+    const int ra = r1 + (s >> 2), rb = r2 + (s >> 2);
+    const int pa = ((col >> 3) ^ tr_swz<PPR>(ra)) << 3, pb = ((col >> 3) ^ tr_swz<PPR>(rb)) << 3;
+    const shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_shortx4 *)(m + ra * (PPR * 8) + pa + (col & 7)));
+    const shortx4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_shortx4 *)(m + rb * (PPR * 8) + pb + (col & 7)));
+    const bf16x4 ab = __builtin_bit_cast(bf16x4, a);
+    const bf16x4 bb = __builtin_bit_cast(bf16x4, b);
+    f.v = bf16x8{ab[0], ab[1], ab[2], ab[3], bb[0], bb[1], bb[2], bb[3]};
+}
+
+template <int N, int Q>
+__global__ __launch_bounds__(512) void chunk_state_bf16_kernel(
+    const bf16_t *__restrict__ x, const bf16_t *__restrict__ B, const bf16_t *__restrict__ dt,
+    const float *__restrict__ dA_cumsum, int L, int H, int G, int nC, float *__restrict__ states) {
+    constexpr int P = 64, NW = 8;
+    constexpr int TP = N >= 128 ? 32 : 64;  // tokens per phase
+    constexpr int NPH = Q / TP;
+    constexpr int PPR = N / 8;               // 16-byte pieces per B row
+    constexpr int XSL = TP * 8 / 64;         // x loads per phase (64 pieces each)
+    constexpr int BSL = TP * PPR / 64;       // B loads per phase
+    constexpr int NTW = (N / 16 + 1) / 2;    // N tiles per wavefront
+    __shared__ __attribute__((aligned(16))) __bf16 xs0[TP * P];
+    __shared__ __attribute__((aligned(16))) __bf16 xs1[TP * P];
+    __shared__ __attribute__((aligned(16))) __bf16 bs0[TP * N];
+    __shared__ __attribute__((aligned(16))) __bf16 bs1[TP * N];
+    __shared__ __attribute__((aligned(16))) float wj[Q];
+
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int g = h / (H / G);
+    const int t0 = c * Q, len = min(Q, L - t0);
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = l >> 4;
+    const size_t xrow = (size_t)H * P, brow = (size_t)G * N;
+    const bf16_t *xh = x + ((size_t)b * L + t0) * xrow + (size_t)h * P;
+    const bf16_t *bg = B + ((size_t)b * L + t0) * brow + (size_t)g * N;
+
+    // one phase's x and B rows into buffer pair `ph & 1`: slot s of a load is
+    // row s / PPR (resp. s / 8) at the piece that its swizzle maps there; rows
+    // past the end repeat the last row (their weight w_j is zero)
+    auto issue = [&](int ph) {
+        __bf16 *xd = (ph & 1) ? xs1 : xs0;
+        __bf16 *bd = (ph & 1) ? bs1 : bs0;
+        for (int i = w; i < XSL; i += NW) {
+            const int s = i * 64 + l, r = s >> 3, q = (s & 7) ^ tr_swz<8>(r);
+            dma16(xh + (size_t)min(ph * TP + r, len - 1) * xrow + q * 8, xd + i * 512);
+        }
+        for (int i = w; i < BSL; i += NW) {
+            const int s = i * 64 + l, r = s / PPR, q = (s % PPR) ^ tr_swz<PPR>(r);
+            dma16(bg + (size_t)min(ph * TP + r, len - 1) * brow + q * 8, bd + i * 512);
+        }
+    };
+    issue(0);
+    // token weights w_j = exp(s_end - s_j) dt_j (zero past the end)
+    const float *s = dA_cumsum + ((size_t)b * H + h) * (size_t)nC * Q + (size_t)c * Q;
+    const float s_end = s[len - 1];
+    for (int j = tid; j < Q; j += 512) {
+        float wv = 0.0f;
+        if (j < len)
+            wv = __builtin_amdgcn_exp2f((s_end - s[j]) * kLog2e) *
+                 bf16_to_f32(dt[((size_t)b * L + t0 + j) * H + h]);
+        wj[j] = wv;
+    }
+
+    const int pt = w % 4;
+    floatx4 acc[NTW];
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) acc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ph = 0; ph < NPH; ++ph) {
+        wait_barrier<0>();  // phase ph in LDS; phase ph-1's buffers free
+        if (ph + 1 < NPH) issue(ph + 1);
+        const __bf16 *xsp = (ph & 1) ? xs1 : xs0;
+        const __bf16 *bsp = (ph & 1) ? bs1 : bs0;
+        const int kend = min(TP, len - ph * TP);  // tokens of this phase (<= 0: none)
+#pragma unroll
+        for (int kb = 0; kb < TP; kb += 32) {
+            if (kb < kend) {  // uniform
+                const int jb = kb + 4 * g4;
+                Frag<bf16_t> xf;
+                colfrag_swz<8>(xf, xsp, jb, jb + 16, pt * 16);
+                const floatx4 w0 = *reinterpret_cast<const floatx4 *>(wj + ph * TP + jb);
+                const floatx4 w1 = *reinterpret_cast<const floatx4 *>(wj + ph * TP + jb + 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    xf.set(r, xf.get(r) * w0[r]);
+                    xf.set(4 + r, xf.get(4 + r) * w1[r]);
+                }
+#pragma unroll
+                for (int i = 0; i < NTW; ++i) {
+                    const int nt = w / 4 + 2 * i;
+                    if (nt < N / 16) {
+                        Frag<bf16_t> bf;
+                        colfrag_swz<PPR>(bf, bsp, jb, jb + 16, nt * 16);
+                        mma(acc[i], xf, bf);
+                    }
+                }
+            }
+        }
+    }
+
+    float *dst = states + (((size_t)b * nC + c) * H + h) * (size_t)P * N;
+    const int cc = l & 15;
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+        const int nt = w / 4 + 2 * i;
+        if (nt < N / 16) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[(size_t)(pt * 16 + 4 * g4 + r) * N + nt * 16 + cc] = acc[i][r];
+        }
+    }
+}
+
 template <typename T, int N, int Q>
 static void launch_cs(const void *x, const void *B, const void *dt, const float *dA, int batch,
                       int L, int H, int G, float *states, hipStream_t stream) {
     const int nC = (L + Q - 1) / Q;
     const dim3 grid(nC, H, batch);
-    chunk_state_kernel<T, N, Q><<<grid, 512, 0, stream>>>(
-        static_cast<const T *>(x), static_cast<const T *>(B), static_cast<const T *>(dt), dA, L, H,
-        G, nC, states);
+    if constexpr (sizeof(T) == 2) {
+        chunk_state_bf16_kernel<N, Q><<<grid, 512, 0, stream>>>(
+            static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(B),
+            static_cast<const bf16_t *>(dt), dA, L, H, G, nC, states);
+    } else {
+        chunk_state_kernel<T, N, Q><<<grid, 512, 0, stream>>>(
+            static_cast<const T *>(x), static_cast<const T *>(B), static_cast<const T *>(dt), dA, L,
+            H, G, nC, states);
+    }
 }
 
 template <typename T, int N>

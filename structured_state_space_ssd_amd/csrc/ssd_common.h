@@ -223,4 +223,59 @@ __host__ __device__ constexpr int colfrag_stride(int cols, int bytes) {
     return w * 4 / bytes;
 }
 
+// ---- direct global-to-LDS loads and LDS-only barriers ------------------------
+//
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte-per-lane global-to-LDS load: lane l's 16 bytes from `src` land
+// at byte lds_base + 16*l (lds_base is the same for the whole wavefront). In
+// inline assembly so that the compiler does not hold later reads of other LDS
+// buffers behind it; completion is awaited explicitly (wait_barrier).
+__device__ __forceinline__ void dma16(const void *src, const void *lds_base) {
+    const uint32_t a =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(a)
+                 : "memory", "m0");
+}
+
+// This wavefront's LDS operations complete and at most VM of its global
+// memory operations (the most recently issued ones) remain outstanding; then
+// the workgroup meets.
+template <int VM>
+__device__ __forceinline__ void wait_barrier() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// LDS operations complete, global ones stay in flight; then the workgroup meets.
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// A 64-column bf16 matrix in LDS (a token tile of x: eight 16-byte pieces per
+// 128-byte row); piece q of row r is stored at piece q ^ (r & 7). A half-wavefront's transposing read covers 8
+// consecutive rows x 2 pieces, which this puts on 16 distinct bank groups.
+__device__ __forceinline__ int x_at(int r, int col) {
+    return r * 64 + ((((col >> 3) ^ r) & 7) << 3) + (col & 7);
+}
+
+// Piece swizzle of a bf16 LDS matrix with PPR 16-byte pieces per row that is
+// read with the transposing read (lds_colfrag's pattern: a half-wavefront
+// reads 8 consecutive rows x 2 adjacent pieces): the XOR mask for row r that
+// puts those 16 pieces on distinct banks.
+template <int PPR>
+__device__ __forceinline__ int tr_swz(int r) {
+    if constexpr (PPR <= 2) return 0;
+    else if constexpr (PPR == 4) return ((r >> 2) & 1) << 1;
+    else if constexpr (PPR == 8) return r & 7;
+    else return (r & 7) << 1;
+}
+
 }  // namespace ssd
