@@ -70,13 +70,16 @@ const char *ssd_strerror(int status);
  * Bytes of workspace ssd_forward needs (0 for invalid sizes). The workspace
  * holds, at 256-byte aligned offsets in this order:
  *   dA_cumsum   float32 [Bt][H][nC*Q]      within-chunk prefix sums of dt*A
+ *   delta       float32 [Bt][H][nC*Q]      dt in the same layout (zero past seqlen)
  *   states      float32 [Bt][nC][H][P][N]  each chunk's own state contribution
  *   chunk_init  [Bt][nC][H][P][N]          state entering each chunk, in the MFMA
  *                                          operand type (bf16 for SSD_BF16, else float32)
  *   cb          SSD_F32 only: ssd_chunk_cb_size(...) bytes, C B^T tiles of every
  *               chunk (the SSD_BF16 chunk scan forms them itself; no space)
  * After the forward pass has run, these hold the intermediate results of the
- * stages below (a caller may read them, e.g. to test a stage).
+ * stages below (a caller may read them, e.g. to test a stage), except that
+ * for SSD_BF16 with batch * nheads >= 512 stages 2 and 3 run as one kernel
+ * that keeps the per-chunk states on chip: `states` is then not written.
  */
 size_t ssd_forward_workspace_size(int batch, int seqlen, int nheads, int headdim,
                                   int ngroups, int dstate, int chunk, int dtype);
@@ -130,10 +133,12 @@ int ssd_step(float *state, const void *x, const void *dt, const float *A,
 /*
  * Stage 1: dA_cumsum[b][h][c*Q + k] = sum_{t=cQ..cQ+k} dt[b][t][h] * A[h]
  * (natural-log units; entries past seqlen continue the sum with zero terms).
- * Output float32 [Bt][H][nC*Q].
+ * Output float32 [Bt][H][nC*Q]. `delta` (nullable) receives dt itself in the
+ * same layout, as float32, zero past seqlen: a copy of dt that the later
+ * stages read contiguously per head.
  */
 int ssd_chunk_cumsum(const void *dt, const float *A, int batch, int seqlen, int nheads,
-                     int chunk, int dtype, float *dA_cumsum, void *stream);
+                     int chunk, int dtype, float *dA_cumsum, float *delta, void *stream);
 
 /*
  * Stage 2: each chunk's state contribution from a zero state,

@@ -117,16 +117,22 @@ def _nc(L, Q):
     return (L + Q - 1) // Q
 
 
-def chunk_cumsum(dt, A, chunk, out=None):
-    """dA_cumsum [Bt,H,nC*Q] float32: within-chunk prefix sums of dt*A."""
+def chunk_cumsum(dt, A, chunk, out=None, delta=None, return_delta=False):
+    """dA_cumsum [Bt,H,nC*Q] float32: within-chunk prefix sums of dt*A; with
+    return_delta (or a given ``delta`` buffer), also dt as float32 in the same
+    layout (zero past the end)."""
     _req(dt, "dt")
     Bt, L, H = dt.shape
+    shape = (Bt, H, _nc(L, chunk) * chunk)
     if out is None:
-        out = torch.empty((Bt, H, _nc(L, chunk) * chunk), dtype=torch.float32, device=dt.device)
+        out = torch.empty(shape, dtype=torch.float32, device=dt.device)
+    if delta is None and return_delta:
+        delta = torch.empty(shape, dtype=torch.float32, device=dt.device)
     rc = _native.lib.ssd_chunk_cumsum(ptr(dt), ptr(_req(A, "A", torch.float32)), Bt, L, H, chunk,
-                                      dtype_code(dt.dtype), ptr(out), stream_handle(dt.device))
+                                      dtype_code(dt.dtype), ptr(out),
+                                      ptr(_opt(delta, "delta")), stream_handle(dt.device))
     check(rc, "ssd_chunk_cumsum")
-    return out
+    return (out, delta) if delta is not None else out
 
 
 def chunk_state(x, B, dt, dA_cumsum, chunk, out=None):
@@ -196,10 +202,11 @@ def stages(x, dt, A, B, C, D=None, chunk=256, init_state=None):
     intermediate (dA_cumsum, states, chunk_init, final_state, cb) and y."""
     Bt, L, H, P = x.shape
     N = B.shape[3]
-    s = chunk_cumsum(dt, A, chunk)
+    s, delta = chunk_cumsum(dt, A, chunk, return_delta=True)
     st = chunk_state(x, B, dt, s, chunk)
     fs = torch.empty((Bt, H, P, N), dtype=torch.float32, device=x.device)
     ci = state_passing(st, s, L, chunk, init_state=init_state, final_state=fs, dtype=x.dtype)
     cb = chunk_cb(B, C, chunk)
     y = chunk_scan(x, dt, s, B, C, cb, D, ci, chunk)
-    return {"dA_cumsum": s, "states": st, "chunk_init": ci, "final_state": fs, "cb": cb, "y": y}
+    return {"dA_cumsum": s, "delta": delta, "states": st, "chunk_init": ci, "final_state": fs,
+            "cb": cb, "y": y}

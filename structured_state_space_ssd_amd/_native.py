@@ -29,7 +29,7 @@ SIGNATURES = {
     "ssd_forward": (_i, [_vp] * 6 + [_i] * 8 + [_vp, _vp, _vp, _vp, _sz, _vp]),
     "ssd_forward_timed": (_i, [_vp] * 6 + [_i] * 8 + [_vp, _vp, _vp, _vp, _sz, _vp, _vp]),
     "ssd_step": (_i, [_vp] * 7 + [_i] * 6 + [_vp, _vp]),
-    "ssd_chunk_cumsum": (_i, [_vp, _vp] + [_i] * 5 + [_vp, _vp]),
+    "ssd_chunk_cumsum": (_i, [_vp, _vp] + [_i] * 5 + [_vp, _vp, _vp]),
     "ssd_chunk_state": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _vp]),
     "ssd_state_passing": (_i, [_vp] * 3 + [_i] * 7 + [_vp, _vp, _vp]),
     "ssd_chunk_scan": (_i, [_vp] * 8 + [_i] * 8 + [_vp, _vp]),

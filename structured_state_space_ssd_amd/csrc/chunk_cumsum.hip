@@ -12,7 +12,10 @@
 // them, and the run total, to LDS; one wavefront per head then turns the 16
 // run totals into run offsets. The outputs are written token-fastest: lanes
 // take consecutive tokens of one head, so each store instruction writes 256
-// contiguous bytes of s[b][h][.].
+// contiguous bytes of s[b][h][.]. If requested, dt itself is also written, as
+// float32 in the same chunk-padded [b][h][token] layout (zero past the end),
+// straight from each thread's run (Q/16 consecutive tokens of one head): a
+// copy of dt that later stages can read contiguously per head.
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -25,7 +28,8 @@ template <typename T, int Q>
 __global__ __launch_bounds__(1024) void chunk_cumsum_kernel(const T *__restrict__ dt,
                                                             const float *__restrict__ A, int L,
                                                             int H, int nC,
-                                                            float *__restrict__ out) {
+                                                            float *__restrict__ out,
+                                                            float *__restrict__ delta) {
     constexpr int R = Q / kCumsumRuns;  // tokens per run: 4, 8 or 16
     __shared__ float tile[Q][kCumsumHeads + 1];
     __shared__ float off[kCumsumRuns][kCumsumHeads];
@@ -35,12 +39,19 @@ __global__ __launch_bounds__(1024) void chunk_cumsum_kernel(const T *__restrict_
     const int hc = min(h, H - 1);
     const int t0 = c * Q;
     const float a = h < H ? A[hc] : 0.0f;
-    float v[R];
+    float v[R], dv[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int t = t0 + k * R + r;
         const float d = to_f32(dt[((size_t)b * L + min(t, L - 1)) * H + hc]);
-        v[r] = (h < H && t < L) ? d * a : 0.0f;
+        dv[r] = (h < H && t < L) ? d : 0.0f;
+        v[r] = dv[r] * a;
+    }
+    if (delta && h < H) {
+        float *dd = delta + ((size_t)b * H + h) * ((size_t)nC * Q) + t0 + k * R;
+#pragma unroll
+        for (int r = 0; r < R; r += 4)
+            *reinterpret_cast<float4 *>(dd + r) = make_float4(dv[r], dv[r + 1], dv[r + 2], dv[r + 3]);
     }
 #pragma unroll
     for (int r = 1; r < R; ++r) v[r] += v[r - 1];
@@ -72,12 +83,13 @@ __global__ __launch_bounds__(1024) void chunk_cumsum_kernel(const T *__restrict_
 }
 
 hipError_t launch_chunk_cumsum(const void *dt, const float *A, int batch, int seqlen, int nheads,
-                               int chunk, bool bf16, float *dA_cumsum, hipStream_t stream) {
+                               int chunk, bool bf16, float *dA_cumsum, float *delta,
+                               hipStream_t stream) {
     const int nC = (seqlen + chunk - 1) / chunk;
     const dim3 grid(nC, batch, (nheads + kCumsumHeads - 1) / kCumsumHeads);
 #define SSD_CUMSUM(T, Q)                                                                       \
     chunk_cumsum_kernel<T, Q><<<grid, 1024, 0, stream>>>(static_cast<const T *>(dt), A, seqlen, \
-                                                        nheads, nC, dA_cumsum)
+                                                        nheads, nC, dA_cumsum, delta)
     if (bf16) {
         if (chunk == 64) SSD_CUMSUM(bf16_t, 64);
         else if (chunk == 128) SSD_CUMSUM(bf16_t, 128);

@@ -263,6 +263,214 @@ __global__ __launch_bounds__(512) void chunk_state_bf16_kernel(
     }
 }
 
+// ---- bf16, stages 2 and 3 together: one workgroup per (batch, head) -------
+//
+// The workgroup walks the chunks of its sequence in order. Chunk c's state
+// contribution S_c is formed as above (phases of TP tokens streamed through
+// LDS, the next phase always in flight, across chunk boundaries too), and the
+// running state H_c of stage 3 stays in registers, in float32, in the layout
+// of the MFMA accumulators: H_{c+1} = exp(s_end(c)) H_c + S_c. The state
+// entering each chunk goes out once (in bf16, the operand type of the chunk
+// scan) and the final state in float32; the per-chunk float32 states of the
+// separate stages never exist. The chunk's prefix sums s and dt (the float32
+// copy stage 1 writes) arrive by direct loads too, so nothing inside the loop
+// waits on a global load. Products are formed transposed, S^T[n][p] (B rows as
+// the A operand, weighted x as the B operand): a lane then holds 4
+// consecutive n of one p, which is how the [P][N] state is stored.
+template <int N, int Q>
+__global__ __launch_bounds__(512) void chunk_state_passing_bf16_kernel(
+    const bf16_t *__restrict__ x, const bf16_t *__restrict__ B,
+    const float *__restrict__ dA_cumsum, const float *__restrict__ delta,
+    const float *__restrict__ init, int L, int H, int G, int nC, __bf16 *__restrict__ chunk_init,
+    float *__restrict__ final_state) {
+    constexpr int P = 64, NW = 8;
+    constexpr int TP = N >= 128 ? 32 : 64;  // tokens per phase
+    constexpr int NPH = Q / TP;              // phases per chunk
+    constexpr int PPR = N / 8;
+    constexpr int XSL = TP * 8 / 64;         // x loads per phase
+    constexpr int BSL = TP * PPR / 64;       // B loads per phase
+    constexpr int SQ = Q < 256 ? 256 : Q;    // s / dt buffers hold whole 1 KB loads
+    constexpr int SL = SQ * 4 / 1024;        // loads of one chunk's s (or dt) row
+    constexpr int NTW = (N / 16 + 1) / 2;    // N tiles per wavefront
+    __shared__ __attribute__((aligned(16))) __bf16 xs0[TP * P];
+    __shared__ __attribute__((aligned(16))) __bf16 xs1[TP * P];
+    __shared__ __attribute__((aligned(16))) __bf16 bs0[TP * N];
+    __shared__ __attribute__((aligned(16))) __bf16 bs1[TP * N];
+    __shared__ __attribute__((aligned(16))) float sv0[SQ], sv1[SQ], dv0[SQ], dv1[SQ];
+    __shared__ __attribute__((aligned(16))) float wj[Q];
+
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = l >> 4, cc = l & 15;
+    const size_t xrow = (size_t)H * P, brow = (size_t)G * N;
+    const bf16_t *xh = x + (size_t)b * L * xrow + (size_t)h * P;
+    const bf16_t *bg = B + (size_t)b * L * brow + (size_t)g * N;
+    const size_t srow = ((size_t)b * H + h) * (size_t)nC * Q;  // this head's s / dt rows
+    const int nph = nC * NPH;
+
+    // phase k (chunk k / NPH, tokens from (k % NPH) * TP) into buffer pair k & 1;
+    // a chunk's first phase also brings its s and dt rows (buffer pair c & 1)
+    auto issue = [&](int k) {
+        const int c = k / NPH, t0 = c * Q + (k % NPH) * TP;
+        __bf16 *xd = (k & 1) ? xs1 : xs0;
+        __bf16 *bd = (k & 1) ? bs1 : bs0;
+        for (int i = w; i < XSL; i += NW) {
+            const int s = i * 64 + l, r = s >> 3, q = (s & 7) ^ tr_swz<8>(r);
+            dma16(xh + (size_t)min(t0 + r, L - 1) * xrow + q * 8, xd + i * 512);
+        }
+        for (int i = w; i < BSL; i += NW) {
+            const int s = i * 64 + l, r = s / PPR, q = (s % PPR) ^ tr_swz<PPR>(r);
+            dma16(bg + (size_t)min(t0 + r, L - 1) * brow + q * 8, bd + i * 512);
+        }
+        if (k % NPH == 0 && w < 2 * SL) {
+            const int i = w % SL;  // waves 0..SL-1: s, SL..2SL-1: dt
+            // (for Q < 256 the lanes past the row re-read its last 16 bytes)
+            const float *src = (w < SL ? dA_cumsum : delta) + srow + (size_t)c * Q +
+                               min(i * 256 + l * 4, Q - 4);
+            float *dst = w < SL ? ((c & 1) ? sv1 : sv0) : ((c & 1) ? dv1 : dv0);
+            dma16(src, dst + i * 256);
+        }
+    };
+
+    const int pt = w % 4;
+    floatx4 acc[NTW], hreg[NTW];  // S^T and H^T tiles: lane (g4, cc) rows n = 16nt + 4g4 + r, column p = 16pt + cc
+    issue(0);
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+        const int nt = w / 4 + 2 * i;
+        acc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        hreg[i] = acc[i];
+        if (init && nt < N / 16) {
+            const float4 v = *reinterpret_cast<const float4 *>(
+                init + (((size_t)b * H + h) * P + pt * 16 + cc) * N + nt * 16 + 4 * g4);
+            hreg[i] = floatx4{v.x, v.y, v.z, v.w};
+        }
+    }
+    // H_0 -> chunk_init[b][0][h]
+    auto put_init = [&](int c) {
+        __bf16 *dst = chunk_init + (((size_t)b * nC + c) * H + h) * (size_t)(P * N);
+#pragma unroll
+        for (int i = 0; i < NTW; ++i) {
+            const int nt = w / 4 + 2 * i;
+            if (nt < N / 16) {
+                const bf16x4 v{static_cast<__bf16>(hreg[i][0]), static_cast<__bf16>(hreg[i][1]),
+                               static_cast<__bf16>(hreg[i][2]), static_cast<__bf16>(hreg[i][3])};
+                *reinterpret_cast<bf16x4 *>(dst + (size_t)(pt * 16 + cc) * N + nt * 16 + 4 * g4) = v;
+            }
+        }
+    };
+    put_init(0);
+
+    for (int k = 0; k < nph; ++k) {
+        const int c = k / NPH, kq = k % NPH;
+        wait_barrier<0>();  // phase k (and, at a chunk start, its s and dt) in LDS
+        if (k + 1 < nph) issue(k + 1);
+        if (kq == 0) {
+            // token weights of chunk c: w_j = exp(s_end - s_j) dt_j (dt is zero past the end)
+            const float *svc = (c & 1) ? sv1 : sv0;
+            const float *dvc = (c & 1) ? dv1 : dv0;
+            const float se = svc[Q - 1];  // s is constant past the end
+            for (int j = tid; j < Q; j += 512)
+                wj[j] = __builtin_amdgcn_exp2f((se - svc[j]) * kLog2e) * dvc[j];
+            barrier_lds();
+        }
+        const __bf16 *xsp = (k & 1) ? xs1 : xs0;
+        const __bf16 *bsp = (k & 1) ? bs1 : bs0;
+        const int kend = min(TP, L - (c * Q + kq * TP));  // tokens of this phase
+#pragma unroll
+        for (int kb = 0; kb < TP; kb += 32) {
+            if (kb < kend) {  // uniform
+                const int jb = kb + 4 * g4;
+                Frag<bf16_t> xf;
+                colfrag_swz<8>(xf, xsp, jb, jb + 16, pt * 16);
+                const floatx4 w0 = *reinterpret_cast<const floatx4 *>(wj + kq * TP + jb);
+                const floatx4 w1 = *reinterpret_cast<const floatx4 *>(wj + kq * TP + jb + 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    xf.set(r, xf.get(r) * w0[r]);
+                    xf.set(4 + r, xf.get(4 + r) * w1[r]);
+                }
+#pragma unroll
+                for (int i = 0; i < NTW; ++i) {
+                    const int nt = w / 4 + 2 * i;
+                    if (nt < N / 16) {
+                        Frag<bf16_t> bf;
+                        colfrag_swz<PPR>(bf, bsp, jb, jb + 16, nt * 16);
+                        mma(acc[i], bf, xf);
+                    }
+                }
+            }
+        }
+        if (kq == NPH - 1) {
+            // end of chunk c: H_{c+1} = exp(s_end(c)) H_c + S_c
+            const float dec = __builtin_amdgcn_exp2f(((c & 1) ? sv1 : sv0)[Q - 1] * kLog2e);
+#pragma unroll
+            for (int i = 0; i < NTW; ++i) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) hreg[i][r] = dec * hreg[i][r] + acc[i][r];
+                acc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+            if (c + 1 < nC) put_init(c + 1);
+        }
+    }
+    if (final_state) {
+#pragma unroll
+        for (int i = 0; i < NTW; ++i) {
+            const int nt = w / 4 + 2 * i;
+            if (nt < N / 16)
+                *reinterpret_cast<float4 *>(final_state + (((size_t)b * H + h) * P + pt * 16 + cc) * N +
+                                            nt * 16 + 4 * g4) =
+                    make_float4(hreg[i][0], hreg[i][1], hreg[i][2], hreg[i][3]);
+        }
+    }
+}
+
+template <int N, int Q>
+static void launch_fused(const void *x, const void *B, const float *dA, const float *delta,
+                         const float *init, int batch, int L, int H, int G, void *chunk_init,
+                         float *final_state, hipStream_t stream) {
+    const int nC = (L + Q - 1) / Q;
+    chunk_state_passing_bf16_kernel<N, Q><<<dim3(H, batch), 512, 0, stream>>>(
+        static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(B), dA, delta, init, L, H, G,
+        nC, static_cast<__bf16 *>(chunk_init), final_state);
+}
+
+template <int N>
+static bool fused_q(int Q, const void *x, const void *B, const float *dA, const float *delta,
+                    const float *init, int batch, int L, int H, int G, void *ci, float *fs,
+                    hipStream_t s) {
+    switch (Q) {
+        case 64: launch_fused<N, 64>(x, B, dA, delta, init, batch, L, H, G, ci, fs, s); return true;
+        case 128: launch_fused<N, 128>(x, B, dA, delta, init, batch, L, H, G, ci, fs, s); return true;
+        case 256: launch_fused<N, 256>(x, B, dA, delta, init, batch, L, H, G, ci, fs, s); return true;
+        default: return false;
+    }
+}
+
+bool state_passing_fused(int batch, int nheads, bool bf16) {
+    // one workgroup per (batch, head): worth it once that fills the GPU (two
+    // per compute unit at least); otherwise the separate stages parallelise
+    // over chunks as well
+    return bf16 && batch * nheads >= 512;
+}
+
+hipError_t launch_chunk_state_passing(const void *x, const void *B, const float *dA_cumsum,
+                                      const float *delta, const float *init, int batch,
+                                      int seqlen, int nheads, int ngroups, int dstate, int chunk,
+                                      void *chunk_init, float *final_state, hipStream_t stream) {
+    bool ok = false;
+    switch (dstate) {
+        case 16: ok = fused_q<16>(chunk, x, B, dA_cumsum, delta, init, batch, seqlen, nheads, ngroups, chunk_init, final_state, stream); break;
+        case 32: ok = fused_q<32>(chunk, x, B, dA_cumsum, delta, init, batch, seqlen, nheads, ngroups, chunk_init, final_state, stream); break;
+        case 64: ok = fused_q<64>(chunk, x, B, dA_cumsum, delta, init, batch, seqlen, nheads, ngroups, chunk_init, final_state, stream); break;
+        case 128: ok = fused_q<128>(chunk, x, B, dA_cumsum, delta, init, batch, seqlen, nheads, ngroups, chunk_init, final_state, stream); break;
+        case 256: ok = fused_q<256>(chunk, x, B, dA_cumsum, delta, init, batch, seqlen, nheads, ngroups, chunk_init, final_state, stream); break;
+        default: break;
+    }
+    if (!ok) return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 template <typename T, int N, int Q>
 static void launch_cs(const void *x, const void *B, const void *dt, const float *dA, int batch,
                       int L, int H, int G, float *states, hipStream_t stream) {

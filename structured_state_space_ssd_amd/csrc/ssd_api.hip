@@ -19,7 +19,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool valid_dtype(int d) { return d == SSD_F32 || d == SSD_BF16; }
 
 struct Workspace {
-    size_t cumsum_off, states_off, init_off, cb_off, total;
+    size_t cumsum_off, delta_off, states_off, init_off, cb_off, total;
 };
 
 Workspace layout(int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate, int chunk,
@@ -31,7 +31,8 @@ Workspace layout(int batch, int seqlen, int nheads, int headdim, int ngroups, in
     const size_t ci = elems * (bf16 ? 2 : 4);
     Workspace w;
     w.cumsum_off = 0;
-    w.states_off = align_up(cumsum);
+    w.delta_off = align_up(cumsum);
+    w.states_off = w.delta_off + align_up(cumsum);
     w.init_off = w.states_off + align_up(st);
     w.cb_off = w.init_off + align_up(ci);
     w.total = w.cb_off;
@@ -95,12 +96,13 @@ int ssd_chunk_cb(const void *B, const void *C, int batch, int seqlen, int ngroup
 }
 
 int ssd_chunk_cumsum(const void *dt, const float *A, int batch, int seqlen, int nheads, int chunk,
-                     int dtype, float *dA_cumsum, void *stream) {
+                     int dtype, float *dA_cumsum, float *delta, void *stream) {
     if (!dt || !A || !dA_cumsum) return SSD_ERR_NULL;
     if (batch < 1 || seqlen < 1 || nheads < 1) return SSD_ERR_SHAPE;
     if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    if (delta && (reinterpret_cast<uintptr_t>(delta) & 15u) != 0) return SSD_ERR_UNSUPPORTED;
     return status_of(ssd::launch_chunk_cumsum(dt, A, batch, seqlen, nheads, chunk,
-                                              dtype == SSD_BF16, dA_cumsum,
+                                              dtype == SSD_BF16, dA_cumsum, delta,
                                               static_cast<hipStream_t>(stream)));
 }
 
@@ -171,6 +173,7 @@ int ssd_forward_timed(const void *x, const void *dt, const float *A, const void 
 
     char *base = static_cast<char *>(workspace);
     float *cumsum = reinterpret_cast<float *>(base + ws.cumsum_off);
+    float *delta = reinterpret_cast<float *>(base + ws.delta_off);
     float *states = reinterpret_cast<float *>(base + ws.states_off);
     void *cinit = base + ws.init_off;
     void *cb = base + ws.cb_off;
@@ -184,15 +187,24 @@ int ssd_forward_timed(const void *x, const void *dt, const float *A, const void 
 
     hipError_t e = mark(0);
     if (e == hipSuccess)
-        e = ssd::launch_chunk_cumsum(dt, A, batch, seqlen, nheads, chunk, bf16, cumsum, s);
+        e = ssd::launch_chunk_cumsum(dt, A, batch, seqlen, nheads, chunk, bf16, cumsum, delta, s);
     if (e == hipSuccess) e = mark(1);
-    if (e == hipSuccess)
-        e = ssd::launch_chunk_state(x, B, dt, cumsum, batch, seqlen, nheads, ngroups, dstate, chunk,
-                                    bf16, states, s);
-    if (e == hipSuccess) e = mark(2);
-    if (e == hipSuccess)
-        e = ssd::launch_state_passing(states, cumsum, init_state, batch, seqlen, nheads, dstate,
-                                      chunk, bf16, cinit, final_state, s);
+    if (ssd::state_passing_fused(batch, nheads, bf16)) {
+        // stages 2 and 3 in one kernel; the state_passing interval stays empty
+        if (e == hipSuccess)
+            e = ssd::launch_chunk_state_passing(x, B, cumsum, delta, init_state, batch, seqlen,
+                                                nheads, ngroups, dstate, chunk, cinit,
+                                                final_state, s);
+        if (e == hipSuccess) e = mark(2);
+    } else {
+        if (e == hipSuccess)
+            e = ssd::launch_chunk_state(x, B, dt, cumsum, batch, seqlen, nheads, ngroups, dstate,
+                                        chunk, bf16, states, s);
+        if (e == hipSuccess) e = mark(2);
+        if (e == hipSuccess)
+            e = ssd::launch_state_passing(states, cumsum, init_state, batch, seqlen, nheads, dstate,
+                                          chunk, bf16, cinit, final_state, s);
+    }
     if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess && ssd::chunk_scan_reads_cb(bf16))
         e = ssd::launch_chunk_cb(B, C, batch, seqlen, ngroups, dstate, chunk, bf16, cb, s);

@@ -8,12 +8,23 @@
 
 namespace ssd {
 
+// delta (nullable): dt as float32 in dA_cumsum's chunk-padded layout.
 hipError_t launch_chunk_cumsum(const void *dt, const float *A, int batch, int seqlen, int nheads,
-                               int chunk, bool bf16, float *dA_cumsum, hipStream_t stream);
+                               int chunk, bool bf16, float *dA_cumsum, float *delta,
+                               hipStream_t stream);
 
 hipError_t launch_chunk_state(const void *x, const void *B, const void *dt, const float *dA_cumsum,
                               int batch, int seqlen, int nheads, int ngroups, int dstate, int chunk,
                               bool bf16, float *states, hipStream_t stream);
+
+// Stages 2 and 3 in one kernel (bf16 only; used when state_passing_fused()):
+// writes chunk_init (bf16) and final_state (nullable) directly, without the
+// per-chunk float32 states. Reads dA_cumsum and delta (stage 1's outputs).
+bool state_passing_fused(int batch, int nheads, bool bf16);
+hipError_t launch_chunk_state_passing(const void *x, const void *B, const float *dA_cumsum,
+                                      const float *delta, const float *init, int batch,
+                                      int seqlen, int nheads, int ngroups, int dstate, int chunk,
+                                      void *chunk_init, float *final_state, hipStream_t stream);
 
 // chunk_init is written in the MFMA operand type of the forward's dtype
 // (bf16 when bf16 is true, else float32).

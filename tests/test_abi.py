@@ -58,12 +58,12 @@ def _cb_expected(Bt, L, G, Q, dtype):
 def _ws_expected(Bt, L, H, P, G, N, Q, dtype):
     al = lambda v: (v + 255) // 256 * 256
     nC = -(-L // Q)
-    cs = Bt * H * nC * Q * 4
+    cs = Bt * H * nC * Q * 4  # dA_cumsum, and the same again for delta
     st = Bt * nC * H * P * N * 4
     ci = Bt * nC * H * P * N * (2 if dtype == 1 else 4)
     # the C B^T scratch is needed by the float path only (bf16 forms the tiles on chip)
     cb = al(_cb_expected(Bt, L, G, Q, dtype)) if dtype == 0 else 0
-    return al(cs) + al(st) + al(ci) + cb
+    return al(cs) + al(cs) + al(st) + al(ci) + cb
 
 
 @pytest.mark.parametrize("dims", [(8, 2048, 80, 64, 1, 64, 256, 1), (1, 65536, 80, 64, 8, 128, 256, 1),
@@ -128,8 +128,10 @@ def test_step_rejects(lib):
 
 
 def test_stage_entry_points_reject(lib):
-    assert lib.ssd_chunk_cumsum(None, FAKE, 1, 10, 2, 64, 1, FAKE, None) == SSD_ERR_NULL
-    assert lib.ssd_chunk_cumsum(FAKE, FAKE, 1, 10, 2, 100, 1, FAKE, None) == SSD_ERR_UNSUPPORTED
+    assert lib.ssd_chunk_cumsum(None, FAKE, 1, 10, 2, 64, 1, FAKE, None, None) == SSD_ERR_NULL
+    assert lib.ssd_chunk_cumsum(FAKE, FAKE, 1, 10, 2, 100, 1, FAKE, None, None) == SSD_ERR_UNSUPPORTED
+    assert lib.ssd_chunk_cumsum(FAKE, FAKE, 1, 10, 2, 64, 1, FAKE, ctypes.c_void_p(0x100004),
+                                None) == SSD_ERR_UNSUPPORTED  # misaligned delta
     assert lib.ssd_chunk_state(FAKE, FAKE, FAKE, FAKE, 1, 10, 3, 64, 2, 64, 64, 1, FAKE, None) == SSD_ERR_SHAPE
     assert lib.ssd_state_passing(FAKE, FAKE, None, 1, 10, 2, 64, 64, 64, 1, None, None, None) == SSD_ERR_NULL
     assert lib.ssd_state_passing(FAKE, FAKE, None, 1, 10, 2, 64, 64, 64, 4, FAKE, None, None) == SSD_ERR_UNSUPPORTED

@@ -142,3 +142,24 @@ def test_strong_decay_and_large_dt():
 
 def test_slow_decay_long():
     check_forward(W.small("slow", 1, 4096, 4, 64, 1, 64, 128, "f32", seed=303, dt_lo=1e-5, dt_hi=1e-4))
+
+
+# ------------------------------------------------- fused stages 2 + 3 (bf16, Bt*H >= 512)
+#
+# With enough (batch, head) units the bf16 forward runs the chunk states and
+# the state passing as one kernel per (batch, head); these cases reach it at
+# sizes the oracle finishes quickly, with ragged ends, an initial state,
+# several groups and every state size and chunk length.
+
+@pytest.mark.parametrize("N,Q", [(16, 64), (32, 128), (64, 256), (128, 128), (256, 64), (64, 64),
+                                 (128, 256)])
+def test_fused_state_path(N, Q):
+    w = W.small(f"fused_N{N}_Q{Q}", 8, 2 * Q + 45, 64, 64, 4, N, Q, "bf16",
+                seed=600 + N + Q, init_std=0.2)
+    assert w.batch * w.nheads >= 512
+    check_forward(w)
+
+
+def test_fused_state_path_single_chunk_short():
+    # one partial chunk only: the state passing reduces to H_1 = exp(s_end) H_0 + S_0
+    check_forward(W.small("fused_short", 16, 37, 32, 64, 1, 64, 256, "bf16", seed=620, init_std=0.3))

@@ -49,6 +49,12 @@ def test_stage_chunk_cumsum(w):
     ref = oracle.chunk_cumsum(d["dt"].val, d["A"], w.chunk)
     # fp32 prefix sums of at most Q terms: relative error well below 1e-5
     assert rel_l2(s, ref) < 1e-5
+    # the float32 copy of dt: exact, zero past the end
+    dl = down(out["delta"])
+    Lp = w.nchunks * w.chunk
+    want = np.zeros((w.batch, w.nheads, Lp))
+    want[:, :, : w.seqlen] = d["dt"].val.astype(np.float64).transpose(0, 2, 1)
+    assert np.array_equal(dl, want)
 
 
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
