@@ -75,14 +75,32 @@ def accounting(w):
     else:
         cb_stage = {"bytes": 2 * bc + cb, "flops": cb_flops}
         scan = {"bytes": x + x + dt + s + bc + cb + ci + H * 4, "flops": scan_flops}
+    # stage 1 writes dA_cumsum and the float32 copy of dt (delta), same size
+    cumsum = {"bytes": dt + H * 4 + 2 * s, "flops": tok * H * 2}
+    state = {"bytes": x + bc + dt + s + st, "flops": tok * H * 2 * P * N}
+    passing = {"bytes": st + ci + send, "flops": Bt * nC * H * P * N * 2}
+    if fused_state_path(w):
+        # one kernel for stages 2 and 3 (the library's rule): reads x, B, s and
+        # delta, writes chunk_init and the final state; no per-chunk states
+        fin = Bt * H * P * N * 4
+        state = {"bytes": x + bc + 2 * s + ci + fin,
+                 "flops": state["flops"] + passing["flops"]}
+        passing = {"bytes": 0, "flops": 0}
     acc = {
-        "chunk_cumsum": {"bytes": dt + H * 4 + s, "flops": tok * H * 2},
-        "chunk_state": {"bytes": x + bc + dt + s + st, "flops": tok * H * 2 * P * N},
-        "state_passing": {"bytes": st + ci + send, "flops": Bt * nC * H * P * N * 2},
+        "chunk_cumsum": cumsum,
+        "chunk_state": state,
+        "state_passing": passing,
         "chunk_cb": cb_stage,
         "chunk_scan": scan,
     }
     return acc
+
+
+def fused_state_path(w):
+    """Whether the library runs stages 2 and 3 as one kernel for this workload
+    (bf16 with batch * nheads >= 512; mirrors state_passing_fused in the
+    library's chunk_state.hip)."""
+    return w.dtype == "bf16" and w.batch * w.nheads >= 512
 
 
 def decode_accounting(w):
@@ -215,6 +233,27 @@ def time_decode(w, warmup=3):
     torch.cuda.synchronize()
     per = [ev[t].elapsed_time(ev[t + 1]) for t in range(w.seqlen)]
     return {"mean_ms": sum(per) / len(per), "min_ms": min(per), "max_ms": max(per)}
+
+
+def hbm_probe(nbytes=1 << 30, reps=5):
+    """A plain 1 GiB device-to-device copy (torch), larger than the 256 MB
+    Infinity Cache, timed with events: the bandwidth a simple streaming kernel
+    reaches on this machine, reported beside the 8 TB/s peak as context."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"copy_bytes": nbytes, "us": round(ms * 1e3, 1),
+            "read_plus_write_GB_s": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
 def cpu_baseline(w, min_seconds=1.5):
@@ -468,6 +507,10 @@ def main():
               "tokens_per_s": round(wd.batch / (dec["mean_ms"] * 1e-3))}
     print(f"[bench] decode {decode['us_per_step']} us/step, {decode['GB_s']} GB/s", file=sys.stderr, flush=True)
 
+    probe = hbm_probe()
+    print(f"[bench] 1 GiB device copy: {probe['read_plus_write_GB_s']} GB/s (read + write)",
+          file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu:
         print("[bench] cpu baseline (fp64 oracle)...", file=sys.stderr, flush=True)
@@ -495,6 +538,7 @@ def main():
         "evented_us_per_step": round(fwd["evented_ms"] * 1e3, 2),
         "kernels": kernels,
         "decode": decode,
+        "hbm_copy_probe": probe,
     }
     if extra:
         out["other_workloads"] = extra
