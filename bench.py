@@ -307,9 +307,12 @@ FETCH_CMD = ('rocprofv3 --pmc FETCH_SIZE --output-format csv -d "$OUT/fetch" -o 
              '-- python bench.py --counters')
 WRITE_CMD = ('rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/write" -o write '
              '-- python bench.py --counters')
-KERNEL_OF = {"chunk_cumsum_kernel": "chunk_cumsum", "chunk_state_kernel": "chunk_state",
-             "state_passing_kernel": "state_passing", "chunk_cb_kernel": "chunk_cb",
-             "chunk_scan": "chunk_scan", "decode_step_kernel": "decode_step"}
+# kernel-name fragment -> stage, first match wins (the fused stage-2+3 kernel
+# fills the chunk_state interval of the forward)
+KERNEL_OF = {"chunk_cumsum_kernel": "chunk_cumsum", "chunk_state_passing": "chunk_state",
+             "state_passing_kernel": "state_passing", "chunk_state": "chunk_state",
+             "chunk_cb_kernel": "chunk_cb", "chunk_scan": "chunk_scan",
+             "decode_step_kernel": "decode_step"}
 CALIBRATION_KERNEL = "__amd_rocclr_copyBuffer"  # the 1 GiB device copy of --counters
 COPY_BYTES = 1 << 30
 
