@@ -14,6 +14,13 @@ Contents
   an independent O(L^2) computation used to pin the recurrence.
 * ``chunk_cumsum``: the within-chunk inclusive prefix sum of dt*A, the first
   step of the block decomposition ("Mamba 模型", section 4.1).
+
+Options (``forward``, ``step``): ``dt_bias`` [H] is added to the raw dt,
+``dt_softplus`` applies log(1 + e^v) (the "从Transformer到Mamba" tutorial,
+section 3.2, makes the step size positive this way), ``dt_limit = (lo, hi)``
+clamps the result (the tutorial's section 8.2 adjusts the step-size range),
+and ``zoh`` replaces the Euler input weight dt by the zero-order-hold weight
+(exp(dt A) - 1) / A (tutorial section 2.2; "Mamba 模型" section 2.3.1).
 """
 from __future__ import annotations
 
@@ -45,6 +52,24 @@ def build(force: bool = True, src: str = SRC_PATH, out: str = LIB_PATH) -> str:
 _libs = {}
 
 
+class _Opts(ctypes.Structure):
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int),
+                ("dt_clamp", ctypes.c_int), ("dt_min", ctypes.c_double),
+                ("dt_max", ctypes.c_double), ("zoh", ctypes.c_int)]
+
+
+def _opts(H, dt_bias, dt_softplus, dt_limit, zoh):
+    """(struct, keep-alive arrays) for the C options, or (None, None) when all are off."""
+    if dt_bias is None and not dt_softplus and dt_limit is None and not zoh:
+        return None, None
+    bias = None if dt_bias is None else _f32(dt_bias)
+    assert bias is None or bias.shape == (H,)
+    lo, hi = (0.0, 0.0) if dt_limit is None else (float(dt_limit[0]), float(dt_limit[1]))
+    o = _Opts(_ptr(bias), int(bool(dt_softplus)), int(dt_limit is not None), lo, hi,
+              int(bool(zoh)))
+    return o, bias
+
+
 def _load(path=None):
     """Load the oracle library (default: the built one; ``path`` loads another
     build of the same source, e.g. one compiled with a planted mistake)."""
@@ -54,10 +79,11 @@ def _load(path=None):
             build()
         lib = ctypes.CDLL(path)
         fp, ip, dp = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
-        lib.ssd_oracle_forward.argtypes = [fp] * 7 + [ip] * 6 + [fp, ip, dp, dp, dp, ip, ip]
-        lib.ssd_oracle_forward.restype = ctypes.c_int
-        lib.ssd_oracle_step.argtypes = [dp] + [fp] * 6 + [ip] * 5 + [fp, ip, dp, ip]
-        lib.ssd_oracle_step.restype = ctypes.c_int
+        op = ctypes.POINTER(_Opts)
+        lib.ssd_oracle_forward_ex.argtypes = [fp] * 7 + [ip] * 6 + [fp, ip, dp, dp, dp, ip, ip, op]
+        lib.ssd_oracle_forward_ex.restype = ctypes.c_int
+        lib.ssd_oracle_step_ex.argtypes = [dp] + [fp] * 6 + [ip] * 5 + [fp, ip, dp, ip, op]
+        lib.ssd_oracle_step_ex.restype = ctypes.c_int
         _libs[path] = lib
     return _libs[path]
 
@@ -81,13 +107,15 @@ def _ptr(a):
 
 
 def forward(x, dt, A, B, C, D=None, init=None, units=None, snap_every=0,
-            want_state=True, nthreads=None, lib=None):
+            want_state=True, nthreads=None, lib=None, dt_bias=None, dt_softplus=False,
+            dt_limit=None, zoh=False):
     """Run the recurrence.
 
     Shapes: x [Bt,L,H,P], dt [Bt,L,H], B, C [Bt,L,G,N], A, D [H],
     init [Bt,H,P,N] (float64) or None. ``units`` lists flat b*H+h indices (default all).
     Returns (y [U,L,P], final state [U,P,N] or None, snapshots or None), float64.
     Snapshots hold the state after tokens snap_every-1, 2*snap_every-1, ...
+    The dt options and ``zoh`` are described in the module docstring.
     """
     x, dt, A, B, C, D = map(_f32, (x, dt, A, B, C, D))
     init = None if init is None else np.ascontiguousarray(init, dtype=np.float64)
@@ -105,19 +133,23 @@ def forward(x, dt, A, B, C, D=None, init=None, units=None, snap_every=0,
     st = np.empty((U, P, N), dtype=np.float64) if want_state else None
     nsnap = L // snap_every if snap_every > 0 else 0
     snaps = np.empty((U, nsnap, P, N), dtype=np.float64) if nsnap else None
-    rc = _load(lib).ssd_oracle_forward(
+    o, _keep = _opts(H, dt_bias, dt_softplus, dt_limit, zoh)
+    rc = _load(lib).ssd_oracle_forward_ex(
         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init),
         Bt, L, H, P, G, N, _ptr(units_arr), U, _ptr(y), _ptr(st), _ptr(snaps),
-        snap_every if nsnap else 0, nthreads or default_threads())
+        snap_every if nsnap else 0, nthreads or default_threads(),
+        None if o is None else ctypes.byref(o))
     if rc != 0:
         raise RuntimeError(f"ssd_oracle_forward failed: {rc}")
     return y, st, snaps
 
 
-def step(state, x, dt, A, B, C, D=None, units=None, nthreads=None, lib=None):
+def step(state, x, dt, A, B, C, D=None, units=None, nthreads=None, lib=None,
+         dt_bias=None, dt_softplus=False, dt_limit=None, zoh=False):
     """One recurrent step. ``state`` [U,P,N] float64 is updated in place.
 
     x [Bt,H,P], dt [Bt,H], B, C [Bt,G,N]. Returns y [U,P] float64.
+    The dt options and ``zoh`` are those of ``forward``.
     """
     x, dt, A, B, C, D = map(_f32, (x, dt, A, B, C, D))
     Bt, H, P = x.shape
@@ -130,16 +162,21 @@ def step(state, x, dt, A, B, C, D=None, units=None, nthreads=None, lib=None):
         U = units_arr.size
     assert state.shape == (U, P, N)
     y = np.empty((U, P), dtype=np.float64)
-    rc = _load(lib).ssd_oracle_step(
+    o, _keep = _opts(H, dt_bias, dt_softplus, dt_limit, zoh)
+    rc = _load(lib).ssd_oracle_step_ex(
         _ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-        Bt, H, P, G, N, _ptr(units_arr), U, _ptr(y), nthreads or default_threads())
+        Bt, H, P, G, N, _ptr(units_arr), U, _ptr(y), nthreads or default_threads(),
+        None if o is None else ctypes.byref(o))
     if rc != 0:
         raise RuntimeError(f"ssd_oracle_step failed: {rc}")
     return y
 
 
-def quadratic(x, dt, A, B, C, D=None, init=None):
+def quadratic(x, dt, A, B, C, D=None, init=None, weights=None):
     """Dual quadratic form, O(L^2) per (batch, head); small inputs only.
+
+    ``weights`` [Bt,L,H] replaces dt as the weight of the input term below
+    (the decay still uses dt); None means the weights are dt.
 
     For each (b, h) with group g = h // (H // G):
       a_k  = dt_k A_h,  cs_i = sum_{k<=i} a_k
@@ -153,6 +190,7 @@ def quadratic(x, dt, A, B, C, D=None, init=None):
     A = np.asarray(A, np.float64)
     B = np.asarray(B, np.float64)
     C = np.asarray(C, np.float64)
+    wt = dt if weights is None else np.asarray(weights, np.float64)
     Bt, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     y = np.zeros((Bt, L, H, P))
@@ -165,9 +203,9 @@ def quadratic(x, dt, A, B, C, D=None, init=None):
             cs = np.cumsum(dt[b, :, h] * A[h])
             Lmat = np.where(causal, np.exp(np.where(causal, cs[:, None] - cs[None, :], 0.0)), 0.0)
             M = Lmat * (C[b, :, g, :] @ B[b, :, g, :].T)
-            u = dt[b, :, h, None] * x[b, :, h, :]
+            u = wt[b, :, h, None] * x[b, :, h, :]
             y[b, :, h, :] = M @ u
-            w = np.exp(cs[-1] - cs) * dt[b, :, h]
+            w = np.exp(cs[-1] - cs) * wt[b, :, h]
             hf[b, h] = (x[b, :, h, :] * w[:, None]).T @ B[b, :, g, :]
             if D is not None:
                 y[b, :, h, :] += float(D[h]) * x[b, :, h, :]

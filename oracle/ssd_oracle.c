@@ -22,7 +22,16 @@
  *     section 3.2: dt, B and C are per token, A is shared (one scalar per
  *     head here, as in the Mamba-2 "Draft:Mamba2" page's SSD section).
  *   - The input is scaled by dt (Bbar = dt * B), the Euler form the layer is
- *     defined with; the tutorial's zero-order-hold Bbar is not used.
+ *     defined with. Optionally (the _ex entry points) the input weight is the
+ *     zero-order hold of the tutorial's section 2.2 and "Mamba 模型" section
+ *     2.3.1, Bbar = (dA)^-1 (exp(dA) - 1) dB, which for a scalar A is
+ *     (exp(dt A) - 1) / A * B (and dt * B at A = 0).
+ *   - Optionally dt is preprocessed. The tutorial's section 3.2 makes the
+ *     step size a linear projection of the input made positive by softplus
+ *     (log(1 + e^v)); the projection's constant term is taken as a per-head
+ *     bias added before softplus. Its section 8.2 speaks of adjusting the
+ *     range the step sizes are produced in; that is read as an optional clamp
+ *     to [dt_min, dt_max] after softplus.
  * The state is stored transposed to the usual N x P: hs[p][n], n fastest.
  *
  * All token inputs arrive as float32 arrays holding the exact values the GPU
@@ -38,6 +47,33 @@
 #include <stdlib.h>
 #include <string.h>
 
+/* Preprocessing of dt and the input discretisation (all off when NULL). */
+typedef struct {
+    const float *dt_bias; /* [nheads] or NULL: added to dt first */
+    int dt_softplus;      /* nonzero: dt <- log(1 + exp(dt)) */
+    int dt_clamp;         /* nonzero: dt <- min(max(dt, dt_min), dt_max) */
+    double dt_min, dt_max;
+    int zoh;              /* nonzero: input weight (exp(dt A) - 1) / A instead of dt */
+} oracle_opts;
+
+/* The step size the recurrence uses for raw dt value v of head h. */
+static double step_size(const oracle_opts *o, double v, int h)
+{
+    if (!o) return v;
+    if (o->dt_bias) v += (double)o->dt_bias[h];
+    if (o->dt_softplus) v = fmax(v, 0.0) + log1p(exp(-fabs(v))); /* log(1 + e^v), no overflow */
+    if (o->dt_clamp) v = fmin(fmax(v, o->dt_min), o->dt_max);
+    return v;
+}
+
+/* The weight of the input term for step size d: dt (Euler) or the zero-order
+ * hold (exp(d A) - 1) / A, with expm1 so that small d A keeps its digits. */
+static double input_weight(const oracle_opts *o, double d, double A)
+{
+    if (o && o->zoh) return A != 0.0 ? expm1(d * A) / A : d;
+    return d;
+}
+
 typedef struct {
     const float *x, *dt, *A, *B, *C, *D;
     const double *init;
@@ -48,6 +84,7 @@ typedef struct {
     double *state;  /* [nunits][headdim][dstate] final state (may be NULL) */
     double *snaps;  /* [nunits][seqlen/snap_every][headdim][dstate] (may be NULL) */
     int snap_every;
+    const oracle_opts *opts;
     atomic_int next;
 } fwd_job;
 
@@ -72,14 +109,15 @@ static void fwd_unit(fwd_job *j, int u, double *hs)
     int nsnap = 0;
     for (int t = 0; t < L; ++t) {
         const size_t tok = (size_t)b * L + t;
-        const double d = j->dt[tok * H + h];
+        const double d = step_size(j->opts, j->dt[tok * H + h], h);
         const double a = exp(d * A);
+        const double wi = input_weight(j->opts, d, A);
         const float *xt = j->x + (tok * H + h) * P;
         const float *Bt = j->B + (tok * G + g) * N;
         const float *Ct = j->C + (tok * G + g) * N;
         for (int p = 0; p < P; ++p) {
             double *row = hs + (size_t)p * N;
-            const double dx = d * (double)xt[p];
+            const double dx = wi * (double)xt[p];
             double acc = 0.0;
             for (int n = 0; n < N; ++n) {
                 row[n] = a * row[n] + dx * (double)Bt[n];
@@ -140,11 +178,11 @@ static int run_threads(void *(*fn)(void *), void *job, int nthreads, int nunits)
  *   snaps: the state after every snap_every-th token (may be NULL).
  * Returns 0, or a negative value on bad arguments / allocation failure.
  */
-int ssd_oracle_forward(const float *x, const float *dt, const float *A, const float *B,
-                       const float *C, const float *D, const double *init,
-                       int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate,
-                       const int *units, int nunits, double *y, double *state,
-                       double *snaps, int snap_every, int nthreads)
+int ssd_oracle_forward_ex(const float *x, const float *dt, const float *A, const float *B,
+                          const float *C, const float *D, const double *init,
+                          int batch, int seqlen, int nheads, int headdim, int ngroups,
+                          int dstate, const int *units, int nunits, double *y, double *state,
+                          double *snaps, int snap_every, int nthreads, const oracle_opts *opts)
 {
     if (!x || !dt || !A || !B || !C) return -1;
     if (batch < 1 || seqlen < 0 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1) return -2;
@@ -155,9 +193,21 @@ int ssd_oracle_forward(const float *x, const float *dt, const float *A, const fl
         if (units[u] < 0 || units[u] >= batch * nheads) return -2;
     if (nunits == 0) return 0;
     fwd_job j = {x, dt, A, B, C, D, init, batch, seqlen, nheads, headdim, ngroups, dstate,
-                 units, nunits, y, state, snaps, snap_every, 0};
+                 units, nunits, y, state, snaps, snap_every, opts, 0};
     atomic_init(&j.next, 0);
     return run_threads(fwd_worker, &j, nthreads, nunits);
+}
+
+/* The plain layer: Euler input weight, dt used as given. */
+int ssd_oracle_forward(const float *x, const float *dt, const float *A, const float *B,
+                       const float *C, const float *D, const double *init,
+                       int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate,
+                       const int *units, int nunits, double *y, double *state,
+                       double *snaps, int snap_every, int nthreads)
+{
+    return ssd_oracle_forward_ex(x, dt, A, B, C, D, init, batch, seqlen, nheads, headdim,
+                                 ngroups, dstate, units, nunits, y, state, snaps, snap_every,
+                                 nthreads, NULL);
 }
 
 typedef struct {
@@ -167,6 +217,7 @@ typedef struct {
     const int *units;
     int nunits;
     double *y;      /* [nunits][headdim] */
+    const oracle_opts *opts;
     atomic_int next;
 } step_job;
 
@@ -179,8 +230,9 @@ static void *step_worker(void *arg)
         if (u >= j->nunits) break;
         const int bh = j->units ? j->units[u] : u;
         const int b = bh / H, h = bh % H, g = h / (H / G);
-        const double d = j->dt[bh];
+        const double d = step_size(j->opts, j->dt[bh], h);
         const double a = exp(d * (double)j->A[h]);
+        const double wi = input_weight(j->opts, d, (double)j->A[h]);
         const double D = j->D ? j->D[h] : 0.0;
         const float *xt = j->x + (size_t)bh * P;
         const float *Bt = j->B + ((size_t)b * G + g) * N;
@@ -188,7 +240,7 @@ static void *step_worker(void *arg)
         double *hs = j->state + (size_t)u * P * N;
         for (int p = 0; p < P; ++p) {
             double *row = hs + (size_t)p * N;
-            const double dx = d * (double)xt[p];
+            const double dx = wi * (double)xt[p];
             double acc = 0.0;
             for (int n = 0; n < N; ++n) {
                 row[n] = a * row[n] + dx * (double)Bt[n];
@@ -207,10 +259,11 @@ static void *step_worker(void *arg)
  *   x [batch][nheads][headdim], dt [batch][nheads], B, C [batch][ngroups][dstate],
  *   y [nunits][headdim].
  */
-int ssd_oracle_step(double *state, const float *x, const float *dt, const float *A,
-                    const float *B, const float *C, const float *D,
-                    int batch, int nheads, int headdim, int ngroups, int dstate,
-                    const int *units, int nunits, double *y, int nthreads)
+int ssd_oracle_step_ex(double *state, const float *x, const float *dt, const float *A,
+                       const float *B, const float *C, const float *D,
+                       int batch, int nheads, int headdim, int ngroups, int dstate,
+                       const int *units, int nunits, double *y, int nthreads,
+                       const oracle_opts *opts)
 {
     if (!state || !x || !dt || !A || !B || !C || !y) return -1;
     if (batch < 1 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1) return -2;
@@ -220,7 +273,16 @@ int ssd_oracle_step(double *state, const float *x, const float *dt, const float 
         if (units[u] < 0 || units[u] >= batch * nheads) return -2;
     if (nunits <= 0) return 0;
     step_job j = {state, x, dt, A, B, C, D, batch, nheads, headdim, ngroups, dstate,
-                  units, nunits, y, 0};
+                  units, nunits, y, opts, 0};
     atomic_init(&j.next, 0);
     return run_threads(step_worker, &j, nthreads, nunits);
+}
+
+int ssd_oracle_step(double *state, const float *x, const float *dt, const float *A,
+                    const float *B, const float *C, const float *D,
+                    int batch, int nheads, int headdim, int ngroups, int dstate,
+                    const int *units, int nunits, double *y, int nthreads)
+{
+    return ssd_oracle_step_ex(state, x, dt, A, B, C, D, batch, nheads, headdim, ngroups, dstate,
+                              units, nunits, y, nthreads, NULL);
 }

@@ -242,5 +242,155 @@ def pin_golden(lib=None):
     assert np.allclose(st[0], np.array(g["final_state"]), rtol=1e-7, atol=1e-7)
 
 
+def _dyadic(rng, shape, lo, hi, denom):
+    """float32 values k / denom, k uniform in [lo*denom, hi*denom]: sums of two
+    such values are exact in float32."""
+    return (rng.integers(int(lo * denom), int(hi * denom) + 1, size=shape) / denom).astype(np.float32)
+
+
+def pin_dt_bias(lib=None):
+    """P11: the per-head bias is added to the raw step size before anything
+    else (the constant term of the step-size projection of the
+    "从Transformer到Mamba" tutorial, section 3.2). With dyadic values the
+    sum is exact, so forward(dt, bias) must equal forward(dt + bias)
+    bit for bit, for the forward and for the recurrent step."""
+    w = W.small("p11", 2, 13, 4, 3, 2, 5, 8, "f32", seed=21, init_std=0.4)
+    v = _vals(w)
+    rng = np.random.default_rng(21)
+    raw = _dyadic(rng, v["dt"].shape, -0.1, 0.1, 256)
+    bias = _dyadic(rng, (4,), 0.11, 0.4, 256)
+    shifted = (raw + bias[None, None, :]).astype(np.float32)
+    assert np.array_equal(shifted.astype(np.float64), raw.astype(np.float64) + bias)
+    args = (v["A"], v["B"], v["C"], v["D"], v["init"])
+    y0, s0, _ = oracle.forward(v["x"], raw, *args, dt_bias=bias, lib=lib)
+    y1, s1, _ = oracle.forward(v["x"], shifted, *args, lib=lib)
+    assert np.array_equal(y0, y1) and np.array_equal(s0, s1)
+    st_a = np.ascontiguousarray(v["init"].reshape(8, 3, 5).astype(np.float64))
+    st_b = st_a.copy()
+    ya = oracle.step(st_a, v["x"][:, 0], raw[:, 0], v["A"], v["B"][:, 0], v["C"][:, 0], v["D"],
+                     dt_bias=bias, lib=lib)
+    yb = oracle.step(st_b, v["x"][:, 0], shifted[:, 0], v["A"], v["B"][:, 0], v["C"][:, 0], v["D"],
+                     lib=lib)
+    assert np.array_equal(ya, yb) and np.array_equal(st_a, st_b)
+
+
+def pin_softplus_and_clamp(lib=None):
+    """P12: softplus (tutorial section 3.2) is log(1 + e^v), checked against
+    numpy's logaddexp(0, v) over raw values from -9 to 40; the clamp (the
+    step-size range of the tutorial's section 8.2) is numpy's clip and comes
+    after softplus, and the bias comes before both."""
+    w = W.small("p12", 2, 17, 4, 3, 2, 5, 8, "f32", seed=22, init_std=0.4)
+    v = _vals(w)
+    rng = np.random.default_rng(22)
+    raw = _dyadic(rng, v["dt"].shape, -9.0, 2.0, 64)
+    raw[0, 3, :] = [20.0, 40.0, -20.0, 0.0]
+    args = (v["A"], v["B"], v["C"], v["D"], v["init"])
+    sp = np.logaddexp(0.0, raw.astype(np.float64)).astype(np.float32)
+    y0, s0, _ = oracle.forward(v["x"], raw, *args, dt_softplus=True, lib=lib)
+    y1, s1, _ = oracle.forward(v["x"], sp, *args, lib=lib)
+    assert _rel(y0, y1) < 2e-6 and _rel(s0, s1) < 2e-6
+    # clamp alone: exact, bounds are float32 values
+    lo, hi = 0.0625, 0.25
+    pos = _dyadic(rng, v["dt"].shape, 0.0, 0.5, 1024)
+    y0, s0, _ = oracle.forward(v["x"], pos, *args, dt_limit=(lo, hi), lib=lib)
+    y1, s1, _ = oracle.forward(v["x"], np.clip(pos, lo, hi), *args, lib=lib)
+    assert np.array_equal(y0, y1) and np.array_equal(s0, s1)
+    # the whole chain: clip(softplus(raw + bias)), bounds hit on both sides
+    bias = np.array([-4.0, -2.5, -1.0, 0.5], np.float32)
+    lo, hi = 0.02, 0.3
+    ref = np.clip(np.logaddexp(0.0, raw.astype(np.float64) + bias), lo, hi)
+    assert (ref == lo).mean() > 0.1 and (ref == hi).mean() > 0.1
+    y0, s0, _ = oracle.forward(v["x"], raw, *args, dt_bias=bias, dt_softplus=True,
+                               dt_limit=(lo, hi), lib=lib)
+    y1, s1, _ = oracle.forward(v["x"], ref.astype(np.float32), *args, lib=lib)
+    assert _rel(y0, y1) < 2e-6 and _rel(s0, s1) < 2e-6
+
+
+def _ode_zoh_reference(x, dt, A, B, C, D, init):
+    """Integrate dh/dtau = A h + x_t B_t^T over [0, dt_t] per token with the
+    input held constant on each interval (zero-order hold), then read
+    y_t = C_t . h + D x_t. One batch, one group; float64 lists of arrays."""
+    from scipy.integrate import solve_ivp
+    L, H, P = x.shape
+    N = B.shape[-1]
+    y = np.zeros((L, H, P))
+    hf = np.zeros((H, P, N))
+    for h in range(H):
+        state = np.array(init[h], np.float64).ravel()
+        for t in range(L):
+            drive = np.outer(x[t, h], B[t]).ravel()
+            sol = solve_ivp(lambda _tau, s, a=float(A[h]), u=drive: a * s + u,
+                            (0.0, float(dt[t, h])), state, method="DOP853",
+                            rtol=1e-12, atol=1e-14)
+            state = sol.y[:, -1]
+            y[t, h] = state.reshape(P, N) @ C[t] + D[h] * x[t, h]
+        hf[h] = state.reshape(P, N)
+    return y, hf
+
+
+def pin_zoh_ode(lib=None):
+    """P13: with zoh, each token advances the state by the exact solution of
+    the continuous SSM dh/dt = A h + B u (tutorial section 2.1) over a step of
+    length dt with the input held constant: the zero-order hold of the
+    tutorial's section 2.2 and "Mamba 模型" section 2.3.1. The reference is a
+    numerical ODE solve, independent of any closed form."""
+    w = W.small("p13", 1, 7, 2, 2, 1, 3, 8, "f32", seed=23, init_std=0.5, dt_lo=0.05, dt_hi=1.5)
+    v = _vals(w)
+    y, st, _ = oracle.forward(v["x"], v["dt"], v["A"], v["B"], v["C"], v["D"], v["init"],
+                              zoh=True, lib=lib)
+    f64 = lambda a: np.asarray(a, np.float64)
+    yr, hr = _ode_zoh_reference(f64(v["x"][0]), f64(v["dt"][0]), f64(v["A"]), f64(v["B"][0, :, 0]),
+                                f64(v["C"][0, :, 0]), f64(v["D"]), f64(v["init"][0]))
+    assert _rel(_units_to_bthp(y, 1, 2)[0], yr) < 1e-9
+    assert _rel(st.reshape(2, 2, 3), hr) < 1e-9
+
+
+def pin_zoh_forms(lib=None):
+    """P14: (a) the zoh weight (exp(dt A) - 1) / A tends to dt as A -> 0, and
+    A = 0 gives the Euler weight exactly; (b) on grouped multi-head inputs
+    with an initial state, the zoh recurrence equals the quadratic form with
+    input weights expm1(dt A) / A (numpy), and differs from Euler."""
+    w = W.small("p14", 2, 21, 4, 3, 2, 5, 8, "f32", seed=24, init_std=0.3, dt_lo=0.02, dt_hi=1.0)
+    v = _vals(w)
+    x, dt, B, C, D, init = v["x"], v["dt"], v["B"], v["C"], v["D"], v["init"]
+    zero_a = np.zeros(4, np.float32)
+    ye, se, _ = oracle.forward(x, dt, zero_a, B, C, D, init, lib=lib)
+    yz, sz, _ = oracle.forward(x, dt, zero_a, B, C, D, init, zoh=True, lib=lib)
+    assert np.array_equal(ye, yz) and np.array_equal(se, sz)
+    tiny_a = np.full(4, -1e-9, np.float32)
+    ye, se, _ = oracle.forward(x, dt, tiny_a, B, C, D, init, lib=lib)
+    yz, sz, _ = oracle.forward(x, dt, tiny_a, B, C, D, init, zoh=True, lib=lib)
+    assert _rel(yz, ye) < 1e-8 and _rel(sz, se) < 1e-8
+    A = v["A"]
+    yz, sz, _ = oracle.forward(x, dt, A, B, C, D, init, zoh=True, lib=lib)
+    wts = np.expm1(dt.astype(np.float64) * A) / A.astype(np.float64)
+    yq, hq = oracle.quadratic(x, dt, A, B, C, D, init, weights=wts)
+    assert _rel(_units_to_bthp(yz, 2, 4), yq) < 1e-11
+    assert _rel(sz.reshape(2, 4, 3, 5), hq) < 1e-11
+    ye, _, _ = oracle.forward(x, dt, A, B, C, D, init, lib=lib)
+    assert _rel(yz, ye) > 1e-3
+
+
+def pin_step_with_options(lib=None):
+    """P15: with every option on, L recurrent steps still equal one forward
+    (the same preprocessing and input weight on both paths)."""
+    w = W.small("p15", 2, 9, 4, 3, 2, 5, 8, "f32", seed=25, init_std=0.5)
+    v = _vals(w)
+    rng = np.random.default_rng(25)
+    raw = _dyadic(rng, v["dt"].shape, -4.0, 1.0, 64)
+    opts = dict(dt_bias=np.array([-1.0, 0.5, -2.0, 0.0], np.float32), dt_softplus=True,
+                dt_limit=(0.05, 0.9), zoh=True)
+    y, st, _ = oracle.forward(v["x"], raw, v["A"], v["B"], v["C"], v["D"], v["init"], lib=lib,
+                              **opts)
+    state = np.ascontiguousarray(v["init"].reshape(8, 3, 5).astype(np.float64))
+    for t in range(9):
+        ys = oracle.step(state, v["x"][:, t], raw[:, t], v["A"], v["B"][:, t], v["C"][:, t],
+                         v["D"], lib=lib, **opts)
+        assert np.max(np.abs(ys - y[:, t])) < 1e-13
+    assert np.max(np.abs(state - st)) < 1e-13
+
+
 ALL_PINS = [pin_duality, pin_cumsum, pin_lti_geometric, pin_single_token, pin_no_memory,
-            pin_state_carry, pin_forward_vs_step, pin_linearity, pin_groups, pin_golden]
+            pin_state_carry, pin_forward_vs_step, pin_linearity, pin_groups, pin_golden,
+            pin_dt_bias, pin_softplus_and_clamp, pin_zoh_ode, pin_zoh_forms,
+            pin_step_with_options]

@@ -13,7 +13,7 @@ MUTATIONS = {
     "dropped_D": ("acc + D * (double)xt[p]", "acc"),
     "sign_of_A": ("const double a = exp(d * A);", "const double a = exp(-d * A);"),
     "no_decay": ("row[n] = a * row[n] + dx * (double)Bt[n];", "row[n] = row[n] + dx * (double)Bt[n];"),
-    "no_dt_on_input": ("const double dx = d * (double)xt[p];\n            double acc = 0.0;\n            for (int n = 0; n < N; ++n) {\n                row[n] = a * row[n]",
+    "no_dt_on_input": ("const double dx = wi * (double)xt[p];\n            double acc = 0.0;\n            for (int n = 0; n < N; ++n) {\n                row[n] = a * row[n]",
                        "const double dx = (double)xt[p];\n            double acc = 0.0;\n            for (int n = 0; n < N; ++n) {\n                row[n] = a * row[n]"),
     "B_C_swapped": ("acc += (double)Ct[n] * row[n];\n            }\n            if (yu)", "acc += (double)Bt[n] * row[n];\n            }\n            if (yu)"),
     "output_before_update": ("row[n] = a * row[n] + dx * (double)Bt[n];\n                acc += (double)Ct[n] * row[n];",
@@ -22,6 +22,21 @@ MUTATIONS = {
     "transposed_state_read": ("acc += (double)Ct[n] * row[n];\n            }\n            if (yu)",
                               "acc += (double)Ct[n] * hs[(size_t)(n % P) * N + (p % N)];\n            }\n            if (yu)"),
     "init_ignored": ("for (size_t k = 0; k < PN; ++k) hs[k] = s0[k];", "(void)s0; memset(hs, 0, PN * sizeof(double));"),
+    "bias_head_index": ("v += (double)o->dt_bias[h];", "v += (double)o->dt_bias[0];"),
+    "bias_after_softplus": ("    if (o->dt_bias) v += (double)o->dt_bias[h];\n    if (o->dt_softplus) v = fmax(v, 0.0) + log1p(exp(-fabs(v)));",
+                            "    if (o->dt_softplus) v = fmax(v, 0.0) + log1p(exp(-fabs(v)));\n    if (o->dt_bias) v += (double)o->dt_bias[h];"),
+    "softplus_dropped_linear_part": ("v = fmax(v, 0.0) + log1p(exp(-fabs(v)));", "v = log1p(exp(-fabs(v)));"),
+    "softplus_as_exp": ("v = fmax(v, 0.0) + log1p(exp(-fabs(v)));", "v = exp(v);"),
+    "clamp_before_softplus": ("    if (o->dt_softplus) v = fmax(v, 0.0) + log1p(exp(-fabs(v))); /* log(1 + e^v), no overflow */\n    if (o->dt_clamp) v = fmin(fmax(v, o->dt_min), o->dt_max);",
+                              "    if (o->dt_clamp) v = fmin(fmax(v, o->dt_min), o->dt_max);\n    if (o->dt_softplus) v = fmax(v, 0.0) + log1p(exp(-fabs(v)));"),
+    "clamp_bounds_swapped": ("v = fmin(fmax(v, o->dt_min), o->dt_max);", "v = fmin(fmax(v, o->dt_max), o->dt_min);"),
+    "zoh_as_euler": ("if (o && o->zoh) return A != 0.0 ? expm1(d * A) / A : d;", "if (o && o->zoh) return d;"),
+    "zoh_sign": ("return A != 0.0 ? expm1(d * A) / A : d;", "return A != 0.0 ? -expm1(d * A) / A : d;"),
+    "zoh_without_division": ("return A != 0.0 ? expm1(d * A) / A : d;", "return A != 0.0 ? expm1(d * A) : d;"),
+    "zoh_times_dt": ("return A != 0.0 ? expm1(d * A) / A : d;", "return A != 0.0 ? d * expm1(d * A) / A : d;"),
+    "zoh_exp_not_expm1": ("return A != 0.0 ? expm1(d * A) / A : d;", "return A != 0.0 ? exp(d * A) / A : d;"),
+    "step_ignores_dt_options": ("step_size(j->opts, j->dt[bh], h)", "(double)j->dt[bh]"),
+    "step_euler_weight": ("input_weight(j->opts, d, (double)j->A[h])", "d"),
     "previous_token_dt_for_decay": ("const double a = exp(d * A);", "const double a = exp((t ? (double)j->dt[(tok - 1) * H + h] : d) * A);"),
 }
 
