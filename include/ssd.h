@@ -3,11 +3,14 @@
  *
  * The layer is the per-head selective state-space model of Mamba-2:
  *
- *   h_t = exp(dt_t * A_h) * h_{t-1} + dt_t * x_t B_t^T      state, P x N per head
+ *   h_t = exp(dt_t * A_h) * h_{t-1} + w_t * x_t B_t^T       state, P x N per head
  *   y_t = h_t C_t + D_h * x_t                               output after the update
  *
  * ("从Transformer到Mamba" tutorial, sections 2.1-2.2: discrete recurrence and
  * feed-through D; "深挖-Mamba", core concept 3: dt, B, C depend on the token.)
+ * The input weight w_t is dt_t (Euler, the default) or, with the zero-order
+ * hold option, (exp(dt_t A_h) - 1) / A_h. dt_t is the caller's dt, optionally
+ * preprocessed first (bias, softplus, clamp; see ssd_options).
  * The forward pass computes it with the block decomposition of the
  * semiseparable matrix ("Mamba 模型", section 4.1 and "Draft:Mamba2", SSD
  * section): diagonal blocks (chunks of Q tokens) as masked matrix products,
@@ -23,7 +26,7 @@
  * - Layouts (Bt batch, L seqlen, H heads, P headdim, G groups, N dstate,
  *   Q chunk, nC = ceil(L / Q)):
  *     x, y          [Bt][L][H][P]        dtype
- *     dt            [Bt][L][H]           dtype (already positive; no softplus)
+ *     dt            [Bt][L][H]           dtype (positive, unless ssd_options applies softplus)
  *     B, C          [Bt][L][G][N]        dtype; head h reads group h / (H / G)
  *     A, D          [H]                  float32 (A < 0 for a decaying state)
  *     states        [Bt][H][P][N]        float32 (init / final / decode state)
@@ -60,8 +63,44 @@ typedef enum {
     SSD_ERR_SHAPE = -2,       /* a size is non-positive or nheads % ngroups != 0   */
     SSD_ERR_UNSUPPORTED = -3, /* outside the supported set above                   */
     SSD_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required        */
-    SSD_ERR_HIP = -5          /* the HIP runtime reported an error at launch       */
+    SSD_ERR_HIP = -5,         /* the HIP runtime reported an error at launch       */
+    SSD_ERR_OPTION = -6       /* an ssd_options field holds an invalid value       */
 } ssd_status;
+
+/* Discretisation of the input term. */
+typedef enum {
+    SSD_DISC_EULER = 0, /* w_t = dt_t: the Mamba-2 layer's form                       */
+    SSD_DISC_ZOH = 1    /* w_t = (exp(dt_t A) - 1) / A (dt_t at A = 0): zero-order hold,
+                           "从Transformer到Mamba" tutorial section 2.2 and
+                           "Mamba 模型" section 2.3.1, for a scalar A                   */
+} ssd_discretization;
+
+/*
+ * Step-size preprocessing and discretisation (a host struct, passed by
+ * pointer; a NULL pointer means every field off / SSD_DISC_EULER). The
+ * selection mechanism of the "从Transformer到Mamba" tutorial (section 3.2)
+ * produces the step size by a linear projection of the input and softplus;
+ * the library takes the projection's output as dt and applies, per token, in
+ * this order:
+ *   dt <- dt + dt_bias[h]                    if dt_bias != NULL (the projection's
+ *                                            per-head constant term)
+ *   dt <- log(1 + exp(dt))                   if dt_softplus
+ *   dt <- min(max(dt, dt_min), dt_max)       if dt_clamp (the step-size range the
+ *                                            tutorial's section 8.2 adjusts)
+ * in float32. The decay uses the result; the input term uses it (Euler) or its
+ * zero-order-hold weight (SSD_DISC_ZOH).
+ *   dt_bias         DEVICE pointer, float32 [H], 4-byte aligned, or NULL.
+ *   dt_min, dt_max  read only when dt_clamp; need dt_min <= dt_max (infinite
+ *                   bounds allowed), else SSD_ERR_OPTION.
+ *   discretization  an ssd_discretization, else SSD_ERR_OPTION.
+ */
+typedef struct {
+    const float *dt_bias;
+    int dt_softplus;
+    int dt_clamp;
+    float dt_min, dt_max;
+    int discretization;
+} ssd_options;
 
 /* Human-readable text for a status code (static storage; never NULL). */
 const char *ssd_strerror(int status);
@@ -70,7 +109,8 @@ const char *ssd_strerror(int status);
  * Bytes of workspace ssd_forward needs (0 for invalid sizes). The workspace
  * holds, at 256-byte aligned offsets in this order:
  *   dA_cumsum   float32 [Bt][H][nC*Q]      within-chunk prefix sums of dt*A
- *   delta       float32 [Bt][H][nC*Q]      dt in the same layout (zero past seqlen)
+ *   delta       float32 [Bt][H][nC*Q]      each token's input weight w_t, same layout
+ *                                          (zero past seqlen)
  *   states      float32 [Bt][nC][H][P][N]  each chunk's own state contribution
  *   chunk_init  [Bt][nC][H][P][N]          state entering each chunk, in the MFMA
  *                                          operand type (bf16 for SSD_BF16, else float32)
@@ -101,6 +141,19 @@ int ssd_forward(const void *x, const void *dt, const float *A, const void *B,
                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ssd_forward with options: `opts` (nullable, see ssd_options) preprocesses dt
+ * and chooses the discretisation; `events` are the timing hooks of
+ * ssd_forward_timed (nullable). ssd_forward is this call with opts = NULL and
+ * events = NULL.
+ */
+int ssd_forward_ex(const void *x, const void *dt, const float *A, const void *B,
+                   const void *C, const float *D, int batch, int seqlen, int nheads,
+                   int headdim, int ngroups, int dstate, int chunk, int dtype,
+                   const float *init_state, void *y, float *final_state,
+                   void *workspace, size_t workspace_bytes, const ssd_options *opts,
+                   void *stream, void *const *events);
+
+/*
  * ssd_forward with per-stage timing hooks for profilers and benchmarks.
  * `events` is NULL (then this is exactly ssd_forward) or an array of 6
  * hipEvent_t owned by the caller, any of which may be NULL (not recorded):
@@ -128,25 +181,40 @@ int ssd_step(float *state, const void *x, const void *dt, const float *A,
              const void *B, const void *C, const float *D, int batch, int nheads,
              int headdim, int ngroups, int dstate, int dtype, void *y, void *stream);
 
+/*
+ * ssd_step with options (nullable, see ssd_options): dt is preprocessed as in
+ * ssd_forward_ex and the input term weighted by w = dt or, for SSD_DISC_ZOH,
+ * (exp(dt A_h) - 1) / A_h:
+ *   state <- exp(dt*A_h) * state + w * x B^T,   y = state C + D_h x.
+ */
+int ssd_step_ex(float *state, const void *x, const void *dt, const float *A,
+                const void *B, const void *C, const float *D, int batch, int nheads,
+                int headdim, int ngroups, int dstate, int dtype, void *y,
+                const ssd_options *opts, void *stream);
+
 /* ---- The forward pass stage by stage (what ssd_forward enqueues) ---------- */
 
 /*
- * Stage 1: dA_cumsum[b][h][c*Q + k] = sum_{t=cQ..cQ+k} dt[b][t][h] * A[h]
- * (natural-log units; entries past seqlen continue the sum with zero terms).
- * Output float32 [Bt][H][nC*Q]. `delta` (nullable) receives dt itself in the
- * same layout, as float32, zero past seqlen: a copy of dt that the later
- * stages read contiguously per head.
+ * Stage 1: dA_cumsum[b][h][c*Q + k] = sum_{t=cQ..cQ+k} dt_t * A[h], with dt_t
+ * the step size of token t after `opts`' preprocessing (opts nullable; see
+ * ssd_options), in natural-log units; entries past seqlen continue the sum
+ * with zero terms. Output float32 [Bt][H][nC*Q]. `delta` (nullable, 16-byte
+ * aligned) receives each token's input weight w_t (dt_t, or its zero-order-hold
+ * weight for SSD_DISC_ZOH) in the same layout, as float32, zero past seqlen:
+ * the later stages read it in place of dt.
  */
 int ssd_chunk_cumsum(const void *dt, const float *A, int batch, int seqlen, int nheads,
-                     int chunk, int dtype, float *dA_cumsum, float *delta, void *stream);
+                     int chunk, int dtype, float *dA_cumsum, float *delta,
+                     const ssd_options *opts, void *stream);
 
 /*
  * Stage 2: each chunk's state contribution from a zero state,
- *   states[b][c][h][p][n] = sum_{t in c} exp(s_end(c) - s_t) * dt_t * x_t[p] * B_t[n],
- * with s from dA_cumsum and s_end(c) its value at the chunk's last token.
+ *   states[b][c][h][p][n] = sum_{t in c} exp(s_end(c) - s_t) * w_t * x_t[p] * B_t[n],
+ * with s from dA_cumsum, s_end(c) its value at the chunk's last token, and
+ * w from `delta` (stage 1's float32 [Bt][H][nC*Q], 16-byte aligned).
  * Output float32 [Bt][nC][H][P][N].
  */
-int ssd_chunk_state(const void *x, const void *B, const void *dt, const float *dA_cumsum,
+int ssd_chunk_state(const void *x, const void *B, const float *delta, const float *dA_cumsum,
                     int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate,
                     int chunk, int dtype, float *states, void *stream);
 
@@ -175,16 +243,17 @@ int ssd_chunk_cb(const void *B, const void *C, int batch, int seqlen, int ngroup
 
 /*
  * Stage 4b: outputs of every chunk,
- *   y_i = sum_{j in c, j <= i} (C_i . B_j) exp(s_i - s_j) dt_j x_j   (diagonal block)
+ *   y_i = sum_{j in c, j <= i} (C_i . B_j) exp(s_i - s_j) w_j x_j    (diagonal block)
  *       + exp(s_i) H_c C_i                                           (off-diagonal blocks)
  *       + D_h x_i,
- * writing y [Bt][L][H][P] in dtype. D is nullable. C_i . B_j comes from
+ * writing y [Bt][L][H][P] in dtype, with w from `delta` (stage 1's float32
+ * [Bt][H][nC*Q], 16-byte aligned). D is nullable. C_i . B_j comes from
  *   SSD_BF16: B itself ([Bt][L][G][N], 16-byte aligned): the kernel forms the
  *             C B^T tiles of each chunk on chip; `cb` is not read (may be NULL);
  *   SSD_F32:  `cb`, the output of ssd_chunk_cb (stage 4a); `B` is not read
  *             (may be NULL).
  */
-int ssd_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *B,
+int ssd_chunk_scan(const void *x, const float *delta, const float *dA_cumsum, const void *B,
                    const void *C, const void *cb, const float *D, const void *chunk_init,
                    int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate,
                    int chunk, int dtype, void *y, void *stream);

@@ -155,6 +155,21 @@ def generate(w: Workload, seed: int | None = None) -> dict:
     return out
 
 
+def generate_dt_raw(w: Workload, seed: int | None = None) -> dict:
+    """Inputs for the step-size preprocessing options: ``dt`` holds raw values
+    (the step-size projection's output before its bias and softplus) drawn
+    N(0, 0.5^2) and stored in ``w.dtype``, shaped like ``generate``'s dt;
+    ``dt_bias`` is float32 [H] drawn U(-6.5, -2.5). softplus of their sum then
+    spans roughly 2e-4 .. 0.3, the range of the plain workloads' dt. Drawn
+    from a stream of its own, so ``generate``'s arrays are unchanged."""
+    base = w.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(base + 0x5EED))
+    Bt, L, H = w.batch, w.seqlen, w.nheads
+    shape = (L, Bt, H) if w.decode else (Bt, L, H)
+    return {"dt": _store(_normal(rng, shape, 0.5), w.dtype),
+            "dt_bias": rng.uniform(-6.5, -2.5, H).astype(np.float32)}
+
+
 def small(name: str, batch: int, seqlen: int, nheads: int, headdim: int, ngroups: int,
           dstate: int, chunk: int, dtype: str, seed: int, init_std: float = 0.0,
           dt_lo: float = 1e-3, dt_hi: float = 1e-1, bc_scale: float | None = None) -> Workload:

@@ -14,7 +14,7 @@ import torch
 from . import _native
 from ._native import SSDError, check, dtype_code, ptr, stream_handle
 
-__all__ = ["forward", "step", "workspace_size", "chunk_cumsum", "chunk_state",
+__all__ = ["forward", "step", "options", "workspace_size", "chunk_cumsum", "chunk_state",
            "state_passing", "chunk_cb", "chunk_scan", "SSDError", "stages"]
 
 HEADDIM = 64
@@ -36,17 +36,44 @@ def _opt(t, name, dtype=torch.float32):
     return None if t is None else _req(t, name, dtype)
 
 
+def options(dt_bias=None, dt_softplus=False, dt_limit=None, zoh=False):
+    """ssd_options for the C ABI, or None when every option is off.
+
+    dt_bias: GPU float32 [H] added to dt first; dt_softplus: apply
+    log(1 + e^dt) next; dt_limit = (lo, hi): clamp last; zoh: weight the
+    input term by (exp(dt A) - 1) / A instead of dt. The returned structure
+    points at dt_bias's memory and holds a reference to the tensor, so the
+    memory stays allocated as long as the structure is alive.
+    """
+    if dt_bias is None and not dt_softplus and dt_limit is None and not zoh:
+        return None
+    if dt_bias is not None:
+        _req(dt_bias, "dt_bias", torch.float32)
+    lo, hi = (0.0, 0.0) if dt_limit is None else (float(dt_limit[0]), float(dt_limit[1]))
+    o = _native.SsdOptions(None if dt_bias is None else dt_bias.data_ptr(), int(bool(dt_softplus)),
+                           int(dt_limit is not None), lo, hi,
+                           _native.SSD_DISC_ZOH if zoh else _native.SSD_DISC_EULER)
+    o.bias_tensor = dt_bias  # keeps the bias memory alive with the structure
+    return o
+
+
+def _optref(o):
+    return None if o is None else ctypes.byref(o)
+
+
 def workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, dtype=torch.bfloat16) -> int:
     return int(_native.lib.ssd_forward_workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate,
                                                       chunk, dtype_code(dtype)))
 
 
 def forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, return_final_state=False,
-            workspace=None, y=None, events=None):
+            workspace=None, y=None, events=None, dt_bias=None, dt_softplus=False,
+            dt_limit=None, zoh=False):
     """y = SSD(x, dt, A, B, C, D) over whole sequences.
 
     x [Bt,L,H,P], dt [Bt,L,H], B, C [Bt,L,G,N] (all float32 or all bfloat16),
     A, D [H] float32, init_state [Bt,H,P,N] float32 or None.
+    dt_bias, dt_softplus, dt_limit, zoh: see ``options``.
     Returns y (and the final state [Bt,H,P,N] float32 if requested).
     ``events``: optional sequence of 6 torch.cuda.Event(enable_timing=True) or None;
     the library records them around its five stages (see ssd_forward_timed),
@@ -78,18 +105,23 @@ def forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, return_final_sta
             if e is not None and not e.cuda_event:
                 e.record()  # torch creates the HIP event on its first record
         ev = (ctypes.c_void_p * 6)(*[e.cuda_event if e is not None else None for e in events])
-    rc = _native.lib.ssd_forward_timed(
+    if dt_bias is not None and tuple(dt_bias.shape) != (H,):
+        raise ValueError("dt_bias must have shape [H]")
+    opts = options(dt_bias, dt_softplus, dt_limit, zoh)
+    rc = _native.lib.ssd_forward_ex(
         ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), Bt, L, H, P, G, N, chunk, dt_,
-        ptr(init_state), ptr(y), ptr(fs), ptr(workspace), workspace.numel(), stream_handle(x.device),
-        ev)
+        ptr(init_state), ptr(y), ptr(fs), ptr(workspace), workspace.numel(), _optref(opts),
+        stream_handle(x.device), ev)
     check(rc, "ssd_forward")
     return (y, fs) if return_final_state else y
 
 
-def step(state, x, dt, A, B, C, D=None, y=None):
+def step(state, x, dt, A, B, C, D=None, y=None, dt_bias=None, dt_softplus=False, dt_limit=None,
+         zoh=False):
     """One decode step; updates state [Bt,H,P,N] float32 in place, returns y [Bt,H,P].
 
     x [Bt,H,P], dt [Bt,H], B, C [Bt,G,N] (float32 or bfloat16), A, D [H] float32.
+    dt_bias, dt_softplus, dt_limit, zoh: see ``options``.
     """
     _req(state, "state", torch.float32)
     _req(x, "x")
@@ -105,8 +137,12 @@ def step(state, x, dt, A, B, C, D=None, y=None):
         raise ValueError("shape mismatch among state, x, dt, B, C")
     if y is None:
         y = torch.empty_like(x)
-    rc = _native.lib.ssd_step(ptr(state), ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D),
-                              Bt, H, P, G, N, dt_, ptr(y), stream_handle(x.device))
+    if dt_bias is not None and tuple(dt_bias.shape) != (H,):
+        raise ValueError("dt_bias must have shape [H]")
+    opts = options(dt_bias, dt_softplus, dt_limit, zoh)
+    rc = _native.lib.ssd_step_ex(ptr(state), ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D),
+                                 Bt, H, P, G, N, dt_, ptr(y), _optref(opts),
+                                 stream_handle(x.device))
     check(rc, "ssd_step")
     return y
 
@@ -117,10 +153,11 @@ def _nc(L, Q):
     return (L + Q - 1) // Q
 
 
-def chunk_cumsum(dt, A, chunk, out=None, delta=None, return_delta=False):
-    """dA_cumsum [Bt,H,nC*Q] float32: within-chunk prefix sums of dt*A; with
-    return_delta (or a given ``delta`` buffer), also dt as float32 in the same
-    layout (zero past the end)."""
+def chunk_cumsum(dt, A, chunk, out=None, delta=None, return_delta=False, opts=None):
+    """dA_cumsum [Bt,H,nC*Q] float32: within-chunk prefix sums of dt*A (dt
+    after the preprocessing in ``opts``, an ``options(...)`` result or None);
+    with return_delta (or a given ``delta`` buffer), also each token's input
+    weight as float32 in the same layout (zero past the end)."""
     _req(dt, "dt")
     Bt, L, H = dt.shape
     shape = (Bt, H, _nc(L, chunk) * chunk)
@@ -130,18 +167,21 @@ def chunk_cumsum(dt, A, chunk, out=None, delta=None, return_delta=False):
         delta = torch.empty(shape, dtype=torch.float32, device=dt.device)
     rc = _native.lib.ssd_chunk_cumsum(ptr(dt), ptr(_req(A, "A", torch.float32)), Bt, L, H, chunk,
                                       dtype_code(dt.dtype), ptr(out),
-                                      ptr(_opt(delta, "delta")), stream_handle(dt.device))
+                                      ptr(_opt(delta, "delta")), _optref(opts),
+                                      stream_handle(dt.device))
     check(rc, "ssd_chunk_cumsum")
     return (out, delta) if delta is not None else out
 
 
-def chunk_state(x, B, dt, dA_cumsum, chunk, out=None):
-    """states [Bt,nC,H,P,N] float32: each chunk's contribution from a zero state."""
+def chunk_state(x, B, delta, dA_cumsum, chunk, out=None):
+    """states [Bt,nC,H,P,N] float32: each chunk's contribution from a zero state
+    (delta: chunk_cumsum's input weights)."""
     Bt, L, H, P = _req(x, "x").shape
     G, N = B.shape[2], B.shape[3]
     if out is None:
         out = torch.empty((Bt, _nc(L, chunk), H, P, N), dtype=torch.float32, device=x.device)
-    rc = _native.lib.ssd_chunk_state(ptr(x), ptr(_req(B, "B", x.dtype)), ptr(_req(dt, "dt", x.dtype)),
+    rc = _native.lib.ssd_chunk_state(ptr(x), ptr(_req(B, "B", x.dtype)),
+                                     ptr(_req(delta, "delta", torch.float32)),
                                      ptr(_req(dA_cumsum, "dA_cumsum", torch.float32)), Bt, L, H, P, G,
                                      N, chunk, dtype_code(x.dtype), ptr(out), stream_handle(x.device))
     check(rc, "ssd_chunk_state")
@@ -176,8 +216,9 @@ def chunk_cb(B, C, chunk, out=None):
     return out
 
 
-def chunk_scan(x, dt, dA_cumsum, B, C, cb, D, chunk_init, chunk, y=None):
-    """y [Bt,L,H,P]: intra-chunk product + state-to-output + D x.
+def chunk_scan(x, delta, dA_cumsum, B, C, cb, D, chunk_init, chunk, y=None):
+    """y [Bt,L,H,P]: intra-chunk product + state-to-output + D x
+    (delta: chunk_cumsum's input weights).
 
     bfloat16 forms C B^T on chip from B (cb may be None); float32 reads the
     C B^T tiles of chunk_cb (B may be None)."""
@@ -186,7 +227,7 @@ def chunk_scan(x, dt, dA_cumsum, B, C, cb, D, chunk_init, chunk, y=None):
     if y is None:
         y = torch.empty_like(x)
     bf16 = x.dtype == torch.bfloat16
-    rc = _native.lib.ssd_chunk_scan(ptr(x), ptr(_req(dt, "dt", x.dtype)),
+    rc = _native.lib.ssd_chunk_scan(ptr(x), ptr(_req(delta, "delta", torch.float32)),
                                     ptr(_req(dA_cumsum, "dA_cumsum", torch.float32)),
                                     ptr(_req(B, "B", x.dtype) if bf16 else B),
                                     ptr(_req(C, "C", x.dtype)), ptr(cb if bf16 else _req(cb, "cb")),
@@ -197,16 +238,18 @@ def chunk_scan(x, dt, dA_cumsum, B, C, cb, D, chunk_init, chunk, y=None):
     return y
 
 
-def stages(x, dt, A, B, C, D=None, chunk=256, init_state=None):
+def stages(x, dt, A, B, C, D=None, chunk=256, init_state=None, dt_bias=None, dt_softplus=False,
+           dt_limit=None, zoh=False):
     """Run the forward stages one call at a time; returns a dict with every
-    intermediate (dA_cumsum, states, chunk_init, final_state, cb) and y."""
+    intermediate (dA_cumsum, delta, states, chunk_init, final_state, cb) and y."""
     Bt, L, H, P = x.shape
     N = B.shape[3]
-    s, delta = chunk_cumsum(dt, A, chunk, return_delta=True)
-    st = chunk_state(x, B, dt, s, chunk)
+    opts = options(dt_bias, dt_softplus, dt_limit, zoh)
+    s, delta = chunk_cumsum(dt, A, chunk, return_delta=True, opts=opts)
+    st = chunk_state(x, B, delta, s, chunk)
     fs = torch.empty((Bt, H, P, N), dtype=torch.float32, device=x.device)
     ci = state_passing(st, s, L, chunk, init_state=init_state, final_state=fs, dtype=x.dtype)
     cb = chunk_cb(B, C, chunk)
-    y = chunk_scan(x, dt, s, B, C, cb, D, ci, chunk)
+    y = chunk_scan(x, delta, s, B, C, cb, D, ci, chunk)
     return {"dA_cumsum": s, "delta": delta, "states": st, "chunk_init": ci, "final_state": fs,
             "cb": cb, "y": y}

@@ -17,8 +17,18 @@ LIB_PATH = os.path.join(HERE, "libssd.so")
 
 SSD_F32, SSD_BF16 = 0, 1
 SSD_OK = 0
+SSD_DISC_EULER, SSD_DISC_ZOH = 0, 1
+
+
+class SsdOptions(ctypes.Structure):
+    """ssd_options of include/ssd.h."""
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int),
+                ("dt_clamp", ctypes.c_int), ("dt_min", ctypes.c_float),
+                ("dt_max", ctypes.c_float), ("discretization", ctypes.c_int)]
+
 
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_op = ctypes.POINTER(SsdOptions)
 
 # name -> (restype, argtypes); mirrors include/ssd.h
 SIGNATURES = {
@@ -28,8 +38,10 @@ SIGNATURES = {
     "ssd_chunk_cb": (_i, [_vp, _vp] + [_i] * 6 + [_vp, _vp]),
     "ssd_forward": (_i, [_vp] * 6 + [_i] * 8 + [_vp, _vp, _vp, _vp, _sz, _vp]),
     "ssd_forward_timed": (_i, [_vp] * 6 + [_i] * 8 + [_vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "ssd_forward_ex": (_i, [_vp] * 6 + [_i] * 8 + [_vp, _vp, _vp, _vp, _sz, _op, _vp, _vp]),
     "ssd_step": (_i, [_vp] * 7 + [_i] * 6 + [_vp, _vp]),
-    "ssd_chunk_cumsum": (_i, [_vp, _vp] + [_i] * 5 + [_vp, _vp, _vp]),
+    "ssd_step_ex": (_i, [_vp] * 7 + [_i] * 6 + [_vp, _op, _vp]),
+    "ssd_chunk_cumsum": (_i, [_vp, _vp] + [_i] * 5 + [_vp, _vp, _op, _vp]),
     "ssd_chunk_state": (_i, [_vp] * 4 + [_i] * 8 + [_vp, _vp]),
     "ssd_state_passing": (_i, [_vp] * 3 + [_i] * 7 + [_vp, _vp, _vp]),
     "ssd_chunk_scan": (_i, [_vp] * 8 + [_i] * 8 + [_vp, _vp]),

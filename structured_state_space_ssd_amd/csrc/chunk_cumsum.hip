@@ -12,10 +12,13 @@
 // them, and the run total, to LDS; one wavefront per head then turns the 16
 // run totals into run offsets. The outputs are written token-fastest: lanes
 // take consecutive tokens of one head, so each store instruction writes 256
-// contiguous bytes of s[b][h][.]. If requested, dt itself is also written, as
-// float32 in the same chunk-padded [b][h][token] layout (zero past the end),
-// straight from each thread's run (Q/16 consecutive tokens of one head): a
-// copy of dt that later stages can read contiguously per head.
+// contiguous bytes of s[b][h][.]. The raw dt is first turned into the step
+// size (bias, softplus, clamp as DtOpts asks) and s sums step * A. If
+// requested, each token's input weight (the step size, or its zero-order-hold
+// weight) is also written, as float32 in the same chunk-padded [b][h][token]
+// layout (zero past the end), straight from each thread's run (Q/16
+// consecutive tokens of one head): the later stages read it contiguously per
+// head instead of dt.
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -29,7 +32,8 @@ __global__ __launch_bounds__(1024) void chunk_cumsum_kernel(const T *__restrict_
                                                             const float *__restrict__ A, int L,
                                                             int H, int nC,
                                                             float *__restrict__ out,
-                                                            float *__restrict__ delta) {
+                                                            float *__restrict__ delta,
+                                                            DtOpts o) {
     constexpr int R = Q / kCumsumRuns;  // tokens per run: 4, 8 or 16
     __shared__ float tile[Q][kCumsumHeads + 1];
     __shared__ float off[kCumsumRuns][kCumsumHeads];
@@ -39,13 +43,32 @@ __global__ __launch_bounds__(1024) void chunk_cumsum_kernel(const T *__restrict_
     const int hc = min(h, H - 1);
     const int t0 = c * Q;
     const float a = h < H ? A[hc] : 0.0f;
-    float v[R], dv[R];
+    const float bias = o.bias ? o.bias[hc] : 0.0f;
+    // all loads first (they stay in flight together), then the options, each
+    // a uniform branch around the whole run
+    float d[R], v[R], dv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        d[r] = to_f32(dt[((size_t)b * L + min(t0 + k * R + r, L - 1)) * H + hc]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) d[r] += bias;
+    if (o.softplus) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) d[r] = fmaxf(d[r], 0.0f) + log1pf(expf(-fabsf(d[r])));
+    }
+    if (o.clamp) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) d[r] = fminf(fmaxf(d[r], o.lo), o.hi);
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int t = t0 + k * R + r;
-        const float d = to_f32(dt[((size_t)b * L + min(t, L - 1)) * H + hc]);
-        dv[r] = (h < H && t < L) ? d : 0.0f;
-        v[r] = dv[r] * a;
+        const bool in = h < H && t0 + k * R + r < L;
+        v[r] = in ? d[r] * a : 0.0f;
+        dv[r] = in ? d[r] : 0.0f;
+    }
+    if (o.zoh) {  // input weight (exp(d a) - 1) / a; d itself where a == 0
+#pragma unroll
+        for (int r = 0; r < R; ++r) dv[r] = a != 0.0f ? expm1f(v[r]) / a : dv[r];
     }
     if (delta && h < H) {
         float *dd = delta + ((size_t)b * H + h) * ((size_t)nC * Q) + t0 + k * R;
@@ -83,13 +106,13 @@ __global__ __launch_bounds__(1024) void chunk_cumsum_kernel(const T *__restrict_
 }
 
 hipError_t launch_chunk_cumsum(const void *dt, const float *A, int batch, int seqlen, int nheads,
-                               int chunk, bool bf16, float *dA_cumsum, float *delta,
-                               hipStream_t stream) {
+                               int chunk, bool bf16, const DtOpts &opts, float *dA_cumsum,
+                               float *delta, hipStream_t stream) {
     const int nC = (seqlen + chunk - 1) / chunk;
     const dim3 grid(nC, batch, (nheads + kCumsumHeads - 1) / kCumsumHeads);
 #define SSD_CUMSUM(T, Q)                                                                       \
     chunk_cumsum_kernel<T, Q><<<grid, 1024, 0, stream>>>(static_cast<const T *>(dt), A, seqlen, \
-                                                        nheads, nC, dA_cumsum, delta)
+                                                        nheads, nC, dA_cumsum, delta, opts)
     if (bf16) {
         if (chunk == 64) SSD_CUMSUM(bf16_t, 64);
         else if (chunk == 128) SSD_CUMSUM(bf16_t, 128);

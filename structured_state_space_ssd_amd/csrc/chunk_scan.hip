@@ -1,9 +1,11 @@
 // Stage 4 of the SSD block decomposition: every chunk's outputs
 // ("Mamba 模型", section 4.1 and "Draft:Mamba2", SSD section):
-//   y_i = sum_{j<=i in chunk} (C_i . B_j) exp(s_i - s_j) dt_j x_j     diagonal block
+//   y_i = sum_{j<=i in chunk} (C_i . B_j) exp(s_i - s_j) delta_j x_j  diagonal block
 //       + exp(s_i) H_c C_i                                            off-diagonal blocks
-//       + D_h x_i.
-// The diagonal block is the masked "attention-like" product (L o C B^T)(dt o x)
+//       + D_h x_i,
+// with delta_j token j's input weight (written by stage 1: the step size, or
+// its zero-order-hold weight). The diagonal block is the masked
+// "attention-like" product (L o C B^T)(delta o x)
 // (quadratic mode of the "Mamba-2架构深度解析" page, section 2.2 table); the
 // off-diagonal part reads the state H_c carried into the chunk (stage 3).
 //
@@ -14,18 +16,18 @@
 //   prologue (the only global-load phase): the chunk's x rows (128 bytes per
 //     token) are loaded with 8 lanes per row and copied to LDS as they are;
 //     H_c (stored by stage 3 in the operand type) is copied to LDS; s*log2(e)
-//     and dt go to LDS. Wavefront w owns output tiles w and Q/16-1-w (equal
+//     and delta go to LDS. Wavefront w owns output tiles w and Q/16-1-w (equal
 //     causal work: Q/32+1 slices of 32 tokens) and loads, in this same phase,
 //     its C rows and all its C B^T fragments into registers.
 //   then, with no further global load, each wavefront computes
 //     - state to output: Y^T += H_c (exp(s_i) C_i)^T on MFMA (K = N);
 //     - D_h x_i;
 //     - per 32-token slice at or below the diagonal: the C B^T fragment times
-//       the decay exp2(s_i - s_j) dt_j in fp32, rounded to the operand type.
+//       the decay exp2(s_i - s_j) delta_j in fp32, rounded to the operand type.
 //       Below the diagonal it factors as exp2(s_i - s_end(slice)) times a
-//       per-token table exp2(s_end(slice) - s_j) dt_j (both factors <= 1):
+//       per-token table exp2(s_end(slice) - s_j) delta_j (both factors <= 1):
 //       one exp per lane per slice. The slice holding the diagonal takes the
-//       exp per element (bf16: exp2(s_i - (s_j - log2 dt_j))) and the causal
+//       exp per element (bf16: exp2(s_i - (s_j - log2 delta_j))) and the causal
 //       mask as a select. The x operand (token index = contraction index)
 //       is read with the transposing LDS read, then Y^T += X^T M^T on MFMA;
 //   epilogue: Y^T tiles go to LDS as 4-element row pieces and leave as full
@@ -42,8 +44,8 @@ struct ScanSmem {
     static constexpr int LDH = colfrag_stride(N, sizeof(E));  // H_c rows [p][n]
     static constexpr int LDY = P + 4;                         // output rows [i][p]
     float sl[Q];    // s * log2(e)
-    float dtl[Q];   // bf16: s * log2(e) - log2(dt) (+inf past the end); float: dt (0 past the end)
-    float colf[Q];  // exp2(s_end(slice of j) - s_j) * dt_j: column factor below the diagonal
+    float dtl[Q];   // bf16: s * log2(e) - log2(delta) (+inf past the end); float: delta (0 past the end)
+    float colf[Q];  // exp2(s_end(slice of j) - s_j) * delta_j: column factor below the diagonal
     union {
         struct {
             E xs[Q * LDX];
@@ -63,7 +65,7 @@ __device__ __forceinline__ void store4_lds(float *p, const floatx4 &v) {
 
 template <typename T, int N, int Q>
 __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_kernel(
-    const T *__restrict__ x, const T *__restrict__ dt, const float *__restrict__ dA_cumsum,
+    const T *__restrict__ x, const float *__restrict__ delta, const float *__restrict__ dA_cumsum,
     const T *__restrict__ C, const typename LdsT<T>::type *__restrict__ cb,
     const float *__restrict__ D, const typename LdsT<T>::type *__restrict__ chunk_init, int L,
     int H, int G, int nC, T *__restrict__ y) {
@@ -133,15 +135,15 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_kernel(
         const int start = (it % 2 == 0) ? m0 * (m0 + 1) : (m0 + 1) * (m0 + 1);
         load_frag8(cbf[k], cbc + (size_t)(start + jp) * 512);
     }
-    // bf16: the decay-and-dt factor exp2(s_i - s_j) * dt_j is formed as one
-    // exp2(s_i - (s_j - log2 dt_j)); float keeps the product (tighter rounding)
+    // bf16: the decay-and-weight factor exp2(s_i - s_j) * delta_j is formed as
+    // one exp2(s_i - (s_j - log2 delta_j)); float keeps the product (tighter rounding)
     constexpr bool kFoldDt = sizeof(T) == 2;
-    const float *s = dA_cumsum + ((size_t)b * H + h) * (size_t)nC * Q + (size_t)c * Q;
+    const size_t srow = ((size_t)b * H + h) * (size_t)nC * Q + (size_t)c * Q;
+    const float *s = dA_cumsum + srow;
     for (int i = tid; i < Q; i += NTHR) {
         const float si_ = s[i] * kLog2e;
         const float se_ = s[i | 31] * kLog2e;  // last token of i's 32-token slice
-        const float draw = to_f32(dt[((size_t)b * L + t0 + min(i, len - 1)) * H + h]);
-        const float d = i < len ? draw : 0.0f;
+        const float d = delta[srow + i];        // zero past the end
         sm.sl[i] = si_;
         sm.dtl[i] = kFoldDt ? si_ - __log2f(d) : d;
         sm.colf[i] = __builtin_amdgcn_exp2f(se_ - si_) * d;
@@ -349,8 +351,8 @@ __device__ __forceinline__ void x_colfrag(Frag<bf16_t> &f, const __bf16 *xs, int
 template <int Q>
 struct ScanTables {
     float sl[Q];    // s * log2(e)
-    float dtl[Q];   // s * log2(e) - log2(dt) (+inf past the end)
-    float colf[Q];  // exp2(s_end(slice of j) - s_j) * dt_j
+    float dtl[Q];   // s * log2(e) - log2(delta) (+inf past the end)
+    float colf[Q];  // exp2(s_end(slice of j) - s_j) * delta_j
 };
 
 // Entry of causal tile (it, jp) in a unit's C B^T tile list: tiles are stored
@@ -383,7 +385,7 @@ __device__ __forceinline__ void scan_slice(floatx4 (&acc)[4], const __bf16 *cbl,
             mf.set(4 + r, cbk.get(4 + r) * (c1[r] * rowf));
         }
     } else {
-        // the slice holding the diagonal: exp2(s_i - (s_j - log2 dt_j)) and the causal mask
+        // the slice holding the diagonal: exp2(s_i - (s_j - log2 delta_j)) and the causal mask
         const floatx4 d0 = *reinterpret_cast<const floatx4 *>(tb.dtl + jb);
         const floatx4 d1 = *reinterpret_cast<const floatx4 *>(tb.dtl + jb + 16);
 #pragma unroll
@@ -445,7 +447,7 @@ struct ScanBf16Lds {
 
 template <int N, int Q>
 __global__ __launch_bounds__(Q * 4) void chunk_scan_bf16_kernel(
-    const bf16_t *__restrict__ x, const bf16_t *__restrict__ dt,
+    const bf16_t *__restrict__ x, const float *__restrict__ delta,
     const float *__restrict__ dA_cumsum, const bf16_t *__restrict__ B,
     const bf16_t *__restrict__ C, const float *__restrict__ D,
     const __bf16 *__restrict__ chunk_init, int L, int H, int G, int nC, int nU, int nblk,
@@ -489,6 +491,7 @@ __global__ __launch_bounds__(Q * 4) void chunk_scan_bf16_kernel(
     bf16_t *ybase = y + ((size_t)b * L + t0) * xrow;
     const __bf16 *hbase = chunk_init + ((size_t)b * nC + c) * H * (size_t)(P * N);
     const float *sbase = dA_cumsum + (size_t)b * H * nC * Q + (size_t)c * Q;
+    const float *dbase = delta + (size_t)b * H * nC * Q + (size_t)c * Q;
     const size_t bcrow = (size_t)G * N;  // token stride of B and C
     const bf16_t *Bc = B + ((size_t)b * L + t0) * bcrow + (size_t)g * N;
     const bf16_t *Cc = C + ((size_t)b * L + t0) * bcrow + (size_t)g * N;
@@ -523,19 +526,18 @@ __global__ __launch_bounds__(Q * 4) void chunk_scan_bf16_kernel(
             dma16(hc + (size_t)p * N + q * 8, hbuf + i * 512);
         }
     };
-    // table inputs are loaded raw (s, s at the slice end, dt's bf16 bits) and
-    // only turned into table entries by tab_store
+    // table inputs are loaded raw (s, s at the slice end, delta) and only
+    // turned into table entries by tab_store
     auto tab_load = [&](int h, int td, float &sv, float &se, float &d) {
         if (td < Q) {
             const float *s = sbase + (size_t)h * nC * Q;
             sv = s[td];
             se = s[td | 31];
-            d = __uint_as_float(dt[((size_t)b * L + t0 + min(td, len - 1)) * H + h]);
+            d = dbase[(size_t)h * nC * Q + td];
         }
     };
-    auto tab_store = [&](ScanTables<Q> &t, int td, float sv, float se, float draw) {
-        if (td < Q) {
-            const float d = td < len ? bf16_to_f32((bf16_t)__float_as_uint(draw)) : 0.0f;
+    auto tab_store = [&](ScanTables<Q> &t, int td, float sv, float se, float d) {
+        if (td < Q) {  // d = delta_j, zero past the end
             const float si_ = sv * kLog2e;
             t.sl[td] = si_;
             t.dtl[td] = si_ - __log2f(d);
@@ -811,7 +813,7 @@ struct PairLds {
 
 template <int N, int Q>
 __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_bf16_pair_kernel(
-    const bf16_t *__restrict__ x, const bf16_t *__restrict__ dt,
+    const bf16_t *__restrict__ x, const float *__restrict__ delta,
     const float *__restrict__ dA_cumsum, const bf16_t *__restrict__ B,
     const bf16_t *__restrict__ C, const float *__restrict__ D,
     const __bf16 *__restrict__ chunk_init, int L, int H, int G, int nC, int nU, int nblk,
@@ -851,6 +853,7 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_bf16_pair_kernel(
     bf16_t *ybase = y + ((size_t)b * L + t0) * xrow;
     const __bf16 *hbase = chunk_init + ((size_t)b * nC + c) * H * (size_t)(P * N);
     const float *sbase = dA_cumsum + (size_t)b * H * nC * Q + (size_t)c * Q;
+    const float *dbase = delta + (size_t)b * H * nC * Q + (size_t)c * Q;
     const size_t bcrow = (size_t)G * N;
     const bf16_t *Bc = B + ((size_t)b * L + t0) * bcrow + (size_t)g * N;
     const bf16_t *Cc = C + ((size_t)b * L + t0) * bcrow + (size_t)g * N;
@@ -884,12 +887,11 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_bf16_pair_kernel(
             const float *s = sbase + (size_t)h * nC * Q;
             sv = s[td];
             se = s[td | 31];
-            d = __uint_as_float(dt[((size_t)b * L + t0 + min(td, len - 1)) * H + h]);
+            d = dbase[(size_t)h * nC * Q + td];
         }
     };
-    auto tab_store = [&](ScanTables<Q> &t, int td, float sv, float se, float draw) {
-        if (td < Q) {
-            const float d = td < len ? bf16_to_f32((bf16_t)__float_as_uint(draw)) : 0.0f;
+    auto tab_store = [&](ScanTables<Q> &t, int td, float sv, float se, float d) {
+        if (td < Q) {  // d = delta_j, zero past the end
             const float si_ = sv * kLog2e;
             t.sl[td] = si_;
             t.dtl[td] = si_ - __log2f(d);
@@ -1011,7 +1013,7 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_bf16_pair_kernel(
 }
 
 template <int N, int Q>
-static void launch_scan_bf16(const void *x, const void *dt, const float *dA, const void *B,
+static void launch_scan_bf16(const void *x, const float *dl, const float *dA, const void *B,
                              const void *C, const float *D, const void *Hc, int batch, int L,
                              int H, int G, void *y, hipStream_t stream) {
     const int nC = (L + Q - 1) / Q;
@@ -1027,58 +1029,58 @@ static void launch_scan_bf16(const void *x, const void *dt, const float *dA, con
     const dim3 grid((unsigned)(8 * nblk) * (unsigned)((nU + 7) / 8));
     if constexpr (kPair) {
         chunk_scan_bf16_pair_kernel<N, Q><<<grid, Q * 2, 0, stream>>>(
-            static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(dt), dA,
+            static_cast<const bf16_t *>(x), dl, dA,
             static_cast<const bf16_t *>(B), static_cast<const bf16_t *>(C), D,
             static_cast<const __bf16 *>(Hc), L, H, G, nC, nU, nblk, static_cast<bf16_t *>(y));
     } else {
         chunk_scan_bf16_kernel<N, Q><<<grid, Q * 4, 0, stream>>>(
-            static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(dt), dA,
+            static_cast<const bf16_t *>(x), dl, dA,
             static_cast<const bf16_t *>(B), static_cast<const bf16_t *>(C), D,
             static_cast<const __bf16 *>(Hc), L, H, G, nC, nU, nblk, static_cast<bf16_t *>(y));
     }
 }
 
 template <typename T, int N, int Q>
-static void launch_scan(const void *x, const void *dt, const float *dA, const void *B,
+static void launch_scan(const void *x, const float *dl, const float *dA, const void *B,
                         const void *C, const void *cb, const float *D, const void *Hc, int batch,
                         int L, int H, int G, void *y, hipStream_t stream) {
     if constexpr (sizeof(T) == 2) {
-        launch_scan_bf16<N, Q>(x, dt, dA, B, C, D, Hc, batch, L, H, G, y, stream);
+        launch_scan_bf16<N, Q>(x, dl, dA, B, C, D, Hc, batch, L, H, G, y, stream);
     } else {
         using E = typename LdsT<T>::type;
         const int nC = (L + Q - 1) / Q;
         const dim3 grid(nC, H, batch);
         chunk_scan_kernel<T, N, Q><<<grid, Q * 2, 0, stream>>>(
-            static_cast<const T *>(x), static_cast<const T *>(dt), dA, static_cast<const T *>(C),
+            static_cast<const T *>(x), dl, dA, static_cast<const T *>(C),
             static_cast<const E *>(cb), D, static_cast<const E *>(Hc), L, H, G, nC,
             static_cast<T *>(y));
     }
 }
 
 template <typename T, int N>
-static bool scan_q(int Q, const void *x, const void *dt, const float *dA, const void *B,
+static bool scan_q(int Q, const void *x, const float *dl, const float *dA, const void *B,
                    const void *C, const void *cb, const float *D, const void *Hc, int batch, int L,
                    int H, int G, void *y, hipStream_t s) {
     switch (Q) {
-        case 64: launch_scan<T, N, 64>(x, dt, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); return true;
-        case 128: launch_scan<T, N, 128>(x, dt, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); return true;
-        case 256: launch_scan<T, N, 256>(x, dt, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); return true;
+        case 64: launch_scan<T, N, 64>(x, dl, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); return true;
+        case 128: launch_scan<T, N, 128>(x, dl, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); return true;
+        case 256: launch_scan<T, N, 256>(x, dl, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); return true;
         default: return false;
     }
 }
 
 template <typename T>
-static hipError_t scan_dispatch(int N, int Q, const void *x, const void *dt, const float *dA,
+static hipError_t scan_dispatch(int N, int Q, const void *x, const float *dl, const float *dA,
                                 const void *B, const void *C, const void *cb, const float *D,
                                 const void *Hc, int batch, int L, int H, int G, void *y,
                                 hipStream_t s) {
     bool ok = false;
     switch (N) {
-        case 16: ok = scan_q<T, 16>(Q, x, dt, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
-        case 32: ok = scan_q<T, 32>(Q, x, dt, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
-        case 64: ok = scan_q<T, 64>(Q, x, dt, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
-        case 128: ok = scan_q<T, 128>(Q, x, dt, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
-        case 256: ok = scan_q<T, 256>(Q, x, dt, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
+        case 16: ok = scan_q<T, 16>(Q, x, dl, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
+        case 32: ok = scan_q<T, 32>(Q, x, dl, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
+        case 64: ok = scan_q<T, 64>(Q, x, dl, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
+        case 128: ok = scan_q<T, 128>(Q, x, dl, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
+        case 256: ok = scan_q<T, 256>(Q, x, dl, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
         default: break;
     }
     if (!ok) return hipErrorInvalidValue;
@@ -1087,14 +1089,14 @@ static hipError_t scan_dispatch(int N, int Q, const void *x, const void *dt, con
 
 bool chunk_scan_reads_cb(bool bf16) { return !bf16; }
 
-hipError_t launch_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *B,
+hipError_t launch_chunk_scan(const void *x, const float *delta, const float *dA_cumsum, const void *B,
                              const void *C, const void *cb, const float *D, const void *chunk_init,
                              int batch, int seqlen, int nheads, int ngroups, int dstate, int chunk,
                              bool bf16, void *y, hipStream_t stream) {
     if (bf16)
-        return scan_dispatch<bf16_t>(dstate, chunk, x, dt, dA_cumsum, B, C, cb, D, chunk_init,
+        return scan_dispatch<bf16_t>(dstate, chunk, x, delta, dA_cumsum, B, C, cb, D, chunk_init,
                                      batch, seqlen, nheads, ngroups, y, stream);
-    return scan_dispatch<float>(dstate, chunk, x, dt, dA_cumsum, B, C, cb, D, chunk_init, batch,
+    return scan_dispatch<float>(dstate, chunk, x, delta, dA_cumsum, B, C, cb, D, chunk_init, batch,
                                 seqlen, nheads, ngroups, y, stream);
 }
 

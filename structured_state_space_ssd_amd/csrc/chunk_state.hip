@@ -1,7 +1,9 @@
 // Stage 2 of the SSD block decomposition: the state each chunk contributes at
 // its right edge, from a zero state ("Mamba 模型", section 4.1: the low-rank
 // factor through which the off-diagonal blocks act):
-//   S_c[p][n] = sum_{j in c} w_j * x_j[p] * B_j[n],  w_j = exp(s_end - s_j) * dt_j.
+//   S_c[p][n] = sum_{j in c} w_j * x_j[p] * B_j[n],  w_j = exp(s_end - s_j) * delta_j,
+// with delta_j token j's input weight (stage 1 writes it: the step size, or its
+// zero-order-hold weight).
 //
 // One workgroup (8 wavefronts) per (chunk, head, batch). S_c = X^T (w o B) is a
 // [P x Q] x [Q x N] product whose contraction index, the token, is the row of
@@ -22,7 +24,7 @@ namespace ssd {
 
 template <typename T, int N, int Q>
 __global__ __launch_bounds__(512) void chunk_state_kernel(
-    const T *__restrict__ x, const T *__restrict__ B, const T *__restrict__ dt,
+    const T *__restrict__ x, const T *__restrict__ B, const float *__restrict__ delta,
     const float *__restrict__ dA_cumsum, int L, int H, int G, int nC,
     float *__restrict__ states) {
     using E = typename LdsT<T>::type;
@@ -63,12 +65,12 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(
         if (idx < Q * BPR && j < len) bv[k].load(bg + (size_t)j * bstride + q * SEG);
         else bv[k].zero();
     }
-    const float *s = dA_cumsum + ((size_t)b * H + h) * (size_t)nC * Q + (size_t)c * Q;
+    const size_t row = ((size_t)b * H + h) * (size_t)nC * Q + (size_t)c * Q;
+    const float *s = dA_cumsum + row, *dl = delta + row;
     const float s_end = s[len - 1];
     for (int j = tid; j < Q; j += NTHR) {
         float wv = 0.0f;
-        if (j < len)
-            wv = __builtin_amdgcn_exp2f((s_end - s[j]) * kLog2e) * to_f32(dt[((size_t)b * L + t0 + j) * H + h]);
+        if (j < len) wv = __builtin_amdgcn_exp2f((s_end - s[j]) * kLog2e) * dl[j];
         wj[j] = wv;
     }
 
@@ -163,7 +165,7 @@ __device__ __forceinline__ void colfrag_swz(Frag<bf16_t> &f, const __bf16 *m, in
 
 template <int N, int Q>
 __global__ __launch_bounds__(512) void chunk_state_bf16_kernel(
-    const bf16_t *__restrict__ x, const bf16_t *__restrict__ B, const bf16_t *__restrict__ dt,
+    const bf16_t *__restrict__ x, const bf16_t *__restrict__ B, const float *__restrict__ delta,
     const float *__restrict__ dA_cumsum, int L, int H, int G, int nC, float *__restrict__ states) {
     constexpr int P = 64, NW = 8;
     constexpr int TP = N >= 128 ? 32 : 64;  // tokens per phase
@@ -202,14 +204,13 @@ __global__ __launch_bounds__(512) void chunk_state_bf16_kernel(
         }
     };
     issue(0);
-    // token weights w_j = exp(s_end - s_j) dt_j (zero past the end)
-    const float *s = dA_cumsum + ((size_t)b * H + h) * (size_t)nC * Q + (size_t)c * Q;
+    // token weights w_j = exp(s_end - s_j) delta_j (zero past the end)
+    const size_t row = ((size_t)b * H + h) * (size_t)nC * Q + (size_t)c * Q;
+    const float *s = dA_cumsum + row, *dl = delta + row;
     const float s_end = s[len - 1];
     for (int j = tid; j < Q; j += 512) {
         float wv = 0.0f;
-        if (j < len)
-            wv = __builtin_amdgcn_exp2f((s_end - s[j]) * kLog2e) *
-                 bf16_to_f32(dt[((size_t)b * L + t0 + j) * H + h]);
+        if (j < len) wv = __builtin_amdgcn_exp2f((s_end - s[j]) * kLog2e) * dl[j];
         wj[j] = wv;
     }
 
@@ -272,8 +273,8 @@ __global__ __launch_bounds__(512) void chunk_state_bf16_kernel(
 // of the MFMA accumulators: H_{c+1} = exp(s_end(c)) H_c + S_c. The state
 // entering each chunk goes out once (in bf16, the operand type of the chunk
 // scan) and the final state in float32; the per-chunk float32 states of the
-// separate stages never exist. The chunk's prefix sums s and dt (the float32
-// copy stage 1 writes) arrive by direct loads too, so nothing inside the loop
+// separate stages never exist. The chunk's prefix sums s and input weights
+// delta (stage 1's float32 outputs) arrive by direct loads too, so nothing inside the loop
 // waits on a global load. Products are formed transposed, S^T[n][p] (B rows as
 // the A operand, weighted x as the B operand): a lane then holds 4
 // consecutive n of one p, which is how the [P][N] state is stored.
@@ -289,8 +290,8 @@ __global__ __launch_bounds__(512) void chunk_state_passing_bf16_kernel(
     constexpr int PPR = N / 8;
     constexpr int XSL = TP * 8 / 64;         // x loads per phase
     constexpr int BSL = TP * PPR / 64;       // B loads per phase
-    constexpr int SQ = Q < 256 ? 256 : Q;    // s / dt buffers hold whole 1 KB loads
-    constexpr int SL = SQ * 4 / 1024;        // loads of one chunk's s (or dt) row
+    constexpr int SQ = Q < 256 ? 256 : Q;    // s / delta buffers hold whole 1 KB loads
+    constexpr int SL = SQ * 4 / 1024;        // loads of one chunk's s (or delta) row
     constexpr int NTW = (N / 16 + 1) / 2;    // N tiles per wavefront
     __shared__ __attribute__((aligned(16))) __bf16 xs0[TP * P];
     __shared__ __attribute__((aligned(16))) __bf16 xs1[TP * P];
@@ -305,11 +306,11 @@ __global__ __launch_bounds__(512) void chunk_state_passing_bf16_kernel(
     const size_t xrow = (size_t)H * P, brow = (size_t)G * N;
     const bf16_t *xh = x + (size_t)b * L * xrow + (size_t)h * P;
     const bf16_t *bg = B + (size_t)b * L * brow + (size_t)g * N;
-    const size_t srow = ((size_t)b * H + h) * (size_t)nC * Q;  // this head's s / dt rows
+    const size_t srow = ((size_t)b * H + h) * (size_t)nC * Q;  // this head's s / delta rows
     const int nph = nC * NPH;
 
     // phase k (chunk k / NPH, tokens from (k % NPH) * TP) into buffer pair k & 1;
-    // a chunk's first phase also brings its s and dt rows (buffer pair c & 1)
+    // a chunk's first phase also brings its s and delta rows (buffer pair c & 1)
     auto issue = [&](int k) {
         const int c = k / NPH, t0 = c * Q + (k % NPH) * TP;
         __bf16 *xd = (k & 1) ? xs1 : xs0;
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(512) void chunk_state_passing_bf16_kernel(
             dma16(bg + (size_t)min(t0 + r, L - 1) * brow + q * 8, bd + i * 512);
         }
         if (k % NPH == 0 && w < 2 * SL) {
-            const int i = w % SL;  // waves 0..SL-1: s, SL..2SL-1: dt
+            const int i = w % SL;  // waves 0..SL-1: s, SL..2SL-1: delta
             // (for Q < 256 the lanes past the row re-read its last 16 bytes)
             const float *src = (w < SL ? dA_cumsum : delta) + srow + (size_t)c * Q +
                                min(i * 256 + l * 4, Q - 4);
@@ -363,10 +364,10 @@ __global__ __launch_bounds__(512) void chunk_state_passing_bf16_kernel(
 
     for (int k = 0; k < nph; ++k) {
         const int c = k / NPH, kq = k % NPH;
-        wait_barrier<0>();  // phase k (and, at a chunk start, its s and dt) in LDS
+        wait_barrier<0>();  // phase k (and, at a chunk start, its s and delta) in LDS
         if (k + 1 < nph) issue(k + 1);
         if (kq == 0) {
-            // token weights of chunk c: w_j = exp(s_end - s_j) dt_j (dt is zero past the end)
+            // token weights of chunk c: w_j = exp(s_end - s_j) delta_j (zero past the end)
             const float *svc = (c & 1) ? sv1 : sv0;
             const float *dvc = (c & 1) ? dv1 : dv0;
             const float se = svc[Q - 1];  // s is constant past the end
@@ -472,56 +473,57 @@ hipError_t launch_chunk_state_passing(const void *x, const void *B, const float 
 }
 
 template <typename T, int N, int Q>
-static void launch_cs(const void *x, const void *B, const void *dt, const float *dA, int batch,
+static void launch_cs(const void *x, const void *B, const float *dl, const float *dA, int batch,
                       int L, int H, int G, float *states, hipStream_t stream) {
     const int nC = (L + Q - 1) / Q;
     const dim3 grid(nC, H, batch);
     if constexpr (sizeof(T) == 2) {
         chunk_state_bf16_kernel<N, Q><<<grid, 512, 0, stream>>>(
             static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(B),
-            static_cast<const bf16_t *>(dt), dA, L, H, G, nC, states);
+            dl, dA, L, H, G, nC, states);
     } else {
         chunk_state_kernel<T, N, Q><<<grid, 512, 0, stream>>>(
-            static_cast<const T *>(x), static_cast<const T *>(B), static_cast<const T *>(dt), dA, L,
+            static_cast<const T *>(x), static_cast<const T *>(B), dl, dA, L,
             H, G, nC, states);
     }
 }
 
 template <typename T, int N>
-static bool cs_q(int Q, const void *x, const void *B, const void *dt, const float *dA, int batch,
+static bool cs_q(int Q, const void *x, const void *B, const float *dl, const float *dA, int batch,
                  int L, int H, int G, float *states, hipStream_t s) {
     switch (Q) {
-        case 64: launch_cs<T, N, 64>(x, B, dt, dA, batch, L, H, G, states, s); return true;
-        case 128: launch_cs<T, N, 128>(x, B, dt, dA, batch, L, H, G, states, s); return true;
-        case 256: launch_cs<T, N, 256>(x, B, dt, dA, batch, L, H, G, states, s); return true;
+        case 64: launch_cs<T, N, 64>(x, B, dl, dA, batch, L, H, G, states, s); return true;
+        case 128: launch_cs<T, N, 128>(x, B, dl, dA, batch, L, H, G, states, s); return true;
+        case 256: launch_cs<T, N, 256>(x, B, dl, dA, batch, L, H, G, states, s); return true;
         default: return false;
     }
 }
 
 template <typename T>
-static hipError_t dispatch_cs(const void *x, const void *B, const void *dt, const float *dA,
+static hipError_t dispatch_cs(const void *x, const void *B, const float *dl, const float *dA,
                               int batch, int L, int H, int G, int N, int Q, float *states,
                               hipStream_t s) {
     bool ok = false;
     switch (N) {
-        case 16: ok = cs_q<T, 16>(Q, x, B, dt, dA, batch, L, H, G, states, s); break;
-        case 32: ok = cs_q<T, 32>(Q, x, B, dt, dA, batch, L, H, G, states, s); break;
-        case 64: ok = cs_q<T, 64>(Q, x, B, dt, dA, batch, L, H, G, states, s); break;
-        case 128: ok = cs_q<T, 128>(Q, x, B, dt, dA, batch, L, H, G, states, s); break;
-        case 256: ok = cs_q<T, 256>(Q, x, B, dt, dA, batch, L, H, G, states, s); break;
+        case 16: ok = cs_q<T, 16>(Q, x, B, dl, dA, batch, L, H, G, states, s); break;
+        case 32: ok = cs_q<T, 32>(Q, x, B, dl, dA, batch, L, H, G, states, s); break;
+        case 64: ok = cs_q<T, 64>(Q, x, B, dl, dA, batch, L, H, G, states, s); break;
+        case 128: ok = cs_q<T, 128>(Q, x, B, dl, dA, batch, L, H, G, states, s); break;
+        case 256: ok = cs_q<T, 256>(Q, x, B, dl, dA, batch, L, H, G, states, s); break;
         default: break;
     }
     if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
-hipError_t launch_chunk_state(const void *x, const void *B, const void *dt, const float *dA_cumsum,
-                              int batch, int seqlen, int nheads, int ngroups, int dstate, int chunk,
-                              bool bf16, float *states, hipStream_t stream) {
+hipError_t launch_chunk_state(const void *x, const void *B, const float *delta,
+                              const float *dA_cumsum, int batch, int seqlen, int nheads,
+                              int ngroups, int dstate, int chunk, bool bf16, float *states,
+                              hipStream_t stream) {
     if (bf16)
-        return dispatch_cs<bf16_t>(x, B, dt, dA_cumsum, batch, seqlen, nheads, ngroups, dstate,
+        return dispatch_cs<bf16_t>(x, B, delta, dA_cumsum, batch, seqlen, nheads, ngroups, dstate,
                                    chunk, states, stream);
-    return dispatch_cs<float>(x, B, dt, dA_cumsum, batch, seqlen, nheads, ngroups, dstate, chunk,
+    return dispatch_cs<float>(x, B, delta, dA_cumsum, batch, seqlen, nheads, ngroups, dstate, chunk,
                               states, stream);
 }
 

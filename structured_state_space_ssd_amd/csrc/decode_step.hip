@@ -1,7 +1,9 @@
 // Recurrent (linear-mode) decode: one token for every (batch, head)
 // ("从Transformer到Mamba" tutorial, section 2.2; the linear mode of the
 // "Mamba-2架构深度解析" page, section 2.2 table):
-//   h <- exp(dt A_h) h + dt x B^T,   y = h C + D_h x   (output after the update).
+//   h <- exp(dt A_h) h + w x B^T,   y = h C + D_h x   (output after the update),
+// with dt the step size after DtOpts' preprocessing and w its input weight
+// (dt itself, or the zero-order hold's (exp(dt A) - 1) / A).
 //
 // Bandwidth-bound: the float32 P x N state is read once and written once.
 // One workgroup (4 wavefronts) per (batch, head); wavefront w owns state rows
@@ -19,15 +21,17 @@ template <typename T, int N>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     float *__restrict__ state, const T *__restrict__ x, const T *__restrict__ dt,
     const float *__restrict__ A, const T *__restrict__ B, const T *__restrict__ C,
-    const float *__restrict__ D, int H, int G, T *__restrict__ y) {
+    const float *__restrict__ D, int H, int G, T *__restrict__ y, DtOpts o) {
     constexpr int P = 64;
     constexpr int ITER = N / 16;  // float4 per lane: 16 rows * N / (64 lanes * 4)
     constexpr int LPR = N / 4;    // lanes sharing one state row within an instruction
     const int bh = blockIdx.x;
     const int b = bh / H, h = bh % H, g = h / (H / G);
     const int w = wave_id(), l = lane_id();
-    const float d = to_f32(dt[bh]);
-    const float a = exp2f(d * A[h] * kLog2e);
+    const float Ah = A[h];
+    const float d = step_size(o, to_f32(dt[bh]), o.bias ? o.bias[h] : 0.0f);
+    const float a = exp2f(d * Ah * kLog2e);
+    const float wt = input_weight(o, d, Ah);
     const float Dh = D ? D[h] : 0.0f;
 
     floatx4 *st = reinterpret_cast<floatx4 *>(state + ((size_t)bh * P + w * 16) * N);
@@ -50,7 +54,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     for (int m = 0; m < ITER; ++m) {
         const int p = w * 16 + (m * 256 + 4 * l) / N;
         xr[m] = to_f32(xp[p]);
-        const float dx = d * xr[m];
+        const float dx = wt * xr[m];
         floatx4 v = hv[m];
         float acc = 0.0f;
 #pragma unroll
@@ -77,17 +81,18 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 template <typename T>
 static hipError_t dispatch_decode(int N, float *state, const void *x, const void *dt,
                                   const float *A, const void *B, const void *C, const float *D,
-                                  int batch, int H, int G, void *y, hipStream_t stream) {
+                                  int batch, int H, int G, void *y, const DtOpts &o,
+                                  hipStream_t stream) {
     const dim3 grid(batch * H);
     const T *xx = static_cast<const T *>(x), *dd = static_cast<const T *>(dt);
     const T *bb = static_cast<const T *>(B), *cc = static_cast<const T *>(C);
     T *yy = static_cast<T *>(y);
     switch (N) {
-        case 16: decode_step_kernel<T, 16><<<grid, 256, 0, stream>>>(state, xx, dd, A, bb, cc, D, H, G, yy); break;
-        case 32: decode_step_kernel<T, 32><<<grid, 256, 0, stream>>>(state, xx, dd, A, bb, cc, D, H, G, yy); break;
-        case 64: decode_step_kernel<T, 64><<<grid, 256, 0, stream>>>(state, xx, dd, A, bb, cc, D, H, G, yy); break;
-        case 128: decode_step_kernel<T, 128><<<grid, 256, 0, stream>>>(state, xx, dd, A, bb, cc, D, H, G, yy); break;
-        case 256: decode_step_kernel<T, 256><<<grid, 256, 0, stream>>>(state, xx, dd, A, bb, cc, D, H, G, yy); break;
+        case 16: decode_step_kernel<T, 16><<<grid, 256, 0, stream>>>(state, xx, dd, A, bb, cc, D, H, G, yy, o); break;
+        case 32: decode_step_kernel<T, 32><<<grid, 256, 0, stream>>>(state, xx, dd, A, bb, cc, D, H, G, yy, o); break;
+        case 64: decode_step_kernel<T, 64><<<grid, 256, 0, stream>>>(state, xx, dd, A, bb, cc, D, H, G, yy, o); break;
+        case 128: decode_step_kernel<T, 128><<<grid, 256, 0, stream>>>(state, xx, dd, A, bb, cc, D, H, G, yy, o); break;
+        case 256: decode_step_kernel<T, 256><<<grid, 256, 0, stream>>>(state, xx, dd, A, bb, cc, D, H, G, yy, o); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -95,12 +100,13 @@ static hipError_t dispatch_decode(int N, float *state, const void *x, const void
 
 hipError_t launch_decode_step(float *state, const void *x, const void *dt, const float *A,
                               const void *B, const void *C, const float *D, int batch, int nheads,
-                              int ngroups, int dstate, bool bf16, void *y, hipStream_t stream) {
+                              int ngroups, int dstate, bool bf16, const DtOpts &opts, void *y,
+                              hipStream_t stream) {
     if (bf16)
         return dispatch_decode<bf16_t>(dstate, state, x, dt, A, B, C, D, batch, nheads, ngroups, y,
-                                       stream);
+                                       opts, stream);
     return dispatch_decode<float>(dstate, state, x, dt, A, B, C, D, batch, nheads, ngroups, y,
-                                  stream);
+                                  opts, stream);
 }
 
 }  // namespace ssd

@@ -51,6 +51,23 @@ int check_dims(int batch, int seqlen, int nheads, int headdim, int ngroups, int 
 
 int status_of(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
+// Checks an ssd_options (NULL: every option off) and converts it for the kernels.
+int dt_opts(const ssd_options *o, ssd::DtOpts &d) {
+    d = ssd::DtOpts{nullptr, 0.0f, 0.0f, 0, 0, 0};
+    if (!o) return SSD_OK;
+    if (o->discretization != SSD_DISC_EULER && o->discretization != SSD_DISC_ZOH)
+        return SSD_ERR_OPTION;
+    if (o->dt_clamp && !(o->dt_min <= o->dt_max)) return SSD_ERR_OPTION;  // NaN bounds fail too
+    if ((reinterpret_cast<uintptr_t>(o->dt_bias) & 3u) != 0) return SSD_ERR_UNSUPPORTED;
+    d.bias = o->dt_bias;
+    d.lo = o->dt_min;
+    d.hi = o->dt_max;
+    d.softplus = o->dt_softplus != 0;
+    d.clamp = o->dt_clamp != 0;
+    d.zoh = o->discretization == SSD_DISC_ZOH;
+    return SSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -65,6 +82,9 @@ const char *ssd_strerror(int status) {
                    "chunk in {64,128,256}, dtype SSD_F32/SSD_BF16, 16-byte aligned buffers)";
         case SSD_ERR_WORKSPACE: return "workspace missing or too small";
         case SSD_ERR_HIP: return "HIP runtime error at kernel launch";
+        case SSD_ERR_OPTION:
+            return "invalid ssd_options (discretization not SSD_DISC_EULER/SSD_DISC_ZOH, or "
+                   "dt_clamp with dt_min > dt_max or a NaN bound)";
         default: return "unknown status";
     }
 }
@@ -96,25 +116,30 @@ int ssd_chunk_cb(const void *B, const void *C, int batch, int seqlen, int ngroup
 }
 
 int ssd_chunk_cumsum(const void *dt, const float *A, int batch, int seqlen, int nheads, int chunk,
-                     int dtype, float *dA_cumsum, float *delta, void *stream) {
+                     int dtype, float *dA_cumsum, float *delta, const ssd_options *opts,
+                     void *stream) {
     if (!dt || !A || !dA_cumsum) return SSD_ERR_NULL;
     if (batch < 1 || seqlen < 1 || nheads < 1) return SSD_ERR_SHAPE;
     if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
-    if (delta && (reinterpret_cast<uintptr_t>(delta) & 15u) != 0) return SSD_ERR_UNSUPPORTED;
+    if (delta && !aligned16(delta)) return SSD_ERR_UNSUPPORTED;
+    ssd::DtOpts o;
+    const int rc = dt_opts(opts, o);
+    if (rc != SSD_OK) return rc;
     return status_of(ssd::launch_chunk_cumsum(dt, A, batch, seqlen, nheads, chunk,
-                                              dtype == SSD_BF16, dA_cumsum, delta,
+                                              dtype == SSD_BF16, o, dA_cumsum, delta,
                                               static_cast<hipStream_t>(stream)));
 }
 
-int ssd_chunk_state(const void *x, const void *B, const void *dt, const float *dA_cumsum, int batch,
-                    int seqlen, int nheads, int headdim, int ngroups, int dstate, int chunk,
-                    int dtype, float *states, void *stream) {
-    if (!x || !B || !dt || !dA_cumsum || !states) return SSD_ERR_NULL;
+int ssd_chunk_state(const void *x, const void *B, const float *delta, const float *dA_cumsum,
+                    int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate,
+                    int chunk, int dtype, float *states, void *stream) {
+    if (!x || !B || !delta || !dA_cumsum || !states) return SSD_ERR_NULL;
     int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
     if (rc != SSD_OK) return rc;
     if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
-    if (!aligned16(x) || !aligned16(B) || !aligned16(states)) return SSD_ERR_UNSUPPORTED;
-    return status_of(ssd::launch_chunk_state(x, B, dt, dA_cumsum, batch, seqlen, nheads, ngroups,
+    if (!aligned16(x) || !aligned16(B) || !aligned16(states) || !aligned16(delta))
+        return SSD_ERR_UNSUPPORTED;
+    return status_of(ssd::launch_chunk_state(x, B, delta, dA_cumsum, batch, seqlen, nheads, ngroups,
                                              dstate, chunk, dtype == SSD_BF16, states,
                                              static_cast<hipStream_t>(stream)));
 }
@@ -134,11 +159,11 @@ int ssd_state_passing(const float *states, const float *dA_cumsum, const float *
                                                final_state, static_cast<hipStream_t>(stream)));
 }
 
-int ssd_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *B,
+int ssd_chunk_scan(const void *x, const float *delta, const float *dA_cumsum, const void *B,
                    const void *C, const void *cb, const float *D, const void *chunk_init,
                    int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate,
                    int chunk, int dtype, void *y, void *stream) {
-    if (!x || !dt || !dA_cumsum || !C || !chunk_init || !y) return SSD_ERR_NULL;
+    if (!x || !delta || !dA_cumsum || !C || !chunk_init || !y) return SSD_ERR_NULL;
     int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
     if (rc != SSD_OK) return rc;
     if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
@@ -146,19 +171,19 @@ int ssd_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const 
     const bool reads_cb = ssd::chunk_scan_reads_cb(bf16);
     if (reads_cb ? !cb : !B) return SSD_ERR_NULL;
     if (!aligned16(x) || !aligned16(C) || !aligned16(chunk_init) || !aligned16(y) ||
-        !aligned16(dA_cumsum) || (reads_cb ? (reinterpret_cast<uintptr_t>(cb) % 32) != 0
-                                           : !aligned16(B)))
+        !aligned16(dA_cumsum) || !aligned16(delta) ||
+        (reads_cb ? (reinterpret_cast<uintptr_t>(cb) % 32) != 0 : !aligned16(B)))
         return SSD_ERR_UNSUPPORTED;
-    return status_of(ssd::launch_chunk_scan(x, dt, dA_cumsum, B, C, cb, D, chunk_init, batch,
+    return status_of(ssd::launch_chunk_scan(x, delta, dA_cumsum, B, C, cb, D, chunk_init, batch,
                                             seqlen, nheads, ngroups, dstate, chunk, bf16, y,
                                             static_cast<hipStream_t>(stream)));
 }
 
-int ssd_forward_timed(const void *x, const void *dt, const float *A, const void *B,
-                      const void *C, const float *D, int batch, int seqlen, int nheads,
-                      int headdim, int ngroups, int dstate, int chunk, int dtype,
-                      const float *init_state, void *y, float *final_state, void *workspace,
-                      size_t workspace_bytes, void *stream, void *const *events) {
+int ssd_forward_ex(const void *x, const void *dt, const float *A, const void *B, const void *C,
+                   const float *D, int batch, int seqlen, int nheads, int headdim, int ngroups,
+                   int dstate, int chunk, int dtype, const float *init_state, void *y,
+                   float *final_state, void *workspace, size_t workspace_bytes,
+                   const ssd_options *opts, void *stream, void *const *events) {
     if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
     int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
     if (rc != SSD_OK) return rc;
@@ -166,6 +191,9 @@ int ssd_forward_timed(const void *x, const void *dt, const float *A, const void 
     if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) ||
         (init_state && !aligned16(init_state)) || (final_state && !aligned16(final_state)))
         return SSD_ERR_UNSUPPORTED;
+    ssd::DtOpts o;
+    rc = dt_opts(opts, o);
+    if (rc != SSD_OK) return rc;
     const Workspace ws = layout(batch, seqlen, nheads, headdim, ngroups, dstate, chunk,
                                 dtype == SSD_BF16);
     if (!workspace || workspace_bytes < ws.total) return SSD_ERR_WORKSPACE;
@@ -187,7 +215,8 @@ int ssd_forward_timed(const void *x, const void *dt, const float *A, const void 
 
     hipError_t e = mark(0);
     if (e == hipSuccess)
-        e = ssd::launch_chunk_cumsum(dt, A, batch, seqlen, nheads, chunk, bf16, cumsum, delta, s);
+        e = ssd::launch_chunk_cumsum(dt, A, batch, seqlen, nheads, chunk, bf16, o, cumsum, delta,
+                                     s);
     if (e == hipSuccess) e = mark(1);
     if (ssd::state_passing_fused(batch, nheads, bf16)) {
         // stages 2 and 3 in one kernel; the state_passing interval stays empty
@@ -198,7 +227,7 @@ int ssd_forward_timed(const void *x, const void *dt, const float *A, const void 
         if (e == hipSuccess) e = mark(2);
     } else {
         if (e == hipSuccess)
-            e = ssd::launch_chunk_state(x, B, dt, cumsum, batch, seqlen, nheads, ngroups, dstate,
+            e = ssd::launch_chunk_state(x, B, delta, cumsum, batch, seqlen, nheads, ngroups, dstate,
                                         chunk, bf16, states, s);
         if (e == hipSuccess) e = mark(2);
         if (e == hipSuccess)
@@ -210,32 +239,52 @@ int ssd_forward_timed(const void *x, const void *dt, const float *A, const void 
         e = ssd::launch_chunk_cb(B, C, batch, seqlen, ngroups, dstate, chunk, bf16, cb, s);
     if (e == hipSuccess) e = mark(4);
     if (e == hipSuccess)
-        e = ssd::launch_chunk_scan(x, dt, cumsum, B, C, cb, D, cinit, batch, seqlen, nheads,
+        e = ssd::launch_chunk_scan(x, delta, cumsum, B, C, cb, D, cinit, batch, seqlen, nheads,
                                    ngroups, dstate, chunk, bf16, y, s);
     if (e == hipSuccess) e = mark(5);
     return status_of(e);
+}
+
+int ssd_forward_timed(const void *x, const void *dt, const float *A, const void *B,
+                      const void *C, const float *D, int batch, int seqlen, int nheads,
+                      int headdim, int ngroups, int dstate, int chunk, int dtype,
+                      const float *init_state, void *y, float *final_state, void *workspace,
+                      size_t workspace_bytes, void *stream, void *const *events) {
+    return ssd_forward_ex(x, dt, A, B, C, D, batch, seqlen, nheads, headdim, ngroups, dstate,
+                          chunk, dtype, init_state, y, final_state, workspace, workspace_bytes,
+                          nullptr, stream, events);
 }
 
 int ssd_forward(const void *x, const void *dt, const float *A, const void *B, const void *C,
                 const float *D, int batch, int seqlen, int nheads, int headdim, int ngroups,
                 int dstate, int chunk, int dtype, const float *init_state, void *y,
                 float *final_state, void *workspace, size_t workspace_bytes, void *stream) {
-    return ssd_forward_timed(x, dt, A, B, C, D, batch, seqlen, nheads, headdim, ngroups, dstate,
-                             chunk, dtype, init_state, y, final_state, workspace, workspace_bytes,
-                             stream, nullptr);
+    return ssd_forward_ex(x, dt, A, B, C, D, batch, seqlen, nheads, headdim, ngroups, dstate,
+                          chunk, dtype, init_state, y, final_state, workspace, workspace_bytes,
+                          nullptr, stream, nullptr);
 }
 
-int ssd_step(float *state, const void *x, const void *dt, const float *A, const void *B,
-             const void *C, const float *D, int batch, int nheads, int headdim, int ngroups,
-             int dstate, int dtype, void *y, void *stream) {
+int ssd_step_ex(float *state, const void *x, const void *dt, const float *A, const void *B,
+                const void *C, const float *D, int batch, int nheads, int headdim, int ngroups,
+                int dstate, int dtype, void *y, const ssd_options *opts, void *stream) {
     if (!state || !x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
     int rc = check_dims(batch, 1, nheads, headdim, ngroups, dstate);
     if (rc != SSD_OK) return rc;
     if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
     if (!aligned16(state)) return SSD_ERR_UNSUPPORTED;
+    ssd::DtOpts o;
+    rc = dt_opts(opts, o);
+    if (rc != SSD_OK) return rc;
     return status_of(ssd::launch_decode_step(state, x, dt, A, B, C, D, batch, nheads, ngroups,
-                                             dstate, dtype == SSD_BF16, y,
+                                             dstate, dtype == SSD_BF16, o, y,
                                              static_cast<hipStream_t>(stream)));
+}
+
+int ssd_step(float *state, const void *x, const void *dt, const float *A, const void *B,
+             const void *C, const float *D, int batch, int nheads, int headdim, int ngroups,
+             int dstate, int dtype, void *y, void *stream) {
+    return ssd_step_ex(state, x, dt, A, B, C, D, batch, nheads, headdim, ngroups, dstate, dtype, y,
+                       nullptr, stream);
 }
 
 }  // extern "C"

@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ssd_launch.h"
+
 namespace ssd {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -22,6 +24,19 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_t;  // bf16 storage in global memory
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// The step size for raw value v of a head whose bias is `bias` (0 if none).
+__device__ __forceinline__ float step_size(const DtOpts &o, float v, float bias) {
+    v += bias;
+    if (o.softplus) v = fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v)));  // log(1 + e^v)
+    if (o.clamp) v = fminf(fmaxf(v, o.lo), o.hi);
+    return v;
+}
+
+// Weight of the input term for step size d of a head with decay rate a.
+__device__ __forceinline__ float input_weight(const DtOpts &o, float d, float a) {
+    return (o.zoh && a != 0.0f) ? expm1f(d * a) / a : d;
+}
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
     return __uint_as_float(static_cast<uint32_t>(v) << 16);

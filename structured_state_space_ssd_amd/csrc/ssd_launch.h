@@ -8,12 +8,29 @@
 
 namespace ssd {
 
-// delta (nullable): dt as float32 in dA_cumsum's chunk-padded layout.
-hipError_t launch_chunk_cumsum(const void *dt, const float *A, int batch, int seqlen, int nheads,
-                               int chunk, bool bf16, float *dA_cumsum, float *delta,
-                               hipStream_t stream);
+// Step-size preprocessing and input discretisation, passed to the kernels by
+// value. The selection mechanism makes the step size a projection of the
+// input made positive by softplus ("从Transformer到Mamba" tutorial, section
+// 3.2): `bias` is that projection's per-head constant term, added first; an
+// optional clamp to [lo, hi] follows softplus (the tutorial's section 8.2
+// adjusts the range step sizes are produced in). The input term is weighted by
+// the step size (Euler) or, with `zoh`, by the zero-order hold's
+// (exp(dt A) - 1) / A (tutorial section 2.2; "Mamba 模型" section 2.3.1).
+struct DtOpts {
+    const float *bias;  // [H], or nullptr
+    float lo, hi;       // clamp bounds, read when clamp != 0
+    int softplus, clamp, zoh;
+};
 
-hipError_t launch_chunk_state(const void *x, const void *B, const void *dt, const float *dA_cumsum,
+// delta (nullable): each token's input weight (the preprocessed step size, or
+// its zero-order-hold weight) as float32 in dA_cumsum's chunk-padded layout,
+// zero past the end. The later stages read it in place of dt.
+hipError_t launch_chunk_cumsum(const void *dt, const float *A, int batch, int seqlen, int nheads,
+                               int chunk, bool bf16, const DtOpts &opts, float *dA_cumsum,
+                               float *delta, hipStream_t stream);
+
+hipError_t launch_chunk_state(const void *x, const void *B, const float *delta,
+                              const float *dA_cumsum,
                               int batch, int seqlen, int nheads, int ngroups, int dstate, int chunk,
                               bool bf16, float *states, hipStream_t stream);
 
@@ -42,13 +59,14 @@ hipError_t launch_chunk_cb(const void *B, const void *C, int batch, int seqlen, 
 // the C B^T tiles of launch_chunk_cb (reads cb, ignores B).
 bool chunk_scan_reads_cb(bool bf16);
 
-hipError_t launch_chunk_scan(const void *x, const void *dt, const float *dA_cumsum, const void *B,
+hipError_t launch_chunk_scan(const void *x, const float *delta, const float *dA_cumsum, const void *B,
                              const void *C, const void *cb, const float *D, const void *chunk_init,
                              int batch, int seqlen, int nheads, int ngroups, int dstate, int chunk,
                              bool bf16, void *y, hipStream_t stream);
 
 hipError_t launch_decode_step(float *state, const void *x, const void *dt, const float *A,
                               const void *B, const void *C, const float *D, int batch, int nheads,
-                              int ngroups, int dstate, bool bf16, void *y, hipStream_t stream);
+                              int ngroups, int dstate, bool bf16, const DtOpts &opts, void *y,
+                              hipStream_t stream);
 
 }  // namespace ssd

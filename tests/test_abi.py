@@ -12,6 +12,7 @@ HEADER = os.path.join(ROOT, "include", "ssd.h")
 LIB = os.path.join(ROOT, "structured_state_space_ssd_amd", "libssd.so")
 
 SSD_OK, SSD_ERR_NULL, SSD_ERR_SHAPE, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = 0, -1, -2, -3, -4, -5
+SSD_ERR_OPTION = -6
 
 
 def declared_functions():
@@ -32,7 +33,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("ssd_forward", "ssd_step", "ssd_forward_workspace_size", "ssd_strerror",
                      "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_cb",
-                     "ssd_chunk_scan", "ssd_forward_timed", "ssd_chunk_cb_size"):
+                     "ssd_chunk_scan", "ssd_forward_timed", "ssd_chunk_cb_size", "ssd_forward_ex",
+                     "ssd_step_ex"):
         assert required in names
 
 
@@ -43,7 +45,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_strerror(lib):
-    for code in (SSD_OK, SSD_ERR_NULL, SSD_ERR_SHAPE, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP, 42):
+    for code in (SSD_OK, SSD_ERR_NULL, SSD_ERR_SHAPE, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP,
+                 SSD_ERR_OPTION, 42):
         s = lib.ssd_strerror(code)
         assert isinstance(s, bytes) and len(s) > 0
     assert lib.ssd_strerror(42) == b"unknown status"
@@ -128,14 +131,17 @@ def test_step_rejects(lib):
 
 
 def test_stage_entry_points_reject(lib):
-    assert lib.ssd_chunk_cumsum(None, FAKE, 1, 10, 2, 64, 1, FAKE, None, None) == SSD_ERR_NULL
-    assert lib.ssd_chunk_cumsum(FAKE, FAKE, 1, 10, 2, 100, 1, FAKE, None, None) == SSD_ERR_UNSUPPORTED
+    assert lib.ssd_chunk_cumsum(None, FAKE, 1, 10, 2, 64, 1, FAKE, None, None, None) == SSD_ERR_NULL
+    assert lib.ssd_chunk_cumsum(FAKE, FAKE, 1, 10, 2, 100, 1, FAKE, None, None, None) == SSD_ERR_UNSUPPORTED
     assert lib.ssd_chunk_cumsum(FAKE, FAKE, 1, 10, 2, 64, 1, FAKE, ctypes.c_void_p(0x100004),
-                                None) == SSD_ERR_UNSUPPORTED  # misaligned delta
+                                None, None) == SSD_ERR_UNSUPPORTED  # misaligned delta
     assert lib.ssd_chunk_state(FAKE, FAKE, FAKE, FAKE, 1, 10, 3, 64, 2, 64, 64, 1, FAKE, None) == SSD_ERR_SHAPE
+    assert lib.ssd_chunk_state(FAKE, FAKE, None, FAKE, 1, 10, 2, 64, 2, 64, 64, 1, FAKE, None) == SSD_ERR_NULL
+    assert lib.ssd_chunk_state(FAKE, FAKE, ctypes.c_void_p(0x100004), FAKE, 1, 10, 2, 64, 2, 64, 64, 1,
+                               FAKE, None) == SSD_ERR_UNSUPPORTED  # misaligned delta
     assert lib.ssd_state_passing(FAKE, FAKE, None, 1, 10, 2, 64, 64, 64, 1, None, None, None) == SSD_ERR_NULL
     assert lib.ssd_state_passing(FAKE, FAKE, None, 1, 10, 2, 64, 64, 64, 4, FAKE, None, None) == SSD_ERR_UNSUPPORTED
-    # ssd_chunk_scan(x, dt, dA, B, C, cb, D, chunk_init, Bt, L, H, P, G, N, Q, dtype, y, stream)
+    # ssd_chunk_scan(x, delta, dA, B, C, cb, D, chunk_init, Bt, L, H, P, G, N, Q, dtype, y, stream)
     assert lib.ssd_chunk_scan(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 10, 2, 64, 1, 64, 256, 9,
                               FAKE, None) == SSD_ERR_UNSUPPORTED
     assert lib.ssd_chunk_scan(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 1, 10, 2, 64, 1, 64, 256, 1,
@@ -147,5 +153,52 @@ def test_stage_entry_points_reject(lib):
                               FAKE, None) == SSD_ERR_NULL
     assert lib.ssd_chunk_scan(FAKE, FAKE, FAKE, ctypes.c_void_p(0x100008), FAKE, None, None, FAKE, 1, 10,
                               2, 64, 1, 64, 256, 1, FAKE, None) == SSD_ERR_UNSUPPORTED
+    assert lib.ssd_chunk_scan(FAKE, None, FAKE, FAKE, FAKE, None, None, FAKE, 1, 10, 2, 64, 1, 64, 256, 1,
+                              FAKE, None) == SSD_ERR_NULL
+    assert lib.ssd_chunk_scan(FAKE, ctypes.c_void_p(0x100004), FAKE, FAKE, FAKE, None, None, FAKE, 1, 10,
+                              2, 64, 1, 64, 256, 1, FAKE, None) == SSD_ERR_UNSUPPORTED  # misaligned delta
     assert lib.ssd_chunk_cb(FAKE, None, 1, 10, 1, 64, 64, 1, FAKE, None) == SSD_ERR_NULL
     assert lib.ssd_chunk_cb(FAKE, FAKE, 1, 10, 1, 48, 64, 1, FAKE, None) == SSD_ERR_UNSUPPORTED
+
+
+def _opts(**kw):
+    from structured_state_space_ssd_amd import _native
+    o = _native.SsdOptions(None, 0, 0, 0.0, 0.0, 0)
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return ctypes.byref(o)
+
+
+BAD_OPTIONS = [
+    (dict(discretization=2), SSD_ERR_OPTION),
+    (dict(discretization=-1), SSD_ERR_OPTION),
+    (dict(dt_clamp=1, dt_min=0.5, dt_max=0.1), SSD_ERR_OPTION),
+    (dict(dt_clamp=1, dt_min=float("nan"), dt_max=0.1), SSD_ERR_OPTION),
+    (dict(dt_clamp=1, dt_min=0.0, dt_max=float("nan")), SSD_ERR_OPTION),
+    (dict(dt_bias=0x100002), SSD_ERR_UNSUPPORTED),  # misaligned float pointer
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_OPTIONS)
+def test_options_rejected(lib, kw, code):
+    """Invalid ssd_options are refused by every entry point that takes them
+    (all other arguments valid, so the options check is what fails)."""
+    o = _opts(**kw)
+    ws = lib.ssd_forward_workspace_size(1, 128, 4, 64, 1, 64, 64, 1)
+    rc = lib.ssd_forward_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 128, 4, 64, 1, 64, 64, 1, None, FAKE,
+                            None, FAKE, ws, o, None, None)
+    assert rc == code
+    rc = lib.ssd_step_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, 8, 64, 2, 128, 1, FAKE, o, None)
+    assert rc == code
+    rc = lib.ssd_chunk_cumsum(FAKE, FAKE, 1, 10, 2, 64, 1, FAKE, FAKE, o, None)
+    assert rc == code
+
+
+def test_options_checked_after_shapes(lib):
+    """A bad size is reported as such even when the options are bad too."""
+    o = _opts(discretization=7)
+    rc = lib.ssd_forward_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 128, 4, 64, 1, 64, 64, 1, None, FAKE,
+                            None, FAKE, 1 << 40, o, None, None)
+    assert rc == SSD_ERR_SHAPE
+    rc = lib.ssd_step_ex(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, 8, 64, 2, 128, 1, FAKE, o, None)
+    assert rc == SSD_ERR_NULL

@@ -21,32 +21,51 @@ def _ssd():
     return ssd
 
 
-def run_forward(w, d, D, init, units=None):
+def run_forward(w, d, D, init, opts=None):
     ssd = _ssd()
+    opts = dict(opts or {})
+    if opts.get("dt_bias") is not None:
+        opts["dt_bias"] = up(opts["dt_bias"])
     y, fs = ssd.forward(up(d["x"]), up(d["dt"]), up(d["A"]), up(d["B"]), up(d["C"]),
                         None if D is None else up(D), chunk=w.chunk, init_state=up(init),
-                        return_final_state=True)
+                        return_final_state=True, **opts)
     torch.cuda.synchronize()
     return y, fs
 
 
-def check_forward(w, units=None, init=None, both_D=True):
-    """Compare y and the final state with the oracle (all units or a sample)."""
+def with_options(w, d, raw=False, dt_softplus=False, dt_limit=None, zoh=False):
+    """The option set for a case: raw=True swaps in pre-softplus dt values and
+    a per-head bias (ssd_workloads.generate_dt_raw); returns the keyword
+    arguments shared by the oracle and the library."""
+    opts = dict(dt_softplus=dt_softplus, dt_limit=dt_limit, zoh=zoh, dt_bias=None)
+    if raw:
+        r = W.generate_dt_raw(w)
+        d["dt"] = r["dt"]
+        opts["dt_bias"] = r["dt_bias"]
+    return opts
+
+
+def check_forward(w, units=None, init=None, both_D=True, **option_kw):
+    """Compare y and the final state with the oracle (all units or a sample).
+    ``option_kw`` (see with_options) turns on step-size preprocessing and the
+    zero-order-hold input weight on both sides."""
     print_case(f"[forward] {w.name} Bt={w.batch} L={w.seqlen} H={w.nheads} G={w.ngroups} "
-               f"N={w.dstate} Q={w.chunk} {w.dtype} units={'all' if units is None else len(units)}")
+               f"N={w.dstate} Q={w.chunk} {w.dtype} units={'all' if units is None else len(units)} "
+               f"options={option_kw or 'none'}")
     d = W.generate(w)
+    opts = with_options(w, d, **option_kw) if option_kw else None
     if init is None:
         init = d["init"]
     H = w.nheads
     uu = np.arange(w.batch * H) if units is None else np.asarray(units)
     # oracle without D; the D x term is added exactly in float64 (y is linear in it)
     y0, s0, _ = oracle.forward(d["x"].val, d["dt"].val, d["A"], d["B"].val, d["C"].val, None,
-                               init, units=None if units is None else uu)
+                               init, units=None if units is None else uu, **(opts or {}))
     xv = units_view(d["x"].val, uu, H).astype(np.float64)
     Dv = d["D"].astype(np.float64)[uu % H][:, None, None]
     errs = {}
     for with_D in ([True, False] if both_D else [True]):
-        y, fs = run_forward(w, d, d["D"] if with_D else None, init)
+        y, fs = run_forward(w, d, d["D"] if with_D else None, init, opts)
         yg = units_view(down(y), uu, H)
         yref = y0 + Dv * xv if with_D else y0
         errs[f"y{'_D' if with_D else '_noD'}"] = rel_l2(yg, yref)
@@ -88,10 +107,15 @@ def test_decode_64_steps_zero_init():
     _decode(W.WORKLOADS["decode"], zero_init=True)
 
 
-def _decode(w, zero_init, nunits=512):
+def _decode(w, zero_init, nunits=512, **option_kw):
     ssd = _ssd()
-    print_case(f"[decode] Bt={w.batch} H={w.nheads} N={w.dstate} steps={w.seqlen} zero_init={zero_init}")
+    print_case(f"[decode] {w.name} Bt={w.batch} H={w.nheads} N={w.dstate} steps={w.seqlen} "
+               f"zero_init={zero_init} options={option_kw or 'none'}")
     d = W.generate(w)
+    opts = with_options(w, d, **option_kw) if option_kw else {}
+    gopts = dict(opts)
+    if gopts.get("dt_bias") is not None:
+        gopts["dt_bias"] = up(gopts["dt_bias"])
     H, P, N = w.nheads, w.headdim, w.dstate
     rng = np.random.default_rng(123)
     units = np.sort(rng.choice(w.batch * H, size=nunits, replace=False))
@@ -102,10 +126,10 @@ def _decode(w, zero_init, nunits=512):
     A, D = up(d["A"]), up(d["D"])
     ys, yos = [], []
     for t in range(w.seqlen):
-        y = ssd.step(state, X[t], DT[t], A, Bv[t], Cv[t], D)
+        y = ssd.step(state, X[t], DT[t], A, Bv[t], Cv[t], D, **gopts)
         ys.append(down(y).reshape(-1, P)[units])
         yos.append(oracle.step(st_o, d["x"].val[t], d["dt"].val[t], d["A"], d["B"].val[t],
-                               d["C"].val[t], d["D"], units=units))
+                               d["C"].val[t], d["D"], units=units, **opts))
     torch.cuda.synchronize()
     ey = rel_l2(np.stack(ys), np.stack(yos))
     es = rel_l2(down(state).reshape(-1, P, N)[units], st_o)
@@ -163,3 +187,57 @@ def test_fused_state_path(N, Q):
 def test_fused_state_path_single_chunk_short():
     # one partial chunk only: the state passing reduces to H_1 = exp(s_end) H_0 + S_0
     check_forward(W.small("fused_short", 16, 37, 32, 64, 1, 64, 256, "bf16", seed=620, init_std=0.3))
+
+
+# ------------------------------------ step-size preprocessing and zero-order hold
+#
+# dt_bias + softplus + clamp (the selection mechanism's step size) and the
+# zero-order-hold input weight (exp(dt A) - 1) / A, alone and together, on the
+# separate-stage path (f32, and bf16 with few units), the fused bf16 path and
+# the decode step. The clamp bounds are hit on both sides.
+
+OPTION_SETS = {
+    "zoh": dict(zoh=True),
+    "softplus_bias": dict(raw=True, dt_softplus=True),
+    "softplus_bias_clamp": dict(raw=True, dt_softplus=True, dt_limit=(4e-3, 3e-2)),
+    "all_zoh": dict(raw=True, dt_softplus=True, dt_limit=(4e-3, 3e-2), zoh=True),
+}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", sorted(OPTION_SETS))
+def test_options_forward(name, dtype):
+    w = W.small(f"opt_{name}_{dtype}", 2, 2 * 128 + 37, 4, 64, 2, 64, 128, dtype,
+                seed=700 + len(name), init_std=0.2)
+    check_forward(w, **OPTION_SETS[name])
+
+
+@pytest.mark.parametrize("name", ["zoh", "all_zoh"])
+def test_options_fused_state_path(name):
+    w = W.small(f"opt_fused_{name}", 8, 2 * 256 + 45, 64, 64, 4, 64, 256, "bf16", seed=710,
+                init_std=0.2)
+    assert w.batch * w.nheads >= 512
+    check_forward(w, **OPTION_SETS[name])
+
+
+def test_options_strong_decay_zoh():
+    # large steps: the zoh weight (1 - e^{dt A}) / |A| saturates at 1/|A|, far from dt
+    check_forward(W.small("opt_strong_zoh", 2, 300, 4, 64, 1, 64, 128, "f32", seed=711,
+                          dt_lo=0.5, dt_hi=2.0), zoh=True)
+
+
+def test_mamba2_2p7b_all_options_sampled():
+    w = W.WORKLOADS["mamba2_2.7b"]
+    check_forward(w, units=[0, 79, 80 * 3 + 41, 80 * 7 + 5, 80 * 8 - 1], both_D=False,
+                  **OPTION_SETS["all_zoh"])
+
+
+@pytest.mark.parametrize("name", ["zoh", "all_zoh"])
+def test_options_decode(name):
+    _decode(W.WORKLOADS["decode"], zero_init=False, nunits=256, **OPTION_SETS[name])
+
+
+def test_options_decode_f32():
+    w = W.Workload("decode_f32_opts", 16, 12, 8, 64, 2, 64, 0, "f32", 1 / 8, 1e-3, 1e-1,
+                   init_std=0.2, decode=True, seed=712)
+    _decode(w, zero_init=False, nunits=64, **OPTION_SETS["all_zoh"])

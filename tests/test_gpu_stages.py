@@ -49,12 +49,42 @@ def test_stage_chunk_cumsum(w):
     ref = oracle.chunk_cumsum(d["dt"].val, d["A"], w.chunk)
     # fp32 prefix sums of at most Q terms: relative error well below 1e-5
     assert rel_l2(s, ref) < 1e-5
-    # the float32 copy of dt: exact, zero past the end
+    # the input weights without options: dt itself in float32, exact, zero past the end
     dl = down(out["delta"])
     Lp = w.nchunks * w.chunk
     want = np.zeros((w.batch, w.nheads, Lp))
     want[:, :, : w.seqlen] = d["dt"].val.astype(np.float64).transpose(0, 2, 1)
     assert np.array_equal(dl, want)
+
+
+@pytest.mark.parametrize("zoh", [False, True])
+@pytest.mark.parametrize("w", CASES[:2], ids=lambda w: w.name)
+def test_stage_chunk_cumsum_options(w, zoh):
+    """Stage 1 with bias + softplus + clamp (and the zero-order hold): s sums
+    step * A over the preprocessed steps and delta holds each token's input
+    weight, both against float64 numpy written from the definitions."""
+    print_case(f"[stage cumsum options] {w.name} zoh={zoh}")
+    ssd = _ssd()
+    raw = W.generate_dt_raw(w)
+    d = W.generate(w)
+    sp = np.logaddexp(0.0, raw["dt"].val.astype(np.float64) + raw["dt_bias"])
+    # clamp bounds at the 15th and 85th percentiles: both sides are hit
+    lo, hi = (np.float32(np.quantile(sp, q)) for q in (0.15, 0.85))
+    opts = ssd.options(dt_bias=up(raw["dt_bias"]), dt_softplus=True, dt_limit=(lo, hi), zoh=zoh)
+    s, dl = ssd.chunk_cumsum(up(raw["dt"]), up(d["A"]), w.chunk, return_delta=True, opts=opts)
+    torch.cuda.synchronize()
+    A = d["A"].astype(np.float64)
+    step = np.clip(sp, lo, hi)
+    assert (step == lo).mean() > 0.1 and (step == hi).mean() > 0.1
+    ref_s = oracle.chunk_cumsum(step, A, w.chunk)
+    assert rel_l2(down(s)[:, :, : w.seqlen], ref_s) < 1e-5
+    wt = np.expm1(step * A) / A if zoh else step
+    Lp = w.nchunks * w.chunk
+    want = np.zeros((w.batch, w.nheads, Lp))
+    want[:, :, : w.seqlen] = wt.transpose(0, 2, 1)
+    got = down(dl)
+    assert np.all(got[:, :, w.seqlen:] == 0)
+    assert np.allclose(got, want, rtol=5e-6, atol=0)
 
 
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
