@@ -42,8 +42,9 @@ def accounting(w):
 
     Bytes: every input read once and every output written once, at its storage
     width (bf16 2 B for x, dt, B, C, y and, in bf16 runs, chunk_init; float32
-    4 B for A, D, dA_cumsum and the chunk states). B and C are counted once per
-    group, not per head.
+    4 B for A, D, dA_cumsum, the per-token input weights delta and the chunk
+    states). B and C are counted once per group, not per head. Stages 2 and 4
+    read delta (written by stage 1, the size of dA_cumsum) in place of dt.
     The C B^T tiles (float path: chunk_cb output, chunk_scan input) are
     counted once each way; the bf16 chunk scan forms them on chip (from B and
     C, counted once per group) and chunk_cb is not launched. Flops (multiply +
@@ -71,13 +72,13 @@ def accounting(w):
     if w.dtype == "bf16":
         # the bf16 chunk scan forms C B^T on chip from B and C: no chunk_cb launch
         cb_stage = {"bytes": 0, "flops": 0}
-        scan = {"bytes": x + x + dt + s + 2 * bc + ci + H * 4, "flops": scan_flops + cb_flops}
+        scan = {"bytes": x + x + 2 * s + 2 * bc + ci + H * 4, "flops": scan_flops + cb_flops}
     else:
         cb_stage = {"bytes": 2 * bc + cb, "flops": cb_flops}
-        scan = {"bytes": x + x + dt + s + bc + cb + ci + H * 4, "flops": scan_flops}
-    # stage 1 writes dA_cumsum and the float32 copy of dt (delta), same size
+        scan = {"bytes": x + x + 2 * s + bc + cb + ci + H * 4, "flops": scan_flops}
+    # stage 1 writes dA_cumsum and the float32 input weights (delta), same size
     cumsum = {"bytes": dt + H * 4 + 2 * s, "flops": tok * H * 2}
-    state = {"bytes": x + bc + dt + s + st, "flops": tok * H * 2 * P * N}
+    state = {"bytes": x + bc + 2 * s + st, "flops": tok * H * 2 * P * N}
     passing = {"bytes": st + ci + send, "flops": Bt * nC * H * P * N * 2}
     if fused_state_path(w):
         # one kernel for stages 2 and 3 (the library's rule): reads x, B, s and
@@ -210,6 +211,35 @@ def time_forward(w, steps, warmup, breakdown_steps=10):
     dom_ms = sum(e0.elapsed_time(e1) for e0, e1 in pairs) / steps
     return {"wall_ms": wall * 1e3 / steps, "evented_ms": evented_ms,
             "stage_ms": dict(zip(STAGES, per_stage)), "dominant": STAGES[dom], "dominant_ms": dom_ms}
+
+
+def time_forward_options(w, steps, warmup):
+    """Whole-forward time (host clock, no events) with every step-size option
+    on: per-head bias, softplus, clamp to [4e-3, 3e-2] and the zero-order-hold
+    input weight, on the same shapes (raw dt from generate_dt_raw)."""
+    import torch
+    import ssd_workloads as W
+    import structured_state_space_ssd_amd as ssd
+
+    d = W.generate(w)
+    r = W.generate_dt_raw(w)
+    d["dt"], d["dt_bias"] = r["dt"], r["dt_bias"]
+    g = upload(d)
+    x = g["x"]
+    ws = torch.empty(ssd.workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate,
+                                        w.chunk, x.dtype), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    kw = dict(chunk=w.chunk, workspace=ws, y=y, dt_bias=g["dt_bias"], dt_softplus=True,
+              dt_limit=(4e-3, 3e-2), zoh=True)
+    args = [g[k] for k in ("x", "dt", "A", "B", "C", "D")]
+    for _ in range(warmup):
+        ssd.forward(*args, **kw)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ssd.forward(*args, **kw)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
 
 
 def time_decode(w, warmup=3):
@@ -490,6 +520,13 @@ def main():
           f"between every two stages; {fwd['dominant']} {fwd['dominant_ms'] * 1e3:.1f} us live); stages " +
           ", ".join(f"{k} {v['us']:.1f} us" for k, v in kernels.items()), file=sys.stderr, flush=True)
 
+    opt_ms = time_forward_options(w, max(10, args.steps // 2), 3)
+    options = {"options": "dt_bias + softplus + clamp + zero-order hold",
+               "us_per_forward": round(opt_ms * 1e3, 2),
+               "tokens_per_s": round(w.tokens / (opt_ms * 1e-3), 1)}
+    print(f"[bench] forward with every step-size option: {opt_ms * 1e3:.1f} us", file=sys.stderr,
+          flush=True)
+
     extra = {}
     if args.all:
         for name in ("tiny_f32", "large_state", "long_seq"):
@@ -540,6 +577,7 @@ def main():
         "cpu_baseline": cpu,
         "evented_us_per_step": round(fwd["evented_ms"] * 1e3, 2),
         "kernels": kernels,
+        "forward_with_options": options,
         "decode": decode,
         "hbm_copy_probe": probe,
     }
