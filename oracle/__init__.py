@@ -14,6 +14,10 @@ Contents
   an independent O(L^2) computation used to pin the recurrence.
 * ``chunk_cumsum``: the within-chunk inclusive prefix sum of dt*A, the first
   step of the block decomposition ("Mamba 模型", section 4.1).
+* ``forward_varlen``: packed variable-length sequences (the dynamic sequence
+  packing of the "Mamba-2架构深度解析" page, section 5): the recurrence with the
+  state reset to zero where each sequence begins, and every sequence's final
+  state.
 
 Options (``forward``, ``step``): ``dt_bias`` [H] is added to the raw dt,
 ``dt_softplus`` applies log(1 + e^v) (the "从Transformer到Mamba" tutorial,
@@ -84,6 +88,8 @@ def _load(path=None):
         lib.ssd_oracle_forward_ex.restype = ctypes.c_int
         lib.ssd_oracle_step_ex.argtypes = [dp] + [fp] * 6 + [ip] * 5 + [fp, ip, dp, ip, op]
         lib.ssd_oracle_step_ex.restype = ctypes.c_int
+        lib.ssd_oracle_forward_varlen.argtypes = [fp] * 6 + [ip] * 5 + [fp, ip, fp, ip, dp, dp, ip, op]
+        lib.ssd_oracle_forward_varlen.restype = ctypes.c_int
         _libs[path] = lib
     return _libs[path]
 
@@ -142,6 +148,39 @@ def forward(x, dt, A, B, C, D=None, init=None, units=None, snap_every=0,
     if rc != 0:
         raise RuntimeError(f"ssd_oracle_forward failed: {rc}")
     return y, st, snaps
+
+
+def forward_varlen(x, dt, A, B, C, D, cu_seqlens, units=None, nthreads=None, lib=None,
+                   dt_bias=None, dt_softplus=False, dt_limit=None, zoh=False):
+    """Packed sequences: x [1,L,H,P] (or [L,H,P]), dt [1,L,H], B, C [1,L,G,N];
+    sequence k is tokens cu_seqlens[k] .. cu_seqlens[k+1]-1, each from the zero
+    state. ``units`` lists heads (default all). Returns y [U,L,P] and the
+    per-sequence final states [U,nseq,P,N], float64. Options as ``forward``.
+    """
+    x, dt, A, B, C, D = map(_f32, (x, dt, A, B, C, D))
+    if x.ndim == 4:
+        assert x.shape[0] == 1, "packed sequences use batch 1"
+        x, dt, B, C = x[0], dt[0], B[0], C[0]
+    L, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    assert dt.shape == (L, H) and B.shape == (L, G, N) and C.shape == B.shape
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    nseq = cu.size - 1
+    if units is None:
+        units_arr, U = None, H
+    else:
+        units_arr = np.ascontiguousarray(units, dtype=np.int32)
+        U = units_arr.size
+    y = np.empty((U, L, P), dtype=np.float64)
+    st = np.empty((U, nseq, P, N), dtype=np.float64)
+    o, _keep = _opts(H, dt_bias, dt_softplus, dt_limit, zoh)
+    rc = _load(lib).ssd_oracle_forward_varlen(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), L, H, P, G, N, _ptr(cu), nseq,
+        _ptr(units_arr), U, _ptr(y), _ptr(st), nthreads or default_threads(),
+        None if o is None else ctypes.byref(o))
+    if rc != 0:
+        raise RuntimeError(f"ssd_oracle_forward_varlen failed: {rc}")
+    return y, st
 
 
 def step(state, x, dt, A, B, C, D=None, units=None, nthreads=None, lib=None,

@@ -32,6 +32,11 @@
  *     bias added before softplus. Its section 8.2 speaks of adjusting the
  *     range the step sizes are produced in; that is read as an optional clamp
  *     to [dt_min, dt_max] after softplus.
+ *   - Packed variable-length sequences (ssd_oracle_forward_varlen): several
+ *     sequences concatenated along the token axis, each with its own
+ *     recurrence. The state is reset to zero where a sequence begins, and
+ *     each sequence's state after its last token is kept (the dynamic packing
+ *     of variable-length sequences on the "Mamba-2架构深度解析" page, section 5).
  * The state is stored transposed to the usual N x P: hs[p][n], n fastest.
  *
  * All token inputs arrive as float32 arrays holding the exact values the GPU
@@ -85,6 +90,9 @@ typedef struct {
     double *snaps;  /* [nunits][seqlen/snap_every][headdim][dstate] (may be NULL) */
     int snap_every;
     const oracle_opts *opts;
+    const int *cu;       /* packed sequences: offsets [nseq + 1], or NULL */
+    int nseq;
+    double *seq_states;  /* [nunits][nseq][headdim][dstate]: state after each sequence */
     atomic_int next;
 } fwd_job;
 
@@ -107,8 +115,15 @@ static void fwd_unit(fwd_job *j, int u, double *hs)
     }
     double *yu = j->y ? j->y + (size_t)u * L * P : NULL;
     int nsnap = 0;
+    int k = 0;  /* packed sequences: the sequence token t belongs to */
+    if (j->cu) memset(j->seq_states + (size_t)u * j->nseq * PN, 0, (size_t)j->nseq * PN * sizeof(double));
     for (int t = 0; t < L; ++t) {
         const size_t tok = (size_t)b * L + t;
+        if (j->cu) {
+            /* the last sequence that starts at or before t (empty ones are skipped) */
+            while (k + 1 < j->nseq && j->cu[k + 1] <= t) ++k;
+            if (k > 0 && j->cu[k] == t) memset(hs, 0, PN * sizeof(double)); /* a new sequence */
+        }
         const double d = step_size(j->opts, j->dt[tok * H + h], h);
         const double a = exp(d * A);
         const double wi = input_weight(j->opts, d, A);
@@ -125,6 +140,8 @@ static void fwd_unit(fwd_job *j, int u, double *hs)
             }
             if (yu) yu[(size_t)t * P + p] = acc + D * (double)xt[p];
         }
+        if (j->cu && t == j->cu[k + 1] - 1)  /* the last token of sequence k */
+            memcpy(j->seq_states + ((size_t)u * j->nseq + k) * PN, hs, PN * sizeof(double));
         if (j->snaps && j->snap_every > 0 && (t + 1) % j->snap_every == 0) {
             const int per = L / j->snap_every;
             memcpy(j->snaps + ((size_t)u * per + nsnap) * PN, hs, PN * sizeof(double));
@@ -193,7 +210,41 @@ int ssd_oracle_forward_ex(const float *x, const float *dt, const float *A, const
         if (units[u] < 0 || units[u] >= batch * nheads) return -2;
     if (nunits == 0) return 0;
     fwd_job j = {x, dt, A, B, C, D, init, batch, seqlen, nheads, headdim, ngroups, dstate,
-                 units, nunits, y, state, snaps, snap_every, opts, 0};
+                 units, nunits, y, state, snaps, snap_every, opts, NULL, 0, NULL, 0};
+    atomic_init(&j.next, 0);
+    return run_threads(fwd_worker, &j, nthreads, nunits);
+}
+
+/*
+ * Packed variable-length sequences: the token axis of x, dt, B, C (batch 1,
+ * seqlen tokens in all) holds nseq sequences, sequence k being tokens
+ * cu_seqlens[k] .. cu_seqlens[k+1]-1 (cu_seqlens[0] = 0, non-decreasing,
+ * cu_seqlens[nseq] = seqlen; empty sequences allowed). Every sequence starts
+ * from the zero state.
+ *   units: head indices (0 .. nheads-1) to compute, or NULL for all.
+ *   y [nunits][seqlen][headdim];
+ *   seq_states [nunits][nseq][headdim][dstate]: each sequence's state after
+ *   its last token (zero for an empty sequence).
+ */
+int ssd_oracle_forward_varlen(const float *x, const float *dt, const float *A, const float *B,
+                              const float *C, const float *D, int seqlen, int nheads, int headdim,
+                              int ngroups, int dstate, const int *cu_seqlens, int nseq,
+                              const int *units, int nunits, double *y, double *seq_states,
+                              int nthreads, const oracle_opts *opts)
+{
+    if (!x || !dt || !A || !B || !C || !cu_seqlens || !seq_states) return -1;
+    if (seqlen < 0 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1 || nseq < 1) return -2;
+    if (nheads % ngroups) return -2;
+    if (cu_seqlens[0] != 0 || cu_seqlens[nseq] != seqlen) return -2;
+    for (int k = 0; k < nseq; ++k)
+        if (cu_seqlens[k + 1] < cu_seqlens[k]) return -2;
+    if (!units) nunits = nheads;
+    if (nunits < 0) return -2;
+    for (int u = 0; units && u < nunits; ++u)
+        if (units[u] < 0 || units[u] >= nheads) return -2;
+    if (nunits == 0) return 0;
+    fwd_job j = {x, dt, A, B, C, D, NULL, 1, seqlen, nheads, headdim, ngroups, dstate,
+                 units, nunits, y, NULL, NULL, 0, opts, cu_seqlens, nseq, seq_states, 0};
     atomic_init(&j.next, 0);
     return run_threads(fwd_worker, &j, nthreads, nunits);
 }

@@ -390,7 +390,48 @@ def pin_step_with_options(lib=None):
     assert np.max(np.abs(state - st)) < 1e-13
 
 
+def pin_varlen(lib=None):
+    """P16: packed variable-length sequences ("Mamba-2架构深度解析" section 5,
+    dynamic packing of variable-length sequences) are independent sequences:
+    the packed run equals separate runs of each slice from the zero state,
+    bit for bit, and the numpy quadratic form of each slice; every sequence's
+    final state is the separate run's final state; an empty sequence's final
+    state is zero; one sequence is the plain forward. Checked with and without
+    the step-size options."""
+    rng = np.random.default_rng(26)
+    L, H, P, G, N = 41, 4, 3, 2, 5
+    x = rng.standard_normal((1, L, H, P)).astype(np.float32)
+    B = (rng.standard_normal((1, L, G, N)) / 2).astype(np.float32)
+    C = (rng.standard_normal((1, L, G, N)) / 2).astype(np.float32)
+    dt = np.exp(rng.uniform(np.log(0.05), np.log(0.8), (1, L, H))).astype(np.float32)
+    A = -np.exp(rng.uniform(0.0, np.log(4.0), H)).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32)
+    raw = _dyadic(rng, (1, L, H), -3.0, 1.0, 64)
+    bias = np.array([-1.0, 0.5, -2.0, 0.0], np.float32)
+    # lengths 1, 0 (empty), 7, 1, 12, 0, 20: ends and starts next to each other
+    cu = np.array([0, 1, 1, 8, 9, 21, 21, 41], np.int32)
+    for opts, dts in ((dict(), dt), (dict(dt_bias=bias, dt_softplus=True, dt_limit=(0.05, 0.9),
+                                         zoh=True), raw)):
+        y, st = oracle.forward_varlen(x, dts, A, B, C, D, cu, lib=lib, **opts)
+        assert y.shape == (H, L, P) and st.shape == (H, 7, P, N)
+        for k in range(7):
+            a, e = int(cu[k]), int(cu[k + 1])
+            if a == e:
+                assert np.all(st[:, k] == 0)
+                continue
+            sl = lambda t: np.ascontiguousarray(t[:, a:e])
+            ys, ss, _ = oracle.forward(sl(x), sl(dts), A, sl(B), sl(C), D, lib=lib, **opts)
+            assert np.array_equal(y[:, a:e], ys) and np.array_equal(st[:, k], ss)
+            if not opts:
+                yq, hq = oracle.quadratic(sl(x), sl(dts), A, sl(B), sl(C), D)
+                assert _rel(_units_to_bthp(np.ascontiguousarray(y[:, a:e]), 1, H), yq) < 1e-12
+                assert _rel(st[:, k], hq[0]) < 1e-12
+    y1, st1 = oracle.forward_varlen(x, dt, A, B, C, D, np.array([0, L], np.int32), lib=lib)
+    yf, sf, _ = oracle.forward(x, dt, A, B, C, D, lib=lib)
+    assert np.array_equal(y1, yf) and np.array_equal(st1[:, 0], sf)
+
+
 ALL_PINS = [pin_duality, pin_cumsum, pin_lti_geometric, pin_single_token, pin_no_memory,
             pin_state_carry, pin_forward_vs_step, pin_linearity, pin_groups, pin_golden,
             pin_dt_bias, pin_softplus_and_clamp, pin_zoh_ode, pin_zoh_forms,
-            pin_step_with_options]
+            pin_step_with_options, pin_varlen]

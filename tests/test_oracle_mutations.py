@@ -37,6 +37,13 @@ MUTATIONS = {
     "zoh_exp_not_expm1": ("return A != 0.0 ? expm1(d * A) / A : d;", "return A != 0.0 ? exp(d * A) / A : d;"),
     "step_ignores_dt_options": ("step_size(j->opts, j->dt[bh], h)", "(double)j->dt[bh]"),
     "step_euler_weight": ("input_weight(j->opts, d, (double)j->A[h])", "d"),
+    "varlen_no_reset": ("if (k > 0 && j->cu[k] == t) memset(hs, 0, PN * sizeof(double));", "if (0) {}"),
+    "varlen_reset_late": ("if (k > 0 && j->cu[k] == t) memset", "if (k > 0 && j->cu[k] == t - 1) memset"),
+    "varlen_capture_early": ("if (j->cu && t == j->cu[k + 1] - 1)", "if (j->cu && t == j->cu[k + 1] - 2)"),
+    "varlen_wrong_slot": ("memcpy(j->seq_states + ((size_t)u * j->nseq + k) * PN",
+                          "memcpy(j->seq_states + ((size_t)u * j->nseq + (k + 1) % j->nseq) * PN"),
+    "varlen_boundary_off_by_one": ("while (k + 1 < j->nseq && j->cu[k + 1] <= t) ++k;",
+                                   "while (k + 1 < j->nseq && j->cu[k + 1] < t) ++k;"),
     "previous_token_dt_for_decay": ("const double a = exp(d * A);", "const double a = exp((t ? (double)j->dt[(tok - 1) * H + h] : d) * A);"),
 }
 
