@@ -171,6 +171,36 @@ int ssd_forward_timed(const void *x, const void *dt, const float *A, const void 
                       void *const *events);
 
 /*
+ * Packed variable-length sequences (the dynamic packing of variable-length
+ * sequences named on the "Mamba-2架构深度解析" page, section 5). The token
+ * axis of a batch-1 input holds nseq sequences one after another: sequence k
+ * is tokens cu_seqlens[k] .. cu_seqlens[k+1]-1. Each has its own recurrence
+ * from the zero state; nothing flows from one sequence into the next.
+ *   x, y        [L][H][P] (= [1][L][H][P]) in dtype; dt [L][H]; B, C [L][G][N].
+ *   cu_seqlens  DEVICE int32 [nseq + 1], 4-byte aligned: cu_seqlens[0] = 0,
+ *               non-decreasing, cu_seqlens[nseq] = seqlen (empty sequences
+ *               allowed). The library does not read device memory on the host,
+ *               so it cannot check these values: other contents give
+ *               unspecified results, but every access stays in bounds.
+ *   seq_states  nullable, float32 [nseq][H][P][N], 16-byte aligned: each
+ *               sequence's state after its last token (zero if empty).
+ *   opts        nullable, as for ssd_forward_ex.
+ *   workspace   at least ssd_forward_varlen_workspace_size(...) bytes,
+ *               256-byte aligned: ssd_forward's layout at batch 1, then one
+ *               int32 per token position of the chunk-padded layout.
+ * Enqueues the separate stages (never the fused stage 2 + 3 kernel), each
+ * masking pairs of tokens from different sequences, then one kernel for the
+ * per-sequence states. nseq < 1 returns SSD_ERR_SHAPE.
+ */
+size_t ssd_forward_varlen_workspace_size(int seqlen, int nheads, int headdim, int ngroups,
+                                         int dstate, int chunk, int dtype);
+int ssd_forward_varlen(const void *x, const void *dt, const float *A, const void *B,
+                       const void *C, const float *D, const int *cu_seqlens, int nseq,
+                       int seqlen, int nheads, int headdim, int ngroups, int dstate, int chunk,
+                       int dtype, void *y, float *seq_states, void *workspace,
+                       size_t workspace_bytes, const ssd_options *opts, void *stream);
+
+/*
  * One recurrent (decode) step for every (batch, head): updates `state`
  * [Bt][H][P][N] float32 in place,
  *   state <- exp(dt*A_h) * state + dt * x B^T,   y = state C + D_h x,

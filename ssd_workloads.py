@@ -170,6 +170,19 @@ def generate_dt_raw(w: Workload, seed: int | None = None) -> dict:
             "dt_bias": rng.uniform(-6.5, -2.5, H).astype(np.float32)}
 
 
+def packed_cu_seqlens(total: int, max_len: int, seed: int) -> np.ndarray:
+    """Offsets [nseq + 1] (int32, from 0 to total) of a packed batch of
+    sequences with lengths floor(exp(U(0, ln(max_len + 1)))), i.e. spread
+    log-uniformly over 1 .. max_len, the last one cut to fit: a mix of very
+    short and long documents, as packing variable-length sequences produces."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cu = [0]
+    while cu[-1] < total:
+        n = max(1, int(np.exp(rng.uniform(0.0, math.log(max_len + 1)))))
+        cu.append(min(total, cu[-1] + min(n, max_len)))
+    return np.asarray(cu, dtype=np.int32)
+
+
 def small(name: str, batch: int, seqlen: int, nheads: int, headdim: int, ngroups: int,
           dstate: int, chunk: int, dtype: str, seed: int, init_std: float = 0.0,
           dt_lo: float = 1e-3, dt_hi: float = 1e-1, bc_scale: float | None = None) -> Workload:

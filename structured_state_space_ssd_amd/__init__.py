@@ -14,7 +14,7 @@ import torch
 from . import _native
 from ._native import SSDError, check, dtype_code, ptr, stream_handle
 
-__all__ = ["forward", "step", "options", "workspace_size", "chunk_cumsum", "chunk_state",
+__all__ = ["forward", "forward_varlen", "step", "options", "workspace_size", "chunk_cumsum", "chunk_state",
            "state_passing", "chunk_cb", "chunk_scan", "SSDError", "stages"]
 
 HEADDIM = 64
@@ -114,6 +114,52 @@ def forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, return_final_sta
         stream_handle(x.device), ev)
     check(rc, "ssd_forward")
     return (y, fs) if return_final_state else y
+
+
+def forward_varlen(x, dt, A, B, C, D, cu_seqlens, chunk=256, return_seq_states=False,
+                   workspace=None, y=None, dt_bias=None, dt_softplus=False, dt_limit=None,
+                   zoh=False):
+    """Packed variable-length sequences: x [L,H,P] or [1,L,H,P], dt [L,H] or
+    [1,L,H], B, C [L,G,N] or [1,L,G,N]; sequence k is tokens
+    cu_seqlens[k] .. cu_seqlens[k+1]-1 (GPU int32 [nseq+1], starting at 0,
+    non-decreasing, ending at L), each from the zero state.
+    Returns y (shaped like x) and, if requested, the per-sequence final states
+    [nseq,H,P,N] float32. Options as ``forward``.
+    """
+    _req(x, "x")
+    dt_ = dtype_code(x.dtype)
+    squeeze = x.dim() == 3
+    xs = x.unsqueeze(0) if squeeze else x
+    if xs.shape[0] != 1:
+        raise ValueError("packed sequences use batch 1")
+    _, L, H, P = xs.shape
+    _req(dt, "dt", x.dtype)
+    _req(B, "B", x.dtype)
+    _req(C, "C", x.dtype)
+    _req(A, "A", torch.float32)
+    _opt(D, "D")
+    _req(cu_seqlens, "cu_seqlens", torch.int32)
+    G, N = B.shape[-2], B.shape[-1]
+    if (dt.numel() != L * H or B.numel() != L * G * N or C.shape != B.shape
+            or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2):
+        raise ValueError("shape mismatch among x, dt, B, C, cu_seqlens")
+    nseq = cu_seqlens.numel() - 1
+    if y is None:
+        y = torch.empty_like(x)
+    ss = (torch.empty((nseq, H, P, N), dtype=torch.float32, device=x.device)
+          if return_seq_states else None)
+    need = int(_native.lib.ssd_forward_varlen_workspace_size(L, H, P, G, N, chunk, dt_))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    if dt_bias is not None and tuple(dt_bias.shape) != (H,):
+        raise ValueError("dt_bias must have shape [H]")
+    opts = options(dt_bias, dt_softplus, dt_limit, zoh)
+    rc = _native.lib.ssd_forward_varlen(
+        ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), ptr(cu_seqlens), nseq, L, H, P, G, N,
+        chunk, dt_, ptr(y), ptr(ss), ptr(workspace), workspace.numel(), _optref(opts),
+        stream_handle(x.device))
+    check(rc, "ssd_forward_varlen")
+    return (y, ss) if return_seq_states else y
 
 
 def step(state, x, dt, A, B, C, D=None, y=None, dt_bias=None, dt_softplus=False, dt_limit=None,

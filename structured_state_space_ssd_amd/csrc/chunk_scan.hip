@@ -63,12 +63,12 @@ __device__ __forceinline__ void store4_lds(float *p, const floatx4 &v) {
     *reinterpret_cast<floatx4 *>(p) = v;
 }
 
-template <typename T, int N, int Q>
+template <typename T, int N, int Q, bool VL>
 __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_kernel(
     const T *__restrict__ x, const float *__restrict__ delta, const float *__restrict__ dA_cumsum,
     const T *__restrict__ C, const typename LdsT<T>::type *__restrict__ cb,
-    const float *__restrict__ D, const typename LdsT<T>::type *__restrict__ chunk_init, int L,
-    int H, int G, int nC, T *__restrict__ y) {
+    const float *__restrict__ D, const typename LdsT<T>::type *__restrict__ chunk_init,
+    const int *__restrict__ seg, int L, int H, int G, int nC, T *__restrict__ y) {
     using E = typename LdsT<T>::type;
     using S = ScanSmem<E, N, Q>;
     constexpr int P = 64, NTHR = Q * 2, NT = Q / 16;
@@ -140,13 +140,16 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_kernel(
     constexpr bool kFoldDt = sizeof(T) == 2;
     const size_t srow = ((size_t)b * H + h) * (size_t)nC * Q + (size_t)c * Q;
     const float *s = dA_cumsum + srow;
+    const int *sg = seg + (size_t)(b * nC + c) * Q;  // packed sequences only (VL)
     for (int i = tid; i < Q; i += NTHR) {
         const float si_ = s[i] * kLog2e;
         const float se_ = s[i | 31] * kLog2e;  // last token of i's 32-token slice
         const float d = delta[srow + i];        // zero past the end
         sm.sl[i] = si_;
         sm.dtl[i] = kFoldDt ? si_ - __log2f(d) : d;
-        sm.colf[i] = __builtin_amdgcn_exp2f(se_ - si_) * d;
+        float cf = __builtin_amdgcn_exp2f(se_ - si_) * d;
+        if constexpr (VL) cf = sg[i | 31] <= i ? cf : 0.0f;  // slice end in i's sequence
+        sm.colf[i] = cf;
     }
 #pragma unroll
     for (int k = 0; k < XPIECES; ++k) {
@@ -167,10 +170,12 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_kernel(
     const float Dh = D ? D[h] : 0.0f;
     floatx4 acc[2][4];  // Y^T tiles: lane 16*g4 + i holds p = 16*pt + 4*g4 + 0..3 of token i
     float si[2];
+    int fs[2];  // first token (within the chunk) of row i's sequence, -1: earlier chunk
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti) {
         const int i0 = tiles[ti] * 16;
         si[ti] = sm.sl[i0 + r16];
+        fs[ti] = VL ? sg[i0 + r16] : -1;
         // ---- state to output: Y^T[p][i] += sum_n H_c[p][n] exp(s_i) C_i[n]
         if (!kEarlyC) {
 #pragma unroll
@@ -180,7 +185,8 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_kernel(
                 else cv[ti][kk].zero();
             }
         }
-        const float sc = __builtin_amdgcn_exp2f(si[ti]);
+        float sc = __builtin_amdgcn_exp2f(si[ti]);
+        if constexpr (VL) sc = fs[ti] < 0 ? sc : 0.0f;  // H_c belongs to row i's sequence
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) acc[ti][pt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -212,12 +218,16 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_kernel(
         const int jp = ti ? k - njp0 : k;
         const int il = tiles[ti] * 16 + r16;
         const float s_i = ti ? si[1] : si[0];
+        const int f_i = ti ? fs[1] : fs[0];
         const int jb = jp * 32 + 4 * g4;  // this lane's first token (elements 0..3)
         Frag<T> mf;
         if (jp != tiles[ti] / 2) {
-            // strictly below the diagonal: exp2(s_i - s_j) dt_j =
-            // exp2(s_i - s_end(slice)) * colf[j], both factors <= 1; no mask
-            const float rowf = __builtin_amdgcn_exp2f(s_i - sm.sl[jp * 32 + 31]);
+            // strictly below the diagonal: exp2(s_i - s_j) delta_j =
+            // exp2(s_i - s_end(slice)) * colf[j], both factors <= 1; no causal
+            // mask (packed sequences: zero unless i, the slice end and j share
+            // a sequence; colf holds the j side)
+            float rowf = __builtin_amdgcn_exp2f(s_i - sm.sl[jp * 32 + 31]);
+            if constexpr (VL) rowf = f_i <= jp * 32 + 31 ? rowf : 0.0f;
             const floatx4 c0 = *reinterpret_cast<const floatx4 *>(sm.colf + jb);
             const floatx4 c1 = *reinterpret_cast<const floatx4 *>(sm.colf + jb + 16);
 #pragma unroll
@@ -246,9 +256,9 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_kernel(
                 }
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                mf.set(r, jb + r <= il ? v[r] : 0.0f);
-                mf.set(4 + r, jb + 16 + r <= il ? v[4 + r] : 0.0f);
+            for (int r = 0; r < 4; ++r) {  // causal, and (packed) j in i's sequence
+                mf.set(r, jb + r <= il && (!VL || jb + r >= f_i) ? v[r] : 0.0f);
+                mf.set(4 + r, jb + 16 + r <= il && (!VL || jb + 16 + r >= f_i) ? v[4 + r] : 0.0f);
             }
         }
 #pragma unroll
@@ -365,18 +375,21 @@ __device__ __forceinline__ int cb_tile_start(int it) {
 // Slice JP (0..JMAX) of this wavefront's row tile it (JMAX = it/2; slice
 // JMAX holds the diagonal). cbl: this lane's C B^T fragment of slice 0 of the
 // tile in LDS (the slices of a tile are consecutive entries).
-template <int Q, int JMAX, int JP>
+template <int Q, int JMAX, int JP, bool VL>
 __device__ __forceinline__ void scan_slice(floatx4 (&acc)[4], const __bf16 *cbl,
                                            const __bf16 *xs, const int (&xo)[4],
-                                           const ScanTables<Q> &tb, float s_i, int il, int g4) {
+                                           const ScanTables<Q> &tb, float s_i, int il, int fs,
+                                           int g4) {
     constexpr bool DIAG = JP == JMAX;
     const int jb = JP * 32 + 4 * g4;
     Frag<bf16_t> cbk, mf;
     cbk.v = *reinterpret_cast<const bf16x8 *>(cbl + JP * 512);
     if constexpr (!DIAG) {
-        // strictly below the diagonal: exp2(s_i - s_j) dt_j =
-        // exp2(s_i - s_end(slice)) * colf[j], both factors <= 1; no mask
-        const float rowf = __builtin_amdgcn_exp2f(s_i - tb.sl[JP * 32 + 31]);
+        // strictly below the diagonal: exp2(s_i - s_j) delta_j =
+        // exp2(s_i - s_end(slice)) * colf[j], both factors <= 1; no causal mask
+        // (packed sequences: fs, the first token of row i's sequence, masks the row side)
+        float rowf = __builtin_amdgcn_exp2f(s_i - tb.sl[JP * 32 + 31]);
+        if constexpr (VL) rowf = fs <= JP * 32 + 31 ? rowf : 0.0f;
         const floatx4 c0 = *reinterpret_cast<const floatx4 *>(tb.colf + jb);
         const floatx4 c1 = *reinterpret_cast<const floatx4 *>(tb.colf + jb + 16);
 #pragma unroll
@@ -392,8 +405,8 @@ __device__ __forceinline__ void scan_slice(floatx4 (&acc)[4], const __bf16 *cbl,
         for (int r = 0; r < 4; ++r) {
             const float v0 = cbk.get(r) * __builtin_amdgcn_exp2f(s_i - d0[r]);
             const float v1 = cbk.get(4 + r) * __builtin_amdgcn_exp2f(s_i - d1[r]);
-            mf.set(r, jb + r <= il ? v0 : 0.0f);
-            mf.set(4 + r, jb + 16 + r <= il ? v1 : 0.0f);
+            mf.set(r, jb + r <= il && (!VL || jb + r >= fs) ? v0 : 0.0f);
+            mf.set(4 + r, jb + 16 + r <= il && (!VL || jb + 16 + r >= fs) ? v1 : 0.0f);
         }
     }
 #pragma unroll
@@ -404,24 +417,26 @@ __device__ __forceinline__ void scan_slice(floatx4 (&acc)[4], const __bf16 *cbl,
     }
 }
 
-template <int Q, int JMAX, int JP>
+template <int Q, int JMAX, int JP, bool VL>
 __device__ __forceinline__ void scan_slices(floatx4 (&acc)[4], const __bf16 *cbl,
                                             const __bf16 *xs, const int (&xo)[4],
-                                            const ScanTables<Q> &tb, float s_i, int il, int g4) {
+                                            const ScanTables<Q> &tb, float s_i, int il, int fs,
+                                            int g4) {
     if constexpr (JP <= JMAX) {
-        scan_slice<Q, JMAX, JP>(acc, cbl, xs, xo, tb, s_i, il, g4);
-        scan_slices<Q, JMAX, JP + 1>(acc, cbl, xs, xo, tb, s_i, il, g4);
+        scan_slice<Q, JMAX, JP, VL>(acc, cbl, xs, xo, tb, s_i, il, fs, g4);
+        scan_slices<Q, JMAX, JP + 1, VL>(acc, cbl, xs, xo, tb, s_i, il, fs, g4);
     }
 }
 
 // Dispatch on the (wavefront-uniform) tile's last slice index jmax.
-template <int Q, int JMAX>
+template <int Q, int JMAX, bool VL>
 __device__ __forceinline__ void scan_tile(int jmax, floatx4 (&acc)[4], const __bf16 *cbl,
                                           const __bf16 *xs, const int (&xo)[4],
-                                          const ScanTables<Q> &tb, float s_i, int il, int g4) {
+                                          const ScanTables<Q> &tb, float s_i, int il, int fs,
+                                          int g4) {
     if constexpr (JMAX < Q / 32) {
-        if (jmax == JMAX) scan_slices<Q, JMAX, 0>(acc, cbl, xs, xo, tb, s_i, il, g4);
-        else scan_tile<Q, JMAX + 1>(jmax, acc, cbl, xs, xo, tb, s_i, il, g4);
+        if (jmax == JMAX) scan_slices<Q, JMAX, 0, VL>(acc, cbl, xs, xo, tb, s_i, il, fs, g4);
+        else scan_tile<Q, JMAX + 1, VL>(jmax, acc, cbl, xs, xo, tb, s_i, il, fs, g4);
     }
 }
 
@@ -445,13 +460,13 @@ struct ScanBf16Lds {
 
 }  // namespace
 
-template <int N, int Q>
+template <int N, int Q, bool VL>
 __global__ __launch_bounds__(Q * 4) void chunk_scan_bf16_kernel(
     const bf16_t *__restrict__ x, const float *__restrict__ delta,
     const float *__restrict__ dA_cumsum, const bf16_t *__restrict__ B,
     const bf16_t *__restrict__ C, const float *__restrict__ D,
-    const __bf16 *__restrict__ chunk_init, int L, int H, int G, int nC, int nU, int nblk,
-    bf16_t *__restrict__ y) {
+    const __bf16 *__restrict__ chunk_init, const int *__restrict__ seg, int L, int H, int G,
+    int nC, int nU, int nblk, bf16_t *__restrict__ y) {
     constexpr int P = 64, NW = Q / 16;  // one wavefront per 16-row tile
     constexpr int NK = (N + 31) / 32;
     constexpr int ENTRIES = ScanBf16Lds<N, Q>::ENTRIES;
@@ -536,12 +551,16 @@ __global__ __launch_bounds__(Q * 4) void chunk_scan_bf16_kernel(
             d = dbase[(size_t)h * nC * Q + td];
         }
     };
+    // packed sequences: the rows' first tokens of their sequences, and whether
+    // this thread's table token shares a sequence with its slice end
+    const int *sg = seg + (size_t)(b * nC + c) * Q;
+    const float cmask = VL && tid < Q ? (sg[tid | 31] <= tid ? 1.0f : 0.0f) : 1.0f;
     auto tab_store = [&](ScanTables<Q> &t, int td, float sv, float se, float d) {
         if (td < Q) {  // d = delta_j, zero past the end
             const float si_ = sv * kLog2e;
             t.sl[td] = si_;
             t.dtl[td] = si_ - __log2f(d);
-            t.colf[td] = __builtin_amdgcn_exp2f(se * kLog2e - si_) * d;
+            t.colf[td] = __builtin_amdgcn_exp2f(se * kLog2e - si_) * (VL ? d * cmask : d);
         }
     };
 
@@ -606,6 +625,7 @@ __global__ __launch_bounds__(Q * 4) void chunk_scan_bf16_kernel(
     const __bf16 *cbl = cbs + cb_tile_start(tile) * 512 + l * 8;
     int xo[4];
     x_colfrag_offsets(xo, l);
+    const int fs = VL ? sg[il] : -1;  // first token (within the chunk) of row il's sequence
 
     for (int k = 0; k < nh; ++k) {
         const int h = hfirst + k * nblk, hn = h + nblk;
@@ -646,7 +666,8 @@ __global__ __launch_bounds__(Q * 4) void chunk_scan_bf16_kernel(
         const float Dh = D ? D[h] : 0.0f;
         const float si = tb.sl[il];
         {
-            const float sc = __builtin_amdgcn_exp2f(si);
+            float sc = __builtin_amdgcn_exp2f(si);
+            if constexpr (VL) sc = fs < 0 ? sc : 0.0f;  // H_c belongs to row il's sequence
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
                 const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xs + x_at(il, pt * 16 + 4 * g4));
@@ -656,7 +677,7 @@ __global__ __launch_bounds__(Q * 4) void chunk_scan_bf16_kernel(
             }
         }
         // ---- diagonal blocks
-        scan_tile<Q, 0>(jmax, acc, cbl, xs, xo, tb, si, il, g4);
+        scan_tile<Q, 0, VL>(jmax, acc, cbl, xs, xo, tb, si, il, fs, g4);
 
         // ---- next head's tables. Their inputs are consumed only here: the
         // empty asm keeps the compiler from waiting for their loads early
@@ -706,12 +727,12 @@ __global__ __launch_bounds__(Q * 4) void chunk_scan_bf16_kernel(
 namespace {
 
 // Slice K of wavefront pair index MM (see scan_slice for the decay).
-template <int N, int Q, int MM, int K>
+template <int N, int Q, int MM, int K, bool VL>
 __device__ __forceinline__ void pair_slice(floatx4 (&acc)[2][4], const Frag<bf16_t> (&cf)[2][(N + 31) / 32],
                                            const __bf16 *bsm, const int (&bo)[(N + 31) / 32],
                                            const __bf16 *xs, const int (&xo)[4],
                                            const ScanTables<Q> &tb, const float (&si)[2], int il0,
-                                           int il1, int g4, int r16) {
+                                           int il1, const int (&fs)[2], int g4, int r16) {
     constexpr int NT = Q / 16, NK = (N + 31) / 32;
     constexpr int TI = K <= MM ? 0 : 1;
     constexpr int JP = TI ? K - MM - 1 : K;
@@ -738,8 +759,10 @@ __device__ __forceinline__ void pair_slice(floatx4 (&acc)[2][4], const Frag<bf16
         }
     }
     Frag<bf16_t> mf;
+    const int f_i = fs[TI];  // packed sequences: first token of row il's sequence
     if constexpr (!DIAG) {
-        const float rowf = __builtin_amdgcn_exp2f(s_i - tb.sl[JP * 32 + 31]);
+        float rowf = __builtin_amdgcn_exp2f(s_i - tb.sl[JP * 32 + 31]);
+        if constexpr (VL) rowf = f_i <= JP * 32 + 31 ? rowf : 0.0f;
         const floatx4 c0 = *reinterpret_cast<const floatx4 *>(tb.colf + jb);
         const floatx4 c1 = *reinterpret_cast<const floatx4 *>(tb.colf + jb + 16);
 #pragma unroll
@@ -754,37 +777,41 @@ __device__ __forceinline__ void pair_slice(floatx4 (&acc)[2][4], const Frag<bf16
         for (int r = 0; r < 4; ++r) {
             const float v0 = m[0][r] * __builtin_amdgcn_exp2f(s_i - d0[r]);
             const float v1 = m[1][r] * __builtin_amdgcn_exp2f(s_i - d1[r]);
-            mf.set(r, jb + r <= il ? v0 : 0.0f);
-            mf.set(4 + r, jb + 16 + r <= il ? v1 : 0.0f);
+            mf.set(r, jb + r <= il && (!VL || jb + r >= f_i) ? v0 : 0.0f);
+            mf.set(4 + r, jb + 16 + r <= il && (!VL || jb + 16 + r >= f_i) ? v1 : 0.0f);
         }
     }
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) mma(acc[TI][pt], xf[pt], mf);
 }
 
-template <int N, int Q, int MM, int K>
+template <int N, int Q, int MM, int K, bool VL>
 __device__ __forceinline__ void pair_slices(floatx4 (&acc)[2][4], const Frag<bf16_t> (&cf)[2][(N + 31) / 32],
                                             const __bf16 *bsm, const int (&bo)[(N + 31) / 32],
                                             const __bf16 *xs, const int (&xo)[4],
                                             const ScanTables<Q> &tb, const float (&si)[2], int il0,
-                                            int il1, int g4, int r16) {
+                                            int il1, const int (&fs)[2], int g4, int r16) {
     if constexpr (K < Q / 32 + 1) {
-        pair_slice<N, Q, MM, K>(acc, cf, bsm, bo, xs, xo, tb, si, il0, il1, g4, r16);
+        pair_slice<N, Q, MM, K, VL>(acc, cf, bsm, bo, xs, xo, tb, si, il0, il1, fs, g4, r16);
         __builtin_amdgcn_sched_barrier(0);  // keep slices apart: bounded register use
-        pair_slices<N, Q, MM, K + 1>(acc, cf, bsm, bo, xs, xo, tb, si, il0, il1, g4, r16);
+        pair_slices<N, Q, MM, K + 1, VL>(acc, cf, bsm, bo, xs, xo, tb, si, il0, il1, fs, g4, r16);
     }
 }
 
-template <int N, int Q, int MM>
+template <int N, int Q, int MM, bool VL>
 __device__ __forceinline__ void pair_slices_of(int M, floatx4 (&acc)[2][4],
                                                const Frag<bf16_t> (&cf)[2][(N + 31) / 32],
                                                const __bf16 *bsm, const int (&bo)[(N + 31) / 32],
                                                const __bf16 *xs, const int (&xo)[4],
                                                const ScanTables<Q> &tb, const float (&si)[2],
-                                               int il0, int il1, int g4, int r16) {
+                                               int il0, int il1, const int (&fs)[2], int g4,
+                                               int r16) {
     if constexpr (MM < Q / 64) {
-        if (M == MM) pair_slices<N, Q, MM, 0>(acc, cf, bsm, bo, xs, xo, tb, si, il0, il1, g4, r16);
-        else pair_slices_of<N, Q, MM + 1>(M, acc, cf, bsm, bo, xs, xo, tb, si, il0, il1, g4, r16);
+        if (M == MM)
+            pair_slices<N, Q, MM, 0, VL>(acc, cf, bsm, bo, xs, xo, tb, si, il0, il1, fs, g4, r16);
+        else
+            pair_slices_of<N, Q, MM + 1, VL>(M, acc, cf, bsm, bo, xs, xo, tb, si, il0, il1, fs, g4,
+                                             r16);
     }
 }
 
@@ -811,13 +838,13 @@ struct PairLds {
 
 }  // namespace
 
-template <int N, int Q>
+template <int N, int Q, bool VL>
 __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_bf16_pair_kernel(
     const bf16_t *__restrict__ x, const float *__restrict__ delta,
     const float *__restrict__ dA_cumsum, const bf16_t *__restrict__ B,
     const bf16_t *__restrict__ C, const float *__restrict__ D,
-    const __bf16 *__restrict__ chunk_init, int L, int H, int G, int nC, int nU, int nblk,
-    bf16_t *__restrict__ y) {
+    const __bf16 *__restrict__ chunk_init, const int *__restrict__ seg, int L, int H, int G,
+    int nC, int nU, int nblk, bf16_t *__restrict__ y) {
     constexpr int P = 64, NW = Q / 32, NT = Q / 16;
     constexpr int NK = (N + 31) / 32;
     constexpr int PPR = N / 8;            // 16-byte pieces per H_c / B row
@@ -890,12 +917,16 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_bf16_pair_kernel(
             d = dbase[(size_t)h * nC * Q + td];
         }
     };
+    // packed sequences: the rows' first tokens of their sequences, and whether
+    // this thread's table token shares a sequence with its slice end
+    const int *sg = seg + (size_t)(b * nC + c) * Q;
+    const float cmask = VL && tid < Q ? (sg[tid | 31] <= tid ? 1.0f : 0.0f) : 1.0f;
     auto tab_store = [&](ScanTables<Q> &t, int td, float sv, float se, float d) {
         if (td < Q) {  // d = delta_j, zero past the end
             const float si_ = sv * kLog2e;
             t.sl[td] = si_;
             t.dtl[td] = si_ - __log2f(d);
-            t.colf[td] = __builtin_amdgcn_exp2f(se * kLog2e - si_) * d;
+            t.colf[td] = __builtin_amdgcn_exp2f(se * kLog2e - si_) * (VL ? d * cmask : d);
         }
     };
 
@@ -931,6 +962,11 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_bf16_pair_kernel(
     x_colfrag_offsets(xo, l);
     int so[NK];  // this lane's H_c / B fragment offsets
     swz_row_offsets<N>(so, l);
+    int fs[2] = {-1, -1};  // first token (within the chunk) of rows il0's and il1's sequences
+    if constexpr (VL) {
+        fs[0] = sg[il0];
+        fs[1] = sg[il1];
+    }
 
     for (int k = 0; k < nh; ++k) {
         const int h = hfirst + k * nblk, hn = h + nblk;
@@ -967,7 +1003,8 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_bf16_pair_kernel(
         for (int ti = 0; ti < 2; ++ti) {
             const int il = ti ? il1 : il0;
             si[ti] = tb.sl[il];
-            const float sc = __builtin_amdgcn_exp2f(si[ti]);
+            float sc = __builtin_amdgcn_exp2f(si[ti]);
+            if constexpr (VL) sc = fs[ti] < 0 ? sc : 0.0f;  // H_c belongs to row il's sequence
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
                 const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xs + x_at(il, pt * 16 + 4 * g4));
@@ -977,7 +1014,7 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_bf16_pair_kernel(
             }
         }
         // ---- diagonal blocks
-        pair_slices_of<N, Q, 0>(M, acc, cf, bsm, so, xs, xo, tb, si, il0, il1, g4, r16);
+        pair_slices_of<N, Q, 0, VL>(M, acc, cf, bsm, so, xs, xo, tb, si, il0, il1, fs, g4, r16);
 
         // ---- next head's tables (see chunk_scan_bf16_kernel)
         asm volatile("" : "+v"(nsv), "+v"(nse), "+v"(nd));
@@ -1012,10 +1049,10 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_bf16_pair_kernel(
     }
 }
 
-template <int N, int Q>
+template <int N, int Q, bool VL>
 static void launch_scan_bf16(const void *x, const float *dl, const float *dA, const void *B,
-                             const void *C, const float *D, const void *Hc, int batch, int L,
-                             int H, int G, void *y, hipStream_t stream) {
+                             const void *C, const float *D, const void *Hc, const int *seg,
+                             int batch, int L, int H, int G, void *y, hipStream_t stream) {
     const int nC = (L + Q - 1) / Q;
     const int hpg = H / G;
     const int nU = batch * nC * G;
@@ -1028,43 +1065,56 @@ static void launch_scan_bf16(const void *x, const float *dl, const float *dA, co
     nblk = nblk < 1 ? 1 : (nblk > hpg ? hpg : nblk);
     const dim3 grid((unsigned)(8 * nblk) * (unsigned)((nU + 7) / 8));
     if constexpr (kPair) {
-        chunk_scan_bf16_pair_kernel<N, Q><<<grid, Q * 2, 0, stream>>>(
+        chunk_scan_bf16_pair_kernel<N, Q, VL><<<grid, Q * 2, 0, stream>>>(
             static_cast<const bf16_t *>(x), dl, dA,
             static_cast<const bf16_t *>(B), static_cast<const bf16_t *>(C), D,
-            static_cast<const __bf16 *>(Hc), L, H, G, nC, nU, nblk, static_cast<bf16_t *>(y));
+            static_cast<const __bf16 *>(Hc), seg, L, H, G, nC, nU, nblk, static_cast<bf16_t *>(y));
     } else {
-        chunk_scan_bf16_kernel<N, Q><<<grid, Q * 4, 0, stream>>>(
+        chunk_scan_bf16_kernel<N, Q, VL><<<grid, Q * 4, 0, stream>>>(
             static_cast<const bf16_t *>(x), dl, dA,
             static_cast<const bf16_t *>(B), static_cast<const bf16_t *>(C), D,
-            static_cast<const __bf16 *>(Hc), L, H, G, nC, nU, nblk, static_cast<bf16_t *>(y));
+            static_cast<const __bf16 *>(Hc), seg, L, H, G, nC, nU, nblk, static_cast<bf16_t *>(y));
     }
 }
 
-template <typename T, int N, int Q>
-static void launch_scan(const void *x, const float *dl, const float *dA, const void *B,
-                        const void *C, const void *cb, const float *D, const void *Hc, int batch,
-                        int L, int H, int G, void *y, hipStream_t stream) {
+template <typename T, int N, int Q, bool VL>
+static void launch_scan_vl(const void *x, const float *dl, const float *dA, const void *B,
+                           const void *C, const void *cb, const float *D, const void *Hc,
+                           const int *seg, int batch, int L, int H, int G, void *y,
+                           hipStream_t stream) {
     if constexpr (sizeof(T) == 2) {
-        launch_scan_bf16<N, Q>(x, dl, dA, B, C, D, Hc, batch, L, H, G, y, stream);
+        launch_scan_bf16<N, Q, VL>(x, dl, dA, B, C, D, Hc, seg, batch, L, H, G, y, stream);
     } else {
         using E = typename LdsT<T>::type;
         const int nC = (L + Q - 1) / Q;
         const dim3 grid(nC, H, batch);
-        chunk_scan_kernel<T, N, Q><<<grid, Q * 2, 0, stream>>>(
+        chunk_scan_kernel<T, N, Q, VL><<<grid, Q * 2, 0, stream>>>(
             static_cast<const T *>(x), dl, dA, static_cast<const T *>(C),
-            static_cast<const E *>(cb), D, static_cast<const E *>(Hc), L, H, G, nC,
+            static_cast<const E *>(cb), D, static_cast<const E *>(Hc), seg, L, H, G, nC,
             static_cast<T *>(y));
     }
 }
 
+// seg (packed sequences, nullable): the kernels' masking variant
+template <typename T, int N, int Q>
+static void launch_scan(const void *x, const float *dl, const float *dA, const void *B,
+                        const void *C, const void *cb, const float *D, const void *Hc,
+                        const int *seg, int batch, int L, int H, int G, void *y,
+                        hipStream_t stream) {
+    if (seg)
+        launch_scan_vl<T, N, Q, true>(x, dl, dA, B, C, cb, D, Hc, seg, batch, L, H, G, y, stream);
+    else
+        launch_scan_vl<T, N, Q, false>(x, dl, dA, B, C, cb, D, Hc, seg, batch, L, H, G, y, stream);
+}
+
 template <typename T, int N>
 static bool scan_q(int Q, const void *x, const float *dl, const float *dA, const void *B,
-                   const void *C, const void *cb, const float *D, const void *Hc, int batch, int L,
-                   int H, int G, void *y, hipStream_t s) {
+                   const void *C, const void *cb, const float *D, const void *Hc, const int *seg,
+                   int batch, int L, int H, int G, void *y, hipStream_t s) {
     switch (Q) {
-        case 64: launch_scan<T, N, 64>(x, dl, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); return true;
-        case 128: launch_scan<T, N, 128>(x, dl, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); return true;
-        case 256: launch_scan<T, N, 256>(x, dl, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); return true;
+        case 64: launch_scan<T, N, 64>(x, dl, dA, B, C, cb, D, Hc, seg, batch, L, H, G, y, s); return true;
+        case 128: launch_scan<T, N, 128>(x, dl, dA, B, C, cb, D, Hc, seg, batch, L, H, G, y, s); return true;
+        case 256: launch_scan<T, N, 256>(x, dl, dA, B, C, cb, D, Hc, seg, batch, L, H, G, y, s); return true;
         default: return false;
     }
 }
@@ -1072,15 +1122,15 @@ static bool scan_q(int Q, const void *x, const float *dl, const float *dA, const
 template <typename T>
 static hipError_t scan_dispatch(int N, int Q, const void *x, const float *dl, const float *dA,
                                 const void *B, const void *C, const void *cb, const float *D,
-                                const void *Hc, int batch, int L, int H, int G, void *y,
-                                hipStream_t s) {
+                                const void *Hc, const int *seg, int batch, int L, int H, int G,
+                                void *y, hipStream_t s) {
     bool ok = false;
     switch (N) {
-        case 16: ok = scan_q<T, 16>(Q, x, dl, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
-        case 32: ok = scan_q<T, 32>(Q, x, dl, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
-        case 64: ok = scan_q<T, 64>(Q, x, dl, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
-        case 128: ok = scan_q<T, 128>(Q, x, dl, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
-        case 256: ok = scan_q<T, 256>(Q, x, dl, dA, B, C, cb, D, Hc, batch, L, H, G, y, s); break;
+        case 16: ok = scan_q<T, 16>(Q, x, dl, dA, B, C, cb, D, Hc, seg, batch, L, H, G, y, s); break;
+        case 32: ok = scan_q<T, 32>(Q, x, dl, dA, B, C, cb, D, Hc, seg, batch, L, H, G, y, s); break;
+        case 64: ok = scan_q<T, 64>(Q, x, dl, dA, B, C, cb, D, Hc, seg, batch, L, H, G, y, s); break;
+        case 128: ok = scan_q<T, 128>(Q, x, dl, dA, B, C, cb, D, Hc, seg, batch, L, H, G, y, s); break;
+        case 256: ok = scan_q<T, 256>(Q, x, dl, dA, B, C, cb, D, Hc, seg, batch, L, H, G, y, s); break;
         default: break;
     }
     if (!ok) return hipErrorInvalidValue;
@@ -1091,13 +1141,13 @@ bool chunk_scan_reads_cb(bool bf16) { return !bf16; }
 
 hipError_t launch_chunk_scan(const void *x, const float *delta, const float *dA_cumsum, const void *B,
                              const void *C, const void *cb, const float *D, const void *chunk_init,
-                             int batch, int seqlen, int nheads, int ngroups, int dstate, int chunk,
-                             bool bf16, void *y, hipStream_t stream) {
+                             const int *seg, int batch, int seqlen, int nheads, int ngroups,
+                             int dstate, int chunk, bool bf16, void *y, hipStream_t stream) {
     if (bf16)
         return scan_dispatch<bf16_t>(dstate, chunk, x, delta, dA_cumsum, B, C, cb, D, chunk_init,
-                                     batch, seqlen, nheads, ngroups, y, stream);
-    return scan_dispatch<float>(dstate, chunk, x, delta, dA_cumsum, B, C, cb, D, chunk_init, batch,
-                                seqlen, nheads, ngroups, y, stream);
+                                     seg, batch, seqlen, nheads, ngroups, y, stream);
+    return scan_dispatch<float>(dstate, chunk, x, delta, dA_cumsum, B, C, cb, D, chunk_init, seg,
+                                batch, seqlen, nheads, ngroups, y, stream);
 }
 
 }  // namespace ssd

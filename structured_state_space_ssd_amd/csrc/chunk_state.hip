@@ -25,7 +25,7 @@ namespace ssd {
 template <typename T, int N, int Q>
 __global__ __launch_bounds__(512) void chunk_state_kernel(
     const T *__restrict__ x, const T *__restrict__ B, const float *__restrict__ delta,
-    const float *__restrict__ dA_cumsum, int L, int H, int G, int nC,
+    const float *__restrict__ dA_cumsum, const int *__restrict__ seg, int L, int H, int G, int nC,
     float *__restrict__ states) {
     using E = typename LdsT<T>::type;
     constexpr int P = 64, NTHR = 512;
@@ -68,9 +68,11 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(
     const size_t row = ((size_t)b * H + h) * (size_t)nC * Q + (size_t)c * Q;
     const float *s = dA_cumsum + row, *dl = delta + row;
     const float s_end = s[len - 1];
+    // packed sequences: only the tokens of the last token's sequence count
+    const int j0 = seg ? seg[(size_t)(b * nC + c) * Q + len - 1] : -1;
     for (int j = tid; j < Q; j += NTHR) {
         float wv = 0.0f;
-        if (j < len) wv = __builtin_amdgcn_exp2f((s_end - s[j]) * kLog2e) * dl[j];
+        if (j < len && j >= j0) wv = __builtin_amdgcn_exp2f((s_end - s[j]) * kLog2e) * dl[j];
         wj[j] = wv;
     }
 
@@ -166,7 +168,8 @@ __device__ __forceinline__ void colfrag_swz(Frag<bf16_t> &f, const __bf16 *m, in
 template <int N, int Q>
 __global__ __launch_bounds__(512) void chunk_state_bf16_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ B, const float *__restrict__ delta,
-    const float *__restrict__ dA_cumsum, int L, int H, int G, int nC, float *__restrict__ states) {
+    const float *__restrict__ dA_cumsum, const int *__restrict__ seg, int L, int H, int G, int nC,
+    float *__restrict__ states) {
     constexpr int P = 64, NW = 8;
     constexpr int TP = N >= 128 ? 32 : 64;  // tokens per phase
     constexpr int NPH = Q / TP;
@@ -208,9 +211,11 @@ __global__ __launch_bounds__(512) void chunk_state_bf16_kernel(
     const size_t row = ((size_t)b * H + h) * (size_t)nC * Q + (size_t)c * Q;
     const float *s = dA_cumsum + row, *dl = delta + row;
     const float s_end = s[len - 1];
+    // packed sequences: only the tokens of the last token's sequence count
+    const int j0 = seg ? seg[(size_t)(b * nC + c) * Q + len - 1] : -1;
     for (int j = tid; j < Q; j += 512) {
         float wv = 0.0f;
-        if (j < len) wv = __builtin_amdgcn_exp2f((s_end - s[j]) * kLog2e) * dl[j];
+        if (j < len && j >= j0) wv = __builtin_amdgcn_exp2f((s_end - s[j]) * kLog2e) * dl[j];
         wj[j] = wv;
     }
 
@@ -473,43 +478,44 @@ hipError_t launch_chunk_state_passing(const void *x, const void *B, const float 
 }
 
 template <typename T, int N, int Q>
-static void launch_cs(const void *x, const void *B, const float *dl, const float *dA, int batch,
-                      int L, int H, int G, float *states, hipStream_t stream) {
+static void launch_cs(const void *x, const void *B, const float *dl, const float *dA,
+                      const int *seg, int batch, int L, int H, int G, float *states,
+                      hipStream_t stream) {
     const int nC = (L + Q - 1) / Q;
     const dim3 grid(nC, H, batch);
     if constexpr (sizeof(T) == 2) {
         chunk_state_bf16_kernel<N, Q><<<grid, 512, 0, stream>>>(
             static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(B),
-            dl, dA, L, H, G, nC, states);
+            dl, dA, seg, L, H, G, nC, states);
     } else {
         chunk_state_kernel<T, N, Q><<<grid, 512, 0, stream>>>(
-            static_cast<const T *>(x), static_cast<const T *>(B), dl, dA, L,
+            static_cast<const T *>(x), static_cast<const T *>(B), dl, dA, seg, L,
             H, G, nC, states);
     }
 }
 
 template <typename T, int N>
-static bool cs_q(int Q, const void *x, const void *B, const float *dl, const float *dA, int batch,
-                 int L, int H, int G, float *states, hipStream_t s) {
+static bool cs_q(int Q, const void *x, const void *B, const float *dl, const float *dA,
+                 const int *seg, int batch, int L, int H, int G, float *states, hipStream_t s) {
     switch (Q) {
-        case 64: launch_cs<T, N, 64>(x, B, dl, dA, batch, L, H, G, states, s); return true;
-        case 128: launch_cs<T, N, 128>(x, B, dl, dA, batch, L, H, G, states, s); return true;
-        case 256: launch_cs<T, N, 256>(x, B, dl, dA, batch, L, H, G, states, s); return true;
+        case 64: launch_cs<T, N, 64>(x, B, dl, dA, seg, batch, L, H, G, states, s); return true;
+        case 128: launch_cs<T, N, 128>(x, B, dl, dA, seg, batch, L, H, G, states, s); return true;
+        case 256: launch_cs<T, N, 256>(x, B, dl, dA, seg, batch, L, H, G, states, s); return true;
         default: return false;
     }
 }
 
 template <typename T>
 static hipError_t dispatch_cs(const void *x, const void *B, const float *dl, const float *dA,
-                              int batch, int L, int H, int G, int N, int Q, float *states,
-                              hipStream_t s) {
+                              const int *seg, int batch, int L, int H, int G, int N, int Q,
+                              float *states, hipStream_t s) {
     bool ok = false;
     switch (N) {
-        case 16: ok = cs_q<T, 16>(Q, x, B, dl, dA, batch, L, H, G, states, s); break;
-        case 32: ok = cs_q<T, 32>(Q, x, B, dl, dA, batch, L, H, G, states, s); break;
-        case 64: ok = cs_q<T, 64>(Q, x, B, dl, dA, batch, L, H, G, states, s); break;
-        case 128: ok = cs_q<T, 128>(Q, x, B, dl, dA, batch, L, H, G, states, s); break;
-        case 256: ok = cs_q<T, 256>(Q, x, B, dl, dA, batch, L, H, G, states, s); break;
+        case 16: ok = cs_q<T, 16>(Q, x, B, dl, dA, seg, batch, L, H, G, states, s); break;
+        case 32: ok = cs_q<T, 32>(Q, x, B, dl, dA, seg, batch, L, H, G, states, s); break;
+        case 64: ok = cs_q<T, 64>(Q, x, B, dl, dA, seg, batch, L, H, G, states, s); break;
+        case 128: ok = cs_q<T, 128>(Q, x, B, dl, dA, seg, batch, L, H, G, states, s); break;
+        case 256: ok = cs_q<T, 256>(Q, x, B, dl, dA, seg, batch, L, H, G, states, s); break;
         default: break;
     }
     if (!ok) return hipErrorInvalidValue;
@@ -517,13 +523,13 @@ static hipError_t dispatch_cs(const void *x, const void *B, const float *dl, con
 }
 
 hipError_t launch_chunk_state(const void *x, const void *B, const float *delta,
-                              const float *dA_cumsum, int batch, int seqlen, int nheads,
-                              int ngroups, int dstate, int chunk, bool bf16, float *states,
-                              hipStream_t stream) {
+                              const float *dA_cumsum, const int *seg, int batch, int seqlen,
+                              int nheads, int ngroups, int dstate, int chunk, bool bf16,
+                              float *states, hipStream_t stream) {
     if (bf16)
-        return dispatch_cs<bf16_t>(x, B, delta, dA_cumsum, batch, seqlen, nheads, ngroups, dstate,
+        return dispatch_cs<bf16_t>(x, B, delta, dA_cumsum, seg, batch, seqlen, nheads, ngroups, dstate,
                                    chunk, states, stream);
-    return dispatch_cs<float>(x, B, delta, dA_cumsum, batch, seqlen, nheads, ngroups, dstate, chunk,
+    return dispatch_cs<float>(x, B, delta, dA_cumsum, seg, batch, seqlen, nheads, ngroups, dstate, chunk,
                               states, stream);
 }
 

@@ -41,6 +41,17 @@ Workspace layout(int batch, int seqlen, int nheads, int headdim, int ngroups, in
     return w;
 }
 
+// Packed sequences: the forward's workspace at batch 1, then seg (one int per
+// token position of the chunk-padded layout).
+Workspace varlen_layout(int seqlen, int nheads, int headdim, int ngroups, int dstate, int chunk,
+                        bool bf16, size_t *seg_off) {
+    Workspace w = layout(1, seqlen, nheads, headdim, ngroups, dstate, chunk, bf16);
+    const size_t nC = (static_cast<size_t>(seqlen) + chunk - 1) / chunk;
+    *seg_off = w.total;
+    w.total += align_up(nC * chunk * sizeof(int));
+    return w;
+}
+
 int check_dims(int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate) {
     if (batch < 1 || seqlen < 1 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1)
         return SSD_ERR_SHAPE;
@@ -97,6 +108,16 @@ size_t ssd_forward_workspace_size(int batch, int seqlen, int nheads, int headdim
     return layout(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, dtype == SSD_BF16).total;
 }
 
+size_t ssd_forward_varlen_workspace_size(int seqlen, int nheads, int headdim, int ngroups,
+                                         int dstate, int chunk, int dtype) {
+    if (check_dims(1, seqlen, nheads, headdim, ngroups, dstate) != SSD_OK ||
+        !supported_chunk(chunk) || !valid_dtype(dtype))
+        return 0;
+    size_t seg_off;
+    return varlen_layout(seqlen, nheads, headdim, ngroups, dstate, chunk, dtype == SSD_BF16,
+                         &seg_off).total;
+}
+
 size_t ssd_chunk_cb_size(int batch, int seqlen, int ngroups, int chunk, int dtype) {
     if (batch < 1 || seqlen < 1 || ngroups < 1 || !supported_chunk(chunk) || !valid_dtype(dtype))
         return 0;
@@ -139,7 +160,7 @@ int ssd_chunk_state(const void *x, const void *B, const float *delta, const floa
     if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(B) || !aligned16(states) || !aligned16(delta))
         return SSD_ERR_UNSUPPORTED;
-    return status_of(ssd::launch_chunk_state(x, B, delta, dA_cumsum, batch, seqlen, nheads, ngroups,
+    return status_of(ssd::launch_chunk_state(x, B, delta, dA_cumsum, nullptr, batch, seqlen, nheads, ngroups,
                                              dstate, chunk, dtype == SSD_BF16, states,
                                              static_cast<hipStream_t>(stream)));
 }
@@ -154,7 +175,7 @@ int ssd_state_passing(const float *states, const float *dA_cumsum, const float *
     if (!aligned16(states) || !aligned16(chunk_init) || (init_state && !aligned16(init_state)) ||
         (final_state && !aligned16(final_state)))
         return SSD_ERR_UNSUPPORTED;
-    return status_of(ssd::launch_state_passing(states, dA_cumsum, init_state, batch, seqlen, nheads,
+    return status_of(ssd::launch_state_passing(states, dA_cumsum, init_state, nullptr, batch, seqlen, nheads,
                                                dstate, chunk, dtype == SSD_BF16, chunk_init,
                                                final_state, static_cast<hipStream_t>(stream)));
 }
@@ -174,7 +195,7 @@ int ssd_chunk_scan(const void *x, const float *delta, const float *dA_cumsum, co
         !aligned16(dA_cumsum) || !aligned16(delta) ||
         (reads_cb ? (reinterpret_cast<uintptr_t>(cb) % 32) != 0 : !aligned16(B)))
         return SSD_ERR_UNSUPPORTED;
-    return status_of(ssd::launch_chunk_scan(x, delta, dA_cumsum, B, C, cb, D, chunk_init, batch,
+    return status_of(ssd::launch_chunk_scan(x, delta, dA_cumsum, B, C, cb, D, chunk_init, nullptr, batch,
                                             seqlen, nheads, ngroups, dstate, chunk, bf16, y,
                                             static_cast<hipStream_t>(stream)));
 }
@@ -227,11 +248,11 @@ int ssd_forward_ex(const void *x, const void *dt, const float *A, const void *B,
         if (e == hipSuccess) e = mark(2);
     } else {
         if (e == hipSuccess)
-            e = ssd::launch_chunk_state(x, B, delta, cumsum, batch, seqlen, nheads, ngroups, dstate,
+            e = ssd::launch_chunk_state(x, B, delta, cumsum, nullptr, batch, seqlen, nheads, ngroups, dstate,
                                         chunk, bf16, states, s);
         if (e == hipSuccess) e = mark(2);
         if (e == hipSuccess)
-            e = ssd::launch_state_passing(states, cumsum, init_state, batch, seqlen, nheads, dstate,
+            e = ssd::launch_state_passing(states, cumsum, init_state, nullptr, batch, seqlen, nheads, dstate,
                                           chunk, bf16, cinit, final_state, s);
     }
     if (e == hipSuccess) e = mark(3);
@@ -239,9 +260,63 @@ int ssd_forward_ex(const void *x, const void *dt, const float *A, const void *B,
         e = ssd::launch_chunk_cb(B, C, batch, seqlen, ngroups, dstate, chunk, bf16, cb, s);
     if (e == hipSuccess) e = mark(4);
     if (e == hipSuccess)
-        e = ssd::launch_chunk_scan(x, delta, cumsum, B, C, cb, D, cinit, batch, seqlen, nheads,
+        e = ssd::launch_chunk_scan(x, delta, cumsum, B, C, cb, D, cinit, nullptr, batch, seqlen, nheads,
                                    ngroups, dstate, chunk, bf16, y, s);
     if (e == hipSuccess) e = mark(5);
+    return status_of(e);
+}
+
+int ssd_forward_varlen(const void *x, const void *dt, const float *A, const void *B,
+                       const void *C, const float *D, const int *cu_seqlens, int nseq,
+                       int seqlen, int nheads, int headdim, int ngroups, int dstate, int chunk,
+                       int dtype, void *y, float *seq_states, void *workspace,
+                       size_t workspace_bytes, const ssd_options *opts, void *stream) {
+    if (!x || !dt || !A || !B || !C || !y || !cu_seqlens) return SSD_ERR_NULL;
+    if (nseq < 1) return SSD_ERR_SHAPE;
+    int rc = check_dims(1, seqlen, nheads, headdim, ngroups, dstate);
+    if (rc != SSD_OK) return rc;
+    if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) ||
+        (seq_states && !aligned16(seq_states)) ||
+        (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
+        return SSD_ERR_UNSUPPORTED;
+    ssd::DtOpts o;
+    rc = dt_opts(opts, o);
+    if (rc != SSD_OK) return rc;
+    const bool bf16 = dtype == SSD_BF16;
+    size_t seg_off;
+    const Workspace ws =
+        varlen_layout(seqlen, nheads, headdim, ngroups, dstate, chunk, bf16, &seg_off);
+    if (!workspace || workspace_bytes < ws.total) return SSD_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return SSD_ERR_WORKSPACE;
+
+    char *base = static_cast<char *>(workspace);
+    float *cumsum = reinterpret_cast<float *>(base + ws.cumsum_off);
+    float *delta = reinterpret_cast<float *>(base + ws.delta_off);
+    float *states = reinterpret_cast<float *>(base + ws.states_off);
+    void *cinit = base + ws.init_off;
+    void *cb = base + ws.cb_off;
+    int *seg = reinterpret_cast<int *>(base + seg_off);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // the separate stages, each masking by seg (no fused stage 2 + 3 here)
+    hipError_t e = ssd::launch_varlen_seg(cu_seqlens, nseq, seqlen, chunk, seg, s);
+    if (e == hipSuccess)
+        e = ssd::launch_chunk_cumsum(dt, A, 1, seqlen, nheads, chunk, bf16, o, cumsum, delta, s);
+    if (e == hipSuccess)
+        e = ssd::launch_chunk_state(x, B, delta, cumsum, seg, 1, seqlen, nheads, ngroups, dstate,
+                                    chunk, bf16, states, s);
+    if (e == hipSuccess)
+        e = ssd::launch_state_passing(states, cumsum, nullptr, seg, 1, seqlen, nheads, dstate,
+                                      chunk, bf16, cinit, nullptr, s);
+    if (e == hipSuccess && ssd::chunk_scan_reads_cb(bf16))
+        e = ssd::launch_chunk_cb(B, C, 1, seqlen, ngroups, dstate, chunk, bf16, cb, s);
+    if (e == hipSuccess)
+        e = ssd::launch_chunk_scan(x, delta, cumsum, B, C, cb, D, cinit, seg, 1, seqlen, nheads,
+                                   ngroups, dstate, chunk, bf16, y, s);
+    if (e == hipSuccess && seq_states)
+        e = ssd::launch_varlen_final_states(x, B, delta, cumsum, cu_seqlens, seg, cinit, nseq,
+                                            seqlen, nheads, ngroups, dstate, chunk, bf16,
+                                            seq_states, s);
     return status_of(e);
 }
 

@@ -29,8 +29,11 @@ hipError_t launch_chunk_cumsum(const void *dt, const float *A, int batch, int se
                                int chunk, bool bf16, const DtOpts &opts, float *dA_cumsum,
                                float *delta, hipStream_t stream);
 
+// seg (nullable): packed sequences, one int per token in dA_cumsum's chunk-padded
+// layout: the first token of the token's sequence relative to its chunk's first
+// token, or -1 if that sequence began in an earlier chunk (launch_varlen_seg).
 hipError_t launch_chunk_state(const void *x, const void *B, const float *delta,
-                              const float *dA_cumsum,
+                              const float *dA_cumsum, const int *seg,
                               int batch, int seqlen, int nheads, int ngroups, int dstate, int chunk,
                               bool bf16, float *states, hipStream_t stream);
 
@@ -46,7 +49,7 @@ hipError_t launch_chunk_state_passing(const void *x, const void *B, const float 
 // chunk_init is written in the MFMA operand type of the forward's dtype
 // (bf16 when bf16 is true, else float32).
 hipError_t launch_state_passing(const float *states, const float *dA_cumsum, const float *init,
-                                int batch, int seqlen, int nheads, int dstate, int chunk,
+                                const int *seg, int batch, int seqlen, int nheads, int dstate, int chunk,
                                 bool bf16, void *chunk_init, float *final_state,
                                 hipStream_t stream);
 
@@ -61,8 +64,20 @@ bool chunk_scan_reads_cb(bool bf16);
 
 hipError_t launch_chunk_scan(const void *x, const float *delta, const float *dA_cumsum, const void *B,
                              const void *C, const void *cb, const float *D, const void *chunk_init,
-                             int batch, int seqlen, int nheads, int ngroups, int dstate, int chunk,
+                             const int *seg, int batch, int seqlen, int nheads, int ngroups, int dstate, int chunk,
                              bool bf16, void *y, hipStream_t stream);
+
+// Packed sequences (batch 1): seg of every token position (nC*Q ints) from
+// cu_seqlens [nseq + 1]; and each sequence's state after its last token,
+// seq_states [nseq][H][P][N] float32, from the stage outputs (chunk_init in the
+// operand type of the forward's dtype).
+hipError_t launch_varlen_seg(const int *cu_seqlens, int nseq, int seqlen, int chunk, int *seg,
+                             hipStream_t stream);
+hipError_t launch_varlen_final_states(const void *x, const void *B, const float *delta,
+                                      const float *dA_cumsum, const int *cu_seqlens,
+                                      const int *seg, const void *chunk_init, int nseq,
+                                      int seqlen, int nheads, int ngroups, int dstate, int chunk,
+                                      bool bf16, float *seq_states, hipStream_t stream);
 
 hipError_t launch_decode_step(float *state, const void *x, const void *dt, const float *A,
                               const void *B, const void *C, const float *D, int batch, int nheads,

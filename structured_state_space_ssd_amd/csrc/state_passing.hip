@@ -3,6 +3,8 @@
 // hidden state). With alpha_c = exp(s_end(c)) the total decay of chunk c and
 // S_c its own contribution (stage 2):
 //   H_0 = init,  H_{c+1} = alpha_c * H_c + S_c,  chunk_init[c] = H_c.
+// Packed sequences (seg given): alpha_c = 0 where the sequence of chunk c's
+// last token begins inside chunk c (S_c then holds that sequence's tokens only).
 //
 // Sequential over chunks, parallel over (batch, head, P*N/4): each thread owns
 // one float4 of a head's P x N state. The chunk loop is unrolled by 8 so that
@@ -28,8 +30,8 @@ __device__ __forceinline__ void store4(__bf16 *p, const floatx4 &v) {
 template <typename OutT>
 __global__ __launch_bounds__(256) void state_passing_kernel(
     const float *__restrict__ states, const float *__restrict__ dA_cumsum,
-    const float *__restrict__ init, int L, int H, int PN, int Q, int nC,
-    OutT *__restrict__ chunk_init, float *__restrict__ final_state) {
+    const float *__restrict__ init, const int *__restrict__ seg, int L, int H, int PN, int Q,
+    int nC, OutT *__restrict__ chunk_init, float *__restrict__ final_state) {
     const int h = blockIdx.y, b = blockIdx.z;
     const int e4 = blockIdx.x * 256 + threadIdx.x;
     if (e4 * 4 >= PN) return;
@@ -51,6 +53,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
                 sv[u] = *reinterpret_cast<const floatx4 *>(sp + c * cstride);
                 const int lenc = min(Q, L - c * Q);
                 dec[u] = exp2f(s[(size_t)c * Q + lenc - 1] * kLog2e);
+                if (seg && seg[((size_t)b * nC + c) * Q + lenc - 1] >= 0) dec[u] = 0.0f;
             }
         }
 #pragma unroll
@@ -66,19 +69,19 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
 }
 
 hipError_t launch_state_passing(const float *states, const float *dA_cumsum, const float *init,
-                                int batch, int seqlen, int nheads, int dstate, int chunk,
-                                bool bf16, void *chunk_init, float *final_state,
+                                const int *seg, int batch, int seqlen, int nheads, int dstate,
+                                int chunk, bool bf16, void *chunk_init, float *final_state,
                                 hipStream_t stream) {
     const int nC = (seqlen + chunk - 1) / chunk;
     const int PN = 64 * dstate;
     const dim3 grid((PN / 4 + 255) / 256, nheads, batch);
     if (bf16)
         state_passing_kernel<__bf16><<<grid, 256, 0, stream>>>(
-            states, dA_cumsum, init, seqlen, nheads, PN, chunk, nC,
+            states, dA_cumsum, init, seg, seqlen, nheads, PN, chunk, nC,
             static_cast<__bf16 *>(chunk_init), final_state);
     else
         state_passing_kernel<float><<<grid, 256, 0, stream>>>(
-            states, dA_cumsum, init, seqlen, nheads, PN, chunk, nC,
+            states, dA_cumsum, init, seg, seqlen, nheads, PN, chunk, nC,
             static_cast<float *>(chunk_init), final_state);
     return hipGetLastError();
 }

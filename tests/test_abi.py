@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     for required in ("ssd_forward", "ssd_step", "ssd_forward_workspace_size", "ssd_strerror",
                      "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_cb",
                      "ssd_chunk_scan", "ssd_forward_timed", "ssd_chunk_cb_size", "ssd_forward_ex",
-                     "ssd_step_ex"):
+                     "ssd_step_ex", "ssd_forward_varlen", "ssd_forward_varlen_workspace_size"):
         assert required in names
 
 
@@ -75,6 +75,15 @@ def test_workspace_size(lib, dims):
     assert lib.ssd_forward_workspace_size(*dims) == _ws_expected(*dims)
     Bt, L, H, P, G, N, Q, dt = dims
     assert lib.ssd_chunk_cb_size(Bt, L, G, Q, dt) == _cb_expected(Bt, L, G, Q, dt)
+
+
+@pytest.mark.parametrize("dims", [(16384, 80, 64, 1, 64, 256, 1), (700, 4, 64, 2, 64, 64, 0),
+                                  (1, 1, 64, 1, 16, 64, 1)])
+def test_varlen_workspace_size(lib, dims):
+    L, H, P, G, N, Q, dt = dims
+    al = lambda v: (v + 255) // 256 * 256
+    seg = al(-(-L // Q) * Q * 4)  # one int32 per token position
+    assert lib.ssd_forward_varlen_workspace_size(*dims) == _ws_expected(1, L, H, P, G, N, Q, dt) + seg
 
 
 def test_workspace_size_invalid(lib):
@@ -202,3 +211,33 @@ def test_options_checked_after_shapes(lib):
     assert rc == SSD_ERR_SHAPE
     rc = lib.ssd_step_ex(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, 8, 64, 2, 128, 1, FAKE, o, None)
     assert rc == SSD_ERR_NULL
+
+
+def _varlen(lib, **kw):
+    a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, cu=FAKE, nseq=3, L=128, H=4, P=64,
+             G=1, N=64, Q=64, dtype=1, y=FAKE, ss=None, ws=FAKE, wsb=1 << 40, opts=None)
+    a.update(kw)
+    return lib.ssd_forward_varlen(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["cu"], a["nseq"],
+                                  a["L"], a["H"], a["P"], a["G"], a["N"], a["Q"], a["dtype"], a["y"],
+                                  a["ss"], a["ws"], a["wsb"], a["opts"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=None), SSD_ERR_NULL),
+    (dict(x=None), SSD_ERR_NULL),
+    (dict(nseq=0), SSD_ERR_SHAPE),
+    (dict(L=0), SSD_ERR_SHAPE),
+    (dict(H=6, G=4), SSD_ERR_SHAPE),
+    (dict(N=48), SSD_ERR_UNSUPPORTED),
+    (dict(Q=32), SSD_ERR_UNSUPPORTED),
+    (dict(cu=ctypes.c_void_p(0x100002)), SSD_ERR_UNSUPPORTED),
+    (dict(ss=ctypes.c_void_p(0x100008)), SSD_ERR_UNSUPPORTED),
+    (dict(ws=None), SSD_ERR_WORKSPACE),
+    (dict(wsb=4096), SSD_ERR_WORKSPACE),
+])
+def test_varlen_rejects(lib, kw, code):
+    assert _varlen(lib, **kw) == code
+
+
+def test_varlen_rejects_bad_options(lib):
+    assert _varlen(lib, opts=_opts(discretization=3)) == SSD_ERR_OPTION
