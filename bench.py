@@ -242,6 +242,43 @@ def time_forward_options(w, steps, warmup):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
+def varlen_workload():
+    """The 2.7B layer's tokens (8 x 2048) packed into one row of sequences of
+    1 .. 4096 tokens (ssd_workloads.packed_cu_seqlens)."""
+    import ssd_workloads as W
+    w = W.Workload("packed_2.7b", 1, 16384, 80, 64, 1, 64, 256, "bf16", 1 / 8, 1e-3, 1e-1,
+                   seed=860)
+    return w, W.packed_cu_seqlens(w.seqlen, 4096, seed=861)
+
+
+def time_forward_varlen(steps, warmup):
+    """Whole-forward time (host clock) of the packed variable-length forward,
+    per-sequence final states included."""
+    import torch
+    import ssd_workloads as W
+    import structured_state_space_ssd_amd as ssd
+
+    w, cu = varlen_workload()
+    g = upload(W.generate(w))
+    cu_g = torch.from_numpy(cu).cuda()
+    x = g["x"]
+    ws = torch.empty(int(ssd._native.lib.ssd_forward_varlen_workspace_size(
+        w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk, 1)), dtype=torch.uint8,
+        device="cuda")
+    y = torch.empty_like(x)
+    args = [g[k] for k in ("x", "dt", "A", "B", "C", "D")] + [cu_g]
+    kw = dict(chunk=w.chunk, workspace=ws, y=y, return_seq_states=True)
+    for _ in range(warmup):
+        ssd.forward_varlen(*args, **kw)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ssd.forward_varlen(*args, **kw)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    return w, cu, ms
+
+
 def time_decode(w, warmup=3):
     import torch
     import ssd_workloads as W
@@ -527,6 +564,14 @@ def main():
     print(f"[bench] forward with every step-size option: {opt_ms * 1e3:.1f} us", file=sys.stderr,
           flush=True)
 
+    wv, cu, vl_ms = time_forward_varlen(max(10, args.steps // 2), 3)
+    varlen = {"workload": f"{wv.seqlen} tokens (the 2.7B layer's 8 x 2048) packed as {cu.size - 1} "
+                          "sequences of 1 .. 4096 tokens, bf16, per-sequence final states",
+              "us_per_forward": round(vl_ms * 1e3, 2),
+              "tokens_per_s": round(wv.seqlen / (vl_ms * 1e-3), 1)}
+    print(f"[bench] packed variable-length forward: {vl_ms * 1e3:.1f} us", file=sys.stderr,
+          flush=True)
+
     extra = {}
     if args.all:
         for name in ("tiny_f32", "large_state", "long_seq"):
@@ -578,6 +623,7 @@ def main():
         "evented_us_per_step": round(fwd["evented_ms"] * 1e3, 2),
         "kernels": kernels,
         "forward_with_options": options,
+        "forward_varlen": varlen,
         "decode": decode,
         "hbm_copy_probe": probe,
     }

@@ -165,10 +165,17 @@ __device__ __forceinline__ void colfrag_swz(Frag<bf16_t> &f, const __bf16 *m, in
     f.v = bf16x8{ab[0], ab[1], ab[2], ab[3], bb[0], bb[1], bb[2], bb[3]};
 }
 
-template <int N, int Q>
+// FIN (packed sequences): one workgroup per (sequence k, head) forms the
+// sequence's final state instead: the chunk c holding its last token te is
+// cut after te (len = te - cQ + 1, so s_end = s_te), its tokens before the
+// sequence's first are masked by seg as usual, and exp(s_te) H_c (chunk_init,
+// the state entering chunk c) is added when the sequence began before chunk c.
+// states is then seq_states [nseq][H][P][N].
+template <int N, int Q, bool FIN>
 __global__ __launch_bounds__(512) void chunk_state_bf16_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ B, const float *__restrict__ delta,
-    const float *__restrict__ dA_cumsum, const int *__restrict__ seg, int L, int H, int G, int nC,
+    const float *__restrict__ dA_cumsum, const int *__restrict__ seg, const int *__restrict__ cu,
+    const __bf16 *__restrict__ chunk_init, int L, int H, int G, int nC,
     float *__restrict__ states) {
     constexpr int P = 64, NW = 8;
     constexpr int TP = N >= 128 ? 32 : 64;  // tokens per phase
@@ -183,10 +190,29 @@ __global__ __launch_bounds__(512) void chunk_state_bf16_kernel(
     __shared__ __attribute__((aligned(16))) __bf16 bs1[TP * N];
     __shared__ __attribute__((aligned(16))) float wj[Q];
 
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int g = h / (H / G);
-    const int t0 = c * Q, len = min(Q, L - t0);
+    const int h = blockIdx.y;
     const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = l >> 4;
+    int c, b, len;
+    float *dst;
+    if constexpr (FIN) {
+        const int k = blockIdx.x;
+        const int a = min(max(cu[k], 0), L), e = min(max(cu[k + 1], a), L);
+        dst = states + ((size_t)k * H + h) * (size_t)P * N;
+        if (e <= a) {  // an empty sequence: zero state (uniform across the workgroup)
+            for (int i = tid; i < P * N; i += 512) dst[i] = 0.0f;
+            return;
+        }
+        b = 0;
+        c = (e - 1) / Q;
+        len = e - c * Q;
+    } else {
+        c = blockIdx.x;
+        b = blockIdx.z;
+        len = min(Q, L - c * Q);
+        dst = states + (((size_t)b * nC + c) * H + h) * (size_t)P * N;
+    }
+    const int g = h / (H / G);
+    const int t0 = c * Q;
     const size_t xrow = (size_t)H * P, brow = (size_t)G * N;
     const bf16_t *xh = x + ((size_t)b * L + t0) * xrow + (size_t)h * P;
     const bf16_t *bg = B + ((size_t)b * L + t0) * brow + (size_t)g * N;
@@ -226,7 +252,7 @@ __global__ __launch_bounds__(512) void chunk_state_bf16_kernel(
 #pragma unroll
     for (int ph = 0; ph < NPH; ++ph) {
         wait_barrier<0>();  // phase ph in LDS; phase ph-1's buffers free
-        if (ph + 1 < NPH) issue(ph + 1);
+        if (ph + 1 < NPH && (ph + 1) * TP < len) issue(ph + 1);  // uniform
         const __bf16 *xsp = (ph & 1) ? xs1 : xs0;
         const __bf16 *bsp = (ph & 1) ? bs1 : bs0;
         const int kend = min(TP, len - ph * TP);  // tokens of this phase (<= 0: none)
@@ -256,15 +282,22 @@ __global__ __launch_bounds__(512) void chunk_state_bf16_kernel(
         }
     }
 
-    float *dst = states + (((size_t)b * nC + c) * H + h) * (size_t)P * N;
     const int cc = l & 15;
+    // FIN: the state the sequence entered chunk c with, decayed to its last token
+    const bool carry = FIN && j0 < 0;
+    const float dec = carry ? __builtin_amdgcn_exp2f(s_end * kLog2e) : 0.0f;
+    const __bf16 *hc = FIN ? chunk_init + ((size_t)c * H + h) * (size_t)P * N : nullptr;
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
         const int nt = w / 4 + 2 * i;
         if (nt < N / 16) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dst[(size_t)(pt * 16 + 4 * g4 + r) * N + nt * 16 + cc] = acc[i][r];
+            for (int r = 0; r < 4; ++r) {
+                const size_t o = (size_t)(pt * 16 + 4 * g4 + r) * N + nt * 16 + cc;
+                float v = acc[i][r];
+                if (carry) v += dec * static_cast<float>(hc[o]);
+                dst[o] = v;
+            }
         }
     }
 }
@@ -484,9 +517,9 @@ static void launch_cs(const void *x, const void *B, const float *dl, const float
     const int nC = (L + Q - 1) / Q;
     const dim3 grid(nC, H, batch);
     if constexpr (sizeof(T) == 2) {
-        chunk_state_bf16_kernel<N, Q><<<grid, 512, 0, stream>>>(
+        chunk_state_bf16_kernel<N, Q, false><<<grid, 512, 0, stream>>>(
             static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(B),
-            dl, dA, seg, L, H, G, nC, states);
+            dl, dA, seg, nullptr, nullptr, L, H, G, nC, states);
     } else {
         chunk_state_kernel<T, N, Q><<<grid, 512, 0, stream>>>(
             static_cast<const T *>(x), static_cast<const T *>(B), dl, dA, seg, L,
@@ -531,6 +564,44 @@ hipError_t launch_chunk_state(const void *x, const void *B, const float *delta,
                                    chunk, states, stream);
     return dispatch_cs<float>(x, B, delta, dA_cumsum, seg, batch, seqlen, nheads, ngroups, dstate, chunk,
                               states, stream);
+}
+
+}  // namespace ssd
+
+namespace ssd {
+
+// Packed sequences, bf16: each sequence's final state by the chunk state
+// kernel's FIN variant (MFMA over the sequence's tokens in its last chunk).
+hipError_t launch_varlen_final_states_bf16(const void *x, const void *B, const float *delta,
+                                           const float *dA_cumsum, const int *cu_seqlens,
+                                           const int *seg, const void *chunk_init, int nseq,
+                                           int seqlen, int nheads, int ngroups, int dstate,
+                                           int chunk, float *seq_states, hipStream_t stream) {
+    const int nC = (seqlen + chunk - 1) / chunk;
+    const dim3 grid(nseq, nheads);
+    const bf16_t *xx = static_cast<const bf16_t *>(x), *bb = static_cast<const bf16_t *>(B);
+    const __bf16 *hc = static_cast<const __bf16 *>(chunk_init);
+#define SSD_FIN(NN, QQ)                                                                         \
+    chunk_state_bf16_kernel<NN, QQ, true><<<grid, 512, 0, stream>>>(                            \
+        xx, bb, delta, dA_cumsum, seg, cu_seqlens, hc, seqlen, nheads, ngroups, nC, seq_states)
+#define SSD_FIN_Q(NN)                                                                           \
+    switch (chunk) {                                                                            \
+        case 64: SSD_FIN(NN, 64); break;                                                        \
+        case 128: SSD_FIN(NN, 128); break;                                                      \
+        case 256: SSD_FIN(NN, 256); break;                                                      \
+        default: return hipErrorInvalidValue;                                                   \
+    }
+    switch (dstate) {
+        case 16: SSD_FIN_Q(16); break;
+        case 32: SSD_FIN_Q(32); break;
+        case 64: SSD_FIN_Q(64); break;
+        case 128: SSD_FIN_Q(128); break;
+        case 256: SSD_FIN_Q(256); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef SSD_FIN_Q
+#undef SSD_FIN
+    return hipGetLastError();
 }
 
 }  // namespace ssd

@@ -16,8 +16,9 @@
 //
 // Each sequence's final state (the state after its last token te, in chunk
 // c) is H = [seg[te] < 0] exp(s_te) H_c + sum_{j = max(seg[te], 0)}^{te}
-// exp(s_te - s_j) w_j x_j B_j^T, formed by varlen_final_state_kernel from
-// the chunk_init of the state passing and the chunk's own tokens.
+// exp(s_te - s_j) w_j x_j B_j^T, from the chunk_init of the state passing and
+// the chunk's own tokens: for bf16 by the chunk state kernel on MFMA (its
+// final-state variant), for float32 by varlen_final_state_kernel below.
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -127,6 +128,12 @@ static hipError_t final_states_n(int N, dim3 grid, const void *x, const void *B,
     return hipGetLastError();
 }
 
+hipError_t launch_varlen_final_states_bf16(const void *x, const void *B, const float *delta,
+                                           const float *dA_cumsum, const int *cu_seqlens,
+                                           const int *seg, const void *chunk_init, int nseq,
+                                           int seqlen, int nheads, int ngroups, int dstate,
+                                           int chunk, float *seq_states, hipStream_t stream);
+
 hipError_t launch_varlen_final_states(const void *x, const void *B, const float *delta,
                                       const float *dA_cumsum, const int *cu_seqlens,
                                       const int *seg, const void *chunk_init, int nseq,
@@ -134,10 +141,10 @@ hipError_t launch_varlen_final_states(const void *x, const void *B, const float 
                                       bool bf16, float *seq_states, hipStream_t stream) {
     const int nC = (seqlen + chunk - 1) / chunk;
     const dim3 grid(nseq, nheads);
-    if (bf16)
-        return final_states_n<bf16_t, __bf16>(dstate, grid, x, B, delta, dA_cumsum, cu_seqlens,
-                                              seg, chunk_init, seqlen, nheads, ngroups, chunk,
-                                              nC, seq_states, stream);
+    if (bf16)  // on MFMA, by the chunk state kernel (chunk_state.hip)
+        return launch_varlen_final_states_bf16(x, B, delta, dA_cumsum, cu_seqlens, seg,
+                                               chunk_init, nseq, seqlen, nheads, ngroups, dstate,
+                                               chunk, seq_states, stream);
     return final_states_n<float, float>(dstate, grid, x, B, delta, dA_cumsum, cu_seqlens, seg,
                                         chunk_init, seqlen, nheads, ngroups, chunk, nC,
                                         seq_states, stream);
