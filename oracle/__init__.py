@@ -14,6 +14,9 @@ Contents
   an independent O(L^2) computation used to pin the recurrence.
 * ``chunk_cumsum``: the within-chunk inclusive prefix sum of dt*A, the first
   step of the block decomposition ("Mamba 模型", section 4.1).
+* ``backward``: reverse-mode gradients of the forward (adjoint recurrence of
+  the state, in fp64, with the states recomputed from checkpoints), with the
+  same options.
 * ``forward_varlen``: packed variable-length sequences (the dynamic sequence
   packing of the "Mamba-2架构深度解析" page, section 5): the recurrence with the
   state reset to zero where each sequence begins, and every sequence's final
@@ -90,6 +93,9 @@ def _load(path=None):
         lib.ssd_oracle_step_ex.restype = ctypes.c_int
         lib.ssd_oracle_forward_varlen.argtypes = [fp] * 6 + [ip] * 5 + [fp, ip, fp, ip, dp, dp, ip, op]
         lib.ssd_oracle_forward_varlen.restype = ctypes.c_int
+        lib.ssd_oracle_backward.argtypes = ([fp] * 6 + [dp, fp, dp] + [ip] * 6 + [fp, ip] +
+                                            [dp] * 8 + [ip, op])
+        lib.ssd_oracle_backward.restype = ctypes.c_int
         _libs[path] = lib
     return _libs[path]
 
@@ -148,6 +154,56 @@ def forward(x, dt, A, B, C, D=None, init=None, units=None, snap_every=0,
     if rc != 0:
         raise RuntimeError(f"ssd_oracle_forward failed: {rc}")
     return y, st, snaps
+
+
+def backward(x, dt, A, B, C, D, init, dy, dfinal=None, units=None, nthreads=None, lib=None,
+             dt_bias=None, dt_softplus=False, dt_limit=None, zoh=False):
+    """Gradients of loss = sum(dy * y) + sum(dfinal * final_state) for
+    ``forward`` with the same inputs and options. Shapes as ``forward``; dy
+    like x, dfinal like init (float64) or None.
+
+    Returns a dict of float64 arrays shaped like the inputs, summed the way
+    the inputs are shared: dx [Bt,L,H,P], ddt [Bt,L,H] (raw dt), dA [H],
+    dB, dC [Bt,L,G,N] (summed over the heads of a group), dD [H],
+    dinit [Bt,H,P,N], dbias [H]. With ``units`` (flat b*H + h) only those
+    units are computed and the per-unit arrays are returned instead:
+    dx [U,L,P], ddt [U,L], dA, dD, dbias [U], dB, dC [U,L,N], dinit [U,P,N].
+    """
+    x, dt, A, B, C, D, dy = map(_f32, (x, dt, A, B, C, D, dy))
+    init = None if init is None else np.ascontiguousarray(init, dtype=np.float64)
+    dfinal = None if dfinal is None else np.ascontiguousarray(dfinal, dtype=np.float64)
+    Bt, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dy.shape == x.shape and dt.shape == (Bt, L, H)
+    if units is None:
+        units_arr, U = None, Bt * H
+    else:
+        units_arr = np.ascontiguousarray(units, dtype=np.int32)
+        U = units_arr.size
+    out = {"dx": np.empty((U, L, P)), "ddt": np.empty((U, L)), "dA": np.empty(U),
+           "dB": np.empty((U, L, N)), "dC": np.empty((U, L, N)), "dD": np.empty(U),
+           "dinit": np.empty((U, P, N)), "dbias": np.empty(U)}
+    o, _keep = _opts(H, dt_bias, dt_softplus, dt_limit, zoh)
+    rc = _load(lib).ssd_oracle_backward(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init), _ptr(dy), _ptr(dfinal),
+        Bt, L, H, P, G, N, _ptr(units_arr), U, *(out[k].ctypes.data for k in
+        ("dx", "ddt", "dA", "dB", "dC", "dD", "dinit", "dbias")),
+        nthreads or default_threads(), None if o is None else ctypes.byref(o))
+    if rc != 0:
+        raise RuntimeError(f"ssd_oracle_backward failed: {rc}")
+    if units is not None:
+        return out
+    hpg = H // G
+    return {
+        "dx": out["dx"].reshape(Bt, H, L, P).transpose(0, 2, 1, 3),
+        "ddt": out["ddt"].reshape(Bt, H, L).transpose(0, 2, 1),
+        "dA": out["dA"].reshape(Bt, H).sum(axis=0),
+        "dB": out["dB"].reshape(Bt, G, hpg, L, N).sum(axis=2).transpose(0, 2, 1, 3),
+        "dC": out["dC"].reshape(Bt, G, hpg, L, N).sum(axis=2).transpose(0, 2, 1, 3),
+        "dD": out["dD"].reshape(Bt, H).sum(axis=0),
+        "dinit": out["dinit"].reshape(Bt, H, P, N),
+        "dbias": out["dbias"].reshape(Bt, H).sum(axis=0),
+    }
 
 
 def forward_varlen(x, dt, A, B, C, D, cu_seqlens, units=None, nthreads=None, lib=None,

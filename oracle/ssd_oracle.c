@@ -337,3 +337,210 @@ int ssd_oracle_step(double *state, const float *x, const float *dt, const float 
     return ssd_oracle_step_ex(state, x, dt, A, B, C, D, batch, nheads, headdim, ngroups, dstate,
                               units, nunits, y, nthreads, NULL);
 }
+
+/* ------------------------------------------------------------------------- */
+/* Gradients (reverse mode) of the forward above.                             */
+/*                                                                            */
+/* With loss = sum_t dy_t . y_t + <dfinal, h_{L-1}>, the adjoint of the state */
+/* g_t = dloss/dh_t obeys g_t = dy_t C_t^T + a_{t+1} g_{t+1} (g_{L-1} starts  */
+/* from dfinal), since h_{t+1} = a_{t+1} h_t + ... and y_t = h_t C_t + D x_t. */
+/* Each token then gives, with hp = h_{t-1} and w the input weight:           */
+/*   dx_t = w g_t B_t + D dy_t,   dB_t = w g_t^T x_t,   dC_t = h_t^T dy_t,    */
+/*   dstep_t = (da/dstep) <g_t, hp> + (dw/dstep) x_t^T g_t B_t,               */
+/*   dA += (da/dA) <g_t, hp> + (dw/dA) x_t^T g_t B_t,   dD += dy_t . x_t,     */
+/* and d(raw dt) = dstep * d(step)/d(raw) through the options; dinit = a_0 g_0.*/
+/* States are recomputed block by block from checkpoints every BWD_BLOCK     */
+/* tokens.                                                                    */
+/* ------------------------------------------------------------------------- */
+
+#define BWD_BLOCK 64
+
+/* d(step)/d(raw dt): 1, times sigmoid for softplus, times 0 outside the clamp
+ * range (the bounds themselves pass the gradient). */
+static double step_slope(const oracle_opts *o, double v, int h)
+{
+    if (!o) return 1.0;
+    double slope = 1.0;
+    if (o->dt_bias) v += (double)o->dt_bias[h];
+    if (o->dt_softplus) {
+        slope = 1.0 / (1.0 + exp(-v));
+        v = fmax(v, 0.0) + log1p(exp(-fabs(v)));
+    }
+    if (o->dt_clamp && (v < o->dt_min || v > o->dt_max)) slope = 0.0;
+    return slope;
+}
+
+/* Derivatives of the input weight w(d, A) with respect to d and A. For the
+ * zero-order hold w = (e^z - 1)/A with z = d A: dw/dd = e^z and
+ * dw/dA = (z e^z - (e^z - 1)) / A^2 = d^2 (1/2 + z/3 + z^2/8 + ...). */
+static void weight_slopes(const oracle_opts *o, double d, double A, double *wd, double *wA)
+{
+    if (!(o && o->zoh)) {
+        *wd = 1.0;
+        *wA = 0.0;
+        return;
+    }
+    const double z = d * A;
+    *wd = exp(z);
+    if (fabs(z) < 1e-3) *wA = d * d * (0.5 + z / 3.0 + z * z / 8.0);
+    else *wA = (z * exp(z) - expm1(z)) / (A * A);
+}
+
+typedef struct {
+    const float *x, *dt, *A, *B, *C, *D, *dy;
+    const double *init, *dfinal;
+    int batch, seqlen, nheads, headdim, ngroups, dstate;
+    const int *units;
+    int nunits;
+    double *dx, *ddt, *dA, *dB, *dC, *dD, *dinit, *dbias;
+    const oracle_opts *opts;
+    atomic_int next;
+} bwd_job;
+
+/* State update of token t (global index tok) from prev into out. */
+static void bwd_advance(const bwd_job *j, size_t tok, int h, int g, const double *prev, double *out)
+{
+    const int H = j->nheads, P = j->headdim, N = j->dstate, G = j->ngroups;
+    const double A = j->A[h];
+    const double d = step_size(j->opts, j->dt[tok * H + h], h);
+    const double a = exp(d * A);
+    const double wi = input_weight(j->opts, d, A);
+    const float *xt = j->x + (tok * H + h) * P;
+    const float *Bt = j->B + (tok * G + g) * N;
+    for (int p = 0; p < P; ++p)
+        for (int n = 0; n < N; ++n)
+            out[(size_t)p * N + n] = a * prev[(size_t)p * N + n] + wi * (double)xt[p] * (double)Bt[n];
+}
+
+static void bwd_unit(bwd_job *j, int u, double *ckpt, double *blk, double *gs)
+{
+    const int H = j->nheads, P = j->headdim, N = j->dstate, L = j->seqlen;
+    const int G = j->ngroups;
+    const int bh = j->units ? j->units[u] : u;
+    const int b = bh / H, h = bh % H;
+    const int g = h / (H / G);
+    const double A = j->A[h];
+    const double D = j->D ? j->D[h] : 0.0;
+    const size_t PN = (size_t)P * N;
+    const int nb = (L + BWD_BLOCK - 1) / BWD_BLOCK;
+
+    /* forward: the state entering every block */
+    double *hs = blk;
+    if (j->init) memcpy(hs, j->init + (size_t)bh * PN, PN * sizeof(double));
+    else memset(hs, 0, PN * sizeof(double));
+    for (int t = 0; t < L; ++t) {
+        if (t % BWD_BLOCK == 0) memcpy(ckpt + (size_t)(t / BWD_BLOCK) * PN, hs, PN * sizeof(double));
+        bwd_advance(j, (size_t)b * L + t, h, g, hs, blk + PN);
+        memcpy(hs, blk + PN, PN * sizeof(double));
+    }
+
+    /* backward */
+    if (j->dfinal) memcpy(gs, j->dfinal + (size_t)bh * PN, PN * sizeof(double));
+    else memset(gs, 0, PN * sizeof(double));
+    double dA = 0.0, dD = 0.0, dbias = 0.0;
+    for (int kb = nb - 1; kb >= 0; --kb) {
+        const int t0 = kb * BWD_BLOCK, t1 = t0 + BWD_BLOCK < L ? t0 + BWD_BLOCK : L;
+        memcpy(blk, ckpt + (size_t)kb * PN, PN * sizeof(double));  /* h_{t0-1} */
+        for (int t = t0; t < t1; ++t)
+            bwd_advance(j, (size_t)b * L + t, h, g, blk + (size_t)(t - t0) * PN,
+                        blk + (size_t)(t - t0 + 1) * PN);
+        for (int t = t1 - 1; t >= t0; --t) {
+            const size_t tok = (size_t)b * L + t;
+            const double raw = j->dt[tok * H + h];
+            const double d = step_size(j->opts, raw, h);
+            const double a = exp(d * A);
+            const double wi = input_weight(j->opts, d, A);
+            double wd, wA;
+            weight_slopes(j->opts, d, A, &wd, &wA);
+            const float *xt = j->x + (tok * H + h) * P;
+            const float *dyt = j->dy + (tok * H + h) * P;
+            const float *Bt = j->B + (tok * G + g) * N;
+            const float *Ct = j->C + (tok * G + g) * N;
+            const double *hcur = blk + (size_t)(t - t0 + 1) * PN;
+            const double *hprev = blk + (size_t)(t - t0) * PN;
+            /* g_t: the output of token t reads h_t */
+            for (int p = 0; p < P; ++p)
+                for (int n = 0; n < N; ++n) gs[(size_t)p * N + n] += (double)dyt[p] * (double)Ct[n];
+            double gh = 0.0, gx = 0.0;
+            double *dxt = j->dx + ((size_t)u * L + t) * P;
+            double *dBt = j->dB + ((size_t)u * L + t) * N;
+            double *dCt = j->dC + ((size_t)u * L + t) * N;
+            for (int n = 0; n < N; ++n) dBt[n] = dCt[n] = 0.0;
+            for (int p = 0; p < P; ++p) {
+                const double *gr = gs + (size_t)p * N;
+                double gB = 0.0;
+                for (int n = 0; n < N; ++n) {
+                    gh += gr[n] * hprev[(size_t)p * N + n];
+                    gB += gr[n] * (double)Bt[n];
+                    dBt[n] += wi * gr[n] * (double)xt[p];
+                    dCt[n] += (double)dyt[p] * hcur[(size_t)p * N + n];
+                }
+                gx += (double)xt[p] * gB;
+                dxt[p] = wi * gB + D * (double)dyt[p];
+                dD += (double)dyt[p] * (double)xt[p];
+            }
+            const double dstep = A * a * gh + wd * gx;
+            dA += d * a * gh + wA * gx;
+            const double draw = dstep * step_slope(j->opts, raw, h);
+            j->ddt[(size_t)u * L + t] = draw;
+            dbias += draw;
+            for (size_t k = 0; k < PN; ++k) gs[k] *= a;  /* to h_{t-1} */
+        }
+    }
+    j->dA[u] = dA;
+    if (j->dD) j->dD[u] = dD;
+    if (j->dbias) j->dbias[u] = dbias;
+    if (j->dinit) memcpy(j->dinit + (size_t)u * PN, gs, PN * sizeof(double));
+}
+
+static void *bwd_worker(void *arg)
+{
+    bwd_job *j = (bwd_job *)arg;
+    const size_t PN = (size_t)j->headdim * j->dstate;
+    const int nb = (j->seqlen + BWD_BLOCK - 1) / BWD_BLOCK;
+    double *ckpt = (double *)malloc((size_t)(nb > 0 ? nb : 1) * PN * sizeof(double));
+    double *blk = (double *)malloc((size_t)(BWD_BLOCK + 1) * PN * sizeof(double));
+    double *gs = (double *)malloc(PN * sizeof(double));
+    void *rc = NULL;
+    if (!ckpt || !blk || !gs) rc = (void *)1;
+    for (; rc == NULL;) {
+        int u = atomic_fetch_add(&j->next, 1);
+        if (u >= j->nunits) break;
+        bwd_unit(j, u, ckpt, blk, gs);
+    }
+    free(ckpt);
+    free(blk);
+    free(gs);
+    return rc;
+}
+
+/*
+ * Gradients of loss = sum dy . y + <dfinal, final state> (dfinal may be NULL)
+ * for the forward of ssd_oracle_forward_ex with the same arguments and options.
+ * Per unit u = (b, h) (units: flat b*nheads + h, or NULL for all):
+ *   dx [U][L][P]; ddt [U][L] (with respect to the raw dt); dA [U];
+ *   dB, dC [U][L][N] (this head's share: a group's gradient is the sum over
+ *   its heads); dD [U] (may be NULL); dinit [U][P][N] (may be NULL);
+ *   dbias [U] (may be NULL; the gradient of opts->dt_bias[h] from this unit).
+ * dy has x's layout; dfinal [batch][nheads][P][N].
+ */
+int ssd_oracle_backward(const float *x, const float *dt, const float *A, const float *B,
+                        const float *C, const float *D, const double *init, const float *dy,
+                        const double *dfinal, int batch, int seqlen, int nheads, int headdim,
+                        int ngroups, int dstate, const int *units, int nunits, double *dx,
+                        double *ddt, double *dA, double *dB, double *dC, double *dD,
+                        double *dinit, double *dbias, int nthreads, const oracle_opts *opts)
+{
+    if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC) return -1;
+    if (batch < 1 || seqlen < 1 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1) return -2;
+    if (nheads % ngroups) return -2;
+    if (!units) nunits = batch * nheads;
+    if (nunits < 0) return -2;
+    for (int u = 0; units && u < nunits; ++u)
+        if (units[u] < 0 || units[u] >= batch * nheads) return -2;
+    if (nunits == 0) return 0;
+    bwd_job j = {x, dt, A, B, C, D, dy, init, dfinal, batch, seqlen, nheads, headdim, ngroups,
+                 dstate, units, nunits, dx, ddt, dA, dB, dC, dD, dinit, dbias, opts, 0};
+    atomic_init(&j.next, 0);
+    return run_threads(bwd_worker, &j, nthreads, nunits);
+}

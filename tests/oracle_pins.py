@@ -431,7 +431,72 @@ def pin_varlen(lib=None):
     assert np.array_equal(y1, yf) and np.array_equal(st1[:, 0], sf)
 
 
+def _loss(x, dt, A, B, C, D, init, dy, dfinal, lib, **opts):
+    """sum(dy * y) + sum(dfinal * final state) of the forward oracle, float64."""
+    y, st, _ = oracle.forward(x, dt, A, B, C, D, init, lib=lib, **opts)
+    Bt, L, H, P = x.shape
+    y = y.reshape(Bt, H, L, P).transpose(0, 2, 1, 3)
+    return float((y * dy).sum() + (st.reshape(dfinal.shape) * dfinal).sum())
+
+
+def pin_backward_finite_differences(lib=None):
+    """P17: every gradient of the backward oracle is the derivative of the
+    (pinned) forward oracle: <dZ, V> equals the central difference
+    (loss(Z + eps V) - loss(Z - eps V)) / (2 eps) for random directions V, with
+    dyadic inputs so that Z +- eps V is exact in float32. The loss is
+    sum(dy * y) + sum(dfinal * final state). Checked without options and with
+    bias + softplus + clamp (bounds hit) + zero-order hold."""
+    rng = np.random.default_rng(27)
+    Bt, L, H, P, G, N = 2, 19, 4, 3, 2, 5
+    dyad = lambda shape, lo, hi, den: _dyadic(rng, shape, lo, hi, den)
+    base = dict(x=dyad((Bt, L, H, P), -2, 2, 16), B=dyad((Bt, L, G, N), -1, 1, 32),
+                C=dyad((Bt, L, G, N), -1, 1, 32), A=-dyad((H,), 0.5, 4, 64), D=dyad((H,), -1, 1, 16),
+                init=dyad((Bt, H, P, N), -1, 1, 8).astype(np.float64))
+    dy = rng.standard_normal((Bt, L, H, P)).astype(np.float32)
+    dfinal = rng.standard_normal((Bt, H, P, N))
+    dts = dyad((Bt, L, H), 0.01, 0.3, 4096)
+    raw = dyad((Bt, L, H), -4.0, 1.0, 4096)
+    bias = np.array([-1.0, 0.25, -2.0, 0.0], np.float32)
+    lo, hi = 0.05, 0.6
+    for _ in range(20):  # keep every step away from the clamp's kinks
+        sp = np.logaddexp(0.0, raw.astype(np.float64) + bias)
+        near = np.minimum(np.abs(sp - lo), np.abs(sp - hi)) <= 1e-3
+        if not near.any():
+            break
+        raw[near] += np.float32(1.0 / 32)
+    assert not near.any()
+    assert (sp < lo).mean() > 0.05 and (sp > hi).mean() > 0.02
+    cases = [(dts, {}), (raw, dict(dt_bias=bias, dt_softplus=True, dt_limit=(lo, hi), zoh=True))]
+    for dt, opts in cases:
+        args = dict(base, dt=dt)
+        grads = oracle.backward(args["x"], dt, args["A"], args["B"], args["C"], args["D"],
+                                args["init"], dy, dfinal, lib=lib, **opts)
+        steps = dict(x=2.0 ** -8, dt=2.0 ** -16, A=2.0 ** -14, B=2.0 ** -8, C=2.0 ** -8,
+                     D=2.0 ** -8, init=2.0 ** -8)
+        for name, eps in steps.items():
+            V = rng.integers(-1, 2, size=args[name].shape).astype(np.float64)
+            plus, minus = dict(args), dict(args)
+            dtype = np.float64 if name == "init" else np.float32
+            plus[name] = (args[name] + eps * V).astype(dtype)
+            minus[name] = (args[name] - eps * V).astype(dtype)
+            assert np.array_equal(plus[name].astype(np.float64) - args[name], eps * V)
+            fd = (_loss(dy=dy, dfinal=dfinal, lib=lib, **plus, **opts) -
+                  _loss(dy=dy, dfinal=dfinal, lib=lib, **minus, **opts)) / (2 * eps)
+            an = float((grads["dinit" if name == "init" else "d" + name] * V).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, bool(opts), fd, an)
+        if opts:  # the bias enters like a shift of every raw dt of its head
+            eps = 2.0 ** -16
+            V = rng.integers(-1, 2, size=H).astype(np.float64)
+            bp = (bias + eps * V).astype(np.float32)
+            bm = (bias - eps * V).astype(np.float32)
+            o2 = dict(opts)
+            fd = (_loss(dy=dy, dfinal=dfinal, lib=lib, **args, **dict(o2, dt_bias=bp)) -
+                  _loss(dy=dy, dfinal=dfinal, lib=lib, **args, **dict(o2, dt_bias=bm))) / (2 * eps)
+            an = float((grads["dbias"] * V).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), ("bias", fd, an)
+
+
 ALL_PINS = [pin_duality, pin_cumsum, pin_lti_geometric, pin_single_token, pin_no_memory,
             pin_state_carry, pin_forward_vs_step, pin_linearity, pin_groups, pin_golden,
             pin_dt_bias, pin_softplus_and_clamp, pin_zoh_ode, pin_zoh_forms,
-            pin_step_with_options, pin_varlen]
+            pin_step_with_options, pin_varlen, pin_backward_finite_differences]

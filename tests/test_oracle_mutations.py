@@ -44,6 +44,22 @@ MUTATIONS = {
                           "memcpy(j->seq_states + ((size_t)u * j->nseq + (k + 1) % j->nseq) * PN"),
     "varlen_boundary_off_by_one": ("while (k + 1 < j->nseq && j->cu[k + 1] <= t) ++k;",
                                    "while (k + 1 < j->nseq && j->cu[k + 1] < t) ++k;"),
+    "bwd_adjoint_not_decayed": ("for (size_t k = 0; k < PN; ++k) gs[k] *= a;", "(void)a;"),
+    "bwd_dinit_not_decayed_by_first_token": ("for (size_t k = 0; k < PN; ++k) gs[k] *= a;",
+                                             "if (t > 0) for (size_t k = 0; k < PN; ++k) gs[k] *= a;"),
+    "bwd_output_adjoint_uses_B": ("gs[(size_t)p * N + n] += (double)dyt[p] * (double)Ct[n];",
+                                  "gs[(size_t)p * N + n] += (double)dyt[p] * (double)Bt[n];"),
+    "bwd_dx_without_weight": ("dxt[p] = wi * gB + D * (double)dyt[p];", "dxt[p] = gB + D * (double)dyt[p];"),
+    "bwd_dB_uses_dy": ("dBt[n] += wi * gr[n] * (double)xt[p];", "dBt[n] += wi * gr[n] * (double)dyt[p];"),
+    "bwd_dC_from_previous_state": ("dCt[n] += (double)dyt[p] * hcur[(size_t)p * N + n];",
+                                   "dCt[n] += (double)dyt[p] * hprev[(size_t)p * N + n];"),
+    "bwd_dstep_sign": ("const double dstep = A * a * gh + wd * gx;", "const double dstep = -A * a * gh + wd * gx;"),
+    "bwd_dA_without_weight_term": ("dA += d * a * gh + wA * gx;", "dA += d * a * gh;"),
+    "bwd_softplus_slope": ("slope = 1.0 / (1.0 + exp(-v));", "slope = 1.0 / (1.0 + exp(v));"),
+    "bwd_clamp_slope_inverted": ("if (o->dt_clamp && (v < o->dt_min || v > o->dt_max)) slope = 0.0;",
+                                 "if (o->dt_clamp && (v >= o->dt_min && v <= o->dt_max)) slope = 0.0;"),
+    "bwd_zoh_slope": ("*wd = exp(z);", "*wd = 1.0;"),
+    "bwd_dD_without_x": ("dD += (double)dyt[p] * (double)xt[p];", "dD += (double)dyt[p];"),
     "previous_token_dt_for_decay": ("const double a = exp(d * A);", "const double a = exp((t ? (double)j->dt[(tok - 1) * H + h] : d) * A);"),
 }
 
