@@ -171,6 +171,43 @@ int ssd_forward_timed(const void *x, const void *dt, const float *A, const void 
                       void *const *events);
 
 /*
+ * Backward pass: the gradients of
+ *   loss = sum(dy * y) + sum(dfinal_state * final_state)
+ * for ssd_forward_ex with the same inputs and options. The adjoint of the
+ * state runs backward in time, g_t = dy_t C_t^T + a_{t+1} g_{t+1}, chunked like
+ * the forward: the forward's per-chunk states are recomputed (not stored), a
+ * reverse pass over the chunks carries the adjoint, and one kernel per
+ * (batch, chunk, group, block of heads) forms every gradient of the chunk on
+ * MFMA. The pages motivate the layer by its training speed ("Mamba-2架构深度解析"
+ * section 1) and recompute states in the backward pass instead of storing
+ * them (the "从Transformer到Mamba" tutorial section 4.2; "Mamba 模型" section 3.4).
+ *   dy           [Bt][L][H][P] in dtype (x's layout).
+ *   dfinal_state nullable, float32 [Bt][H][P][N]: the final state's gradient.
+ *   init_state   nullable, as for ssd_forward.
+ * Outputs (overwritten):
+ *   dx [Bt][L][H][P], ddt [Bt][L][H] (with respect to the raw dt, through the
+ *   options), dB, dC [Bt][L][G][N] (summed over the heads of each group): dtype.
+ *   dA [H] float32. dD [H] float32 (nullable; sum of dy.x whether or not D is
+ *   given). dinit_state [Bt][H][P][N] float32 (nullable). ddt_bias [H] float32
+ *   (nullable; the gradient of opts->dt_bias, which is the sum of ddt per head).
+ * The backward picks its own chunk length for the state size (its LDS holds
+ * a chunk's x, dy, B, C and two states): 256 tokens for N <= 32, 128 for N 64
+ * and 128, 64 for N 256 (bf16); float32 supports N <= 64 only (else
+ * SSD_ERR_UNSUPPORTED). The result does not depend on it beyond rounding.
+ * Clamp bounds pass the gradient (d clamp / d dt = 1 for dt_min <= dt <= dt_max).
+ * workspace: at least ssd_backward_workspace_size(...) bytes, 256-byte aligned.
+ * x, dy, B, C, dx, dB, dC and the state arguments need 16-byte alignment.
+ */
+size_t ssd_backward_workspace_size(int batch, int seqlen, int nheads, int headdim, int ngroups,
+                                   int dstate, int dtype);
+int ssd_backward(const void *x, const void *dt, const float *A, const void *B, const void *C,
+                 const float *D, const float *init_state, const void *dy,
+                 const float *dfinal_state, int batch, int seqlen, int nheads, int headdim,
+                 int ngroups, int dstate, int dtype, void *dx, void *ddt, float *dA, void *dB,
+                 void *dC, float *dD, float *dinit_state, float *ddt_bias, void *workspace,
+                 size_t workspace_bytes, const ssd_options *opts, void *stream);
+
+/*
  * Packed variable-length sequences (the dynamic packing of variable-length
  * sequences named on the "Mamba-2架构深度解析" page, section 5). The token
  * axis of a batch-1 input holds nseq sequences one after another: sequence k

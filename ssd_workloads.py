@@ -170,6 +170,17 @@ def generate_dt_raw(w: Workload, seed: int | None = None) -> dict:
             "dt_bias": rng.uniform(-6.5, -2.5, H).astype(np.float32)}
 
 
+def generate_grads(w: Workload, seed: int | None = None) -> dict:
+    """Incoming gradients for the backward: dy ~ N(0, 1) shaped like x in
+    ``w.dtype`` and dfinal ~ N(0, 1) float32 [Bt,H,P,N], from a stream of
+    their own."""
+    base = w.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(base + 0xB4C))
+    Bt, L, H, P, N = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate
+    return {"dy": _store(_normal(rng, (Bt, L, H, P)), w.dtype),
+            "dfinal": _normal(rng, (Bt, H, P, N))}
+
+
 def packed_cu_seqlens(total: int, max_len: int, seed: int) -> np.ndarray:
     """Offsets [nseq + 1] (int32, from 0 to total) of a packed batch of
     sequences with lengths floor(exp(U(0, ln(max_len + 1)))), i.e. spread

@@ -14,7 +14,7 @@ import torch
 from . import _native
 from ._native import SSDError, check, dtype_code, ptr, stream_handle
 
-__all__ = ["forward", "forward_varlen", "step", "options", "workspace_size", "chunk_cumsum", "chunk_state",
+__all__ = ["forward", "backward", "forward_varlen", "step", "options", "workspace_size", "chunk_cumsum", "chunk_state",
            "state_passing", "chunk_cb", "chunk_scan", "SSDError", "stages"]
 
 HEADDIM = 64
@@ -114,6 +114,52 @@ def forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, return_final_sta
         stream_handle(x.device), ev)
     check(rc, "ssd_forward")
     return (y, fs) if return_final_state else y
+
+
+def backward(x, dt, A, B, C, D, dy, init_state=None, dfinal_state=None, dt_bias=None,
+             dt_softplus=False, dt_limit=None, zoh=False, workspace=None, want_dinit=True):
+    """Gradients of sum(dy * y) + sum(dfinal_state * final_state) for
+    ``forward`` with the same inputs and options (ssd_backward).
+
+    Returns a dict: dx, ddt, dB, dC (input dtype, shaped like x, dt, B, C),
+    dA, dD (float32 [H]), dinit (float32 [Bt,H,P,N], or None if not
+    want_dinit) and, when dt_bias is given, ddt_bias (float32 [H]).
+    """
+    _req(x, "x")
+    dt_ = dtype_code(x.dtype)
+    Bt, L, H, P = x.shape
+    for t, n in ((dt, "dt"), (B, "B"), (C, "C"), (dy, "dy")):
+        _req(t, n, x.dtype)
+    _req(A, "A", torch.float32)
+    _opt(D, "D")
+    _opt(init_state, "init_state")
+    _opt(dfinal_state, "dfinal_state")
+    G, N = B.shape[2], B.shape[3]
+    if (tuple(dt.shape) != (Bt, L, H) or tuple(B.shape) != (Bt, L, G, N) or C.shape != B.shape
+            or dy.shape != x.shape):
+        raise ValueError("shape mismatch among x, dt, B, C, dy")
+    if dt_bias is not None and tuple(dt_bias.shape) != (H,):
+        raise ValueError("dt_bias must have shape [H]")
+    dev = x.device
+    out = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt), "dB": torch.empty_like(B),
+           "dC": torch.empty_like(C), "dA": torch.empty(H, dtype=torch.float32, device=dev),
+           "dD": torch.empty(H, dtype=torch.float32, device=dev),
+           "dinit": (torch.empty((Bt, H, P, N), dtype=torch.float32, device=dev)
+                     if want_dinit else None)}
+    if dt_bias is not None:
+        out["ddt_bias"] = torch.empty(H, dtype=torch.float32, device=dev)
+    need = int(_native.lib.ssd_backward_workspace_size(Bt, L, H, P, G, N, dt_))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    opts = options(dt_bias, dt_softplus, dt_limit, zoh)
+    rc = _native.lib.ssd_backward(
+        ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), ptr(init_state), ptr(dy),
+        ptr(dfinal_state), Bt, L, H, P, G, N, dt_, ptr(out["dx"]), ptr(out["ddt"]),
+        ptr(out["dA"]), ptr(out["dB"]), ptr(out["dC"]), ptr(out["dD"]), ptr(out["dinit"]),
+        ptr(out.get("ddt_bias")), ptr(workspace), workspace.numel(), _optref(opts),
+        stream_handle(dev))
+    check(rc, "ssd_backward")
+    return out
 
 
 def forward_varlen(x, dt, A, B, C, D, cu_seqlens, chunk=256, return_seq_states=False,

@@ -1,0 +1,648 @@
+// Backward pass of the chunked SSD layer: the gradients of
+//   loss = sum_t dy_t . y_t + <dfinal, h_L>
+// with respect to x, dt, A, B, C, D, the initial state and the dt bias.
+//
+// The adjoint of the state, g_t = dloss/dh_t, runs backward in time:
+// g_t = dy_t C_t^T + a_{t+1} g_{t+1}. Chunked like the forward ("Mamba 模型",
+// section 4.1: the same semiseparable matrix, transposed), with s the
+// within-chunk prefix sums of step*A, w the input weights, H_c the state
+// entering chunk c (forward recompute) and G_{c+1} the adjoint of the state
+// leaving chunk c (the reverse state passing over dS_c = sum_i e^{s_i} dy_i C_i^T),
+// one chunk's gradients are, for tokens i >= j of the chunk,
+//   dx_j  = w_j sum_i e^{s_i-s_j} (C_i.B_j) dy_i + w_j e^{s_end-s_j} G B_j + D dy_j
+//   dw_j  = sum_i e^{s_i-s_j} (C_i.B_j)(dy_i.x_j) + e^{s_end-s_j} x_j.(G B_j)
+//   dB_j += w_j sum_i e^{s_i-s_j} (dy_i.x_j) C_i + w_j e^{s_end-s_j} G^T x_j
+//   dC_i += sum_j e^{s_i-s_j} w_j (dy_i.x_j) B_j + e^{s_i} H^T dy_i
+//   ds_i  = sum_{j<i} T_ij - sum_{k>i} T_ki + e^{s_i} dy_i.(H C_i)
+//           - w_i e^{s_end-s_i} x_i.(G B_i),   T_ij = e^{s_i-s_j}(C_i.B_j) w_j (dy_i.x_j),
+// and the chunk's last token also takes d/ds_end = sum_j w_j e^{s_end-s_j}
+// x_j.(G B_j) + e^{s_end} <G, H>. The stage-1 backward then turns ds into
+// dstep = A * (suffix sums of ds) and adds the weight's dw.
+//
+// chunk_bwd_kernel: one workgroup per (batch, chunk, B/C group) and block of
+// heads of that group, Q/16 wavefronts; wavefront w owns tokens 16w..16w+15
+// both as the column index j (first pass: the products over the tokens
+// i >= j of every 32-token slice, dx, dB, dw and the column sums of T) and as
+// the row index i (second pass: slices j <= i, dC and the row sums of T), so
+// the causal work is the same for every wavefront. Every 16x16 block of
+// dy.x and C.B is formed on MFMA in the orientation the next product needs
+// (its rows the contraction index, split over the two halves of a slice),
+// decayed and masked in fp32, rounded to the operand type and multiplied.
+// dB and dC accumulate over the block's heads in registers and leave as
+// float32 partial sums per head block (reduced by bwd_reduce_kernel).
+#include "ssd_common.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+namespace {
+
+__device__ __forceinline__ float xor_sum_groups(float v) {  // over the 4 lane groups of 16
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+__device__ __forceinline__ float xor_sum_16(float v) {  // over the 16 lanes of a group
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ void store4_global(T *p, const floatx4 &v);
+template <>
+__device__ __forceinline__ void store4_global<bf16_t>(bf16_t *p, const floatx4 &v) {
+    *reinterpret_cast<bf16x4 *>(p) = bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]),
+                                            static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
+}
+template <>
+__device__ __forceinline__ void store4_global<float>(float *p, const floatx4 &v) {
+    *reinterpret_cast<floatx4 *>(p) = v;
+}
+
+}  // namespace
+
+template <typename T, int N, int Q>
+struct BwdLds {
+    using E = typename LdsT<T>::type;
+    static constexpr int P = 64;
+    static constexpr int LDX = colfrag_stride(P, sizeof(E));
+    static constexpr int LDB = colfrag_stride(N, sizeof(E));
+    static constexpr size_t kBytes =
+        sizeof(E) * ((size_t)2 * Q * LDX + (size_t)2 * Q * LDB + (size_t)2 * P * LDB) +
+        2 * Q * sizeof(float) + 16;
+};
+
+template <typename T, int N, int Q>
+__global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
+    const T *__restrict__ x, const T *__restrict__ dy, const float *__restrict__ dA_cumsum,
+    const float *__restrict__ delta, const T *__restrict__ B, const T *__restrict__ C,
+    const float *__restrict__ D, const typename LdsT<T>::type *__restrict__ chunk_init,
+    const typename LdsT<T>::type *__restrict__ grad_next, int batch, int L, int H, int G, int nC,
+    int nblk,
+    T *__restrict__ dx, float *__restrict__ ds_out, float *__restrict__ dw_out,
+    float *__restrict__ dB_part, float *__restrict__ dC_part, float *__restrict__ dD_part) {
+    using E = typename LdsT<T>::type;
+    using S = BwdLds<T, N, Q>;
+    constexpr int P = 64, NTHR = Q * 4, NT = N / 16, NK = (N + 31) / 32;
+    constexpr int LDX = S::LDX, LDB = S::LDB;
+    constexpr int XPR = P * (int)sizeof(T) / 16;  // 16-byte pieces per x / dy row
+    constexpr int BPR = N * (int)sizeof(T) / 16;  // ... per B / C / H / G row
+    constexpr int EPP = 16 / (int)sizeof(T);      // elements per piece
+    __shared__ __attribute__((aligned(32))) E xs[Q * LDX];
+    __shared__ __attribute__((aligned(32))) E dys[Q * LDX];
+    __shared__ __attribute__((aligned(32))) E bs[Q * LDB];
+    __shared__ __attribute__((aligned(32))) E cs[Q * LDB];
+    __shared__ __attribute__((aligned(32))) E hs[P * LDB];
+    __shared__ __attribute__((aligned(32))) E gs[P * LDB];
+    __shared__ __attribute__((aligned(16))) float slt[Q];  // s * log2(e)
+    __shared__ __attribute__((aligned(16))) float wt[Q];   // input weights (0 past the end)
+    __shared__ float red[4];
+
+    const int kb = blockIdx.x % nblk, u = blockIdx.x / nblk;
+    const int hpg = H / G;
+    const int c = u % nC, g = (u / nC) % G, b = u / (nC * G);
+    const int nh = (hpg - kb + nblk - 1) / nblk;
+    const int t0 = c * Q, len = min(Q, L - t0);
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = l >> 4, c16 = l & 15;
+    const int tok = 16 * w + c16;  // this lane's token: column j of pass 1, row i of pass 2
+    const size_t xrow = (size_t)H * P, brow = (size_t)G * N;
+
+    // ---- B and C rows of the chunk (zero past the end), for every head
+    for (int idx = tid; idx < Q * BPR; idx += NTHR) {
+        const int j = idx / BPR, q = idx % BPR;
+        uint4 vb = make_uint4(0, 0, 0, 0), vc = make_uint4(0, 0, 0, 0);
+        if (j < len) {
+            const size_t o = ((size_t)b * L + t0 + j) * brow + (size_t)g * N + q * EPP;
+            vb = *reinterpret_cast<const uint4 *>(B + o);
+            vc = *reinterpret_cast<const uint4 *>(C + o);
+        }
+        *reinterpret_cast<uint4 *>(bs + j * LDB + q * EPP) = vb;
+        *reinterpret_cast<uint4 *>(cs + j * LDB + q * EPP) = vc;
+    }
+
+    floatx4 dBT[NT], dCT[NT];  // lane (g4, c16): rows n = 16nt + 4g4 + e, column token tok
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) dBT[nt] = dCT[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int k = 0; k < nh; ++k) {
+        const int h = g * hpg + kb + k * nblk;
+        __syncthreads();  // the previous head is done with LDS
+        if (tid < 4) red[tid] = 0.0f;
+        const T *xh = x + ((size_t)b * L + t0) * xrow + (size_t)h * P;
+        const T *dyh = dy + ((size_t)b * L + t0) * xrow + (size_t)h * P;
+        for (int idx = tid; idx < Q * XPR; idx += NTHR) {
+            const int j = idx / XPR, q = idx % XPR;
+            uint4 vx = make_uint4(0, 0, 0, 0), vd = make_uint4(0, 0, 0, 0);
+            if (j < len) {
+                vx = *reinterpret_cast<const uint4 *>(xh + (size_t)j * xrow + q * EPP);
+                vd = *reinterpret_cast<const uint4 *>(dyh + (size_t)j * xrow + q * EPP);
+            }
+            *reinterpret_cast<uint4 *>(xs + j * LDX + q * EPP) = vx;
+            *reinterpret_cast<uint4 *>(dys + j * LDX + q * EPP) = vd;
+        }
+        const size_t st = (((size_t)b * nC + c) * H + h) * (size_t)P * N;
+        for (int idx = tid; idx < P * BPR; idx += NTHR) {
+            const int p = idx / BPR, q = idx % BPR;
+            *reinterpret_cast<uint4 *>(hs + p * LDB + q * EPP) =
+                *reinterpret_cast<const uint4 *>(chunk_init + st + (size_t)p * N + q * EPP);
+            *reinterpret_cast<uint4 *>(gs + p * LDB + q * EPP) =
+                *reinterpret_cast<const uint4 *>(grad_next + st + (size_t)p * N + q * EPP);
+        }
+        const size_t srow = ((size_t)b * H + h) * (size_t)nC * Q + (size_t)c * Q;
+        for (int i = tid; i < Q; i += NTHR) {
+            slt[i] = dA_cumsum[srow + i] * kLog2e;
+            wt[i] = delta[srow + i];
+        }
+        __syncthreads();
+
+        const float sl_t = slt[tok], w_t = wt[tok];
+        const float sl_end = slt[len - 1];
+        const float f_t = __builtin_amdgcn_exp2f(sl_end - sl_t);  // exp(s_end - s_tok)
+        const float e_t = __builtin_amdgcn_exp2f(sl_t);           // exp(s_tok)
+        const float Dh = D ? D[h] : 0.0f;
+
+        // ================= pass 1: tok as column j, slices of rows i >= j
+        floatx4 dxT[4];  // lane (g4, c16): dx[tok][16pt + 4g4 + e]
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) dxT[pt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        float cin = 0.0f, cex = 0.0f;  // column sums of e^{s_i-s_j} CB DX (with / without i = j)
+        for (int sl = w / 2; sl < Q / 32; ++sl) {
+            floatx4 dxo[2], cbo[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int ir = 32 * sl + 16 * half + c16;  // A-operand row (token i)
+                dxo[half] = cbo[half] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kk = 0; kk < P / 32; ++kk) {
+                    Frag<T> fa, fb;
+                    lds_frag8(fa, dys + ir * LDX + kk * 32 + 8 * g4);
+                    lds_frag8(fb, xs + tok * LDX + kk * 32 + 8 * g4);
+                    mma(dxo[half], fa, fb);
+                }
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    const int n0 = kk * 32 + 8 * g4;
+                    Frag<T> fa, fb;
+                    if (n0 < N) {
+                        lds_frag8(fa, cs + ir * LDB + n0);
+                        lds_frag8(fb, bs + tok * LDB + n0);
+                    } else {
+                        fa.zero();
+                        fb.zero();
+                    }
+                    mma(cbo[half], fa, fb);
+                }
+            }
+            // element (half, e): token i = 32 sl + 16 half + 4 g4 + e, column j = tok
+            Frag<T> mf, ef;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int i0 = 32 * sl + 16 * half + 4 * g4;
+                const floatx4 si4 = *reinterpret_cast<const floatx4 *>(slt + i0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = i0 + e;
+                    const float lij = i >= tok ? __builtin_amdgcn_exp2f(si4[e] - sl_t) : 0.0f;
+                    const float lcb = lij * cbo[half][e];
+                    const float t = lcb * dxo[half][e];
+                    cin += t;
+                    cex += i != tok ? t : 0.0f;
+                    mf.set(4 * half + e, lcb * w_t);
+                    ef.set(4 * half + e, lij * dxo[half][e] * w_t);
+                }
+            }
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                Frag<T> fa;  // dy^T: rows p = 16pt + c16, contraction over the slice's tokens
+                lds_colfrag(fa, dys, LDX, 32 * sl + 4 * g4, 32 * sl + 16 + 4 * g4, pt * 16);
+                mma(dxT[pt], fa, mf);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                Frag<T> fa;  // C^T: rows n = 16nt + c16
+                lds_colfrag(fa, cs, LDB, 32 * sl + 4 * g4, 32 * sl + 16 + 4 * g4, nt * 16);
+                mma(dBT[nt], fa, ef);
+            }
+        }
+        // ---- the state leaving the chunk: U = G B_j^T, V = G^T x_j
+        float xu = 0.0f;  // x_j . (G B_j), partial over this lane's p
+        const float wf = w_t * f_t;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+            floatx4 uo = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                const int n0 = kk * 32 + 8 * g4;
+                Frag<T> fa, fb;
+                if (n0 < N) {
+                    lds_frag8(fa, gs + (pt * 16 + c16) * LDB + n0);
+                    lds_frag8(fb, bs + tok * LDB + n0);
+                } else {
+                    fa.zero();
+                    fb.zero();
+                }
+                mma(uo, fa, fb);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int p = pt * 16 + 4 * g4 + e;
+                xu += static_cast<float>(xs[tok * LDX + p]) * uo[e];
+                dxT[pt][e] += wf * uo[e] + Dh * static_cast<float>(dys[tok * LDX + p]);
+            }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            floatx4 vo = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < P / 32; ++kk) {
+                Frag<T> fa, fb;  // contraction over p
+                lds_colfrag(fa, gs, LDB, kk * 32 + 4 * g4, kk * 32 + 16 + 4 * g4, nt * 16);
+                lds_frag4x2(fb, xs + tok * LDX + kk * 32 + 4 * g4, xs + tok * LDX + kk * 32 + 16 + 4 * g4);
+                mma(vo, fa, fb);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dBT[nt][e] += wf * vo[e];
+        }
+        if (tok < len) {
+            T *dxr = dx + ((size_t)b * L + t0 + tok) * xrow + (size_t)h * P;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) store4_global<T>(dxr + pt * 16 + 4 * g4, dxT[pt]);
+        }
+        cin = xor_sum_groups(cin);
+        cex = xor_sum_groups(cex);
+        xu = xor_sum_groups(xu);
+        const float dw_t = cin + f_t * xu;
+        float ds_t = -w_t * cex - wf * xu;
+        {  // d/ds_end: sum_j w_j f_j x_j.(G B_j), one wavefront partial
+            const float part = xor_sum_16(g4 == 0 ? wf * xu : 0.0f);
+            if (l == 0) atomicAdd(&red[0], part);
+        }
+
+        // ================= pass 2: tok as row i, slices of columns j <= i
+        float rs = 0.0f;  // row sum of T over j < i
+        for (int sl = 0; sl <= w / 2; ++sl) {
+            floatx4 dxo[2], cbo[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int jr = 32 * sl + 16 * half + c16;  // A-operand row (token j)
+                dxo[half] = cbo[half] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kk = 0; kk < P / 32; ++kk) {
+                    Frag<T> fa, fb;
+                    lds_frag8(fa, xs + jr * LDX + kk * 32 + 8 * g4);
+                    lds_frag8(fb, dys + tok * LDX + kk * 32 + 8 * g4);
+                    mma(dxo[half], fa, fb);
+                }
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    const int n0 = kk * 32 + 8 * g4;
+                    Frag<T> fa, fb;
+                    if (n0 < N) {
+                        lds_frag8(fa, bs + jr * LDB + n0);
+                        lds_frag8(fb, cs + tok * LDB + n0);
+                    } else {
+                        fa.zero();
+                        fb.zero();
+                    }
+                    mma(cbo[half], fa, fb);
+                }
+            }
+            Frag<T> wfr;  // e^{s_i-s_j} w_j (dy_i.x_j), rows j of the slice
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int j0 = 32 * sl + 16 * half + 4 * g4;
+                const floatx4 sj4 = *reinterpret_cast<const floatx4 *>(slt + j0);
+                const floatx4 wj4 = *reinterpret_cast<const floatx4 *>(wt + j0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = j0 + e;
+                    const float lw = j <= tok ? __builtin_amdgcn_exp2f(sl_t - sj4[e]) * wj4[e] : 0.0f;
+                    const float v = lw * dxo[half][e];
+                    wfr.set(4 * half + e, v);
+                    rs += j < tok ? v * cbo[half][e] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                Frag<T> fa;  // B^T: rows n = 16nt + c16, contraction over the slice's tokens
+                lds_colfrag(fa, bs, LDB, 32 * sl + 4 * g4, 32 * sl + 16 + 4 * g4, nt * 16);
+                mma(dCT[nt], fa, wfr);
+            }
+        }
+        // ---- the state entering the chunk: H^T dy_i and H C_i
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            floatx4 vo = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < P / 32; ++kk) {
+                Frag<T> fa, fb;
+                lds_colfrag(fa, hs, LDB, kk * 32 + 4 * g4, kk * 32 + 16 + 4 * g4, nt * 16);
+                lds_frag4x2(fb, dys + tok * LDX + kk * 32 + 4 * g4, dys + tok * LDX + kk * 32 + 16 + 4 * g4);
+                mma(vo, fa, fb);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dCT[nt][e] += e_t * vo[e];
+        }
+        float dych = 0.0f, dd = 0.0f;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+            floatx4 co = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                const int n0 = kk * 32 + 8 * g4;
+                Frag<T> fa, fb;
+                if (n0 < N) {
+                    lds_frag8(fa, hs + (pt * 16 + c16) * LDB + n0);
+                    lds_frag8(fb, cs + tok * LDB + n0);
+                } else {
+                    fa.zero();
+                    fb.zero();
+                }
+                mma(co, fa, fb);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int p = pt * 16 + 4 * g4 + e;
+                const float dyv = static_cast<float>(dys[tok * LDX + p]);
+                dych += dyv * co[e];
+                dd += dyv * static_cast<float>(xs[tok * LDX + p]);
+            }
+        }
+        rs = xor_sum_groups(rs);
+        dych = xor_sum_groups(dych);
+        dd = xor_sum_groups(dd);
+        ds_t += rs + e_t * dych;
+        {
+            const float part = xor_sum_16(g4 == 0 ? dd : 0.0f);
+            if (l == 0) atomicAdd(&red[2], part);
+        }
+        {  // <G, H>, spread over the workgroup
+            float gh = 0.0f;
+            for (int idx = tid; idx < P * N; idx += NTHR) {
+                const int p = idx / N, n = idx % N;
+                gh += static_cast<float>(gs[p * LDB + n]) * static_cast<float>(hs[p * LDB + n]);
+            }
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) gh += __shfl_xor(gh, o);
+            if (l == 0) atomicAdd(&red[1], gh);
+        }
+        __syncthreads();  // red[] complete
+        if (tok == len - 1) ds_t += red[0] + __builtin_amdgcn_exp2f(sl_end) * red[1];
+        if (g4 == 0) {
+            ds_out[srow + tok] = ds_t;
+            dw_out[srow + tok] = dw_t;
+        }
+        if (tid == 0) dD_part[((size_t)b * nC + c) * H + h] = red[2];
+    }
+
+    // ---- this head block's share of dB and dC: dB_part[kb][b][t][g][n]
+    if (tok < len) {
+        const size_t o = ((size_t)kb * batch + b) * L * brow + (size_t)(t0 + tok) * brow + (size_t)g * N;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            *reinterpret_cast<floatx4 *>(dB_part + o + nt * 16 + 4 * g4) = dBT[nt];
+            *reinterpret_cast<floatx4 *>(dC_part + o + nt * 16 + 4 * g4) = dCT[nt];
+        }
+    }
+}
+
+// dB, dC (input dtype) = the sum of the head blocks' float32 partial sums.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *__restrict__ part, int nblk,
+                                                         size_t n4, T *__restrict__ out) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    floatx4 acc = reinterpret_cast<const floatx4 *>(part)[i];
+    for (int k = 1; k < nblk; ++k) {
+        const floatx4 v = reinterpret_cast<const floatx4 *>(part)[(size_t)k * n4 + i];
+        acc += v;
+    }
+    store4_global<T>(out + 4 * i, acc);
+}
+
+// Stage-1 backward: per (chunk, batch, block of 64 heads), thread (run k,
+// head hh) owns Q/16 consecutive tokens (the layout of chunk_cumsum). With da
+// the suffix sums of ds within the chunk (s_i sums step_k A over k <= i):
+//   dstep = A da + dw dw/dstep,   dA += step da + dw dw/dA,
+//   d(raw dt) = dstep d(step)/d(raw)  (softplus: sigmoid; clamp: 0 outside),
+// written as ddt (input dtype); the per-(batch, chunk, head) sums of the dA
+// and dt-bias terms go to dA_part, dbias_part.
+template <typename T, int Q>
+__global__ __launch_bounds__(1024) void bwd_dt_kernel(
+    const T *__restrict__ dt, const float *__restrict__ A, const float *__restrict__ ds,
+    const float *__restrict__ dw, int L, int H, int nC, DtOpts o, T *__restrict__ ddt,
+    float *__restrict__ dA_part, float *__restrict__ dbias_part) {
+    constexpr int R = Q / 16, HB = 64, RUNS = 16;
+    __shared__ float tot[RUNS][HB];
+    __shared__ float pa[RUNS][HB], pb[RUNS][HB];
+    const int c = blockIdx.x, b = blockIdx.y, h0 = blockIdx.z * HB;
+    const int tid = threadIdx.x, hh = tid & 63, k = tid >> 6, h = h0 + hh;
+    const int hc = min(h, H - 1);
+    const int t0 = c * Q + k * R;
+    const size_t row = ((size_t)b * H + hc) * (size_t)nC * Q + t0;
+    float dsv[R], dwv[R], raw[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        dsv[r] = h < H ? ds[row + r] : 0.0f;
+        dwv[r] = h < H ? dw[row + r] : 0.0f;
+        raw[r] = to_f32(dt[((size_t)b * L + min(t0 + r, L - 1)) * H + hc]);
+    }
+    // suffix sums within the run, then across runs
+#pragma unroll
+    for (int r = R - 2; r >= 0; --r) dsv[r] += dsv[r + 1];
+    tot[k][hh] = dsv[0];
+    __syncthreads();
+    float after = 0.0f;  // sum of the later runs of this chunk
+    for (int kk = k + 1; kk < RUNS; ++kk) after += tot[kk][hh];
+    const float a = h < H ? A[hc] : 0.0f;
+    const float bias = o.bias ? o.bias[hc] : 0.0f;
+    float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int t = t0 + r;
+        const float da = dsv[r] + after;
+        float v = raw[r] + bias, slope = 1.0f;
+        if (o.softplus) {
+            slope = 1.0f / (1.0f + expf(-v));
+            v = fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v)));
+        }
+        if (o.clamp) {
+            if (v < o.lo || v > o.hi) slope = 0.0f;
+            v = fminf(fmaxf(v, o.lo), o.hi);
+        }
+        float wd = 1.0f, wa = 0.0f;  // dw/dstep, dw/dA
+        if (o.zoh) {
+            const float z = v * a;
+            wd = expf(z);
+            if (fabsf(z) < 0.5f) {  // step^2 sum_{m>=2} (m-1)/m! z^(m-2)
+                wa = v * v * (0.5f + z * (1.0f / 3 + z * (1.0f / 8 + z * (1.0f / 30 + z * (1.0f / 144 +
+                     z * (1.0f / 840 + z * (1.0f / 5760 + z * (1.0f / 45360))))))));
+            } else {
+                wa = (z * expf(z) - expm1f(z)) / (a * a);
+            }
+        }
+        const float dstep = a * da + dwv[r] * wd;
+        const float draw = dstep * slope;
+        if (h < H && t < L) {
+            ddt[((size_t)b * L + t) * H + h] = from_f32<T>(draw);
+            sa += v * da + dwv[r] * wa;
+            sb += draw;
+        }
+    }
+    pa[k][hh] = sa;
+    pb[k][hh] = sb;
+    __syncthreads();
+    if (k == 0 && h < H) {
+        float ta = 0.0f, tb = 0.0f;
+        for (int kk = 0; kk < RUNS; ++kk) {
+            ta += pa[kk][hh];
+            tb += pb[kk][hh];
+        }
+        dA_part[((size_t)b * nC + c) * H + h] = ta;
+        dbias_part[((size_t)b * nC + c) * H + h] = tb;
+    }
+}
+
+// Per-head totals of the (batch, chunk) partial sums: one workgroup per head.
+__global__ __launch_bounds__(256) void bwd_head_sum_kernel(const float *__restrict__ part, int nbc,
+                                                           int H, float *__restrict__ out) {
+    __shared__ float red[4];
+    const int h = blockIdx.x;
+    float v = 0.0f;
+    for (int i = threadIdx.x; i < nbc; i += 256) v += part[(size_t)i * H + h];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+    if (lane_id() == 0) red[wave_id()] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) out[h] = red[0] + red[1] + red[2] + red[3];
+}
+
+// ---- launchers
+
+// Chunk length of the backward for a state size (its LDS holds a chunk's x,
+// dy, B, C and two P x N states): the largest of 256, 128, 64 that fits.
+int bwd_chunk(int dstate, bool bf16) {
+    for (int q = 256; q >= 64; q /= 2) {
+        size_t bytes = 0;
+#define SSD_BWD_BYTES(TT, NN, QQ)                        \
+    if (dstate == NN && q == QQ) bytes = BwdLds<TT, NN, QQ>::kBytes;
+#define SSD_BWD_BYTES_Q(TT, NN) SSD_BWD_BYTES(TT, NN, 64) SSD_BWD_BYTES(TT, NN, 128) SSD_BWD_BYTES(TT, NN, 256)
+        if (bf16) {
+            SSD_BWD_BYTES_Q(bf16_t, 16) SSD_BWD_BYTES_Q(bf16_t, 32) SSD_BWD_BYTES_Q(bf16_t, 64)
+            SSD_BWD_BYTES_Q(bf16_t, 128) SSD_BWD_BYTES_Q(bf16_t, 256)
+        } else {
+            SSD_BWD_BYTES_Q(float, 16) SSD_BWD_BYTES_Q(float, 32) SSD_BWD_BYTES_Q(float, 64)
+            SSD_BWD_BYTES_Q(float, 128) SSD_BWD_BYTES_Q(float, 256)
+        }
+#undef SSD_BWD_BYTES_Q
+#undef SSD_BWD_BYTES
+        if (bytes && bytes <= 160 * 1024) return q;
+    }
+    return 0;
+}
+
+int bwd_head_blocks(int batch, int seqlen, int nheads, int ngroups, int chunk) {
+    const int nC = (seqlen + chunk - 1) / chunk;
+    const int nU = batch * nC * ngroups;
+    int nblk = (512 + nU - 1) / nU;
+    const int hpg = nheads / ngroups;
+    return nblk < 1 ? 1 : (nblk > hpg ? hpg : nblk);
+}
+
+template <typename T, int N, int Q>
+static void launch_bwd_q(const BwdArgs &a, hipStream_t s) {
+    using E = typename LdsT<T>::type;
+    const int nC = (a.seqlen + Q - 1) / Q;
+    const int nU = a.batch * nC * a.ngroups;
+    chunk_bwd_kernel<T, N, Q><<<nU * a.nblk, Q * 4, 0, s>>>(
+        static_cast<const T *>(a.x), static_cast<const T *>(a.dy), a.dA_cumsum, a.delta,
+        static_cast<const T *>(a.B), static_cast<const T *>(a.C), a.D,
+        static_cast<const E *>(a.chunk_init), static_cast<const E *>(a.grad_next), a.batch,
+        a.seqlen, a.nheads, a.ngroups, nC, a.nblk, static_cast<T *>(a.dx), a.ds, a.dw, a.dB_part,
+        a.dC_part, a.dD_part);
+}
+
+template <typename T, int N>
+static bool launch_bwd_n(int Q, const BwdArgs &a, hipStream_t s) {
+    switch (Q) {
+        case 64: launch_bwd_q<T, N, 64>(a, s); return true;
+        case 128:
+            if constexpr (BwdLds<T, N, 128>::kBytes <= 160 * 1024) {
+                launch_bwd_q<T, N, 128>(a, s);
+                return true;
+            }
+            return false;
+        case 256:
+            if constexpr (BwdLds<T, N, 256>::kBytes <= 160 * 1024) {
+                launch_bwd_q<T, N, 256>(a, s);
+                return true;
+            }
+            return false;
+        default: return false;
+    }
+}
+
+template <typename T>
+static bool launch_bwd_t(const BwdArgs &a, hipStream_t s) {
+    switch (a.dstate) {
+        case 16: return launch_bwd_n<T, 16>(a.chunk, a, s);
+        case 32: return launch_bwd_n<T, 32>(a.chunk, a, s);
+        case 64: return launch_bwd_n<T, 64>(a.chunk, a, s);
+        case 128:
+            if constexpr (BwdLds<T, 128, 64>::kBytes <= 160 * 1024) return launch_bwd_n<T, 128>(a.chunk, a, s);
+            return false;
+        case 256:
+            if constexpr (BwdLds<T, 256, 64>::kBytes <= 160 * 1024) return launch_bwd_n<T, 256>(a.chunk, a, s);
+            return false;
+        default: return false;
+    }
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t stream) {
+    const bool ok = a.bf16 ? launch_bwd_t<bf16_t>(a, stream) : launch_bwd_t<float>(a, stream);
+    return ok ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_reduce(const float *part, int nblk, size_t count, bool bf16, void *out,
+                             hipStream_t stream) {
+    const size_t n4 = count / 4;
+    const unsigned blocks = (unsigned)((n4 + 255) / 256);
+    if (bf16) bwd_reduce_kernel<bf16_t><<<blocks, 256, 0, stream>>>(part, nblk, n4, static_cast<bf16_t *>(out));
+    else bwd_reduce_kernel<float><<<blocks, 256, 0, stream>>>(part, nblk, n4, static_cast<float *>(out));
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dt(const void *dt, const float *A, const float *ds, const float *dw,
+                         int batch, int seqlen, int nheads, int chunk, bool bf16,
+                         const DtOpts &opts, void *ddt, float *dA_part, float *dbias_part,
+                         hipStream_t stream) {
+    const int nC = (seqlen + chunk - 1) / chunk;
+    const dim3 grid(nC, batch, (nheads + 63) / 64);
+#define SSD_BWD_DT(TT, QQ)                                                                    \
+    bwd_dt_kernel<TT, QQ><<<grid, 1024, 0, stream>>>(static_cast<const TT *>(dt), A, ds, dw,  \
+                                                     seqlen, nheads, nC, opts,                \
+                                                     static_cast<TT *>(ddt), dA_part, dbias_part)
+    if (bf16) {
+        if (chunk == 64) SSD_BWD_DT(bf16_t, 64);
+        else if (chunk == 128) SSD_BWD_DT(bf16_t, 128);
+        else if (chunk == 256) SSD_BWD_DT(bf16_t, 256);
+        else return hipErrorInvalidValue;
+    } else {
+        if (chunk == 64) SSD_BWD_DT(float, 64);
+        else if (chunk == 128) SSD_BWD_DT(float, 128);
+        else if (chunk == 256) SSD_BWD_DT(float, 256);
+        else return hipErrorInvalidValue;
+    }
+#undef SSD_BWD_DT
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_head_sum(const float *part, int nbc, int nheads, float *out,
+                               hipStream_t stream) {
+    bwd_head_sum_kernel<<<nheads, 256, 0, stream>>>(part, nbc, nheads, out);
+    return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -25,8 +25,8 @@ namespace ssd {
 template <typename T, int N, int Q>
 __global__ __launch_bounds__(512) void chunk_state_kernel(
     const T *__restrict__ x, const T *__restrict__ B, const float *__restrict__ delta,
-    const float *__restrict__ dA_cumsum, const int *__restrict__ seg, int L, int H, int G, int nC,
-    float *__restrict__ states) {
+    const float *__restrict__ dA_cumsum, const int *__restrict__ seg, int dout, int L, int H,
+    int G, int nC, float *__restrict__ states) {
     using E = typename LdsT<T>::type;
     constexpr int P = 64, NTHR = 512;
     constexpr int LDX = colfrag_stride(P, sizeof(E));
@@ -72,7 +72,9 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(
     const int j0 = seg ? seg[(size_t)(b * nC + c) * Q + len - 1] : -1;
     for (int j = tid; j < Q; j += NTHR) {
         float wv = 0.0f;
-        if (j < len && j >= j0) wv = __builtin_amdgcn_exp2f((s_end - s[j]) * kLog2e) * dl[j];
+        if (j < len && j >= j0)
+            wv = dout ? __builtin_amdgcn_exp2f(s[j] * kLog2e)
+                      : __builtin_amdgcn_exp2f((s_end - s[j]) * kLog2e) * dl[j];
         wj[j] = wv;
     }
 
@@ -175,7 +177,7 @@ template <int N, int Q, bool FIN>
 __global__ __launch_bounds__(512) void chunk_state_bf16_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ B, const float *__restrict__ delta,
     const float *__restrict__ dA_cumsum, const int *__restrict__ seg, const int *__restrict__ cu,
-    const __bf16 *__restrict__ chunk_init, int L, int H, int G, int nC,
+    const __bf16 *__restrict__ chunk_init, int dout, int L, int H, int G, int nC,
     float *__restrict__ states) {
     constexpr int P = 64, NW = 8;
     constexpr int TP = N >= 128 ? 32 : 64;  // tokens per phase
@@ -241,7 +243,9 @@ __global__ __launch_bounds__(512) void chunk_state_bf16_kernel(
     const int j0 = seg ? seg[(size_t)(b * nC + c) * Q + len - 1] : -1;
     for (int j = tid; j < Q; j += 512) {
         float wv = 0.0f;
-        if (j < len && j >= j0) wv = __builtin_amdgcn_exp2f((s_end - s[j]) * kLog2e) * dl[j];
+        if (j < len && j >= j0)
+            wv = dout ? __builtin_amdgcn_exp2f(s[j] * kLog2e)
+                      : __builtin_amdgcn_exp2f((s_end - s[j]) * kLog2e) * dl[j];
         wj[j] = wv;
     }
 
@@ -512,43 +516,43 @@ hipError_t launch_chunk_state_passing(const void *x, const void *B, const float 
 
 template <typename T, int N, int Q>
 static void launch_cs(const void *x, const void *B, const float *dl, const float *dA,
-                      const int *seg, int batch, int L, int H, int G, float *states,
+                      const int *seg, int dout, int batch, int L, int H, int G, float *states,
                       hipStream_t stream) {
     const int nC = (L + Q - 1) / Q;
     const dim3 grid(nC, H, batch);
     if constexpr (sizeof(T) == 2) {
         chunk_state_bf16_kernel<N, Q, false><<<grid, 512, 0, stream>>>(
             static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(B),
-            dl, dA, seg, nullptr, nullptr, L, H, G, nC, states);
+            dl, dA, seg, nullptr, nullptr, dout, L, H, G, nC, states);
     } else {
         chunk_state_kernel<T, N, Q><<<grid, 512, 0, stream>>>(
-            static_cast<const T *>(x), static_cast<const T *>(B), dl, dA, seg, L,
+            static_cast<const T *>(x), static_cast<const T *>(B), dl, dA, seg, dout, L,
             H, G, nC, states);
     }
 }
 
 template <typename T, int N>
 static bool cs_q(int Q, const void *x, const void *B, const float *dl, const float *dA,
-                 const int *seg, int batch, int L, int H, int G, float *states, hipStream_t s) {
+                 const int *seg, int dout, int batch, int L, int H, int G, float *states, hipStream_t s) {
     switch (Q) {
-        case 64: launch_cs<T, N, 64>(x, B, dl, dA, seg, batch, L, H, G, states, s); return true;
-        case 128: launch_cs<T, N, 128>(x, B, dl, dA, seg, batch, L, H, G, states, s); return true;
-        case 256: launch_cs<T, N, 256>(x, B, dl, dA, seg, batch, L, H, G, states, s); return true;
+        case 64: launch_cs<T, N, 64>(x, B, dl, dA, seg, dout, batch, L, H, G, states, s); return true;
+        case 128: launch_cs<T, N, 128>(x, B, dl, dA, seg, dout, batch, L, H, G, states, s); return true;
+        case 256: launch_cs<T, N, 256>(x, B, dl, dA, seg, dout, batch, L, H, G, states, s); return true;
         default: return false;
     }
 }
 
 template <typename T>
 static hipError_t dispatch_cs(const void *x, const void *B, const float *dl, const float *dA,
-                              const int *seg, int batch, int L, int H, int G, int N, int Q,
+                              const int *seg, int dout, int batch, int L, int H, int G, int N, int Q,
                               float *states, hipStream_t s) {
     bool ok = false;
     switch (N) {
-        case 16: ok = cs_q<T, 16>(Q, x, B, dl, dA, seg, batch, L, H, G, states, s); break;
-        case 32: ok = cs_q<T, 32>(Q, x, B, dl, dA, seg, batch, L, H, G, states, s); break;
-        case 64: ok = cs_q<T, 64>(Q, x, B, dl, dA, seg, batch, L, H, G, states, s); break;
-        case 128: ok = cs_q<T, 128>(Q, x, B, dl, dA, seg, batch, L, H, G, states, s); break;
-        case 256: ok = cs_q<T, 256>(Q, x, B, dl, dA, seg, batch, L, H, G, states, s); break;
+        case 16: ok = cs_q<T, 16>(Q, x, B, dl, dA, seg, dout, batch, L, H, G, states, s); break;
+        case 32: ok = cs_q<T, 32>(Q, x, B, dl, dA, seg, dout, batch, L, H, G, states, s); break;
+        case 64: ok = cs_q<T, 64>(Q, x, B, dl, dA, seg, dout, batch, L, H, G, states, s); break;
+        case 128: ok = cs_q<T, 128>(Q, x, B, dl, dA, seg, dout, batch, L, H, G, states, s); break;
+        case 256: ok = cs_q<T, 256>(Q, x, B, dl, dA, seg, dout, batch, L, H, G, states, s); break;
         default: break;
     }
     if (!ok) return hipErrorInvalidValue;
@@ -558,12 +562,12 @@ static hipError_t dispatch_cs(const void *x, const void *B, const float *dl, con
 hipError_t launch_chunk_state(const void *x, const void *B, const float *delta,
                               const float *dA_cumsum, const int *seg, int batch, int seqlen,
                               int nheads, int ngroups, int dstate, int chunk, bool bf16,
-                              float *states, hipStream_t stream) {
+                              float *states, hipStream_t stream, bool dout) {
     if (bf16)
-        return dispatch_cs<bf16_t>(x, B, delta, dA_cumsum, seg, batch, seqlen, nheads, ngroups, dstate,
-                                   chunk, states, stream);
-    return dispatch_cs<float>(x, B, delta, dA_cumsum, seg, batch, seqlen, nheads, ngroups, dstate, chunk,
-                              states, stream);
+        return dispatch_cs<bf16_t>(x, B, delta, dA_cumsum, seg, dout, batch, seqlen, nheads,
+                                   ngroups, dstate, chunk, states, stream);
+    return dispatch_cs<float>(x, B, delta, dA_cumsum, seg, dout, batch, seqlen, nheads, ngroups,
+                              dstate, chunk, states, stream);
 }
 
 }  // namespace ssd
@@ -583,7 +587,7 @@ hipError_t launch_varlen_final_states_bf16(const void *x, const void *B, const f
     const __bf16 *hc = static_cast<const __bf16 *>(chunk_init);
 #define SSD_FIN(NN, QQ)                                                                         \
     chunk_state_bf16_kernel<NN, QQ, true><<<grid, 512, 0, stream>>>(                            \
-        xx, bb, delta, dA_cumsum, seg, cu_seqlens, hc, seqlen, nheads, ngroups, nC, seq_states)
+        xx, bb, delta, dA_cumsum, seg, cu_seqlens, hc, 0, seqlen, nheads, ngroups, nC, seq_states)
 #define SSD_FIN_Q(NN)                                                                           \
     switch (chunk) {                                                                            \
         case 64: SSD_FIN(NN, 64); break;                                                        \

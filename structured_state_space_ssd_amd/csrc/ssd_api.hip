@@ -52,6 +52,46 @@ Workspace varlen_layout(int seqlen, int nheads, int headdim, int ngroups, int ds
     return w;
 }
 
+// The backward's workspace (its own chunk length, see ssd::bwd_chunk).
+struct BwdWorkspace {
+    size_t s_off, delta_off, states_off, init_off, gnext_off, ds_off, dw_off, dB_off, dC_off,
+        dA_off, dbias_off, dD_off, total;
+    int chunk, nblk;
+};
+
+BwdWorkspace bwd_layout(int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate,
+                        bool bf16) {
+    BwdWorkspace w{};
+    w.chunk = ssd::bwd_chunk(dstate, bf16);
+    if (!w.chunk) return w;
+    w.nblk = ssd::bwd_head_blocks(batch, seqlen, nheads, ngroups, w.chunk);
+    const size_t nC = (static_cast<size_t>(seqlen) + w.chunk - 1) / w.chunk;
+    const size_t tok = static_cast<size_t>(batch) * nheads * nC * w.chunk * sizeof(float);
+    const size_t elems = static_cast<size_t>(batch) * nC * nheads * headdim * dstate;
+    const size_t part = static_cast<size_t>(w.nblk) * batch * seqlen * ngroups * dstate * sizeof(float);
+    const size_t per_chunk = static_cast<size_t>(batch) * nC * nheads * sizeof(float);
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += align_up(bytes);
+        return at;
+    };
+    w.s_off = take(tok);
+    w.delta_off = take(tok);
+    w.states_off = take(elems * sizeof(float));
+    w.init_off = take(elems * (bf16 ? 2 : 4));
+    w.gnext_off = take(elems * (bf16 ? 2 : 4));
+    w.ds_off = take(tok);
+    w.dw_off = take(tok);
+    w.dB_off = take(part);
+    w.dC_off = take(part);
+    w.dA_off = take(per_chunk);
+    w.dbias_off = take(per_chunk);
+    w.dD_off = take(per_chunk);
+    w.total = o;
+    return w;
+}
+
 int check_dims(int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate) {
     if (batch < 1 || seqlen < 1 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1)
         return SSD_ERR_SHAPE;
@@ -116,6 +156,13 @@ size_t ssd_forward_varlen_workspace_size(int seqlen, int nheads, int headdim, in
     size_t seg_off;
     return varlen_layout(seqlen, nheads, headdim, ngroups, dstate, chunk, dtype == SSD_BF16,
                          &seg_off).total;
+}
+
+size_t ssd_backward_workspace_size(int batch, int seqlen, int nheads, int headdim, int ngroups,
+                                   int dstate, int dtype) {
+    if (check_dims(batch, seqlen, nheads, headdim, ngroups, dstate) != SSD_OK || !valid_dtype(dtype))
+        return 0;
+    return bwd_layout(batch, seqlen, nheads, headdim, ngroups, dstate, dtype == SSD_BF16).total;
 }
 
 size_t ssd_chunk_cb_size(int batch, int seqlen, int ngroups, int chunk, int dtype) {
@@ -317,6 +364,81 @@ int ssd_forward_varlen(const void *x, const void *dt, const float *A, const void
         e = ssd::launch_varlen_final_states(x, B, delta, cumsum, cu_seqlens, seg, cinit, nseq,
                                             seqlen, nheads, ngroups, dstate, chunk, bf16,
                                             seq_states, s);
+    return status_of(e);
+}
+
+int ssd_backward(const void *x, const void *dt, const float *A, const void *B, const void *C,
+                 const float *D, const float *init_state, const void *dy,
+                 const float *dfinal_state, int batch, int seqlen, int nheads, int headdim,
+                 int ngroups, int dstate, int dtype, void *dx, void *ddt, float *dA, void *dB,
+                 void *dC, float *dD, float *dinit_state, float *ddt_bias, void *workspace,
+                 size_t workspace_bytes, const ssd_options *opts, void *stream) {
+    if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC) return SSD_ERR_NULL;
+    int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
+    if (rc != SSD_OK) return rc;
+    if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    const bool bf16 = dtype == SSD_BF16;
+    if (!ssd::bwd_chunk(dstate, bf16)) return SSD_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(dy) || !aligned16(dx) ||
+        !aligned16(dB) || !aligned16(dC) || (init_state && !aligned16(init_state)) ||
+        (dfinal_state && !aligned16(dfinal_state)) || (dinit_state && !aligned16(dinit_state)))
+        return SSD_ERR_UNSUPPORTED;
+    ssd::DtOpts o;
+    rc = dt_opts(opts, o);
+    if (rc != SSD_OK) return rc;
+    const BwdWorkspace ws = bwd_layout(batch, seqlen, nheads, headdim, ngroups, dstate, bf16);
+    if (!workspace || workspace_bytes < ws.total) return SSD_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return SSD_ERR_WORKSPACE;
+
+    char *base = static_cast<char *>(workspace);
+    auto f32 = [&](size_t off) { return reinterpret_cast<float *>(base + off); };
+    float *s_ = f32(ws.s_off), *delta = f32(ws.delta_off), *states = f32(ws.states_off);
+    void *cinit = base + ws.init_off, *gnext = base + ws.gnext_off;
+    const int Q = ws.chunk, nC = (seqlen + Q - 1) / Q;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    // forward recompute: prefix sums, input weights, the state entering each chunk
+    hipError_t e = ssd::launch_chunk_cumsum(dt, A, batch, seqlen, nheads, Q, bf16, o, s_, delta, st);
+    if (e == hipSuccess) {
+        if (ssd::state_passing_fused(batch, nheads, bf16)) {
+            e = ssd::launch_chunk_state_passing(x, B, s_, delta, init_state, batch, seqlen, nheads,
+                                                ngroups, dstate, Q, cinit, nullptr, st);
+        } else {
+            e = ssd::launch_chunk_state(x, B, delta, s_, nullptr, batch, seqlen, nheads, ngroups,
+                                        dstate, Q, bf16, states, st);
+            if (e == hipSuccess)
+                e = ssd::launch_state_passing(states, s_, init_state, nullptr, batch, seqlen,
+                                              nheads, dstate, Q, bf16, cinit, nullptr, st);
+        }
+    }
+    // the adjoint of the state leaving each chunk: dS_c, then the reverse pass
+    if (e == hipSuccess)
+        e = ssd::launch_chunk_state(dy, C, nullptr, s_, nullptr, batch, seqlen, nheads, ngroups,
+                                    dstate, Q, bf16, states, st, /*dout=*/true);
+    if (e == hipSuccess)
+        e = ssd::launch_state_passing(states, s_, dfinal_state, nullptr, batch, seqlen, nheads,
+                                      dstate, Q, bf16, gnext, dinit_state, st, /*reverse=*/true);
+    // the chunks' gradients
+    ssd::BwdArgs a{};
+    a.x = x; a.dy = dy; a.B = B; a.C = C; a.dA_cumsum = s_; a.delta = delta; a.D = D;
+    a.chunk_init = cinit; a.grad_next = gnext;
+    a.batch = batch; a.seqlen = seqlen; a.nheads = nheads; a.ngroups = ngroups;
+    a.dstate = dstate; a.chunk = Q; a.nblk = ws.nblk; a.bf16 = bf16;
+    a.dx = dx; a.ds = f32(ws.ds_off); a.dw = f32(ws.dw_off);
+    a.dB_part = f32(ws.dB_off); a.dC_part = f32(ws.dC_off); a.dD_part = f32(ws.dD_off);
+    if (e == hipSuccess) e = ssd::launch_chunk_bwd(a, st);
+    const size_t bc = static_cast<size_t>(batch) * seqlen * ngroups * dstate;
+    if (e == hipSuccess) e = ssd::launch_bwd_reduce(a.dB_part, ws.nblk, bc, bf16, dB, st);
+    if (e == hipSuccess) e = ssd::launch_bwd_reduce(a.dC_part, ws.nblk, bc, bf16, dC, st);
+    // stage 1: dt, A, dt bias
+    if (e == hipSuccess)
+        e = ssd::launch_bwd_dt(dt, A, a.ds, a.dw, batch, seqlen, nheads, Q, bf16, o, ddt,
+                               f32(ws.dA_off), f32(ws.dbias_off), st);
+    const int nbc = batch * nC;
+    if (e == hipSuccess) e = ssd::launch_bwd_head_sum(f32(ws.dA_off), nbc, nheads, dA, st);
+    if (e == hipSuccess && ddt_bias)
+        e = ssd::launch_bwd_head_sum(f32(ws.dbias_off), nbc, nheads, ddt_bias, st);
+    if (e == hipSuccess && dD) e = ssd::launch_bwd_head_sum(a.dD_part, nbc, nheads, dD, st);
     return status_of(e);
 }
 

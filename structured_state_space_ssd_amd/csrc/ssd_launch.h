@@ -32,10 +32,13 @@ hipError_t launch_chunk_cumsum(const void *dt, const float *A, int batch, int se
 // seg (nullable): packed sequences, one int per token in dA_cumsum's chunk-padded
 // layout: the first token of the token's sequence relative to its chunk's first
 // token, or -1 if that sequence began in an earlier chunk (launch_varlen_seg).
+// dout (backward): the same contraction with token weights exp(s_j) instead of
+// exp(s_end - s_j) delta_j, i.e. sum_j exp(s_j) x_j B_j^T with x := dy and
+// B := C: how a chunk's outputs depend on the state entering it (delta unused).
 hipError_t launch_chunk_state(const void *x, const void *B, const float *delta,
                               const float *dA_cumsum, const int *seg,
                               int batch, int seqlen, int nheads, int ngroups, int dstate, int chunk,
-                              bool bf16, float *states, hipStream_t stream);
+                              bool bf16, float *states, hipStream_t stream, bool dout = false);
 
 // Stages 2 and 3 in one kernel (bf16 only; used when state_passing_fused()):
 // writes chunk_init (bf16) and final_state (nullable) directly, without the
@@ -47,11 +50,12 @@ hipError_t launch_chunk_state_passing(const void *x, const void *B, const float 
                                       void *chunk_init, float *final_state, hipStream_t stream);
 
 // chunk_init is written in the MFMA operand type of the forward's dtype
-// (bf16 when bf16 is true, else float32).
+// (bf16 when bf16 is true, else float32). reverse (backward): the adjoint pass,
+// from init = dfinal over the chunks in reverse (see state_passing.hip).
 hipError_t launch_state_passing(const float *states, const float *dA_cumsum, const float *init,
                                 const int *seg, int batch, int seqlen, int nheads, int dstate, int chunk,
                                 bool bf16, void *chunk_init, float *final_state,
-                                hipStream_t stream);
+                                hipStream_t stream, bool reverse = false);
 
 size_t chunk_cb_bytes(int batch, int seqlen, int ngroups, int chunk, bool bf16);
 
@@ -78,6 +82,34 @@ hipError_t launch_varlen_final_states(const void *x, const void *B, const float 
                                       const int *seg, const void *chunk_init, int nseq,
                                       int seqlen, int nheads, int ngroups, int dstate, int chunk,
                                       bool bf16, float *seq_states, hipStream_t stream);
+
+// ---- backward (chunk_bwd.hip)
+// Chunk length the backward runs with (0: unsupported) and its head blocks.
+int bwd_chunk(int dstate, bool bf16);
+int bwd_head_blocks(int batch, int seqlen, int nheads, int ngroups, int chunk);
+
+struct BwdArgs {
+    const void *x, *dy, *B, *C;
+    const float *dA_cumsum, *delta, *D;
+    const void *chunk_init, *grad_next;  // operand type: H_c and the adjoint G_{c+1}
+    int batch, seqlen, nheads, ngroups, dstate, chunk, nblk;
+    bool bf16;
+    void *dx;
+    float *ds, *dw;                 // [Bt][H][nC*Q]
+    float *dB_part, *dC_part;       // [nblk][Bt][L][G][N]
+    float *dD_part;                 // [Bt][nC][H]
+};
+hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t stream);
+// out (input dtype, count elements) = sum over nblk of part[k][count]
+hipError_t launch_bwd_reduce(const float *part, int nblk, size_t count, bool bf16, void *out,
+                             hipStream_t stream);
+hipError_t launch_bwd_dt(const void *dt, const float *A, const float *ds, const float *dw,
+                         int batch, int seqlen, int nheads, int chunk, bool bf16,
+                         const DtOpts &opts, void *ddt, float *dA_part, float *dbias_part,
+                         hipStream_t stream);
+// out[h] = sum_i part[i][h], i < nbc
+hipError_t launch_bwd_head_sum(const float *part, int nbc, int nheads, float *out,
+                               hipStream_t stream);
 
 hipError_t launch_decode_step(float *state, const void *x, const void *dt, const float *A,
                               const void *B, const void *C, const float *D, int batch, int nheads,

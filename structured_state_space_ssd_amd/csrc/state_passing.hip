@@ -5,6 +5,9 @@
 //   H_0 = init,  H_{c+1} = alpha_c * H_c + S_c,  chunk_init[c] = H_c.
 // Packed sequences (seg given): alpha_c = 0 where the sequence of chunk c's
 // last token begins inside chunk c (S_c then holds that sequence's tokens only).
+// REV (backward): the adjoint pass over the chunks in reverse, G_nC = dfinal,
+// G_c = alpha_c G_{c+1} + dS_c, writing out[c] = G_{c+1} (the gradient of the
+// state leaving chunk c) and G_0 (the initial state's gradient) as "final".
 //
 // Sequential over chunks, parallel over (batch, head, P*N/4): each thread owns
 // one float4 of a head's P x N state. The chunk loop is unrolled by 8 so that
@@ -27,7 +30,7 @@ __device__ __forceinline__ void store4(__bf16 *p, const floatx4 &v) {
 
 // OutT: element type of chunk_init (float, or __bf16 = the bf16 MFMA operand
 // type chunk_scan reads; the recurrence itself always runs in float32).
-template <typename OutT>
+template <typename OutT, bool REV>
 __global__ __launch_bounds__(256) void state_passing_kernel(
     const float *__restrict__ states, const float *__restrict__ dA_cumsum,
     const float *__restrict__ init, const int *__restrict__ seg, int L, int H, int PN, int Q,
@@ -48,8 +51,8 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
         float dec[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int c = c0 + u;
-            if (c < nC) {
+            const int c = REV ? nC - 1 - (c0 + u) : c0 + u;
+            if (c0 + u < nC) {
                 sv[u] = *reinterpret_cast<const floatx4 *>(sp + c * cstride);
                 const int lenc = min(Q, L - c * Q);
                 dec[u] = exp2f(s[(size_t)c * Q + lenc - 1] * kLog2e);
@@ -58,8 +61,8 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int c = c0 + u;
-            if (c < nC) {
+            const int c = REV ? nC - 1 - (c0 + u) : c0 + u;
+            if (c0 + u < nC) {
                 store4(cp + c * cstride, hc);
                 hc = dec[u] * hc + sv[u];
             }
@@ -68,22 +71,34 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
     if (final_state) reinterpret_cast<floatx4 *>(final_state + head * PN)[e4] = hc;
 }
 
-hipError_t launch_state_passing(const float *states, const float *dA_cumsum, const float *init,
-                                const int *seg, int batch, int seqlen, int nheads, int dstate,
-                                int chunk, bool bf16, void *chunk_init, float *final_state,
-                                hipStream_t stream) {
+template <bool REV>
+static hipError_t launch_sp(const float *states, const float *dA_cumsum, const float *init,
+                            const int *seg, int batch, int seqlen, int nheads, int dstate,
+                            int chunk, bool bf16, void *chunk_init, float *final_state,
+                            hipStream_t stream) {
     const int nC = (seqlen + chunk - 1) / chunk;
     const int PN = 64 * dstate;
     const dim3 grid((PN / 4 + 255) / 256, nheads, batch);
     if (bf16)
-        state_passing_kernel<__bf16><<<grid, 256, 0, stream>>>(
+        state_passing_kernel<__bf16, REV><<<grid, 256, 0, stream>>>(
             states, dA_cumsum, init, seg, seqlen, nheads, PN, chunk, nC,
             static_cast<__bf16 *>(chunk_init), final_state);
     else
-        state_passing_kernel<float><<<grid, 256, 0, stream>>>(
+        state_passing_kernel<float, REV><<<grid, 256, 0, stream>>>(
             states, dA_cumsum, init, seg, seqlen, nheads, PN, chunk, nC,
             static_cast<float *>(chunk_init), final_state);
     return hipGetLastError();
+}
+
+hipError_t launch_state_passing(const float *states, const float *dA_cumsum, const float *init,
+                                const int *seg, int batch, int seqlen, int nheads, int dstate,
+                                int chunk, bool bf16, void *chunk_init, float *final_state,
+                                hipStream_t stream, bool reverse) {
+    if (reverse)
+        return launch_sp<true>(states, dA_cumsum, init, seg, batch, seqlen, nheads, dstate, chunk,
+                               bf16, chunk_init, final_state, stream);
+    return launch_sp<false>(states, dA_cumsum, init, seg, batch, seqlen, nheads, dstate, chunk,
+                            bf16, chunk_init, final_state, stream);
 }
 
 }  // namespace ssd

@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
     for required in ("ssd_forward", "ssd_step", "ssd_forward_workspace_size", "ssd_strerror",
                      "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_cb",
                      "ssd_chunk_scan", "ssd_forward_timed", "ssd_chunk_cb_size", "ssd_forward_ex",
-                     "ssd_step_ex", "ssd_forward_varlen", "ssd_forward_varlen_workspace_size"):
+                     "ssd_step_ex", "ssd_forward_varlen", "ssd_forward_varlen_workspace_size",
+                     "ssd_backward", "ssd_backward_workspace_size"):
         assert required in names
 
 
@@ -241,3 +242,37 @@ def test_varlen_rejects(lib, kw, code):
 
 def test_varlen_rejects_bad_options(lib):
     assert _varlen(lib, opts=_opts(discretization=3)) == SSD_ERR_OPTION
+
+
+def _bwd(lib, **kw):
+    a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, init=None, dy=FAKE, dfinal=None,
+             Bt=1, L=128, H=4, P=64, G=1, N=64, dtype=1, dx=FAKE, ddt=FAKE, dA=FAKE, dB=FAKE,
+             dC=FAKE, dD=None, dinit=None, dbias=None, ws=FAKE, wsb=1 << 40, opts=None)
+    a.update(kw)
+    return lib.ssd_backward(*(a[k] for k in ("x", "dt", "A", "B", "C", "D", "init", "dy", "dfinal",
+                                             "Bt", "L", "H", "P", "G", "N", "dtype", "dx", "ddt",
+                                             "dA", "dB", "dC", "dD", "dinit", "dbias", "ws", "wsb",
+                                             "opts")), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dy=None), SSD_ERR_NULL),
+    (dict(dx=None), SSD_ERR_NULL),
+    (dict(dA=None), SSD_ERR_NULL),
+    (dict(Bt=0), SSD_ERR_SHAPE),
+    (dict(H=6, G=4), SSD_ERR_SHAPE),
+    (dict(N=48), SSD_ERR_UNSUPPORTED),
+    (dict(dtype=0, N=128), SSD_ERR_UNSUPPORTED),   # float32 backward: N <= 64
+    (dict(dx=ctypes.c_void_p(0x100008)), SSD_ERR_UNSUPPORTED),
+    (dict(ws=None), SSD_ERR_WORKSPACE),
+    (dict(wsb=4096), SSD_ERR_WORKSPACE),
+    (dict(opts=_opts(discretization=9)), SSD_ERR_OPTION),
+])
+def test_backward_rejects(lib, kw, code):
+    assert _bwd(lib, **kw) == code
+
+
+def test_backward_workspace_size(lib):
+    assert lib.ssd_backward_workspace_size(8, 2048, 80, 64, 1, 64, 1) > 0
+    assert lib.ssd_backward_workspace_size(1, 256, 2, 64, 1, 128, 0) == 0  # unsupported
+    assert lib.ssd_backward_workspace_size(1, 256, 2, 64, 1, 64, 0) > 0
