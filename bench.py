@@ -279,6 +279,31 @@ def time_forward_varlen(steps, warmup):
     return w, cu, ms
 
 
+def time_backward(w, steps, warmup):
+    """Whole-backward time (host clock): gradients of every input for the
+    workload's forward, with a final-state gradient and every dt option off."""
+    import torch
+    import ssd_workloads as W
+    import structured_state_space_ssd_amd as ssd
+
+    d = W.generate(w)
+    d.update(W.generate_grads(w))
+    g = upload(d)
+    ws = torch.empty(int(ssd._native.lib.ssd_backward_workspace_size(
+        w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate, 1 if w.dtype == "bf16" else 0)),
+        dtype=torch.uint8, device="cuda")
+    args = [g[k] for k in ("x", "dt", "A", "B", "C", "D", "dy")]
+    kw = dict(init_state=g["init"], dfinal_state=g["dfinal"], workspace=ws)
+    for _ in range(warmup):
+        ssd.backward(*args, **kw)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ssd.backward(*args, **kw)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
 def time_decode(w, warmup=3):
     import torch
     import ssd_workloads as W
@@ -379,7 +404,9 @@ WRITE_CMD = ('rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/write" -o 
 KERNEL_OF = {"chunk_cumsum_kernel": "chunk_cumsum", "chunk_state_passing": "chunk_state",
              "state_passing_kernel": "state_passing", "chunk_state": "chunk_state",
              "chunk_cb_kernel": "chunk_cb", "chunk_scan": "chunk_scan",
-             "decode_step_kernel": "decode_step"}
+             "decode_step_kernel": "decode_step", "chunk_bwd_kernel": "backward: chunk gradients",
+             "bwd_dt_kernel": "backward: dt, A, bias", "bwd_reduce_kernel": "backward: dB, dC sums",
+             "bwd_head_sum_kernel": "backward: per-head sums", "varlen_seg": "packed: token masks"}
 CALIBRATION_KERNEL = "__amd_rocclr_copyBuffer"  # the 1 GiB device copy of --counters
 COPY_BYTES = 1 << 30
 
@@ -407,6 +434,11 @@ def summarize_trace(stats_csv, bench_log):
             if line.startswith("{"):
                 bench = json.loads(line)
     out = ["# Kernel trace: SSD forward stages (Mamba-2 2.7B-shaped layer) and decode step", "",
+           "The same run also times the forward with every step-size option, the packed",
+           "variable-length forward and the backward on the same shapes (bench.py's",
+           "forward_with_options, forward_varlen and backward entries); their kernels are",
+           "listed too. A kernel name can appear for several uses (e.g. the chunk-state",
+           "kernel computes the backward's output-gradient contributions as well).", "",
            "Commands, from the repository root on one MI355X:", "", "```",
            "cd /tmp && export TMPDIR=/tmp && cd -", TRACE_CMD,
            f'python bench.py --summarize-trace "$OUT/trace/trace_kernel_stats.csv" "$OUT/bench_trace.log"',
@@ -572,6 +604,12 @@ def main():
     print(f"[bench] packed variable-length forward: {vl_ms * 1e3:.1f} us", file=sys.stderr,
           flush=True)
 
+    bw_ms = time_backward(w, max(10, args.steps // 2), 3)
+    backward = {"workload": "gradients of x, dt, A, B, C, D and the initial state, same shapes",
+                "us_per_backward": round(bw_ms * 1e3, 2),
+                "tokens_per_s": round(w.tokens / (bw_ms * 1e-3), 1)}
+    print(f"[bench] backward: {bw_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+
     extra = {}
     if args.all:
         for name in ("tiny_f32", "large_state", "long_seq"):
@@ -624,6 +662,7 @@ def main():
         "kernels": kernels,
         "forward_with_options": options,
         "forward_varlen": varlen,
+        "backward": backward,
         "decode": decode,
         "hbm_copy_probe": probe,
     }
