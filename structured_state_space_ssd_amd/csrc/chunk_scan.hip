@@ -308,8 +308,10 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_kernel(
 //     for the wait counter, so a wait on any global load issued after the
 //     prefetch would also wait for the prefetch.)
 //   - Outputs are staged through the head's x buffer and leave as whole
-//     128-byte token rows; the next head's first wait leaves those stores in
-//     flight.
+//     128-byte token rows, with non-temporal stores (y is not read again on
+//     the GPU; ordinary stores would displace the x, H_c and B rows other
+//     workgroups are about to read); the next head's first wait leaves those
+//     stores in flight.
 // The products are those of the float kernel above, except that the
 // state-to-output product takes raw C rows and scales its result by exp(s_i)
 // per token, and every wavefront's slice sequence is fixed at compile time
@@ -703,7 +705,7 @@ __global__ __launch_bounds__(Q * 4) void chunk_scan_bf16_kernel(
             const int s = i * 64 + ln;
             const int r = s >> 3, q = (s & 7) ^ (r & 7);
             const uint4 v = *reinterpret_cast<const uint4 *>(xs + s * 8);
-            if (r < len) *reinterpret_cast<uint4 *>(yh + (size_t)r * xrow + q * 8) = v;
+            if (r < len) store_nt16(yh + (size_t)r * xrow + q * 8, v);
         }
         if (!DBUF && more) {
             barrier_lds();  // every wavefront has read its outputs out of x(h)
@@ -1040,7 +1042,7 @@ __global__ __launch_bounds__(Q * 2, 4) void chunk_scan_bf16_pair_kernel(
             const int s = i * 64 + ln;
             const int r = s >> 3, q = (s & 7) ^ (r & 7);
             const uint4 v = *reinterpret_cast<const uint4 *>(xs + s * 8);
-            if (r < len) *reinterpret_cast<uint4 *>(yh + (size_t)r * xrow + q * 8) = v;
+            if (r < len) store_nt16(yh + (size_t)r * xrow + q * 8, v);
         }
         if (more) {
             barrier_lds();  // the outputs have left the x buffer

@@ -186,6 +186,14 @@ template <> struct Raw8<float> {
     }
 };
 
+// 16-byte non-temporal store: for outputs nothing on the GPU reads again soon
+// (the chunk scan's y), so that they do not displace inputs other workgroups
+// are about to read from the caches.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_nt16(void *p, const uint4 &v) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4 *>(p));
+}
+
 // Copy 16 bytes.
 __device__ __forceinline__ void copy16(void *dst, const void *src) {
     *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
