@@ -61,6 +61,32 @@ __device__ __forceinline__ void store4_global<float>(float *p, const floatx4 &v)
     *reinterpret_cast<floatx4 *>(p) = v;
 }
 
+// Non-temporal variants, for dx (never read again on the GPU).
+template <typename T>
+__device__ __forceinline__ void store4_global_nt(T *p, const floatx4 &v);
+template <>
+__device__ __forceinline__ void store4_global_nt<bf16_t>(bf16_t *p, const floatx4 &v) {
+    const bf16x4 b = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]),
+                      static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
+    __builtin_nontemporal_store(b, reinterpret_cast<bf16x4 *>(p));
+}
+template <>
+__device__ __forceinline__ void store4_global_nt<float>(float *p, const floatx4 &v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<floatx4 *>(p));
+}
+
+// Four consecutive LDS elements as floats (8- or 16-byte aligned).
+__device__ __forceinline__ void read4(float (&v)[4], const __bf16 *p) {
+    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(b[e]);
+}
+__device__ __forceinline__ void read4(float (&v)[4], const float *p) {
+    const floatx4 b = *reinterpret_cast<const floatx4 *>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = b[e];
+}
+
 }  // namespace
 
 template <typename T, int N, int Q>
@@ -126,42 +152,110 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) dBT[nt] = dCT[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int k = 0; k < nh; ++k) {
-        const int h = g * hpg + kb + k * nblk;
-        __syncthreads();  // the previous head is done with LDS
-        if (tid < 4) red[tid] = 0.0f;
+    // Per head, x, dy, H_c, G and the tables travel through registers: the next
+    // head's loads are issued right after this head's values reach LDS and
+    // complete while this head computes (nothing in between waits on a global
+    // load: the head's barrier below is an LDS-only one).
+    constexpr int XI = (Q * XPR + NTHR - 1) / NTHR, HI = (P * BPR + NTHR - 1) / NTHR;
+    uint4 px[XI], pd[XI], ph[HI], pg[HI];
+    float ps = 0.0f, pw = 0.0f, pD = 0.0f;
+    auto fetch = [&](int h) {
         const T *xh = x + ((size_t)b * L + t0) * xrow + (size_t)h * P;
         const T *dyh = dy + ((size_t)b * L + t0) * xrow + (size_t)h * P;
-        for (int idx = tid; idx < Q * XPR; idx += NTHR) {
-            const int j = idx / XPR, q = idx % XPR;
-            uint4 vx = make_uint4(0, 0, 0, 0), vd = make_uint4(0, 0, 0, 0);
-            if (j < len) {
-                vx = *reinterpret_cast<const uint4 *>(xh + (size_t)j * xrow + q * EPP);
-                vd = *reinterpret_cast<const uint4 *>(dyh + (size_t)j * xrow + q * EPP);
+#pragma unroll
+        for (int i = 0; i < XI; ++i) {
+            const int idx = tid + i * NTHR, j = idx / XPR, q = idx % XPR;
+            px[i] = pd[i] = make_uint4(0, 0, 0, 0);
+            if (idx < Q * XPR && j < len) {
+                px[i] = *reinterpret_cast<const uint4 *>(xh + (size_t)j * xrow + q * EPP);
+                pd[i] = *reinterpret_cast<const uint4 *>(dyh + (size_t)j * xrow + q * EPP);
             }
-            *reinterpret_cast<uint4 *>(xs + j * LDX + q * EPP) = vx;
-            *reinterpret_cast<uint4 *>(dys + j * LDX + q * EPP) = vd;
         }
         const size_t st = (((size_t)b * nC + c) * H + h) * (size_t)P * N;
-        for (int idx = tid; idx < P * BPR; idx += NTHR) {
-            const int p = idx / BPR, q = idx % BPR;
-            *reinterpret_cast<uint4 *>(hs + p * LDB + q * EPP) =
-                *reinterpret_cast<const uint4 *>(chunk_init + st + (size_t)p * N + q * EPP);
-            *reinterpret_cast<uint4 *>(gs + p * LDB + q * EPP) =
-                *reinterpret_cast<const uint4 *>(grad_next + st + (size_t)p * N + q * EPP);
+#pragma unroll
+        for (int i = 0; i < HI; ++i) {
+            const int idx = tid + i * NTHR, p = idx / BPR, q = idx % BPR;
+            if (idx < P * BPR) {
+                ph[i] = *reinterpret_cast<const uint4 *>(chunk_init + st + (size_t)p * N + q * EPP);
+                pg[i] = *reinterpret_cast<const uint4 *>(grad_next + st + (size_t)p * N + q * EPP);
+            }
         }
+        if (tid < Q) {
+            const size_t srow = ((size_t)b * H + h) * (size_t)nC * Q + (size_t)c * Q;
+            ps = dA_cumsum[srow + tid];
+            pw = delta[srow + tid];
+        }
+        pD = D ? D[h] : 0.0f;
+    };
+    fetch(g * hpg + kb);
+
+    for (int k = 0; k < nh; ++k) {
+        const int h = g * hpg + kb + k * nblk;
+        __syncthreads();  // the previous head is done with LDS; this head's loads are in
+        if (tid < 4) red[tid] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < XI; ++i) {
+            const int idx = tid + i * NTHR, j = idx / XPR, q = idx % XPR;
+            if (idx < Q * XPR) {
+                *reinterpret_cast<uint4 *>(xs + j * LDX + q * EPP) = px[i];
+                *reinterpret_cast<uint4 *>(dys + j * LDX + q * EPP) = pd[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < HI; ++i) {
+            const int idx = tid + i * NTHR, p = idx / BPR, q = idx % BPR;
+            if (idx < P * BPR) {
+                *reinterpret_cast<uint4 *>(hs + p * LDB + q * EPP) = ph[i];
+                *reinterpret_cast<uint4 *>(gs + p * LDB + q * EPP) = pg[i];
+            }
+        }
+        if (tid < Q) {
+            slt[tid] = ps * kLog2e;
+            wt[tid] = pw;
+        }
+        const float Dh = pD;
         const size_t srow = ((size_t)b * H + h) * (size_t)nC * Q + (size_t)c * Q;
-        for (int i = tid; i < Q; i += NTHR) {
-            slt[i] = dA_cumsum[srow + i] * kLog2e;
-            wt[i] = delta[srow + i];
-        }
-        __syncthreads();
+        barrier_lds();
+        if (k + 1 < nh) fetch(h + nblk);
 
         const float sl_t = slt[tok], w_t = wt[tok];
         const float sl_end = slt[len - 1];
         const float f_t = __builtin_amdgcn_exp2f(sl_end - sl_t);  // exp(s_end - s_tok)
         const float e_t = __builtin_amdgcn_exp2f(sl_t);           // exp(s_tok)
-        const float Dh = D ? D[h] : 0.0f;
+
+        // the lane's own token rows as MFMA B operands, for every slice of both
+        // passes (B and C rows kept in registers for N <= 64, else re-read)
+        constexpr bool kKeepBC = NK <= 2;
+        Frag<T> tx[P / 32], tdy[P / 32], tb[kKeepBC ? NK : 1], tc[kKeepBC ? NK : 1];
+#pragma unroll
+        for (int kk = 0; kk < P / 32; ++kk) {
+            lds_frag8(tx[kk], xs + tok * LDX + kk * 32 + 8 * g4);
+            lds_frag8(tdy[kk], dys + tok * LDX + kk * 32 + 8 * g4);
+        }
+        auto own = [&](const E *m, int kk, Frag<T> &f) {  // row tok of B or C at k-step kk
+            const int n0 = kk * 32 + 8 * g4;
+            if (n0 < N) lds_frag8(f, m + tok * LDB + n0);
+            else f.zero();
+        };
+        if constexpr (kKeepBC) {
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                own(bs, kk, tb[kk]);
+                own(cs, kk, tc[kk]);
+            }
+        }
+        auto own_b = [&](int kk) -> Frag<T> {
+            if constexpr (kKeepBC) return tb[kk];
+            Frag<T> f;
+            own(bs, kk, f);
+            return f;
+        };
+        auto own_c = [&](int kk) -> Frag<T> {
+            if constexpr (kKeepBC) return tc[kk];
+            Frag<T> f;
+            own(cs, kk, f);
+            return f;
+        };
 
         // ================= pass 1: tok as column j, slices of rows i >= j
         floatx4 dxT[4];  // lane (g4, c16): dx[tok][16pt + 4g4 + e]
@@ -176,23 +270,17 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
                 dxo[half] = cbo[half] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int kk = 0; kk < P / 32; ++kk) {
-                    Frag<T> fa, fb;
+                    Frag<T> fa;
                     lds_frag8(fa, dys + ir * LDX + kk * 32 + 8 * g4);
-                    lds_frag8(fb, xs + tok * LDX + kk * 32 + 8 * g4);
-                    mma(dxo[half], fa, fb);
+                    mma(dxo[half], fa, tx[kk]);
                 }
 #pragma unroll
                 for (int kk = 0; kk < NK; ++kk) {
                     const int n0 = kk * 32 + 8 * g4;
-                    Frag<T> fa, fb;
-                    if (n0 < N) {
-                        lds_frag8(fa, cs + ir * LDB + n0);
-                        lds_frag8(fb, bs + tok * LDB + n0);
-                    } else {
-                        fa.zero();
-                        fb.zero();
-                    }
-                    mma(cbo[half], fa, fb);
+                    Frag<T> fa;
+                    if (n0 < N) lds_frag8(fa, cs + ir * LDB + n0);
+                    else fa.zero();
+                    mma(cbo[half], fa, own_b(kk));
                 }
             }
             // element (half, e): token i = 32 sl + 16 half + 4 g4 + e, column j = tok
@@ -235,21 +323,18 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk) {
                 const int n0 = kk * 32 + 8 * g4;
-                Frag<T> fa, fb;
-                if (n0 < N) {
-                    lds_frag8(fa, gs + (pt * 16 + c16) * LDB + n0);
-                    lds_frag8(fb, bs + tok * LDB + n0);
-                } else {
-                    fa.zero();
-                    fb.zero();
-                }
-                mma(uo, fa, fb);
+                Frag<T> fa;
+                if (n0 < N) lds_frag8(fa, gs + (pt * 16 + c16) * LDB + n0);
+                else fa.zero();
+                mma(uo, fa, own_b(kk));
             }
+            float xv[4], dv[4];
+            read4(xv, xs + tok * LDX + pt * 16 + 4 * g4);
+            read4(dv, dys + tok * LDX + pt * 16 + 4 * g4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int p = pt * 16 + 4 * g4 + e;
-                xu += static_cast<float>(xs[tok * LDX + p]) * uo[e];
-                dxT[pt][e] += wf * uo[e] + Dh * static_cast<float>(dys[tok * LDX + p]);
+                xu += xv[e] * uo[e];
+                dxT[pt][e] += wf * uo[e] + Dh * dv[e];
             }
         }
 #pragma unroll
@@ -268,7 +353,7 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
         if (tok < len) {
             T *dxr = dx + ((size_t)b * L + t0 + tok) * xrow + (size_t)h * P;
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) store4_global<T>(dxr + pt * 16 + 4 * g4, dxT[pt]);
+            for (int pt = 0; pt < 4; ++pt) store4_global_nt<T>(dxr + pt * 16 + 4 * g4, dxT[pt]);
         }
         cin = xor_sum_groups(cin);
         cex = xor_sum_groups(cex);
@@ -290,23 +375,17 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
                 dxo[half] = cbo[half] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int kk = 0; kk < P / 32; ++kk) {
-                    Frag<T> fa, fb;
+                    Frag<T> fa;
                     lds_frag8(fa, xs + jr * LDX + kk * 32 + 8 * g4);
-                    lds_frag8(fb, dys + tok * LDX + kk * 32 + 8 * g4);
-                    mma(dxo[half], fa, fb);
+                    mma(dxo[half], fa, tdy[kk]);
                 }
 #pragma unroll
                 for (int kk = 0; kk < NK; ++kk) {
                     const int n0 = kk * 32 + 8 * g4;
-                    Frag<T> fa, fb;
-                    if (n0 < N) {
-                        lds_frag8(fa, bs + jr * LDB + n0);
-                        lds_frag8(fb, cs + tok * LDB + n0);
-                    } else {
-                        fa.zero();
-                        fb.zero();
-                    }
-                    mma(cbo[half], fa, fb);
+                    Frag<T> fa;
+                    if (n0 < N) lds_frag8(fa, bs + jr * LDB + n0);
+                    else fa.zero();
+                    mma(cbo[half], fa, own_c(kk));
                 }
             }
             Frag<T> wfr;  // e^{s_i-s_j} w_j (dy_i.x_j), rows j of the slice
@@ -352,22 +431,18 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk) {
                 const int n0 = kk * 32 + 8 * g4;
-                Frag<T> fa, fb;
-                if (n0 < N) {
-                    lds_frag8(fa, hs + (pt * 16 + c16) * LDB + n0);
-                    lds_frag8(fb, cs + tok * LDB + n0);
-                } else {
-                    fa.zero();
-                    fb.zero();
-                }
-                mma(co, fa, fb);
+                Frag<T> fa;
+                if (n0 < N) lds_frag8(fa, hs + (pt * 16 + c16) * LDB + n0);
+                else fa.zero();
+                mma(co, fa, own_c(kk));
             }
+            float xv[4], dv[4];
+            read4(xv, xs + tok * LDX + pt * 16 + 4 * g4);
+            read4(dv, dys + tok * LDX + pt * 16 + 4 * g4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int p = pt * 16 + 4 * g4 + e;
-                const float dyv = static_cast<float>(dys[tok * LDX + p]);
-                dych += dyv * co[e];
-                dd += dyv * static_cast<float>(xs[tok * LDX + p]);
+                dych += dv[e] * co[e];
+                dd += dv[e] * xv[e];
             }
         }
         rs = xor_sum_groups(rs);
@@ -388,7 +463,7 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
             for (int o = 1; o < 64; o <<= 1) gh += __shfl_xor(gh, o);
             if (l == 0) atomicAdd(&red[1], gh);
         }
-        __syncthreads();  // red[] complete
+        barrier_lds();  // red[] complete
         if (tok == len - 1) ds_t += red[0] + __builtin_amdgcn_exp2f(sl_end) * red[1];
         if (g4 == 0) {
             ds_out[srow + tok] = ds_t;
@@ -524,21 +599,25 @@ __global__ __launch_bounds__(256) void bwd_head_sum_kernel(const float *__restri
 // Chunk length of the backward for a state size (its LDS holds a chunk's x,
 // dy, B, C and two P x N states): the largest of 256, 128, 64 that fits.
 int bwd_chunk(int dstate, bool bf16) {
-    for (int q = 256; q >= 64; q /= 2) {
-        size_t bytes = 0;
-#define SSD_BWD_BYTES(TT, NN, QQ)                        \
+    // 512 threads (Q = 128) keep the accumulators of N <= 64 in registers;
+    // larger states take Q = 64 (256 threads, twice the registers per thread)
+    const int q = dstate <= 64 ? 128 : 64;
+    size_t bytes = 0;
+#define SSD_BWD_BYTES(TT, NN, QQ) \
     if (dstate == NN && q == QQ) bytes = BwdLds<TT, NN, QQ>::kBytes;
-#define SSD_BWD_BYTES_Q(TT, NN) SSD_BWD_BYTES(TT, NN, 64) SSD_BWD_BYTES(TT, NN, 128) SSD_BWD_BYTES(TT, NN, 256)
-        if (bf16) {
-            SSD_BWD_BYTES_Q(bf16_t, 16) SSD_BWD_BYTES_Q(bf16_t, 32) SSD_BWD_BYTES_Q(bf16_t, 64)
-            SSD_BWD_BYTES_Q(bf16_t, 128) SSD_BWD_BYTES_Q(bf16_t, 256)
-        } else {
-            SSD_BWD_BYTES_Q(float, 16) SSD_BWD_BYTES_Q(float, 32) SSD_BWD_BYTES_Q(float, 64)
-            SSD_BWD_BYTES_Q(float, 128) SSD_BWD_BYTES_Q(float, 256)
-        }
+#define SSD_BWD_BYTES_Q(TT, NN) SSD_BWD_BYTES(TT, NN, 64) SSD_BWD_BYTES(TT, NN, 128)
+    if (bf16) {
+        SSD_BWD_BYTES_Q(bf16_t, 16) SSD_BWD_BYTES_Q(bf16_t, 32) SSD_BWD_BYTES_Q(bf16_t, 64)
+        SSD_BWD_BYTES_Q(bf16_t, 128) SSD_BWD_BYTES_Q(bf16_t, 256)
+    } else {
+        SSD_BWD_BYTES_Q(float, 16) SSD_BWD_BYTES_Q(float, 32) SSD_BWD_BYTES_Q(float, 64)
+        SSD_BWD_BYTES_Q(float, 128) SSD_BWD_BYTES_Q(float, 256)
+    }
 #undef SSD_BWD_BYTES_Q
 #undef SSD_BWD_BYTES
-        if (bytes && bytes <= 160 * 1024) return q;
+    if (bytes && bytes <= 160 * 1024) return q;
+    if (q == 128) {  // float32 N = 64: half the chunk
+        if (!bf16 && dstate == 64 && BwdLds<float, 64, 64>::kBytes <= 160 * 1024) return 64;
     }
     return 0;
 }
@@ -571,12 +650,6 @@ static bool launch_bwd_n(int Q, const BwdArgs &a, hipStream_t s) {
         case 128:
             if constexpr (BwdLds<T, N, 128>::kBytes <= 160 * 1024) {
                 launch_bwd_q<T, N, 128>(a, s);
-                return true;
-            }
-            return false;
-        case 256:
-            if constexpr (BwdLds<T, N, 256>::kBytes <= 160 * 1024) {
-                launch_bwd_q<T, N, 256>(a, s);
                 return true;
             }
             return false;
