@@ -155,7 +155,7 @@ def upload(d):
     return out
 
 
-def time_forward(w, steps, warmup, breakdown_steps=10, event_every=5):
+def time_forward(w, steps, warmup, breakdown_steps=10, event_every=5, spin_seconds=0.15):
     """Two passes over the same resident inputs.
 
     Breakdown pass (not the timed region): ``breakdown_steps`` forwards with a
@@ -180,9 +180,17 @@ def time_forward(w, steps, warmup, breakdown_steps=10, event_every=5):
     ns = len(STAGES)
     mk = lambda: torch.cuda.Event(enable_timing=True)
 
+    # ---- spin-up: the GPU raises its clocks only under sustained load (the
+    # first tens of milliseconds of back-to-back forwards run up to 20% slower),
+    # so about 0.1 s of untimed forwards come before anything is measured
+    torch.cuda.synchronize()
+    t_spin = time.perf_counter()
+    while time.perf_counter() - t_spin < spin_seconds:
+        for _ in range(20):
+            ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y)
+        torch.cuda.synchronize()
+
     # ---- breakdown pass
-    for _ in range(3):
-        ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y)
     bd = [[mk() for _ in range(ns + 1)] for _ in range(breakdown_steps)]
     for evs in bd:
         ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y, events=evs)
@@ -520,8 +528,8 @@ def W_decode():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="mamba2_2.7b")
     ap.add_argument("--all", action="store_true", help="also time the other forward workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
