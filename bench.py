@@ -1,11 +1,13 @@
 """SSD layer benchmark on one MI355X.
 
-One step = one full SSD forward (chunk_cumsum, chunk_state, state_passing,
-chunk_cb, chunk_scan) over the Mamba-2 2.7B-shaped layer: batch 8, L 2048, 80 heads x
-P 64, N 64, one B/C group, chunk 256, bf16 inputs, fp32 accumulation, inputs
-already resident in HBM. Prints ONE JSON line.
+One step = one full SSD forward over the Mamba-2 2.7B-shaped layer: batch 8,
+L 2048, 80 heads x P 64, N 64, one B/C group, chunk 256, bf16 inputs, fp32
+accumulation, inputs already resident in HBM. Prints ONE JSON line. For this
+shape the library runs the whole forward as its single-pass kernel
+(forward_onepass); other shapes run the stages chunk_cumsum, chunk_state,
+state_passing, chunk_cb, chunk_scan.
 
-Per-stage GPU times come from HIP events the library records between its
+Per-kernel GPU times come from HIP events the library records between its
 launches (ssd_forward_timed) on the launch stream, inside the timed region.
 Roofline figures use algorithmic bytes / flops (what the method must read,
 write and compute), not executed ones. The decode step (256 x 80 heads,
@@ -32,10 +34,41 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (no sparsity)
 FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix
 STAGES = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_cb", "chunk_scan"]
+ONEPASS = ["forward_onepass"]
+SOURCE_OF = {"forward_onepass": "fwd_onepass"}  # kernel -> its source file in csrc/
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 # ---------------------------------------------------------------- accounting
+
+def onepass_path(w):
+    """Whether the library runs this forward as its single-pass kernel (bf16,
+    dstate 64, heads a multiple of 8, batch * nheads >= 512; mirrors
+    forward_onepass_ok in the library's fwd_onepass.hip)."""
+    return (w.dtype == "bf16" and w.dstate == 64 and w.nheads % 8 == 0
+            and w.batch * w.nheads >= 512)
+
+
+def stages_of(w):
+    return ONEPASS if onepass_path(w) else STAGES
+
+
+def onepass_accounting(w):
+    """Algorithmic bytes and flops of the single-pass forward kernel.
+
+    Bytes: x and dt read, y written (bf16), B and C read once per group, A and
+    D (float32) once per head; nothing else leaves the chip. Flops (multiply +
+    add = 2) of the chunked algorithm at the kernel's 64-token blocks:
+    (T+1)P per token-head for the causal block products, 2NP for the state to
+    output, 2NP for the state update, 2P for the D term, and (T+1)N per token
+    per group for the causal C B^T products."""
+    Bt, L, H, P, G, N = w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate
+    T = 64
+    tok = Bt * L
+    nbytes = 2 * tok * H * P * 2 + tok * H * 2 + 2 * tok * G * N * 2 + 2 * H * 4
+    flops = tok * H * ((T + 1) * P + 4 * N * P + 2 * P) + tok * G * (T + 1) * N
+    return {"forward_onepass": {"bytes": nbytes, "flops": flops}}
+
 
 def accounting(w):
     """Algorithmic bytes and flops per launch of each forward stage.
@@ -54,6 +87,8 @@ def accounting(w):
     (Q+1)N per token per group (causal C B^T); state_passing 2PN per
     chunk-head element pair.
     """
+    if onepass_path(w):
+        return onepass_accounting(w)
     Bt, L, H, P, G, N, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk
     e = 2 if w.dtype == "bf16" else 4
     nC = -(-L // Q)
@@ -115,7 +150,7 @@ def decode_accounting(w):
 def kernel_source_digest(name):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "structured_state_space_ssd_amd", "csrc")
-    for f in (f"{name}.hip", "ssd_common.h"):
+    for f in (f"{SOURCE_OF.get(name, name)}.hip", "ssd_common.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -177,8 +212,10 @@ def time_forward(w, steps, warmup, breakdown_steps=10, event_every=5, spin_secon
     ws = torch.empty(ssd.workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate,
                                         w.chunk, x.dtype), dtype=torch.uint8, device="cuda")
     y = torch.empty_like(x)
-    ns = len(STAGES)
+    stages = stages_of(w)
+    ns = len(stages)  # events 0..ns used (the single-pass kernel: events 0 and 1)
     mk = lambda: torch.cuda.Event(enable_timing=True)
+    pad = lambda evs: list(evs) + [None] * (len(STAGES) + 1 - len(evs))
 
     # ---- spin-up: the GPU raises its clocks only under sustained load (the
     # first tens of milliseconds of back-to-back forwards run up to 20% slower),
@@ -193,7 +230,7 @@ def time_forward(w, steps, warmup, breakdown_steps=10, event_every=5, spin_secon
     # ---- breakdown pass
     bd = [[mk() for _ in range(ns + 1)] for _ in range(breakdown_steps)]
     for evs in bd:
-        ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y, events=evs)
+        ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y, events=pad(evs))
     torch.cuda.synchronize()
     per_stage = [sum(evs[i].elapsed_time(evs[i + 1]) for evs in bd) / breakdown_steps
                  for i in range(ns)]
@@ -209,7 +246,7 @@ def time_forward(w, steps, warmup, breakdown_steps=10, event_every=5, spin_secon
         evs[dom], evs[dom + 1] = e0, e1
         for e in (e0, e1):
             e.record()  # create the HIP events before the timed region
-        events[k] = evs
+        events[k] = pad(evs)
     for _ in range(warmup):
         ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y)
     torch.cuda.synchronize()
@@ -220,7 +257,7 @@ def time_forward(w, steps, warmup, breakdown_steps=10, event_every=5, spin_secon
     wall = time.perf_counter() - t0
     dom_ms = sum(e0.elapsed_time(e1) for e0, e1 in pairs) / len(pairs)
     return {"wall_ms": wall * 1e3 / steps, "evented_ms": evented_ms,
-            "stage_ms": dict(zip(STAGES, per_stage)), "dominant": STAGES[dom], "dominant_ms": dom_ms}
+            "stage_ms": dict(zip(stages, per_stage)), "dominant": stages[dom], "dominant_ms": dom_ms}
 
 
 def time_forward_options(w, steps, warmup):
@@ -411,7 +448,8 @@ WRITE_CMD = ('rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/write" -o 
              '-- python bench.py --counters')
 # kernel-name fragment -> stage, first match wins (the fused stage-2+3 kernel
 # fills the chunk_state interval of the forward)
-KERNEL_OF = {"chunk_cumsum_kernel": "chunk_cumsum", "chunk_state_passing": "chunk_state",
+KERNEL_OF = {"ssd_forward_onepass": "forward_onepass",
+             "chunk_cumsum_kernel": "chunk_cumsum", "chunk_state_passing": "chunk_state",
              "state_passing_kernel": "state_passing", "chunk_state": "chunk_state",
              "chunk_cb_kernel": "chunk_cb", "chunk_scan": "chunk_scan",
              "decode_step_kernel": "decode_step", "chunk_bwd_kernel": "backward: chunk gradients",
@@ -505,7 +543,9 @@ def summarize_traffic(fetch_csv, write_csv, workload="mamba2_2.7b"):
            f"WRITE_SIZE by {w_scale:.3f}.", "",
            "| kernel | dispatches | fetch MB | write MB | HBM MB / launch | algorithmic MB | ratio |",
            "|---|---|---|---|---|---|---|"]
-    for k in ("chunk_cumsum", "chunk_state", "state_passing", "chunk_cb", "chunk_scan", "decode_step"):
+    for k in ONEPASS + STAGES + ["decode_step"]:
+        if k not in acc:
+            continue
         if k not in per or "fetch" not in per[k] or "write" not in per[k]:
             continue
         fk = sum(per[k]["fetch"]) / len(per[k]["fetch"])
@@ -574,7 +614,7 @@ def main():
     ms = fwd["wall_ms"]
     acc = accounting(w)
     kernels = {}
-    for name in STAGES:
+    for name in stages_of(w):
         t = fwd["stage_ms"][name] * 1e-3
         a = acc[name]
         if a["bytes"] == 0:  # stage not launched for this dtype (only event gaps in between)
@@ -596,7 +636,7 @@ def main():
                 "us_per_launch": round(fwd["dominant_ms"] * 1e3, 2),
                 "traffic": measured_traffic(dom)}
     print(f"[bench] forward {ms * 1e3:.1f} us/step ({fwd['evented_ms'] * 1e3:.1f} us with an event "
-          f"between every two stages; {fwd['dominant']} {fwd['dominant_ms'] * 1e3:.1f} us live); stages " +
+          f"between every two kernels; {fwd['dominant']} {fwd['dominant_ms'] * 1e3:.1f} us live); kernels " +
           ", ".join(f"{k} {v['us']:.1f} us" for k, v in kernels.items()), file=sys.stderr, flush=True)
 
     opt_ms = time_forward_options(w, max(10, args.steps // 2), 3)

@@ -119,7 +119,9 @@ const char *ssd_strerror(int status);
  * After the forward pass has run, these hold the intermediate results of the
  * stages below (a caller may read them, e.g. to test a stage), except that
  * for SSD_BF16 with batch * nheads >= 512 stages 2 and 3 run as one kernel
- * that keeps the per-chunk states on chip: `states` is then not written.
+ * that keeps the per-chunk states on chip (`states` is then not written),
+ * and when the forward runs as the single-pass kernel (see ssd_forward) the
+ * workspace is not touched at all.
  */
 size_t ssd_forward_workspace_size(int batch, int seqlen, int nheads, int headdim,
                                   int ngroups, int dstate, int chunk, int dtype);
@@ -127,7 +129,14 @@ size_t ssd_forward_workspace_size(int batch, int seqlen, int nheads, int headdim
 /*
  * Full SSD layer forward: enqueues ssd_chunk_cumsum, ssd_chunk_state,
  * ssd_state_passing, ssd_chunk_cb (SSD_F32 only) and ssd_chunk_scan on
- * `stream`.
+ * `stream`. For SSD_BF16 with dstate 64, nheads a multiple of 8,
+ * batch * nheads >= 512 and a 16-byte aligned dt, it enqueues instead one
+ * single-pass kernel that computes the same result (up to rounding): one
+ * workgroup per (batch, head) walks the sequence in blocks of 64 tokens,
+ * carrying the state from block to block in registers (the chunk-to-chunk
+ * recurrence of the "Mamba 模型" page, section 4.1, run within the
+ * workgroup), so x is read from memory once. `chunk` must still be valid but
+ * does not set that kernel's block length.
  *   D           nullable: no feed-through term.
  *   init_state  nullable: the state before token 0 is zero.
  *   y           output, [Bt][L][H][P] in dtype.
@@ -161,7 +170,9 @@ int ssd_forward_ex(const void *x, const void *dt, const float *A, const void *B,
  * events[5] after the last stage, so the
  * elapsed time between consecutive events is each stage's GPU time (stages in
  * the order listed for ssd_forward; for SSD_BF16 the ssd_chunk_cb interval is
- * empty, that work being part of ssd_chunk_scan).
+ * empty, that work being part of ssd_chunk_scan). When the forward runs as the
+ * single-pass kernel (see ssd_forward), events[0] is recorded before it and
+ * events[1..5] after it: its time is the first interval.
  */
 int ssd_forward_timed(const void *x, const void *dt, const float *A, const void *B,
                       const void *C, const float *D, int batch, int seqlen, int nheads,

@@ -150,23 +150,9 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(
 // loading everything and then computing. The token weights w_j are applied to
 // the x^T operand fragments (8 multiplies per fragment, shared by the
 // wavefront's N tiles), so x and B land in LDS exactly as stored. Both tiles
-// are read with the transposing LDS read (contraction index = token = row).
-template <int PPR>
-__device__ __forceinline__ void colfrag_swz(Frag<bf16_t> &f, const __bf16 *m, int r1, int r2,
-                                            int cb) {
-    const int s = lane_id() & 15;
-    const int col = cb + 4 * (s & 3);
-    const int ra = r1 + (s >> 2), rb = r2 + (s >> 2);
-    const int pa = ((col >> 3) ^ tr_swz<PPR>(ra)) << 3, pb = ((col >> 3) ^ tr_swz<PPR>(rb)) << 3;
-    const shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_shortx4 *)(m + ra * (PPR * 8) + pa + (col & 7)));
-    const shortx4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_shortx4 *)(m + rb * (PPR * 8) + pb + (col & 7)));
-    const bf16x4 ab = __builtin_bit_cast(bf16x4, a);
-    const bf16x4 bb = __builtin_bit_cast(bf16x4, b);
-    f.v = bf16x8{ab[0], ab[1], ab[2], ab[3], bb[0], bb[1], bb[2], bb[3]};
-}
-
+// are read with the transposing LDS read (colfrag_swz; contraction index =
+// token = row).
+//
 // FIN (packed sequences): one workgroup per (sequence k, head) forms the
 // sequence's final state instead: the chunk c holding its last token te is
 // cut after te (len = te - cQ + 1, so s_end = s_te), its tokens before the

@@ -301,4 +301,50 @@ __device__ __forceinline__ int tr_swz(int r) {
     else return (r & 7) << 1;
 }
 
+// Transposing read of a bf16 LDS matrix of PPR 16-byte pieces per row stored
+// with the tr_swz<PPR> piece swizzle: lds_colfrag's result (column cb + c at
+// rows r1 + 0..3 and r2 + 0..3 for lane 16*g + c).
+template <int PPR>
+__device__ __forceinline__ void colfrag_swz(Frag<bf16_t> &f, const __bf16 *m, int r1, int r2,
+                                            int cb) {
+    const int s = lane_id() & 15;
+    const int col = cb + 4 * (s & 3);
+    const int ra = r1 + (s >> 2), rb = r2 + (s >> 2);
+    const int pa = ((col >> 3) ^ tr_swz<PPR>(ra)) << 3, pb = ((col >> 3) ^ tr_swz<PPR>(rb)) << 3;
+    const shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_shortx4 *)(m + ra * (PPR * 8) + pa + (col & 7)));
+    const shortx4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_shortx4 *)(m + rb * (PPR * 8) + pb + (col & 7)));
+    const bf16x4 ab = __builtin_bit_cast(bf16x4, a);
+    const bf16x4 bb = __builtin_bit_cast(bf16x4, b);
+    f.v = bf16x8{ab[0], ab[1], ab[2], ab[3], bb[0], bb[1], bb[2], bb[3]};
+}
+
+// Transposing reads of the swizzled x tile. Lane 16*g + s of a fragment for
+// head-dim columns 16*pt + 0..15 reads row 32*jp + 4*g + s/4 (+16 for the
+// second half) at column 16*pt + 4*(s%4); since 32*jp and 16 are multiples of
+// 8, the swizzle term r & 7 = (4*g + s/4) & 7 is the same for every slice, and
+// the element offset splits into a per-lane part, 16 * (pt ^ zt) with a
+// per-lane zt, and compile-time multiples of 2048 (jp) and 1024 (second half).
+__device__ __forceinline__ void x_colfrag_offsets(int (&xo)[4], int l) {
+    const int s = l & 15, g = l >> 4;
+    const int r = 4 * g + (s >> 2);
+    const int z = r & 7;
+    const int base = r * 64 + 8 * (((s >> 1) & 1) ^ (z & 1)) + 4 * (s & 1);
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) xo[pt] = base + 16 * (pt ^ (z >> 1));
+}
+
+// x^T operand fragment: lane 16*g + c receives x[32*jp + 4*g + 0..3][16*pt + c]
+// (elements 0..3) and x[32*jp + 16 + 4*g + 0..3][16*pt + c] (elements 4..7).
+template <int JP>
+__device__ __forceinline__ void x_colfrag(Frag<bf16_t> &f, const __bf16 *xs, int xo) {
+    const shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(xs + xo + JP * 2048));
+    const shortx4 b =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(xs + xo + JP * 2048 + 1024));
+    const bf16x4 ab = __builtin_bit_cast(bf16x4, a);
+    const bf16x4 bb = __builtin_bit_cast(bf16x4, b);
+    f.v = bf16x8{ab[0], ab[1], ab[2], ab[3], bb[0], bb[1], bb[2], bb[3]};
+}
+
 }  // namespace ssd

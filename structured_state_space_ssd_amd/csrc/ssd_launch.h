@@ -43,6 +43,13 @@ hipError_t launch_chunk_state(const void *x, const void *B, const float *delta,
 // Stages 2 and 3 in one kernel (bf16 only; used when state_passing_fused()):
 // writes chunk_init (bf16) and final_state (nullable) directly, without the
 // per-chunk float32 states. Reads dA_cumsum and delta (stage 1's outputs).
+// The single-pass bf16 forward (fwd_onepass.hip): whether it applies, and the launch.
+bool forward_onepass_ok(int batch, int nheads, int dstate, bool bf16, const void *dt);
+hipError_t launch_forward_onepass(const void *x, const void *dt, const float *A, const void *B,
+                                  const void *C, const float *D, const float *init,
+                                  const DtOpts &opts, int batch, int seqlen, int nheads,
+                                  int ngroups, int dstate, void *y, float *final_state,
+                                  hipStream_t stream);
 bool state_passing_fused(int batch, int nheads, bool bf16);
 hipError_t launch_chunk_state_passing(const void *x, const void *B, const float *dA_cumsum,
                                       const float *delta, const float *init, int batch,

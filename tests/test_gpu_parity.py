@@ -173,7 +173,9 @@ def test_slow_decay_long():
 # With enough (batch, head) units the bf16 forward runs the chunk states and
 # the state passing as one kernel per (batch, head); these cases reach it at
 # sizes the oracle finishes quickly, with ragged ends, an initial state,
-# several groups and every state size and chunk length.
+# several groups and every state size and chunk length. (With N = 64 and a
+# multiple of 8 heads the whole forward runs as the single-pass kernel
+# instead: see the next section.)
 
 @pytest.mark.parametrize("N,Q", [(16, 64), (32, 128), (64, 256), (128, 128), (256, 64), (64, 64),
                                  (128, 256)])
@@ -187,6 +189,43 @@ def test_fused_state_path(N, Q):
 def test_fused_state_path_single_chunk_short():
     # one partial chunk only: the state passing reduces to H_1 = exp(s_end) H_0 + S_0
     check_forward(W.small("fused_short", 16, 37, 32, 64, 1, 64, 256, "bf16", seed=620, init_std=0.3))
+
+
+# ------------------------------------------- single-pass forward (bf16, N = 64, Bt*H >= 512)
+#
+# One workgroup per (batch, head) walks the sequence in 64-token blocks with
+# the state in registers. Cases: a single token, one partial block, exactly
+# one block, one block plus one token, several blocks with a ragged end; an
+# initial state; several groups; every chunk argument (it does not change the
+# kernel's blocks, only the rounding order against the oracle).
+
+@pytest.mark.parametrize("L", [1, 37, 64, 65, 200, 1000])
+def test_onepass_lengths(L):
+    w = W.small(f"onepass_L{L}", 8, L, 64, 64, 4, 64, 256, "bf16", seed=800 + L, init_std=0.2)
+    assert w.batch * w.nheads >= 512
+    check_forward(w)
+
+
+@pytest.mark.parametrize("Q", [64, 128])
+def test_onepass_chunk_argument(Q):
+    w = W.small(f"onepass_Q{Q}", 4, 3 * Q + 11, 128, 64, 1, 64, Q, "bf16", seed=810 + Q)
+    check_forward(w)
+
+
+def test_onepass_groups_no_init():
+    check_forward(W.small("onepass_g8", 2, 333, 256, 64, 8, 64, 256, "bf16", seed=820))
+
+
+@pytest.mark.parametrize("name", ["all_zoh", "softplus_bias", "softplus_bias_clamp", "zoh"])
+def test_onepass_options(name):
+    w = W.small(f"onepass_opt_{name}", 8, 2 * 64 + 29, 64, 64, 2, 64, 256, "bf16", seed=830,
+                init_std=0.2)
+    check_forward(w, **OPTION_SETS[name])
+
+
+def test_heads_not_multiple_of_8_many_units():
+    # 9 x 60 units but 60 heads: the separate-stage path (its fused state kernel)
+    check_forward(W.small("h60", 9, 300, 60, 64, 3, 64, 128, "bf16", seed=840, init_std=0.2))
 
 
 # ------------------------------------ step-size preprocessing and zero-order hold
