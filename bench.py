@@ -190,6 +190,19 @@ def upload(d):
     return out
 
 
+def spin_up(call, seconds=0.15):
+    """Back-to-back calls for about `seconds`, untimed: the GPU raises its
+    clocks only under sustained load (the first tens of milliseconds run up to
+    20% slower), so every timed region starts with the clocks up."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+
+
 def time_forward(w, steps, warmup, breakdown_steps=10, event_every=5, spin_seconds=0.15):
     """Two passes over the same resident inputs.
 
@@ -217,15 +230,8 @@ def time_forward(w, steps, warmup, breakdown_steps=10, event_every=5, spin_secon
     mk = lambda: torch.cuda.Event(enable_timing=True)
     pad = lambda evs: list(evs) + [None] * (len(STAGES) + 1 - len(evs))
 
-    # ---- spin-up: the GPU raises its clocks only under sustained load (the
-    # first tens of milliseconds of back-to-back forwards run up to 20% slower),
-    # so about 0.1 s of untimed forwards come before anything is measured
-    torch.cuda.synchronize()
-    t_spin = time.perf_counter()
-    while time.perf_counter() - t_spin < spin_seconds:
-        for _ in range(20):
-            ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y)
-        torch.cuda.synchronize()
+    # ---- spin-up (see spin_up) before anything is measured
+    spin_up(lambda: ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y), spin_seconds)
 
     # ---- breakdown pass
     bd = [[mk() for _ in range(ns + 1)] for _ in range(breakdown_steps)]
@@ -261,8 +267,8 @@ def time_forward(w, steps, warmup, breakdown_steps=10, event_every=5, spin_secon
 
 
 def time_forward_options(w, steps, warmup):
-    """Whole-forward time (host clock, no events) with every step-size option
-    on: per-head bias, softplus, clamp to [4e-3, 3e-2] and the zero-order-hold
+    """Whole-forward time (host clock, no events, after spin_up) with every
+    step-size option on: per-head bias, softplus, clamp to [4e-3, 3e-2] and the zero-order-hold
     input weight, on the same shapes (raw dt from generate_dt_raw)."""
     import torch
     import ssd_workloads as W
@@ -279,6 +285,7 @@ def time_forward_options(w, steps, warmup):
     kw = dict(chunk=w.chunk, workspace=ws, y=y, dt_bias=g["dt_bias"], dt_softplus=True,
               dt_limit=(4e-3, 3e-2), zoh=True)
     args = [g[k] for k in ("x", "dt", "A", "B", "C", "D")]
+    spin_up(lambda: ssd.forward(*args, **kw))
     for _ in range(warmup):
         ssd.forward(*args, **kw)
     torch.cuda.synchronize()
@@ -315,6 +322,7 @@ def time_forward_varlen(steps, warmup):
     y = torch.empty_like(x)
     args = [g[k] for k in ("x", "dt", "A", "B", "C", "D")] + [cu_g]
     kw = dict(chunk=w.chunk, workspace=ws, y=y, return_seq_states=True)
+    spin_up(lambda: ssd.forward_varlen(*args, **kw))
     for _ in range(warmup):
         ssd.forward_varlen(*args, **kw)
     torch.cuda.synchronize()
@@ -341,6 +349,7 @@ def time_backward(w, steps, warmup):
         dtype=torch.uint8, device="cuda")
     args = [g[k] for k in ("x", "dt", "A", "B", "C", "D", "dy")]
     kw = dict(init_state=g["init"], dfinal_state=g["dfinal"], workspace=ws)
+    spin_up(lambda: ssd.backward(*args, **kw))
     for _ in range(warmup):
         ssd.backward(*args, **kw)
     torch.cuda.synchronize()

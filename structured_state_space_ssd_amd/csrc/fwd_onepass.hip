@@ -25,21 +25,24 @@
 // x^T operand fragments. The block's x rows (triple-buffered), B and C rows
 // (single-buffered: they are shared by all heads of a group and come from
 // L2), and the 8-head piece of dt holding this head's values arrive by direct
-// global-to-LDS loads; x is two blocks ahead, B, C and dt one. The masked
+// global-to-LDS loads; x and dt are two blocks ahead, B and C one. The masked
 // C B^T products of a block (6 tiles of 16 x 32) are formed once per block,
 // spread over the wavefronts, and shared through LDS.
 //
 // Per block, per wavefront:
-//   tables    s * log2(e), w and exp(s_end - s_j) w_j for the 64 tokens, one
-//             token per lane (wave-wide prefix sum), in the wavefront's own
-//             LDS table (no barrier);
+//   tables    s * log2(e), w and exp(s_end - s_j) w_j for the 64 tokens
+//             (step sizes with bias, softplus, clamp; zero-order-hold weights;
+//             one token per lane, wave-wide prefix sum): made once, by
+//             wavefront 3, during the block before, into one of two LDS
+//             tables that the barriers of that block publish;
 //   C H       Y^T = H (C_i)^T on MFMA (A operand straight from the state
 //             registers), scaled per token by exp(s_i);
 //   C B^T     this wavefront's causal tiles, times exp(s_i - s_j) w_j, masked
 //             j <= i, rounded to bf16 into LDS;
 //   state     H^T = exp(s_end) H^T + B^T (w' o x) on MFMA;
 //   -- barrier: tiles visible; B, C, dt buffers free: next loads issued --
-//   diagonal  Y^T += X^T M^T over the 6 tiles; D x;
+//   diagonal  Y^T += X^T M^T over the 6 tiles; D x as X^T diag(D) (D split
+//             into two bf16 parts) on the diagonal slices;
 //   outputs   staged in the block's x buffer (only this wavefront's columns,
 //             which only it reads), then -- barrier -- whole 128-byte rows
 //             out with non-temporal stores.
@@ -52,20 +55,67 @@ namespace {
 
 constexpr int kOpT = 64;  // tokens per block
 
-// causal tiles of a block: (row tile it of 16 outputs, slice js of 32 inputs)
+// Causal 16 x 32 tiles of a block, u -> (row tile it of 16 outputs, slice js
+// of 32 inputs). u = 0..3 hold the diagonal (it = u, js = u / 2) and are
+// formed by wavefront u; u = 4, 5 lie wholly below it (it = 2, 3, js = 0) and
+// are formed by wavefronts 0 and 1, whose diagonal tiles are the smaller ones.
 __device__ __forceinline__ int op_tile_it(int u) { return u < 4 ? u : u - 2; }
-__device__ __forceinline__ int op_tile_js(int u) { return u < 4 ? 0 : 1; }
+__device__ __forceinline__ int op_tile_js(int u) { return u < 4 ? u >> 1 : 0; }
 
 template <int N>
 struct OnepassLds {
-    static constexpr int PPR = N / 8;  // 16-byte pieces per B / C row
     __bf16 xb[3][kOpT * 64];
     __bf16 bb[kOpT * N];
     __bf16 cs[kOpT * N];
-    __bf16 m[6 * 512];                // masked, weighted C B^T tiles, fragment order
-    __bf16 dts[kOpT * 8];             // dt pieces: token j's 8 heads around this head
-    float sl[4][kOpT], wt[4][kOpT], wp[4][kOpT];  // per-wavefront tables
+    __bf16 m[6 * 512];     // masked, weighted C B^T tiles, fragment order
+    __bf16 dts[2][kOpT * 8];  // dt pieces of blocks k, k+1: token j's 8 heads around this head
+    // tables of blocks k, k+1: s * log2(e), w, exp(s_end - s_j) w_j, and for
+    // the first 32 tokens exp(s_31 - s_j) w_j (column factor below the diagonal)
+    struct {
+        float sl[kOpT], wt[kOpT], wp[kOpT], cf[32];
+    } tab[2];
 };
+
+// One 16-byte-per-lane global-to-LDS load from the wave-uniform base `sbase`
+// plus this lane's byte offset `voff` (lane l's 16 bytes land at lds_base +
+// 16 l): the scalar-base form, so a block's loads cost no per-lane 64-bit
+// address arithmetic.
+__device__ __forceinline__ void dma16_sv(const void *sbase, uint32_t voff, const void *lds_base) {
+    const uint32_t a =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)lds_base);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(a)
+                 : "memory", "m0");
+}
+
+// Inclusive prefix sum over the 64 lanes: shifts within rows of 16 lanes,
+// then row totals broadcast forward (DPP; no LDS round trips).
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
+    return v;
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Eight floats -> one bf16 operand fragment (round to nearest even, in pairs).
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void pack8(Frag<bf16_t> &f, const float (&v)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const bf16x2 p = __builtin_convertvector(floatx2{v[e], v[e + 1]}, bf16x2);
+        f.v[e] = p[0];
+        f.v[e + 1] = p[1];
+    }
+}
 
 }  // namespace
 
@@ -102,29 +152,52 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
     const float Dh = D ? D[h] : 0.0f;
     const float bias = o.bias ? o.bias[h] : 0.0f;
 
-    // ---- direct loads (16 bytes per lane; rows past the end re-read row L-1)
-    auto issue_x = [&](int k) {
-        const int t0 = k * T;
-        __bf16 *dst = sm.xb[k % 3];
-#pragma unroll
-        for (int i = w; i < 8; i += 4) {
-            const int s = i * 64 + l, r = s >> 3, q = (s & 7) ^ (r & 7);
-            dma16(xh + (size_t)min(t0 + r, L - 1) * xrow + q * 8, dst + i * 512);
-        }
+    // ---- direct loads: scalar base at the block's first token, per-lane byte
+    // offsets of whole 16-byte pieces (rows past the end re-read the last row)
+    const uint32_t xrb = (uint32_t)(xrow * 2), brb = (uint32_t)(brow * 2), drb = (uint32_t)H * 2;
+    auto x_off = [&](int i, int len) {
+        const int s = i * 64 + l, r = s >> 3, q = (s & 7) ^ (r & 7);
+        return (uint32_t)min(r, len - 1) * xrb + q * 16;
     };
+    auto bc_off = [&](int i, int len) {
+        const int s = i * 64 + l, r = s / PPR, q = (s % PPR) ^ tr_swz<PPR>(r);
+        return (uint32_t)min(r, len - 1) * brb + q * 16;
+    };
+    auto issue_x = [&](int k) {
+        const int t0 = k * T, len = min(T, L - t0);
+        const bf16_t *base = xh + (size_t)t0 * xrow;
+#pragma unroll
+        for (int i = w; i < 8; i += 4) dma16_sv(base, x_off(i, len), sm.xb[k % 3] + i * 512);
+    };
+    auto issue_dt = [&](int k) {  // wavefront 0 only
+        const int t0 = k * T, len = min(T, L - t0);
+        dma16_sv(dth + (size_t)t0 * H, (uint32_t)min(l, len - 1) * drb, sm.dts[k & 1]);
+    };
+    // B and C of block k, after dt of block k+1 (so that waiting for block k's
+    // B and C also brings the dt the next block's step sizes are made from)
     auto issue_bcd = [&](int k) {
-        const int t0 = k * T;
+        const int t0 = k * T, len = min(T, L - t0);
+        if (w == 0 && k + 1 < nblk) issue_dt(k + 1);
+        const bf16_t *bb_ = bg + (size_t)t0 * brow, *cb_ = cg + (size_t)t0 * brow;
 #pragma unroll
-        for (int i = w; i < T * PPR / 64; i += 4) {
-            const int s = i * 64 + l, r = s / PPR, q = (s % PPR) ^ tr_swz<PPR>(r);
-            dma16(bg + (size_t)min(t0 + r, L - 1) * brow + q * 8, sm.bb + i * 512);
-        }
+        for (int i = w; i < T * PPR / 64; i += 4) dma16_sv(bb_, bc_off(i, len), sm.bb + i * 512);
 #pragma unroll
-        for (int i = w; i < T * PPR / 64; i += 4) {
-            const int s = i * 64 + l, r = s / PPR, q = (s % PPR) ^ tr_swz<PPR>(r);
-            dma16(cg + (size_t)min(t0 + r, L - 1) * brow + q * 8, sm.cs + i * 512);
-        }
-        if (w == 0) dma16(dth + (size_t)min(t0 + l, L - 1) * H, sm.dts);
+        for (int i = w; i < T * PPR / 64; i += 4) dma16_sv(cb_, bc_off(i, len), sm.cs + i * 512);
+    };
+    // block k's tables from its dt piece (one wavefront; lane j is token t0 + j)
+    auto make_tables = [&](int k) {
+        const int len = min(T, L - k * T);
+        const bool valid = l < len;
+        const float raw = static_cast<float>(sm.dts[k & 1][l * 8 + (h & 7)]);
+        const float st = valid ? step_size(o, raw, bias) : 0.0f;
+        const float wgt = valid ? input_weight(o, st, Ah) : 0.0f;
+        const float sl = wave_prefix_sum(st * Ah) * kLog2e;
+        const float sle = lane_value(sl, 63), s31 = lane_value(sl, 31);
+        auto &t = sm.tab[k & 1];
+        t.sl[l] = sl;
+        t.wt[l] = wgt;
+        t.wp[l] = __builtin_amdgcn_exp2f(sle - sl) * wgt;
+        if (l < 32) t.cf[l] = __builtin_amdgcn_exp2f(s31 - sl) * wgt;
     };
 
     // the state H^T: lane (g4, cc) of wavefront w holds rows n = 16 nt + 4 g4 + r
@@ -141,12 +214,33 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
     }
 
     issue_x(0);
+    if (w == 0) issue_dt(0);
     issue_bcd(0);
     if (nblk > 1) issue_x(1);
 
     int xo[4];
     x_colfrag_offsets(xo, l);
-    float *tsl = sm.sl[w], *twt = sm.wt[w], *twp = sm.wp[w];
+
+    // D x on MFMA: Y^T += X^T diag(D) over the slice holding each row tile's
+    // diagonal, with D split as D_hi + D_lo (bf16 each, 16 mantissa bits in
+    // all; both products exact in float32). B-operand lane (g4, cc) is column
+    // i = 16 it + cc; its element e is token 32 js + 4 g4 + e (e < 4) or
+    // 32 js + 16 + 4 g4 + e - 4, which is i for element cc - 4 g4 (it even)
+    // or 4 + cc - 4 g4 (it odd) when 0 <= cc - 4 g4 < 4.
+    Frag<bf16_t> dfr[2][2];  // [it & 1][hi, lo]
+    {
+        const __bf16 dhi = static_cast<__bf16>(Dh);
+        const __bf16 dlo = static_cast<__bf16>(Dh - static_cast<float>(dhi));
+        const int e0 = cc - 4 * g4;
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const bool on = e == (par ? 4 + e0 : e0) && e0 >= 0 && e0 < 4;
+                dfr[par][0].v[e] = on ? dhi : static_cast<__bf16>(0.0f);
+                dfr[par][1].v[e] = on ? dlo : static_cast<__bf16>(0.0f);
+            }
+    }
 
     for (int k = 0; k < nblk; ++k) {
         const int t0 = k * T, len = min(T, L - t0);
@@ -162,39 +256,28 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
             wait_barrier<2>();
         }
         const __bf16 *xs = sm.xb[k % 3];
-
-        // ---- tables: lane j is token t0 + j
-        float sle, dec;
-        {
-            const bool valid = l < len;
-            const float raw = static_cast<float>(sm.dts[l * 8 + (h & 7)]);
-            const float st = valid ? step_size(o, raw, bias) : 0.0f;
-            float s = st * Ah;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const float v = __shfl_up(s, d);
-                if (l >= d) s += v;
-            }
-            const float wgt = valid ? input_weight(o, st, Ah) : 0.0f;
-            const float sl = s * kLog2e;
-            sle = __shfl(sl, 63);
-            dec = __builtin_amdgcn_exp2f(sle);
-            tsl[l] = sl;
-            twt[l] = wgt;
-            twp[l] = __builtin_amdgcn_exp2f(sle - sl) * wgt;
+        if (k == 0) {  // later blocks' tables are made during the block before
+            if (w == 3) make_tables(0);
+            barrier_lds();
         }
+        const float *tsl = sm.tab[k & 1].sl, *twt = sm.tab[k & 1].wt, *twp = sm.tab[k & 1].wp,
+                    *tcf = sm.tab[k & 1].cf;
 
-        // ---- state to output: Y^T[p][i] = sum_n H[p][n] C_i[n], times exp(s_i)
+        // ---- state to output: Y^T[p][i] = sum_n H[p][n] C_i[n] (scaled by
+        // exp(s_i) once the tables exist); issued first, to overlap the tables
         floatx4 acc[4];
         {
             Frag<bf16_t> hf[NK];
 #pragma unroll
-            for (int kk = 0; kk < NK; ++kk)
+            for (int kk = 0; kk < NK; ++kk) {
+                float v[8];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    hf[kk].set(r, hreg[2 * kk][r]);
-                    hf[kk].set(4 + r, hreg[2 * kk + 1][r]);
+                    v[r] = hreg[2 * kk][r];
+                    v[4 + r] = hreg[2 * kk + 1][r];
                 }
+                pack8(hf[kk], v);
+            }
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
                 const int i = 16 * it + cc;
@@ -209,13 +292,18 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
                                 sm.cs + i * N + ((q1 ^ sw) << 3) + (n0 & 7));
                     mma(acc[it], hf[kk], cf);
                 }
-                const float e = __builtin_amdgcn_exp2f(tsl[i]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[it][r] *= e;
             }
         }
 
-        // ---- causal C B^T tiles u = w and w + 4: M[i][j] = (C_i . B_j) exp(s_i - s_j) w_j, j <= i
+        const float dec = __builtin_amdgcn_exp2f(tsl[T - 1]), s31 = tsl[31];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const float e = __builtin_amdgcn_exp2f(tsl[16 * it + cc]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[it][r] *= e;
+        }
+
+        // ---- causal C B^T tiles: M[i][j] = (C_i . B_j) exp(s_i - s_j) w_j, j <= i
 #pragma unroll
         for (int u = w; u < 6; u += 4) {
             const int it = op_tile_it(u), js = op_tile_js(u);
@@ -236,19 +324,35 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
             }
             // lane (g4, cc): rows j = 32 js + 16 half + 4 g4 + r of column i
             const int j0 = 32 * js + 4 * g4;
-            const float si = tsl[i];
-            const floatx4 s0 = *reinterpret_cast<const floatx4 *>(tsl + j0);
-            const floatx4 s1 = *reinterpret_cast<const floatx4 *>(tsl + j0 + 16);
-            const floatx4 w0 = *reinterpret_cast<const floatx4 *>(twt + j0);
-            const floatx4 w1 = *reinterpret_cast<const floatx4 *>(twt + j0 + 16);
-            Frag<bf16_t> mf;
+            float v[8];
+            if (u < 4) {
+                // holds the diagonal: exp per element, causal mask
+                const float si = tsl[i];
+                const floatx4 s0 = *reinterpret_cast<const floatx4 *>(tsl + j0);
+                const floatx4 s1 = *reinterpret_cast<const floatx4 *>(tsl + j0 + 16);
+                const floatx4 w0 = *reinterpret_cast<const floatx4 *>(twt + j0);
+                const floatx4 w1 = *reinterpret_cast<const floatx4 *>(twt + j0 + 16);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float v0 = m[0][r] * (__builtin_amdgcn_exp2f(si - s0[r]) * w0[r]);
-                const float v1 = m[1][r] * (__builtin_amdgcn_exp2f(si - s1[r]) * w1[r]);
-                mf.set(r, j0 + r <= i ? v0 : 0.0f);
-                mf.set(4 + r, j0 + 16 + r <= i ? v1 : 0.0f);
+                for (int r = 0; r < 4; ++r) {
+                    const float a0 = m[0][r] * (__builtin_amdgcn_exp2f(si - s0[r]) * w0[r]);
+                    const float a1 = m[1][r] * (__builtin_amdgcn_exp2f(si - s1[r]) * w1[r]);
+                    v[r] = j0 + r <= i ? a0 : 0.0f;
+                    v[4 + r] = j0 + 16 + r <= i ? a1 : 0.0f;
+                }
+            } else {
+                // wholly below it (i >= 32 > j): exp(s_i - s_31) exp(s_31 - s_j) w_j,
+                // both factors <= 1, no mask
+                const float rowf = __builtin_amdgcn_exp2f(tsl[i] - s31);
+                const floatx4 c0 = *reinterpret_cast<const floatx4 *>(tcf + j0);
+                const floatx4 c1 = *reinterpret_cast<const floatx4 *>(tcf + j0 + 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    v[r] = m[0][r] * (c0[r] * rowf);
+                    v[4 + r] = m[1][r] * (c1[r] * rowf);
+                }
             }
+            Frag<bf16_t> mf;
+            pack8(mf, v);
             store_frag8(sm.m + u * 512 + l * 8, mf);
         }
 
@@ -265,12 +369,14 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
             const int jb = 32 * js + 4 * g4;
             const floatx4 p0 = *reinterpret_cast<const floatx4 *>(twp + jb);
             const floatx4 p1 = *reinterpret_cast<const floatx4 *>(twp + jb + 16);
-            Frag<bf16_t> xw;
+            float v[8];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                xw.set(r, xr[js].get(r) * p0[r]);
-                xw.set(4 + r, xr[js].get(4 + r) * p1[r]);
+                v[r] = xr[js].get(r) * p0[r];
+                v[4 + r] = xr[js].get(4 + r) * p1[r];
             }
+            Frag<bf16_t> xw;
+            pack8(xw, v);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 Frag<bf16_t> bf;
@@ -279,29 +385,37 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
             }
         }
 
-        // tiles complete; B, C and dt of this block consumed by every wavefront
+        // the next block's tables, by the wavefront with the least tile work
+        if (w == 3 && k + 1 < nblk) make_tables(k + 1);
+
+        // tiles complete; B, C and the dt pieces read by every wavefront
         barrier_lds();
         if (k + 1 < nblk) issue_bcd(k + 1);
         if (k + 2 < nblk) issue_x(k + 2);
 
-        // ---- diagonal blocks: Y^T[p][i] += sum_j x_j[p] M[i][j]
+        // ---- diagonal blocks: Y^T[p][i] += sum_j x_j[p] M[i][j], and D x
 #pragma unroll
         for (int u = 0; u < 6; ++u) {
             Frag<bf16_t> mf;
             load_frag8(mf, sm.m + u * 512 + l * 8);
             mma(acc[op_tile_it(u)], xr[op_tile_js(u)], mf);
         }
+        if (D) {  // uniform
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                mma(acc[it], xr[it >> 1], dfr[it & 1][0]);
+                mma(acc[it], xr[it >> 1], dfr[it & 1][1]);
+            }
+        }
 
-        // ---- D x, then the outputs into this wavefront's columns of the x buffer
+        // ---- the outputs into this wavefront's columns of the x buffer
         __bf16 *xw_ = sm.xb[k % 3];
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            const int i = 16 * it + cc, off = x_at(i, 16 * w + 4 * g4);
-            const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xs + off);
-            bf16x4 yv;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) yv[r] = static_cast<__bf16>(acc[it][r] + Dh * static_cast<float>(xv[r]));
-            *reinterpret_cast<bf16x4 *>(xw_ + off) = yv;
+            const int off = x_at(16 * it + cc, 16 * w + 4 * g4);
+            const bf16x2 lo = __builtin_convertvector(floatx2{acc[it][0], acc[it][1]}, bf16x2);
+            const bf16x2 hi = __builtin_convertvector(floatx2{acc[it][2], acc[it][3]}, bf16x2);
+            *reinterpret_cast<bf16x4 *>(xw_ + off) = bf16x4{lo[0], lo[1], hi[0], hi[1]};
         }
         barrier_lds();  // every wavefront's columns staged
 #pragma unroll
