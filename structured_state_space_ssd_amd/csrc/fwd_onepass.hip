@@ -22,10 +22,15 @@
 // of everything per-p: the state H^T[n][p] (float32, in the MFMA accumulator
 // layout, which is also the operand layout the state-to-output product
 // needs, so the state never goes through LDS), the outputs Y^T[p][i] and the
-// x^T operand fragments. The block's x rows (triple-buffered), B and C rows
+// x^T operand fragments. The block's x rows (double-buffered), B and C rows
 // (single-buffered: they are shared by all heads of a group and come from
 // L2), and the 8-head piece of dt holding this head's values arrive by direct
-// global-to-LDS loads; x and dt are two blocks ahead, B and C one. The masked
+// global-to-LDS loads: x one block ahead (issued as the block starts), dt two,
+// B and C one (issued mid-block, once the current ones are consumed). Memory
+// instructions are spread over the block (x at its start, the previous
+// block's two output stores after the first products, B / C / dt after the
+// middle barrier): issued in one burst they queue in the address unit and
+// stall every wavefront behind them. The masked
 // C B^T products of a block (6 tiles of 16 x 32) are formed once per block,
 // spread over the wavefronts, and shared through LDS.
 //
@@ -45,7 +50,7 @@
 //             into two bf16 parts) on the diagonal slices;
 //   outputs   staged in the block's x buffer (only this wavefront's columns,
 //             which only it reads), then -- barrier -- whole 128-byte rows
-//             out with non-temporal stores.
+//             into registers, stored (non-temporal) during the next block.
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -64,7 +69,7 @@ __device__ __forceinline__ int op_tile_js(int u) { return u < 4 ? u >> 1 : 0; }
 
 template <int N>
 struct OnepassLds {
-    __bf16 xb[3][kOpT * 64];
+    __bf16 xb[2][kOpT * 64];
     __bf16 bb[kOpT * N];
     __bf16 cs[kOpT * N];
     __bf16 m[6 * 512];     // masked, weighted C B^T tiles, fragment order
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
         const int t0 = k * T, len = min(T, L - t0);
         const bf16_t *base = xh + (size_t)t0 * xrow;
 #pragma unroll
-        for (int i = w; i < 8; i += 4) dma16_sv(base, x_off(i, len), sm.xb[k % 3] + i * 512);
+        for (int i = w; i < 8; i += 4) dma16_sv(base, x_off(i, len), sm.xb[k & 1] + i * 512);
     };
     auto issue_dt = [&](int k) {  // wavefront 0 only
         const int t0 = k * T, len = min(T, L - t0);
@@ -216,7 +221,6 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
     issue_x(0);
     if (w == 0) issue_dt(0);
     issue_bcd(0);
-    if (nblk > 1) issue_x(1);
 
     int xo[4];
     x_colfrag_offsets(xo, l);
@@ -242,20 +246,16 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
             }
     }
 
+    uint4 ystage[2];  // this lane's two 16-byte pieces of the previous block's outputs
     for (int k = 0; k < nblk; ++k) {
         const int t0 = k * T, len = min(T, L - t0);
-        // block k's x, B, C and dt are in LDS. Still in flight (most recent
-        // first): block k-1's output stores (2, full blocks) and x of block k+1
-        // (2, if there is one), issued after them
-        if (k == 0) {
-            if (nblk > 1) wait_barrier<2>();
-            else wait_barrier<0>();
-        } else if (k + 1 < nblk) {
-            wait_barrier<4>();
-        } else {
-            wait_barrier<2>();
-        }
-        const __bf16 *xs = sm.xb[k % 3];
+        // every load issued so far has landed (block k's x, B, C, this and
+        // the next block's dt) and every store has left; every wavefront has
+        // read the previous block's staged outputs out of x buffer (k+1) & 1,
+        // which now takes block k+1's x
+        wait_barrier<0>();
+        if (k + 1 < nblk) issue_x(k + 1);
+        const __bf16 *xs = sm.xb[k & 1];
         if (k == 0) {  // later blocks' tables are made during the block before
             if (w == 3) make_tables(0);
             barrier_lds();
@@ -301,6 +301,16 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
             const float e = __builtin_amdgcn_exp2f(tsl[16 * it + cc]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[it][r] *= e;
+        }
+
+        // ---- the previous block's outputs leave here, between compute phases
+        // (a full block: every row is in range)
+        if (k > 0) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int s = (w + 4 * m) * 64 + l, r = s >> 3, q = (s & 7) ^ (r & 7);
+                store_nt16(yh + (size_t)(t0 - T + r) * xrow + q * 8, ystage[m]);
+            }
         }
 
         // ---- causal C B^T tiles: M[i][j] = (C_i . B_j) exp(s_i - s_j) w_j, j <= i
@@ -391,7 +401,6 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
         // tiles complete; B, C and the dt pieces read by every wavefront
         barrier_lds();
         if (k + 1 < nblk) issue_bcd(k + 1);
-        if (k + 2 < nblk) issue_x(k + 2);
 
         // ---- diagonal blocks: Y^T[p][i] += sum_j x_j[p] M[i][j], and D x
 #pragma unroll
@@ -409,7 +418,7 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
         }
 
         // ---- the outputs into this wavefront's columns of the x buffer
-        __bf16 *xw_ = sm.xb[k % 3];
+        __bf16 *xw_ = sm.xb[k & 1];
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int off = x_at(16 * it + cc, 16 * w + 4 * g4);
@@ -418,11 +427,17 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
             *reinterpret_cast<bf16x4 *>(xw_ + off) = bf16x4{lo[0], lo[1], hi[0], hi[1]};
         }
         barrier_lds();  // every wavefront's columns staged
+        // whole rows into registers; stored during the next block
 #pragma unroll
-        for (int i = w; i < 8; i += 4) {
-            const int s = i * 64 + l, r = s >> 3, q = (s & 7) ^ (r & 7);
-            const uint4 v = *reinterpret_cast<const uint4 *>(xs + s * 8);
-            if (r < len) store_nt16(yh + (size_t)(t0 + r) * xrow + q * 8, v);
+        for (int m = 0; m < 2; ++m)
+            ystage[m] = *reinterpret_cast<const uint4 *>(xs + ((w + 4 * m) * 64 + l) * 8);
+    }
+    {  // the last block's outputs (possibly a partial block)
+        const int t0 = (nblk - 1) * T, len = L - t0;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int s = (w + 4 * m) * 64 + l, r = s >> 3, q = (s & 7) ^ (r & 7);
+            if (r < len) store_nt16(yh + (size_t)(t0 + r) * xrow + q * 8, ystage[m]);
         }
     }
 
