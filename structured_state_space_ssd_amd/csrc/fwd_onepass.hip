@@ -60,19 +60,12 @@ namespace {
 
 constexpr int kOpT = 64;  // tokens per block
 
-// Causal 16 x 32 tiles of a block, u -> (row tile it of 16 outputs, slice js
-// of 32 inputs). u = 0..3 hold the diagonal (it = u, js = u / 2) and are
-// formed by wavefront u; u = 4, 5 lie wholly below it (it = 2, 3, js = 0) and
-// are formed by wavefronts 0 and 1, whose diagonal tiles are the smaller ones.
-__device__ __forceinline__ int op_tile_it(int u) { return u < 4 ? u : u - 2; }
-__device__ __forceinline__ int op_tile_js(int u) { return u < 4 ? u >> 1 : 0; }
-
 template <int N>
 struct OnepassLds {
     __bf16 xb[2][kOpT * 64];
     __bf16 bb[kOpT * N];
     __bf16 cs[kOpT * N];
-    __bf16 m[6 * 512];     // masked, weighted C B^T tiles, fragment order
+    __bf16 hb[64 * N];     // the state entering the block, bf16, [p][n], pieces swizzled by p & 7
     __bf16 dts[2][kOpT * 8];  // dt pieces of blocks k, k+1: token j's 8 heads around this head
     // tables of blocks k, k+1: s * log2(e), w, exp(s_end - s_j) w_j, and for
     // the first 32 tokens exp(s_31 - s_j) w_j (column factor below the diagonal)
@@ -224,27 +217,41 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
 
     int xo[4];
     x_colfrag_offsets(xo, l);
+    const int i = 16 * w + cc;  // this lane's output token: wavefront w owns rows 16w..16w+15
 
-    // D x on MFMA: Y^T += X^T diag(D) over the slice holding each row tile's
+    // D x on MFMA: Y^T += X^T diag(D) over the slice holding the row tile's
     // diagonal, with D split as D_hi + D_lo (bf16 each, 16 mantissa bits in
     // all; both products exact in float32). B-operand lane (g4, cc) is column
-    // i = 16 it + cc; its element e is token 32 js + 4 g4 + e (e < 4) or
-    // 32 js + 16 + 4 g4 + e - 4, which is i for element cc - 4 g4 (it even)
-    // or 4 + cc - 4 g4 (it odd) when 0 <= cc - 4 g4 < 4.
-    Frag<bf16_t> dfr[2][2];  // [it & 1][hi, lo]
+    // i; its element e is token 32 js + 4 g4 + e (e < 4) or 32 js + 16 + 4 g4
+    // + e - 4, which is i for element cc - 4 g4 (w even) or 4 + cc - 4 g4
+    // (w odd) when 0 <= cc - 4 g4 < 4.
+    Frag<bf16_t> dfr[2];  // hi, lo
     {
         const __bf16 dhi = static_cast<__bf16>(Dh);
         const __bf16 dlo = static_cast<__bf16>(Dh - static_cast<float>(dhi));
         const int e0 = cc - 4 * g4;
 #pragma unroll
-        for (int par = 0; par < 2; ++par)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const bool on = e == (par ? 4 + e0 : e0) && e0 >= 0 && e0 < 4;
-                dfr[par][0].v[e] = on ? dhi : static_cast<__bf16>(0.0f);
-                dfr[par][1].v[e] = on ? dlo : static_cast<__bf16>(0.0f);
-            }
+        for (int e = 0; e < 8; ++e) {
+            const bool on = e == ((w & 1) ? 4 + e0 : e0) && e0 >= 0 && e0 < 4;
+            dfr[0].v[e] = on ? dhi : static_cast<__bf16>(0.0f);
+            dfr[1].v[e] = on ? dlo : static_cast<__bf16>(0.0f);
+        }
     }
+
+    // the state (bf16) into LDS for the next state-to-output product: this
+    // wavefront's columns p = 16 w + cc, 4 consecutive n per accumulator tile
+    auto put_h = [&]() {
+        const int pp = 16 * w + cc;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int n0 = 16 * nt + 4 * g4, q = n0 >> 3;
+            const bf16x2 lo = __builtin_convertvector(floatx2{hreg[nt][0], hreg[nt][1]}, bf16x2);
+            const bf16x2 hi = __builtin_convertvector(floatx2{hreg[nt][2], hreg[nt][3]}, bf16x2);
+            *reinterpret_cast<bf16x4 *>(sm.hb + pp * N + ((q ^ (pp & 7)) << 3) + (n0 & 7)) =
+                bf16x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+    };
+    put_h();  // published by the first block's barrier
 
     uint4 ystage[2];  // this lane's two 16-byte pieces of the previous block's outputs
     for (int k = 0; k < nblk; ++k) {
@@ -252,55 +259,43 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
         // every load issued so far has landed (block k's x, B, C, this and
         // the next block's dt) and every store has left; every wavefront has
         // read the previous block's staged outputs out of x buffer (k+1) & 1,
-        // which now takes block k+1's x
+        // which now takes block k+1's x; the state entering the block is in LDS
         wait_barrier<0>();
         if (k + 1 < nblk) issue_x(k + 1);
         const __bf16 *xs = sm.xb[k & 1];
         if (k == 0) {  // later blocks' tables are made during the block before
-            if (w == 3) make_tables(0);
+            if (w == 0) make_tables(0);
             barrier_lds();
         }
         const float *tsl = sm.tab[k & 1].sl, *twt = sm.tab[k & 1].wt, *twp = sm.tab[k & 1].wp,
                     *tcf = sm.tab[k & 1].cf;
+        const float dec = __builtin_amdgcn_exp2f(tsl[T - 1]), s31 = tsl[31], si = tsl[i];
 
-        // ---- state to output: Y^T[p][i] = sum_n H[p][n] C_i[n] (scaled by
-        // exp(s_i) once the tables exist); issued first, to overlap the tables
+        // C_i (n = 32 kk + 8 g4 .. +7), the B operand of both C H and C B^T
+        Frag<bf16_t> cfr[NK];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+            lds_frag8(cfr[kk], sm.cs + i * N + (((4 * kk + g4) ^ tr_swz<PPR>(i)) << 3));
+
+        // ---- state to output: Y^T[p][i] = exp(s_i) sum_n H[p][n] C_i[n], every p tile
         floatx4 acc[4];
-        {
-            Frag<bf16_t> hf[NK];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+            const int pp = 16 * pt + cc;
+            acc[pt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk) {
-                float v[8];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    v[r] = hreg[2 * kk][r];
-                    v[4 + r] = hreg[2 * kk + 1][r];
-                }
-                pack8(hf[kk], v);
-            }
-#pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const int i = 16 * it + cc;
-                acc[it] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    // C_i at n = 32 kk + 4 g4 + 0..3 and 32 kk + 16 + 4 g4 + 0..3
-                    const int n0 = 32 * kk + 4 * g4;
-                    const int q0 = n0 >> 3, q1 = q0 + 2, sw = tr_swz<PPR>(i);
-                    Frag<bf16_t> cf;
-                    lds_frag4x2(cf, sm.cs + i * N + ((q0 ^ sw) << 3) + (n0 & 7),
-                                sm.cs + i * N + ((q1 ^ sw) << 3) + (n0 & 7));
-                    mma(acc[it], hf[kk], cf);
-                }
+                Frag<bf16_t> hf;
+                lds_frag8(hf, sm.hb + pp * N + (((4 * kk + g4) ^ (pp & 7)) << 3));
+                mma(acc[pt], hf, cfr[kk]);
             }
         }
-
-        const float dec = __builtin_amdgcn_exp2f(tsl[T - 1]), s31 = tsl[31];
+        {
+            const float e = __builtin_amdgcn_exp2f(si);
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const float e = __builtin_amdgcn_exp2f(tsl[16 * it + cc]);
+            for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[it][r] *= e;
+                for (int r = 0; r < 4; ++r) acc[pt][r] *= e;
         }
 
         // ---- the previous block's outputs leave here, between compute phases
@@ -313,31 +308,28 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
             }
         }
 
-        // ---- causal C B^T tiles: M[i][j] = (C_i . B_j) exp(s_i - s_j) w_j, j <= i
-#pragma unroll
-        for (int u = w; u < 6; u += 4) {
-            const int it = op_tile_it(u), js = op_tile_js(u);
-            const int i = 16 * it + cc;
+        // ---- the row tile's causal C B^T tiles (slices js <= w / 2), kept in
+        // registers as the B operand of the diagonal products over every p tile:
+        // M[i][j] = (C_i . B_j) exp(s_i - s_j) w_j, j <= i
+        for (int js = 0; js <= (w >> 1); ++js) {  // wave-uniform trip count
             floatx4 m[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk) {
                 const int q = 4 * kk + g4;
-                Frag<bf16_t> cf;
-                lds_frag8(cf, sm.cs + i * N + ((q ^ tr_swz<PPR>(i)) << 3));
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     const int j = 32 * js + 16 * half + cc;
                     Frag<bf16_t> bf;
                     lds_frag8(bf, sm.bb + j * N + ((q ^ tr_swz<PPR>(j)) << 3));
-                    mma(m[half], bf, cf);
+                    mma(m[half], bf, cfr[kk]);
                 }
             }
             // lane (g4, cc): rows j = 32 js + 16 half + 4 g4 + r of column i
             const int j0 = 32 * js + 4 * g4;
+            const bool diag = js == (w >> 1);
             float v[8];
-            if (u < 4) {
+            if (diag) {
                 // holds the diagonal: exp per element, causal mask
-                const float si = tsl[i];
                 const floatx4 s0 = *reinterpret_cast<const floatx4 *>(tsl + j0);
                 const floatx4 s1 = *reinterpret_cast<const floatx4 *>(tsl + j0 + 16);
                 const floatx4 w0 = *reinterpret_cast<const floatx4 *>(twt + j0);
@@ -352,7 +344,7 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
             } else {
                 // wholly below it (i >= 32 > j): exp(s_i - s_31) exp(s_31 - s_j) w_j,
                 // both factors <= 1, no mask
-                const float rowf = __builtin_amdgcn_exp2f(tsl[i] - s31);
+                const float rowf = __builtin_amdgcn_exp2f(si - s31);
                 const floatx4 c0 = *reinterpret_cast<const floatx4 *>(tcf + j0);
                 const floatx4 c1 = *reinterpret_cast<const floatx4 *>(tcf + j0 + 16);
 #pragma unroll
@@ -363,10 +355,21 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
             }
             Frag<bf16_t> mf;
             pack8(mf, v);
-            store_frag8(sm.m + u * 512 + l * 8, mf);
+            // Y^T[p][i] += sum_j x_j[p] M[i][j] (and D x on the diagonal slice)
+            const __bf16 *xsl = xs + js * 2048;
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                Frag<bf16_t> xf;
+                x_colfrag<0>(xf, xsl, xo[pt]);
+                mma(acc[pt], xf, mf);
+                if (diag && D) {  // uniform
+                    mma(acc[pt], xf, dfr[0]);
+                    mma(acc[pt], xf, dfr[1]);
+                }
+            }
         }
 
-        // ---- state: H^T = exp(s_end) H^T + sum_j B_j (exp(s_end - s_j) w_j x_j)^T
+        // ---- state (p tile w): H^T = exp(s_end) H^T + sum_j B_j (exp(s_end - s_j) w_j x_j)^T
         Frag<bf16_t> xr[2];
         x_colfrag<0>(xr[0], xs, xo[w]);
         x_colfrag<1>(xr[1], xs, xo[w]);
@@ -395,38 +398,24 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
             }
         }
 
-        // the next block's tables, by the wavefront with the least tile work
-        if (w == 3 && k + 1 < nblk) make_tables(k + 1);
+        // the next block's tables, by a wavefront with one C B^T tile
+        if (w == 0 && k + 1 < nblk) make_tables(k + 1);
 
-        // tiles complete; B, C and the dt pieces read by every wavefront
+        // x, B, C, dt and the state of this block consumed by every wavefront
         barrier_lds();
+        put_h();
         if (k + 1 < nblk) issue_bcd(k + 1);
 
-        // ---- diagonal blocks: Y^T[p][i] += sum_j x_j[p] M[i][j], and D x
-#pragma unroll
-        for (int u = 0; u < 6; ++u) {
-            Frag<bf16_t> mf;
-            load_frag8(mf, sm.m + u * 512 + l * 8);
-            mma(acc[op_tile_it(u)], xr[op_tile_js(u)], mf);
-        }
-        if (D) {  // uniform
-#pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                mma(acc[it], xr[it >> 1], dfr[it & 1][0]);
-                mma(acc[it], xr[it >> 1], dfr[it & 1][1]);
-            }
-        }
-
-        // ---- the outputs into this wavefront's columns of the x buffer
+        // ---- the outputs: this wavefront's rows, every column, into the x buffer
         __bf16 *xw_ = sm.xb[k & 1];
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int off = x_at(16 * it + cc, 16 * w + 4 * g4);
-            const bf16x2 lo = __builtin_convertvector(floatx2{acc[it][0], acc[it][1]}, bf16x2);
-            const bf16x2 hi = __builtin_convertvector(floatx2{acc[it][2], acc[it][3]}, bf16x2);
+        for (int pt = 0; pt < 4; ++pt) {
+            const int off = x_at(i, 16 * pt + 4 * g4);
+            const bf16x2 lo = __builtin_convertvector(floatx2{acc[pt][0], acc[pt][1]}, bf16x2);
+            const bf16x2 hi = __builtin_convertvector(floatx2{acc[pt][2], acc[pt][3]}, bf16x2);
             *reinterpret_cast<bf16x4 *>(xw_ + off) = bf16x4{lo[0], lo[1], hi[0], hi[1]};
         }
-        barrier_lds();  // every wavefront's columns staged
+        barrier_lds();  // every row staged
         // whole rows into registers; stored during the next block
 #pragma unroll
         for (int m = 0; m < 2; ++m)
