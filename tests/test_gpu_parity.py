@@ -223,6 +223,15 @@ def test_onepass_options(name):
     check_forward(w, **OPTION_SETS[name])
 
 
+def test_onepass_strong_decay():
+    # steps up to 2 with A down to -16: within a 64-token block the log-decay
+    # spans far more than fp32's exponent range (every decay factor the
+    # kernel forms must stay <= 1, with no inf times 0)
+    w = W.small("onepass_strong", 8, 300, 64, 64, 2, 64, 256, "bf16", seed=850,
+                dt_lo=0.5, dt_hi=2.0, init_std=0.2)
+    check_forward(w)
+
+
 def test_heads_not_multiple_of_8_many_units():
     # 9 x 60 units but 60 heads: the separate-stage path (its fused state kernel)
     check_forward(W.small("h60", 9, 300, 60, 64, 3, 64, 128, "bf16", seed=840, init_std=0.2))
