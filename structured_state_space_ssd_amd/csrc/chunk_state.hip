@@ -306,7 +306,14 @@ __global__ __launch_bounds__(512) void chunk_state_bf16_kernel(
 // waits on a global load. Products are formed transposed, S^T[n][p] (B rows as
 // the A operand, weighted x as the B operand): a lane then holds 4
 // consecutive n of one p, which is how the [P][N] state is stored.
-template <int N, int Q>
+//
+// REV (backward): the adjoint of the state, the same recurrence run over the
+// chunks in reverse, G_nC = dfinal (`init`), G_c = exp(s_end(c)) G_{c+1} + dS_c
+// with dS_c = sum_i exp(s_i) dy_i C_i^T: `x` is dy, `B` is C, the token
+// weights are exp(s_i) (zero past the end; delta is not read), chunk_init[c]
+// receives G_{c+1} (the gradient of the state leaving chunk c) and
+// final_state G_0 (the initial state's gradient).
+template <int N, int Q, bool REV>
 __global__ __launch_bounds__(512) void chunk_state_passing_bf16_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ B,
     const float *__restrict__ dA_cumsum, const float *__restrict__ delta,
@@ -337,10 +344,13 @@ __global__ __launch_bounds__(512) void chunk_state_passing_bf16_kernel(
     const size_t srow = ((size_t)b * H + h) * (size_t)nC * Q;  // this head's s / delta rows
     const int nph = nC * NPH;
 
-    // phase k (chunk k / NPH, tokens from (k % NPH) * TP) into buffer pair k & 1;
-    // a chunk's first phase also brings its s and delta rows (buffer pair c & 1)
+    // chunk of phase k (the chunks run in reverse for REV)
+    auto chunk_of = [&](int k) { return REV ? nC - 1 - k / NPH : k / NPH; };
+    // phase k (chunk chunk_of(k), tokens from (k % NPH) * TP) into buffer pair
+    // k & 1; a chunk's first phase also brings its s and delta rows (buffer
+    // pair c & 1; REV reads no delta)
     auto issue = [&](int k) {
-        const int c = k / NPH, t0 = c * Q + (k % NPH) * TP;
+        const int c = chunk_of(k), t0 = c * Q + (k % NPH) * TP;
         __bf16 *xd = (k & 1) ? xs1 : xs0;
         __bf16 *bd = (k & 1) ? bs1 : bs0;
         for (int i = w; i < XSL; i += NW) {
@@ -351,7 +361,7 @@ __global__ __launch_bounds__(512) void chunk_state_passing_bf16_kernel(
             const int s = i * 64 + l, r = s / PPR, q = (s % PPR) ^ tr_swz<PPR>(r);
             dma16(bg + (size_t)min(t0 + r, L - 1) * brow + q * 8, bd + i * 512);
         }
-        if (k % NPH == 0 && w < 2 * SL) {
+        if (k % NPH == 0 && w < (REV ? SL : 2 * SL)) {
             const int i = w % SL;  // waves 0..SL-1: s, SL..2SL-1: delta
             // (for Q < 256 the lanes past the row re-read its last 16 bytes)
             const float *src = (w < SL ? dA_cumsum : delta) + srow + (size_t)c * Q +
@@ -388,10 +398,10 @@ __global__ __launch_bounds__(512) void chunk_state_passing_bf16_kernel(
             }
         }
     };
-    put_init(0);
+    put_init(REV ? nC - 1 : 0);
 
     for (int k = 0; k < nph; ++k) {
-        const int c = k / NPH, kq = k % NPH;
+        const int c = chunk_of(k), kq = k % NPH;
         wait_barrier<0>();  // phase k (and, at a chunk start, its s and delta) in LDS
         if (k + 1 < nph) issue(k + 1);
         if (kq == 0) {
@@ -399,8 +409,11 @@ __global__ __launch_bounds__(512) void chunk_state_passing_bf16_kernel(
             const float *svc = (c & 1) ? sv1 : sv0;
             const float *dvc = (c & 1) ? dv1 : dv0;
             const float se = svc[Q - 1];  // s is constant past the end
-            for (int j = tid; j < Q; j += 512)
-                wj[j] = __builtin_amdgcn_exp2f((se - svc[j]) * kLog2e) * dvc[j];
+            const int lenc = min(Q, L - c * Q);
+            for (int j = tid; j < Q; j += 512) {
+                if (REV) wj[j] = j < lenc ? __builtin_amdgcn_exp2f(svc[j] * kLog2e) : 0.0f;
+                else wj[j] = __builtin_amdgcn_exp2f((se - svc[j]) * kLog2e) * dvc[j];
+            }
             barrier_lds();
         }
         const __bf16 *xsp = (k & 1) ? xs1 : xs0;
@@ -439,7 +452,7 @@ __global__ __launch_bounds__(512) void chunk_state_passing_bf16_kernel(
                 for (int r = 0; r < 4; ++r) hreg[i][r] = dec * hreg[i][r] + acc[i][r];
                 acc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
             }
-            if (c + 1 < nC) put_init(c + 1);
+            if (REV ? c > 0 : c + 1 < nC) put_init(REV ? c - 1 : c + 1);
         }
     }
     if (final_state) {
@@ -457,21 +470,26 @@ __global__ __launch_bounds__(512) void chunk_state_passing_bf16_kernel(
 template <int N, int Q>
 static void launch_fused(const void *x, const void *B, const float *dA, const float *delta,
                          const float *init, int batch, int L, int H, int G, void *chunk_init,
-                         float *final_state, hipStream_t stream) {
+                         float *final_state, bool rev, hipStream_t stream) {
     const int nC = (L + Q - 1) / Q;
-    chunk_state_passing_bf16_kernel<N, Q><<<dim3(H, batch), 512, 0, stream>>>(
-        static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(B), dA, delta, init, L, H, G,
-        nC, static_cast<__bf16 *>(chunk_init), final_state);
+    if (rev)
+        chunk_state_passing_bf16_kernel<N, Q, true><<<dim3(H, batch), 512, 0, stream>>>(
+            static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(B), dA, delta, init, L,
+            H, G, nC, static_cast<__bf16 *>(chunk_init), final_state);
+    else
+        chunk_state_passing_bf16_kernel<N, Q, false><<<dim3(H, batch), 512, 0, stream>>>(
+            static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(B), dA, delta, init, L,
+            H, G, nC, static_cast<__bf16 *>(chunk_init), final_state);
 }
 
 template <int N>
 static bool fused_q(int Q, const void *x, const void *B, const float *dA, const float *delta,
                     const float *init, int batch, int L, int H, int G, void *ci, float *fs,
-                    hipStream_t s) {
+                    bool rev, hipStream_t s) {
     switch (Q) {
-        case 64: launch_fused<N, 64>(x, B, dA, delta, init, batch, L, H, G, ci, fs, s); return true;
-        case 128: launch_fused<N, 128>(x, B, dA, delta, init, batch, L, H, G, ci, fs, s); return true;
-        case 256: launch_fused<N, 256>(x, B, dA, delta, init, batch, L, H, G, ci, fs, s); return true;
+        case 64: launch_fused<N, 64>(x, B, dA, delta, init, batch, L, H, G, ci, fs, rev, s); return true;
+        case 128: launch_fused<N, 128>(x, B, dA, delta, init, batch, L, H, G, ci, fs, rev, s); return true;
+        case 256: launch_fused<N, 256>(x, B, dA, delta, init, batch, L, H, G, ci, fs, rev, s); return true;
         default: return false;
     }
 }
@@ -486,14 +504,15 @@ bool state_passing_fused(int batch, int nheads, bool bf16) {
 hipError_t launch_chunk_state_passing(const void *x, const void *B, const float *dA_cumsum,
                                       const float *delta, const float *init, int batch,
                                       int seqlen, int nheads, int ngroups, int dstate, int chunk,
-                                      void *chunk_init, float *final_state, hipStream_t stream) {
+                                      void *chunk_init, float *final_state, hipStream_t stream,
+                                      bool reverse) {
     bool ok = false;
     switch (dstate) {
-        case 16: ok = fused_q<16>(chunk, x, B, dA_cumsum, delta, init, batch, seqlen, nheads, ngroups, chunk_init, final_state, stream); break;
-        case 32: ok = fused_q<32>(chunk, x, B, dA_cumsum, delta, init, batch, seqlen, nheads, ngroups, chunk_init, final_state, stream); break;
-        case 64: ok = fused_q<64>(chunk, x, B, dA_cumsum, delta, init, batch, seqlen, nheads, ngroups, chunk_init, final_state, stream); break;
-        case 128: ok = fused_q<128>(chunk, x, B, dA_cumsum, delta, init, batch, seqlen, nheads, ngroups, chunk_init, final_state, stream); break;
-        case 256: ok = fused_q<256>(chunk, x, B, dA_cumsum, delta, init, batch, seqlen, nheads, ngroups, chunk_init, final_state, stream); break;
+        case 16: ok = fused_q<16>(chunk, x, B, dA_cumsum, delta, init, batch, seqlen, nheads, ngroups, chunk_init, final_state, reverse, stream); break;
+        case 32: ok = fused_q<32>(chunk, x, B, dA_cumsum, delta, init, batch, seqlen, nheads, ngroups, chunk_init, final_state, reverse, stream); break;
+        case 64: ok = fused_q<64>(chunk, x, B, dA_cumsum, delta, init, batch, seqlen, nheads, ngroups, chunk_init, final_state, reverse, stream); break;
+        case 128: ok = fused_q<128>(chunk, x, B, dA_cumsum, delta, init, batch, seqlen, nheads, ngroups, chunk_init, final_state, reverse, stream); break;
+        case 256: ok = fused_q<256>(chunk, x, B, dA_cumsum, delta, init, batch, seqlen, nheads, ngroups, chunk_init, final_state, reverse, stream); break;
         default: break;
     }
     if (!ok) return hipErrorInvalidValue;

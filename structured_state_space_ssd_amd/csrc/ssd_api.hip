@@ -420,12 +420,21 @@ int ssd_backward(const void *x, const void *dt, const float *A, const void *B, c
         }
     }
     // the adjoint of the state leaving each chunk: dS_c, then the reverse pass
-    if (e == hipSuccess)
-        e = ssd::launch_chunk_state(dy, C, nullptr, s_, nullptr, batch, seqlen, nheads, ngroups,
-                                    dstate, Q, bf16, states, st, /*dout=*/true);
-    if (e == hipSuccess)
-        e = ssd::launch_state_passing(states, s_, dfinal_state, nullptr, batch, seqlen, nheads,
-                                      dstate, Q, bf16, gnext, dinit_state, st, /*reverse=*/true);
+    // (one kernel per (b, h) walking the chunks backward when that fills the GPU)
+    if (ssd::state_passing_fused(batch, nheads, bf16)) {
+        if (e == hipSuccess)
+            e = ssd::launch_chunk_state_passing(dy, C, s_, nullptr, dfinal_state, batch, seqlen,
+                                                nheads, ngroups, dstate, Q, gnext, dinit_state,
+                                                st, /*reverse=*/true);
+    } else {
+        if (e == hipSuccess)
+            e = ssd::launch_chunk_state(dy, C, nullptr, s_, nullptr, batch, seqlen, nheads,
+                                        ngroups, dstate, Q, bf16, states, st, /*dout=*/true);
+        if (e == hipSuccess)
+            e = ssd::launch_state_passing(states, s_, dfinal_state, nullptr, batch, seqlen,
+                                          nheads, dstate, Q, bf16, gnext, dinit_state, st,
+                                          /*reverse=*/true);
+    }
     // the chunks' gradients
     ssd::BwdArgs a{};
     a.x = x; a.dy = dy; a.B = B; a.C = C; a.dA_cumsum = s_; a.delta = delta; a.D = D;

@@ -51,10 +51,13 @@ hipError_t launch_forward_onepass(const void *x, const void *dt, const float *A,
                                   int ngroups, int dstate, void *y, float *final_state,
                                   hipStream_t stream);
 bool state_passing_fused(int batch, int nheads, bool bf16);
+// reverse (backward): the adjoint pass (x = dy, B = C, init = dfinal; chunk_init
+// receives the gradient of the state leaving each chunk, final_state G_0).
 hipError_t launch_chunk_state_passing(const void *x, const void *B, const float *dA_cumsum,
                                       const float *delta, const float *init, int batch,
                                       int seqlen, int nheads, int ngroups, int dstate, int chunk,
-                                      void *chunk_init, float *final_state, hipStream_t stream);
+                                      void *chunk_init, float *final_state, hipStream_t stream,
+                                      bool reverse = false);
 
 // chunk_init is written in the MFMA operand type of the forward's dtype
 // (bf16 when bf16 is true, else float32). reverse (backward): the adjoint pass,

@@ -7,7 +7,8 @@ state's, and with options the dt bias's) by relative L2 at the forward's
 tolerances: 1e-4 for float32 inputs, 2e-2 for bf16. Cases cover every state
 size with several chunks and a ragged tail, groups, an initial state and a
 final-state gradient, the step-size options, the fused forward recompute
-(bf16, Bt*H >= 512), and the 2.7B layer's shape (one batch row checked).
+and the fused reverse adjoint pass (bf16, Bt*H >= 512), and the 2.7B
+layer's shape (one batch row checked).
 """
 import numpy as np
 import pytest
@@ -103,6 +104,19 @@ def test_backward_fused_recompute():
     # Bt*H >= 512: the forward recompute runs stages 2 and 3 as one kernel
     w = W.small("bwd_fused", 8, 300, 64, 64, 4, 64, 64, "bf16", seed=940, init_std=0.2)
     check_backward(w, batches=[0, 5])
+
+
+def test_backward_fused_adjoint_options_no_dfinal():
+    # Bt*H >= 512: the adjoint pass runs as one reverse kernel per (b, h);
+    # here with every step-size option and no final-state gradient
+    w = W.small("bwd_fused_opt", 8, 333, 64, 64, 2, 64, 64, "bf16", seed=941, init_std=0.2)
+    check_backward(w, with_dfinal=False, batches=[1, 6], raw=True, dt_softplus=True,
+                   dt_limit=(4e-3, 3e-2), zoh=True)
+
+
+def test_backward_fused_adjoint_single_chunk():
+    w = W.small("bwd_fused_short", 8, 50, 64, 64, 1, 64, 64, "bf16", seed=942, init_std=0.3)
+    check_backward(w, batches=[0, 7])
 
 
 def test_backward_strong_decay():
