@@ -137,7 +137,9 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
     const int lin = (id & 7) * per + (id >> 3);
     if (lin >= batch * H) return;  // whole workgroup
     const int b = lin / H, h = lin % H, g = h / (H / G);
-    const int w = wave_id(), l = lane_id(), g4 = l >> 4, cc = l & 15;
+    // the wavefront index as a scalar (uniform branches and loop bounds)
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l = lane_id(), g4 = l >> 4, cc = l & 15;
     const int nblk = (L + T - 1) / T;
 
     const size_t xrow = (size_t)H * P, brow = (size_t)G * N;
