@@ -48,9 +48,9 @@
 //   -- barrier: tiles visible; B, C, dt buffers free: next loads issued --
 //   diagonal  Y^T += X^T M^T over the 6 tiles; D x as X^T diag(D) (D split
 //             into two bf16 parts) on the diagonal slices;
-//   outputs   staged in the block's x buffer (only this wavefront's columns,
-//             which only it reads), then -- barrier -- whole 128-byte rows
-//             into registers, stored (non-temporal) during the next block.
+//   outputs   this wavefront's 16 rows staged in the block's x buffer and
+//             read back as whole 128-byte rows by the same wavefront (no
+//             barrier), stored (non-temporal) during the next block.
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
         if (k > 0) {
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                const int s = (w + 4 * m) * 64 + l, r = s >> 3, q = (s & 7) ^ (r & 7);
+                const int s = 128 * w + 64 * m + l, r = s >> 3, q = (s & 7) ^ (r & 7);
                 store_nt16(yh + (size_t)(t0 - T + r) * xrow + q * 8, ystage[m]);
             }
         }
@@ -417,17 +417,17 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
             const bf16x2 hi = __builtin_convertvector(floatx2{acc[pt][2], acc[pt][3]}, bf16x2);
             *reinterpret_cast<bf16x4 *>(xw_ + off) = bf16x4{lo[0], lo[1], hi[0], hi[1]};
         }
-        barrier_lds();  // every row staged
-        // whole rows into registers; stored during the next block
+        // this wavefront's 16 rows (staged by itself: no barrier) into
+        // registers; stored during the next block
 #pragma unroll
         for (int m = 0; m < 2; ++m)
-            ystage[m] = *reinterpret_cast<const uint4 *>(xs + ((w + 4 * m) * 64 + l) * 8);
+            ystage[m] = *reinterpret_cast<const uint4 *>(xs + (128 * w + 64 * m + l) * 8);
     }
     {  // the last block's outputs (possibly a partial block)
         const int t0 = (nblk - 1) * T, len = L - t0;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const int s = (w + 4 * m) * 64 + l, r = s >> 3, q = (s & 7) ^ (r & 7);
+            const int s = 128 * w + 64 * m + l, r = s >> 3, q = (s & 7) ^ (r & 7);
             if (r < len) store_nt16(yh + (size_t)(t0 + r) * xrow + q * 8, ystage[m]);
         }
     }
