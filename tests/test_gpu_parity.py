@@ -223,6 +223,12 @@ def test_onepass_options(name):
     check_forward(w, **OPTION_SETS[name])
 
 
+def test_onepass_one_head_per_group():
+    # ngroups = nheads: every workgroup reads its own B and C rows
+    check_forward(W.small("onepass_g64", 8, 150, 64, 64, 64, 64, 128, "bf16", seed=860,
+                          init_std=0.2))
+
+
 def test_onepass_strong_decay():
     # steps up to 2 with A down to -16: within a 64-token block the log-decay
     # spans far more than fp32's exponent range (every decay factor the
