@@ -131,7 +131,9 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
     const int c = u % nC, g = (u / nC) % G, b = u / (nC * G);
     const int nh = (hpg - kb + nblk - 1) / nblk;
     const int t0 = c * Q, len = min(Q, L - t0);
-    const int tid = threadIdx.x, w = wave_id(), l = lane_id(), g4 = l >> 4, c16 = l & 15;
+    // (the wavefront index as a scalar: the slice loops below run per wavefront)
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l = lane_id(), g4 = l >> 4, c16 = l & 15;
     const int tok = 16 * w + c16;  // this lane's token: column j of pass 1, row i of pass 2
     const size_t xrow = (size_t)H * P, brow = (size_t)G * N;
 
