@@ -238,6 +238,27 @@ def test_onepass_strong_decay():
     check_forward(w)
 
 
+def test_onepass_misaligned_dt_falls_back():
+    # dt 2 bytes off a 16-byte boundary: the single-pass kernel reads dt as
+    # 16-byte pieces, so the forward takes the stage kernels instead
+    ssd = _ssd()
+    w = W.small("onepass_dt_off", 8, 130, 64, 64, 2, 64, 128, "bf16", seed=870)
+    d = W.generate(w)
+    dtg = up(d["dt"])
+    buf = torch.empty(dtg.numel() + 8, dtype=dtg.dtype, device=dtg.device)
+    dt_off = buf[1:1 + dtg.numel()].view(dtg.shape)
+    dt_off.copy_(dtg)
+    assert dt_off.data_ptr() % 16 != 0
+    y = ssd.forward(up(d["x"]), dt_off, up(d["A"]), up(d["B"]), up(d["C"]), up(d["D"]),
+                    chunk=w.chunk)
+    torch.cuda.synchronize()
+    y0, _, _ = oracle.forward(d["x"].val, d["dt"].val, d["A"], d["B"].val, d["C"].val, d["D"],
+                              None)
+    e = rel_l2(units_view(down(y), np.arange(w.batch * w.nheads), w.nheads), y0)
+    print_case(f"[forward] misaligned dt: rel_l2(y) = {e:.3e}")
+    assert e < tol(w.dtype), e
+
+
 def test_heads_not_multiple_of_8_many_units():
     # 9 x 60 units but 60 heads: the separate-stage path (its fused state kernel)
     check_forward(W.small("h60", 9, 300, 60, 64, 3, 64, 128, "bf16", seed=840, init_std=0.2))
