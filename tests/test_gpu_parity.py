@@ -238,6 +238,14 @@ def test_onepass_strong_decay():
     check_forward(w)
 
 
+def test_onepass_long_sequence_sampled():
+    # 16384 tokens (256 blocks per (batch, head)), x about 1 GB; the oracle
+    # checks a first, a middle and a last unit, across batch rows and groups
+    w = W.small("onepass_long", 8, 16384, 64, 64, 4, 64, 256, "bf16", seed=880, init_std=0.1,
+                dt_lo=1e-4, dt_hi=1e-2)
+    check_forward(w, units=[0, 64 * 3 + 37, 8 * 64 - 1], both_D=False)
+
+
 def test_onepass_misaligned_dt_falls_back():
     # dt 2 bytes off a 16-byte boundary: the single-pass kernel reads dt as
     # 16-byte pieces, so the forward takes the stage kernels instead
