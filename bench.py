@@ -35,39 +35,89 @@ BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (no sparsity)
 FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix
 STAGES = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_cb", "chunk_scan"]
 ONEPASS = ["forward_onepass"]
-SOURCE_OF = {"forward_onepass": "fwd_onepass"}  # kernel -> its source file in csrc/
+ONEPASS_SEG = ["segment_states", "forward_onepass"]  # sequences cut into segments
+SOURCE_OF = {"forward_onepass": "fwd_onepass", "segment_states": "fwd_onepass"}  # -> csrc/ file
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 # ---------------------------------------------------------------- accounting
 
+def segments_of(w):
+    """The library's own plan for this forward (ssd_forward_plan): S >= 1
+    segments per sequence on the single-pass kernel, 0 for the stage kernels."""
+    import torch
+    import structured_state_space_ssd_amd as ssd
+    return ssd.forward_plan(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk,
+                            torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+
+
 def onepass_path(w):
-    """Whether the library runs this forward as its single-pass kernel (bf16,
-    dstate 64, heads a multiple of 8, batch * nheads >= 512; mirrors
-    forward_onepass_ok in the library's fwd_onepass.hip)."""
-    return (w.dtype == "bf16" and w.dstate == 64 and w.nheads % 8 == 0
-            and w.batch * w.nheads >= 512)
+    """Whether the library runs this forward as its single-pass kernel."""
+    return segments_of(w) > 0
 
 
 def stages_of(w):
-    return ONEPASS if onepass_path(w) else STAGES
+    S = segments_of(w)
+    return STAGES if S == 0 else (ONEPASS if S == 1 else ONEPASS_SEG)
 
 
 def onepass_accounting(w):
-    """Algorithmic bytes and flops of the single-pass forward kernel.
+    """Algorithmic bytes and flops of the single-pass forward kernel (and, when
+    the sequences are cut into S segments, of the segment-state kernel).
 
     Bytes: x and dt read, y written (bf16), B and C read once per group, A and
     D (float32) once per head; nothing else leaves the chip. Flops (multiply +
     add = 2) of the chunked algorithm at the kernel's 64-token blocks:
     (T+1)P per token-head for the causal block products, 2NP for the state to
     output, 2NP for the state update, 2P for the D term, and (T+1)N per token
-    per group for the causal C B^T products."""
+    per group for the causal C B^T products. With S segments the segment-state
+    kernel reads x, dt and B over the first S-1 segments and writes their
+    states (float32 P x N per (batch, head, segment), 2NP flops per
+    token-head), which the single-pass kernel reads back."""
     Bt, L, H, P, G, N = w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate
     T = 64
     tok = Bt * L
-    nbytes = 2 * tok * H * P * 2 + tok * H * 2 + 2 * tok * G * N * 2 + 2 * H * 4
+    S, k, per_seg = onepass_plan(w)
+    seg_states = Bt * H * (S - 1) * k * (P * N + 1) * 4  # one state + decay per piece
+    nbytes = 2 * tok * H * P * 2 + tok * H * 2 + 2 * tok * G * N * 2 + 2 * H * 4 + seg_states
     flops = tok * H * ((T + 1) * P + 4 * N * P + 2 * P) + tok * G * (T + 1) * N
-    return {"forward_onepass": {"bytes": nbytes, "flops": flops}}
+    acc = {"forward_onepass": {"bytes": nbytes, "flops": flops}}
+    if S > 1:
+        pre = Bt * (S - 1) * per_seg * T  # tokens of the first S-1 segments
+        acc["segment_states"] = {"bytes": pre * H * (P * 2 + 2) + pre * G * N * 2 + H * 4 +
+                                          seg_states,
+                                 "flops": pre * H * 2 * N * P}
+    return acc
+
+
+def onepass_plan(w):
+    """(S, k, per_seg): segments, pieces per segment and blocks per segment of
+    the single-pass forward, mirroring onepass_plan in the library's
+    fwd_onepass.hip (its scratch: the workspace's float32 states region); S is
+    checked against the library's own ssd_forward_plan."""
+    Bt, L, H, P, N, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.chunk
+    slots, so_slots = (3 if N == 64 else 2) * 256, (4 if N == 64 else 3) * 256
+    units, blocks = Bt * H, -(-L // 64)
+    scratch = Bt * (-(-L // Q)) * H * P * N * 4
+    plan = (1, 1, blocks)
+    S0 = min(slots // units, blocks // 4)
+    if S0 > 1:
+        per = -(-blocks // S0)
+        max_pieces = scratch // ((64 * N + 1) * 4)
+        k = max(1, min(so_slots // (units * (S0 - 1)), per // 2))
+        while True:
+            per_seg = k * (-(-per // k))
+            S = -(-blocks // per_seg)
+            if S <= 1:
+                break
+            if (S - 1) * k <= max_pieces:
+                plan = (S, k, per_seg)
+                break
+            if k == 1:
+                break
+            k = max(1, min(max_pieces // (S - 1), k - 1))
+    assert plan[0] == segments_of(w), (plan, segments_of(w))
+    return plan
 
 
 def accounting(w):
@@ -457,7 +507,9 @@ WRITE_CMD = ('rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/write" -o 
              '-- python bench.py --counters')
 # kernel-name fragment -> stage, first match wins (the fused stage-2+3 kernel
 # fills the chunk_state interval of the forward)
-KERNEL_OF = {"ssd_forward_onepass": "forward_onepass",
+KERNEL_OF = {"onepass_kernel<64, true>": "segment_states",
+             "onepass_kernel<128, true>": "segment_states",
+             "ssd_forward_onepass": "forward_onepass",
              "chunk_cumsum_kernel": "chunk_cumsum", "chunk_state_passing": "chunk_state",
              "state_passing_kernel": "state_passing", "chunk_state": "chunk_state",
              "chunk_cb_kernel": "chunk_cb", "chunk_scan": "chunk_scan",
@@ -552,7 +604,7 @@ def summarize_traffic(fetch_csv, write_csv, workload="mamba2_2.7b"):
            f"WRITE_SIZE by {w_scale:.3f}.", "",
            "| kernel | dispatches | fetch MB | write MB | HBM MB / launch | algorithmic MB | ratio |",
            "|---|---|---|---|---|---|---|"]
-    for k in ONEPASS + STAGES + ["decode_step"]:
+    for k in ONEPASS_SEG + STAGES + ["decode_step"]:
         if k not in acc:
             continue
         if k not in per or "fetch" not in per[k] or "write" not in per[k]:
@@ -674,9 +726,18 @@ def main():
         for name in ("tiny_f32", "large_state", "long_seq"):
             wl = W.WORKLOADS[name]
             r = time_forward(wl, 10, 3)
+            acc_w = accounting(wl)
+            hbm = {}
+            for k, v in r["stage_ms"].items():
+                nb = acc_w[k]["bytes"]
+                if nb and v > 0:
+                    gbs = nb / (v * 1e-3) / 1e9
+                    hbm[k] = {"alg_MB": round(nb / 1e6, 1), "GB_s": round(gbs, 1),
+                              "hbm_frac": round(gbs / HBM_PEAK_GBS, 3)}
             extra[name] = {"us_per_forward": round(r["wall_ms"] * 1e3, 1),
                            "tokens_per_s": round(wl.tokens / (r["wall_ms"] * 1e-3)),
-                           "stage_us": {k: round(v * 1e3, 1) for k, v in r["stage_ms"].items()}}
+                           "stage_us": {k: round(v * 1e3, 1) for k, v in r["stage_ms"].items()},
+                           "stage_hbm": hbm}
             print(f"[bench] {name}: {r['wall_ms'] * 1e3:.1f} us", file=sys.stderr, flush=True)
 
     wd = W.WORKLOADS["decode"]

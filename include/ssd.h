@@ -119,9 +119,13 @@ const char *ssd_strerror(int status);
  * After the forward pass has run, these hold the intermediate results of the
  * stages below (a caller may read them, e.g. to test a stage), except that
  * for SSD_BF16 with batch * nheads >= 512 stages 2 and 3 run as one kernel
- * that keeps the per-chunk states on chip (`states` is then not written),
- * and when the forward runs as the single-pass kernel (see ssd_forward) the
- * workspace is not touched at all.
+ * that keeps the per-chunk states on chip (`states` is then not written).
+ * When the forward runs as the single-pass kernel (see ssd_forward) only the
+ * start of `states` is used, and only when the sequences are cut into S > 1
+ * segments: the first S-1 segments are cut into K pieces each (K chosen by
+ * the library), and `states` receives float32 [Bt][H][(S-1)K][P][N], the
+ * state each piece produces from a zero state, then float32 [Bt][H][(S-1)K],
+ * each piece's total log2-decay (sum of dt*A over the piece, times log2(e)).
  */
 size_t ssd_forward_workspace_size(int batch, int seqlen, int nheads, int headdim,
                                   int ngroups, int dstate, int chunk, int dtype);
@@ -129,14 +133,19 @@ size_t ssd_forward_workspace_size(int batch, int seqlen, int nheads, int headdim
 /*
  * Full SSD layer forward: enqueues ssd_chunk_cumsum, ssd_chunk_state,
  * ssd_state_passing, ssd_chunk_cb (SSD_F32 only) and ssd_chunk_scan on
- * `stream`. For SSD_BF16 with dstate 64, nheads a multiple of 8,
- * batch * nheads >= 512 and a 16-byte aligned dt, it enqueues instead one
- * single-pass kernel that computes the same result (up to rounding): one
- * workgroup per (batch, head) walks the sequence in blocks of 64 tokens,
- * carrying the state from block to block in registers (the chunk-to-chunk
- * recurrence of the "Mamba 模型" page, section 4.1, run within the
- * workgroup), so x is read from memory once. `chunk` must still be valid but
- * does not set that kernel's block length.
+ * `stream`. For SSD_BF16 with dstate 64 or 128, nheads a multiple of 8 and
+ * a 16-byte aligned dt, it enqueues instead one single-pass kernel that
+ * computes the same result (up to rounding): one workgroup per (batch, head)
+ * walks the sequence in blocks of 64 tokens, carrying the state from block to
+ * block in registers (the chunk-to-chunk recurrence of the "Mamba 模型" page,
+ * section 4.1, run within the workgroup), so x is read from memory once.
+ * With too few (batch, head) pairs to fill the GPU, each sequence is cut into
+ * S segments of whole blocks (ssd_forward_plan gives S): a first kernel
+ * computes the state that each piece of the first S-1 segments produces from
+ * a zero state, and the single-pass kernel then runs one workgroup per
+ * (batch, head, segment), each starting from the state the pieces before it
+ * pass on (the same recurrence at piece granularity). `chunk` must still be valid but does
+ * not set that kernel's block length.
  *   D           nullable: no feed-through term.
  *   init_state  nullable: the state before token 0 is zero.
  *   y           output, [Bt][L][H][P] in dtype.
@@ -148,6 +157,16 @@ int ssd_forward(const void *x, const void *dt, const float *A, const void *B,
                 int headdim, int ngroups, int dstate, int chunk, int dtype,
                 const float *init_state, void *y, float *final_state,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Which path ssd_forward takes for these sizes and this dt pointer (only its
+ * alignment is looked at; it is not read): the number S >= 1 of segments per
+ * sequence when it runs the single-pass kernel, 0 when it runs the stage
+ * kernels, or a negative ssd_status for sizes ssd_forward rejects. The same
+ * for ssd_forward_ex and ssd_forward_timed.
+ */
+int ssd_forward_plan(int batch, int seqlen, int nheads, int headdim, int ngroups,
+                     int dstate, int chunk, int dtype, const void *dt);
 
 /*
  * ssd_forward with options: `opts` (nullable, see ssd_options) preprocesses dt
@@ -172,7 +191,9 @@ int ssd_forward_ex(const void *x, const void *dt, const float *A, const void *B,
  * the order listed for ssd_forward; for SSD_BF16 the ssd_chunk_cb interval is
  * empty, that work being part of ssd_chunk_scan). When the forward runs as the
  * single-pass kernel (see ssd_forward), events[0] is recorded before it and
- * events[1..5] after it: its time is the first interval.
+ * events[1..5] after it: its time is the first interval; with S > 1 segments,
+ * events[0] before the segment-state kernel, events[1] between the two
+ * kernels and events[2..5] after the single-pass kernel.
  */
 int ssd_forward_timed(const void *x, const void *dt, const float *A, const void *B,
                       const void *C, const float *D, int batch, int seqlen, int nheads,

@@ -14,7 +14,7 @@ import torch
 from . import _native
 from ._native import SSDError, check, dtype_code, ptr, stream_handle
 
-__all__ = ["forward", "backward", "forward_varlen", "step", "options", "workspace_size", "chunk_cumsum", "chunk_state",
+__all__ = ["forward", "forward_plan", "backward", "forward_varlen", "step", "options", "workspace_size", "chunk_cumsum", "chunk_state",
            "state_passing", "chunk_cb", "chunk_scan", "SSDError", "stages"]
 
 HEADDIM = 64
@@ -64,6 +64,19 @@ def _optref(o):
 def workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, dtype=torch.bfloat16) -> int:
     return int(_native.lib.ssd_forward_workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate,
                                                       chunk, dtype_code(dtype)))
+
+
+def forward_plan(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, dtype=torch.bfloat16,
+                 dt=None) -> int:
+    """Segments per sequence of the single-pass forward for these sizes (0: the
+    stage kernels run; ssd_forward_plan). ``dt`` (a tensor, or None for an
+    aligned pointer) matters only through its alignment."""
+    ptr = dt.data_ptr() if dt is not None else 256
+    r = int(_native.lib.ssd_forward_plan(batch, seqlen, nheads, headdim, ngroups, dstate, chunk,
+                                         dtype_code(dtype), ptr))
+    if r < 0:
+        _native.check(r, "ssd_forward_plan")
+    return r
 
 
 def forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, return_final_state=False,

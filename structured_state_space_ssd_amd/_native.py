@@ -34,6 +34,7 @@ _op = ctypes.POINTER(SsdOptions)
 SIGNATURES = {
     "ssd_strerror": (ctypes.c_char_p, [_i]),
     "ssd_forward_workspace_size": (_sz, [_i] * 8),
+    "ssd_forward_plan": (_i, [_i] * 8 + [_vp]),
     "ssd_chunk_cb_size": (_sz, [_i] * 5),
     "ssd_chunk_cb": (_i, [_vp, _vp] + [_i] * 6 + [_vp, _vp]),
     "ssd_forward": (_i, [_vp] * 6 + [_i] * 8 + [_vp, _vp, _vp, _vp, _sz, _vp]),

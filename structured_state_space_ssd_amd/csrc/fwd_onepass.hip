@@ -51,6 +51,8 @@
 //   outputs   this wavefront's 16 rows staged in the block's x buffer and
 //             read back as whole 128-byte rows by the same wavefront (no
 //             barrier), stored (non-temporal) during the next block.
+#include <algorithm>
+
 #include "ssd_common.h"
 #include "ssd_launch.h"
 
@@ -117,37 +119,53 @@ __device__ __forceinline__ void pack8(Frag<bf16_t> &f, const float (&v)[8]) {
 
 }  // namespace
 
+// How a launch cuts each sequence. The single-pass kernel runs nseg segments
+// of len tokens (the last may hold fewer), each starting from the state the
+// kpc * seg pieces before it pass on; the segment-state kernel runs
+// nseg = npc pieces of len tokens and stores for each the state it produces
+// from a zero state and its total log2-decay.
+struct OnepassSegs {
+    int nseg, len, npc, kpc;
+    float *state;  // float32 [Bt][H][npc][P][N]
+    float *ld;     // float32 [Bt][H][npc]
+};
+
 template <int N>
-__global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
+__global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ dt, const float *__restrict__ A,
     const bf16_t *__restrict__ B, const bf16_t *__restrict__ C, const float *__restrict__ D,
     const float *__restrict__ init, DtOpts o, int batch, int L, int H, int G, int per,
-    bf16_t *__restrict__ y, float *__restrict__ final_state) {
+    OnepassSegs sg, bf16_t *__restrict__ y, float *__restrict__ final_state) {
     constexpr int P = 64, T = kOpT;
     constexpr int PPR = N / 8, NT = N / 16, NK = N / 32;
+    constexpr int HSW = PPR >= 16 ? 15 : PPR - 1;  // piece swizzle mask of the bf16 state rows
     constexpr int BL = T * PPR / 256;  // B (and C) loads per lane per block
     static_assert(N % 32 == 0 && BL >= 1, "state size");
     __shared__ __attribute__((aligned(16))) OnepassLds<N> sm;
 
-    // workgroup -> (batch, head): consecutive workgroup ids go round the 8
-    // XCDs, so id -> (id % 8) * per + id / 8 gives each XCD a contiguous
-    // range of (batch, head) pairs: the heads of one batch (and B/C group)
-    // share an L2
+    // workgroup -> (batch, segment, head): consecutive workgroup ids go round
+    // the 8 XCDs, so id -> (id % 8) * per + id / 8 gives each XCD a contiguous
+    // range of units: the heads of one batch row and segment (and B/C group)
+    // share an L2.
+    const int nseg = sg.nseg;
     const int id = blockIdx.x;
     const int lin = (id & 7) * per + (id >> 3);
-    if (lin >= batch * H) return;  // whole workgroup
-    const int b = lin / H, h = lin % H, g = h / (H / G);
+    if (lin >= batch * nseg * H) return;  // whole workgroup
+    const int h = lin % H, bs = lin / H, seg = bs % nseg, b = bs / nseg, g = h / (H / G);
+    // this workgroup's tokens: [tb, tb + Lw) of its batch row
+    const int tb = seg * sg.len, Lw = min(sg.len, L - tb);
+    const size_t bh = (size_t)b * H + h;
     // the wavefront index as a scalar (uniform branches and loop bounds)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = lane_id(), g4 = l >> 4, cc = l & 15;
-    const int nblk = (L + T - 1) / T;
+    const int nblk = (Lw + T - 1) / T;
 
-    const size_t xrow = (size_t)H * P, brow = (size_t)G * N;
-    const bf16_t *xh = x + (size_t)b * L * xrow + (size_t)h * P;
-    bf16_t *yh = y + (size_t)b * L * xrow + (size_t)h * P;
-    const bf16_t *bg = B + (size_t)b * L * brow + (size_t)g * N;
-    const bf16_t *cg = C + (size_t)b * L * brow + (size_t)g * N;
-    const bf16_t *dth = dt + (size_t)b * L * H + (h & ~7);
+    const size_t xrow = (size_t)H * P, brow = (size_t)G * N, row0 = (size_t)b * L + tb;
+    const bf16_t *xh = x + row0 * xrow + (size_t)h * P;
+    bf16_t *yh = y + row0 * xrow + (size_t)h * P;
+    const bf16_t *bg = B + row0 * brow + (size_t)g * N;
+    const bf16_t *cg = C + row0 * brow + (size_t)g * N;
+    const bf16_t *dth = dt + row0 * H + (h & ~7);
     const float Ah = A[h];
     const float Dh = D ? D[h] : 0.0f;
     const float bias = o.bias ? o.bias[h] : 0.0f;
@@ -164,19 +182,19 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
         return (uint32_t)min(r, len - 1) * brb + q * 16;
     };
     auto issue_x = [&](int k) {
-        const int t0 = k * T, len = min(T, L - t0);
+        const int t0 = k * T, len = min(T, Lw - t0);
         const bf16_t *base = xh + (size_t)t0 * xrow;
 #pragma unroll
         for (int i = w; i < 8; i += 4) dma16_sv(base, x_off(i, len), sm.xb[k & 1] + i * 512);
     };
     auto issue_dt = [&](int k) {  // wavefront 0 only
-        const int t0 = k * T, len = min(T, L - t0);
+        const int t0 = k * T, len = min(T, Lw - t0);
         dma16_sv(dth + (size_t)t0 * H, (uint32_t)min(l, len - 1) * drb, sm.dts[k & 1]);
     };
     // B and C of block k, after dt of block k+1 (so that waiting for block k's
     // B and C also brings the dt the next block's step sizes are made from)
     auto issue_bcd = [&](int k) {
-        const int t0 = k * T, len = min(T, L - t0);
+        const int t0 = k * T, len = min(T, Lw - t0);
         if (w == 0 && k + 1 < nblk) issue_dt(k + 1);
         const bf16_t *bb_ = bg + (size_t)t0 * brow, *cb_ = cg + (size_t)t0 * brow;
 #pragma unroll
@@ -186,7 +204,7 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
     };
     // block k's tables from its dt piece (one wavefront; lane j is token t0 + j)
     auto make_tables = [&](int k) {
-        const int len = min(T, L - k * T);
+        const int len = min(T, Lw - k * T);
         const bool valid = l < len;
         const float raw = static_cast<float>(sm.dts[k & 1][l * 8 + (h & 7)]);
         const float st = valid ? step_size(o, raw, bias) : 0.0f;
@@ -202,14 +220,30 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
 
     // the state H^T: lane (g4, cc) of wavefront w holds rows n = 16 nt + 4 g4 + r
     // of column p = 16 w + cc
+    // (the initial state, brought through the pieces before this segment)
     floatx4 hreg[NT];
+    const size_t hoff = (size_t)(16 * w + cc) * N + 4 * g4;  // this lane's state offset
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         hreg[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
         if (init) {
-            const float4 v = *reinterpret_cast<const float4 *>(
-                init + (((size_t)b * H + h) * P + 16 * w + cc) * N + 16 * nt + 4 * g4);
+            const float4 v =
+                *reinterpret_cast<const float4 *>(init + bh * P * N + hoff + 16 * nt);
             hreg[nt] = floatx4{v.x, v.y, v.z, v.w};
+        }
+    }
+    // H <- exp(d_j) H + H_j over the pieces j before this segment (the
+    // chunk-to-chunk recurrence at piece granularity, float32)
+    for (int j = 0; j < seg * sg.kpc; ++j) {  // uniform
+        const float f = __builtin_amdgcn_exp2f(sg.ld[bh * sg.npc + j]);
+        const float *sj = sg.state + (bh * sg.npc + j) * P * N + hoff;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const float4 v = *reinterpret_cast<const float4 *>(sj + 16 * nt);
+            hreg[nt][0] = hreg[nt][0] * f + v.x;
+            hreg[nt][1] = hreg[nt][1] * f + v.y;
+            hreg[nt][2] = hreg[nt][2] * f + v.z;
+            hreg[nt][3] = hreg[nt][3] * f + v.w;
         }
     }
 
@@ -249,7 +283,7 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
             const int n0 = 16 * nt + 4 * g4, q = n0 >> 3;
             const bf16x2 lo = __builtin_convertvector(floatx2{hreg[nt][0], hreg[nt][1]}, bf16x2);
             const bf16x2 hi = __builtin_convertvector(floatx2{hreg[nt][2], hreg[nt][3]}, bf16x2);
-            *reinterpret_cast<bf16x4 *>(sm.hb + pp * N + ((q ^ (pp & 7)) << 3) + (n0 & 7)) =
+            *reinterpret_cast<bf16x4 *>(sm.hb + pp * N + ((q ^ (pp & HSW)) << 3) + (n0 & 7)) =
                 bf16x4{lo[0], lo[1], hi[0], hi[1]};
         }
     };
@@ -257,7 +291,7 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
 
     uint4 ystage[2];  // this lane's two 16-byte pieces of the previous block's outputs
     for (int k = 0; k < nblk; ++k) {
-        const int t0 = k * T, len = min(T, L - t0);
+        const int t0 = k * T;
         // every load issued so far has landed (block k's x, B, C, this and
         // the next block's dt) and every store has left; every wavefront has
         // read the previous block's staged outputs out of x buffer (k+1) & 1,
@@ -288,7 +322,7 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk) {
                 Frag<bf16_t> hf;
-                lds_frag8(hf, sm.hb + pp * N + (((4 * kk + g4) ^ (pp & 7)) << 3));
+                lds_frag8(hf, sm.hb + pp * N + (((4 * kk + g4) ^ (pp & HSW)) << 3));
                 mma(acc[pt], hf, cfr[kk]);
             }
         }
@@ -424,7 +458,7 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
             ystage[m] = *reinterpret_cast<const uint4 *>(xs + (128 * w + 64 * m + l) * 8);
     }
     {  // the last block's outputs (possibly a partial block)
-        const int t0 = (nblk - 1) * T, len = L - t0;
+        const int t0 = (nblk - 1) * T, len = Lw - t0;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int s = 128 * w + 64 * m + l, r = s >> 3, q = (s & 7) ^ (r & 7);
@@ -432,35 +466,258 @@ __global__ __launch_bounds__(256, 3) void ssd_forward_onepass_kernel(
         }
     }
 
-    if (final_state) {
+    if (final_state && seg == nseg - 1) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-            *reinterpret_cast<float4 *>(final_state + (((size_t)b * H + h) * P + 16 * w + cc) * N +
-                                        16 * nt + 4 * g4) =
+            *reinterpret_cast<float4 *>(final_state + bh * P * N + hoff + 16 * nt) =
                 make_float4(hreg[nt][0], hreg[nt][1], hreg[nt][2], hreg[nt][3]);
     }
 }
 
+// ---- segment states
+//
+// For each piece of the first S-1 segments of a (batch, head): the state the
+// piece produces from a zero state, H = sum_t exp(s_end - s_t) w_t x_t B_t^T
+// (the single-pass kernel's state update, block by block), and the piece's
+// total log2-decay. Only x, B and dt are read. Every block's inputs are loaded
+// a whole block ahead into double buffers, issued as the block before starts,
+// so one barrier per block suffices (the single-pass kernel, short of LDS,
+// single-buffers B and issues it mid-block).
+template <int N>
+struct SegStateLds {
+    __bf16 xb[2][kOpT * 64];
+    __bf16 bb[2][kOpT * N];
+    __bf16 dts[2][kOpT * 8];
+    struct {
+        float sl[kOpT], wp[kOpT];
+    } tab[2];
+};
+
+template <int N>
+__global__ __launch_bounds__(256, N == 64 ? 4 : 3) void ssd_segment_states_kernel(
+    const bf16_t *__restrict__ x, const bf16_t *__restrict__ dt, const float *__restrict__ A,
+    const bf16_t *__restrict__ B, DtOpts o, int batch, int L, int H, int G, int per,
+    OnepassSegs sg) {
+    constexpr int P = 64, T = kOpT;
+    constexpr int PPR = N / 8, NT = N / 16;
+    static_assert(N % 32 == 0 && T * PPR >= 256, "state size");
+    __shared__ __attribute__((aligned(16))) SegStateLds<N> sm;
+
+    // workgroup -> (batch, piece, head), XCD-aware as in the single-pass kernel
+    const int id = blockIdx.x;
+    const int lin = (id & 7) * per + (id >> 3);
+    if (lin >= batch * sg.nseg * H) return;  // whole workgroup
+    const int h = lin % H, bs = lin / H, pc = bs % sg.nseg, b = bs / sg.nseg, g = h / (H / G);
+    const int tb = pc * sg.len, Lw = min(sg.len, L - tb);
+    const size_t bh = (size_t)b * H + h;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l = lane_id(), g4 = l >> 4, cc = l & 15;
+    const int nblk = (Lw + T - 1) / T;
+
+    const size_t xrow = (size_t)H * P, brow = (size_t)G * N, row0 = (size_t)b * L + tb;
+    const bf16_t *xh = x + row0 * xrow + (size_t)h * P;
+    const bf16_t *bg = B + row0 * brow + (size_t)g * N;
+    const bf16_t *dth = dt + row0 * H + (h & ~7);
+    const float Ah = A[h];
+    const float bias = o.bias ? o.bias[h] : 0.0f;
+    const uint32_t xrb = (uint32_t)(xrow * 2), brb = (uint32_t)(brow * 2), drb = (uint32_t)H * 2;
+
+    auto issue_dt = [&](int k) {  // wavefront 0 only
+        const int t0 = k * T, len = min(T, Lw - t0);
+        dma16_sv(dth + (size_t)t0 * H, (uint32_t)min(l, len - 1) * drb, sm.dts[k & 1]);
+    };
+    // block k's x and B, and (wavefront 0) the dt of block k + 1
+    auto issue = [&](int k) {
+        const int t0 = k * T, len = min(T, Lw - t0);
+        if (w == 0 && k + 1 < nblk) issue_dt(k + 1);
+        const bf16_t *xk = xh + (size_t)t0 * xrow, *bk = bg + (size_t)t0 * brow;
+#pragma unroll
+        for (int i = w; i < 8; i += 4) {
+            const int s = i * 64 + l, r = s >> 3, q = (s & 7) ^ (r & 7);
+            dma16_sv(xk, (uint32_t)min(r, len - 1) * xrb + q * 16, sm.xb[k & 1] + i * 512);
+        }
+#pragma unroll
+        for (int i = w; i < T * PPR / 64; i += 4) {
+            const int s = i * 64 + l, r = s / PPR, q = (s % PPR) ^ tr_swz<PPR>(r);
+            dma16_sv(bk, (uint32_t)min(r, len - 1) * brb + q * 16, sm.bb[k & 1] + i * 512);
+        }
+    };
+    // block k's prefix sums and state weights (wavefront 0; lane j is token t0 + j)
+    auto make_tables = [&](int k) {
+        const int len = min(T, Lw - k * T);
+        const bool valid = l < len;
+        const float raw = static_cast<float>(sm.dts[k & 1][l * 8 + (h & 7)]);
+        const float st = valid ? step_size(o, raw, bias) : 0.0f;
+        const float wgt = valid ? input_weight(o, st, Ah) : 0.0f;
+        const float sl = wave_prefix_sum(st * Ah) * kLog2e;
+        const float sle = lane_value(sl, 63);
+        sm.tab[k & 1].sl[l] = sl;
+        sm.tab[k & 1].wp[l] = __builtin_amdgcn_exp2f(sle - sl) * wgt;
+    };
+
+    floatx4 hreg[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) hreg[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    float ld = 0.0f;  // the piece's log2-decay so far
+    int xo[4];
+    x_colfrag_offsets(xo, l);
+
+    if (w == 0) issue_dt(0);
+    issue(0);
+    for (int k = 0; k < nblk; ++k) {
+        // block k's inputs (and the dt of block k + 1) have landed; every
+        // wavefront is done with block k - 1's buffers and tables
+        wait_barrier<0>();
+        if (k == 0) {  // later blocks' tables are made during the block before
+            if (w == 0) make_tables(0);
+            barrier_lds();
+        }
+        if (k + 1 < nblk) issue(k + 1);
+        const __bf16 *xs = sm.xb[k & 1], *bs_ = sm.bb[k & 1];
+        const float *tsl = sm.tab[k & 1].sl, *twp = sm.tab[k & 1].wp;
+        const float sle = tsl[T - 1];
+        ld += sle;
+
+        // H^T = exp(s_end) H^T + sum_j B_j (exp(s_end - s_j) w_j x_j)^T, p tile w
+        Frag<bf16_t> xr[2];
+        x_colfrag<0>(xr[0], xs, xo[w]);
+        x_colfrag<1>(xr[1], xs, xo[w]);
+        const float dec = __builtin_amdgcn_exp2f(sle);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hreg[nt][r] *= dec;
+#pragma unroll
+        for (int js = 0; js < 2; ++js) {
+            const int jb = 32 * js + 4 * g4;
+            const floatx4 p0 = *reinterpret_cast<const floatx4 *>(twp + jb);
+            const floatx4 p1 = *reinterpret_cast<const floatx4 *>(twp + jb + 16);
+            float v[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                v[r] = xr[js].get(r) * p0[r];
+                v[4 + r] = xr[js].get(4 + r) * p1[r];
+            }
+            Frag<bf16_t> xw;
+            pack8(xw, v);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                Frag<bf16_t> bf;
+                colfrag_swz<PPR>(bf, bs_, jb, jb + 16, nt * 16);
+                mma(hreg[nt], bf, xw);
+            }
+        }
+        // the next block's tables (its dt landed with this block's inputs)
+        if (w == 0 && k + 1 < nblk) make_tables(k + 1);
+    }
+
+    float *sj = sg.state + (bh * sg.npc + pc) * P * N + (size_t)(16 * w + cc) * N + 4 * g4;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+        *reinterpret_cast<float4 *>(sj + 16 * nt) =
+            make_float4(hreg[nt][0], hreg[nt][1], hreg[nt][2], hreg[nt][3]);
+    if (w == 0 && l == 0) sg.ld[bh * sg.npc + pc] = ld;
+}
+
 bool forward_onepass_ok(int batch, int nheads, int dstate, bool bf16, const void *dt) {
-    // one workgroup per (batch, head), three per compute unit: worth it once
-    // that fills the GPU; dt is read as 16-byte pieces of 8 heads
-    return bf16 && dstate == 64 && nheads % 8 == 0 && batch * nheads >= 512 &&
+    // dt is read as 16-byte pieces of 8 heads
+    (void)batch;
+    return bf16 && (dstate == 64 || dstate == 128) && nheads % 8 == 0 &&
            (reinterpret_cast<uintptr_t>(dt) & 15u) == 0;
+}
+
+namespace {
+
+// The plan of a single-pass forward: S segments of per_seg blocks (the last
+// may hold fewer), and, when S > 1, the first S - 1 segments cut into k
+// pieces of psub blocks for the segment-state kernel.
+struct OnepassPlan {
+    int S, k, per_seg, psub;
+};
+
+size_t piece_bytes(int dstate) { return (64 * (size_t)dstate + 1) * sizeof(float); }
+
+// Enough (batch, head) pairs fill the GPU with one workgroup each (three per
+// compute unit at N = 64, two at N = 128). With fewer, each sequence is cut
+// into S segments of whole 64-token blocks, S the number of workgroups per
+// pair that still fit in one round of workgroups, each segment at least 4
+// blocks long. The segment-state kernel, lighter (four workgroups per
+// compute unit at N = 64, three at N = 128), cuts each of the first S - 1
+// segments into k pieces of at least 2 blocks so that it, too, fills the GPU.
+// The scratch holds one float32 state and one decay per piece: a smaller
+// scratch lowers k, then S.
+OnepassPlan onepass_plan(int batch, int seqlen, int nheads, int dstate, size_t scratch_bytes) {
+    const int slots = (dstate == 64 ? 3 : 2) * 256, so_slots = (dstate == 64 ? 4 : 3) * 256;
+    const int units = batch * nheads;
+    const int blocks = (seqlen + kOpT - 1) / kOpT;
+    const OnepassPlan one{1, 1, blocks, blocks};
+    const int S0 = std::min(slots / units, blocks / 4);
+    if (S0 <= 1) return one;
+    const int per = (blocks + S0 - 1) / S0;
+    const size_t max_pieces = scratch_bytes / piece_bytes(dstate);
+    int k = std::max(1, std::min(so_slots / (units * (S0 - 1)), per / 2));
+    for (;;) {
+        const int psub = (per + k - 1) / k, per_seg = k * psub;
+        const int S = (blocks + per_seg - 1) / per_seg;  // the last segment is not empty
+        if (S <= 1) return one;
+        if ((size_t)(S - 1) * k <= max_pieces) return OnepassPlan{S, k, per_seg, psub};
+        if (k == 1) return one;
+        k = std::max<int>(1, (int)std::min<size_t>(max_pieces / (S - 1), k - 1));
+    }
+}
+
+}  // namespace
+
+int forward_onepass_segments(int batch, int seqlen, int nheads, int dstate,
+                             size_t scratch_bytes) {
+    return onepass_plan(batch, seqlen, nheads, dstate, scratch_bytes).S;
+}
+
+template <int N>
+static hipError_t launch_onepass_n(const void *x, const void *dt, const float *A, const void *B,
+                                   const void *C, const float *D, const float *init,
+                                   const DtOpts &opts, int batch, int seqlen, int nheads,
+                                   int ngroups, const OnepassPlan &pl, float *scratch, void *y,
+                                   float *final_state, hipEvent_t between, hipStream_t stream) {
+    const auto xb = static_cast<const bf16_t *>(x);
+    const auto dtb = static_cast<const bf16_t *>(dt);
+    const auto Bb = static_cast<const bf16_t *>(B);
+    const auto Cb = static_cast<const bf16_t *>(C);
+    const int npc = pl.S > 1 ? (pl.S - 1) * pl.k : 0;
+    float *ld = scratch ? scratch + (size_t)batch * nheads * npc * 64 * N : nullptr;
+    if (pl.S > 1) {
+        const OnepassSegs pieces{npc, pl.psub * kOpT, npc, 0, scratch, ld};
+        const int units = batch * nheads * npc;
+        const int per = (units + 7) / 8;
+        ssd_segment_states_kernel<N><<<per * 8, 256, 0, stream>>>(
+            xb, dtb, A, Bb, opts, batch, seqlen, nheads, ngroups, per, pieces);
+        hipError_t e = hipGetLastError();
+        if (e == hipSuccess && between) e = hipEventRecord(between, stream);
+        if (e != hipSuccess) return e;
+    }
+    const OnepassSegs segs{pl.S, pl.per_seg * kOpT, npc, pl.k, scratch, ld};
+    const int units = batch * nheads * pl.S;
+    const int per = (units + 7) / 8;
+    ssd_forward_onepass_kernel<N><<<per * 8, 256, 0, stream>>>(
+        xb, dtb, A, Bb, Cb, D, init, opts, batch, seqlen, nheads, ngroups, per, segs,
+        static_cast<bf16_t *>(y), final_state);
+    return hipGetLastError();
 }
 
 hipError_t launch_forward_onepass(const void *x, const void *dt, const float *A, const void *B,
                                   const void *C, const float *D, const float *init,
                                   const DtOpts &opts, int batch, int seqlen, int nheads,
-                                  int ngroups, int dstate, void *y, float *final_state,
+                                  int ngroups, int dstate, float *scratch, size_t scratch_bytes,
+                                  void *y, float *final_state, hipEvent_t between,
                                   hipStream_t stream) {
-    if (dstate != 64) return hipErrorInvalidValue;
-    const int units = batch * nheads;
-    const int per = (units + 7) / 8;
-    ssd_forward_onepass_kernel<64><<<per * 8, 256, 0, stream>>>(
-        static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(dt), A,
-        static_cast<const bf16_t *>(B), static_cast<const bf16_t *>(C), D, init, opts, batch,
-        seqlen, nheads, ngroups, per, static_cast<bf16_t *>(y), final_state);
-    return hipGetLastError();
+    const OnepassPlan pl = onepass_plan(batch, seqlen, nheads, dstate, scratch ? scratch_bytes : 0);
+    if (dstate == 64)
+        return launch_onepass_n<64>(x, dt, A, B, C, D, init, opts, batch, seqlen, nheads,
+                                    ngroups, pl, scratch, y, final_state, between, stream);
+    if (dstate == 128)
+        return launch_onepass_n<128>(x, dt, A, B, C, D, init, opts, batch, seqlen, nheads,
+                                     ngroups, pl, scratch, y, final_state, between, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace ssd

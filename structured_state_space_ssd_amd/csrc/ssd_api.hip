@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "ssd.h"
 #include "ssd_launch.h"
 
@@ -92,6 +94,17 @@ BwdWorkspace bwd_layout(int batch, int seqlen, int nheads, int headdim, int ngro
     return w;
 }
 
+// Segments of the single-pass forward for these sizes (0: the stage kernels
+// run). Their scratch is the workspace's `states` region.
+size_t onepass_scratch(const Workspace &ws) { return ws.init_off - ws.states_off; }
+
+int onepass_plan(int batch, int seqlen, int nheads, int dstate, int chunk, bool bf16,
+                 const void *dt) {
+    if (!ssd::forward_onepass_ok(batch, nheads, dstate, bf16, dt)) return 0;
+    const Workspace ws = layout(batch, seqlen, nheads, kHeaddim, 1, dstate, chunk, bf16);
+    return ssd::forward_onepass_segments(batch, seqlen, nheads, dstate, onepass_scratch(ws));
+}
+
 int check_dims(int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate) {
     if (batch < 1 || seqlen < 1 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1)
         return SSD_ERR_SHAPE;
@@ -146,6 +159,14 @@ size_t ssd_forward_workspace_size(int batch, int seqlen, int nheads, int headdim
         !supported_chunk(chunk) || !valid_dtype(dtype))
         return 0;
     return layout(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, dtype == SSD_BF16).total;
+}
+
+int ssd_forward_plan(int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate,
+                     int chunk, int dtype, const void *dt) {
+    const int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
+    if (rc != SSD_OK) return rc;
+    if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    return onepass_plan(batch, seqlen, nheads, dstate, chunk, dtype == SSD_BF16, dt);
 }
 
 size_t ssd_forward_varlen_workspace_size(int seqlen, int nheads, int headdim, int ngroups,
@@ -282,12 +303,16 @@ int ssd_forward_ex(const void *x, const void *dt, const float *A, const void *B,
     };
 
     hipError_t e = mark(0);
-    if (ssd::forward_onepass_ok(batch, nheads, dstate, bf16, dt)) {
-        // every stage in one kernel: its time is the first interval, the others are empty
+    const int segments = onepass_plan(batch, seqlen, nheads, dstate, chunk, bf16, dt);
+    if (segments > 0) {
+        // every stage in one kernel (after the segment-state kernel when the
+        // sequences are cut into segments): intervals 0 (and 1), the others empty
         if (e == hipSuccess)
-            e = ssd::launch_forward_onepass(x, dt, A, B, C, D, init_state, o, batch, seqlen,
-                                            nheads, ngroups, dstate, y, final_state, s);
-        for (int k = 1; k <= 5 && e == hipSuccess; ++k) e = mark(k);
+            e = ssd::launch_forward_onepass(
+                x, dt, A, B, C, D, init_state, o, batch, seqlen, nheads, ngroups, dstate, states,
+                onepass_scratch(ws), y, final_state,
+                segments > 1 && events ? static_cast<hipEvent_t>(events[1]) : nullptr, s);
+        for (int k = segments > 1 ? 2 : 1; k <= 5 && e == hipSuccess; ++k) e = mark(k);
         return status_of(e);
     }
     if (e == hipSuccess)

@@ -40,16 +40,23 @@ hipError_t launch_chunk_state(const void *x, const void *B, const float *delta,
                               int batch, int seqlen, int nheads, int ngroups, int dstate, int chunk,
                               bool bf16, float *states, hipStream_t stream, bool dout = false);
 
-// Stages 2 and 3 in one kernel (bf16 only; used when state_passing_fused()):
-// writes chunk_init (bf16) and final_state (nullable) directly, without the
-// per-chunk float32 states. Reads dA_cumsum and delta (stage 1's outputs).
-// The single-pass bf16 forward (fwd_onepass.hip): whether it applies, and the launch.
+// The single-pass bf16 forward (fwd_onepass.hip): whether it applies; into
+// how many segments it cuts each sequence given `scratch_bytes` of float32
+// scratch for the segment states (1: none needed); and the launch (two
+// kernels when there are several segments: the segment states, then the
+// forward proper; `between` (nullable) is recorded between them).
 bool forward_onepass_ok(int batch, int nheads, int dstate, bool bf16, const void *dt);
+int forward_onepass_segments(int batch, int seqlen, int nheads, int dstate, size_t scratch_bytes);
 hipError_t launch_forward_onepass(const void *x, const void *dt, const float *A, const void *B,
                                   const void *C, const float *D, const float *init,
                                   const DtOpts &opts, int batch, int seqlen, int nheads,
-                                  int ngroups, int dstate, void *y, float *final_state,
+                                  int ngroups, int dstate, float *scratch, size_t scratch_bytes,
+                                  void *y, float *final_state, hipEvent_t between,
                                   hipStream_t stream);
+
+// Stages 2 and 3 in one kernel (bf16 only; used when state_passing_fused()):
+// writes chunk_init (bf16) and final_state (nullable) directly, without the
+// per-chunk float32 states. Reads dA_cumsum and delta (stage 1's outputs).
 bool state_passing_fused(int batch, int nheads, bool bf16);
 // reverse (backward): the adjoint pass (x = dy, B = C, init = dfinal; chunk_init
 // receives the gradient of the state leaving each chunk, final_state G_0).

@@ -276,3 +276,24 @@ def test_backward_workspace_size(lib):
     assert lib.ssd_backward_workspace_size(8, 2048, 80, 64, 1, 64, 1) > 0
     assert lib.ssd_backward_workspace_size(1, 256, 2, 64, 1, 128, 0) == 0  # unsupported
     assert lib.ssd_backward_workspace_size(1, 256, 2, 64, 1, 64, 0) > 0
+
+
+def test_forward_plan(lib):
+    # which path ssd_forward takes (host arithmetic only): segments of the
+    # single-pass kernel, 0 for the stage kernels, a status for bad sizes
+    al, off = 256, 258  # an aligned and a misaligned dt address (never read)
+    plan = lambda Bt, L, H, G, N, Q, dtype=1, dt=al: lib.ssd_forward_plan(Bt, L, H, 64, G, N, Q,
+                                                                           dtype, dt)
+    assert plan(8, 2048, 80, 1, 64, 256) == 1       # enough (batch, head) pairs
+    assert plan(1, 65536, 80, 8, 128, 256) > 1     # few pairs, long sequence: segments
+    assert plan(1, 100, 8, 1, 64, 64) == 1         # too short to cut
+    assert plan(4, 4096, 32, 1, 256, 128) == 0     # N 256: stage kernels
+    assert plan(8, 2048, 80, 1, 64, 256, dtype=0) == 0   # float32: stage kernels
+    assert plan(8, 2048, 68, 4, 64, 256) == 0      # heads not a multiple of 8
+    assert plan(8, 2048, 80, 1, 64, 256, dt=off) == 0    # dt not 16-byte aligned
+    assert plan(0, 2048, 80, 1, 64, 256) == SSD_ERR_SHAPE
+    assert plan(8, 2048, 80, 1, 64, 100) == SSD_ERR_UNSUPPORTED
+    # segments never outnumber the 4-block minimum, and grow as pairs shrink
+    for L in (256, 1000, 4096, 65536):
+        s = [plan(1, L, H, 1, 64, 256) for H in (512, 64, 16, 8)]
+        assert s == sorted(s) and s[-1] <= max(1, -(-L // 64) // 4), (L, s)

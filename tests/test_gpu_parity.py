@@ -33,6 +33,12 @@ def run_forward(w, d, D, init, opts=None):
     return y, fs
 
 
+def plan(w):
+    """Segments of the single-pass forward for this workload (0: stage kernels)."""
+    return _ssd().forward_plan(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate,
+                               w.chunk, torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+
+
 def with_options(w, d, raw=False, dt_softplus=False, dt_limit=None, zoh=False):
     """The option set for a case: raw=True swaps in pre-softplus dt values and
     a per-head bias (ssd_workloads.generate_dt_raw); returns the keyword
@@ -180,9 +186,10 @@ def test_slow_decay_long():
 @pytest.mark.parametrize("N,Q", [(16, 64), (32, 128), (64, 256), (128, 128), (256, 64), (64, 64),
                                  (128, 256)])
 def test_fused_state_path(N, Q):
-    w = W.small(f"fused_N{N}_Q{Q}", 8, 2 * Q + 45, 64, 64, 4, N, Q, "bf16",
+    # 68 heads (not a multiple of 8): the stage kernels run at every N
+    w = W.small(f"fused_N{N}_Q{Q}", 8, 2 * Q + 45, 68, 64, 4, N, Q, "bf16",
                 seed=600 + N + Q, init_std=0.2)
-    assert w.batch * w.nheads >= 512
+    assert w.batch * w.nheads >= 512 and plan(w) == 0
     check_forward(w)
 
 
@@ -267,6 +274,54 @@ def test_onepass_misaligned_dt_falls_back():
     assert e < tol(w.dtype), e
 
 
+# ----------------------- single-pass forward over segments (few (batch, head) pairs)
+#
+# With fewer (batch, head) pairs than fill the GPU, each sequence is cut into
+# S segments of whole 64-token blocks: a first kernel computes each segment's
+# state from zero, the single-pass kernel starts each segment from the state
+# the earlier segments pass on. Cases: N 64 and 128; S from 2 to 8, ragged
+# last segments, an initial state and none, several groups (every step-size
+# option further down); a single segment at N 128 (enough pairs) and sequences too short to
+# cut.
+
+@pytest.mark.parametrize("N", [64, 128])
+@pytest.mark.parametrize("L", [37 * 64 + 13, 8 * 64, 1000])
+def test_segments(N, L):
+    w = W.small(f"seg_N{N}_L{L}", 1, L, 16, 64, 2, N, 256, "bf16", seed=900 + L + N,
+                init_std=0.2)
+    S = plan(w)
+    print_case(f"   segments {S}")
+    assert S > 1
+    check_forward(w)
+
+
+def test_segments_many_groups_no_init():
+    w = W.small("seg_g8", 2, 3000, 8, 64, 8, 128, 128, "bf16", seed=930)
+    assert plan(w) > 1
+    check_forward(w)
+
+
+def test_segments_strong_decay():
+    # fast decay: each segment's contribution to the next almost vanishes
+    w = W.small("seg_strong", 1, 2000, 16, 64, 1, 64, 256, "bf16", seed=950, init_std=0.2,
+                dt_lo=0.2, dt_hi=1.0)
+    assert plan(w) > 1
+    check_forward(w, both_D=False)
+
+
+@pytest.mark.parametrize("L", [1, 100, 255])
+def test_segments_too_short_to_cut(L):
+    w = W.small(f"seg_short_L{L}", 1, L, 8, 64, 1, 128, 64, "bf16", seed=960 + L, init_std=0.2)
+    assert plan(w) == 1
+    check_forward(w)
+
+
+def test_onepass_n128_one_segment():
+    w = W.small("onepass_n128", 8, 333, 64, 64, 4, 128, 256, "bf16", seed=970, init_std=0.2)
+    assert plan(w) == 1
+    check_forward(w)
+
+
 def test_heads_not_multiple_of_8_many_units():
     # 9 x 60 units but 60 heads: the separate-stage path (its fused state kernel)
     check_forward(W.small("h60", 9, 300, 60, 64, 3, 64, 128, "bf16", seed=840, init_std=0.2))
@@ -297,10 +352,19 @@ def test_options_forward(name, dtype):
 
 @pytest.mark.parametrize("name", ["zoh", "all_zoh"])
 def test_options_fused_state_path(name):
-    w = W.small(f"opt_fused_{name}", 8, 2 * 256 + 45, 64, 64, 4, 64, 256, "bf16", seed=710,
+    w = W.small(f"opt_fused_{name}", 8, 2 * 256 + 45, 68, 64, 4, 64, 256, "bf16", seed=710,
                 init_std=0.2)
-    assert w.batch * w.nheads >= 512
+    assert w.batch * w.nheads >= 512 and plan(w) == 0
     check_forward(w, **OPTION_SETS[name])
+
+
+@pytest.mark.parametrize("name", sorted(OPTION_SETS))
+def test_segments_options(name):
+    # the single-pass forward over segments (N 128), every option set
+    w = W.small(f"seg_opt_{name}", 2, 1500, 8, 64, 2, 128, 256, "bf16", seed=940,
+                init_std=0.2)
+    assert plan(w) > 1
+    check_forward(w, both_D=False, **OPTION_SETS[name])
 
 
 def test_options_strong_decay_zoh():
