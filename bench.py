@@ -507,9 +507,8 @@ WRITE_CMD = ('rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/write" -o 
              '-- python bench.py --counters')
 # kernel-name fragment -> stage, first match wins (the fused stage-2+3 kernel
 # fills the chunk_state interval of the forward)
-KERNEL_OF = {"onepass_kernel<64, true>": "segment_states",
-             "onepass_kernel<128, true>": "segment_states",
-             "ssd_forward_onepass": "forward_onepass",
+KERNEL_OF = {"segment_states_kernel": "segment_states",
+             "ssd_forward_onepass": "forward_onepass", "onepass_varlen": "packed: token int4s",
              "chunk_cumsum_kernel": "chunk_cumsum", "chunk_state_passing": "chunk_state",
              "state_passing_kernel": "state_passing", "chunk_state": "chunk_state",
              "chunk_cb_kernel": "chunk_cb", "chunk_scan": "chunk_scan",

@@ -257,9 +257,18 @@ int ssd_backward(const void *x, const void *dt, const float *A, const void *B, c
  *   workspace   at least ssd_forward_varlen_workspace_size(...) bytes,
  *               256-byte aligned: ssd_forward's layout at batch 1, then one
  *               int32 per token position of the chunk-padded layout.
- * Enqueues the separate stages (never the fused stage 2 + 3 kernel), each
- * masking pairs of tokens from different sequences, then one kernel for the
- * per-sequence states. nseq < 1 returns SSD_ERR_SHAPE.
+ * Where ssd_forward would run its single-pass kernel at batch 1
+ * (ssd_forward_plan(1, ...) > 0: SSD_BF16, dstate 64 or 128, nheads a
+ * multiple of 8, 16-byte aligned dt) it runs that kernel with sequence masks
+ * (over segments of the token axis, with the segment-state kernel first):
+ * rows ignore the state of earlier sequences, the state restarts from zero
+ * where a sequence begins, and each sequence's final state is taken at its
+ * last token. The workspace then holds one int4 per token (first token of
+ * its sequence, sequence index, last-token flag) where dA_cumsum would be,
+ * and the segment scratch as for ssd_forward. Otherwise it enqueues the
+ * separate stages (never the fused stage 2 + 3 kernel), each masking pairs of
+ * tokens from different sequences, then one kernel for the per-sequence
+ * states. nseq < 1 returns SSD_ERR_SHAPE.
  */
 size_t ssd_forward_varlen_workspace_size(int seqlen, int nheads, int headdim, int ngroups,
                                          int dstate, int chunk, int dtype);

@@ -62,7 +62,22 @@ namespace {
 
 constexpr int kOpT = 64;  // tokens per block
 
-template <int N>
+// Packed sequences (VL): one int4 per token, {first token of its sequence,
+// sequence index, whether it is its sequence's last token, 0}.
+template <bool VL>
+struct VlTab {  // per block: each row's first token of its sequence (relative
+                // to the block; negative: the sequence began earlier), the
+                // state's decay across the block (0 where a sequence begins in
+                // it) and the tokens that end a sequence
+    int fs[kOpT];
+    float dec;
+    uint32_t ends[2];
+    int pad;
+};
+template <>
+struct VlTab<false> {};
+
+template <int N, bool VL>
 struct OnepassLds {
     __bf16 xb[2][kOpT * 64];
     __bf16 bb[kOpT * N];
@@ -74,6 +89,8 @@ struct OnepassLds {
     struct {
         float sl[kOpT], wt[kOpT], wp[kOpT], cf[32];
     } tab[2];
+    VlTab<VL> vt[2];
+    int4 mts[VL ? 2 : 1][VL ? kOpT : 1];  // the tokens' int4 of blocks k, k+1
 };
 
 // One 16-byte-per-lane global-to-LDS load from the wave-uniform base `sbase`
@@ -130,18 +147,46 @@ struct OnepassSegs {
     float *ld;     // float32 [Bt][H][npc]
 };
 
-template <int N>
+// Packed sequences: the tokens' int4 (see VlTab) and each sequence's final
+// state, float32 [nseq][H][P][N].
+struct OnepassVl {
+    const int4 *meta;
+    float *seq_states;
+};
+
+// The masks of packed sequences (VL) from block k's token int4s, for rows and
+// state weights: wavefront 0, lane j = token j of the block (len valid).
+template <bool VL>
+__device__ __forceinline__ void vl_tables(VlTab<VL> &vt, const int4 &m, int tblk, int len,
+                                          float sle, float &wp) {
+    if constexpr (VL) {
+        const int l = lane_id();
+        const bool valid = l < len;
+        const int fs = m.x - tblk;  // first token of this token's sequence, block-relative
+        const int fsl = __builtin_amdgcn_readlane(fs, len - 1);  // ... of the block's last token
+        if (l < fsl) wp = 0.0f;  // a sequence the block's last token does not belong to
+        const uint64_t ends = __ballot(valid && m.z != 0);
+        vt.fs[l] = valid ? fs : kOpT;
+        if (l == 0) {
+            vt.dec = fsl < 0 ? __builtin_amdgcn_exp2f(sle) : 0.0f;
+            vt.ends[0] = (uint32_t)ends;
+            vt.ends[1] = (uint32_t)(ends >> 32);
+        }
+    }
+}
+
+template <int N, bool VL>
 __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ dt, const float *__restrict__ A,
     const bf16_t *__restrict__ B, const bf16_t *__restrict__ C, const float *__restrict__ D,
     const float *__restrict__ init, DtOpts o, int batch, int L, int H, int G, int per,
-    OnepassSegs sg, bf16_t *__restrict__ y, float *__restrict__ final_state) {
+    OnepassSegs sg, OnepassVl vl, bf16_t *__restrict__ y, float *__restrict__ final_state) {
     constexpr int P = 64, T = kOpT;
     constexpr int PPR = N / 8, NT = N / 16, NK = N / 32;
     constexpr int HSW = PPR >= 16 ? 15 : PPR - 1;  // piece swizzle mask of the bf16 state rows
     constexpr int BL = T * PPR / 256;  // B (and C) loads per lane per block
     static_assert(N % 32 == 0 && BL >= 1, "state size");
-    __shared__ __attribute__((aligned(16))) OnepassLds<N> sm;
+    __shared__ __attribute__((aligned(16))) OnepassLds<N, VL> sm;
 
     // workgroup -> (batch, segment, head): consecutive workgroup ids go round
     // the 8 XCDs, so id -> (id % 8) * per + id / 8 gives each XCD a contiguous
@@ -190,6 +235,8 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kern
     auto issue_dt = [&](int k) {  // wavefront 0 only
         const int t0 = k * T, len = min(T, Lw - t0);
         dma16_sv(dth + (size_t)t0 * H, (uint32_t)min(l, len - 1) * drb, sm.dts[k & 1]);
+        if constexpr (VL)
+            dma16_sv(vl.meta + row0 + t0, (uint32_t)min(l, len - 1) * 16, sm.mts[k & 1]);
     };
     // B and C of block k, after dt of block k+1 (so that waiting for block k's
     // B and C also brings the dt the next block's step sizes are made from)
@@ -212,9 +259,11 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kern
         const float sl = wave_prefix_sum(st * Ah) * kLog2e;
         const float sle = lane_value(sl, 63), s31 = lane_value(sl, 31);
         auto &t = sm.tab[k & 1];
+        float wp = __builtin_amdgcn_exp2f(sle - sl) * wgt;
+        if constexpr (VL) vl_tables<VL>(sm.vt[k & 1], sm.mts[k & 1][l], tb + k * T, len, sle, wp);
         t.sl[l] = sl;
         t.wt[l] = wgt;
-        t.wp[l] = __builtin_amdgcn_exp2f(sle - sl) * wgt;
+        t.wp[l] = wp;
         if (l < 32) t.cf[l] = __builtin_amdgcn_exp2f(s31 - sl) * wgt;
     };
 
@@ -305,7 +354,15 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kern
         }
         const float *tsl = sm.tab[k & 1].sl, *twt = sm.tab[k & 1].wt, *twp = sm.tab[k & 1].wp,
                     *tcf = sm.tab[k & 1].cf;
-        const float dec = __builtin_amdgcn_exp2f(tsl[T - 1]), s31 = tsl[31], si = tsl[i];
+        const float s31 = tsl[31], si = tsl[i];
+        float dec;
+        int fsi = 0;  // packed sequences: row i's first token of its sequence (block-relative)
+        if constexpr (VL) {
+            dec = sm.vt[k & 1].dec;
+            fsi = sm.vt[k & 1].fs[i];
+        } else {
+            dec = __builtin_amdgcn_exp2f(tsl[T - 1]);
+        }
 
         // C_i (n = 32 kk + 8 g4 .. +7), the B operand of both C H and C B^T
         Frag<bf16_t> cfr[NK];
@@ -327,7 +384,8 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kern
             }
         }
         {
-            const float e = __builtin_amdgcn_exp2f(si);
+            float e = __builtin_amdgcn_exp2f(si);
+            if constexpr (VL) e = fsi < 0 ? e : 0.0f;  // H belongs to row i's sequence
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
@@ -374,8 +432,8 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kern
                 for (int r = 0; r < 4; ++r) {
                     const float a0 = m[0][r] * (__builtin_amdgcn_exp2f(si - s0[r]) * w0[r]);
                     const float a1 = m[1][r] * (__builtin_amdgcn_exp2f(si - s1[r]) * w1[r]);
-                    v[r] = j0 + r <= i ? a0 : 0.0f;
-                    v[4 + r] = j0 + 16 + r <= i ? a1 : 0.0f;
+                    v[r] = j0 + r <= i && (!VL || j0 + r >= fsi) ? a0 : 0.0f;
+                    v[4 + r] = j0 + 16 + r <= i && (!VL || j0 + 16 + r >= fsi) ? a1 : 0.0f;
                 }
             } else {
                 // wholly below it (i >= 32 > j): exp(s_i - s_31) exp(s_31 - s_j) w_j,
@@ -387,6 +445,10 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kern
                 for (int r = 0; r < 4; ++r) {
                     v[r] = m[0][r] * (c0[r] * rowf);
                     v[4 + r] = m[1][r] * (c1[r] * rowf);
+                    if constexpr (VL) {  // tokens of earlier sequences
+                        v[r] = j0 + r >= fsi ? v[r] : 0.0f;
+                        v[4 + r] = j0 + 16 + r >= fsi ? v[4 + r] : 0.0f;
+                    }
                 }
             }
             Frag<bf16_t> mf;
@@ -409,6 +471,52 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kern
         Frag<bf16_t> xr[2];
         x_colfrag<0>(xr[0], xs, xo[w]);
         x_colfrag<1>(xr[1], xs, xo[w]);
+        const int lenk = min(T, Lw - t0);
+        if constexpr (VL) {
+            // sequences that end inside the block, before its last token je =
+            // lenk - 1: the state after their last token e, [fs_e < 0] e^{s_e}
+            // H + sum_{fs_e <= j <= e} e^{s_e - s_j} w_j x_j B_j^T, from the
+            // state entering the block (this wavefront's columns)
+            uint64_t ends = ((uint64_t)sm.vt[k & 1].ends[1] << 32) | sm.vt[k & 1].ends[0];
+            ends &= ~(1ull << (lenk - 1));
+            while (ends && vl.seq_states) {  // uniform
+                const int e = __builtin_ctzll(ends);
+                ends &= ends - 1;
+                const int fe = sm.vt[k & 1].fs[e];
+                const float se = tsl[e];
+                const float f = fe < 0 ? __builtin_amdgcn_exp2f(se) : 0.0f;
+                floatx4 he[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) he[nt][r] = hreg[nt][r] * f;
+#pragma unroll
+                for (int js = 0; js < 2; ++js) {
+                    const int jb = 32 * js + 4 * g4;
+                    float v[8];
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        const int j = jb + (r < 4 ? r : 12 + r);
+                        v[r] = j >= fe && j <= e ? xr[js].get(r) *
+                                                       (__builtin_amdgcn_exp2f(se - tsl[j]) * twt[j])
+                                                 : 0.0f;
+                    }
+                    Frag<bf16_t> xw;
+                    pack8(xw, v);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        Frag<bf16_t> bf;
+                        colfrag_swz<PPR>(bf, sm.bb, jb, jb + 16, nt * 16);
+                        mma(he[nt], bf, xw);
+                    }
+                }
+                float *out = vl.seq_states + ((size_t)sm.mts[k & 1][e].y * H + h) * P * N + hoff;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    *reinterpret_cast<float4 *>(out + 16 * nt) =
+                        make_float4(he[nt][0], he[nt][1], he[nt][2], he[nt][3]);
+            }
+        }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -431,6 +539,18 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kern
                 Frag<bf16_t> bf;
                 colfrag_swz<PPR>(bf, sm.bb, jb, jb + 16, nt * 16);
                 mma(hreg[nt], bf, xw);
+            }
+        }
+        if constexpr (VL) {
+            // a sequence ending at the block's last token: the state is H itself
+            const uint32_t eb = sm.vt[k & 1].ends[(lenk - 1) >> 5];
+            if (((eb >> ((lenk - 1) & 31)) & 1u) && vl.seq_states) {  // uniform
+                float *out =
+                    vl.seq_states + ((size_t)sm.mts[k & 1][lenk - 1].y * H + h) * P * N + hoff;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    *reinterpret_cast<float4 *>(out + 16 * nt) =
+                        make_float4(hreg[nt][0], hreg[nt][1], hreg[nt][2], hreg[nt][3]);
             }
         }
 
@@ -483,25 +603,27 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kern
 // a whole block ahead into double buffers, issued as the block before starts,
 // so one barrier per block suffices (the single-pass kernel, short of LDS,
 // single-buffers B and issues it mid-block).
-template <int N>
+template <int N, bool VL>
 struct SegStateLds {
     __bf16 xb[2][kOpT * 64];
     __bf16 bb[2][kOpT * N];
     __bf16 dts[2][kOpT * 8];
     struct {
-        float sl[kOpT], wp[kOpT];
+        float wp[kOpT];
+        float dec, ld;  // the state's decay across the block and its log2 (-inf: a reset)
     } tab[2];
+    int4 mts[VL ? 2 : 1][VL ? kOpT : 1];  // packed sequences: the tokens' int4 of blocks k, k+1
 };
 
-template <int N>
+template <int N, bool VL>
 __global__ __launch_bounds__(256, N == 64 ? 4 : 3) void ssd_segment_states_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ dt, const float *__restrict__ A,
     const bf16_t *__restrict__ B, DtOpts o, int batch, int L, int H, int G, int per,
-    OnepassSegs sg) {
+    OnepassSegs sg, OnepassVl vl) {
     constexpr int P = 64, T = kOpT;
     constexpr int PPR = N / 8, NT = N / 16;
     static_assert(N % 32 == 0 && T * PPR >= 256, "state size");
-    __shared__ __attribute__((aligned(16))) SegStateLds<N> sm;
+    __shared__ __attribute__((aligned(16))) SegStateLds<N, VL> sm;
 
     // workgroup -> (batch, piece, head), XCD-aware as in the single-pass kernel
     const int id = blockIdx.x;
@@ -525,6 +647,8 @@ __global__ __launch_bounds__(256, N == 64 ? 4 : 3) void ssd_segment_states_kerne
     auto issue_dt = [&](int k) {  // wavefront 0 only
         const int t0 = k * T, len = min(T, Lw - t0);
         dma16_sv(dth + (size_t)t0 * H, (uint32_t)min(l, len - 1) * drb, sm.dts[k & 1]);
+        if constexpr (VL)
+            dma16_sv(vl.meta + row0 + t0, (uint32_t)min(l, len - 1) * 16, sm.mts[k & 1]);
     };
     // block k's x and B, and (wavefront 0) the dt of block k + 1
     auto issue = [&](int k) {
@@ -551,8 +675,19 @@ __global__ __launch_bounds__(256, N == 64 ? 4 : 3) void ssd_segment_states_kerne
         const float wgt = valid ? input_weight(o, st, Ah) : 0.0f;
         const float sl = wave_prefix_sum(st * Ah) * kLog2e;
         const float sle = lane_value(sl, 63);
-        sm.tab[k & 1].sl[l] = sl;
-        sm.tab[k & 1].wp[l] = __builtin_amdgcn_exp2f(sle - sl) * wgt;
+        float wp = __builtin_amdgcn_exp2f(sle - sl) * wgt;
+        bool reset = false;  // packed sequences: the block's last token's sequence begins in it
+        if constexpr (VL) {
+            const int fs = sm.mts[k & 1][l].x - (tb + k * T);
+            const int fsl = __builtin_amdgcn_readlane(fs, len - 1);
+            if (l < fsl) wp = 0.0f;
+            reset = fsl >= 0;
+        }
+        sm.tab[k & 1].wp[l] = wp;
+        if (l == 0) {
+            sm.tab[k & 1].dec = reset ? 0.0f : __builtin_amdgcn_exp2f(sle);
+            sm.tab[k & 1].ld = reset ? -__builtin_inff() : sle;
+        }
     };
 
     floatx4 hreg[NT];
@@ -574,15 +709,14 @@ __global__ __launch_bounds__(256, N == 64 ? 4 : 3) void ssd_segment_states_kerne
         }
         if (k + 1 < nblk) issue(k + 1);
         const __bf16 *xs = sm.xb[k & 1], *bs_ = sm.bb[k & 1];
-        const float *tsl = sm.tab[k & 1].sl, *twp = sm.tab[k & 1].wp;
-        const float sle = tsl[T - 1];
-        ld += sle;
+        const float *twp = sm.tab[k & 1].wp;
+        const float dec = sm.tab[k & 1].dec;
+        ld += sm.tab[k & 1].ld;
 
         // H^T = exp(s_end) H^T + sum_j B_j (exp(s_end - s_j) w_j x_j)^T, p tile w
         Frag<bf16_t> xr[2];
         x_colfrag<0>(xr[0], xs, xo[w]);
         x_colfrag<1>(xr[1], xs, xo[w]);
-        const float dec = __builtin_amdgcn_exp2f(sle);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -673,12 +807,13 @@ int forward_onepass_segments(int batch, int seqlen, int nheads, int dstate,
     return onepass_plan(batch, seqlen, nheads, dstate, scratch_bytes).S;
 }
 
-template <int N>
+template <int N, bool VL>
 static hipError_t launch_onepass_n(const void *x, const void *dt, const float *A, const void *B,
                                    const void *C, const float *D, const float *init,
                                    const DtOpts &opts, int batch, int seqlen, int nheads,
-                                   int ngroups, const OnepassPlan &pl, float *scratch, void *y,
-                                   float *final_state, hipEvent_t between, hipStream_t stream) {
+                                   int ngroups, const OnepassPlan &pl, float *scratch,
+                                   const OnepassVl &vl, void *y, float *final_state,
+                                   hipEvent_t between, hipStream_t stream) {
     const auto xb = static_cast<const bf16_t *>(x);
     const auto dtb = static_cast<const bf16_t *>(dt);
     const auto Bb = static_cast<const bf16_t *>(B);
@@ -689,8 +824,8 @@ static hipError_t launch_onepass_n(const void *x, const void *dt, const float *A
         const OnepassSegs pieces{npc, pl.psub * kOpT, npc, 0, scratch, ld};
         const int units = batch * nheads * npc;
         const int per = (units + 7) / 8;
-        ssd_segment_states_kernel<N><<<per * 8, 256, 0, stream>>>(
-            xb, dtb, A, Bb, opts, batch, seqlen, nheads, ngroups, per, pieces);
+        ssd_segment_states_kernel<N, VL><<<per * 8, 256, 0, stream>>>(
+            xb, dtb, A, Bb, opts, batch, seqlen, nheads, ngroups, per, pieces, vl);
         hipError_t e = hipGetLastError();
         if (e == hipSuccess && between) e = hipEventRecord(between, stream);
         if (e != hipSuccess) return e;
@@ -698,8 +833,8 @@ static hipError_t launch_onepass_n(const void *x, const void *dt, const float *A
     const OnepassSegs segs{pl.S, pl.per_seg * kOpT, npc, pl.k, scratch, ld};
     const int units = batch * nheads * pl.S;
     const int per = (units + 7) / 8;
-    ssd_forward_onepass_kernel<N><<<per * 8, 256, 0, stream>>>(
-        xb, dtb, A, Bb, Cb, D, init, opts, batch, seqlen, nheads, ngroups, per, segs,
+    ssd_forward_onepass_kernel<N, VL><<<per * 8, 256, 0, stream>>>(
+        xb, dtb, A, Bb, Cb, D, init, opts, batch, seqlen, nheads, ngroups, per, segs, vl,
         static_cast<bf16_t *>(y), final_state);
     return hipGetLastError();
 }
@@ -709,15 +844,69 @@ hipError_t launch_forward_onepass(const void *x, const void *dt, const float *A,
                                   const DtOpts &opts, int batch, int seqlen, int nheads,
                                   int ngroups, int dstate, float *scratch, size_t scratch_bytes,
                                   void *y, float *final_state, hipEvent_t between,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, const void *varlen_meta,
+                                  float *seq_states) {
     const OnepassPlan pl = onepass_plan(batch, seqlen, nheads, dstate, scratch ? scratch_bytes : 0);
-    if (dstate == 64)
-        return launch_onepass_n<64>(x, dt, A, B, C, D, init, opts, batch, seqlen, nheads,
-                                    ngroups, pl, scratch, y, final_state, between, stream);
-    if (dstate == 128)
-        return launch_onepass_n<128>(x, dt, A, B, C, D, init, opts, batch, seqlen, nheads,
-                                     ngroups, pl, scratch, y, final_state, between, stream);
+    const OnepassVl vl{static_cast<const int4 *>(varlen_meta), seq_states};
+    if (varlen_meta && (batch != 1 || init || final_state)) return hipErrorInvalidValue;
+#define SSD_ONEPASS(NN, VV)                                                                      \
+    return launch_onepass_n<NN, VV>(x, dt, A, B, C, D, init, opts, batch, seqlen, nheads,       \
+                                    ngroups, pl, scratch, vl, y, final_state, between, stream)
+    if (dstate == 64) {
+        if (varlen_meta) SSD_ONEPASS(64, true);
+        SSD_ONEPASS(64, false);
+    }
+    if (dstate == 128) {
+        if (varlen_meta) SSD_ONEPASS(128, true);
+        SSD_ONEPASS(128, false);
+    }
+#undef SSD_ONEPASS
     return hipErrorInvalidValue;
+}
+
+// ---- packed sequences: the tokens' int4 and the states of empty sequences
+
+// meta[t] = {first token of t's sequence, its index, whether t is its last
+// token, 0} for t < L. Any cu_seqlens contents give in-range values (the
+// index is the largest k < nseq with cu[k] <= t).
+__global__ __launch_bounds__(256) void onepass_varlen_meta_kernel(const int *__restrict__ cu,
+                                                                  int nseq, int L,
+                                                                  int4 *__restrict__ meta) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= L) return;
+    int lo = 0, hi = nseq - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    const int start = min(max(cu[lo], 0), t);
+    const bool last = t == L - 1 || (lo + 1 <= nseq && cu[lo + 1] == t + 1);
+    meta[t] = make_int4(start, lo, last ? 1 : 0, 0);
+}
+
+// zero states for the empty sequences (no token ends them)
+__global__ __launch_bounds__(256) void onepass_varlen_empty_kernel(const int *__restrict__ cu,
+                                                                   int PN,
+                                                                   float *__restrict__ seq_states) {
+    const int k = blockIdx.x, h = blockIdx.y, H = gridDim.y;
+    if (cu[k + 1] > cu[k]) return;  // whole workgroup
+    float4 *out = reinterpret_cast<float4 *>(seq_states + ((size_t)k * H + h) * PN);
+    for (int i = threadIdx.x; i < PN / 4; i += 256) out[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+}
+
+hipError_t launch_onepass_varlen_prep(const int *cu_seqlens, int nseq, int seqlen, int nheads,
+                                      int dstate, void *meta, float *seq_states,
+                                      hipStream_t stream) {
+    onepass_varlen_meta_kernel<<<(seqlen + 255) / 256, 256, 0, stream>>>(
+        cu_seqlens, nseq, seqlen, static_cast<int4 *>(meta));
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && seq_states) {
+        onepass_varlen_empty_kernel<<<dim3(nseq, nheads), 256, 0, stream>>>(
+            cu_seqlens, 64 * dstate, seq_states);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 }  // namespace ssd

@@ -378,6 +378,18 @@ int ssd_forward_varlen(const void *x, const void *dt, const float *A, const void
     void *cb = base + ws.cb_off;
     int *seg = reinterpret_cast<int *>(base + seg_off);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (onepass_plan(1, seqlen, nheads, dstate, chunk, bf16, dt) > 0) {
+        // the single-pass kernel with sequence masks; the tokens' int4s (16
+        // bytes per token) go where dA_cumsum would (H >= 8 floats per token)
+        void *meta = base + ws.cumsum_off;
+        hipError_t e = ssd::launch_onepass_varlen_prep(cu_seqlens, nseq, seqlen, nheads, dstate,
+                                                       meta, seq_states, s);
+        if (e == hipSuccess)
+            e = ssd::launch_forward_onepass(x, dt, A, B, C, D, nullptr, o, 1, seqlen, nheads,
+                                            ngroups, dstate, states, onepass_scratch(ws), y,
+                                            nullptr, nullptr, s, meta, seq_states);
+        return status_of(e);
+    }
     // the separate stages, each masking by seg (no fused stage 2 + 3 here)
     hipError_t e = ssd::launch_varlen_seg(cu_seqlens, nseq, seqlen, chunk, seg, s);
     if (e == hipSuccess)

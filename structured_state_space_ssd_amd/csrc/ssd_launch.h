@@ -47,12 +47,20 @@ hipError_t launch_chunk_state(const void *x, const void *B, const float *delta,
 // forward proper; `between` (nullable) is recorded between them).
 bool forward_onepass_ok(int batch, int nheads, int dstate, bool bf16, const void *dt);
 int forward_onepass_segments(int batch, int seqlen, int nheads, int dstate, size_t scratch_bytes);
+// Packed sequences (batch 1, no init_state / final_state): `varlen_meta`
+// holds one int4 per token made by launch_onepass_varlen_prep from cu_seqlens
+// (16 * seqlen bytes, 16-byte aligned); each sequence's final state goes to
+// seq_states (nullable) [nseq][H][P][N]; the prep also zeroes the empty ones.
 hipError_t launch_forward_onepass(const void *x, const void *dt, const float *A, const void *B,
                                   const void *C, const float *D, const float *init,
                                   const DtOpts &opts, int batch, int seqlen, int nheads,
                                   int ngroups, int dstate, float *scratch, size_t scratch_bytes,
                                   void *y, float *final_state, hipEvent_t between,
-                                  hipStream_t stream);
+                                  hipStream_t stream, const void *varlen_meta = nullptr,
+                                  float *seq_states = nullptr);
+hipError_t launch_onepass_varlen_prep(const int *cu_seqlens, int nseq, int seqlen, int nheads,
+                                      int dstate, void *meta, float *seq_states,
+                                      hipStream_t stream);
 
 // Stages 2 and 3 in one kernel (bf16 only; used when state_passing_fused()):
 // writes chunk_init (bf16) and final_state (nullable) directly, without the

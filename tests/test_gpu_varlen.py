@@ -175,3 +175,102 @@ def test_varlen_errors():
         ssd.forward_varlen(x, dt, A, B, B, None, torch.tensor([0, 10], device="cuda"))
     with pytest.raises(ValueError):  # no sequence
         ssd.forward_varlen(x, dt, A, B, B, None, torch.tensor([0], dtype=torch.int32, device="cuda"))
+
+
+# ------------------- packed sequences on the single-pass kernel (bf16, N 64 / 128)
+#
+# With nheads a multiple of 8 the packed forward runs as the single-pass
+# kernel with sequence masks (over several segments of the token axis): rows
+# ignore the entering state and earlier sequences' tokens, the state resets
+# where a sequence begins, and a sequence ending inside a 64-token block gets
+# its state from the state entering the block and the block's own tokens.
+
+def _plan(w):
+    return _ssd().forward_plan(1, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk,
+                               torch.bfloat16)
+
+
+# boundaries on 64-token block starts (64, 128, 192, 1024) and ends (63, 191),
+# inside blocks and at their 32-token half (160), an empty sequence, one-token
+# sequences (at the start, 1999), sequences across the segments of the
+# token axis (200 .. 700 .. 1024 .. 1500)
+EXPLICIT_OP = [0, 1, 1, 9, 63, 64, 65, 128, 160, 191, 192, 200, 700, 701, 1024, 1500, 1999,
+               2000]
+
+
+@pytest.mark.parametrize("N", [64, 128])
+def test_varlen_onepass_explicit_boundaries(N):
+    w = _w(f"vl_op_explicit_N{N}", 2000, 8, 2, N, 256, "bf16", 880 + N)
+    assert _plan(w) > 1
+    check_varlen(w, EXPLICIT_OP)
+
+
+@pytest.mark.parametrize("N", [64, 128])
+def test_varlen_onepass_length_mix(N):
+    L = 3000
+    cu = W.packed_cu_seqlens(L, 400, seed=890 + N)
+    w = _w(f"vl_op_mix_N{N}", L, 16, 2, N, 128, "bf16", 891 + N)
+    assert _plan(w) > 1
+    check_varlen(w, cu)
+
+
+def test_varlen_onepass_many_short_sequences():
+    # every sequence shorter than 12 tokens: several ends in every block
+    L = 1024
+    cu = W.packed_cu_seqlens(L, 12, seed=900)
+    w = _w("vl_op_short", L, 8, 1, 64, 256, "bf16", 901)
+    assert cu.size > 100 and _plan(w) > 1
+    check_varlen(w, cu)
+
+
+def test_varlen_onepass_with_options():
+    L = 1200
+    cu = W.packed_cu_seqlens(L, 300, seed=910)
+    w = _w("vl_op_opts", L, 8, 2, 128, 128, "bf16", 911)
+    assert _plan(w) > 1
+    check_varlen(w, cu, raw=True, dt_softplus=True, dt_limit=(4e-3, 3e-2), zoh=True)
+
+
+@pytest.mark.parametrize("N", [64, 128])
+def test_varlen_onepass_one_sequence_equals_forward(N):
+    """One sequence: the masks select what the plain single-pass forward
+    computes (several segments). The two kernels are separate compilations
+    whose multiply-adds may fuse differently, so outputs agree to rounding:
+    almost every y element identical, the rest within rel-L2 1e-4 (a
+    hundredth of the bf16 tolerance), float32 states within 1e-5."""
+    ssd = _ssd()
+    w = _w(f"vl_op_single_N{N}", 1500, 8, 2, N, 256, "bf16", 920 + N)
+    assert _plan(w) > 1
+    d = W.generate(w)
+    g = {k: up(d[k]) for k in ("x", "dt", "A", "B", "C", "D")}
+    cu = torch.tensor([0, w.seqlen], dtype=torch.int32, device="cuda")
+    y1, s1 = ssd.forward_varlen(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], cu,
+                                chunk=w.chunk, return_seq_states=True)
+    y2, s2 = ssd.forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk=w.chunk,
+                         return_final_state=True)
+    torch.cuda.synchronize()
+    same = (y1 == y2).float().mean().item()
+    ey, es = rel_l2(down(y1), down(y2)), rel_l2(down(s1[0]), down(s2[0]))
+    print_case(f"   identical y: {same:.6f}, rel_l2 y {ey:.2e}, state {es:.2e}")
+    assert same > 0.99 and ey < 1e-4 and es < 1e-5
+
+
+def test_varlen_onepass_sequences_are_independent():
+    """Changing one sequence's inputs changes nothing in the others."""
+    ssd = _ssd()
+    w = _w("vl_op_indep", 1000, 8, 1, 64, 64, "bf16", 930)
+    d = W.generate(w)
+    g = {k: up(d[k]) for k in ("x", "dt", "A", "B", "C", "D")}
+    cu = torch.tensor([0, 70, 450, 451, 1000], dtype=torch.int32, device="cuda")
+    assert _plan(w) > 1
+    y1, s1 = ssd.forward_varlen(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], cu, chunk=64,
+                                return_seq_states=True)
+    x2 = g["x"].clone()
+    x2[0, 70:450] = torch.randn_like(x2[0, 70:450].float()).to(x2.dtype)
+    y2, s2 = ssd.forward_varlen(x2, g["dt"], g["A"], g["B"], g["C"], g["D"], cu, chunk=64,
+                                return_seq_states=True)
+    torch.cuda.synchronize()
+    keep = torch.ones(1000, dtype=torch.bool, device="cuda")
+    keep[70:450] = False
+    assert torch.equal(y1[0, keep], y2[0, keep])
+    assert torch.equal(s1[[0, 2, 3]], s2[[0, 2, 3]]) and not torch.equal(s1[1], s2[1])
