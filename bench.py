@@ -500,7 +500,7 @@ def counters_run(w):
 #
 # The rocprofv3 runs these read (OUT is any scratch directory):
 TRACE_CMD = ('rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/trace" -o trace '
-             '-- python bench.py --steps 20 --warmup 5 > "$OUT/bench_trace.log"')
+             '-- python bench.py --steps 20 --warmup 5 --all > "$OUT/bench_trace.log"')
 FETCH_CMD = ('rocprofv3 --pmc FETCH_SIZE --output-format csv -d "$OUT/fetch" -o fetch '
              '-- python bench.py --counters')
 WRITE_CMD = ('rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/write" -o write '
@@ -508,7 +508,7 @@ WRITE_CMD = ('rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/write" -o 
 # kernel-name fragment -> stage, first match wins (the fused stage-2+3 kernel
 # fills the chunk_state interval of the forward)
 KERNEL_OF = {"segment_states_kernel": "segment_states",
-             "ssd_forward_onepass": "forward_onepass", "onepass_varlen": "packed: token int4s",
+             "ssd_forward_onepass": "forward_onepass", "onepass_varlen_prep": "packed: token int4s",
              "chunk_cumsum_kernel": "chunk_cumsum", "chunk_state_passing": "chunk_state",
              "state_passing_kernel": "state_passing", "chunk_state": "chunk_state",
              "chunk_cb_kernel": "chunk_cb", "chunk_scan": "chunk_scan",
@@ -592,12 +592,16 @@ def summarize_traffic(fetch_csv, write_csv, workload="mamba2_2.7b"):
                             "fetch_kib": max(cal["fetch"]), "write_kib": max(cal["write"]),
                             "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
                             "commands": [FETCH_CMD, WRITE_CMD]}}
-    out = ["# HBM traffic per launch: SSD forward stages (Mamba-2 2.7B-shaped layer) and decode step",
+    wopt = "" if workload == "mamba2_2.7b" else f" --workload {workload}"
+    title = {"mamba2_2.7b": "Mamba-2 2.7B-shaped layer",
+             "long_seq": "long sequence: batch 1, L 65536, 80 heads, N 128, 8 groups"}.get(
+                 workload, workload)
+    out = [f"# HBM traffic per launch: SSD forward kernels ({title}) and decode step",
            "", "Commands, from the repository root on one MI355X:", "", "```",
-           "cd /tmp && export TMPDIR=/tmp && cd -", f"timeout -s KILL 60 {FETCH_CMD}",
-           f"timeout -s KILL 60 {WRITE_CMD}",
+           "cd /tmp && export TMPDIR=/tmp && cd -", f"timeout -s KILL 60 {FETCH_CMD}{wopt}",
+           f"timeout -s KILL 60 {WRITE_CMD}{wopt}",
            'python bench.py --summarize-traffic "$OUT/fetch/fetch_counter_collection.csv" '
-           '"$OUT/write/write_counter_collection.csv"', "```", "",
+           f'"$OUT/write/write_counter_collection.csv"{wopt}', "```", "",
            f"Calibration: the 1 GiB device copy reads FETCH_SIZE {max(cal['fetch']):.0f} KiB and "
            f"WRITE_SIZE {max(cal['write']):.0f} KiB, so FETCH_SIZE is scaled by {f_scale:.3f} and "
            f"WRITE_SIZE by {w_scale:.3f}.", "",
@@ -646,10 +650,11 @@ def main():
         print(summarize_trace(*args.summarize_trace))
         return
     if args.summarize_traffic:
-        md, rec = summarize_traffic(*args.summarize_traffic)
-        with open(TRAFFIC_FILE, "w") as f:
-            json.dump(rec, f, indent=1)
-            f.write("\n")
+        md, rec = summarize_traffic(*args.summarize_traffic, workload=args.workload)
+        if args.workload == "mamba2_2.7b":  # the bench line's roofline.traffic reads this one
+            with open(TRAFFIC_FILE, "w") as f:
+                json.dump(rec, f, indent=1)
+                f.write("\n")
         print(md)
         return
     if args.gpus != 1:

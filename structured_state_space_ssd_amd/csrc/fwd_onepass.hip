@@ -865,13 +865,25 @@ hipError_t launch_forward_onepass(const void *x, const void *dt, const float *A,
 }
 
 // ---- packed sequences: the tokens' int4 and the states of empty sequences
-
-// meta[t] = {first token of t's sequence, its index, whether t is its last
-// token, 0} for t < L. Any cu_seqlens contents give in-range values (the
-// index is the largest k < nseq with cu[k] <= t).
-__global__ __launch_bounds__(256) void onepass_varlen_meta_kernel(const int *__restrict__ cu,
-                                                                  int nseq, int L,
-                                                                  int4 *__restrict__ meta) {
+//
+// Workgroups 0 .. ceil(L / 256) - 1: meta[t] = {first token of t's sequence,
+// its index, whether t is its last token, 0} for t < L (any cu_seqlens
+// contents give in-range values: the index is the largest k < nseq with
+// cu[k] <= t). The next nseq workgroups (when seq_states is given): zero
+// states for the empty sequences, which no token ends.
+__global__ __launch_bounds__(256) void onepass_varlen_prep_kernel(const int *__restrict__ cu,
+                                                                  int nseq, int L, int H, int PN,
+                                                                  int4 *__restrict__ meta,
+                                                                  float *__restrict__ seq_states) {
+    const int nb = (L + 255) / 256;
+    if ((int)blockIdx.x >= nb) {
+        const int k = blockIdx.x - nb;
+        if (cu[k + 1] > cu[k]) return;  // whole workgroup
+        float4 *out = reinterpret_cast<float4 *>(seq_states + (size_t)k * H * PN);
+        for (int i = threadIdx.x; i < H * PN / 4; i += 256)
+            out[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        return;
+    }
     const int t = blockIdx.x * 256 + threadIdx.x;
     if (t >= L) return;
     int lo = 0, hi = nseq - 1;
@@ -881,32 +893,17 @@ __global__ __launch_bounds__(256) void onepass_varlen_meta_kernel(const int *__r
         else hi = mid - 1;
     }
     const int start = min(max(cu[lo], 0), t);
-    const bool last = t == L - 1 || (lo + 1 <= nseq && cu[lo + 1] == t + 1);
+    const bool last = t == L - 1 || cu[lo + 1] == t + 1;
     meta[t] = make_int4(start, lo, last ? 1 : 0, 0);
-}
-
-// zero states for the empty sequences (no token ends them)
-__global__ __launch_bounds__(256) void onepass_varlen_empty_kernel(const int *__restrict__ cu,
-                                                                   int PN,
-                                                                   float *__restrict__ seq_states) {
-    const int k = blockIdx.x, h = blockIdx.y, H = gridDim.y;
-    if (cu[k + 1] > cu[k]) return;  // whole workgroup
-    float4 *out = reinterpret_cast<float4 *>(seq_states + ((size_t)k * H + h) * PN);
-    for (int i = threadIdx.x; i < PN / 4; i += 256) out[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 }
 
 hipError_t launch_onepass_varlen_prep(const int *cu_seqlens, int nseq, int seqlen, int nheads,
                                       int dstate, void *meta, float *seq_states,
                                       hipStream_t stream) {
-    onepass_varlen_meta_kernel<<<(seqlen + 255) / 256, 256, 0, stream>>>(
-        cu_seqlens, nseq, seqlen, static_cast<int4 *>(meta));
-    hipError_t e = hipGetLastError();
-    if (e == hipSuccess && seq_states) {
-        onepass_varlen_empty_kernel<<<dim3(nseq, nheads), 256, 0, stream>>>(
-            cu_seqlens, 64 * dstate, seq_states);
-        e = hipGetLastError();
-    }
-    return e;
+    const int nb = (seqlen + 255) / 256;
+    onepass_varlen_prep_kernel<<<nb + (seq_states ? nseq : 0), 256, 0, stream>>>(
+        cu_seqlens, nseq, seqlen, nheads, 64 * dstate, static_cast<int4 *>(meta), seq_states);
+    return hipGetLastError();
 }
 
 }  // namespace ssd
