@@ -544,20 +544,24 @@ def summarize_trace(stats_csv, bench_log):
     out = ["# Kernel trace: SSD forward stages (Mamba-2 2.7B-shaped layer) and decode step", "",
            "The same run also times the forward with every step-size option, the packed",
            "variable-length forward and the backward on the same shapes (bench.py's",
-           "forward_with_options, forward_varlen and backward entries); their kernels are",
-           "listed too. A kernel name can appear for several uses (e.g. the chunk-state",
-           "kernel computes the backward's output-gradient contributions as well).", "",
+           "forward_with_options, forward_varlen and backward entries) and, with --all, the",
+           "tiny, large-state and long-sequence forwards; their kernels are listed too. A",
+           "kernel name can appear for several uses (e.g. the chunk-state kernel computes the",
+           "backward's output-gradient contributions as well). The bench's own event time is",
+           "given beside the 2.7B forward's kernel (the first row of its stage) only.", "",
            "Commands, from the repository root on one MI355X:", "", "```",
            "cd /tmp && export TMPDIR=/tmp && cd -", TRACE_CMD,
            f'python bench.py --summarize-trace "$OUT/trace/trace_kernel_stats.csv" "$OUT/bench_trace.log"',
            "```", "",
            "| kernel | stage | calls | avg us | min us | max us | bench event avg us |",
            "|---|---|---|---|---|---|---|"]
+    seen = set()
     for r in rows:
         stage = _stage_of(r["Name"])
         ev = ""
-        if bench and stage in bench.get("kernels", {}):
+        if bench and stage in bench.get("kernels", {}) and stage not in seen:
             ev = f"{bench['kernels'][stage]['us']:.2f}"
+            seen.add(stage)
         elif bench and stage == "decode_step":
             ev = f"{bench['decode']['us_per_step']:.2f}"
         name = r["Name"].split("(")[0].replace("void ", "")
