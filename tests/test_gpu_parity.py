@@ -198,10 +198,11 @@ def test_fused_state_path_single_chunk_short():
     check_forward(W.small("fused_short", 16, 37, 32, 64, 1, 64, 256, "bf16", seed=620, init_std=0.3))
 
 
-# ------------------------------------------- single-pass forward (bf16, N = 64, Bt*H >= 512)
+# --------------------- single-pass forward (bf16, N 64 or 128, heads a multiple of 8)
 #
 # One workgroup per (batch, head) walks the sequence in 64-token blocks with
-# the state in registers. Cases: a single token, one partial block, exactly
+# the state in registers (these cases have enough (batch, head) pairs for one
+# segment; the segmented form follows further down). Cases: a single token, one partial block, exactly
 # one block, one block plus one token, several blocks with a ragged end; an
 # initial state; several groups; every chunk argument (it does not change the
 # kernel's blocks, only the rounding order against the oracle).
