@@ -515,6 +515,10 @@ KERNEL_OF = {"segment_states_kernel": "segment_states",
              "decode_step_kernel": "decode_step", "chunk_bwd_kernel": "backward: chunk gradients",
              "bwd_dt_kernel": "backward: dt, A, bias", "bwd_reduce_kernel": "backward: dB, dC sums",
              "bwd_head_sum_kernel": "backward: per-head sums", "varlen_seg": "packed: token masks"}
+UTIL_CMDS = ('rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil --output-format csv -d "$OUT/util" -o util '
+             '-- python bench.py --counters',
+             'rocprofv3 --pmc MfmaFlopsBF16 --output-format csv -d "$OUT/mops" -o mops '
+             '-- python bench.py --counters')
 CALIBRATION_KERNEL = "__amd_rocclr_copyBuffer"  # the 1 GiB device copy of --counters
 COPY_BYTES = 1 << 30
 
@@ -628,6 +632,46 @@ def summarize_traffic(fetch_csv, write_csv, workload="mamba2_2.7b"):
     return "\n".join(out), rec
 
 
+def summarize_util(util_csv, mops_csv, workload="mamba2_2.7b"):
+    """Markdown table of the MFMA-busy, VALU-busy and LDS counters (percent of
+    the kernel's active cycles, averaged over its dispatches) and the executed
+    bf16 MFMA flops against the algorithmic ones, per forward kernel."""
+    import ssd_workloads as W
+    per = {}
+    for path in (util_csv, mops_csv):
+        for r in _read_csv(path):
+            k = _stage_of(r["Kernel_Name"])
+            if k is None:
+                continue
+            per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    acc = accounting(W.WORKLOADS[workload])
+    wopt = "" if workload == "mamba2_2.7b" else f" --workload {workload}"
+    out = [f"# MFMA, VALU and LDS utilisation: SSD forward kernels ({workload})", "",
+           "rocprofv3 derived counters, each the average over the kernel's dispatches:",
+           "MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), VALUBusy and",
+           "LdsUtil likewise in percent of busy cycles; MfmaFlopsBF16 = 512 x",
+           "SQ_INSTS_VALU_MFMA_MOPS_BF16, the executed bf16 MFMA flops per launch, beside",
+           "the algorithmic flops the accounting counts (the executed ones include the",
+           "zero-padded halves of causal tiles and the D x products).", "",
+           "Commands, from the repository root on one MI355X:", "", "```",
+           "cd /tmp && export TMPDIR=/tmp && cd -"] + \
+          [f"timeout -s KILL 60 {c}{wopt}" for c in UTIL_CMDS] + \
+          ['python bench.py --summarize-util "$OUT/util/util_counter_collection.csv" '
+           f'"$OUT/mops/mops_counter_collection.csv"{wopt}', "```", "",
+           "| kernel | dispatches | MfmaUtil % | VALUBusy % | LdsUtil % | executed MFMA GFLOP "
+           "| algorithmic GFLOP |", "|---|---|---|---|---|---|---|"]
+    avg = lambda v: sum(v) / len(v) if v else float("nan")
+    for k in ONEPASS_SEG + STAGES:
+        if k not in per or k not in acc:
+            continue
+        c = per[k]
+        out.append(f"| {k} | {len(c.get('MfmaUtil', []))} | {avg(c.get('MfmaUtil', [])):.1f} | "
+                   f"{avg(c.get('VALUBusy', [])):.1f} | {avg(c.get('LdsUtil', [])):.1f} | "
+                   f"{avg(c.get('MfmaFlopsBF16', [])) / 1e9:.2f} | {acc[k]['flops'] / 1e9:.2f} |")
+    return "\n".join(out)
+
+
 def W_decode():
     import ssd_workloads as W
     return W.WORKLOADS["decode"]
@@ -646,12 +690,18 @@ def main():
                          "steps and a plain 1 GiB device copy that calibrates the byte counters")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "BENCH_LOG"),
                     help="print the markdown summary of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--summarize-util", nargs=2, metavar=("UTIL_CSV", "MOPS_CSV"),
+                    help="print the MFMA / VALU / LDS utilisation summary of two rocprofv3 "
+                         "--pmc runs")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM-traffic summary of two rocprofv3 --pmc runs and write "
                          "profiles/hbm_traffic.json")
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(*args.summarize_trace))
+        return
+    if args.summarize_util:
+        print(summarize_util(*args.summarize_util, workload=args.workload))
         return
     if args.summarize_traffic:
         md, rec = summarize_traffic(*args.summarize_traffic, workload=args.workload)
