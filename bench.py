@@ -316,6 +316,39 @@ def time_forward(w, steps, warmup, breakdown_steps=10, event_every=5, spin_secon
             "stage_ms": dict(zip(stages, per_stage)), "dominant": stages[dom], "dominant_ms": dom_ms}
 
 
+def time_forward_cold(w, reps=30, flush_bytes=1 << 30):
+    """Single forwards with nothing of the inputs in the caches: before each,
+    outside its events, a 1 GiB buffer is read (a sum: clean lines only, so
+    the forward does not also write back a flush's dirty lines), which leaves
+    neither L2 nor the 256 MB Infinity Cache holding x, B, C or dt. The 2.7B
+    inputs (175 MB) fit in the Infinity Cache, so back-to-back forwards (the
+    timed region) find part of them there. Returns the median and p10 / p90
+    in ms."""
+    import torch
+    import ssd_workloads as W
+    import structured_state_space_ssd_amd as ssd
+
+    g = upload(W.generate(w))
+    x, dt, A, B, C, D = (g[k] for k in ("x", "dt", "A", "B", "C", "D"))
+    ws = torch.empty(ssd.workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate,
+                                        w.chunk, x.dtype), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    flush = torch.ones(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros((), dtype=torch.float32, device="cuda")
+    call = lambda: ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y)
+    spin_up(call)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for e0, e1 in evs:
+        sink += flush.sum()
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    return {"median_ms": t[reps // 2], "p10_ms": t[reps // 10], "p90_ms": t[(9 * reps) // 10]}
+
+
 def time_forward_options(w, steps, warmup):
     """Whole-forward time (host clock, no events, after spin_up) with every
     step-size option on: per-head bias, softplus, clamp to [4e-3, 3e-2] and the zero-order-hold
@@ -758,6 +791,15 @@ def main():
           f"between every two kernels; {fwd['dominant']} {fwd['dominant_ms'] * 1e3:.1f} us live); kernels " +
           ", ".join(f"{k} {v['us']:.1f} us" for k, v in kernels.items()), file=sys.stderr, flush=True)
 
+    cold = time_forward_cold(w)
+    cold_rec = {"protocol": "one forward per rep after reading a 1 GiB buffer (L2 and Infinity "
+                            "Cache hold none of the inputs); 30 reps",
+                "us_per_forward": round(cold["median_ms"] * 1e3, 2),
+                "p10_us": round(cold["p10_ms"] * 1e3, 2), "p90_us": round(cold["p90_ms"] * 1e3, 2),
+                "tokens_per_s": round(w.tokens / (cold["median_ms"] * 1e-3), 1)}
+    print(f"[bench] cold-cache forward: {cold_rec['us_per_forward']} us (median)", file=sys.stderr,
+          flush=True)
+
     opt_ms = time_forward_options(w, max(10, args.steps // 2), 3)
     options = {"options": "dt_bias + softplus + clamp + zero-order hold",
                "us_per_forward": round(opt_ms * 1e3, 2),
@@ -838,6 +880,7 @@ def main():
         "cpu_baseline": cpu,
         "evented_us_per_step": round(fwd["evented_ms"] * 1e3, 2),
         "kernels": kernels,
+        "forward_cold_cache": cold_rec,
         "forward_with_options": options,
         "forward_varlen": varlen,
         "backward": backward,

@@ -77,9 +77,16 @@ struct VlTab {  // per block: each row's first token of its sequence (relative
 template <>
 struct VlTab<false> {};
 
+// x buffers of the single-pass kernel: three (x two blocks ahead) where three
+// workgroups per compute unit still fit, else two (x one block ahead).
+template <int N, bool VL>
+constexpr int onepass_xbufs() {
+    return N == 64 && VL ? 2 : 3;  // packed sequences at N 64: their tables take the room
+}
+
 template <int N, bool VL>
 struct OnepassLds {
-    __bf16 xb[2][kOpT * 64];
+    __bf16 xb[onepass_xbufs<N, VL>()][kOpT * 64];
     __bf16 bb[kOpT * N];
     __bf16 cs[kOpT * N];
     __bf16 hb[64 * N];     // the state entering the block, bf16, [p][n], pieces swizzled by p & 7
@@ -184,6 +191,7 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kern
     constexpr int P = 64, T = kOpT;
     constexpr int PPR = N / 8, NT = N / 16, NK = N / 32;
     constexpr int HSW = PPR >= 16 ? 15 : PPR - 1;  // piece swizzle mask of the bf16 state rows
+    constexpr int NXB = onepass_xbufs<N, VL>();
     constexpr int BL = T * PPR / 256;  // B (and C) loads per lane per block
     static_assert(N % 32 == 0 && BL >= 1, "state size");
     __shared__ __attribute__((aligned(16))) OnepassLds<N, VL> sm;
@@ -230,7 +238,7 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kern
         const int t0 = k * T, len = min(T, Lw - t0);
         const bf16_t *base = xh + (size_t)t0 * xrow;
 #pragma unroll
-        for (int i = w; i < 8; i += 4) dma16_sv(base, x_off(i, len), sm.xb[k & 1] + i * 512);
+        for (int i = w; i < 8; i += 4) dma16_sv(base, x_off(i, len), sm.xb[k % NXB] + i * 512);
     };
     auto issue_dt = [&](int k) {  // wavefront 0 only
         const int t0 = k * T, len = min(T, Lw - t0);
@@ -299,6 +307,7 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kern
     issue_x(0);
     if (w == 0) issue_dt(0);
     issue_bcd(0);
+    if (NXB == 3 && nblk > 1) issue_x(1);
 
     int xo[4];
     x_colfrag_offsets(xo, l);
@@ -341,13 +350,20 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kern
     uint4 ystage[2];  // this lane's two 16-byte pieces of the previous block's outputs
     for (int k = 0; k < nblk; ++k) {
         const int t0 = k * T;
-        // every load issued so far has landed (block k's x, B, C, this and
-        // the next block's dt) and every store has left; every wavefront has
-        // read the previous block's staged outputs out of x buffer (k+1) & 1,
-        // which now takes block k+1's x; the state entering the block is in LDS
-        wait_barrier<0>();
-        if (k + 1 < nblk) issue_x(k + 1);
-        const __bf16 *xs = sm.xb[k & 1];
+        // block k's x, B, C, this and the next block's dt have landed and the
+        // stores issued before them have left; every wavefront has read the
+        // previous block's staged outputs; the state entering the block is in
+        // LDS. Three x buffers: block k+1's x (the last loads issued, two per
+        // wavefront) may stay in flight. Two: it is issued now, into the
+        // buffer of the previous block's staged outputs.
+        if constexpr (NXB == 3) {
+            if (k + 1 < nblk) wait_barrier<2>();
+            else wait_barrier<0>();
+        } else {
+            wait_barrier<0>();
+            if (k + 1 < nblk) issue_x(k + 1);
+        }
+        const __bf16 *xs = sm.xb[k % NXB];
         if (k == 0) {  // later blocks' tables are made during the block before
             if (w == 0) make_tables(0);
             barrier_lds();
@@ -561,9 +577,12 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kern
         barrier_lds();
         put_h();
         if (k + 1 < nblk) issue_bcd(k + 1);
+        // (three buffers: x two blocks ahead, into the buffer of the previous
+        // block, whose staged outputs every wavefront has read)
+        if (NXB == 3 && k + 2 < nblk) issue_x(k + 2);
 
         // ---- the outputs: this wavefront's rows, every column, into the x buffer
-        __bf16 *xw_ = sm.xb[k & 1];
+        __bf16 *xw_ = sm.xb[k % NXB];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
             const int off = x_at(i, 16 * pt + 4 * g4);
