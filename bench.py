@@ -198,11 +198,18 @@ def decode_accounting(w):
 
 
 def kernel_source_digest(name):
+    """Digest of a kernel's source file and the shared header, comments and
+    whitespace left out (a counter record stays valid across comment edits,
+    not across code changes)."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "structured_state_space_ssd_amd", "csrc")
     for f in (f"{SOURCE_OF.get(name, name)}.hip", "ssd_common.h"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -18,36 +18,47 @@
 // to rounding: the block length only decides which products run as the
 // quadratic (attention-like) form and which through the state.
 //
-// Layout: 4 wavefronts; wavefront w owns head-dim columns p in [16w, 16w+16)
-// of everything per-p: the state H^T[n][p] (float32, in the MFMA accumulator
-// layout, which is also the operand layout the state-to-output product
-// needs, so the state never goes through LDS), the outputs Y^T[p][i] and the
-// x^T operand fragments. The block's x rows (double-buffered), B and C rows
+// Segments: with too few (batch, head) pairs to fill the GPU, each sequence
+// is cut into segments of whole blocks, one workgroup per (batch, head,
+// segment). A segment-state kernel first computes, for pieces of the earlier
+// segments, the state each piece produces from zero and its total decay; a
+// segment's workgroup starts from the initial state brought through those
+// pieces (H <- exp(d) H + H_piece: the same recurrence at a coarser grain).
+// Packed sequences (VL) mask rows, pairs and the state update by each
+// token's first token of its sequence, and take each sequence's final state
+// at its last token.
+//
+// Layout: 4 wavefronts. Wavefront w owns the 16 output tokens 16w..16w+15
+// (Y^T tiles for every head-dim column) and the head-dim columns
+// 16w..16w+15 of the state H^T (float32 registers, MFMA accumulator layout).
+// The block's x rows (three buffers where LDS allows, else two), B and C rows
 // (single-buffered: they are shared by all heads of a group and come from
 // L2), and the 8-head piece of dt holding this head's values arrive by direct
-// global-to-LDS loads: x one block ahead (issued as the block starts), dt two,
-// B and C one (issued mid-block, once the current ones are consumed). Memory
-// instructions are spread over the block (x at its start, the previous
-// block's two output stores after the first products, B / C / dt after the
-// middle barrier): issued in one burst they queue in the address unit and
-// stall every wavefront behind them. The masked
-// C B^T products of a block (6 tiles of 16 x 32) are formed once per block,
-// spread over the wavefronts, and shared through LDS.
+// global-to-LDS loads: x two blocks ahead (issued after the next block's B
+// and C, so that the wait at a block's start leaves it in flight; one block
+// ahead with two buffers), dt two blocks ahead, B and C one (issued mid-block,
+// once the current ones are consumed). Memory instructions are spread over
+// the block (the previous block's two output stores after the first
+// products, B / C / dt / x after the middle barrier): issued in one burst
+// they queue in the address unit and stall every wavefront behind them.
 //
 // Per block, per wavefront:
 //   tables    s * log2(e), w and exp(s_end - s_j) w_j for the 64 tokens
 //             (step sizes with bias, softplus, clamp; zero-order-hold weights;
 //             one token per lane, wave-wide prefix sum): made once, by
-//             wavefront 3, during the block before, into one of two LDS
+//             wavefront 0, during the block before, into one of two LDS
 //             tables that the barriers of that block publish;
-//   C H       Y^T = H (C_i)^T on MFMA (A operand straight from the state
-//             registers), scaled per token by exp(s_i);
-//   C B^T     this wavefront's causal tiles, times exp(s_i - s_j) w_j, masked
-//             j <= i, rounded to bf16 into LDS;
-//   state     H^T = exp(s_end) H^T + B^T (w' o x) on MFMA;
-//   -- barrier: tiles visible; B, C, dt buffers free: next loads issued --
-//   diagonal  Y^T += X^T M^T over the 6 tiles; D x as X^T diag(D) (D split
-//             into two bf16 parts) on the diagonal slices;
+//   C H       Y^T = H C_i^T for the wavefront's rows on MFMA (H from LDS in
+//             bf16, where the previous block's update left it; C_i fragments
+//             shared with the next step), scaled per token by exp(s_i);
+//   C B^T     the row tile's causal tiles (slices j <= i), decayed by
+//             exp(s_i - s_j) w_j (below the diagonal as exp(s_i - s_31) times
+//             a per-token column factor), masked, kept in registers as the
+//             B operand of Y^T += X^T M^T over every head-dim tile; D x as
+//             X^T diag(D) (D split into two bf16 parts) on the diagonal slice;
+//   state     H^T = exp(s_end) H^T + B^T (w' o x) on MFMA for the
+//             wavefront's columns;
+//   -- barrier: B, C, dt buffers free; next loads issued; H to LDS in bf16 --
 //   outputs   this wavefront's 16 rows staged in the block's x buffer and
 //             read back as whole 128-byte rows by the same wavefront (no
 //             barrier), stored (non-temporal) during the next block.
