@@ -96,7 +96,8 @@ def onepass_plan(w):
     fwd_onepass.hip (its scratch: the workspace's float32 states region); S is
     checked against the library's own ssd_forward_plan."""
     Bt, L, H, P, N, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.chunk
-    slots, so_slots = (3 if N == 64 else 2) * 256, (4 if N == 64 else 3) * 256
+    slots = {64: 3, 128: 2}.get(N, 1) * 256
+    so_slots = {64: 4, 128: 3}.get(N, 1) * 256
     units, blocks = Bt * H, -(-L // 64)
     scratch = Bt * (-(-L // Q)) * H * P * N * 4
     plan = (1, 1, blocks)

@@ -133,7 +133,7 @@ size_t ssd_forward_workspace_size(int batch, int seqlen, int nheads, int headdim
 /*
  * Full SSD layer forward: enqueues ssd_chunk_cumsum, ssd_chunk_state,
  * ssd_state_passing, ssd_chunk_cb (SSD_F32 only) and ssd_chunk_scan on
- * `stream`. For SSD_BF16 with dstate 64 or 128, nheads a multiple of 8 and
+ * `stream`. For SSD_BF16 with dstate 64, 128 or 256, nheads a multiple of 8 and
  * a 16-byte aligned dt, it enqueues instead one single-pass kernel that
  * computes the same result (up to rounding): one workgroup per (batch, head)
  * walks the sequence in blocks of 64 tokens, carrying the state from block to
@@ -258,7 +258,7 @@ int ssd_backward(const void *x, const void *dt, const float *A, const void *B, c
  *               256-byte aligned: ssd_forward's layout at batch 1, then one
  *               int32 per token position of the chunk-padded layout.
  * Where ssd_forward would run its single-pass kernel at batch 1
- * (ssd_forward_plan(1, ...) > 0: SSD_BF16, dstate 64 or 128, nheads a
+ * (ssd_forward_plan(1, ...) > 0: SSD_BF16, dstate 64, 128 or 256, nheads a
  * multiple of 8, 16-byte aligned dt) it runs that kernel with sequence masks
  * (over segments of the token axis, with the segment-state kernel first):
  * rows ignore the state of earlier sequences, the state restarts from zero

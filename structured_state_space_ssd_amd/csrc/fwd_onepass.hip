@@ -92,7 +92,7 @@ struct VlTab<false> {};
 // workgroups per compute unit still fit, else two (x one block ahead).
 template <int N, bool VL>
 constexpr int onepass_xbufs() {
-    return N == 64 && VL ? 2 : 3;  // packed sequences at N 64: their tables take the room
+    return (N == 64 && VL) || N == 256 ? 2 : 3;  // packed sequences at N 64: their tables take the room
 }
 
 template <int N, bool VL>
@@ -194,7 +194,7 @@ __device__ __forceinline__ void vl_tables(VlTab<VL> &vt, const int4 &m, int tblk
 }
 
 template <int N, bool VL>
-__global__ __launch_bounds__(256, N == 64 ? 3 : 2) void ssd_forward_onepass_kernel(
+__global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forward_onepass_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ dt, const float *__restrict__ A,
     const bf16_t *__restrict__ B, const bf16_t *__restrict__ C, const float *__restrict__ D,
     const float *__restrict__ init, DtOpts o, int batch, int L, int H, int G, int per,
@@ -646,7 +646,7 @@ struct SegStateLds {
 };
 
 template <int N, bool VL>
-__global__ __launch_bounds__(256, N == 64 ? 4 : 3) void ssd_segment_states_kernel(
+__global__ __launch_bounds__(256, N == 64 ? 4 : N == 128 ? 3 : 1) void ssd_segment_states_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ dt, const float *__restrict__ A,
     const bf16_t *__restrict__ B, DtOpts o, int batch, int L, int H, int G, int per,
     OnepassSegs sg, OnepassVl vl) {
@@ -786,7 +786,7 @@ __global__ __launch_bounds__(256, N == 64 ? 4 : 3) void ssd_segment_states_kerne
 bool forward_onepass_ok(int batch, int nheads, int dstate, bool bf16, const void *dt) {
     // dt is read as 16-byte pieces of 8 heads
     (void)batch;
-    return bf16 && (dstate == 64 || dstate == 128) && nheads % 8 == 0 &&
+    return bf16 && (dstate == 64 || dstate == 128 || dstate == 256) && nheads % 8 == 0 &&
            (reinterpret_cast<uintptr_t>(dt) & 15u) == 0;
 }
 
@@ -802,16 +802,18 @@ struct OnepassPlan {
 size_t piece_bytes(int dstate) { return (64 * (size_t)dstate + 1) * sizeof(float); }
 
 // Enough (batch, head) pairs fill the GPU with one workgroup each (three per
-// compute unit at N = 64, two at N = 128). With fewer, each sequence is cut
+// compute unit at N = 64, two at N = 128, one at N = 256). With fewer, each sequence is cut
 // into S segments of whole 64-token blocks, S the number of workgroups per
 // pair that still fit in one round of workgroups, each segment at least 4
 // blocks long. The segment-state kernel, lighter (four workgroups per
-// compute unit at N = 64, three at N = 128), cuts each of the first S - 1
-// segments into k pieces of at least 2 blocks so that it, too, fills the GPU.
+// compute unit at N = 64, three at N = 128, one at N = 256), cuts each of the
+// first S - 1 segments into k pieces of at least 2 blocks so that it, too,
+// fills the GPU.
 // The scratch holds one float32 state and one decay per piece: a smaller
 // scratch lowers k, then S.
 OnepassPlan onepass_plan(int batch, int seqlen, int nheads, int dstate, size_t scratch_bytes) {
-    const int slots = (dstate == 64 ? 3 : 2) * 256, so_slots = (dstate == 64 ? 4 : 3) * 256;
+    const int slots = (dstate == 64 ? 3 : dstate == 128 ? 2 : 1) * 256,
+              so_slots = (dstate == 64 ? 4 : dstate == 128 ? 3 : 1) * 256;
     const int units = batch * nheads;
     const int blocks = (seqlen + kOpT - 1) / kOpT;
     const OnepassPlan one{1, 1, blocks, blocks};
@@ -889,6 +891,10 @@ hipError_t launch_forward_onepass(const void *x, const void *dt, const float *A,
     if (dstate == 128) {
         if (varlen_meta) SSD_ONEPASS(128, true);
         SSD_ONEPASS(128, false);
+    }
+    if (dstate == 256) {
+        if (varlen_meta) SSD_ONEPASS(256, true);
+        SSD_ONEPASS(256, false);
     }
 #undef SSD_ONEPASS
     return hipErrorInvalidValue;

@@ -287,7 +287,8 @@ def test_forward_plan(lib):
     assert plan(8, 2048, 80, 1, 64, 256) == 1       # enough (batch, head) pairs
     assert plan(1, 65536, 80, 8, 128, 256) > 1     # few pairs, long sequence: segments
     assert plan(1, 100, 8, 1, 64, 64) == 1         # too short to cut
-    assert plan(4, 4096, 32, 1, 256, 128) == 0     # N 256: stage kernels
+    assert plan(4, 4096, 32, 1, 256, 128) == 2     # N 256: one workgroup per CU, 2 segments
+    assert plan(8, 2048, 80, 1, 32, 256) == 0      # N 32: stage kernels
     assert plan(8, 2048, 80, 1, 64, 256, dtype=0) == 0   # float32: stage kernels
     assert plan(8, 2048, 68, 4, 64, 256) == 0      # heads not a multiple of 8
     assert plan(8, 2048, 80, 1, 64, 256, dt=off) == 0    # dt not 16-byte aligned

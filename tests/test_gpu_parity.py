@@ -285,7 +285,7 @@ def test_onepass_misaligned_dt_falls_back():
 # option further down); a single segment at N 128 (enough pairs) and sequences too short to
 # cut.
 
-@pytest.mark.parametrize("N", [64, 128])
+@pytest.mark.parametrize("N", [64, 128, 256])
 @pytest.mark.parametrize("L", [37 * 64 + 13, 8 * 64, 1000])
 def test_segments(N, L):
     w = W.small(f"seg_N{N}_L{L}", 1, L, 16, 64, 2, N, 256, "bf16", seed=900 + L + N,
@@ -321,6 +321,18 @@ def test_onepass_n128_one_segment():
     w = W.small("onepass_n128", 8, 333, 64, 64, 4, 128, 256, "bf16", seed=970, init_std=0.2)
     assert plan(w) == 1
     check_forward(w)
+
+
+def test_onepass_n256_one_segment():
+    w = W.small("onepass_n256", 8, 333, 32, 64, 4, 256, 128, "bf16", seed=971, init_std=0.2)
+    assert plan(w) == 1
+    check_forward(w)
+
+
+def test_onepass_n256_options_segments():
+    w = W.small("onepass_n256_opt", 2, 1100, 8, 64, 2, 256, 64, "bf16", seed=972, init_std=0.2)
+    assert plan(w) > 1
+    check_forward(w, both_D=False, raw=True, dt_softplus=True, dt_limit=(4e-3, 3e-2), zoh=True)
 
 
 def test_heads_not_multiple_of_8_many_units():

@@ -205,7 +205,7 @@ def test_varlen_onepass_explicit_boundaries(N):
     check_varlen(w, EXPLICIT_OP)
 
 
-@pytest.mark.parametrize("N", [64, 128])
+@pytest.mark.parametrize("N", [64, 128, 256])
 def test_varlen_onepass_length_mix(N):
     L = 3000
     cu = W.packed_cu_seqlens(L, 400, seed=890 + N)
