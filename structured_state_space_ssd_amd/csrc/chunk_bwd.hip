@@ -625,9 +625,12 @@ int bwd_chunk(int dstate, bool bf16) {
 }
 
 int bwd_head_blocks(int batch, int seqlen, int nheads, int ngroups, int chunk) {
+    // the chunk kernel runs one workgroup per compute unit (its LDS): split the
+    // heads of each (batch, chunk, group) unit so that one round of about 256
+    // workgroups covers them (fewer rounds, fewer dB / dC partial sums)
     const int nC = (seqlen + chunk - 1) / chunk;
     const int nU = batch * nC * ngroups;
-    int nblk = (512 + nU - 1) / nU;
+    int nblk = (256 + nU - 1) / nU;
     const int hpg = nheads / ngroups;
     return nblk < 1 ? 1 : (nblk > hpg ? hpg : nblk);
 }
