@@ -31,6 +31,11 @@
 // Layout: 4 wavefronts. Wavefront w owns the 16 output tokens 16w..16w+15
 // (Y^T tiles for every head-dim column) and the head-dim columns
 // 16w..16w+15 of the state H^T (float32 registers, MFMA accumulator layout).
+// At N 256 (one workgroup per compute unit) 8 wavefronts: w and w + 4 share
+// tile w, each holding half of the state's n and forming its half of the
+// sums over n (C H, C B^T, the update); the second hands its partial outputs
+// to the first through LDS at the middle barrier, and the first stages and
+// stores them.
 // The block's x rows (three buffers where LDS allows, else two), B and C rows
 // (single-buffered: they are shared by all heads of a group and come from
 // L2), and the 8-head piece of dt holding this head's values arrive by direct
@@ -109,6 +114,9 @@ struct OnepassLds {
     } tab[2];
     VlTab<VL> vt[2];
     int4 mts[VL ? 2 : 1][VL ? kOpT : 1];  // the tokens' int4 of blocks k, k+1
+    // N 256: the second half-N wavefront of each tile pair hands its partial
+    // outputs over here ([row tile][head-dim tile][lane])
+    floatx4 xch[N == 256 ? 16 : 1][N == 256 ? 64 : 1];
 };
 
 // One 16-byte-per-lane global-to-LDS load from the wave-uniform base `sbase`
@@ -194,7 +202,7 @@ __device__ __forceinline__ void vl_tables(VlTab<VL> &vt, const int4 &m, int tblk
 }
 
 template <int N, bool VL>
-__global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forward_onepass_kernel(
+__global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forward_onepass_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ dt, const float *__restrict__ A,
     const bf16_t *__restrict__ B, const bf16_t *__restrict__ C, const float *__restrict__ D,
     const float *__restrict__ init, DtOpts o, int batch, int L, int H, int G, int per,
@@ -203,6 +211,12 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
     constexpr int PPR = N / 8, NT = N / 16, NK = N / 32;
     constexpr int HSW = PPR >= 16 ? 15 : PPR - 1;  // piece swizzle mask of the bf16 state rows
     constexpr int NXB = onepass_xbufs<N, VL>();
+    // N 256: eight wavefronts, two per row / head-dim tile, each with half of N
+    // (its half of the state, of the C H and C B^T sums and of the update)
+    constexpr bool HALVES = N == 256;
+    constexpr int NWV = HALVES ? 8 : 4;        // wavefronts
+    constexpr int NKH = HALVES ? NK / 2 : NK;  // k-steps over N per wavefront
+    constexpr int NTH = HALVES ? NT / 2 : NT;  // state tiles per wavefront
     constexpr int BL = T * PPR / 256;  // B (and C) loads per lane per block
     static_assert(N % 32 == 0 && BL >= 1, "state size");
     __shared__ __attribute__((aligned(16))) OnepassLds<N, VL> sm;
@@ -221,6 +235,8 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
     const size_t bh = (size_t)b * H + h;
     // the wavefront index as a scalar (uniform branches and loop bounds)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = HALVES ? (w & 3) : w;  // the row / head-dim tile
+    const int nh = HALVES ? (w >> 2) : 0;  // the half of N
     const int l = lane_id(), g4 = l >> 4, cc = l & 15;
     const int nblk = (Lw + T - 1) / T;
 
@@ -249,7 +265,7 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
         const int t0 = k * T, len = min(T, Lw - t0);
         const bf16_t *base = xh + (size_t)t0 * xrow;
 #pragma unroll
-        for (int i = w; i < 8; i += 4) dma16_sv(base, x_off(i, len), sm.xb[k % NXB] + i * 512);
+        for (int i = w; i < 8; i += NWV) dma16_sv(base, x_off(i, len), sm.xb[k % NXB] + i * 512);
     };
     auto issue_dt = [&](int k) {  // wavefront 0 only
         const int t0 = k * T, len = min(T, Lw - t0);
@@ -264,9 +280,9 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
         if (w == 0 && k + 1 < nblk) issue_dt(k + 1);
         const bf16_t *bb_ = bg + (size_t)t0 * brow, *cb_ = cg + (size_t)t0 * brow;
 #pragma unroll
-        for (int i = w; i < T * PPR / 64; i += 4) dma16_sv(bb_, bc_off(i, len), sm.bb + i * 512);
+        for (int i = w; i < T * PPR / 64; i += NWV) dma16_sv(bb_, bc_off(i, len), sm.bb + i * 512);
 #pragma unroll
-        for (int i = w; i < T * PPR / 64; i += 4) dma16_sv(cb_, bc_off(i, len), sm.cs + i * 512);
+        for (int i = w; i < T * PPR / 64; i += NWV) dma16_sv(cb_, bc_off(i, len), sm.cs + i * 512);
     };
     // block k's tables from its dt piece (one wavefront; lane j is token t0 + j)
     auto make_tables = [&](int k) {
@@ -289,10 +305,11 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
     // the state H^T: lane (g4, cc) of wavefront w holds rows n = 16 nt + 4 g4 + r
     // of column p = 16 w + cc
     // (the initial state, brought through the pieces before this segment)
-    floatx4 hreg[NT];
-    const size_t hoff = (size_t)(16 * w + cc) * N + 4 * g4;  // this lane's state offset
+    floatx4 hreg[NTH];  // n tiles nh * NTH + 0 .. NTH-1
+    // this lane's state offset (its column; its rows in the first n tile it holds)
+    const size_t hoff = (size_t)(16 * wr + cc) * N + 4 * g4 + 16 * NTH * nh;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NTH; ++nt) {
         hreg[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
         if (init) {
             const float4 v =
@@ -306,7 +323,7 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
         const float f = __builtin_amdgcn_exp2f(sg.ld[bh * sg.npc + j]);
         const float *sj = sg.state + (bh * sg.npc + j) * P * N + hoff;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+        for (int nt = 0; nt < NTH; ++nt) {
             const float4 v = *reinterpret_cast<const float4 *>(sj + 16 * nt);
             hreg[nt][0] = hreg[nt][0] * f + v.x;
             hreg[nt][1] = hreg[nt][1] * f + v.y;
@@ -322,7 +339,7 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
 
     int xo[4];
     x_colfrag_offsets(xo, l);
-    const int i = 16 * w + cc;  // this lane's output token: wavefront w owns rows 16w..16w+15
+    const int i = 16 * wr + cc;  // this lane's output token: row tile wr is rows 16wr..16wr+15
 
     // D x on MFMA: Y^T += X^T diag(D) over the slice holding the row tile's
     // diagonal, with D split as D_hi + D_lo (bf16 each, 16 mantissa bits in
@@ -337,7 +354,7 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
         const int e0 = cc - 4 * g4;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const bool on = e == ((w & 1) ? 4 + e0 : e0) && e0 >= 0 && e0 < 4;
+            const bool on = e == ((wr & 1) ? 4 + e0 : e0) && e0 >= 0 && e0 < 4;
             dfr[0].v[e] = on ? dhi : static_cast<__bf16>(0.0f);
             dfr[1].v[e] = on ? dlo : static_cast<__bf16>(0.0f);
         }
@@ -346,12 +363,13 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
     // the state (bf16) into LDS for the next state-to-output product: this
     // wavefront's columns p = 16 w + cc, 4 consecutive n per accumulator tile
     auto put_h = [&]() {
-        const int pp = 16 * w + cc;
+        const int pp = 16 * wr + cc;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+        for (int nq = 0; nq < NTH; ++nq) {
+            const int nt = nh * NTH + nq;
             const int n0 = 16 * nt + 4 * g4, q = n0 >> 3;
-            const bf16x2 lo = __builtin_convertvector(floatx2{hreg[nt][0], hreg[nt][1]}, bf16x2);
-            const bf16x2 hi = __builtin_convertvector(floatx2{hreg[nt][2], hreg[nt][3]}, bf16x2);
+            const bf16x2 lo = __builtin_convertvector(floatx2{hreg[nq][0], hreg[nq][1]}, bf16x2);
+            const bf16x2 hi = __builtin_convertvector(floatx2{hreg[nq][2], hreg[nq][3]}, bf16x2);
             *reinterpret_cast<bf16x4 *>(sm.hb + pp * N + ((q ^ (pp & HSW)) << 3) + (n0 & 7)) =
                 bf16x4{lo[0], lo[1], hi[0], hi[1]};
         }
@@ -392,10 +410,11 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
         }
 
         // C_i (n = 32 kk + 8 g4 .. +7), the B operand of both C H and C B^T
-        Frag<bf16_t> cfr[NK];
+        Frag<bf16_t> cfr[NKH];  // k-steps nh * NKH + 0 .. NKH-1
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk)
-            lds_frag8(cfr[kk], sm.cs + i * N + (((4 * kk + g4) ^ tr_swz<PPR>(i)) << 3));
+        for (int kq = 0; kq < NKH; ++kq)
+            lds_frag8(cfr[kq],
+                      sm.cs + i * N + (((4 * (nh * NKH + kq) + g4) ^ tr_swz<PPR>(i)) << 3));
 
         // ---- state to output: Y^T[p][i] = exp(s_i) sum_n H[p][n] C_i[n], every p tile
         floatx4 acc[4];
@@ -404,10 +423,10 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
             const int pp = 16 * pt + cc;
             acc[pt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
+            for (int kq = 0; kq < NKH; ++kq) {
                 Frag<bf16_t> hf;
-                lds_frag8(hf, sm.hb + pp * N + (((4 * kk + g4) ^ (pp & HSW)) << 3));
-                mma(acc[pt], hf, cfr[kk]);
+                lds_frag8(hf, sm.hb + pp * N + (((4 * (nh * NKH + kq) + g4) ^ (pp & HSW)) << 3));
+                mma(acc[pt], hf, cfr[kq]);
             }
         }
         {
@@ -421,10 +440,10 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
 
         // ---- the previous block's outputs leave here, between compute phases
         // (a full block: every row is in range)
-        if (k > 0) {
+        if (k > 0 && nh == 0) {
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                const int s = 128 * w + 64 * m + l, r = s >> 3, q = (s & 7) ^ (r & 7);
+                const int s = 128 * wr + 64 * m + l, r = s >> 3, q = (s & 7) ^ (r & 7);
                 store_nt16(yh + (size_t)(t0 - T + r) * xrow + q * 8, ystage[m]);
             }
         }
@@ -432,22 +451,22 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
         // ---- the row tile's causal C B^T tiles (slices js <= w / 2), kept in
         // registers as the B operand of the diagonal products over every p tile:
         // M[i][j] = (C_i . B_j) exp(s_i - s_j) w_j, j <= i
-        for (int js = 0; js <= (w >> 1); ++js) {  // wave-uniform trip count
+        for (int js = 0; js <= (wr >> 1); ++js) {  // wave-uniform trip count
             floatx4 m[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                const int q = 4 * kk + g4;
+            for (int kq = 0; kq < NKH; ++kq) {
+                const int q = 4 * (nh * NKH + kq) + g4;
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     const int j = 32 * js + 16 * half + cc;
                     Frag<bf16_t> bf;
                     lds_frag8(bf, sm.bb + j * N + ((q ^ tr_swz<PPR>(j)) << 3));
-                    mma(m[half], bf, cfr[kk]);
+                    mma(m[half], bf, cfr[kq]);
                 }
             }
             // lane (g4, cc): rows j = 32 js + 16 half + 4 g4 + r of column i
             const int j0 = 32 * js + 4 * g4;
-            const bool diag = js == (w >> 1);
+            const bool diag = js == (wr >> 1);
             float v[8];
             if (diag) {
                 // holds the diagonal: exp per element, causal mask
@@ -487,7 +506,7 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
                 Frag<bf16_t> xf;
                 x_colfrag<0>(xf, xsl, xo[pt]);
                 mma(acc[pt], xf, mf);
-                if (diag && D) {  // uniform
+                if (diag && D && nh == 0) {  // uniform
                     mma(acc[pt], xf, dfr[0]);
                     mma(acc[pt], xf, dfr[1]);
                 }
@@ -496,8 +515,8 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
 
         // ---- state (p tile w): H^T = exp(s_end) H^T + sum_j B_j (exp(s_end - s_j) w_j x_j)^T
         Frag<bf16_t> xr[2];
-        x_colfrag<0>(xr[0], xs, xo[w]);
-        x_colfrag<1>(xr[1], xs, xo[w]);
+        x_colfrag<0>(xr[0], xs, xo[wr]);
+        x_colfrag<1>(xr[1], xs, xo[wr]);
         const int lenk = min(T, Lw - t0);
         if constexpr (VL) {
             // sequences that end inside the block, before its last token je =
@@ -512,9 +531,9 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
                 const int fe = sm.vt[k & 1].fs[e];
                 const float se = tsl[e];
                 const float f = fe < 0 ? __builtin_amdgcn_exp2f(se) : 0.0f;
-                floatx4 he[NT];
+                floatx4 he[NTH];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
+                for (int nt = 0; nt < NTH; ++nt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) he[nt][r] = hreg[nt][r] * f;
 #pragma unroll
@@ -531,21 +550,21 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
                     Frag<bf16_t> xw;
                     pack8(xw, v);
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
+                    for (int nt = 0; nt < NTH; ++nt) {
                         Frag<bf16_t> bf;
-                        colfrag_swz<PPR>(bf, sm.bb, jb, jb + 16, nt * 16);
+                        colfrag_swz<PPR>(bf, sm.bb, jb, jb + 16, (nh * NTH + nt) * 16);
                         mma(he[nt], bf, xw);
                     }
                 }
                 float *out = vl.seq_states + ((size_t)sm.mts[k & 1][e].y * H + h) * P * N + hoff;
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
+                for (int nt = 0; nt < NTH; ++nt)
                     *reinterpret_cast<float4 *>(out + 16 * nt) =
                         make_float4(he[nt][0], he[nt][1], he[nt][2], he[nt][3]);
             }
         }
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int nt = 0; nt < NTH; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) hreg[nt][r] *= dec;
 #pragma unroll
@@ -562,9 +581,9 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
             Frag<bf16_t> xw;
             pack8(xw, v);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
+            for (int nt = 0; nt < NTH; ++nt) {
                 Frag<bf16_t> bf;
-                colfrag_swz<PPR>(bf, sm.bb, jb, jb + 16, nt * 16);
+                colfrag_swz<PPR>(bf, sm.bb, jb, jb + 16, (nh * NTH + nt) * 16);
                 mma(hreg[nt], bf, xw);
             }
         }
@@ -575,7 +594,7 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
                 float *out =
                     vl.seq_states + ((size_t)sm.mts[k & 1][lenk - 1].y * H + h) * P * N + hoff;
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
+                for (int nt = 0; nt < NTH; ++nt)
                     *reinterpret_cast<float4 *>(out + 16 * nt) =
                         make_float4(hreg[nt][0], hreg[nt][1], hreg[nt][2], hreg[nt][3]);
             }
@@ -583,6 +602,13 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
 
         // the next block's tables, by a wavefront with one C B^T tile
         if (w == 0 && k + 1 < nblk) make_tables(k + 1);
+
+        if constexpr (HALVES) {  // the second half's partial outputs to the first
+            if (nh == 1) {
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) sm.xch[4 * wr + pt][l] = acc[pt];
+            }
+        }
 
         // x, B, C, dt and the state of this block consumed by every wavefront
         barrier_lds();
@@ -592,6 +618,15 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
         // block, whose staged outputs every wavefront has read)
         if (NXB == 3 && k + 2 < nblk) issue_x(k + 2);
 
+        if constexpr (HALVES) {
+            if (nh == 1) continue;  // uniform: the first half stages and stores the rows
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const floatx4 o = sm.xch[4 * wr + pt][l];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[pt][r] += o[r];
+            }
+        }
         // ---- the outputs: this wavefront's rows, every column, into the x buffer
         __bf16 *xw_ = sm.xb[k % NXB];
 #pragma unroll
@@ -605,20 +640,20 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : N == 128 ? 2 : 1) void ssd_forwa
         // registers; stored during the next block
 #pragma unroll
         for (int m = 0; m < 2; ++m)
-            ystage[m] = *reinterpret_cast<const uint4 *>(xs + (128 * w + 64 * m + l) * 8);
+            ystage[m] = *reinterpret_cast<const uint4 *>(xs + (128 * wr + 64 * m + l) * 8);
     }
-    {  // the last block's outputs (possibly a partial block)
+    if (nh == 0) {  // the last block's outputs (possibly a partial block)
         const int t0 = (nblk - 1) * T, len = Lw - t0;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const int s = 128 * w + 64 * m + l, r = s >> 3, q = (s & 7) ^ (r & 7);
+            const int s = 128 * wr + 64 * m + l, r = s >> 3, q = (s & 7) ^ (r & 7);
             if (r < len) store_nt16(yh + (size_t)(t0 + r) * xrow + q * 8, ystage[m]);
         }
     }
 
     if (final_state && seg == nseg - 1) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int nt = 0; nt < NTH; ++nt)
             *reinterpret_cast<float4 *>(final_state + bh * P * N + hoff + 16 * nt) =
                 make_float4(hreg[nt][0], hreg[nt][1], hreg[nt][2], hreg[nt][3]);
     }
@@ -865,7 +900,7 @@ static hipError_t launch_onepass_n(const void *x, const void *dt, const float *A
     const OnepassSegs segs{pl.S, pl.per_seg * kOpT, npc, pl.k, scratch, ld};
     const int units = batch * nheads * pl.S;
     const int per = (units + 7) / 8;
-    ssd_forward_onepass_kernel<N, VL><<<per * 8, 256, 0, stream>>>(
+    ssd_forward_onepass_kernel<N, VL><<<per * 8, N == 256 ? 512 : 256, 0, stream>>>(
         xb, dtb, A, Bb, Cb, D, init, opts, batch, seqlen, nheads, ngroups, per, segs, vl,
         static_cast<bf16_t *>(y), final_state);
     return hipGetLastError();
