@@ -681,12 +681,15 @@ struct SegStateLds {
 };
 
 template <int N, bool VL>
-__global__ __launch_bounds__(256, N == 64 ? 4 : N == 128 ? 3 : 1) void ssd_segment_states_kernel(
+__global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 4 : N == 128 ? 3 : 1) void ssd_segment_states_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ dt, const float *__restrict__ A,
     const bf16_t *__restrict__ B, DtOpts o, int batch, int L, int H, int G, int per,
     OnepassSegs sg, OnepassVl vl) {
     constexpr int P = 64, T = kOpT;
     constexpr int PPR = N / 8, NT = N / 16;
+    // N 256: eight wavefronts, w and w + 4 with halves of the state's n
+    constexpr bool HALVES = N == 256;
+    constexpr int NWV = HALVES ? 8 : 4, NTH = HALVES ? NT / 2 : NT;
     static_assert(N % 32 == 0 && T * PPR >= 256, "state size");
     __shared__ __attribute__((aligned(16))) SegStateLds<N, VL> sm;
 
@@ -698,6 +701,7 @@ __global__ __launch_bounds__(256, N == 64 ? 4 : N == 128 ? 3 : 1) void ssd_segme
     const int tb = pc * sg.len, Lw = min(sg.len, L - tb);
     const size_t bh = (size_t)b * H + h;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = HALVES ? (w & 3) : w, nh = HALVES ? (w >> 2) : 0;  // head-dim tile, n half
     const int l = lane_id(), g4 = l >> 4, cc = l & 15;
     const int nblk = (Lw + T - 1) / T;
 
@@ -721,12 +725,12 @@ __global__ __launch_bounds__(256, N == 64 ? 4 : N == 128 ? 3 : 1) void ssd_segme
         if (w == 0 && k + 1 < nblk) issue_dt(k + 1);
         const bf16_t *xk = xh + (size_t)t0 * xrow, *bk = bg + (size_t)t0 * brow;
 #pragma unroll
-        for (int i = w; i < 8; i += 4) {
+        for (int i = w; i < 8; i += NWV) {
             const int s = i * 64 + l, r = s >> 3, q = (s & 7) ^ (r & 7);
             dma16_sv(xk, (uint32_t)min(r, len - 1) * xrb + q * 16, sm.xb[k & 1] + i * 512);
         }
 #pragma unroll
-        for (int i = w; i < T * PPR / 64; i += 4) {
+        for (int i = w; i < T * PPR / 64; i += NWV) {
             const int s = i * 64 + l, r = s / PPR, q = (s % PPR) ^ tr_swz<PPR>(r);
             dma16_sv(bk, (uint32_t)min(r, len - 1) * brb + q * 16, sm.bb[k & 1] + i * 512);
         }
@@ -755,9 +759,9 @@ __global__ __launch_bounds__(256, N == 64 ? 4 : N == 128 ? 3 : 1) void ssd_segme
         }
     };
 
-    floatx4 hreg[NT];
+    floatx4 hreg[NTH];  // n tiles nh * NTH + 0 .. NTH-1
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) hreg[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nt = 0; nt < NTH; ++nt) hreg[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     float ld = 0.0f;  // the piece's log2-decay so far
     int xo[4];
     x_colfrag_offsets(xo, l);
@@ -780,10 +784,10 @@ __global__ __launch_bounds__(256, N == 64 ? 4 : N == 128 ? 3 : 1) void ssd_segme
 
         // H^T = exp(s_end) H^T + sum_j B_j (exp(s_end - s_j) w_j x_j)^T, p tile w
         Frag<bf16_t> xr[2];
-        x_colfrag<0>(xr[0], xs, xo[w]);
-        x_colfrag<1>(xr[1], xs, xo[w]);
+        x_colfrag<0>(xr[0], xs, xo[wr]);
+        x_colfrag<1>(xr[1], xs, xo[wr]);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+        for (int nt = 0; nt < NTH; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) hreg[nt][r] *= dec;
 #pragma unroll
@@ -800,9 +804,9 @@ __global__ __launch_bounds__(256, N == 64 ? 4 : N == 128 ? 3 : 1) void ssd_segme
             Frag<bf16_t> xw;
             pack8(xw, v);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
+            for (int nt = 0; nt < NTH; ++nt) {
                 Frag<bf16_t> bf;
-                colfrag_swz<PPR>(bf, bs_, jb, jb + 16, nt * 16);
+                colfrag_swz<PPR>(bf, bs_, jb, jb + 16, (nh * NTH + nt) * 16);
                 mma(hreg[nt], bf, xw);
             }
         }
@@ -810,9 +814,10 @@ __global__ __launch_bounds__(256, N == 64 ? 4 : N == 128 ? 3 : 1) void ssd_segme
         if (w == 0 && k + 1 < nblk) make_tables(k + 1);
     }
 
-    float *sj = sg.state + (bh * sg.npc + pc) * P * N + (size_t)(16 * w + cc) * N + 4 * g4;
+    float *sj = sg.state + (bh * sg.npc + pc) * P * N + (size_t)(16 * wr + cc) * N + 4 * g4 +
+                16 * NTH * nh;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NTH; ++nt)
         *reinterpret_cast<float4 *>(sj + 16 * nt) =
             make_float4(hreg[nt][0], hreg[nt][1], hreg[nt][2], hreg[nt][3]);
     if (w == 0 && l == 0) sg.ld[bh * sg.npc + pc] = ld;
@@ -891,7 +896,7 @@ static hipError_t launch_onepass_n(const void *x, const void *dt, const float *A
         const OnepassSegs pieces{npc, pl.psub * kOpT, npc, 0, scratch, ld};
         const int units = batch * nheads * npc;
         const int per = (units + 7) / 8;
-        ssd_segment_states_kernel<N, VL><<<per * 8, 256, 0, stream>>>(
+        ssd_segment_states_kernel<N, VL><<<per * 8, N == 256 ? 512 : 256, 0, stream>>>(
             xb, dtb, A, Bb, opts, batch, seqlen, nheads, ngroups, per, pieces, vl);
         hipError_t e = hipGetLastError();
         if (e == hipSuccess && between) e = hipEventRecord(between, stream);
