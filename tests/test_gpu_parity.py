@@ -401,3 +401,14 @@ def test_options_decode_f32():
     w = W.Workload("decode_f32_opts", 16, 12, 8, 64, 2, 64, 0, "f32", 1 / 8, 1e-3, 1e-1,
                    init_std=0.2, decode=True, seed=712)
     _decode(w, zero_init=False, nunits=64, **OPTION_SETS["all_zoh"])
+
+
+def test_segments_many_n256_sampled():
+    # batch 1, 16 heads, 16384 tokens at N 256: many segments and pieces of the
+    # eight-wavefront kernels, an initial state; sampled heads against the oracle
+    w = W.small("seg_many_n256", 1, 16384, 16, 64, 2, 256, 128, "bf16", seed=980, init_std=0.1,
+                dt_lo=1e-4, dt_hi=1e-2)
+    S = plan(w)
+    print_case(f"   segments {S}")
+    assert S >= 8
+    check_forward(w, units=[0, 7, 8, 15], both_D=False)

@@ -274,3 +274,15 @@ def test_varlen_onepass_sequences_are_independent():
     keep[70:450] = False
     assert torch.equal(y1[0, keep], y2[0, keep])
     assert torch.equal(s1[[0, 2, 3]], s2[[0, 2, 3]]) and not torch.equal(s1[1], s2[1])
+
+
+def test_varlen_onepass_sequences_across_segments():
+    # 8192 tokens of 16 heads at N 128 in sequences of up to 3000 tokens: the
+    # token axis runs as many segments, most sequences span several of them
+    L = 8192
+    cu = W.packed_cu_seqlens(L, 3000, seed=940)
+    w = _w("vl_op_across", L, 16, 2, 128, 256, "bf16", 941)
+    S = _plan(w)
+    print_case(f"   segments {S}, sequences {cu.size - 1}")
+    assert S >= 8
+    check_varlen(w, cu, units=[0, 5, 9, 15])
