@@ -837,11 +837,14 @@ def main():
             acc_w = accounting(wl)
             hbm = {}
             for k, v in r["stage_ms"].items():
-                nb = acc_w[k]["bytes"]
+                nb, nf = acc_w[k]["bytes"], acc_w[k]["flops"]
                 if nb and v > 0:
                     gbs = nb / (v * 1e-3) / 1e9
+                    tfl = nf / (v * 1e-3) / 1e12
+                    peak = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
                     hbm[k] = {"alg_MB": round(nb / 1e6, 1), "GB_s": round(gbs, 1),
-                              "hbm_frac": round(gbs / HBM_PEAK_GBS, 3)}
+                              "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
+                              "TFLOP_s": round(tfl, 2), "mfma_frac": round(tfl / peak, 4)}
             extra[name] = {"us_per_forward": round(r["wall_ms"] * 1e3, 1),
                            "tokens_per_s": round(wl.tokens / (r["wall_ms"] * 1e-3)),
                            "stage_us": {k: round(v * 1e3, 1) for k, v in r["stage_ms"].items()},
