@@ -4,8 +4,10 @@ One step = one full SSD forward over the Mamba-2 2.7B-shaped layer: batch 8,
 L 2048, 80 heads x P 64, N 64, one B/C group, chunk 256, bf16 inputs, fp32
 accumulation, inputs already resident in HBM. Prints ONE JSON line. For this
 shape the library runs the whole forward as its single-pass kernel
-(forward_onepass); other shapes run the stages chunk_cumsum, chunk_state,
-state_passing, chunk_cb, chunk_scan.
+(forward_onepass); with few (batch, head) pairs it adds a segment-state
+kernel first (segment_states); shapes outside the single-pass kernel run
+the stages chunk_cumsum, chunk_state, state_passing, chunk_cb, chunk_scan.
+The library's own ssd_forward_plan says which.
 
 Per-kernel GPU times come from HIP events the library records between its
 launches (ssd_forward_timed) on the launch stream, inside the timed region.
