@@ -94,33 +94,13 @@ def onepass_accounting(w):
 
 def onepass_plan(w):
     """(S, k, per_seg): segments, pieces per segment and blocks per segment of
-    the single-pass forward, mirroring onepass_plan in the library's
-    fwd_onepass.hip (its scratch: the workspace's float32 states region); S is
-    checked against the library's own ssd_forward_plan."""
-    Bt, L, H, P, N, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.chunk
-    slots = {64: 3, 128: 2}.get(N, 1) * 256
-    so_slots = {64: 4, 128: 3}.get(N, 1) * 256
-    units, blocks = Bt * H, -(-L // 64)
-    scratch = Bt * (-(-L // Q)) * H * P * N * 4
-    plan = (1, 1, blocks)
-    S0 = min(slots // units, blocks // 4)
-    if S0 > 1:
-        per = -(-blocks // S0)
-        max_pieces = scratch // ((64 * N + 1) * 4)
-        k = max(1, min(so_slots // (units * (S0 - 1)), per // 2))
-        while True:
-            per_seg = k * (-(-per // k))
-            S = -(-blocks // per_seg)
-            if S <= 1:
-                break
-            if (S - 1) * k <= max_pieces:
-                plan = (S, k, per_seg)
-                break
-            if k == 1:
-                break
-            k = max(1, min(max_pieces // (S - 1), k - 1))
-    assert plan[0] == segments_of(w), (plan, segments_of(w))
-    return plan
+    the single-pass forward, from the library's own plan (ssd_forward_plan_info)."""
+    import torch
+    import structured_state_space_ssd_amd as ssd
+    p = ssd.plan_info(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk,
+                      torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+    assert p["path"] == "single_pass", p
+    return p["segments"], max(1, p["pieces"]), p["segment_blocks"]
 
 
 def accounting(w):

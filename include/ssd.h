@@ -106,8 +106,37 @@ typedef struct {
 const char *ssd_strerror(int status);
 
 /*
- * Bytes of workspace ssd_forward needs (0 for invalid sizes). The workspace
- * holds, at 256-byte aligned offsets in this order:
+ * How ssd_forward runs for given sizes and dt pointer (ssd_forward_plan_info).
+ *   path            SSD_PATH_SINGLE_PASS: the single-pass kernel (SSD_BF16, dstate
+ *                   64, 128 or 256, nheads a multiple of 8, 16-byte aligned dt);
+ *                   SSD_PATH_STAGES: the stage kernels listed under ssd_forward.
+ *   segments        S >= 1 segments per sequence on the single-pass kernel; 0 on
+ *                   the stage kernels.
+ *   pieces          K: pieces per segment of the first S-1 segments (0 when S == 1).
+ *   block_tokens    tokens per block: 64 on the single-pass kernel (whatever
+ *                   `chunk` says), the chunk length on the stage kernels.
+ *   segment_blocks  blocks per segment (the last segment may hold fewer).
+ *   piece_blocks    blocks per piece (0 when S == 1).
+ *   workspace_bytes workspace ssd_forward needs for exactly these arguments.
+ */
+typedef enum { SSD_PATH_STAGES = 0, SSD_PATH_SINGLE_PASS = 1 } ssd_path;
+typedef struct {
+    int path, segments, pieces, block_tokens, segment_blocks, piece_blocks;
+    size_t workspace_bytes;
+} ssd_plan;
+
+/*
+ * Fills *out with the plan of ssd_forward (and ssd_forward_ex / _timed) for
+ * these sizes and this dt pointer (only its alignment is looked at; it is not
+ * read). Returns SSD_OK, SSD_ERR_NULL for a NULL `out`, or the status
+ * ssd_forward would return for these sizes (then *out is zeroed).
+ *
+ * Workspace layout. On the single-pass path it is the segment scratch only,
+ * and only when S > 1: float32 [Bt][H][(S-1)K][P][N], the state each piece of
+ * the first S-1 segments produces from a zero state, then float32
+ * [Bt][H][(S-1)K], each piece's total log2-decay (sum of dt*A over the piece,
+ * times log2(e)); with S == 1 no workspace is needed (NULL is accepted). On
+ * the stage path it holds, at 256-byte aligned offsets in this order:
  *   dA_cumsum   float32 [Bt][H][nC*Q]      within-chunk prefix sums of dt*A
  *   delta       float32 [Bt][H][nC*Q]      each token's input weight w_t, same layout
  *                                          (zero past seqlen)
@@ -116,16 +145,19 @@ const char *ssd_strerror(int status);
  *                                          operand type (bf16 for SSD_BF16, else float32)
  *   cb          SSD_F32 only: ssd_chunk_cb_size(...) bytes, C B^T tiles of every
  *               chunk (the SSD_BF16 chunk scan forms them itself; no space)
- * After the forward pass has run, these hold the intermediate results of the
- * stages below (a caller may read them, e.g. to test a stage), except that
- * for SSD_BF16 with batch * nheads >= 512 stages 2 and 3 run as one kernel
- * that keeps the per-chunk states on chip (`states` is then not written).
- * When the forward runs as the single-pass kernel (see ssd_forward) only the
- * start of `states` is used, and only when the sequences are cut into S > 1
- * segments: the first S-1 segments are cut into K pieces each (K chosen by
- * the library), and `states` receives float32 [Bt][H][(S-1)K][P][N], the
- * state each piece produces from a zero state, then float32 [Bt][H][(S-1)K],
- * each piece's total log2-decay (sum of dt*A over the piece, times log2(e)).
+ * After a stage-path forward these hold the intermediate results of the
+ * stages (a caller may read them, e.g. to test a stage), except that for
+ * SSD_BF16 with batch * nheads >= 512 stages 2 and 3 run as one kernel that
+ * keeps the per-chunk states on chip (`states` is then not written).
+ */
+int ssd_forward_plan_info(int batch, int seqlen, int nheads, int headdim, int ngroups,
+                          int dstate, int chunk, int dtype, const void *dt, ssd_plan *out);
+
+/*
+ * Bytes of workspace ssd_forward needs for these sizes with a 16-byte aligned
+ * dt (0 for invalid sizes, and 0 where the forward needs none). An unaligned
+ * dt makes the forward take the stage kernels, whose larger need
+ * ssd_forward_plan_info reports for that pointer.
  */
 size_t ssd_forward_workspace_size(int batch, int seqlen, int nheads, int headdim,
                                   int ngroups, int dstate, int chunk, int dtype);
@@ -145,12 +177,15 @@ size_t ssd_forward_workspace_size(int batch, int seqlen, int nheads, int headdim
  * a zero state, and the single-pass kernel then runs one workgroup per
  * (batch, head, segment), each starting from the state the pieces before it
  * pass on (the same recurrence at piece granularity). `chunk` must still be valid but does
- * not set that kernel's block length.
+ * not set that kernel's block length. ssd_forward_plan_info reports the path,
+ * the cut and the workspace.
  *   D           nullable: no feed-through term.
  *   init_state  nullable: the state before token 0 is zero.
  *   y           output, [Bt][L][H][P] in dtype.
  *   final_state nullable: if given, receives the state after token L-1.
- *   workspace   at least ssd_forward_workspace_size(...) bytes, 256-byte aligned.
+ *   workspace   at least ssd_plan.workspace_bytes for these arguments (for an
+ *               aligned dt: ssd_forward_workspace_size(...)), 256-byte aligned;
+ *               NULL when that is 0. Too small: SSD_ERR_WORKSPACE.
  */
 int ssd_forward(const void *x, const void *dt, const float *A, const void *B,
                 const void *C, const float *D, int batch, int seqlen, int nheads,

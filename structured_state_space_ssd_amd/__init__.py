@@ -14,7 +14,7 @@ import torch
 from . import _native
 from ._native import SSDError, check, dtype_code, ptr, stream_handle
 
-__all__ = ["forward", "forward_plan", "backward", "forward_varlen", "step", "options", "workspace_size", "chunk_cumsum", "chunk_state",
+__all__ = ["forward", "forward_plan", "plan_info", "backward", "forward_varlen", "step", "options", "workspace_size", "chunk_cumsum", "chunk_state",
            "state_passing", "chunk_cb", "chunk_scan", "SSDError", "stages"]
 
 HEADDIM = 64
@@ -66,6 +66,23 @@ def workspace_size(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, dtype
                                                       chunk, dtype_code(dtype)))
 
 
+def plan_info(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, dtype=torch.bfloat16,
+              dt=None) -> dict:
+    """How ``forward`` runs for these sizes (ssd_forward_plan_info): path
+    ("single_pass" or "stages"), segments S, pieces K, block_tokens,
+    segment_blocks, piece_blocks and workspace_bytes. ``dt`` (a tensor, or
+    None for an aligned pointer) matters only through its alignment."""
+    p = _native.SsdPlan()
+    addr = dt.data_ptr() if dt is not None else 256
+    rc = int(_native.lib.ssd_forward_plan_info(batch, seqlen, nheads, headdim, ngroups, dstate,
+                                               chunk, dtype_code(dtype), addr, ctypes.byref(p)))
+    check(rc, "ssd_forward_plan_info")
+    return {"path": "single_pass" if p.path == 1 else "stages", "segments": p.segments,
+            "pieces": p.pieces, "block_tokens": p.block_tokens,
+            "segment_blocks": p.segment_blocks, "piece_blocks": p.piece_blocks,
+            "workspace_bytes": int(p.workspace_bytes)}
+
+
 def forward_plan(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, dtype=torch.bfloat16,
                  dt=None) -> int:
     """Segments per sequence of the single-pass forward for these sizes (0: the
@@ -77,6 +94,19 @@ def forward_plan(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, dtype=t
     if r < 0:
         _native.check(r, "ssd_forward_plan")
     return r
+
+
+def _shape(t, name, want):
+    """ValueError unless tensor t (None allowed) has shape ``want``."""
+    if t is not None and tuple(t.shape) != tuple(want):
+        raise ValueError(f"{name} must have shape {tuple(want)}, got {tuple(t.shape)}")
+
+
+def _params(A, D, H, dt_bias=None):
+    """A and D (nullable) float32 [H], dt_bias (nullable) float32 [H]."""
+    _shape(A, "A", (H,))
+    _shape(D, "D", (H,))
+    _shape(dt_bias, "dt_bias", (H,))
 
 
 def forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, return_final_state=False,
@@ -92,22 +122,33 @@ def forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, return_final_sta
     the library records them around its five stages (see ssd_forward_timed),
     skipping the None entries.
     """
+    # shapes first (the C ABI takes sizes, not shapes: a mis-shaped tensor
+    # would be read or written out of bounds), then device, layout and dtype
+    for t, n in ((x, "x"), (dt, "dt"), (A, "A"), (B, "B"), (C, "C")):
+        if t is None:
+            raise ValueError(f"{n} is required")
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [Bt, L, H, P] and B [Bt, L, G, N]")
+    Bt, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if tuple(dt.shape) != (Bt, L, H) or tuple(B.shape) != (Bt, L, G, N) or C.shape != B.shape:
+        raise ValueError("shape mismatch among x, dt, B, C")
+    _params(A, D, H, dt_bias)
+    _shape(init_state, "init_state", (Bt, H, P, N))
+    _shape(y, "y", x.shape)
     _req(x, "x")
     dt_ = dtype_code(x.dtype)
-    Bt, L, H, P = x.shape
     _req(dt, "dt", x.dtype)
     _req(B, "B", x.dtype)
     _req(C, "C", x.dtype)
     _req(A, "A", torch.float32)
     _opt(D, "D")
     _opt(init_state, "init_state")
-    G, N = B.shape[2], B.shape[3]
-    if tuple(dt.shape) != (Bt, L, H) or tuple(B.shape) != (Bt, L, G, N) or C.shape != B.shape:
-        raise ValueError("shape mismatch among x, dt, B, C")
     if y is None:
         y = torch.empty_like(x)
+    _req(y, "y", x.dtype)
     fs = torch.empty((Bt, H, P, N), dtype=torch.float32, device=x.device) if return_final_state else None
-    need = workspace_size(Bt, L, H, P, G, N, chunk, x.dtype)
+    need = plan_info(Bt, L, H, P, G, N, chunk, x.dtype, dt)["workspace_bytes"]
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     ev = None
@@ -118,12 +159,10 @@ def forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, return_final_sta
             if e is not None and not e.cuda_event:
                 e.record()  # torch creates the HIP event on its first record
         ev = (ctypes.c_void_p * 6)(*[e.cuda_event if e is not None else None for e in events])
-    if dt_bias is not None and tuple(dt_bias.shape) != (H,):
-        raise ValueError("dt_bias must have shape [H]")
     opts = options(dt_bias, dt_softplus, dt_limit, zoh)
     rc = _native.lib.ssd_forward_ex(
         ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), Bt, L, H, P, G, N, chunk, dt_,
-        ptr(init_state), ptr(y), ptr(fs), ptr(workspace), workspace.numel(), _optref(opts),
+        ptr(init_state), ptr(y), ptr(fs), ptr(workspace), workspace.numel() * workspace.element_size(), _optref(opts),
         stream_handle(x.device), ev)
     check(rc, "ssd_forward")
     return (y, fs) if return_final_state else y
@@ -138,21 +177,27 @@ def backward(x, dt, A, B, C, D, dy, init_state=None, dfinal_state=None, dt_bias=
     dA, dD (float32 [H]), dinit (float32 [Bt,H,P,N], or None if not
     want_dinit) and, when dt_bias is given, ddt_bias (float32 [H]).
     """
+    for t, n in ((x, "x"), (dt, "dt"), (A, "A"), (B, "B"), (C, "C"), (dy, "dy")):
+        if t is None:
+            raise ValueError(f"{n} is required")
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [Bt, L, H, P] and B [Bt, L, G, N]")
+    Bt, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if (tuple(dt.shape) != (Bt, L, H) or tuple(B.shape) != (Bt, L, G, N) or C.shape != B.shape
+            or dy.shape != x.shape):
+        raise ValueError("shape mismatch among x, dt, B, C, dy")
+    _params(A, D, H, dt_bias)
+    _shape(init_state, "init_state", (Bt, H, P, N))
+    _shape(dfinal_state, "dfinal_state", (Bt, H, P, N))
     _req(x, "x")
     dt_ = dtype_code(x.dtype)
-    Bt, L, H, P = x.shape
     for t, n in ((dt, "dt"), (B, "B"), (C, "C"), (dy, "dy")):
         _req(t, n, x.dtype)
     _req(A, "A", torch.float32)
     _opt(D, "D")
     _opt(init_state, "init_state")
     _opt(dfinal_state, "dfinal_state")
-    G, N = B.shape[2], B.shape[3]
-    if (tuple(dt.shape) != (Bt, L, H) or tuple(B.shape) != (Bt, L, G, N) or C.shape != B.shape
-            or dy.shape != x.shape):
-        raise ValueError("shape mismatch among x, dt, B, C, dy")
-    if dt_bias is not None and tuple(dt_bias.shape) != (H,):
-        raise ValueError("dt_bias must have shape [H]")
     dev = x.device
     out = {"dx": torch.empty_like(x), "ddt": torch.empty_like(dt), "dB": torch.empty_like(B),
            "dC": torch.empty_like(C), "dA": torch.empty(H, dtype=torch.float32, device=dev),
@@ -169,7 +214,7 @@ def backward(x, dt, A, B, C, D, dy, init_state=None, dfinal_state=None, dt_bias=
         ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), ptr(init_state), ptr(dy),
         ptr(dfinal_state), Bt, L, H, P, G, N, dt_, ptr(out["dx"]), ptr(out["ddt"]),
         ptr(out["dA"]), ptr(out["dB"]), ptr(out["dC"]), ptr(out["dD"]), ptr(out["dinit"]),
-        ptr(out.get("ddt_bias")), ptr(workspace), workspace.numel(), _optref(opts),
+        ptr(out.get("ddt_bias")), ptr(workspace), workspace.numel() * workspace.element_size(), _optref(opts),
         stream_handle(dev))
     check(rc, "ssd_backward")
     return out
@@ -185,23 +230,30 @@ def forward_varlen(x, dt, A, B, C, D, cu_seqlens, chunk=256, return_seq_states=F
     Returns y (shaped like x) and, if requested, the per-sequence final states
     [nseq,H,P,N] float32. Options as ``forward``.
     """
-    _req(x, "x")
-    dt_ = dtype_code(x.dtype)
+    for t, n in ((x, "x"), (dt, "dt"), (A, "A"), (B, "B"), (C, "C"), (cu_seqlens, "cu_seqlens")):
+        if t is None:
+            raise ValueError(f"{n} is required")
     squeeze = x.dim() == 3
     xs = x.unsqueeze(0) if squeeze else x
-    if xs.shape[0] != 1:
-        raise ValueError("packed sequences use batch 1")
+    if xs.dim() != 4 or xs.shape[0] != 1:
+        raise ValueError("packed sequences use batch 1: x [L, H, P] or [1, L, H, P]")
     _, L, H, P = xs.shape
+    if B.dim() not in (3, 4) or (B.dim() == 4 and B.shape[0] != 1):
+        raise ValueError("B must be [L, G, N] or [1, L, G, N]")
+    G, N = B.shape[-2], B.shape[-1]
+    if (dt.numel() != L * H or B.numel() != L * G * N or C.shape != B.shape
+            or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2):
+        raise ValueError("shape mismatch among x, dt, B, C, cu_seqlens")
+    _params(A, D, H, dt_bias)
+    _shape(y, "y", x.shape)
+    _req(x, "x")
+    dt_ = dtype_code(x.dtype)
     _req(dt, "dt", x.dtype)
     _req(B, "B", x.dtype)
     _req(C, "C", x.dtype)
     _req(A, "A", torch.float32)
     _opt(D, "D")
     _req(cu_seqlens, "cu_seqlens", torch.int32)
-    G, N = B.shape[-2], B.shape[-1]
-    if (dt.numel() != L * H or B.numel() != L * G * N or C.shape != B.shape
-            or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2):
-        raise ValueError("shape mismatch among x, dt, B, C, cu_seqlens")
     nseq = cu_seqlens.numel() - 1
     if y is None:
         y = torch.empty_like(x)
@@ -210,12 +262,10 @@ def forward_varlen(x, dt, A, B, C, D, cu_seqlens, chunk=256, return_seq_states=F
     need = int(_native.lib.ssd_forward_varlen_workspace_size(L, H, P, G, N, chunk, dt_))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    if dt_bias is not None and tuple(dt_bias.shape) != (H,):
-        raise ValueError("dt_bias must have shape [H]")
     opts = options(dt_bias, dt_softplus, dt_limit, zoh)
     rc = _native.lib.ssd_forward_varlen(
         ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), ptr(cu_seqlens), nseq, L, H, P, G, N,
-        chunk, dt_, ptr(y), ptr(ss), ptr(workspace), workspace.numel(), _optref(opts),
+        chunk, dt_, ptr(y), ptr(ss), ptr(workspace), workspace.numel() * workspace.element_size(), _optref(opts),
         stream_handle(x.device))
     check(rc, "ssd_forward_varlen")
     return (y, ss) if return_seq_states else y
@@ -228,22 +278,29 @@ def step(state, x, dt, A, B, C, D=None, y=None, dt_bias=None, dt_softplus=False,
     x [Bt,H,P], dt [Bt,H], B, C [Bt,G,N] (float32 or bfloat16), A, D [H] float32.
     dt_bias, dt_softplus, dt_limit, zoh: see ``options``.
     """
+    for t, n in ((state, "state"), (x, "x"), (dt, "dt"), (A, "A"), (B, "B"), (C, "C")):
+        if t is None:
+            raise ValueError(f"{n} is required")
+    if x.dim() != 3 or B.dim() != 3:
+        raise ValueError("x must be [Bt, H, P] and B [Bt, G, N]")
+    Bt, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    if (tuple(state.shape) != (Bt, H, P, N) or tuple(dt.shape) != (Bt, H)
+            or tuple(B.shape) != (Bt, G, N) or C.shape != B.shape):
+        raise ValueError("shape mismatch among state, x, dt, B, C")
+    _params(A, D, H, dt_bias)
+    _shape(y, "y", x.shape)
     _req(state, "state", torch.float32)
     _req(x, "x")
     dt_ = dtype_code(x.dtype)
-    Bt, H, P = x.shape
     _req(dt, "dt", x.dtype)
     _req(B, "B", x.dtype)
     _req(C, "C", x.dtype)
     _req(A, "A", torch.float32)
     _opt(D, "D")
-    G, N = B.shape[1], B.shape[2]
-    if tuple(state.shape) != (Bt, H, P, N) or tuple(dt.shape) != (Bt, H) or C.shape != B.shape:
-        raise ValueError("shape mismatch among state, x, dt, B, C")
     if y is None:
         y = torch.empty_like(x)
-    if dt_bias is not None and tuple(dt_bias.shape) != (H,):
-        raise ValueError("dt_bias must have shape [H]")
+    _req(y, "y", x.dtype)
     opts = options(dt_bias, dt_softplus, dt_limit, zoh)
     rc = _native.lib.ssd_step_ex(ptr(state), ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D),
                                  Bt, H, P, G, N, dt_, ptr(y), _optref(opts),

@@ -27,14 +27,23 @@ class SsdOptions(ctypes.Structure):
                 ("dt_max", ctypes.c_float), ("discretization", ctypes.c_int)]
 
 
+class SsdPlan(ctypes.Structure):
+    """ssd_plan of include/ssd.h."""
+    _fields_ = [("path", ctypes.c_int), ("segments", ctypes.c_int), ("pieces", ctypes.c_int),
+                ("block_tokens", ctypes.c_int), ("segment_blocks", ctypes.c_int),
+                ("piece_blocks", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
+
+
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _op = ctypes.POINTER(SsdOptions)
+_pp = ctypes.POINTER(SsdPlan)
 
 # name -> (restype, argtypes); mirrors include/ssd.h
 SIGNATURES = {
     "ssd_strerror": (ctypes.c_char_p, [_i]),
     "ssd_forward_workspace_size": (_sz, [_i] * 8),
     "ssd_forward_plan": (_i, [_i] * 8 + [_vp]),
+    "ssd_forward_plan_info": (_i, [_i] * 8 + [_vp, _pp]),
     "ssd_chunk_cb_size": (_sz, [_i] * 5),
     "ssd_chunk_cb": (_i, [_vp, _vp] + [_i] * 6 + [_vp, _vp]),
     "ssd_forward": (_i, [_vp] * 6 + [_i] * 8 + [_vp, _vp, _vp, _vp, _sz, _vp]),

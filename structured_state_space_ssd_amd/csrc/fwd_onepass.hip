@@ -832,51 +832,42 @@ bool forward_onepass_ok(int batch, int nheads, int dstate, bool bf16, const void
 
 namespace {
 
-// The plan of a single-pass forward: S segments of per_seg blocks (the last
-// may hold fewer), and, when S > 1, the first S - 1 segments cut into k
-// pieces of psub blocks for the segment-state kernel.
-struct OnepassPlan {
-    int S, k, per_seg, psub;
-};
-
 size_t piece_bytes(int dstate) { return (64 * (size_t)dstate + 1) * sizeof(float); }
 
+}  // namespace
+
 // Enough (batch, head) pairs fill the GPU with one workgroup each (three per
-// compute unit at N = 64, two at N = 128, one at N = 256). With fewer, each sequence is cut
-// into S segments of whole 64-token blocks, S the number of workgroups per
-// pair that still fit in one round of workgroups, each segment at least 4
-// blocks long. The segment-state kernel, lighter (four workgroups per
-// compute unit at N = 64, three at N = 128, one at N = 256), cuts each of the
-// first S - 1 segments into k pieces of at least 2 blocks so that it, too,
+// compute unit at N = 64, two at N = 128, one at N = 256). With fewer, each
+// sequence is cut into S segments of whole 64-token blocks, S the number of
+// workgroups per pair that still fit in one round of workgroups, each segment
+// at least 4 blocks long. The segment-state kernel, lighter (four workgroups
+// per compute unit at N = 64, three at N = 128, one at N = 256), cuts each of
+// the first S - 1 segments into k pieces of at least 2 blocks so that it, too,
 // fills the GPU.
-// The scratch holds one float32 state and one decay per piece: a smaller
-// scratch lowers k, then S.
-OnepassPlan onepass_plan(int batch, int seqlen, int nheads, int dstate, size_t scratch_bytes) {
+// The scratch holds one float32 state and one decay per piece of every
+// (batch, head): batch * nheads * (S - 1) * k of them. A cap smaller than
+// what that needs lowers k, then gives up the segments.
+OnepassPlan forward_onepass_plan(int batch, int seqlen, int nheads, int dstate, size_t cap) {
     const int slots = (dstate == 64 ? 3 : dstate == 128 ? 2 : 1) * 256,
               so_slots = (dstate == 64 ? 4 : dstate == 128 ? 3 : 1) * 256;
-    const int units = batch * nheads;
+    const size_t units = (size_t)batch * nheads;
     const int blocks = (seqlen + kOpT - 1) / kOpT;
-    const OnepassPlan one{1, 1, blocks, blocks};
-    const int S0 = std::min(slots / units, blocks / 4);
+    const OnepassPlan one{1, 0, blocks, blocks, 0};
+    if (units >= (size_t)slots) return one;
+    const int S0 = std::min((int)(slots / units), blocks / 4);
     if (S0 <= 1) return one;
     const int per = (blocks + S0 - 1) / S0;
-    const size_t max_pieces = scratch_bytes / piece_bytes(dstate);
-    int k = std::max(1, std::min(so_slots / (units * (S0 - 1)), per / 2));
+    const size_t max_pieces = cap / piece_bytes(dstate);
+    int k = std::max(1, std::min((int)(so_slots / (units * (S0 - 1))), per / 2));
     for (;;) {
         const int psub = (per + k - 1) / k, per_seg = k * psub;
         const int S = (blocks + per_seg - 1) / per_seg;  // the last segment is not empty
         if (S <= 1) return one;
-        if ((size_t)(S - 1) * k <= max_pieces) return OnepassPlan{S, k, per_seg, psub};
+        const size_t pieces = units * (size_t)(S - 1) * k;
+        if (pieces <= max_pieces) return OnepassPlan{S, k, per_seg, psub, pieces * piece_bytes(dstate)};
         if (k == 1) return one;
-        k = std::max<int>(1, (int)std::min<size_t>(max_pieces / (S - 1), k - 1));
+        k = std::max<int>(1, (int)std::min<size_t>(max_pieces / (units * (S - 1)), k - 1));
     }
-}
-
-}  // namespace
-
-int forward_onepass_segments(int batch, int seqlen, int nheads, int dstate,
-                             size_t scratch_bytes) {
-    return onepass_plan(batch, seqlen, nheads, dstate, scratch_bytes).S;
 }
 
 template <int N, bool VL>
@@ -891,7 +882,7 @@ static hipError_t launch_onepass_n(const void *x, const void *dt, const float *A
     const auto Bb = static_cast<const bf16_t *>(B);
     const auto Cb = static_cast<const bf16_t *>(C);
     const int npc = pl.S > 1 ? (pl.S - 1) * pl.k : 0;
-    float *ld = scratch ? scratch + (size_t)batch * nheads * npc * 64 * N : nullptr;
+    float *ld = npc ? scratch + (size_t)batch * nheads * npc * 64 * N : nullptr;
     if (pl.S > 1) {
         const OnepassSegs pieces{npc, pl.psub * kOpT, npc, 0, scratch, ld};
         const int units = batch * nheads * npc;
@@ -914,13 +905,13 @@ static hipError_t launch_onepass_n(const void *x, const void *dt, const float *A
 hipError_t launch_forward_onepass(const void *x, const void *dt, const float *A, const void *B,
                                   const void *C, const float *D, const float *init,
                                   const DtOpts &opts, int batch, int seqlen, int nheads,
-                                  int ngroups, int dstate, float *scratch, size_t scratch_bytes,
+                                  int ngroups, int dstate, const OnepassPlan &pl, float *scratch,
                                   void *y, float *final_state, hipEvent_t between,
                                   hipStream_t stream, const void *varlen_meta,
                                   float *seq_states) {
-    const OnepassPlan pl = onepass_plan(batch, seqlen, nheads, dstate, scratch ? scratch_bytes : 0);
     const OnepassVl vl{static_cast<const int4 *>(varlen_meta), seq_states};
     if (varlen_meta && (batch != 1 || init || final_state)) return hipErrorInvalidValue;
+    if (pl.S > 1 && !scratch) return hipErrorInvalidValue;
 #define SSD_ONEPASS(NN, VV)                                                                      \
     return launch_onepass_n<NN, VV>(x, dt, A, B, C, D, init, opts, batch, seqlen, nheads,       \
                                     ngroups, pl, scratch, vl, y, final_state, between, stream)

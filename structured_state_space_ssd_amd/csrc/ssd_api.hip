@@ -94,16 +94,33 @@ BwdWorkspace bwd_layout(int batch, int seqlen, int nheads, int headdim, int ngro
     return w;
 }
 
-// Segments of the single-pass forward for these sizes (0: the stage kernels
-// run). Their scratch is the workspace's `states` region.
-size_t onepass_scratch(const Workspace &ws) { return ws.init_off - ws.states_off; }
+// The path ssd_forward takes and the workspace it needs. The single-pass
+// kernel needs scratch only for the pieces' states when the sequences are cut
+// into segments (at most `cap` bytes of it); the stage kernels need the whole
+// layout above.
+struct FwdPlan {
+    bool onepass;
+    ssd::OnepassPlan op;
+    Workspace ws;
+    size_t need;
+};
 
-int onepass_plan(int batch, int seqlen, int nheads, int dstate, int chunk, bool bf16,
-                 const void *dt) {
-    if (!ssd::forward_onepass_ok(batch, nheads, dstate, bf16, dt)) return 0;
-    const Workspace ws = layout(batch, seqlen, nheads, kHeaddim, 1, dstate, chunk, bf16);
-    return ssd::forward_onepass_segments(batch, seqlen, nheads, dstate, onepass_scratch(ws));
+FwdPlan plan_forward(int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate,
+                     int chunk, bool bf16, const void *dt, size_t cap) {
+    FwdPlan f{};
+    f.onepass = ssd::forward_onepass_ok(batch, nheads, dstate, bf16, dt);
+    if (f.onepass) {
+        f.op = ssd::forward_onepass_plan(batch, seqlen, nheads, dstate, cap);
+        f.need = f.op.scratch_bytes;
+    } else {
+        f.ws = layout(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, bf16);
+        f.need = f.ws.total;
+    }
+    return f;
 }
+
+// Any 16-byte aligned address: what the sizing calls assume for dt.
+const void *const kAlignedDt = reinterpret_cast<const void *>(uintptr_t{256});
 
 int check_dims(int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate) {
     if (batch < 1 || seqlen < 1 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1)
@@ -155,18 +172,38 @@ const char *ssd_strerror(int status) {
 
 size_t ssd_forward_workspace_size(int batch, int seqlen, int nheads, int headdim, int ngroups,
                                   int dstate, int chunk, int dtype) {
-    if (batch < 1 || seqlen < 1 || nheads < 1 || headdim < 1 || ngroups < 1 || dstate < 1 ||
-        !supported_chunk(chunk) || !valid_dtype(dtype))
+    ssd_plan p;
+    if (ssd_forward_plan_info(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, dtype,
+                              kAlignedDt, &p) != SSD_OK)
         return 0;
-    return layout(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, dtype == SSD_BF16).total;
+    return p.workspace_bytes;
+}
+
+int ssd_forward_plan_info(int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate,
+                          int chunk, int dtype, const void *dt, ssd_plan *out) {
+    if (!out) return SSD_ERR_NULL;
+    *out = ssd_plan{};
+    const int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
+    if (rc != SSD_OK) return rc;
+    if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    const FwdPlan f = plan_forward(batch, seqlen, nheads, headdim, ngroups, dstate, chunk,
+                                   dtype == SSD_BF16, dt, SIZE_MAX);
+    out->path = f.onepass ? SSD_PATH_SINGLE_PASS : SSD_PATH_STAGES;
+    out->segments = f.onepass ? f.op.S : 0;
+    out->pieces = f.onepass ? f.op.k : 0;
+    out->block_tokens = f.onepass ? 64 : chunk;
+    out->segment_blocks = f.onepass ? f.op.per_seg : 0;
+    out->piece_blocks = f.onepass && f.op.S > 1 ? f.op.psub : 0;
+    out->workspace_bytes = f.need;
+    return SSD_OK;
 }
 
 int ssd_forward_plan(int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate,
                      int chunk, int dtype, const void *dt) {
-    const int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
-    if (rc != SSD_OK) return rc;
-    if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
-    return onepass_plan(batch, seqlen, nheads, dstate, chunk, dtype == SSD_BF16, dt);
+    ssd_plan p;
+    const int rc = ssd_forward_plan_info(batch, seqlen, nheads, headdim, ngroups, dstate, chunk,
+                                         dtype, dt, &p);
+    return rc != SSD_OK ? rc : p.segments;
 }
 
 size_t ssd_forward_varlen_workspace_size(int seqlen, int nheads, int headdim, int ngroups,
@@ -268,11 +305,16 @@ int ssd_chunk_scan(const void *x, const float *delta, const float *dA_cumsum, co
                                             static_cast<hipStream_t>(stream)));
 }
 
-int ssd_forward_ex(const void *x, const void *dt, const float *A, const void *B, const void *C,
-                   const float *D, int batch, int seqlen, int nheads, int headdim, int ngroups,
-                   int dstate, int chunk, int dtype, const float *init_state, void *y,
-                   float *final_state, void *workspace, size_t workspace_bytes,
-                   const ssd_options *opts, void *stream, void *const *events) {
+}  // extern "C"
+
+namespace {
+
+// ssd_forward_ex with the plan's scratch capped at `cap` bytes.
+int forward_impl(const void *x, const void *dt, const float *A, const void *B, const void *C,
+                 const float *D, int batch, int seqlen, int nheads, int headdim, int ngroups,
+                 int dstate, int chunk, int dtype, const float *init_state, void *y,
+                 float *final_state, void *workspace, size_t workspace_bytes,
+                 const ssd_options *opts, void *stream, void *const *events, size_t cap) {
     if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
     int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
     if (rc != SSD_OK) return rc;
@@ -283,38 +325,39 @@ int ssd_forward_ex(const void *x, const void *dt, const float *A, const void *B,
     ssd::DtOpts o;
     rc = dt_opts(opts, o);
     if (rc != SSD_OK) return rc;
-    const Workspace ws = layout(batch, seqlen, nheads, headdim, ngroups, dstate, chunk,
-                                dtype == SSD_BF16);
-    if (!workspace || workspace_bytes < ws.total) return SSD_ERR_WORKSPACE;
+    const bool bf16 = dtype == SSD_BF16;
+    const FwdPlan f =
+        plan_forward(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, bf16, dt, cap);
+    if (f.need > cap) return SSD_ERR_WORKSPACE;
+    if (f.need > 0 && (!workspace || workspace_bytes < f.need)) return SSD_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return SSD_ERR_WORKSPACE;
 
     char *base = static_cast<char *>(workspace);
-    float *cumsum = reinterpret_cast<float *>(base + ws.cumsum_off);
-    float *delta = reinterpret_cast<float *>(base + ws.delta_off);
-    float *states = reinterpret_cast<float *>(base + ws.states_off);
-    void *cinit = base + ws.init_off;
-    void *cb = base + ws.cb_off;
-    const bool bf16 = dtype == SSD_BF16;
     hipStream_t s = static_cast<hipStream_t>(stream);
-
     auto mark = [&](int k) -> hipError_t {
         return events && events[k] ? hipEventRecord(static_cast<hipEvent_t>(events[k]), s)
                                    : hipSuccess;
     };
 
     hipError_t e = mark(0);
-    const int segments = onepass_plan(batch, seqlen, nheads, dstate, chunk, bf16, dt);
-    if (segments > 0) {
+    if (f.onepass) {
         // every stage in one kernel (after the segment-state kernel when the
         // sequences are cut into segments): intervals 0 (and 1), the others empty
+        const int segments = f.op.S;
         if (e == hipSuccess)
             e = ssd::launch_forward_onepass(
-                x, dt, A, B, C, D, init_state, o, batch, seqlen, nheads, ngroups, dstate, states,
-                onepass_scratch(ws), y, final_state,
+                x, dt, A, B, C, D, init_state, o, batch, seqlen, nheads, ngroups, dstate, f.op,
+                reinterpret_cast<float *>(base), y, final_state,
                 segments > 1 && events ? static_cast<hipEvent_t>(events[1]) : nullptr, s);
         for (int k = segments > 1 ? 2 : 1; k <= 5 && e == hipSuccess; ++k) e = mark(k);
         return status_of(e);
     }
+    const Workspace &ws = f.ws;
+    float *cumsum = reinterpret_cast<float *>(base + ws.cumsum_off);
+    float *delta = reinterpret_cast<float *>(base + ws.delta_off);
+    float *states = reinterpret_cast<float *>(base + ws.states_off);
+    void *cinit = base + ws.init_off;
+    void *cb = base + ws.cb_off;
     if (e == hipSuccess)
         e = ssd::launch_chunk_cumsum(dt, A, batch, seqlen, nheads, chunk, bf16, o, cumsum, delta,
                                      s);
@@ -344,6 +387,20 @@ int ssd_forward_ex(const void *x, const void *dt, const float *A, const void *B,
                                    ngroups, dstate, chunk, bf16, y, s);
     if (e == hipSuccess) e = mark(5);
     return status_of(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_forward_ex(const void *x, const void *dt, const float *A, const void *B, const void *C,
+                   const float *D, int batch, int seqlen, int nheads, int headdim, int ngroups,
+                   int dstate, int chunk, int dtype, const float *init_state, void *y,
+                   float *final_state, void *workspace, size_t workspace_bytes,
+                   const ssd_options *opts, void *stream, void *const *events) {
+    return forward_impl(x, dt, A, B, C, D, batch, seqlen, nheads, headdim, ngroups, dstate, chunk,
+                        dtype, init_state, y, final_state, workspace, workspace_bytes, opts,
+                        stream, events, SIZE_MAX);
 }
 
 int ssd_forward_varlen(const void *x, const void *dt, const float *A, const void *B,
@@ -378,16 +435,19 @@ int ssd_forward_varlen(const void *x, const void *dt, const float *A, const void
     void *cb = base + ws.cb_off;
     int *seg = reinterpret_cast<int *>(base + seg_off);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (onepass_plan(1, seqlen, nheads, dstate, chunk, bf16, dt) > 0) {
+    if (ssd::forward_onepass_ok(1, nheads, dstate, bf16, dt)) {
         // the single-pass kernel with sequence masks; the tokens' int4s (16
-        // bytes per token) go where dA_cumsum would (H >= 8 floats per token)
+        // bytes per token) go where dA_cumsum would (H >= 8 floats per token),
+        // the pieces' states into the `states` region (the plan fits them there)
         void *meta = base + ws.cumsum_off;
+        const ssd::OnepassPlan pl =
+            ssd::forward_onepass_plan(1, seqlen, nheads, dstate, ws.init_off - ws.states_off);
         hipError_t e = ssd::launch_onepass_varlen_prep(cu_seqlens, nseq, seqlen, nheads, dstate,
                                                        meta, seq_states, s);
         if (e == hipSuccess)
             e = ssd::launch_forward_onepass(x, dt, A, B, C, D, nullptr, o, 1, seqlen, nheads,
-                                            ngroups, dstate, states, onepass_scratch(ws), y,
-                                            nullptr, nullptr, s, meta, seq_states);
+                                            ngroups, dstate, pl, states, y, nullptr, nullptr, s,
+                                            meta, seq_states);
         return status_of(e);
     }
     // the separate stages, each masking by seg (no fused stage 2 + 3 here)

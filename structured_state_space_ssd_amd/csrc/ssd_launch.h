@@ -40,21 +40,31 @@ hipError_t launch_chunk_state(const void *x, const void *B, const float *delta,
                               int batch, int seqlen, int nheads, int ngroups, int dstate, int chunk,
                               bool bf16, float *states, hipStream_t stream, bool dout = false);
 
-// The single-pass bf16 forward (fwd_onepass.hip): whether it applies; into
-// how many segments it cuts each sequence given `scratch_bytes` of float32
-// scratch for the segment states (1: none needed); and the launch (two
-// kernels when there are several segments: the segment states, then the
-// forward proper; `between` (nullable) is recorded between them).
+// The single-pass bf16 forward (fwd_onepass.hip): whether it applies; how
+// it cuts each sequence; and the launch (two kernels when there are several
+// segments: the segment states, then the forward proper; `between`
+// (nullable) is recorded between them).
 bool forward_onepass_ok(int batch, int nheads, int dstate, bool bf16, const void *dt);
-int forward_onepass_segments(int batch, int seqlen, int nheads, int dstate, size_t scratch_bytes);
+// S segments of per_seg 64-token blocks each (the last may hold fewer); when
+// S > 1 the first S - 1 segments are cut into k pieces of psub blocks, whose
+// states (float32 [Bt][H][(S-1)k][P][N]) and log2-decays (float32
+// [Bt][H][(S-1)k]) take scratch_bytes of scratch. S == 1: k == 0, no scratch.
+struct OnepassPlan {
+    int S, k, per_seg, psub;
+    size_t scratch_bytes;
+};
+// cap: the most scratch the plan may take (SIZE_MAX: no limit); a smaller cap
+// lowers k, then gives up the segments.
+OnepassPlan forward_onepass_plan(int batch, int seqlen, int nheads, int dstate, size_t cap);
 // Packed sequences (batch 1, no init_state / final_state): `varlen_meta`
 // holds one int4 per token made by launch_onepass_varlen_prep from cu_seqlens
 // (16 * seqlen bytes, 16-byte aligned); each sequence's final state goes to
 // seq_states (nullable) [nseq][H][P][N]; the prep also zeroes the empty ones.
+// `scratch` must hold pl.scratch_bytes (it may be NULL when that is 0).
 hipError_t launch_forward_onepass(const void *x, const void *dt, const float *A, const void *B,
                                   const void *C, const float *D, const float *init,
                                   const DtOpts &opts, int batch, int seqlen, int nheads,
-                                  int ngroups, int dstate, float *scratch, size_t scratch_bytes,
+                                  int ngroups, int dstate, const OnepassPlan &pl, float *scratch,
                                   void *y, float *final_state, hipEvent_t between,
                                   hipStream_t stream, const void *varlen_meta = nullptr,
                                   float *seq_states = nullptr);

@@ -37,6 +37,34 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
 
 
+def unit_rel_l2(a, b):
+    """Relative L2 of each unit (leading axis) of a against b: an array of
+    ||a_u - b_u|| / ||b_u||, in float64 (a unit whose reference is all zero
+    gives ||a_u||). Each head's semiseparable matrix is an independent unit of
+    the computation, so a wrong unit shows here even when the whole-tensor
+    norm would hide it."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    a = a.reshape(a.shape[0], -1)
+    b = b.reshape(b.shape[0], -1)
+    den = np.linalg.norm(b, axis=1)
+    return np.linalg.norm(a - b, axis=1) / np.where(den > 0, den, 1.0)
+
+
+def check_units(name, a, b, t, labels=None):
+    """Assert every unit's relative L2 below t; print the worst unit. Returns
+    the worst error."""
+    e = unit_rel_l2(a, b)
+    if e.size == 0:
+        return 0.0
+    k = int(np.argmax(e))
+    lab = labels[k] if labels is not None else k
+    print(f"   per-unit {name}: worst {e[k]:.3e} at unit {lab} of {e.size}, median "
+          f"{float(np.median(e)):.3e}", flush=True)
+    assert e[k] < t, (name, lab, float(e[k]))
+    return float(e[k])
+
+
 def units_view(y_bthp, units, H):
     """Gather [U, L, P] from y [Bt, L, H, P] for flat units b*H + h."""
     u = np.asarray(units)

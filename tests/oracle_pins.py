@@ -496,7 +496,45 @@ def pin_backward_finite_differences(lib=None):
             assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), ("bias", fd, an)
 
 
+def pin_backward_zoh_small_decay(lib=None):
+    """P18: the zero-order-hold weight's derivative with respect to A where
+    |dt A| is small (below 1e-3: the backward oracle's series form of
+    (z e^z - expm1(z)) / A^2, whose closed form cancels there), checked like
+    P17 against central differences of the pinned forward oracle. The heads'
+    A are tiny dyadic values, so the weight w = expm1(dt A)/A is close to dt
+    and its A-derivative is about dt^2/2 (1 + 2 z / 3): the step eps in A is
+    small enough that the difference quotient resolves the z-term."""
+    rng = np.random.default_rng(31)
+    Bt, L, H, P, G, N = 1, 23, 3, 4, 1, 6
+    dyad = lambda shape, lo, hi, den: _dyadic(rng, shape, lo, hi, den)
+    args = dict(x=dyad((Bt, L, H, P), -2, 2, 16), B=dyad((Bt, L, G, N), -1, 1, 32),
+                C=dyad((Bt, L, G, N), -1, 1, 32), D=dyad((H,), -1, 1, 16),
+                init=dyad((Bt, H, P, N), -1, 1, 8).astype(np.float64),
+                A=-np.array([2.0 ** -12 * 3, 2.0 ** -11 * 3, 2.0 ** -10 * 3], np.float32),
+                dt=dyad((Bt, L, H), 0.02, 0.3, 4096))
+    z = np.abs(args["dt"].astype(np.float64) * args["A"].astype(np.float64))
+    assert z.max() < 1e-3 and (z > 3e-4).mean() > 0.15  # the series branch, with a z-term that shows
+    dy = rng.standard_normal((Bt, L, H, P)).astype(np.float32)
+    dfinal = rng.standard_normal((Bt, H, P, N))
+    opts = dict(zoh=True)
+    grads = oracle.backward(args["x"], args["dt"], args["A"], args["B"], args["C"], args["D"],
+                            args["init"], dy, dfinal, lib=lib, **opts)
+    for h in range(H):  # one head at a time: each dA[h] is checked on its own
+        eps = 2.0 ** -20
+        plus, minus = dict(args), dict(args)
+        plus["A"] = args["A"].copy()
+        minus["A"] = args["A"].copy()
+        plus["A"][h] += np.float32(eps)
+        minus["A"][h] -= np.float32(eps)
+        assert plus["A"][h] - args["A"][h] == eps and args["A"][h] - minus["A"][h] == eps
+        fd = (_loss(dy=dy, dfinal=dfinal, lib=lib, **plus, **opts) -
+              _loss(dy=dy, dfinal=dfinal, lib=lib, **minus, **opts)) / (2 * eps)
+        an = float(grads["dA"][h])
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (h, fd, an)
+
+
 ALL_PINS = [pin_duality, pin_cumsum, pin_lti_geometric, pin_single_token, pin_no_memory,
             pin_state_carry, pin_forward_vs_step, pin_linearity, pin_groups, pin_golden,
             pin_dt_bias, pin_softplus_and_clamp, pin_zoh_ode, pin_zoh_forms,
-            pin_step_with_options, pin_varlen, pin_backward_finite_differences]
+            pin_step_with_options, pin_varlen, pin_backward_finite_differences,
+            pin_backward_zoh_small_decay]

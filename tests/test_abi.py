@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
                      "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_cb",
                      "ssd_chunk_scan", "ssd_forward_timed", "ssd_chunk_cb_size", "ssd_forward_ex",
                      "ssd_step_ex", "ssd_forward_varlen", "ssd_forward_varlen_workspace_size",
-                     "ssd_backward", "ssd_backward_workspace_size"):
+                     "ssd_backward", "ssd_backward_workspace_size", "ssd_forward_plan",
+                     "ssd_forward_plan_info"):
         assert required in names
 
 
@@ -70,12 +71,93 @@ def _ws_expected(Bt, L, H, P, G, N, Q, dtype):
     return al(cs) + al(cs) + al(st) + al(ci) + cb
 
 
-@pytest.mark.parametrize("dims", [(8, 2048, 80, 64, 1, 64, 256, 1), (1, 65536, 80, 64, 8, 128, 256, 1),
-                                  (1, 1, 1, 64, 1, 16, 64, 0), (3, 77, 5, 64, 5, 32, 128, 0)])
-def test_workspace_size(lib, dims):
+class Plan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("segments", ctypes.c_int), ("pieces", ctypes.c_int),
+                ("block_tokens", ctypes.c_int), ("segment_blocks", ctypes.c_int),
+                ("piece_blocks", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
+
+
+def plan_info(lib, Bt, L, H, P, G, N, Q, dtype, dt=256):
+    p = Plan()
+    rc = ctypes.CDLL(LIB).ssd_forward_plan_info(Bt, L, H, P, G, N, Q, dtype, ctypes.c_void_p(dt),
+                                                ctypes.byref(p))
+    return rc, p
+
+
+def _scratch_expected(Bt, H, N, S, K):
+    """The single-pass path's scratch: one float32 P x N state and one float32
+    log2-decay per piece of the first S-1 segments of every (batch, head)."""
+    pieces = Bt * H * (S - 1) * K
+    return pieces * 64 * N * 4 + pieces * 4
+
+
+@pytest.mark.parametrize("dims", [(3, 77, 5, 64, 5, 32, 128, 0), (1, 1, 1, 64, 1, 16, 64, 0),
+                                  (8, 2048, 68, 64, 4, 64, 256, 1), (2, 300, 4, 64, 2, 128, 64, 1)])
+def test_workspace_size_stage_path(lib, dims):
+    # float32, N 16 / 32, heads not a multiple of 8: the stage kernels and their layout
     assert lib.ssd_forward_workspace_size(*dims) == _ws_expected(*dims)
+    rc, p = plan_info(lib, *dims)
+    assert rc == SSD_OK and p.path == 0 and p.segments == 0 and p.block_tokens == dims[6]
+    assert p.workspace_bytes == _ws_expected(*dims)
     Bt, L, H, P, G, N, Q, dt = dims
     assert lib.ssd_chunk_cb_size(Bt, L, G, Q, dt) == _cb_expected(Bt, L, G, Q, dt)
+
+
+SINGLE_PASS = [(8, 2048, 80, 64, 1, 64, 256, 1), (1, 65536, 80, 64, 8, 128, 256, 1),
+               (4, 4096, 32, 64, 1, 256, 128, 1), (1, 2000, 16, 64, 1, 64, 256, 1),
+               (1, 1000, 16, 64, 2, 64, 256, 1), (1, 37 * 64 + 13, 16, 64, 2, 128, 256, 1),
+               (1, 16384, 16, 64, 2, 256, 128, 1), (1, 100, 8, 64, 1, 64, 64, 1)]
+
+
+@pytest.mark.parametrize("dims", SINGLE_PASS)
+def test_workspace_size_single_pass(lib, dims):
+    """The single-pass path needs exactly the scratch its plan writes: nothing
+    with one segment, one state and decay per piece otherwise (the segment
+    kernels write units * (S-1) * K pieces, so this is the bound every write
+    stays inside)."""
+    Bt, L, H, P, G, N, Q, dt = dims
+    rc, p = plan_info(lib, *dims)
+    assert rc == SSD_OK and p.path == 1 and p.block_tokens == 64
+    blocks = -(-L // 64)
+    assert p.segments >= 1 and p.segment_blocks * (p.segments - 1) < blocks <= p.segment_blocks * p.segments
+    if p.segments == 1:
+        assert p.pieces == 0 and p.workspace_bytes == 0
+    else:
+        assert p.pieces >= 1 and p.piece_blocks * p.pieces == p.segment_blocks
+        assert p.workspace_bytes == _scratch_expected(Bt, H, N, p.segments, p.pieces)
+    assert lib.ssd_forward_workspace_size(*dims) == p.workspace_bytes
+    # an unaligned dt takes the stage kernels, with their layout
+    rc, q = plan_info(lib, *dims, dt=258)
+    assert rc == SSD_OK and q.path == 0 and q.workspace_bytes == _ws_expected(*dims)
+
+
+def test_plan_info_sweep(lib):
+    """Over a sweep of shapes: segments only when the (batch, head) pairs alone
+    leave the GPU part idle, at least 4 blocks per segment, pieces of at least
+    2 blocks, and never more pieces than the segment-state kernel fills the GPU
+    with (so the scratch stays a few tens of MB)."""
+    slots = {64: 3 * 256, 128: 2 * 256, 256: 256}
+    for N in (64, 128, 256):
+        for Bt, H in ((1, 8), (1, 16), (2, 16), (1, 80), (4, 32), (8, 80), (3, 64)):
+            for L in (1, 64, 255, 256, 1000, 4096, 20000, 65536):
+                rc, p = plan_info(lib, Bt, L, H, 64, 1, N, 256, 1)
+                assert rc == SSD_OK and p.path == 1
+                blocks = -(-L // 64)
+                if Bt * H >= slots[N] or blocks < 8:
+                    assert p.segments == 1, (N, Bt, H, L)
+                if p.segments > 1:
+                    assert p.segment_blocks >= 4 and p.piece_blocks >= 2 or p.pieces == 1
+                    assert Bt * H * p.segments <= slots[N] + Bt * H
+                    assert p.workspace_bytes <= 32 << 20, (N, Bt, H, L, p.workspace_bytes)
+                    assert p.workspace_bytes == _scratch_expected(Bt, H, N, p.segments, p.pieces)
+
+
+def test_plan_info_rejects(lib):
+    rc, p = plan_info(lib, 0, 10, 8, 64, 1, 64, 64, 1)
+    assert rc == SSD_ERR_SHAPE and p.workspace_bytes == 0
+    rc, _ = plan_info(lib, 1, 10, 8, 64, 1, 48, 64, 1)
+    assert rc == SSD_ERR_UNSUPPORTED
+    assert ctypes.CDLL(LIB).ssd_forward_plan_info(1, 10, 8, 64, 1, 64, 64, 1, None, None) == SSD_ERR_NULL
 
 
 @pytest.mark.parametrize("dims", [(16384, 80, 64, 1, 64, 256, 1), (700, 4, 64, 2, 64, 64, 0),
@@ -89,6 +171,7 @@ def test_varlen_workspace_size(lib, dims):
 
 def test_workspace_size_invalid(lib):
     assert lib.ssd_forward_workspace_size(0, 10, 1, 64, 1, 16, 64, 1) == 0
+    assert lib.ssd_forward_workspace_size(1, 10, 1, 64, 1, 48, 64, 1) == 0
     assert lib.ssd_forward_workspace_size(1, 10, 1, 64, 1, 16, 0, 1) == 0
     assert lib.ssd_forward_workspace_size(1, 10, 1, 64, 1, 16, 64, 5) == 0
     assert lib.ssd_chunk_cb_size(1, 10, 1, 96, 1) == 0

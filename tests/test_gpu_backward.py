@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import ssd_workloads as W
-from gpu_util import down, print_case, rel_l2, tol, up
+from gpu_util import check_units, down, print_case, rel_l2, tol, up
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -56,10 +56,24 @@ def check_backward(w, with_dfinal=True, batches=None, **option_kw):
                           sel(d["C"].val), d["D"], sel(d["init"]), sel(gr["dy"].val), sel(dfinal),
                           **opts)
     errs = {}
+    t = tol(w.dtype)
+    H, G = w.nheads, w.ngroups
     for k in ("dx", "ddt", "dB", "dC"):
-        errs[k] = rel_l2(down(g[k])[rows], ref[k])
+        gk = down(g[k])[rows]
+        errs[k] = rel_l2(gk, ref[k])
+        # every (batch, head) unit (dB, dC: every (batch, group)) on its own:
+        # [Bt, L, U, ...] -> [Bt * U, L, ...]
+        nu = G if k in ("dB", "dC") else H
+        per = lambda a: np.moveaxis(np.asarray(a).reshape(len(rows), w.seqlen, nu, -1), 2, 1)
+        lab = [f"(b {rows[i // nu]}, {'g' if nu == G else 'h'} {i % nu})"
+               for i in range(len(rows) * nu)]
+        check_units(k, per(gk).reshape(len(rows) * nu, -1), per(ref[k]).reshape(len(rows) * nu, -1),
+                    t, lab)
     if d["init"] is not None or with_dfinal:
-        errs["dinit"] = rel_l2(down(g["dinit"])[rows], ref["dinit"])
+        gi = down(g["dinit"])[rows]
+        errs["dinit"] = rel_l2(gi, ref["dinit"])
+        check_units("dinit", gi.reshape(len(rows) * H, -1), np.asarray(ref["dinit"]).reshape(
+            len(rows) * H, -1), t)
     if batches is None:
         for k in ("dA", "dD"):
             errs[k] = rel_l2(down(g[k]), ref[k])
@@ -67,7 +81,7 @@ def check_backward(w, with_dfinal=True, batches=None, **option_kw):
             errs["ddt_bias"] = rel_l2(down(g["ddt_bias"]), ref["dbias"])
     print_case(f"   errors { {k: f'{v:.2e}' for k, v in errs.items()} }")
     for k, e in errs.items():
-        assert e < tol(w.dtype), (w.name, k, e)
+        assert e < t, (w.name, k, e)
 
 
 SWEEP = [("f32", n) for n in (16, 32, 64)] + [("bf16", n) for n in (16, 32, 64, 128, 256)]
@@ -124,11 +138,11 @@ def test_backward_strong_decay():
     check_backward(w)
 
 
-def test_backward_mamba2_2p7b_one_row():
-    """The 2.7B layer's shape; the oracle checks batch row 3 (dx, ddt, dB, dC,
-    dinit of all 80 heads)."""
+def test_backward_mamba2_2p7b_full():
+    """The 2.7B layer's shape, every batch row and head (dx, ddt, dB, dC,
+    dinit, dA, dD)."""
     w = W.WORKLOADS["mamba2_2.7b"]
-    check_backward(w, with_dfinal=True, batches=[3])
+    check_backward(w, with_dfinal=True)
 
 
 def test_backward_errors():

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import ssd_workloads as W
-from gpu_util import down, print_case, rel_l2, tol, units_view, up
+from gpu_util import check_units, down, print_case, rel_l2, tol, units_view, up
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -70,16 +70,21 @@ def check_forward(w, units=None, init=None, both_D=True, **option_kw):
     xv = units_view(d["x"].val, uu, H).astype(np.float64)
     Dv = d["D"].astype(np.float64)[uu % H][:, None, None]
     errs = {}
+    t = tol(w.dtype)
+    labels = [f"(b {u // H}, h {u % H})" for u in uu]
     for with_D in ([True, False] if both_D else [True]):
         y, fs = run_forward(w, d, d["D"] if with_D else None, init, opts)
         yg = units_view(down(y), uu, H)
         yref = y0 + Dv * xv if with_D else y0
-        errs[f"y{'_D' if with_D else '_noD'}"] = rel_l2(yg, yref)
+        tag = f"y{'_D' if with_D else '_noD'}"
+        errs[tag] = rel_l2(yg, yref)
+        # every (batch, head) unit on its own, too
+        errs[tag + "_worst_unit"] = check_units(tag, yg, yref, t, labels)
         fsg = down(fs).reshape(-1, w.headdim, w.dstate)[uu]
         errs["state"] = rel_l2(fsg, s0)
-        del y, fs
+        errs["state_worst_unit"] = check_units("state", fsg, s0, t, labels)
+        del y, fs, yg
     print_case(f"   errors {errs}")
-    t = tol(w.dtype)
     for k, e in errs.items():
         assert e < t, (w.name, k, e)
     return errs
@@ -99,18 +104,18 @@ def test_large_state_full():
     check_forward(W.WORKLOADS["large_state"])
 
 
-def test_long_seq_sampled():
-    w = W.WORKLOADS["long_seq"]
-    # heads from every other group, first / last head of a group
-    check_forward(w, units=[0, 9, 10, 37, 44, 79])
+def test_long_seq_full():
+    # every one of the 80 heads (8 groups), y with and without D, the final state
+    check_forward(W.WORKLOADS["long_seq"])
 
 
 def test_decode_64_steps():
-    _decode(W.WORKLOADS["decode"], zero_init=False)
+    # every one of the 256 x 80 (batch, head) units
+    _decode(W.WORKLOADS["decode"], zero_init=False, nunits=None)
 
 
 def test_decode_64_steps_zero_init():
-    _decode(W.WORKLOADS["decode"], zero_init=True)
+    _decode(W.WORKLOADS["decode"], zero_init=True, nunits=None)
 
 
 def _decode(w, zero_init, nunits=512, **option_kw):
@@ -124,7 +129,8 @@ def _decode(w, zero_init, nunits=512, **option_kw):
         gopts["dt_bias"] = up(gopts["dt_bias"])
     H, P, N = w.nheads, w.headdim, w.dstate
     rng = np.random.default_rng(123)
-    units = np.sort(rng.choice(w.batch * H, size=nunits, replace=False))
+    units = (np.arange(w.batch * H) if nunits is None else
+             np.sort(rng.choice(w.batch * H, size=nunits, replace=False)))
     init = np.zeros_like(d["init"]) if zero_init else d["init"]
     state = up(init)
     st_o = np.ascontiguousarray(init.reshape(-1, P, N)[units].astype(np.float64))
@@ -137,9 +143,14 @@ def _decode(w, zero_init, nunits=512, **option_kw):
         yos.append(oracle.step(st_o, d["x"].val[t], d["dt"].val[t], d["A"], d["B"].val[t],
                                d["C"].val[t], d["D"], units=units, **opts))
     torch.cuda.synchronize()
-    ey = rel_l2(np.stack(ys), np.stack(yos))
-    es = rel_l2(down(state).reshape(-1, P, N)[units], st_o)
+    yg, yr = np.stack(ys, axis=1), np.stack(yos, axis=1)  # [U, steps, P]
+    ey = rel_l2(yg, yr)
+    sg = down(state).reshape(-1, P, N)[units]
+    es = rel_l2(sg, st_o)
     print_case(f"   rel_l2 y={ey:.3e} state={es:.3e}")
+    labels = [f"(b {u // w.nheads}, h {u % w.nheads})" for u in units]
+    check_units("y", yg, yr, tol(w.dtype), labels)
+    check_units("state", sg, st_o, 1e-3, labels)
     assert ey < tol(w.dtype) and es < 1e-3
 
 
@@ -386,10 +397,9 @@ def test_options_strong_decay_zoh():
                           dt_lo=0.5, dt_hi=2.0), zoh=True)
 
 
-def test_mamba2_2p7b_all_options_sampled():
-    w = W.WORKLOADS["mamba2_2.7b"]
-    check_forward(w, units=[0, 79, 80 * 3 + 41, 80 * 7 + 5, 80 * 8 - 1], both_D=False,
-                  **OPTION_SETS["all_zoh"])
+def test_mamba2_2p7b_all_options():
+    # every (batch, head) unit of the 2.7B shape with every option on
+    check_forward(W.WORKLOADS["mamba2_2.7b"], both_D=False, **OPTION_SETS["all_zoh"])
 
 
 @pytest.mark.parametrize("name", ["zoh", "all_zoh"])
@@ -412,3 +422,55 @@ def test_segments_many_n256_sampled():
     print_case(f"   segments {S}")
     assert S >= 8
     check_forward(w, units=[0, 7, 8, 15], both_D=False)
+
+
+# ------------------------------------------------- workspace bounds of the segmented path
+#
+# The segment-state kernel writes one float32 state and decay per piece of
+# every (batch, head); the plan sizes the workspace to exactly that. Canary
+# bytes after an exact-size workspace must come back untouched (they did not
+# before the piece count was taken per (batch, head) times their number).
+
+@pytest.mark.parametrize("L,H,G,N", [(2000, 16, 1, 64), (1000, 16, 2, 64), (1000, 16, 2, 128),
+                                     (37 * 64 + 13, 16, 2, 256), (700, 8, 2, 128)])
+def test_segments_workspace_canary(L, H, G, N):
+    ssd = _ssd()
+    w = W.small(f"canary_L{L}_N{N}", 1, L, H, 64, G, N, 256, "bf16", seed=990 + N, init_std=0.2)
+    d = W.generate(w)
+    g = {k: up(d[k]) for k in ("x", "dt", "A", "B", "C", "D", "init")}
+    p = ssd.plan_info(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk,
+                      torch.bfloat16, g["dt"])
+    print_case(f"   plan {p}")
+    assert p["segments"] > 1 and p["workspace_bytes"] > 0
+    need, pad = p["workspace_bytes"], 1 << 20
+    ws = torch.full((need + pad,), 0xA5, dtype=torch.uint8, device="cuda")
+    y, fs = ssd.forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], chunk=w.chunk,
+                        init_state=g["init"], return_final_state=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert bool((ws[need:] == 0xA5).all()), "the forward wrote past its workspace"
+    y0, s0, _ = oracle.forward(d["x"].val, d["dt"].val, d["A"], d["B"].val, d["C"].val, d["D"],
+                               d["init"])
+    e = rel_l2(units_view(down(y), np.arange(H), H), y0)
+    print_case(f"   rel_l2(y) = {e:.3e}")
+    assert e < tol(w.dtype)
+
+
+def test_varlen_workspace_canary():
+    ssd = _ssd()
+    w = W.small("canary_varlen", 1, 3000, 16, 64, 2, 128, 256, "bf16", seed=995)
+    cu = W.packed_cu_seqlens(w.seqlen, 700, seed=996)
+    d = W.generate(w)
+    g = {k: up(d[k]) for k in ("x", "dt", "A", "B", "C", "D")}
+    need = int(ssd._native.lib.ssd_forward_varlen_workspace_size(
+        w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk, 1))
+    ws = torch.full((need + (1 << 20),), 0x5A, dtype=torch.uint8, device="cuda")
+    y, ss = ssd.forward_varlen(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"],
+                               torch.from_numpy(cu).cuda(), chunk=w.chunk, return_seq_states=True,
+                               workspace=ws)
+    torch.cuda.synchronize()
+    assert bool((ws[need:] == 0x5A).all()), "the packed forward wrote past its workspace"
+    y0, st0 = oracle.forward_varlen(d["x"].val, d["dt"].val, d["A"], d["B"].val, d["C"].val,
+                                    d["D"], cu)
+    e = rel_l2(down(y)[0].transpose(1, 0, 2), y0)
+    print_case(f"   rel_l2(y) = {e:.3e}")
+    assert e < tol(w.dtype)

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import ssd_workloads as W
-from gpu_util import down, print_case, rel_l2, tol, up
+from gpu_util import check_units, down, print_case, rel_l2, tol, up
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -57,9 +57,25 @@ def check_varlen(w, cu, units=None, **option_kw):
         yg = down(y)[0].transpose(1, 0, 2)[uu]  # [U, L, P]
         yref = y0 + (d["D"].astype(np.float64)[uu][:, None, None] *
                      d["x"].val[0].transpose(1, 0, 2)[uu]) if with_D else y0
-        errs["y_D" if with_D else "y_noD"] = rel_l2(yg, yref)
+        tag = "y_D" if with_D else "y_noD"
+        errs[tag] = rel_l2(yg, yref)
+        # every (sequence, head) unit on its own: [U, L, P] -> one row per pair
+        pg, pr, lab = [], [], []
+        for k in range(cu.size - 1):
+            if cu[k + 1] > cu[k]:
+                pg += list(yg[:, cu[k]:cu[k + 1]])
+                pr += list(yref[:, cu[k]:cu[k + 1]])
+                lab += [f"(seq {k}, h {u})" for u in uu]
+        e = [rel_l2(a, b) for a, b in zip(pg, pr)]
+        worst = int(np.argmax(e))
+        print_case(f"   per-unit {tag}: worst {e[worst]:.3e} at {lab[worst]} of {len(e)}")
+        assert e[worst] < tol(w.dtype), (tag, lab[worst], e[worst])
         sg = down(ss).transpose(1, 0, 2, 3)[uu]  # [U, nseq, P, N]
         errs["states"] = rel_l2(sg, st0)
+        nonempty = np.flatnonzero(np.diff(cu) > 0)
+        check_units("states", sg[:, nonempty].reshape(-1, w.headdim * w.dstate),
+                    np.asarray(st0)[:, nonempty].reshape(-1, w.headdim * w.dstate), tol(w.dtype),
+                    [f"(h {u}, seq {k})" for u in uu for k in nonempty])
         # empty sequences have exactly zero states
         empty = np.flatnonzero(np.diff(cu) == 0)
         assert np.all(sg[:, empty] == 0)

@@ -59,6 +59,10 @@ MUTATIONS = {
     "bwd_clamp_slope_inverted": ("if (o->dt_clamp && (v < o->dt_min || v > o->dt_max)) slope = 0.0;",
                                  "if (o->dt_clamp && (v >= o->dt_min && v <= o->dt_max)) slope = 0.0;"),
     "bwd_zoh_slope": ("*wd = exp(z);", "*wd = 1.0;"),
+    "bwd_zoh_small_z_slope_zero": ("if (fabs(z) < 1e-3) *wA = d * d * (0.5 + z / 3.0 + z * z / 8.0);",
+                                   "if (fabs(z) < 1e-3) *wA = 0.0;"),
+    "bwd_zoh_small_z_linear_term": ("0.5 + z / 3.0", "0.5 + z / 6.0"),
+    "bwd_zoh_small_z_leading_term": ("0.5 + z / 3.0", "0.25 + z / 3.0"),
     "bwd_dD_without_x": ("dD += (double)dyt[p] * (double)xt[p];", "dD += (double)dyt[p];"),
     "previous_token_dt_for_decay": ("const double a = exp(d * A);", "const double a = exp((t ? (double)j->dt[(tok - 1) * H + h] : d) * A);"),
 }
