@@ -160,6 +160,26 @@ __device__ __forceinline__ void pack8(Frag<bf16_t> &f, const float (&v)[8]) {
     }
 }
 
+// Four floats -> one bf16 operand of the 16x16x16 product (the k = 16 half of
+// a 32-wide slice; lane 16g + r holds k = 4g .. 4g + 3 of row r).
+__device__ __forceinline__ bf16x4 pack4(const float (&v)[4]) {
+    const bf16x2 a = __builtin_convertvector(floatx2{v[0], v[1]}, bf16x2);
+    const bf16x2 b = __builtin_convertvector(floatx2{v[2], v[3]}, bf16x2);
+    return bf16x4{a[0], a[1], b[0], b[1]};
+}
+
+__device__ __forceinline__ void mma16(floatx4 &acc, const bf16x4 &a, const bf16x4 &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, a),
+                                                    __builtin_bit_cast(shortx4, b), acc, 0, 0, 0);
+}
+
+// Half of x_colfrag<JP>'s fragment: rows 32 jp + 16 hf + 4 g + 0..3 of
+// head-dim column 16 pt + c for lane 16 g + c (one transposing read).
+__device__ __forceinline__ bf16x4 x_colfrag_half(const __bf16 *xs, int off) {
+    return __builtin_bit_cast(bf16x4,
+                              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4 *)(xs + off)));
+}
+
 }  // namespace
 
 // How a launch cuts each sequence. The single-pass kernel runs nseg segments
@@ -215,7 +235,6 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
     // (its half of the state, of the C H and C B^T sums and of the update)
     constexpr bool HALVES = N == 256;
     constexpr int NWV = HALVES ? 8 : 4;        // wavefronts
-    constexpr int NKH = HALVES ? NK / 2 : NK;  // k-steps over N per wavefront
     constexpr int NTH = HALVES ? NT / 2 : NT;  // state tiles per wavefront
     constexpr int BL = T * PPR / 256;  // B (and C) loads per lane per block
     static_assert(N % 32 == 0 && BL >= 1, "state size");
@@ -348,6 +367,7 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
     // + e - 4, which is i for element cc - 4 g4 (w even) or 4 + cc - 4 g4
     // (w odd) when 0 <= cc - 4 g4 < 4.
     Frag<bf16_t> dfr[2];  // hi, lo
+    bf16x4 dfr4[2];       // N 256: the same for the k = 16 half holding the diagonal
     {
         const __bf16 dhi = static_cast<__bf16>(Dh);
         const __bf16 dlo = static_cast<__bf16>(Dh - static_cast<float>(dhi));
@@ -357,6 +377,12 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
             const bool on = e == ((wr & 1) ? 4 + e0 : e0) && e0 >= 0 && e0 < 4;
             dfr[0].v[e] = on ? dhi : static_cast<__bf16>(0.0f);
             dfr[1].v[e] = on ? dlo : static_cast<__bf16>(0.0f);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool on = e == e0;
+            dfr4[0][e] = on ? dhi : static_cast<__bf16>(0.0f);
+            dfr4[1][e] = on ? dlo : static_cast<__bf16>(0.0f);
         }
     }
 
@@ -409,23 +435,25 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
             dec = __builtin_amdgcn_exp2f(tsl[T - 1]);
         }
 
-        // C_i (n = 32 kk + 8 g4 .. +7), the B operand of both C H and C B^T
-        Frag<bf16_t> cfr[NKH];  // k-steps nh * NKH + 0 .. NKH-1
+        // C_i (n = 32 kk + 8 g4 .. +7) over the whole of N, the B operand of
+        // both C H and C B^T
+        Frag<bf16_t> cfr[NK];
 #pragma unroll
-        for (int kq = 0; kq < NKH; ++kq)
-            lds_frag8(cfr[kq],
-                      sm.cs + i * N + (((4 * (nh * NKH + kq) + g4) ^ tr_swz<PPR>(i)) << 3));
+        for (int kq = 0; kq < NK; ++kq)
+            lds_frag8(cfr[kq], sm.cs + i * N + (((4 * kq + g4) ^ tr_swz<PPR>(i)) << 3));
 
         // ---- state to output: Y^T[p][i] = exp(s_i) sum_n H[p][n] C_i[n], every p tile
+        // (N 256: the wavefront of half nh takes p tiles 2 nh, 2 nh + 1)
         floatx4 acc[4];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
             const int pp = 16 * pt + cc;
             acc[pt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (HALVES && (pt >> 1) != nh) continue;  // uniform
 #pragma unroll
-            for (int kq = 0; kq < NKH; ++kq) {
+            for (int kq = 0; kq < NK; ++kq) {
                 Frag<bf16_t> hf;
-                lds_frag8(hf, sm.hb + pp * N + (((4 * (nh * NKH + kq) + g4) ^ (pp & HSW)) << 3));
+                lds_frag8(hf, sm.hb + pp * N + (((4 * kq + g4) ^ (pp & HSW)) << 3));
                 mma(acc[pt], hf, cfr[kq]);
             }
         }
@@ -452,10 +480,58 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
         // registers as the B operand of the diagonal products over every p tile:
         // M[i][j] = (C_i . B_j) exp(s_i - s_j) w_j, j <= i
         for (int js = 0; js <= (wr >> 1); ++js) {  // wave-uniform trip count
+            const int j0 = 32 * js + 4 * g4;
+            const bool diag = js == (wr >> 1);
+            if constexpr (HALVES) {
+                // N 256: the wavefront of half nh takes the 16 columns j =
+                // 32 js + 16 nh + 0..15 of the slice, each C_i . B_j summed over
+                // the whole of N in float32 (rounded to bf16 once, after the
+                // decay), and their part of Y^T += X^T M^T as k = 16 products
+                floatx4 m = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+                const int jn = 32 * js + 16 * nh + cc;
+#pragma unroll
+                for (int kq = 0; kq < NK; ++kq) {
+                    Frag<bf16_t> bf;
+                    lds_frag8(bf, sm.bb + jn * N + (((4 * kq + g4) ^ tr_swz<PPR>(jn)) << 3));
+                    mma(m, bf, cfr[kq]);
+                }
+                // lane (g4, cc): rows j = jh + r of column i
+                const int jh = j0 + 16 * nh;
+                float v[4];
+                if (diag) {
+                    const floatx4 s0 = *reinterpret_cast<const floatx4 *>(tsl + jh);
+                    const floatx4 w0 = *reinterpret_cast<const floatx4 *>(twt + jh);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float a0 = m[r] * (__builtin_amdgcn_exp2f(si - s0[r]) * w0[r]);
+                        v[r] = jh + r <= i && (!VL || jh + r >= fsi) ? a0 : 0.0f;
+                    }
+                } else {
+                    const float rowf = __builtin_amdgcn_exp2f(si - s31);
+                    const floatx4 c0 = *reinterpret_cast<const floatx4 *>(tcf + jh);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        v[r] = m[r] * (c0[r] * rowf);
+                        if constexpr (VL) v[r] = jh + r >= fsi ? v[r] : 0.0f;
+                    }
+                }
+                const bf16x4 mf = pack4(v);
+                const __bf16 *xsl = xs + js * 2048 + nh * 1024;
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const bf16x4 xf = x_colfrag_half(xsl, xo[pt]);
+                    mma16(acc[pt], xf, mf);
+                    if (diag && D && nh == (wr & 1)) {  // uniform: the half holding i
+                        mma16(acc[pt], xf, dfr4[0]);
+                        mma16(acc[pt], xf, dfr4[1]);
+                    }
+                }
+                continue;
+            }
             floatx4 m[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-            for (int kq = 0; kq < NKH; ++kq) {
-                const int q = 4 * (nh * NKH + kq) + g4;
+            for (int kq = 0; kq < NK; ++kq) {
+                const int q = 4 * kq + g4;
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     const int j = 32 * js + 16 * half + cc;
@@ -465,8 +541,6 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
                 }
             }
             // lane (g4, cc): rows j = 32 js + 16 half + 4 g4 + r of column i
-            const int j0 = 32 * js + 4 * g4;
-            const bool diag = js == (wr >> 1);
             float v[8];
             if (diag) {
                 // holds the diagonal: exp per element, causal mask
@@ -506,7 +580,7 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
                 Frag<bf16_t> xf;
                 x_colfrag<0>(xf, xsl, xo[pt]);
                 mma(acc[pt], xf, mf);
-                if (diag && D && nh == 0) {  // uniform
+                if (diag && D) {  // uniform
                     mma(acc[pt], xf, dfr[0]);
                     mma(acc[pt], xf, dfr[1]);
                 }

@@ -37,24 +37,33 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
 
 
-def unit_rel_l2(a, b):
+def unit_rel_l2(a, b, part=None):
     """Relative L2 of each unit (leading axis) of a against b: an array of
     ||a_u - b_u|| / ||b_u||, in float64 (a unit whose reference is all zero
     gives ||a_u||). Each head's semiseparable matrix is an independent unit of
     the computation, so a wrong unit shows here even when the whole-tensor
-    norm would hide it."""
+    norm would hide it.
+
+    ``part`` (optional, same shape as b): one of two terms that b is the sum
+    of (y = state-space part + D x); the denominator is then the larger of
+    ||b_u|| and ||part_u||. A unit whose two terms nearly cancel (a head with
+    D close to minus the state-space gain, over a one-token sequence) has a
+    tiny ||b_u||, and the rounding of each term, which both sides take in
+    their own precision, is measured against the terms' own size."""
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     a = a.reshape(a.shape[0], -1)
     b = b.reshape(b.shape[0], -1)
     den = np.linalg.norm(b, axis=1)
+    if part is not None:
+        den = np.maximum(den, np.linalg.norm(np.asarray(part, np.float64).reshape(b.shape), axis=1))
     return np.linalg.norm(a - b, axis=1) / np.where(den > 0, den, 1.0)
 
 
-def check_units(name, a, b, t, labels=None):
-    """Assert every unit's relative L2 below t; print the worst unit. Returns
-    the worst error."""
-    e = unit_rel_l2(a, b)
+def check_units(name, a, b, t, labels=None, part=None):
+    """Assert every unit's relative L2 (unit_rel_l2) below t; print the worst
+    unit. Returns the worst error."""
+    e = unit_rel_l2(a, b, part)
     if e.size == 0:
         return 0.0
     k = int(np.argmax(e))

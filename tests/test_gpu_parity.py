@@ -79,7 +79,7 @@ def check_forward(w, units=None, init=None, both_D=True, **option_kw):
         tag = f"y{'_D' if with_D else '_noD'}"
         errs[tag] = rel_l2(yg, yref)
         # every (batch, head) unit on its own, too
-        errs[tag + "_worst_unit"] = check_units(tag, yg, yref, t, labels)
+        errs[tag + "_worst_unit"] = check_units(tag, yg, yref, t, labels, part=y0)
         fsg = down(fs).reshape(-1, w.headdim, w.dstate)[uu]
         errs["state"] = rel_l2(fsg, s0)
         errs["state_worst_unit"] = check_units("state", fsg, s0, t, labels)

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import ssd_workloads as W
-from gpu_util import check_units, down, print_case, rel_l2, tol, up
+from gpu_util import check_units, down, print_case, rel_l2, tol, unit_rel_l2, up
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -60,13 +60,16 @@ def check_varlen(w, cu, units=None, **option_kw):
         tag = "y_D" if with_D else "y_noD"
         errs[tag] = rel_l2(yg, yref)
         # every (sequence, head) unit on its own: [U, L, P] -> one row per pair
-        pg, pr, lab = [], [], []
+        # (y = the state-space part y0 + D x: measured against the larger of
+        # the two, see gpu_util.unit_rel_l2)
+        pg, pr, p0, lab = [], [], [], []
         for k in range(cu.size - 1):
             if cu[k + 1] > cu[k]:
                 pg += list(yg[:, cu[k]:cu[k + 1]])
                 pr += list(yref[:, cu[k]:cu[k + 1]])
+                p0 += list(y0[:, cu[k]:cu[k + 1]])
                 lab += [f"(seq {k}, h {u})" for u in uu]
-        e = [rel_l2(a, b) for a, b in zip(pg, pr)]
+        e = [float(unit_rel_l2(a[None], b[None], c[None])[0]) for a, b, c in zip(pg, pr, p0)]
         worst = int(np.argmax(e))
         print_case(f"   per-unit {tag}: worst {e[worst]:.3e} at {lab[worst]} of {len(e)}")
         assert e[worst] < tol(w.dtype), (tag, lab[worst], e[worst])
