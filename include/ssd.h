@@ -64,7 +64,8 @@ typedef enum {
     SSD_ERR_UNSUPPORTED = -3, /* outside the supported set above                   */
     SSD_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required        */
     SSD_ERR_HIP = -5,         /* the HIP runtime reported an error at launch       */
-    SSD_ERR_OPTION = -6       /* an ssd_options field holds an invalid value       */
+    SSD_ERR_OPTION = -6,      /* an ssd_options field holds an invalid value       */
+    SSD_ERR_TOO_LARGE = -7    /* ssd_forward_static: needs more than its fixed scratch */
 } ssd_status;
 
 /* Discretisation of the input term. */
@@ -192,6 +193,29 @@ int ssd_forward(const void *x, const void *dt, const float *A, const void *B,
                 int headdim, int ngroups, int dstate, int chunk, int dtype,
                 const float *init_state, void *y, float *final_state,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ssd_forward_ex for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument and no events. Its scratch is one device array of
+ * SSD_STATIC_SCRATCH_BYTES (32 MiB) that the library holds on every GPU it
+ * runs on until the process ends; this call allocates nothing. It uses the
+ * array of the current device (hipGetDevice); `stream` must belong to it.
+ * The plan is ssd_forward_ex's with the segment scratch capped at the
+ * array's size; arguments whose forward needs more (ssd_plan.workspace_bytes,
+ * e.g. a large shape on the stage kernels) return SSD_ERR_TOO_LARGE and
+ * enqueue nothing. Every call on one GPU shares that GPU's array, which keeps
+ * the last call's contents (nothing in it must start at zero: each kernel
+ * writes what a later one reads): calls that overlap on one GPU (on
+ * different streams or from different host threads) race and give wrong
+ * results.
+ */
+#define SSD_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+int ssd_forward_static(const void *x, const void *dt, const float *A, const void *B,
+                       const void *C, const float *D, int batch, int seqlen, int nheads,
+                       int headdim, int ngroups, int dstate, int chunk, int dtype,
+                       const float *init_state, void *y, float *final_state,
+                       const ssd_options *opts, void *stream);
 
 /*
  * Which path ssd_forward takes for these sizes and this dt pointer (only its

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "ssd.h"
 #include "ssd_launch.h"
@@ -166,6 +167,9 @@ const char *ssd_strerror(int status) {
         case SSD_ERR_OPTION:
             return "invalid ssd_options (discretization not SSD_DISC_EULER/SSD_DISC_ZOH, or "
                    "dt_clamp with dt_min > dt_max or a NaN bound)";
+        case SSD_ERR_TOO_LARGE:
+            return "the forward needs more scratch than ssd_forward_static's fixed device array "
+                   "holds (SSD_STATIC_SCRATCH_BYTES); use ssd_forward with a workspace";
         default: return "unknown status";
     }
 }
@@ -310,11 +314,17 @@ int ssd_chunk_scan(const void *x, const float *delta, const float *dA_cumsum, co
 namespace {
 
 // ssd_forward_ex with the plan's scratch capped at `cap` bytes.
+hipError_t static_scratch(void **out);
+
+// ssd_forward_ex with the plan's scratch capped at `cap` bytes; with
+// `fixed_scratch` the workspace is the current device's fixed scratch array
+// (ssd_forward_static), and `workspace` / `workspace_bytes` are not read.
 int forward_impl(const void *x, const void *dt, const float *A, const void *B, const void *C,
                  const float *D, int batch, int seqlen, int nheads, int headdim, int ngroups,
                  int dstate, int chunk, int dtype, const float *init_state, void *y,
                  float *final_state, void *workspace, size_t workspace_bytes,
-                 const ssd_options *opts, void *stream, void *const *events, size_t cap) {
+                 const ssd_options *opts, void *stream, void *const *events, size_t cap,
+                 bool fixed_scratch = false) {
     if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
     int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
     if (rc != SSD_OK) return rc;
@@ -328,6 +338,15 @@ int forward_impl(const void *x, const void *dt, const float *A, const void *B, c
     const bool bf16 = dtype == SSD_BF16;
     const FwdPlan f =
         plan_forward(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, bf16, dt, cap);
+    if (fixed_scratch) {
+        if (f.need > cap) return SSD_ERR_TOO_LARGE;
+        workspace = nullptr;
+        if (f.need > 0) {
+            const hipError_t e = static_scratch(&workspace);
+            if (e != hipSuccess) return SSD_ERR_HIP;
+        }
+        workspace_bytes = cap;
+    }
     if (f.need > cap) return SSD_ERR_WORKSPACE;
     if (f.need > 0 && (!workspace || workspace_bytes < f.need)) return SSD_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return SSD_ERR_WORKSPACE;
@@ -389,9 +408,48 @@ int forward_impl(const void *x, const void *dt, const float *A, const void *B, c
     return status_of(e);
 }
 
+// ---- the fixed scratch of ssd_forward_static
+//
+// One array per GPU the library runs on, held until the process ends. Host
+// code never uses the array's name as an address (on the host it names a
+// stand-in, not device memory): the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address reaches the kernels.
+static __device__ __align__(256) unsigned char scratch[SSD_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];  // device address of `scratch`, per device
+
+hipError_t static_scratch(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
+
+int ssd_forward_static(const void *x, const void *dt, const float *A, const void *B,
+                       const void *C, const float *D, int batch, int seqlen, int nheads,
+                       int headdim, int ngroups, int dstate, int chunk, int dtype,
+                       const float *init_state, void *y, float *final_state,
+                       const ssd_options *opts, void *stream) {
+    return forward_impl(x, dt, A, B, C, D, batch, seqlen, nheads, headdim, ngroups, dstate, chunk,
+                        dtype, init_state, y, final_state, nullptr, 0, opts, stream, nullptr,
+                        SSD_STATIC_SCRATCH_BYTES, /*fixed_scratch=*/true);
+}
 
 int ssd_forward_ex(const void *x, const void *dt, const float *A, const void *B, const void *C,
                    const float *D, int batch, int seqlen, int nheads, int headdim, int ngroups,

@@ -381,3 +381,32 @@ def test_forward_plan(lib):
     for L in (256, 1000, 4096, 65536):
         s = [plan(1, L, H, 1, 64, 256) for H in (512, 64, 16, 8)]
         assert s == sorted(s) and s[-1] <= max(1, -(-L // 64) // 4), (L, s)
+
+
+SSD_ERR_TOO_LARGE = -7
+
+
+def _static(lib, **kw):
+    a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, batch=1, seqlen=128, nheads=4,
+             headdim=64, ngroups=1, dstate=64, chunk=64, dtype=1, init=None, y=FAKE, fs=None,
+             opts=None, stream=None)
+    a.update(kw)
+    return lib.ssd_forward_static(*(a[k] for k in ("x", "dt", "A", "B", "C", "D", "batch", "seqlen",
+                                                   "nheads", "headdim", "ngroups", "dstate", "chunk",
+                                                   "dtype", "init", "y", "fs", "opts", "stream")))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), SSD_ERR_NULL),
+    (dict(batch=0), SSD_ERR_SHAPE),
+    (dict(dstate=48), SSD_ERR_UNSUPPORTED),
+    (dict(opts=_opts(discretization=4)), SSD_ERR_OPTION),
+    # the stage kernels' workspace for 8 x 2048 tokens x 80 heads in float32 is far
+    # beyond the fixed 32 MiB array: refused before anything touches the GPU
+    (dict(batch=8, seqlen=2048, nheads=80, dtype=0), SSD_ERR_TOO_LARGE),
+    (dict(batch=1, seqlen=65536, nheads=80, ngroups=8, dstate=128, dt=ctypes.c_void_p(0x100002)),
+     SSD_ERR_TOO_LARGE),
+])
+def test_forward_static_rejects(lib, kw, code):
+    assert _static(lib, **kw) == code
+    assert lib.ssd_strerror(SSD_ERR_TOO_LARGE) != b"unknown status"
