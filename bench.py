@@ -1,23 +1,35 @@
 """SSD layer benchmark on one MI355X.
 
 One step = one full SSD forward over the Mamba-2 2.7B-shaped layer: batch 8,
-L 2048, 80 heads x P 64, N 64, one B/C group, chunk 256, bf16 inputs, fp32
-accumulation, inputs already resident in HBM. Prints ONE JSON line. For this
-shape the library runs the whole forward as its single-pass kernel
-(forward_onepass); with few (batch, head) pairs it adds a segment-state
-kernel first (segment_states); shapes outside the single-pass kernel run
-the stages chunk_cumsum, chunk_state, state_passing, chunk_cb, chunk_scan.
-The library's own ssd_forward_plan says which.
+L 2048, 80 heads x P 64, N 64, one B/C group, chunk argument 256, bf16
+inputs, fp32 accumulation, inputs resident in HBM. Prints ONE JSON line.
 
-Per-kernel GPU times come from HIP events the library records between its
-launches (ssd_forward_timed) on the launch stream, inside the timed region.
-Roofline figures use algorithmic bytes / flops (what the method must read,
-write and compute), not executed ones. The decode step (256 x 80 heads,
-P 64, N 128, fp32 state, 64 consecutive tokens) is reported alongside.
-The CPU baseline is the fp64 oracle (test infrastructure) on the same
-workload, timed on this host.
+The timed region is cold: before each step, outside its events, a 1 GiB
+buffer is read, so neither L2 nor the 256 MB Infinity Cache holds any input;
+HIP events around each forward (and between its kernels) on the launch
+stream give its time, and ``value`` is tokens over the mean. The warm figure
+(back-to-back forwards, inputs partly from the Infinity Cache) is reported
+beside it as ``forward_warm``.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--all] [--no-cpu]
+For this shape the library runs the whole forward as its single-pass kernel
+(forward_onepass, 64-token blocks whatever the chunk argument); with few
+(batch, head) pairs it adds a segment-state kernel first (segment_states);
+shapes outside the single-pass kernel run the stages chunk_cumsum,
+chunk_state, state_passing, chunk_cb, chunk_scan. The library's own plan
+(ssd_forward_plan_info) says which, and the bench line's config reports it.
+
+Also reported: the tiny, large-state and long-sequence forwards (cold, per
+kernel), the stage kernels called one by one at the 2.7B and large-state
+shapes (state passing's HBM GB/s among them), the forward with every
+step-size option, packed variable-length sequences, the backward (with the
+chunk-gradient kernel's roofline), the decode step (256 x 80 heads, P 64,
+N 128, fp32 state, 64 consecutive tokens) and a plain device copy's
+bandwidth. Roofline figures use algorithmic bytes / flops (what the method
+must read, write and compute), not executed ones. The CPU baseline is the
+fp64 oracle (test infrastructure) on the same workload, timed on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
+       python bench.py --trace-run | --counters [--backward] [--workload NAME]
 """
 from __future__ import annotations
 
@@ -44,23 +56,21 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 # ---------------------------------------------------------------- accounting
 
-def segments_of(w):
-    """The library's own plan for this forward (ssd_forward_plan): S >= 1
-    segments per sequence on the single-pass kernel, 0 for the stage kernels."""
+def plan_of(w, dt=None):
+    """The library's own plan for this forward (ssd_forward_plan_info): path,
+    segments S, pieces K, block length, blocks per segment, workspace bytes."""
     import torch
     import structured_state_space_ssd_amd as ssd
-    return ssd.forward_plan(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk,
-                            torch.bfloat16 if w.dtype == "bf16" else torch.float32)
-
-
-def onepass_path(w):
-    """Whether the library runs this forward as its single-pass kernel."""
-    return segments_of(w) > 0
+    return ssd.plan_info(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk,
+                         torch.bfloat16 if w.dtype == "bf16" else torch.float32, dt)
 
 
 def stages_of(w):
-    S = segments_of(w)
-    return STAGES if S == 0 else (ONEPASS if S == 1 else ONEPASS_SEG)
+    """Kernels the forward launches, in order (the library's plan decides)."""
+    p = plan_of(w)
+    if p["path"] == "stages":
+        return STAGES
+    return ONEPASS if p["segments"] == 1 else ONEPASS_SEG
 
 
 def onepass_accounting(w):
@@ -74,13 +84,14 @@ def onepass_accounting(w):
     output, 2NP for the state update, 2P for the D term, and (T+1)N per token
     per group for the causal C B^T products. With S segments the segment-state
     kernel reads x, dt and B over the first S-1 segments and writes their
-    states (float32 P x N per (batch, head, segment), 2NP flops per
-    token-head), which the single-pass kernel reads back."""
+    pieces' states (float32 P x N and a log2-decay per (batch, head, piece),
+    2NP flops per token-head), which the single-pass kernel reads back."""
     Bt, L, H, P, G, N = w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate
-    T = 64
+    p = plan_of(w)
+    T = p["block_tokens"]
+    S, k, per_seg = p["segments"], max(1, p["pieces"]), p["segment_blocks"]
     tok = Bt * L
-    S, k, per_seg = onepass_plan(w)
-    seg_states = Bt * H * (S - 1) * k * (P * N + 1) * 4  # one state + decay per piece
+    seg_states = p["workspace_bytes"]  # exactly the pieces' states and decays
     nbytes = 2 * tok * H * P * 2 + tok * H * 2 + 2 * tok * G * N * 2 + 2 * H * 4 + seg_states
     flops = tok * H * ((T + 1) * P + 4 * N * P + 2 * P) + tok * G * (T + 1) * N
     acc = {"forward_onepass": {"bytes": nbytes, "flops": flops}}
@@ -92,18 +103,7 @@ def onepass_accounting(w):
     return acc
 
 
-def onepass_plan(w):
-    """(S, k, per_seg): segments, pieces per segment and blocks per segment of
-    the single-pass forward, from the library's own plan (ssd_forward_plan_info)."""
-    import torch
-    import structured_state_space_ssd_amd as ssd
-    p = ssd.plan_info(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk,
-                      torch.bfloat16 if w.dtype == "bf16" else torch.float32)
-    assert p["path"] == "single_pass", p
-    return p["segments"], max(1, p["pieces"]), p["segment_blocks"]
-
-
-def accounting(w):
+def stage_accounting(w, fused=None):
     """Algorithmic bytes and flops per launch of each forward stage.
 
     Bytes: every input read once and every output written once, at its storage
@@ -118,10 +118,10 @@ def accounting(w):
     chunk_scan (Q+1)P (causal masked product: Q(Q+1)/2 pairs x 2P per
     chunk-head) + 2NP (state to output) + 2P (skip) per token-head; chunk_cb
     (Q+1)N per token per group (causal C B^T); state_passing 2PN per
-    chunk-head element pair.
+    chunk-head element pair. ``fused``: whether stages 2 and 3 run as one
+    kernel (None: the forward's own rule, bf16 with batch * nheads >= 512;
+    the stage entry points called one by one never fuse).
     """
-    if onepass_path(w):
-        return onepass_accounting(w)
     Bt, L, H, P, G, N, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk
     e = 2 if w.dtype == "bf16" else 4
     nC = -(-L // Q)
@@ -148,28 +148,49 @@ def accounting(w):
     cumsum = {"bytes": dt + H * 4 + 2 * s, "flops": tok * H * 2}
     state = {"bytes": x + bc + 2 * s + st, "flops": tok * H * 2 * P * N}
     passing = {"bytes": st + ci + send, "flops": Bt * nC * H * P * N * 2}
-    if fused_state_path(w):
-        # one kernel for stages 2 and 3 (the library's rule): reads x, B, s and
-        # delta, writes chunk_init and the final state; no per-chunk states
+    if fused is None:
+        fused = w.dtype == "bf16" and Bt * H >= 512
+    if fused:
+        # one kernel for stages 2 and 3: reads x, B, s and delta, writes
+        # chunk_init and the final state; no per-chunk states
         fin = Bt * H * P * N * 4
         state = {"bytes": x + bc + 2 * s + ci + fin,
                  "flops": state["flops"] + passing["flops"]}
         passing = {"bytes": 0, "flops": 0}
-    acc = {
-        "chunk_cumsum": cumsum,
-        "chunk_state": state,
-        "state_passing": passing,
-        "chunk_cb": cb_stage,
-        "chunk_scan": scan,
-    }
-    return acc
+    return {"chunk_cumsum": cumsum, "chunk_state": state, "state_passing": passing,
+            "chunk_cb": cb_stage, "chunk_scan": scan}
 
 
-def fused_state_path(w):
-    """Whether the library runs stages 2 and 3 as one kernel for this workload
-    (bf16 with batch * nheads >= 512; mirrors state_passing_fused in the
-    library's chunk_state.hip)."""
-    return w.dtype == "bf16" and w.batch * w.nheads >= 512
+def accounting(w):
+    """Per-kernel algorithmic bytes and flops of the forward as the library runs it."""
+    return onepass_accounting(w) if plan_of(w)["path"] == "single_pass" else stage_accounting(w)
+
+
+def backward_accounting(w):
+    """Algorithmic bytes and flops of the backward's chunk-gradient kernel (one
+    launch). Bytes: it reads x and dy (input dtype), B and C once per group,
+    the prefix sums s and weights w (float32 per token-head, chunk-padded),
+    the state entering each chunk H_c and the adjoint leaving it G_{c+1}
+    (operand type, [Bt][nC][H][P][N]); it writes dx (input dtype), ds and dw
+    (float32 per token-head), the dB and dC partial sums (float32 per head
+    block) and dD per chunk-head. Flops (multiply + add = 2) per token-head:
+    the causal dy.x^T blocks and dx (2 (Q+1) P), the causal dB and dC
+    products (2 (Q+1) N), the state terms G B, G^T x, H^T dy, H C (8 N P);
+    plus (Q+1) N per token and group for the causal C.B^T blocks. Q is the
+    backward's own chunk length (128 for N <= 64, else 64)."""
+    Bt, L, H, P, G, N = w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate
+    e = 2 if w.dtype == "bf16" else 4
+    Q = 128 if N <= 64 else 64
+    nC = -(-L // Q)
+    nU = Bt * nC * G
+    nblk = max(1, min(H // G, -(-256 // nU)))
+    tok = Bt * L
+    tokh = Bt * H * nC * Q * 4
+    states = Bt * nC * H * P * N * e
+    nbytes = (3 * tok * H * P * e + 2 * tok * G * N * e + 2 * tokh + 2 * states + 2 * tokh +
+              2 * nblk * tok * G * N * 4 + Bt * nC * H * 4)
+    flops = tok * H * (2 * (Q + 1) * P + 2 * (Q + 1) * N + 8 * N * P) + tok * G * (Q + 1) * N
+    return {"chunk_bwd": {"bytes": nbytes, "flops": flops, "chunk": Q, "head_blocks": nblk}}
 
 
 def decode_accounting(w):
@@ -196,7 +217,7 @@ def kernel_source_digest(name):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel):
+def measured_traffic(kernel, workload="mamba2_2.7b"):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
     were taken on the current source of the kernel; else None."""
     try:
@@ -204,13 +225,38 @@ def measured_traffic(kernel):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    rec = t.get(kernel)
+    rec = t.get(workload, {}).get(kernel)
     if not rec or rec.get("source_digest") != kernel_source_digest(kernel):
         return None
     return rec.get("bytes_per_launch")
 
 
+def kernel_figures(a, seconds, dtype):
+    """Per-kernel figures from algorithmic bytes / flops and a time."""
+    gbs = a["bytes"] / seconds / 1e9
+    tfl = a["flops"] / seconds / 1e12
+    peak_f = BF16_PEAK_TFLOPS if dtype == "bf16" else FP32_PEAK_TFLOPS
+    intensity = a["flops"] / a["bytes"] if a["bytes"] else 0.0
+    applicable = min(peak_f, intensity * HBM_PEAK_GBS / 1e3)  # TFLOP/s roof at this intensity
+    return {"us": round(seconds * 1e6, 2), "alg_bytes": a["bytes"], "alg_flops": a["flops"],
+            "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "TFLOP_s": round(tfl, 2), "mfma_frac": round(tfl / peak_f, 4),
+            "roofline_frac": round(tfl / applicable, 4) if applicable else None}
+
+
 # ---------------------------------------------------------------- GPU timing
+
+_GEN = {}
+
+
+def gen(w):
+    """W.generate(w), drawn once per workload and run (a shallow copy: callers
+    may replace entries)."""
+    import ssd_workloads as W
+    if w.name not in _GEN:
+        _GEN[w.name] = W.generate(w)
+    return dict(_GEN[w.name])
+
 
 def upload(d):
     import numpy as np
@@ -243,100 +289,151 @@ def spin_up(call, seconds=0.15):
         torch.cuda.synchronize()
 
 
-def time_forward(w, steps, warmup, breakdown_steps=10, event_every=5, spin_seconds=0.15):
-    """Two passes over the same resident inputs.
+class Flush:
+    """Reads a 1 GiB buffer (a sum: clean lines only, so the next kernel does
+    not also write back a flush's dirty lines), which leaves neither L2 nor
+    the 256 MB Infinity Cache holding any input of the next kernel."""
 
-    Breakdown pass (not the timed region): ``breakdown_steps`` forwards with a
-    HIP event between every two stages, giving each stage's GPU time (an event
-    between launches also adds a small gap of its own).
-    Timed region: ``warmup`` untimed forwards, then ``steps`` forwards between
-    two synchronizations, timed by the host clock; inside it, events are
-    recorded only around the dominant stage of the breakdown pass, on the
-    launch stream, in every ``event_every``-th forward (an event pair costs a
-    few microseconds of pipeline gap), so that the dominant kernel's average
-    time is measured live with little added overhead."""
+    def __init__(self, nbytes=1 << 30):
+        import torch
+        self.buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        self.sink = torch.zeros((), dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        self.sink += self.buf.sum()
+
+
+COLD = ("cold caches: before each step, outside its events, a 1 GiB buffer is read, so "
+        "that neither L2 nor the 256 MB Infinity Cache holds any input")
+
+
+def _stats(v):
+    v = sorted(v)
+    n = len(v)
+    return {"mean": sum(v) / n, "median": v[n // 2], "p10": v[n // 10], "p90": v[(9 * n) // 10]}
+
+
+def time_forward_cold(w, steps, warmup, flush=None):
+    """The timed region: ``warmup`` untimed cold forwards, then ``steps`` cold
+    forwards between two synchronizations. Before each, outside its events, a
+    1 GiB read (Flush); around each forward and between its kernels, HIP
+    events on the launch stream (ssd_forward_timed). Returns the forward's
+    mean / median / p10 / p90 (ms), each kernel's mean (ms) and the host wall
+    time of the region (flushes included)."""
     import torch
     import ssd_workloads as W
     import structured_state_space_ssd_amd as ssd
 
-    d = W.generate(w)
-    g = upload(d)
+    g = upload(gen(w))
     x, dt, A, B, C, D = (g[k] for k in ("x", "dt", "A", "B", "C", "D"))
-    ws = torch.empty(ssd.workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate,
-                                        w.chunk, x.dtype), dtype=torch.uint8, device="cuda")
+    need = plan_of(w, dt)["workspace_bytes"]
+    ws = torch.empty(max(1, need), dtype=torch.uint8, device="cuda")
     y = torch.empty_like(x)
+    flush = flush or Flush()
     stages = stages_of(w)
-    ns = len(stages)  # events 0..ns used (the single-pass kernel: events 0 and 1)
+    ns = len(stages)
     mk = lambda: torch.cuda.Event(enable_timing=True)
     pad = lambda evs: list(evs) + [None] * (len(STAGES) + 1 - len(evs))
-
-    # ---- spin-up (see spin_up) before anything is measured
-    spin_up(lambda: ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y), spin_seconds)
-
-    # ---- breakdown pass
-    bd = [[mk() for _ in range(ns + 1)] for _ in range(breakdown_steps)]
-    for evs in bd:
-        ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y, events=pad(evs))
-    torch.cuda.synchronize()
-    per_stage = [sum(evs[i].elapsed_time(evs[i + 1]) for evs in bd) / breakdown_steps
-                 for i in range(ns)]
-    evented_ms = sum(evs[0].elapsed_time(evs[ns]) for evs in bd) / breakdown_steps
-    dom = max(range(ns), key=lambda i: per_stage[i])
-
-    # ---- timed region
-    sampled = list(range(0, steps, event_every))
-    pairs = [(mk(), mk()) for _ in sampled]
-    events = [None] * steps
-    for k, (e0, e1) in zip(sampled, pairs):
-        evs = [None] * (ns + 1)
-        evs[dom], evs[dom + 1] = e0, e1
-        for e in (e0, e1):
-            e.record()  # create the HIP events before the timed region
-        events[k] = pad(evs)
+    call = lambda ev=None: ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y,
+                                       events=ev)
+    spin_up(call)
     for _ in range(warmup):
-        ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y)
+        flush()
+        call()
+    evs = [[mk() for _ in range(ns + 1)] for _ in range(steps)]
+    for e in evs:
+        for ev in e:
+            ev.record()  # create the HIP events before the timed region
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(steps):
-        ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y, events=events[k])
+    for e in evs:
+        flush()
+        call(pad(e))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dom_ms = sum(e0.elapsed_time(e1) for e0, e1 in pairs) / len(pairs)
-    return {"wall_ms": wall * 1e3 / steps, "evented_ms": evented_ms,
-            "stage_ms": dict(zip(stages, per_stage)), "dominant": stages[dom], "dominant_ms": dom_ms}
+    fwd = _stats([e[0].elapsed_time(e[ns]) for e in evs])
+    per = {stages[i]: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i in range(ns)}
+    del x, dt, B, C, y, ws, g
+    return {"forward_ms": fwd, "kernel_ms": per, "wall_ms": wall * 1e3 / steps}
 
 
-def time_forward_cold(w, reps=30, flush_bytes=1 << 30):
-    """Single forwards with nothing of the inputs in the caches: before each,
-    outside its events, a 1 GiB buffer is read (a sum: clean lines only, so
-    the forward does not also write back a flush's dirty lines), which leaves
-    neither L2 nor the 256 MB Infinity Cache holding x, B, C or dt. The 2.7B
-    inputs (175 MB) fit in the Infinity Cache, so back-to-back forwards (the
-    timed region) find part of them there. Returns the median and p10 / p90
-    in ms."""
+def time_forward_warm(w, steps, warmup):
+    """Back-to-back forwards over the same resident inputs (host clock around
+    ``steps`` of them, after ``warmup``): part of the inputs then comes from
+    the Infinity Cache when they fit in it."""
     import torch
     import ssd_workloads as W
     import structured_state_space_ssd_amd as ssd
 
-    g = upload(W.generate(w))
+    g = upload(gen(w))
     x, dt, A, B, C, D = (g[k] for k in ("x", "dt", "A", "B", "C", "D"))
-    ws = torch.empty(ssd.workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate,
-                                        w.chunk, x.dtype), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(1, plan_of(w, dt)["workspace_bytes"]), dtype=torch.uint8, device="cuda")
     y = torch.empty_like(x)
-    flush = torch.ones(flush_bytes // 4, dtype=torch.float32, device="cuda")
-    sink = torch.zeros((), dtype=torch.float32, device="cuda")
     call = lambda: ssd.forward(x, dt, A, B, C, D, chunk=w.chunk, workspace=ws, y=y)
     spin_up(call)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    for e0, e1 in evs:
-        sink += flush.sum()
-        e0.record()
+    for _ in range(warmup):
         call()
-        e1.record()
     torch.cuda.synchronize()
-    t = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
-    return {"median_ms": t[reps // 2], "p10_ms": t[reps // 10], "p90_ms": t[(9 * reps) // 10]}
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def time_stages_cold(w, reps=20, flush=None):
+    """The forward's stage kernels called one by one through their entry
+    points (ssd_chunk_cumsum, ssd_chunk_state, ssd_state_passing,
+    ssd_chunk_cb for float32, ssd_chunk_scan: the chunked form with the
+    per-chunk states in HBM, never fused), cold (Flush before each pass),
+    with HIP events between them. Returns each stage's mean time (ms)."""
+    import torch
+    import ssd_workloads as W
+    import structured_state_space_ssd_amd as ssd
+
+    g = upload(gen(w))
+    x, dt, A, B, C, D = (g[k] for k in ("x", "dt", "A", "B", "C", "D"))
+    Bt, L, H, P, N, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.chunk
+    nC = -(-L // Q)
+    f32 = torch.float32
+    s = torch.empty((Bt, H, nC * Q), dtype=f32, device="cuda")
+    delta = torch.empty_like(s)
+    st = torch.empty((Bt, nC, H, P, N), dtype=f32, device="cuda")
+    ci = torch.empty((Bt, nC, H, P, N), dtype=x.dtype, device="cuda")
+    fs = torch.empty((Bt, H, P, N), dtype=f32, device="cuda")
+    y = torch.empty_like(x)
+    bf16 = w.dtype == "bf16"
+    cb = None if bf16 else ssd.chunk_cb(B, C, Q)
+
+    def run(ev):
+        ev[0].record()
+        ssd.chunk_cumsum(dt, A, Q, out=s, delta=delta)
+        ev[1].record()
+        ssd.chunk_state(x, B, delta, s, Q, out=st)
+        ev[2].record()
+        ssd.state_passing(st, s, L, Q, out=ci, final_state=fs, dtype=x.dtype)
+        ev[3].record()
+        if not bf16:
+            ssd.chunk_cb(B, C, Q, out=cb)
+        ev[4].record()
+        ssd.chunk_scan(x, delta, s, B, C, cb, D, ci, Q, y=y)
+        ev[5].record()
+
+    flush = flush or Flush()
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    spin_up(lambda: run([mk() for _ in range(6)]), 0.1)
+    evs = [[mk() for _ in range(6)] for _ in range(reps)]
+    for e in evs:
+        flush()
+        run(e)
+    torch.cuda.synchronize()
+    out = {}
+    for i, name in enumerate(STAGES):
+        if name == "chunk_cb" and bf16:
+            continue
+        out[name] = sum(e[i].elapsed_time(e[i + 1]) for e in evs) / reps
+    out["_total"] = sum(e[0].elapsed_time(e[5]) for e in evs) / reps
+    return out
 
 
 def time_forward_options(w, steps, warmup):
@@ -347,13 +444,13 @@ def time_forward_options(w, steps, warmup):
     import ssd_workloads as W
     import structured_state_space_ssd_amd as ssd
 
-    d = W.generate(w)
+    d = gen(w)
     r = W.generate_dt_raw(w)
     d["dt"], d["dt_bias"] = r["dt"], r["dt_bias"]
     g = upload(d)
     x = g["x"]
-    ws = torch.empty(ssd.workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.ngroups, w.dstate,
-                                        w.chunk, x.dtype), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(1, plan_of(w, g["dt"])["workspace_bytes"]), dtype=torch.uint8,
+                     device="cuda")
     y = torch.empty_like(x)
     kw = dict(chunk=w.chunk, workspace=ws, y=y, dt_bias=g["dt_bias"], dt_softplus=True,
               dt_limit=(4e-3, 3e-2), zoh=True)
@@ -386,7 +483,7 @@ def time_forward_varlen(steps, warmup):
     import structured_state_space_ssd_amd as ssd
 
     w, cu = varlen_workload()
-    g = upload(W.generate(w))
+    g = upload(gen(w))
     cu_g = torch.from_numpy(cu).cuda()
     x = g["x"]
     ws = torch.empty(int(ssd._native.lib.ssd_forward_varlen_workspace_size(
@@ -407,14 +504,20 @@ def time_forward_varlen(steps, warmup):
     return w, cu, ms
 
 
-def time_backward(w, steps, warmup):
-    """Whole-backward time (host clock): gradients of every input for the
-    workload's forward, with a final-state gradient and every dt option off."""
+BWD_PHASES = ["recompute", "adjoint", "chunk_bwd", "reductions"]
+
+
+def time_backward(w, steps, warmup, cold=False, flush=None):
+    """Whole-backward time: gradients of every input for the workload's
+    forward, with a final-state gradient and every dt option off. Warm: host
+    clock over back-to-back backwards. Cold (Flush before each, outside the
+    events): the mean of HIP events around each backward and its phases
+    (ssd_backward_timed)."""
     import torch
     import ssd_workloads as W
     import structured_state_space_ssd_amd as ssd
 
-    d = W.generate(w)
+    d = gen(w)
     d.update(W.generate_grads(w))
     g = upload(d)
     ws = torch.empty(int(ssd._native.lib.ssd_backward_workspace_size(
@@ -426,11 +529,23 @@ def time_backward(w, steps, warmup):
     for _ in range(warmup):
         ssd.backward(*args, **kw)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        ssd.backward(*args, **kw)
+    if not cold:
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            ssd.backward(*args, **kw)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+    flush = flush or Flush()
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [[mk() for _ in range(5)] for _ in range(steps)]
+    for e in evs:
+        flush()
+        ssd.backward(*args, events=e, **kw)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3 / steps
+    out = {name: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps
+           for i, name in enumerate(BWD_PHASES)}
+    out["_total"] = sum(e[0].elapsed_time(e[4]) for e in evs) / steps
+    return out
 
 
 def time_decode(w, warmup=3):
@@ -484,8 +599,7 @@ def cpu_baseline(w, min_seconds=1.5):
     at least ``min_seconds`` of wall time (about 10-30 s of CPU work on the
     threads it uses)."""
     import oracle
-    import ssd_workloads as W
-    d = W.generate(w)
+    d = gen(w)
     n = oracle.default_threads()
     passes, sec = 0, 0.0
     while passes == 0 or sec < min_seconds:
@@ -501,8 +615,11 @@ def cpu_baseline(w, min_seconds=1.5):
                       f"state), fp64 recurrence on {n} threads, {sec:.2f} s wall"}
 
 
-def counters_run(w):
-    """A short, fixed sequence of launches for counter collection."""
+def counters_run(w, backward=False):
+    """A short, fixed sequence of launches for counter collection: a plain
+    1 GiB device copy (it calibrates the byte counters), a few cold forwards
+    of the workload (and with ``backward`` a few cold backwards), and the
+    decode steps."""
     import torch
     copy_bytes = 1 << 30
     src = torch.empty(copy_bytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -513,35 +630,52 @@ def counters_run(w):
     torch.cuda.synchronize()
     print(f"[counters] copy of {copy_bytes} bytes x2 done", file=sys.stderr, flush=True)
     del src, dst
-    time_forward(w, steps=3, warmup=1)
+    time_forward_cold(w, steps=3, warmup=1)
     print("[counters] forward x4 done", file=sys.stderr, flush=True)
-    time_decode(W_decode(), warmup=0)
-    print("[counters] decode done", file=sys.stderr, flush=True)
+    if backward:
+        time_backward(w, steps=2, warmup=0, cold=True)
+        print("[counters] backward done", file=sys.stderr, flush=True)
+    else:
+        time_decode(W_decode(), warmup=0)
+        print("[counters] decode done", file=sys.stderr, flush=True)
+
+
+def trace_run(w, steps, warmup):
+    """Only the headline's timed region (warmup + cold timed forwards, each
+    after its 1 GiB read), for a kernel trace whose last ``steps`` dispatches
+    of each forward kernel are exactly the timed ones."""
+    r = time_forward_cold(w, steps, warmup)
+    print(json.dumps({"workload": w.name, "steps": steps, "warmup": warmup,
+                      "forward_us_mean": round(r["forward_ms"]["mean"] * 1e3, 2),
+                      "kernel_us": {k: round(v * 1e3, 2) for k, v in r["kernel_ms"].items()}}),
+          flush=True)
 
 
 # ---------------------------------------------------------------- profile summaries
 #
-# The rocprofv3 runs these read (OUT is any scratch directory):
-TRACE_CMD = ('rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/trace" -o trace '
-             '-- python bench.py --steps 20 --warmup 5 --all > "$OUT/bench_trace.log"')
-FETCH_CMD = ('rocprofv3 --pmc FETCH_SIZE --output-format csv -d "$OUT/fetch" -o fetch '
-             '-- python bench.py --counters')
-WRITE_CMD = ('rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/write" -o write '
-             '-- python bench.py --counters')
-# kernel-name fragment -> stage, first match wins (the fused stage-2+3 kernel
+# The rocprofv3 runs these read (OUT is any scratch directory; WL a workload
+# name: mamba2_2.7b, large_state, long_seq):
+TRACE_CMD = ('rocprofv3 --kernel-trace --stats --output-format csv -d "$OUT/trace_$WL" -o trace '
+             '-- python bench.py --trace-run --workload $WL --steps 50 --warmup 10 '
+             '> "$OUT/trace_$WL.log"')
+FETCH_CMD = ('rocprofv3 --pmc FETCH_SIZE --output-format csv -d "$OUT/fetch_$WL" -o fetch '
+             '-- python bench.py --counters --workload $WL')
+WRITE_CMD = ('rocprofv3 --pmc WRITE_SIZE --output-format csv -d "$OUT/write_$WL" -o write '
+             '-- python bench.py --counters --workload $WL')
+UTIL_CMDS = ('rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil --output-format csv -d "$OUT/util_$WL" '
+             '-o util -- python bench.py --counters --workload $WL',
+             'rocprofv3 --pmc MfmaFlopsBF16 --output-format csv -d "$OUT/mops_$WL" -o mops '
+             '-- python bench.py --counters --workload $WL')
+# kernel-name fragment -> kernel, first match wins (the fused stage-2+3 kernel
 # fills the chunk_state interval of the forward)
 KERNEL_OF = {"segment_states_kernel": "segment_states",
              "ssd_forward_onepass": "forward_onepass", "onepass_varlen_prep": "packed: token int4s",
              "chunk_cumsum_kernel": "chunk_cumsum", "chunk_state_passing": "chunk_state",
              "state_passing_kernel": "state_passing", "chunk_state": "chunk_state",
              "chunk_cb_kernel": "chunk_cb", "chunk_scan": "chunk_scan",
-             "decode_step_kernel": "decode_step", "chunk_bwd_kernel": "backward: chunk gradients",
+             "decode_step_kernel": "decode_step", "chunk_bwd_kernel": "chunk_bwd",
              "bwd_dt_kernel": "backward: dt, A, bias", "bwd_reduce_kernel": "backward: dB, dC sums",
              "bwd_head_sum_kernel": "backward: per-head sums", "varlen_seg": "packed: token masks"}
-UTIL_CMDS = ('rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil --output-format csv -d "$OUT/util" -o util '
-             '-- python bench.py --counters',
-             'rocprofv3 --pmc MfmaFlopsBF16 --output-format csv -d "$OUT/mops" -o mops '
-             '-- python bench.py --counters')
 CALIBRATION_KERNEL = "__amd_rocclr_copyBuffer"  # the 1 GiB device copy of --counters
 COPY_BYTES = 1 << 30
 
@@ -559,53 +693,71 @@ def _read_csv(path):
         return list(csv.DictReader(f))
 
 
-def summarize_trace(stats_csv, bench_log):
-    """Markdown table of a --kernel-trace --stats run, with the bench line's own
-    event timings of the same run beside the profiler's averages."""
-    rows = _read_csv(stats_csv)
-    bench = None
-    with open(bench_log) as f:
+def _col(row, *names):
+    for n in names:
+        if n in row:
+            return row[n]
+    raise KeyError(names)
+
+
+def summarize_trace(trace_csv, run_log):
+    """Markdown table of a --kernel-trace run of ``bench.py --trace-run``: for
+    each kernel, its dispatch count and the average, min and max duration of
+    its last ``steps`` dispatches (exactly the timed cold forwards), beside the
+    run's own event timings."""
+    rows = _read_csv(trace_csv)
+    run = None
+    with open(run_log) as f:
         for line in f:
             if line.startswith("{"):
-                bench = json.loads(line)
-    out = ["# Kernel trace: SSD forward stages (Mamba-2 2.7B-shaped layer) and decode step", "",
-           "The same run also times the forward with every step-size option, the packed",
-           "variable-length forward and the backward on the same shapes (bench.py's",
-           "forward_with_options, forward_varlen and backward entries) and, with --all, the",
-           "tiny, large-state and long-sequence forwards; their kernels are listed too. A",
-           "kernel name can appear for several uses (e.g. the chunk-state kernel computes the",
-           "backward's output-gradient contributions as well). The bench's own event time is",
-           "given beside the 2.7B forward's kernel (the first row of its stage) only.", "",
-           "Commands, from the repository root on one MI355X:", "", "```",
-           "cd /tmp && export TMPDIR=/tmp && cd -", TRACE_CMD,
-           f'python bench.py --summarize-trace "$OUT/trace/trace_kernel_stats.csv" "$OUT/bench_trace.log"',
-           "```", "",
-           "| kernel | stage | calls | avg us | min us | max us | bench event avg us |",
-           "|---|---|---|---|---|---|---|"]
-    seen = set()
+                run = json.loads(line)
+    steps = run["steps"]
+    per = {}
     for r in rows:
-        stage = _stage_of(r["Name"])
-        ev = ""
-        if bench and stage in bench.get("kernels", {}) and stage not in seen:
-            ev = f"{bench['kernels'][stage]['us']:.2f}"
-            seen.add(stage)
-        elif bench and stage == "decode_step":
-            ev = f"{bench['decode']['us_per_step']:.2f}"
-        name = r["Name"].split("(")[0].replace("void ", "")
-        out.append(f"| `{name}` | {stage or '-'} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {ev} |")
-    if bench:
-        out += ["", f"Bench line of the same run: value {bench['value']:.4g} tokens/s, "
-                    f"{bench['ms_per_step'] * 1e3:.1f} us per forward, roofline "
-                    f"{json.dumps(bench['roofline'])}."]
+        name = _col(r, "Kernel_Name", "Name")
+        t = (int(_col(r, "End_Timestamp", "End")) - int(_col(r, "Start_Timestamp", "Start"))) / 1e3
+        per.setdefault(name, []).append((int(_col(r, "Start_Timestamp", "Start")), t))
+    wl = run["workload"]
+    out = [f"# Kernel trace: the timed cold forwards of `{wl}`", "",
+           f"`bench.py --trace-run` runs {run['warmup']} untimed and {steps} timed forwards, each",
+           "after a 1 GiB read that leaves no input in L2 or the Infinity Cache (the bench",
+           "line's timed region), and nothing else on the GPU but the reads' own reduction",
+           "kernels. Durations are from the per-dispatch kernel trace: the last "
+           f"{steps} dispatches of each kernel are the timed ones.", "",
+           "Commands, from the repository root on one MI355X:", "", "```",
+           "cd /tmp && export TMPDIR=/tmp && cd -", f"WL={wl}", TRACE_CMD,
+           f'python bench.py --summarize-trace "$OUT/trace_$WL/trace_kernel_trace.csv" '
+           f'"$OUT/trace_$WL.log"', "```", "",
+           "| kernel | role | dispatches | avg us (timed) | min us | max us | bench event avg us |",
+           "|---|---|---|---|---|---|---|"]
+    for name, v in sorted(per.items(), key=lambda kv: -sum(t for _, t in kv[1])):
+        role = _stage_of(name)
+        if role is None:
+            continue
+        v.sort()
+        last = [t for _, t in v[-steps:]]
+        ev = run["kernel_us"].get(role, "")
+        short = name.split("(")[0].replace("void ", "")
+        out.append(f"| `{short}` | {role} | {len(v)} | {sum(last) / len(last):.2f} | "
+                   f"{min(last):.2f} | {max(last):.2f} | {ev} |")
+    out += ["", f"The run's own figure: {run['forward_us_mean']} us per cold forward (HIP events "
+                f"around each), kernels {json.dumps(run['kernel_us'])}."]
     return "\n".join(out)
+
+
+def _summary_accounting(workload):
+    import ssd_workloads as W
+    w = W.WORKLOADS[workload]
+    acc = dict(accounting(w))
+    acc.update({k: v for k, v in backward_accounting(w).items()})
+    acc["decode_step"] = decode_accounting(W_decode())
+    return acc
 
 
 def summarize_traffic(fetch_csv, write_csv, workload="mamba2_2.7b"):
     """HBM bytes per launch of each kernel from FETCH_SIZE and WRITE_SIZE
     (KiB per dispatch), each scaled by what the same counter reads for the
     plain 1 GiB device copy of the same run. Returns (markdown, json dict)."""
-    import ssd_workloads as W
     per = {}
     for tag, path in (("fetch", fetch_csv), ("write", write_csv)):
         for r in _read_csv(path):
@@ -617,28 +769,24 @@ def summarize_traffic(fetch_csv, write_csv, workload="mamba2_2.7b"):
     cal = per[CALIBRATION_KERNEL]
     f_scale = COPY_BYTES / 1024 / max(cal["fetch"])
     w_scale = COPY_BYTES / 1024 / max(cal["write"])
-    acc = accounting(W.WORKLOADS[workload])
-    acc["decode_step"] = decode_accounting(W_decode())
+    acc = _summary_accounting(workload)
     rec = {"_calibration": {"kernel": CALIBRATION_KERNEL, "copy_bytes": COPY_BYTES,
                             "fetch_kib": max(cal["fetch"]), "write_kib": max(cal["write"]),
                             "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
                             "commands": [FETCH_CMD, WRITE_CMD]}}
-    wopt = "" if workload == "mamba2_2.7b" else f" --workload {workload}"
-    title = {"mamba2_2.7b": "Mamba-2 2.7B-shaped layer",
-             "long_seq": "long sequence: batch 1, L 65536, 80 heads, N 128, 8 groups"}.get(
-                 workload, workload)
-    out = [f"# HBM traffic per launch: SSD forward kernels ({title}) and decode step",
-           "", "Commands, from the repository root on one MI355X:", "", "```",
-           "cd /tmp && export TMPDIR=/tmp && cd -", f"timeout -s KILL 60 {FETCH_CMD}{wopt}",
-           f"timeout -s KILL 60 {WRITE_CMD}{wopt}",
-           'python bench.py --summarize-traffic "$OUT/fetch/fetch_counter_collection.csv" '
-           f'"$OUT/write/write_counter_collection.csv"{wopt}', "```", "",
+    out = [f"# HBM traffic per launch: SSD kernels (`{workload}`)",
+           "", "Commands, from the repository root on one MI355X (add `--backward` to both",
+           "counter runs for the backward's kernels):", "", "```",
+           "cd /tmp && export TMPDIR=/tmp && cd -", f"WL={workload}",
+           f"timeout -s KILL 60 {FETCH_CMD}", f"timeout -s KILL 60 {WRITE_CMD}",
+           'python bench.py --summarize-traffic "$OUT/fetch_$WL/fetch_counter_collection.csv" '
+           f'"$OUT/write_$WL/write_counter_collection.csv" --workload $WL', "```", "",
            f"Calibration: the 1 GiB device copy reads FETCH_SIZE {max(cal['fetch']):.0f} KiB and "
            f"WRITE_SIZE {max(cal['write']):.0f} KiB, so FETCH_SIZE is scaled by {f_scale:.3f} and "
            f"WRITE_SIZE by {w_scale:.3f}.", "",
            "| kernel | dispatches | fetch MB | write MB | HBM MB / launch | algorithmic MB | ratio |",
            "|---|---|---|---|---|---|---|"]
-    for k in ONEPASS_SEG + STAGES + ["decode_step"]:
+    for k in ONEPASS_SEG + STAGES + ["chunk_bwd", "decode_step"]:
         if k not in acc:
             continue
         if k not in per or "fetch" not in per[k] or "write" not in per[k]:
@@ -658,8 +806,7 @@ def summarize_traffic(fetch_csv, write_csv, workload="mamba2_2.7b"):
 def summarize_util(util_csv, mops_csv, workload="mamba2_2.7b"):
     """Markdown table of the MFMA-busy, VALU-busy and LDS counters (percent of
     the kernel's active cycles, averaged over its dispatches) and the executed
-    bf16 MFMA flops against the algorithmic ones, per forward kernel."""
-    import ssd_workloads as W
+    bf16 MFMA flops against the algorithmic ones, per kernel."""
     per = {}
     for path in (util_csv, mops_csv):
         for r in _read_csv(path):
@@ -668,24 +815,24 @@ def summarize_util(util_csv, mops_csv, workload="mamba2_2.7b"):
                 continue
             per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
                 float(r["Counter_Value"]))
-    acc = accounting(W.WORKLOADS[workload])
-    wopt = "" if workload == "mamba2_2.7b" else f" --workload {workload}"
-    out = [f"# MFMA, VALU and LDS utilisation: SSD forward kernels ({workload})", "",
+    acc = _summary_accounting(workload)
+    out = [f"# MFMA, VALU and LDS utilisation: SSD kernels (`{workload}`)", "",
            "rocprofv3 derived counters, each the average over the kernel's dispatches:",
            "MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), VALUBusy and",
            "LdsUtil likewise in percent of busy cycles; MfmaFlopsBF16 = 512 x",
            "SQ_INSTS_VALU_MFMA_MOPS_BF16, the executed bf16 MFMA flops per launch, beside",
            "the algorithmic flops the accounting counts (the executed ones include the",
            "zero-padded halves of causal tiles and the D x products).", "",
-           "Commands, from the repository root on one MI355X:", "", "```",
-           "cd /tmp && export TMPDIR=/tmp && cd -"] + \
-          [f"timeout -s KILL 60 {c}{wopt}" for c in UTIL_CMDS] + \
-          ['python bench.py --summarize-util "$OUT/util/util_counter_collection.csv" '
-           f'"$OUT/mops/mops_counter_collection.csv"{wopt}', "```", "",
+           "Commands, from the repository root on one MI355X (add `--backward` to both",
+           "counter runs for the backward's kernels):", "", "```",
+           "cd /tmp && export TMPDIR=/tmp && cd -", f"WL={workload}"] + \
+          [f"timeout -s KILL 60 {c}" for c in UTIL_CMDS] + \
+          ['python bench.py --summarize-util "$OUT/util_$WL/util_counter_collection.csv" '
+           f'"$OUT/mops_$WL/mops_counter_collection.csv" --workload $WL', "```", "",
            "| kernel | dispatches | MfmaUtil % | VALUBusy % | LdsUtil % | executed MFMA GFLOP "
            "| algorithmic GFLOP |", "|---|---|---|---|---|---|---|"]
     avg = lambda v: sum(v) / len(v) if v else float("nan")
-    for k in ONEPASS_SEG + STAGES:
+    for k in ONEPASS_SEG + STAGES + ["chunk_bwd"]:
         if k not in per or k not in acc:
             continue
         c = per[k]
@@ -700,25 +847,43 @@ def W_decode():
     return W.WORKLOADS["decode"]
 
 
+def _workload_line(w, r, acc):
+    """Figures of one cold-timed forward workload."""
+    kern = {k: kernel_figures(acc[k], v * 1e-3, w.dtype) for k, v in r["kernel_ms"].items()
+            if acc[k]["bytes"]}
+    f = r["forward_ms"]
+    p = plan_of(w)
+    return {"us_per_forward": round(f["mean"] * 1e3, 2), "p10_us": round(f["p10"] * 1e3, 2),
+            "p90_us": round(f["p90"] * 1e3, 2),
+            "tokens_per_s": round(w.tokens / (f["mean"] * 1e-3), 1),
+            "plan": {k: p[k] for k in ("path", "segments", "pieces", "block_tokens")},
+            "kernels": kern}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="mamba2_2.7b")
-    ap.add_argument("--all", action="store_true", help="also time the other forward workloads")
+    ap.add_argument("--quick", action="store_true",
+                    help="the headline only: skip the other workloads and the stage kernels")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--counters", action="store_true",
-                    help="short run for rocprofv3 counter collection: a few forwards, a few decode "
-                         "steps and a plain 1 GiB device copy that calibrates the byte counters")
-    ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "BENCH_LOG"),
-                    help="print the markdown summary of a rocprofv3 --kernel-trace --stats run")
+                    help="short run for rocprofv3 counter collection: a plain 1 GiB device copy "
+                         "that calibrates the byte counters, a few forwards of --workload, and the "
+                         "decode steps (with --backward: a few backwards instead)")
+    ap.add_argument("--backward", action="store_true", help="with --counters: the backward")
+    ap.add_argument("--trace-run", action="store_true",
+                    help="only the timed region of --workload (for a kernel trace)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "RUN_LOG"),
+                    help="print the markdown summary of a rocprofv3 --kernel-trace run of --trace-run")
     ap.add_argument("--summarize-util", nargs=2, metavar=("UTIL_CSV", "MOPS_CSV"),
                     help="print the MFMA / VALU / LDS utilisation summary of two rocprofv3 "
                          "--pmc runs")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="print the HBM-traffic summary of two rocprofv3 --pmc runs and write "
-                         "profiles/hbm_traffic.json")
+                    help="print the HBM-traffic summary of two rocprofv3 --pmc runs and record "
+                         "it in profiles/hbm_traffic.json")
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(*args.summarize_trace))
@@ -728,10 +893,15 @@ def main():
         return
     if args.summarize_traffic:
         md, rec = summarize_traffic(*args.summarize_traffic, workload=args.workload)
-        if args.workload == "mamba2_2.7b":  # the bench line's roofline.traffic reads this one
-            with open(TRAFFIC_FILE, "w") as f:
-                json.dump(rec, f, indent=1)
-                f.write("\n")
+        try:
+            with open(TRAFFIC_FILE) as f:
+                allrec = json.load(f)
+        except (OSError, ValueError):
+            allrec = {}
+        allrec.setdefault(args.workload, {}).update(rec)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(allrec, f, indent=1)
+            f.write("\n")
         print(md)
         return
     if args.gpus != 1:
@@ -749,89 +919,89 @@ def main():
         sys.exit(1)
     w = W.WORKLOADS[args.workload]
     if args.counters:
-        counters_run(w)
+        counters_run(w, args.backward)
         return
-    print(f"[bench] {w.name}: timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
-    fwd = time_forward(w, args.steps, args.warmup)
-    ms = fwd["wall_ms"]
+    if args.trace_run:
+        trace_run(w, args.steps, args.warmup)
+        return
+    say = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+    say(f"{w.name}: {args.warmup} warmup + {args.steps} timed cold forwards")
+    flush = Flush()
+    cold = time_forward_cold(w, args.steps, args.warmup, flush)
+    f = cold["forward_ms"]
+    ms = f["mean"]
     acc = accounting(w)
-    kernels = {}
-    for name in stages_of(w):
-        t = fwd["stage_ms"][name] * 1e-3
-        a = acc[name]
-        if a["bytes"] == 0:  # stage not launched for this dtype (only event gaps in between)
-            kernels[name] = {"us": round(t * 1e6, 2), "launched": False}
-            continue
-        gbs = a["bytes"] / t / 1e9
-        tfl = a["flops"] / t / 1e12
-        peak_f = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
-        intensity = a["flops"] / a["bytes"]
-        applicable = min(peak_f, intensity * HBM_PEAK_GBS / 1e3)  # TFLOP/s roof at this intensity
-        kernels[name] = {"us": round(t * 1e6, 2), "alg_bytes": a["bytes"], "alg_flops": a["flops"],
-                         "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "TFLOP_s": round(tfl, 2), "mfma_frac": round(tfl / peak_f, 4),
-                         "roofline_frac": round(tfl / applicable, 4)}
-    dom = fwd["dominant"]
-    dom_gbs = acc[dom]["bytes"] / (fwd["dominant_ms"] * 1e-3) / 1e9  # live, in the timed region
+    kernels = {k: kernel_figures(acc[k], v * 1e-3, w.dtype) for k, v in cold["kernel_ms"].items()
+               if acc[k]["bytes"]}
+    dom = max(kernels, key=lambda k: kernels[k]["us"])
+    dom_s = cold["kernel_ms"][dom] * 1e-3
+    dom_gbs = acc[dom]["bytes"] / dom_s / 1e9
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                "us_per_launch": round(fwd["dominant_ms"] * 1e3, 2),
-                "traffic": measured_traffic(dom)}
-    print(f"[bench] forward {ms * 1e3:.1f} us/step ({fwd['evented_ms'] * 1e3:.1f} us with an event "
-          f"between every two kernels; {fwd['dominant']} {fwd['dominant_ms'] * 1e3:.1f} us live); kernels " +
-          ", ".join(f"{k} {v['us']:.1f} us" for k, v in kernels.items()), file=sys.stderr, flush=True)
+                "us_per_launch": round(dom_s * 1e6, 2), "alg_bytes_per_launch": acc[dom]["bytes"],
+                "traffic": measured_traffic(dom, w.name), "cache": "cold"}
+    say(f"cold forward {ms * 1e3:.1f} us (median {f['median'] * 1e3:.1f}); " +
+        ", ".join(f"{k} {v['us']:.1f} us" for k, v in kernels.items()))
 
-    cold = time_forward_cold(w)
-    cold_rec = {"protocol": "one forward per rep after reading a 1 GiB buffer (L2 and Infinity "
-                            "Cache hold none of the inputs); 30 reps",
-                "us_per_forward": round(cold["median_ms"] * 1e3, 2),
-                "p10_us": round(cold["p10_ms"] * 1e3, 2), "p90_us": round(cold["p90_ms"] * 1e3, 2),
-                "tokens_per_s": round(w.tokens / (cold["median_ms"] * 1e-3), 1)}
-    print(f"[bench] cold-cache forward: {cold_rec['us_per_forward']} us (median)", file=sys.stderr,
-          flush=True)
+    warm_ms = time_forward_warm(w, args.steps, max(3, args.warmup // 4))
+    warm = {"protocol": "back-to-back forwards over the same resident inputs, host clock around "
+                        f"{args.steps} of them; inputs that fit in the 256 MB Infinity Cache are "
+                        "partly read from it",
+            "us_per_forward": round(warm_ms * 1e3, 2),
+            "tokens_per_s": round(w.tokens / (warm_ms * 1e-3), 1),
+            "hbm_frac": round(sum(a["bytes"] for a in acc.values()) / (warm_ms * 1e-3) / 1e9 /
+                              HBM_PEAK_GBS, 4)}
+    say(f"warm forward {warm_ms * 1e3:.1f} us")
+
+    extra, stage_lines = {}, {}
+    if not args.quick:
+        for name in ("tiny_f32", "large_state", "long_seq"):
+            wl = W.WORKLOADS[name]
+            r = time_forward_cold(wl, 20, 5, flush)
+            extra[name] = _workload_line(wl, r, accounting(wl))
+            say(f"{name}: {extra[name]['us_per_forward']} us cold; " +
+                ", ".join(f"{k} {v['us']:.1f} us ({v['hbm_frac']:.3f} of HBM)"
+                          for k, v in extra[name]["kernels"].items()))
+        for name in ("mamba2_2.7b", "large_state"):
+            wl = W.WORKLOADS[name]
+            r = time_stages_cold(wl, 20, flush)
+            sa = stage_accounting(wl, fused=False)
+            stage_lines[name] = {
+                "protocol": "the stage entry points one by one (per-chunk states in HBM, never "
+                            "fused), cold, HIP events between them, mean of 20",
+                "us_total": round(r.pop("_total") * 1e3, 2),
+                "kernels": {k: kernel_figures(sa[k], v * 1e-3, wl.dtype) for k, v in r.items()}}
+            say(f"{name} stage kernels: " + ", ".join(
+                f"{k} {v['us']:.1f} us ({v['hbm_frac']:.3f} of HBM, {v['mfma_frac']:.3f} of MFMA)"
+                for k, v in stage_lines[name]["kernels"].items()))
 
     opt_ms = time_forward_options(w, max(10, args.steps // 2), 3)
-    options = {"options": "dt_bias + softplus + clamp + zero-order hold",
+    options = {"options": "dt_bias + softplus + clamp + zero-order hold (warm, back to back)",
                "us_per_forward": round(opt_ms * 1e3, 2),
                "tokens_per_s": round(w.tokens / (opt_ms * 1e-3), 1)}
-    print(f"[bench] forward with every step-size option: {opt_ms * 1e3:.1f} us", file=sys.stderr,
-          flush=True)
+    say(f"forward with every step-size option: {opt_ms * 1e3:.1f} us")
 
     wv, cu, vl_ms = time_forward_varlen(max(10, args.steps // 2), 3)
     varlen = {"workload": f"{wv.seqlen} tokens (the 2.7B layer's 8 x 2048) packed as {cu.size - 1} "
-                          "sequences of 1 .. 4096 tokens, bf16, per-sequence final states",
+                          "sequences of 1 .. 4096 tokens, bf16, per-sequence final states "
+                          "(warm, back to back)",
               "us_per_forward": round(vl_ms * 1e3, 2),
               "tokens_per_s": round(wv.seqlen / (vl_ms * 1e-3), 1)}
-    print(f"[bench] packed variable-length forward: {vl_ms * 1e3:.1f} us", file=sys.stderr,
-          flush=True)
+    say(f"packed variable-length forward: {vl_ms * 1e3:.1f} us")
 
     bw_ms = time_backward(w, max(10, args.steps // 2), 3)
+    bwc = time_backward(w, 20, 3, cold=True, flush=flush)
+    ba = backward_accounting(w)
+    cb = kernel_figures(ba["chunk_bwd"], bwc["chunk_bwd"] * 1e-3, w.dtype)
+    cb.update({"chunk": ba["chunk_bwd"]["chunk"], "head_blocks": ba["chunk_bwd"]["head_blocks"]})
     backward = {"workload": "gradients of x, dt, A, B, C, D and the initial state, same shapes",
                 "us_per_backward": round(bw_ms * 1e3, 2),
-                "tokens_per_s": round(w.tokens / (bw_ms * 1e-3), 1)}
-    print(f"[bench] backward: {bw_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
-
-    extra = {}
-    if args.all:
-        for name in ("tiny_f32", "large_state", "long_seq"):
-            wl = W.WORKLOADS[name]
-            r = time_forward(wl, 10, 3)
-            acc_w = accounting(wl)
-            hbm = {}
-            for k, v in r["stage_ms"].items():
-                nb, nf = acc_w[k]["bytes"], acc_w[k]["flops"]
-                if nb and v > 0:
-                    gbs = nb / (v * 1e-3) / 1e9
-                    tfl = nf / (v * 1e-3) / 1e12
-                    peak = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
-                    hbm[k] = {"alg_MB": round(nb / 1e6, 1), "GB_s": round(gbs, 1),
-                              "hbm_frac": round(gbs / HBM_PEAK_GBS, 3),
-                              "TFLOP_s": round(tfl, 2), "mfma_frac": round(tfl / peak, 4)}
-            extra[name] = {"us_per_forward": round(r["wall_ms"] * 1e3, 1),
-                           "tokens_per_s": round(wl.tokens / (r["wall_ms"] * 1e-3)),
-                           "stage_us": {k: round(v * 1e3, 1) for k, v in r["stage_ms"].items()},
-                           "stage_hbm": hbm}
-            print(f"[bench] {name}: {r['wall_ms'] * 1e3:.1f} us", file=sys.stderr, flush=True)
+                "tokens_per_s": round(w.tokens / (bw_ms * 1e-3), 1),
+                "cold_us_per_backward": round(bwc["_total"] * 1e3, 2),
+                "cold_phase_us": {k: round(bwc[k] * 1e3, 2) for k in BWD_PHASES},
+                "chunk_bwd": cb}
+    say(f"backward: {bw_ms * 1e3:.1f} us warm, {bwc['_total'] * 1e3:.1f} us cold; chunk_bwd "
+        f"{cb['us']} us ({cb['hbm_frac']:.3f} of HBM)")
 
     wd = W.WORKLOADS["decode"]
     dec = time_decode(wd)
@@ -841,17 +1011,18 @@ def main():
               "us_per_step": round(dec["mean_ms"] * 1e3, 2), "GB_s": round(dec_gbs, 1),
               "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4), "alg_bytes_per_step": da["bytes"],
               "tokens_per_s": round(wd.batch / (dec["mean_ms"] * 1e-3))}
-    print(f"[bench] decode {decode['us_per_step']} us/step, {decode['GB_s']} GB/s", file=sys.stderr, flush=True)
+    say(f"decode {decode['us_per_step']} us/step, {decode['GB_s']} GB/s")
 
+    del flush
     probe = hbm_probe()
-    print(f"[bench] 1 GiB device copy: {probe['read_plus_write_GB_s']} GB/s (read + write)",
-          file=sys.stderr, flush=True)
+    say(f"1 GiB device copy: {probe['read_plus_write_GB_s']} GB/s (read + write)")
 
     cpu = None
     if not args.no_cpu:
-        print("[bench] cpu baseline (fp64 oracle)...", file=sys.stderr, flush=True)
+        say("cpu baseline (fp64 oracle)...")
         cpu = cpu_baseline(w)
 
+    p = plan_of(w)
     out = {
         "metric": METRIC,
         "value": round(w.tokens / (ms * 1e-3), 1),
@@ -868,12 +1039,17 @@ def main():
         "config": {"workload": "SSD layer forward, Mamba-2 2.7B shape", "batch": w.batch,
                    "seq_len": w.seqlen, "nheads": w.nheads, "headdim": w.headdim,
                    "dstate": w.dstate, "ngroups": w.ngroups, "chunk": w.chunk,
-                   "parallelism": "single GPU"},
+                   "path": p["path"], "block_tokens": p["block_tokens"],
+                   "segments": p["segments"], "cache": "cold", "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "evented_us_per_step": round(fwd["evented_ms"] * 1e3, 2),
+        "timing": {"protocol": COLD + "; HIP events around each forward and between its "
+                               "kernels on the launch stream; value = tokens / mean",
+                   "median_us": round(f["median"] * 1e3, 2), "p10_us": round(f["p10"] * 1e3, 2),
+                   "p90_us": round(f["p90"] * 1e3, 2),
+                   "wall_ms_per_step_with_flush": round(cold["wall_ms"], 4)},
         "kernels": kernels,
-        "forward_cold_cache": cold_rec,
+        "forward_warm": warm,
         "forward_with_options": options,
         "forward_varlen": varlen,
         "backward": backward,
@@ -882,6 +1058,12 @@ def main():
     }
     if extra:
         out["other_workloads"] = extra
+    if stage_lines:
+        out["stage_kernels"] = stage_lines
+        out["state_passing"] = {k: {"GB_s": v["kernels"]["state_passing"]["GB_s"],
+                                    "hbm_frac": v["kernels"]["state_passing"]["hbm_frac"],
+                                    "us": v["kernels"]["state_passing"]["us"]}
+                                for k, v in stage_lines.items()}
     print(json.dumps(out), flush=True)
 
 

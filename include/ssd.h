@@ -291,6 +291,22 @@ int ssd_forward_timed(const void *x, const void *dt, const float *A, const void 
  */
 size_t ssd_backward_workspace_size(int batch, int seqlen, int nheads, int headdim, int ngroups,
                                    int dstate, int dtype);
+/*
+ * ssd_backward with timing hooks: `events` is NULL (then this is exactly
+ * ssd_backward) or an array of 5 hipEvent_t owned by the caller, any of which
+ * may be NULL (not recorded), recorded on `stream`: [0] before the forward
+ * recompute (prefix sums, weights, the state entering each chunk), [1] before
+ * the adjoint pass over the chunks, [2] before the chunk-gradient kernel,
+ * [3] after it, [4] after the last kernel (the dB / dC sums and the dt, A,
+ * bias stage).
+ */
+int ssd_backward_timed(const void *x, const void *dt, const float *A, const void *B,
+                       const void *C, const float *D, const float *init_state, const void *dy,
+                       const float *dfinal_state, int batch, int seqlen, int nheads, int headdim,
+                       int ngroups, int dstate, int dtype, void *dx, void *ddt, float *dA,
+                       void *dB, void *dC, float *dD, float *dinit_state, float *ddt_bias,
+                       void *workspace, size_t workspace_bytes, const ssd_options *opts,
+                       void *stream, void *const *events);
 int ssd_backward(const void *x, const void *dt, const float *A, const void *B, const void *C,
                  const float *D, const float *init_state, const void *dy,
                  const float *dfinal_state, int batch, int seqlen, int nheads, int headdim,

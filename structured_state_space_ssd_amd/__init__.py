@@ -151,14 +151,7 @@ def forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, return_final_sta
     need = plan_info(Bt, L, H, P, G, N, chunk, x.dtype, dt)["workspace_bytes"]
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    ev = None
-    if events is not None:
-        if len(events) != 6:
-            raise ValueError("events must hold 6 entries (torch.cuda.Event or None)")
-        for e in events:
-            if e is not None and not e.cuda_event:
-                e.record()  # torch creates the HIP event on its first record
-        ev = (ctypes.c_void_p * 6)(*[e.cuda_event if e is not None else None for e in events])
+    ev = _event_array(events, 6)
     opts = options(dt_bias, dt_softplus, dt_limit, zoh)
     rc = _native.lib.ssd_forward_ex(
         ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), Bt, L, H, P, G, N, chunk, dt_,
@@ -168,10 +161,25 @@ def forward(x, dt, A, B, C, D=None, chunk=256, init_state=None, return_final_sta
     return (y, fs) if return_final_state else y
 
 
+def _event_array(events, n):
+    """ctypes array of n hipEvent_t from torch.cuda.Event (or None) entries."""
+    if events is None:
+        return None
+    if len(events) != n:
+        raise ValueError(f"events must hold {n} entries (torch.cuda.Event or None)")
+    for e in events:
+        if e is not None and not e.cuda_event:
+            e.record()  # torch creates the HIP event on its first record
+    return (ctypes.c_void_p * n)(*[e.cuda_event if e is not None else None for e in events])
+
+
 def backward(x, dt, A, B, C, D, dy, init_state=None, dfinal_state=None, dt_bias=None,
-             dt_softplus=False, dt_limit=None, zoh=False, workspace=None, want_dinit=True):
+             dt_softplus=False, dt_limit=None, zoh=False, workspace=None, want_dinit=True,
+             events=None):
     """Gradients of sum(dy * y) + sum(dfinal_state * final_state) for
     ``forward`` with the same inputs and options (ssd_backward).
+    ``events``: optional sequence of 5 torch.cuda.Event or None, recorded
+    around the backward's phases (see ssd_backward_timed).
 
     Returns a dict: dx, ddt, dB, dC (input dtype, shaped like x, dt, B, C),
     dA, dD (float32 [H]), dinit (float32 [Bt,H,P,N], or None if not
@@ -210,12 +218,12 @@ def backward(x, dt, A, B, C, D, dy, init_state=None, dfinal_state=None, dt_bias=
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     opts = options(dt_bias, dt_softplus, dt_limit, zoh)
-    rc = _native.lib.ssd_backward(
+    rc = _native.lib.ssd_backward_timed(
         ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), ptr(init_state), ptr(dy),
         ptr(dfinal_state), Bt, L, H, P, G, N, dt_, ptr(out["dx"]), ptr(out["ddt"]),
         ptr(out["dA"]), ptr(out["dB"]), ptr(out["dC"]), ptr(out["dD"]), ptr(out["dinit"]),
-        ptr(out.get("ddt_bias")), ptr(workspace), workspace.numel() * workspace.element_size(), _optref(opts),
-        stream_handle(dev))
+        ptr(out.get("ddt_bias")), ptr(workspace), workspace.numel() * workspace.element_size(),
+        _optref(opts), stream_handle(dev), _event_array(events, 5))
     check(rc, "ssd_backward")
     return out
 

@@ -52,6 +52,7 @@ SIGNATURES = {
     "ssd_forward_static": (_i, [_vp] * 6 + [_i] * 8 + [_vp, _vp, _vp, _op, _vp]),
     "ssd_backward_workspace_size": (_sz, [_i] * 7),
     "ssd_backward": (_i, [_vp] * 9 + [_i] * 7 + [_vp] * 9 + [_sz, _op, _vp]),
+    "ssd_backward_timed": (_i, [_vp] * 9 + [_i] * 7 + [_vp] * 9 + [_sz, _op, _vp, _vp]),
     "ssd_forward_varlen_workspace_size": (_sz, [_i] * 7),
     "ssd_forward_varlen": (_i, [_vp] * 7 + [_i] * 8 + [_vp, _vp, _vp, _sz, _op, _vp]),
     "ssd_step": (_i, [_vp] * 7 + [_i] * 6 + [_vp, _vp]),

@@ -536,6 +536,19 @@ int ssd_backward(const void *x, const void *dt, const float *A, const void *B, c
                  int ngroups, int dstate, int dtype, void *dx, void *ddt, float *dA, void *dB,
                  void *dC, float *dD, float *dinit_state, float *ddt_bias, void *workspace,
                  size_t workspace_bytes, const ssd_options *opts, void *stream) {
+    return ssd_backward_timed(x, dt, A, B, C, D, init_state, dy, dfinal_state, batch, seqlen,
+                              nheads, headdim, ngroups, dstate, dtype, dx, ddt, dA, dB, dC, dD,
+                              dinit_state, ddt_bias, workspace, workspace_bytes, opts, stream,
+                              nullptr);
+}
+
+int ssd_backward_timed(const void *x, const void *dt, const float *A, const void *B,
+                       const void *C, const float *D, const float *init_state, const void *dy,
+                       const float *dfinal_state, int batch, int seqlen, int nheads, int headdim,
+                       int ngroups, int dstate, int dtype, void *dx, void *ddt, float *dA,
+                       void *dB, void *dC, float *dD, float *dinit_state, float *ddt_bias,
+                       void *workspace, size_t workspace_bytes, const ssd_options *opts,
+                       void *stream, void *const *events) {
     if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC) return SSD_ERR_NULL;
     int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
     if (rc != SSD_OK) return rc;
@@ -559,9 +572,15 @@ int ssd_backward(const void *x, const void *dt, const float *A, const void *B, c
     void *cinit = base + ws.init_off, *gnext = base + ws.gnext_off;
     const int Q = ws.chunk, nC = (seqlen + Q - 1) / Q;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    auto mark = [&](int k) -> hipError_t {
+        return events && events[k] ? hipEventRecord(static_cast<hipEvent_t>(events[k]), st)
+                                   : hipSuccess;
+    };
 
     // forward recompute: prefix sums, input weights, the state entering each chunk
-    hipError_t e = ssd::launch_chunk_cumsum(dt, A, batch, seqlen, nheads, Q, bf16, o, s_, delta, st);
+    hipError_t e = mark(0);
+    if (e == hipSuccess)
+        e = ssd::launch_chunk_cumsum(dt, A, batch, seqlen, nheads, Q, bf16, o, s_, delta, st);
     if (e == hipSuccess) {
         if (ssd::state_passing_fused(batch, nheads, bf16)) {
             e = ssd::launch_chunk_state_passing(x, B, s_, delta, init_state, batch, seqlen, nheads,
@@ -576,6 +595,7 @@ int ssd_backward(const void *x, const void *dt, const float *A, const void *B, c
     }
     // the adjoint of the state leaving each chunk: dS_c, then the reverse pass
     // (one kernel per (b, h) walking the chunks backward when that fills the GPU)
+    if (e == hipSuccess) e = mark(1);
     if (ssd::state_passing_fused(batch, nheads, bf16)) {
         if (e == hipSuccess)
             e = ssd::launch_chunk_state_passing(dy, C, s_, nullptr, dfinal_state, batch, seqlen,
@@ -598,7 +618,9 @@ int ssd_backward(const void *x, const void *dt, const float *A, const void *B, c
     a.dstate = dstate; a.chunk = Q; a.nblk = ws.nblk; a.bf16 = bf16;
     a.dx = dx; a.ds = f32(ws.ds_off); a.dw = f32(ws.dw_off);
     a.dB_part = f32(ws.dB_off); a.dC_part = f32(ws.dC_off); a.dD_part = f32(ws.dD_off);
+    if (e == hipSuccess) e = mark(2);
     if (e == hipSuccess) e = ssd::launch_chunk_bwd(a, st);
+    if (e == hipSuccess) e = mark(3);
     const size_t bc = static_cast<size_t>(batch) * seqlen * ngroups * dstate;
     if (e == hipSuccess) e = ssd::launch_bwd_reduce(a.dB_part, ws.nblk, bc, bf16, dB, st);
     if (e == hipSuccess) e = ssd::launch_bwd_reduce(a.dC_part, ws.nblk, bc, bf16, dC, st);
@@ -611,6 +633,7 @@ int ssd_backward(const void *x, const void *dt, const float *A, const void *B, c
     if (e == hipSuccess && ddt_bias)
         e = ssd::launch_bwd_head_sum(f32(ws.dbias_off), nbc, nheads, ddt_bias, st);
     if (e == hipSuccess && dD) e = ssd::launch_bwd_head_sum(a.dD_part, nbc, nheads, dD, st);
+    if (e == hipSuccess) e = mark(4);
     return status_of(e);
 }
 
