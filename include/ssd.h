@@ -35,9 +35,16 @@
  * - dtype is SSD_F32 (all of x, dt, B, C, y float32) or SSD_BF16 (all bf16);
  *   A, D and every state are float32. Products run on MFMA in the input
  *   dtype with float32 accumulation.
- * - Supported set: headdim == 64; dstate in {16, 32, 64, 128, 256};
- *   chunk in {64, 128, 256}; any seqlen >= 1 (the last chunk may be short);
- *   nheads % ngroups == 0. Anything else returns SSD_ERR_UNSUPPORTED.
+ * - Supported set: headdim == 64; dstate any multiple of 16 from 16 to 256
+ *   (ssd_forward*, ssd_backward*, ssd_step*; the kernels are built for 16, 32,
+ *   64, 128 and 256, and the forward and backward run other sizes
+ *   zero-padded to the next of these, which changes nothing but the work: the
+ *   padded columns of B, C and the states are zeros and add exact zeros to
+ *   every sum over the state dimension; the workspace then also holds the
+ *   padded copies); the separate stage entry points and ssd_forward_varlen
+ *   take dstate in {16, 32, 64, 128, 256} only; chunk in {64, 128, 256}; any
+ *   seqlen >= 1 (the last chunk may be short); nheads % ngroups == 0.
+ *   Anything else returns SSD_ERR_UNSUPPORTED.
  * - stream is a hipStream_t (NULL: the null stream). Calls only enqueue work
  *   and return before it finishes; no host synchronisation happens inside.
  * - Arguments are checked before anything is enqueued; a failed check returns
@@ -123,6 +130,8 @@ const char *ssd_strerror(int status);
 typedef enum { SSD_PATH_STAGES = 0, SSD_PATH_SINGLE_PASS = 1 } ssd_path;
 typedef struct {
     int path, segments, pieces, block_tokens, segment_blocks, piece_blocks;
+    int kernel_dstate; /* the state size the kernels run with (dstate, or the next of
+                          16, 32, 64, 128, 256 when dstate is zero-padded)          */
     size_t workspace_bytes;
 } ssd_plan;
 
@@ -137,7 +146,8 @@ typedef struct {
  * the first S-1 segments produces from a zero state, then float32
  * [Bt][H][(S-1)K], each piece's total log2-decay (sum of dt*A over the piece,
  * times log2(e)); with S == 1 no workspace is needed (NULL is accepted). On
- * the stage path it holds, at 256-byte aligned offsets in this order:
+ * the stage path it holds, at 256-byte aligned offsets in this order (with
+ * N = kernel_dstate):
  *   dA_cumsum   float32 [Bt][H][nC*Q]      within-chunk prefix sums of dt*A
  *   delta       float32 [Bt][H][nC*Q]      each token's input weight w_t, same layout
  *                                          (zero past seqlen)
@@ -150,6 +160,10 @@ typedef struct {
  * stages (a caller may read them, e.g. to test a stage), except that for
  * SSD_BF16 with batch * nheads >= 512 stages 2 and 3 run as one kernel that
  * keeps the per-chunk states on chip (`states` is then not written).
+ * When kernel_dstate != dstate, the kernels' part above is followed (at a
+ * 256-byte aligned offset) by the zero-padded copies of B and C
+ * ([Bt][L][G][kernel_dstate] in dtype) and of the initial and final states
+ * ([Bt][H][P][kernel_dstate] float32), each 256-byte aligned.
  */
 int ssd_forward_plan_info(int batch, int seqlen, int nheads, int headdim, int ngroups,
                           int dstate, int chunk, int dtype, const void *dt, ssd_plan *out);

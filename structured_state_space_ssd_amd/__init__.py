@@ -80,7 +80,7 @@ def plan_info(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, dtype=torc
     return {"path": "single_pass" if p.path == 1 else "stages", "segments": p.segments,
             "pieces": p.pieces, "block_tokens": p.block_tokens,
             "segment_blocks": p.segment_blocks, "piece_blocks": p.piece_blocks,
-            "workspace_bytes": int(p.workspace_bytes)}
+            "kernel_dstate": p.kernel_dstate, "workspace_bytes": int(p.workspace_bytes)}
 
 
 def forward_plan(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, dtype=torch.bfloat16,

@@ -31,7 +31,8 @@ class SsdPlan(ctypes.Structure):
     """ssd_plan of include/ssd.h."""
     _fields_ = [("path", ctypes.c_int), ("segments", ctypes.c_int), ("pieces", ctypes.c_int),
                 ("block_tokens", ctypes.c_int), ("segment_blocks", ctypes.c_int),
-                ("piece_blocks", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
+                ("piece_blocks", ctypes.c_int), ("kernel_dstate", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 _vp, _i, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t

@@ -78,6 +78,63 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     }
 }
 
+// State sizes that are not powers of two (48, 80, ..., 240): a row's N/4
+// float4s do not line up with lane groups of a power of two, so each lane's
+// four-term products go to LDS and lane r of the wavefront then sums row r's
+// N/4 of them in order. Same layout and streaming as above; B and C of the
+// group are staged in LDS first.
+template <typename T, int N>
+__global__ __launch_bounds__(256) void decode_step_rows_kernel(
+    float *__restrict__ state, const T *__restrict__ x, const T *__restrict__ dt,
+    const float *__restrict__ A, const T *__restrict__ B, const T *__restrict__ C,
+    const float *__restrict__ D, int H, int G, T *__restrict__ y, DtOpts o) {
+    constexpr int P = 64;
+    constexpr int F = 4 * N;      // float4s per wavefront: 16 rows x N/4
+    constexpr int ITER = N / 16;  // float4s per lane
+    constexpr int FPR = N / 4;    // float4s per state row
+    __shared__ float part[4][F];
+    __shared__ float bs[N], cs[N];
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh % H, g = h / (H / G);
+    const int w = wave_id(), l = lane_id();
+    const float Ah = A[h];
+    const float d = step_size(o, to_f32(dt[bh]), o.bias ? o.bias[h] : 0.0f);
+    const float a = exp2f(d * Ah * kLog2e);
+    const float wt = input_weight(o, d, Ah);
+    const float Dh = D ? D[h] : 0.0f;
+    for (int i = threadIdx.x; i < N; i += 256) {
+        bs[i] = to_f32(B[((size_t)b * G + g) * N + i]);
+        cs[i] = to_f32(C[((size_t)b * G + g) * N + i]);
+    }
+
+    floatx4 *st = reinterpret_cast<floatx4 *>(state + ((size_t)bh * P + w * 16) * N);
+    floatx4 hv[ITER];
+#pragma unroll
+    for (int m = 0; m < ITER; ++m) hv[m] = __builtin_nontemporal_load(st + m * 64 + l);
+    __syncthreads();
+    const T *xp = x + (size_t)bh * P + w * 16;
+#pragma unroll
+    for (int m = 0; m < ITER; ++m) {
+        const int f = m * 64 + l, r = f / FPR, n = 4 * (f - r * FPR);
+        const float dx = wt * to_f32(xp[r]);
+        floatx4 v = hv[m];
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[k] = a * v[k] + dx * bs[n + k];
+            acc += cs[n + k] * v[k];
+        }
+        part[w][f] = acc;
+        __builtin_nontemporal_store(v, st + m * 64 + l);
+    }
+    __syncthreads();
+    if (l < 16) {
+        float sum = 0.0f;
+        for (int q = 0; q < FPR; ++q) sum += part[w][l * FPR + q];
+        y[(size_t)bh * P + w * 16 + l] = from_f32<T>(sum + Dh * to_f32(xp[l]));
+    }
+}
+
 template <typename T>
 static hipError_t dispatch_decode(int N, float *state, const void *x, const void *dt,
                                   const float *A, const void *B, const void *C, const float *D,
@@ -93,6 +150,12 @@ static hipError_t dispatch_decode(int N, float *state, const void *x, const void
         case 64: decode_step_kernel<T, 64><<<grid, 256, 0, stream>>>(state, xx, dd, A, bb, cc, D, H, G, yy, o); break;
         case 128: decode_step_kernel<T, 128><<<grid, 256, 0, stream>>>(state, xx, dd, A, bb, cc, D, H, G, yy, o); break;
         case 256: decode_step_kernel<T, 256><<<grid, 256, 0, stream>>>(state, xx, dd, A, bb, cc, D, H, G, yy, o); break;
+#define SSD_DECODE_ROWS(NN) \
+        case NN: decode_step_rows_kernel<T, NN><<<grid, 256, 0, stream>>>(state, xx, dd, A, bb, cc, D, H, G, yy, o); break;
+        SSD_DECODE_ROWS(48) SSD_DECODE_ROWS(80) SSD_DECODE_ROWS(96) SSD_DECODE_ROWS(112)
+        SSD_DECODE_ROWS(144) SSD_DECODE_ROWS(160) SSD_DECODE_ROWS(176) SSD_DECODE_ROWS(192)
+        SSD_DECODE_ROWS(208) SSD_DECODE_ROWS(224) SSD_DECODE_ROWS(240)
+#undef SSD_DECODE_ROWS
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

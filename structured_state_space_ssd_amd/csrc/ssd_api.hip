@@ -16,7 +16,11 @@ constexpr int kHeaddim = 64;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-bool supported_dstate(int n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
+// N the kernels are built for; every other multiple of 16 up to 256 runs the
+// forward, the backward and the decode step zero-padded to the next of these
+// (pad.hip)
+bool kernel_dstate_ok(int n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
+bool supported_dstate(int n) { return n >= 16 && n <= 256 && n % 16 == 0; }
 bool supported_chunk(int q) { return q == 64 || q == 128 || q == 256; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool valid_dtype(int d) { return d == SSD_F32 || d == SSD_BF16; }
@@ -99,23 +103,50 @@ BwdWorkspace bwd_layout(int batch, int seqlen, int nheads, int headdim, int ngro
 // kernel needs scratch only for the pieces' states when the sequences are cut
 // into segments (at most `cap` bytes of it); the stage kernels need the whole
 // layout above.
+// With a state size outside the kernels' set, the kernels run at nk (the
+// next size of the set) on zero-padded copies of B, C and the initial state
+// held after the kernels' own part of the workspace, from pad_off on: B', C'
+// [Bt][L][G][nk] in the input dtype, then the initial and final states
+// [Bt][H][P][nk] float32.
 struct FwdPlan {
     bool onepass;
     ssd::OnepassPlan op;
     Workspace ws;
-    size_t need;
+    int nk;
+    size_t pad_off, need;
 };
+
+struct PadLayout {
+    size_t bc, st;  // bytes of one padded B / C, and of one padded state (aligned)
+};
+PadLayout pad_layout(int batch, int seqlen, int nheads, int headdim, int ngroups, int nk,
+                     bool bf16) {
+    return PadLayout{align_up((size_t)batch * seqlen * ngroups * nk * (bf16 ? 2 : 4)),
+                     align_up((size_t)batch * nheads * headdim * nk * sizeof(float))};
+}
 
 FwdPlan plan_forward(int batch, int seqlen, int nheads, int headdim, int ngroups, int dstate,
                      int chunk, bool bf16, const void *dt, size_t cap) {
     FwdPlan f{};
-    f.onepass = ssd::forward_onepass_ok(batch, nheads, dstate, bf16, dt);
+    f.nk = ssd::kernel_dstate(dstate);
+    size_t pad_total = 0;
+    if (f.nk != dstate) {
+        const PadLayout pl = pad_layout(batch, seqlen, nheads, headdim, ngroups, f.nk, bf16);
+        pad_total = 2 * pl.bc + 2 * pl.st + kAlign;
+    }
+    f.onepass = ssd::forward_onepass_ok(batch, nheads, f.nk, bf16, dt);
     if (f.onepass) {
-        f.op = ssd::forward_onepass_plan(batch, seqlen, nheads, dstate, cap);
+        f.op = ssd::forward_onepass_plan(batch, seqlen, nheads, f.nk,
+                                         cap > pad_total ? cap - pad_total : 0);
         f.need = f.op.scratch_bytes;
     } else {
-        f.ws = layout(batch, seqlen, nheads, headdim, ngroups, dstate, chunk, bf16);
+        f.ws = layout(batch, seqlen, nheads, headdim, ngroups, f.nk, chunk, bf16);
         f.need = f.ws.total;
+    }
+    if (f.nk != dstate) {
+        const PadLayout pl = pad_layout(batch, seqlen, nheads, headdim, ngroups, f.nk, bf16);
+        f.pad_off = align_up(f.need);
+        f.need = f.pad_off + 2 * pl.bc + 2 * pl.st;
     }
     return f;
 }
@@ -132,6 +163,15 @@ int check_dims(int batch, int seqlen, int nheads, int headdim, int ngroups, int 
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+// The backward's workspace: its kernels' layout at nk, then (nk != dstate)
+// the padded copies B', C', dB', dC' and three padded states.
+size_t bwd_need(const BwdWorkspace &ws, int batch, int seqlen, int nheads, int headdim,
+                int ngroups, int dstate, int nk, bool bf16) {
+    if (nk == dstate) return ws.total;
+    const PadLayout pl = pad_layout(batch, seqlen, nheads, headdim, ngroups, nk, bf16);
+    return align_up(ws.total) + 4 * pl.bc + 3 * pl.st;
+}
 
 // Checks an ssd_options (NULL: every option off) and converts it for the kernels.
 int dt_opts(const ssd_options *o, ssd::DtOpts &d) {
@@ -160,8 +200,10 @@ const char *ssd_strerror(int status) {
         case SSD_ERR_NULL: return "a required pointer is NULL";
         case SSD_ERR_SHAPE: return "invalid sizes (non-positive, or nheads not a multiple of ngroups)";
         case SSD_ERR_UNSUPPORTED:
-            return "unsupported configuration (need headdim 64, dstate in {16,32,64,128,256}, "
-                   "chunk in {64,128,256}, dtype SSD_F32/SSD_BF16, 16-byte aligned buffers)";
+            return "unsupported configuration (need headdim 64, dstate a multiple of 16 up to "
+                   "256 (16, 32, 64, 128 or 256 for the stage entry points and packed "
+                   "sequences), chunk in {64,128,256}, dtype SSD_F32/SSD_BF16, 16-byte aligned "
+                   "buffers)";
         case SSD_ERR_WORKSPACE: return "workspace missing or too small";
         case SSD_ERR_HIP: return "HIP runtime error at kernel launch";
         case SSD_ERR_OPTION:
@@ -198,6 +240,7 @@ int ssd_forward_plan_info(int batch, int seqlen, int nheads, int headdim, int ng
     out->block_tokens = f.onepass ? 64 : chunk;
     out->segment_blocks = f.onepass ? f.op.per_seg : 0;
     out->piece_blocks = f.onepass && f.op.S > 1 ? f.op.psub : 0;
+    out->kernel_dstate = f.nk;
     out->workspace_bytes = f.need;
     return SSD_OK;
 }
@@ -213,7 +256,7 @@ int ssd_forward_plan(int batch, int seqlen, int nheads, int headdim, int ngroups
 size_t ssd_forward_varlen_workspace_size(int seqlen, int nheads, int headdim, int ngroups,
                                          int dstate, int chunk, int dtype) {
     if (check_dims(1, seqlen, nheads, headdim, ngroups, dstate) != SSD_OK ||
-        !supported_chunk(chunk) || !valid_dtype(dtype))
+        !kernel_dstate_ok(dstate) || !supported_chunk(chunk) || !valid_dtype(dtype))
         return 0;
     size_t seg_off;
     return varlen_layout(seqlen, nheads, headdim, ngroups, dstate, chunk, dtype == SSD_BF16,
@@ -224,7 +267,11 @@ size_t ssd_backward_workspace_size(int batch, int seqlen, int nheads, int headdi
                                    int dstate, int dtype) {
     if (check_dims(batch, seqlen, nheads, headdim, ngroups, dstate) != SSD_OK || !valid_dtype(dtype))
         return 0;
-    return bwd_layout(batch, seqlen, nheads, headdim, ngroups, dstate, dtype == SSD_BF16).total;
+    const int nk = ssd::kernel_dstate(dstate);
+    const bool bf16 = dtype == SSD_BF16;
+    const BwdWorkspace ws = bwd_layout(batch, seqlen, nheads, headdim, ngroups, nk, bf16);
+    if (!ws.chunk) return 0;
+    return bwd_need(ws, batch, seqlen, nheads, headdim, ngroups, dstate, nk, bf16);
 }
 
 size_t ssd_chunk_cb_size(int batch, int seqlen, int ngroups, int chunk, int dtype) {
@@ -237,7 +284,7 @@ int ssd_chunk_cb(const void *B, const void *C, int batch, int seqlen, int ngroup
                  int chunk, int dtype, void *cb, void *stream) {
     if (!B || !C || !cb) return SSD_ERR_NULL;
     if (batch < 1 || seqlen < 1 || ngroups < 1 || dstate < 1) return SSD_ERR_SHAPE;
-    if (!supported_dstate(dstate) || !supported_chunk(chunk) || !valid_dtype(dtype))
+    if (!kernel_dstate_ok(dstate) || !supported_chunk(chunk) || !valid_dtype(dtype))
         return SSD_ERR_UNSUPPORTED;
     if (!aligned16(B) || !aligned16(C) || (reinterpret_cast<uintptr_t>(cb) % 32) != 0)
         return SSD_ERR_UNSUPPORTED;
@@ -266,6 +313,7 @@ int ssd_chunk_state(const void *x, const void *B, const float *delta, const floa
     if (!x || !B || !delta || !dA_cumsum || !states) return SSD_ERR_NULL;
     int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
     if (rc != SSD_OK) return rc;
+    if (!kernel_dstate_ok(dstate)) return SSD_ERR_UNSUPPORTED;
     if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(B) || !aligned16(states) || !aligned16(delta))
         return SSD_ERR_UNSUPPORTED;
@@ -280,6 +328,7 @@ int ssd_state_passing(const float *states, const float *dA_cumsum, const float *
     if (!states || !dA_cumsum || !chunk_init) return SSD_ERR_NULL;
     int rc = check_dims(batch, seqlen, nheads, headdim, 1, dstate);
     if (rc != SSD_OK) return rc;
+    if (!kernel_dstate_ok(dstate)) return SSD_ERR_UNSUPPORTED;
     if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
     if (!aligned16(states) || !aligned16(chunk_init) || (init_state && !aligned16(init_state)) ||
         (final_state && !aligned16(final_state)))
@@ -296,6 +345,7 @@ int ssd_chunk_scan(const void *x, const float *delta, const float *dA_cumsum, co
     if (!x || !delta || !dA_cumsum || !C || !chunk_init || !y) return SSD_ERR_NULL;
     int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
     if (rc != SSD_OK) return rc;
+    if (!kernel_dstate_ok(dstate)) return SSD_ERR_UNSUPPORTED;
     if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
     const bool bf16 = dtype == SSD_BF16;
     const bool reads_cb = ssd::chunk_scan_reads_cb(bf16);
@@ -313,8 +363,70 @@ int ssd_chunk_scan(const void *x, const float *delta, const float *dA_cumsum, co
 
 namespace {
 
-// ssd_forward_ex with the plan's scratch capped at `cap` bytes.
 hipError_t static_scratch(void **out);
+
+// The forward's launches for a plan at the kernels' own state size f.nk,
+// with B, C and the states already of that size; `base` holds the plan's
+// workspace (f.need bytes before any padding region).
+hipError_t forward_run(const FwdPlan &f, const void *x, const void *dt, const float *A,
+                       const void *B, const void *C, const float *D, int batch, int seqlen,
+                       int nheads, int ngroups, int chunk, bool bf16, const float *init_state,
+                       void *y, float *final_state, char *base, const ssd::DtOpts &o,
+                       hipStream_t s, void *const *events) {
+    const int dstate = f.nk;
+    auto mark = [&](int k) -> hipError_t {
+        return events && events[k] ? hipEventRecord(static_cast<hipEvent_t>(events[k]), s)
+                                   : hipSuccess;
+    };
+    hipError_t e = mark(0);
+    if (f.onepass) {
+        // every stage in one kernel (after the segment-state kernel when the
+        // sequences are cut into segments): intervals 0 (and 1), the others empty
+        const int segments = f.op.S;
+        if (e == hipSuccess)
+            e = ssd::launch_forward_onepass(
+                x, dt, A, B, C, D, init_state, o, batch, seqlen, nheads, ngroups, dstate, f.op,
+                reinterpret_cast<float *>(base), y, final_state,
+                segments > 1 && events ? static_cast<hipEvent_t>(events[1]) : nullptr, s);
+        for (int k = segments > 1 ? 2 : 1; k <= 5 && e == hipSuccess; ++k) e = mark(k);
+        return e;
+    }
+    const Workspace &ws = f.ws;
+    float *cumsum = reinterpret_cast<float *>(base + ws.cumsum_off);
+    float *delta = reinterpret_cast<float *>(base + ws.delta_off);
+    float *states = reinterpret_cast<float *>(base + ws.states_off);
+    void *cinit = base + ws.init_off;
+    void *cb = base + ws.cb_off;
+    if (e == hipSuccess)
+        e = ssd::launch_chunk_cumsum(dt, A, batch, seqlen, nheads, chunk, bf16, o, cumsum, delta,
+                                     s);
+    if (e == hipSuccess) e = mark(1);
+    if (ssd::state_passing_fused(batch, nheads, bf16)) {
+        // stages 2 and 3 in one kernel; the state_passing interval stays empty
+        if (e == hipSuccess)
+            e = ssd::launch_chunk_state_passing(x, B, cumsum, delta, init_state, batch, seqlen,
+                                                nheads, ngroups, dstate, chunk, cinit,
+                                                final_state, s);
+        if (e == hipSuccess) e = mark(2);
+    } else {
+        if (e == hipSuccess)
+            e = ssd::launch_chunk_state(x, B, delta, cumsum, nullptr, batch, seqlen, nheads,
+                                        ngroups, dstate, chunk, bf16, states, s);
+        if (e == hipSuccess) e = mark(2);
+        if (e == hipSuccess)
+            e = ssd::launch_state_passing(states, cumsum, init_state, nullptr, batch, seqlen,
+                                          nheads, dstate, chunk, bf16, cinit, final_state, s);
+    }
+    if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess && ssd::chunk_scan_reads_cb(bf16))
+        e = ssd::launch_chunk_cb(B, C, batch, seqlen, ngroups, dstate, chunk, bf16, cb, s);
+    if (e == hipSuccess) e = mark(4);
+    if (e == hipSuccess)
+        e = ssd::launch_chunk_scan(x, delta, cumsum, B, C, cb, D, cinit, nullptr, batch, seqlen,
+                                   nheads, ngroups, dstate, chunk, bf16, y, s);
+    if (e == hipSuccess) e = mark(5);
+    return e;
+}
 
 // ssd_forward_ex with the plan's scratch capped at `cap` bytes; with
 // `fixed_scratch` the workspace is the current device's fixed scratch array
@@ -353,58 +465,28 @@ int forward_impl(const void *x, const void *dt, const float *A, const void *B, c
 
     char *base = static_cast<char *>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    auto mark = [&](int k) -> hipError_t {
-        return events && events[k] ? hipEventRecord(static_cast<hipEvent_t>(events[k]), s)
-                                   : hipSuccess;
-    };
-
-    hipError_t e = mark(0);
-    if (f.onepass) {
-        // every stage in one kernel (after the segment-state kernel when the
-        // sequences are cut into segments): intervals 0 (and 1), the others empty
-        const int segments = f.op.S;
-        if (e == hipSuccess)
-            e = ssd::launch_forward_onepass(
-                x, dt, A, B, C, D, init_state, o, batch, seqlen, nheads, ngroups, dstate, f.op,
-                reinterpret_cast<float *>(base), y, final_state,
-                segments > 1 && events ? static_cast<hipEvent_t>(events[1]) : nullptr, s);
-        for (int k = segments > 1 ? 2 : 1; k <= 5 && e == hipSuccess; ++k) e = mark(k);
-        return status_of(e);
-    }
-    const Workspace &ws = f.ws;
-    float *cumsum = reinterpret_cast<float *>(base + ws.cumsum_off);
-    float *delta = reinterpret_cast<float *>(base + ws.delta_off);
-    float *states = reinterpret_cast<float *>(base + ws.states_off);
-    void *cinit = base + ws.init_off;
-    void *cb = base + ws.cb_off;
+    if (f.nk == dstate)
+        return status_of(forward_run(f, x, dt, A, B, C, D, batch, seqlen, nheads, ngroups, chunk,
+                                     bf16, init_state, y, final_state, base, o, s, events));
+    // zero-padded to the kernels' state size (pad.hip): B, C, the initial state
+    // in; the final state cut back to dstate
+    const PadLayout pl = pad_layout(batch, seqlen, nheads, headdim, ngroups, f.nk, bf16);
+    char *pb = base + f.pad_off;
+    void *Bp = pb, *Cp = pb + pl.bc;
+    float *ip = reinterpret_cast<float *>(pb + 2 * pl.bc);
+    float *fp = reinterpret_cast<float *>(pb + 2 * pl.bc + pl.st);
+    const size_t bc_rows = (size_t)batch * seqlen * ngroups, st_rows = (size_t)batch * nheads * headdim;
+    const int es = bf16 ? 2 : 4;
+    hipError_t e = ssd::launch_pad_rows(B, Bp, bc_rows, dstate, f.nk, es, s);
+    if (e == hipSuccess) e = ssd::launch_pad_rows(C, Cp, bc_rows, dstate, f.nk, es, s);
+    if (e == hipSuccess && init_state)
+        e = ssd::launch_pad_rows(init_state, ip, st_rows, dstate, f.nk, 4, s);
     if (e == hipSuccess)
-        e = ssd::launch_chunk_cumsum(dt, A, batch, seqlen, nheads, chunk, bf16, o, cumsum, delta,
-                                     s);
-    if (e == hipSuccess) e = mark(1);
-    if (ssd::state_passing_fused(batch, nheads, bf16)) {
-        // stages 2 and 3 in one kernel; the state_passing interval stays empty
-        if (e == hipSuccess)
-            e = ssd::launch_chunk_state_passing(x, B, cumsum, delta, init_state, batch, seqlen,
-                                                nheads, ngroups, dstate, chunk, cinit,
-                                                final_state, s);
-        if (e == hipSuccess) e = mark(2);
-    } else {
-        if (e == hipSuccess)
-            e = ssd::launch_chunk_state(x, B, delta, cumsum, nullptr, batch, seqlen, nheads, ngroups, dstate,
-                                        chunk, bf16, states, s);
-        if (e == hipSuccess) e = mark(2);
-        if (e == hipSuccess)
-            e = ssd::launch_state_passing(states, cumsum, init_state, nullptr, batch, seqlen, nheads, dstate,
-                                          chunk, bf16, cinit, final_state, s);
-    }
-    if (e == hipSuccess) e = mark(3);
-    if (e == hipSuccess && ssd::chunk_scan_reads_cb(bf16))
-        e = ssd::launch_chunk_cb(B, C, batch, seqlen, ngroups, dstate, chunk, bf16, cb, s);
-    if (e == hipSuccess) e = mark(4);
-    if (e == hipSuccess)
-        e = ssd::launch_chunk_scan(x, delta, cumsum, B, C, cb, D, cinit, nullptr, batch, seqlen, nheads,
-                                   ngroups, dstate, chunk, bf16, y, s);
-    if (e == hipSuccess) e = mark(5);
+        e = forward_run(f, x, dt, A, Bp, Cp, D, batch, seqlen, nheads, ngroups, chunk, bf16,
+                        init_state ? ip : nullptr, y, final_state ? fp : nullptr, base, o, s,
+                        events);
+    if (e == hipSuccess && final_state)
+        e = ssd::launch_pad_rows(fp, final_state, st_rows, f.nk, dstate, 4, s);
     return status_of(e);
 }
 
@@ -470,6 +552,7 @@ int ssd_forward_varlen(const void *x, const void *dt, const float *A, const void
     if (nseq < 1) return SSD_ERR_SHAPE;
     int rc = check_dims(1, seqlen, nheads, headdim, ngroups, dstate);
     if (rc != SSD_OK) return rc;
+    if (!kernel_dstate_ok(dstate)) return SSD_ERR_UNSUPPORTED;
     if (!supported_chunk(chunk) || !valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) ||
         (seq_states && !aligned16(seq_states)) ||
@@ -542,36 +625,23 @@ int ssd_backward(const void *x, const void *dt, const float *A, const void *B, c
                               nullptr);
 }
 
-int ssd_backward_timed(const void *x, const void *dt, const float *A, const void *B,
-                       const void *C, const float *D, const float *init_state, const void *dy,
-                       const float *dfinal_state, int batch, int seqlen, int nheads, int headdim,
-                       int ngroups, int dstate, int dtype, void *dx, void *ddt, float *dA,
-                       void *dB, void *dC, float *dD, float *dinit_state, float *ddt_bias,
-                       void *workspace, size_t workspace_bytes, const ssd_options *opts,
-                       void *stream, void *const *events) {
-    if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC) return SSD_ERR_NULL;
-    int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
-    if (rc != SSD_OK) return rc;
-    if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
-    const bool bf16 = dtype == SSD_BF16;
-    if (!ssd::bwd_chunk(dstate, bf16)) return SSD_ERR_UNSUPPORTED;
-    if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(dy) || !aligned16(dx) ||
-        !aligned16(dB) || !aligned16(dC) || (init_state && !aligned16(init_state)) ||
-        (dfinal_state && !aligned16(dfinal_state)) || (dinit_state && !aligned16(dinit_state)))
-        return SSD_ERR_UNSUPPORTED;
-    ssd::DtOpts o;
-    rc = dt_opts(opts, o);
-    if (rc != SSD_OK) return rc;
-    const BwdWorkspace ws = bwd_layout(batch, seqlen, nheads, headdim, ngroups, dstate, bf16);
-    if (!workspace || workspace_bytes < ws.total) return SSD_ERR_WORKSPACE;
-    if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return SSD_ERR_WORKSPACE;
+}  // extern "C"
 
-    char *base = static_cast<char *>(workspace);
+namespace {
+
+// The backward's launches at the kernels' own state size (dstate here is
+// one of 16, 32, 64, 128, 256), with `base` holding the layout `ws`.
+hipError_t backward_run(const BwdWorkspace &ws, const void *x, const void *dt, const float *A,
+                        const void *B, const void *C, const float *D, const float *init_state,
+                        const void *dy, const float *dfinal_state, int batch, int seqlen,
+                        int nheads, int ngroups, int dstate, bool bf16, void *dx, void *ddt,
+                        float *dA, void *dB, void *dC, float *dD, float *dinit_state,
+                        float *ddt_bias, char *base, const ssd::DtOpts &o, hipStream_t st,
+                        void *const *events) {
     auto f32 = [&](size_t off) { return reinterpret_cast<float *>(base + off); };
     float *s_ = f32(ws.s_off), *delta = f32(ws.delta_off), *states = f32(ws.states_off);
     void *cinit = base + ws.init_off, *gnext = base + ws.gnext_off;
     const int Q = ws.chunk, nC = (seqlen + Q - 1) / Q;
-    hipStream_t st = static_cast<hipStream_t>(stream);
     auto mark = [&](int k) -> hipError_t {
         return events && events[k] ? hipEventRecord(static_cast<hipEvent_t>(events[k]), st)
                                    : hipSuccess;
@@ -634,6 +704,72 @@ int ssd_backward_timed(const void *x, const void *dt, const float *A, const void
         e = ssd::launch_bwd_head_sum(f32(ws.dbias_off), nbc, nheads, ddt_bias, st);
     if (e == hipSuccess && dD) e = ssd::launch_bwd_head_sum(a.dD_part, nbc, nheads, dD, st);
     if (e == hipSuccess) e = mark(4);
+    return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+
+int ssd_backward_timed(const void *x, const void *dt, const float *A, const void *B,
+                       const void *C, const float *D, const float *init_state, const void *dy,
+                       const float *dfinal_state, int batch, int seqlen, int nheads, int headdim,
+                       int ngroups, int dstate, int dtype, void *dx, void *ddt, float *dA,
+                       void *dB, void *dC, float *dD, float *dinit_state, float *ddt_bias,
+                       void *workspace, size_t workspace_bytes, const ssd_options *opts,
+                       void *stream, void *const *events) {
+    if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC) return SSD_ERR_NULL;
+    int rc = check_dims(batch, seqlen, nheads, headdim, ngroups, dstate);
+    if (rc != SSD_OK) return rc;
+    if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    const bool bf16 = dtype == SSD_BF16;
+    const int nk = ssd::kernel_dstate(dstate);
+    if (!ssd::bwd_chunk(nk, bf16)) return SSD_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(dy) || !aligned16(dx) ||
+        !aligned16(dB) || !aligned16(dC) || (init_state && !aligned16(init_state)) ||
+        (dfinal_state && !aligned16(dfinal_state)) || (dinit_state && !aligned16(dinit_state)))
+        return SSD_ERR_UNSUPPORTED;
+    ssd::DtOpts o;
+    rc = dt_opts(opts, o);
+    if (rc != SSD_OK) return rc;
+    const BwdWorkspace ws = bwd_layout(batch, seqlen, nheads, headdim, ngroups, nk, bf16);
+    const size_t need = bwd_need(ws, batch, seqlen, nheads, headdim, ngroups, dstate, nk, bf16);
+    if (!workspace || workspace_bytes < need) return SSD_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return SSD_ERR_WORKSPACE;
+    char *base = static_cast<char *>(workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (nk == dstate)
+        return status_of(backward_run(ws, x, dt, A, B, C, D, init_state, dy, dfinal_state, batch,
+                                      seqlen, nheads, ngroups, nk, bf16, dx, ddt, dA, dB, dC, dD,
+                                      dinit_state, ddt_bias, base, o, st, events));
+    // zero-padded to the kernels' state size (pad.hip): B, C and the states
+    // in, their gradients cut back to dstate. After the kernels' workspace:
+    // B', C', dB', dC' [Bt][L][G][nk] (input dtype), then the initial state,
+    // the final state's gradient and the initial state's gradient [Bt][H][P][nk]
+    const PadLayout pl = pad_layout(batch, seqlen, nheads, headdim, ngroups, nk, bf16);
+    char *pb = base + align_up(ws.total);
+    void *Bp = pb, *Cp = pb + pl.bc, *dBp = pb + 2 * pl.bc, *dCp = pb + 3 * pl.bc;
+    float *ip = reinterpret_cast<float *>(pb + 4 * pl.bc);
+    float *dfp = reinterpret_cast<float *>(pb + 4 * pl.bc + pl.st);
+    float *dip = reinterpret_cast<float *>(pb + 4 * pl.bc + 2 * pl.st);
+    const size_t bc_rows = (size_t)batch * seqlen * ngroups, st_rows = (size_t)batch * nheads * headdim;
+    const int es = bf16 ? 2 : 4;
+    hipError_t e = ssd::launch_pad_rows(B, Bp, bc_rows, dstate, nk, es, st);
+    if (e == hipSuccess) e = ssd::launch_pad_rows(C, Cp, bc_rows, dstate, nk, es, st);
+    if (e == hipSuccess && init_state)
+        e = ssd::launch_pad_rows(init_state, ip, st_rows, dstate, nk, 4, st);
+    if (e == hipSuccess && dfinal_state)
+        e = ssd::launch_pad_rows(dfinal_state, dfp, st_rows, dstate, nk, 4, st);
+    if (e == hipSuccess)
+        e = backward_run(ws, x, dt, A, Bp, Cp, D, init_state ? ip : nullptr, dy,
+                         dfinal_state ? dfp : nullptr, batch, seqlen, nheads, ngroups, nk, bf16,
+                         dx, ddt, dA, dBp, dCp, dD, dinit_state ? dip : nullptr, ddt_bias, base, o,
+                         st, events);
+    if (e == hipSuccess) e = ssd::launch_pad_rows(dBp, dB, bc_rows, nk, dstate, es, st);
+    if (e == hipSuccess) e = ssd::launch_pad_rows(dCp, dC, bc_rows, nk, dstate, es, st);
+    if (e == hipSuccess && dinit_state)
+        e = ssd::launch_pad_rows(dip, dinit_state, st_rows, nk, dstate, 4, st);
     return status_of(e);
 }
 

@@ -146,6 +146,18 @@ hipError_t launch_bwd_dt(const void *dt, const float *A, const float *ds, const 
 hipError_t launch_bwd_head_sum(const float *part, int nbc, int nheads, float *out,
                                hipStream_t stream);
 
+// State-size padding (pad.hip): the N the kernels run with for dstate (the
+// smallest of 16, 32, 64, 128, 256 not below it; 0 above 256), and a copy of
+// `rows` rows of src_cols elements into rows of dst_cols elements, zero-filled
+// past src_cols or cut to dst_cols (both column counts times elem_bytes must
+// be multiples of 16; src and dst 16-byte aligned).
+int kernel_dstate(int dstate);
+hipError_t launch_pad_rows(const void *src, void *dst, size_t rows, int src_cols, int dst_cols,
+                           int elem_bytes, hipStream_t stream);
+
+// dstate: any multiple of 16 up to 256 (the kernel for 16, 32, 64, 128, 256
+// keeps the state's rows in lanes that share them by powers of two; the other
+// sizes reduce each row's products through LDS).
 hipError_t launch_decode_step(float *state, const void *x, const void *dt, const float *A,
                               const void *B, const void *C, const float *D, int batch, int nheads,
                               int ngroups, int dstate, bool bf16, const DtOpts &opts, void *y,

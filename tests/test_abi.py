@@ -74,7 +74,8 @@ def _ws_expected(Bt, L, H, P, G, N, Q, dtype):
 class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("segments", ctypes.c_int), ("pieces", ctypes.c_int),
                 ("block_tokens", ctypes.c_int), ("segment_blocks", ctypes.c_int),
-                ("piece_blocks", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
+                ("piece_blocks", ctypes.c_int), ("kernel_dstate", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 def plan_info(lib, Bt, L, H, P, G, N, Q, dtype, dt=256):
@@ -155,7 +156,7 @@ def test_plan_info_sweep(lib):
 def test_plan_info_rejects(lib):
     rc, p = plan_info(lib, 0, 10, 8, 64, 1, 64, 64, 1)
     assert rc == SSD_ERR_SHAPE and p.workspace_bytes == 0
-    rc, _ = plan_info(lib, 1, 10, 8, 64, 1, 48, 64, 1)
+    rc, _ = plan_info(lib, 1, 10, 8, 64, 1, 40, 64, 1)
     assert rc == SSD_ERR_UNSUPPORTED
     assert ctypes.CDLL(LIB).ssd_forward_plan_info(1, 10, 8, 64, 1, 64, 64, 1, None, None) == SSD_ERR_NULL
 
@@ -171,7 +172,8 @@ def test_varlen_workspace_size(lib, dims):
 
 def test_workspace_size_invalid(lib):
     assert lib.ssd_forward_workspace_size(0, 10, 1, 64, 1, 16, 64, 1) == 0
-    assert lib.ssd_forward_workspace_size(1, 10, 1, 64, 1, 48, 64, 1) == 0
+    assert lib.ssd_forward_workspace_size(1, 10, 1, 64, 1, 40, 64, 1) == 0
+    assert lib.ssd_forward_workspace_size(1, 10, 1, 64, 1, 272, 64, 1) == 0
     assert lib.ssd_forward_workspace_size(1, 10, 1, 64, 1, 16, 0, 1) == 0
     assert lib.ssd_forward_workspace_size(1, 10, 1, 64, 1, 16, 64, 5) == 0
     assert lib.ssd_chunk_cb_size(1, 10, 1, 96, 1) == 0
@@ -198,7 +200,8 @@ def _fwd(lib, **kw):
     (dict(seqlen=0), SSD_ERR_SHAPE),
     (dict(nheads=6, ngroups=4), SSD_ERR_SHAPE),
     (dict(headdim=32), SSD_ERR_UNSUPPORTED),
-    (dict(dstate=48), SSD_ERR_UNSUPPORTED),
+    (dict(dstate=40), SSD_ERR_UNSUPPORTED),
+    (dict(dstate=272), SSD_ERR_UNSUPPORTED),
     (dict(chunk=96), SSD_ERR_UNSUPPORTED),
     (dict(dtype=7), SSD_ERR_UNSUPPORTED),
     (dict(x=ctypes.c_void_p(0x100002)), SSD_ERR_UNSUPPORTED),
@@ -344,8 +347,9 @@ def _bwd(lib, **kw):
     (dict(dA=None), SSD_ERR_NULL),
     (dict(Bt=0), SSD_ERR_SHAPE),
     (dict(H=6, G=4), SSD_ERR_SHAPE),
-    (dict(N=48), SSD_ERR_UNSUPPORTED),
+    (dict(N=40), SSD_ERR_UNSUPPORTED),
     (dict(dtype=0, N=128), SSD_ERR_UNSUPPORTED),   # float32 backward: N <= 64
+    (dict(dtype=0, N=96), SSD_ERR_UNSUPPORTED),    # ... padded to 128
     (dict(dx=ctypes.c_void_p(0x100008)), SSD_ERR_UNSUPPORTED),
     (dict(ws=None), SSD_ERR_WORKSPACE),
     (dict(wsb=4096), SSD_ERR_WORKSPACE),
@@ -399,7 +403,7 @@ def _static(lib, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), SSD_ERR_NULL),
     (dict(batch=0), SSD_ERR_SHAPE),
-    (dict(dstate=48), SSD_ERR_UNSUPPORTED),
+    (dict(dstate=40), SSD_ERR_UNSUPPORTED),
     (dict(opts=_opts(discretization=4)), SSD_ERR_OPTION),
     # the stage kernels' workspace for 8 x 2048 tokens x 80 heads in float32 is far
     # beyond the fixed 32 MiB array: refused before anything touches the GPU
@@ -410,3 +414,37 @@ def _static(lib, **kw):
 def test_forward_static_rejects(lib, kw, code):
     assert _static(lib, **kw) == code
     assert lib.ssd_strerror(SSD_ERR_TOO_LARGE) != b"unknown status"
+
+
+@pytest.mark.parametrize("N", [48, 80, 96, 112, 144, 160, 176, 192, 208, 224, 240])
+def test_plan_info_padded_dstate(lib, N):
+    """A state size outside 16, 32, 64, 128, 256 runs the kernels of the next
+    of these on zero-padded copies of B, C and the states: the plan names the
+    kernels' size, and the workspace is the kernels' own need plus the copies
+    (B' and C' in the input dtype, two float32 states)."""
+    al = lambda v: (v + 255) // 256 * 256
+    nk = next(k for k in (64, 128, 256) if N <= k)
+    for dims, dtype in (((8, 2048, 80, 64, 1), 1), ((1, 4096, 16, 64, 2), 1), ((2, 300, 4, 64, 2), 0)):
+        Bt, L, H, P, G = dims
+        rc, p = plan_info(lib, Bt, L, H, P, G, N, 128, dtype)
+        assert rc == SSD_OK and p.kernel_dstate == nk
+        rc, q = plan_info(lib, Bt, L, H, P, G, nk, 128, dtype)
+        assert (p.path, p.segments, p.pieces) == (q.path, q.segments, q.pieces)
+        e = 2 if dtype == 1 else 4
+        pad = 2 * al(Bt * L * G * nk * e) + 2 * al(Bt * H * P * nk * 4)
+        assert p.workspace_bytes == al(q.workspace_bytes) + pad
+        assert lib.ssd_forward_workspace_size(Bt, L, H, P, G, N, 128, dtype) == p.workspace_bytes
+    # the backward: its kernels' layout at nk plus B', C', dB', dC' and three states
+    Bt, L, H, P, G = 2, 300, 4, 64, 2
+    if nk <= 256:
+        w0 = lib.ssd_backward_workspace_size(Bt, L, H, P, G, nk, 1)
+        w1 = lib.ssd_backward_workspace_size(Bt, L, H, P, G, N, 1)
+        assert w1 == al(w0) + 4 * al(Bt * L * G * nk * 2) + 3 * al(Bt * H * P * nk * 4)
+
+
+def test_padded_dstate_kernel_sizes_only_on_stages_and_varlen(lib):
+    # the stage entry points and the packed forward take the kernels' sizes only
+    assert lib.ssd_chunk_cb(FAKE, FAKE, 1, 10, 1, 48, 64, 1, FAKE, None) == SSD_ERR_UNSUPPORTED
+    assert lib.ssd_chunk_state(FAKE, FAKE, FAKE, FAKE, 1, 10, 2, 64, 2, 96, 64, 1, FAKE, None) == SSD_ERR_UNSUPPORTED
+    assert _varlen(lib, N=48) == SSD_ERR_UNSUPPORTED
+    assert lib.ssd_forward_varlen_workspace_size(100, 4, 64, 1, 48, 64, 1) == 0

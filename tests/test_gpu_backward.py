@@ -156,3 +156,12 @@ def test_backward_errors():
     with pytest.raises(ValueError):
         ssd.backward(x, dt, A, B[..., :64].contiguous(), B[..., :64].contiguous(), None,
                      x[:, :5].contiguous())
+
+
+@pytest.mark.parametrize("dtype,N", [("bf16", 48), ("f32", 48), ("bf16", 96), ("bf16", 192)])
+def test_backward_padded_dstate(dtype, N):
+    # state sizes outside the kernels' set: B, C, the states zero-padded to the
+    # next kernel size, dB, dC and the initial state's gradient cut back
+    w = W.small(f"bwd_pad_{dtype}_N{N}", 2, 333, 4, 64, 2, N, 64, dtype, seed=1400 + N,
+                init_std=0.2)
+    check_backward(w)

@@ -5,6 +5,8 @@ compares relative L2 at the stated tolerances (1e-4 float32, 2e-2 bf16, 1e-3
 for the decode state). Each forward case is also run with D = 0, because the
 D x term dominates y and would otherwise hide errors in the SSM part.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -474,3 +476,39 @@ def test_varlen_workspace_canary():
     e = rel_l2(down(y)[0].transpose(1, 0, 2), y0)
     print_case(f"   rel_l2(y) = {e:.3e}")
     assert e < tol(w.dtype)
+
+
+# ------------------------------------- state sizes outside the kernels' own set
+#
+# Any multiple of 16 up to 256 runs the kernels of the next of 16, 32, 64,
+# 128, 256 on zero-padded copies of B, C and the states (the padded columns
+# add exact zeros). Cases reach the single-pass kernel (bf16, heads a multiple
+# of 8, with and without segments) and the stage kernels (float32, and bf16
+# with 4 heads), with an initial state and the final state compared.
+
+PADDED = [(48, "bf16", 8, 64), (48, "f32", 1, 4), (80, "bf16", 1, 16), (96, "bf16", 4, 4),
+          (112, "f32", 2, 4), (144, "bf16", 1, 8), (192, "bf16", 2, 32), (240, "bf16", 1, 4)]
+
+
+@pytest.mark.parametrize("N,dtype,Bt,H", PADDED, ids=[f"N{n}-{d}-B{b}-H{h}" for n, d, b, h in PADDED])
+def test_padded_dstate_forward(N, dtype, Bt, H):
+    w = W.small(f"pad_N{N}_{dtype}_B{Bt}_H{H}", Bt, 2 * 128 + 77, H, 64, 2, N, 128, dtype,
+                seed=1300 + N + Bt, init_std=0.2)
+    p = _ssd().plan_info(w.batch, w.seqlen, w.nheads, 64, w.ngroups, N, w.chunk,
+                         torch.bfloat16 if dtype == "bf16" else torch.float32)
+    print_case(f"   plan {p}")
+    assert p["kernel_dstate"] > N
+    check_forward(w)
+
+
+def test_padded_dstate_segments_with_options():
+    w = W.small("pad_seg_opts", 1, 3000, 8, 64, 2, 96, 256, "bf16", seed=1350, init_std=0.2)
+    assert plan(w) > 1
+    check_forward(w, both_D=False, **OPTION_SETS["all_zoh"])
+
+
+@pytest.mark.parametrize("N", [48, 96, 240])
+def test_padded_dstate_decode(N):
+    w = W.Workload(f"decode_N{N}", 8, 16, 8, 64, 2, N, 0, "bf16", 1 / math.sqrt(N), 1e-3, 1e-1,
+                   init_std=0.1, decode=True, seed=1360 + N)
+    _decode(w, zero_init=False, nunits=None)
