@@ -869,6 +869,8 @@ def main():
     ap.add_argument("--quick", action="store_true",
                     help="the headline only: skip the other workloads and the stage kernels")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="only the cold and warm forward of --workload (no JSON contract line)")
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 counter collection: a plain 1 GiB device copy "
                          "that calibrates the byte counters, a few forwards of --workload, and the "
@@ -943,6 +945,13 @@ def main():
     say(f"cold forward {ms * 1e3:.1f} us (median {f['median'] * 1e3:.1f}); " +
         ", ".join(f"{k} {v['us']:.1f} us" for k, v in kernels.items()))
 
+    if args.forward_only:
+        print(json.dumps({"workload": w.name, "cold_us": round(ms * 1e3, 2),
+                          "kernels": {k: {"us": v["us"], "hbm_frac": v["hbm_frac"]}
+                                      for k, v in kernels.items()},
+                          "warm_us": round(time_forward_warm(w, args.steps, 3) * 1e3, 2),
+                          "plan": plan_of(w)}), flush=True)
+        return
     warm_ms = time_forward_warm(w, args.steps, max(3, args.warmup // 4))
     warm = {"protocol": "back-to-back forwards over the same resident inputs, host clock around "
                         f"{args.steps} of them; inputs that fit in the 256 MB Infinity Cache are "

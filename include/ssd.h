@@ -145,7 +145,11 @@ typedef struct {
  * and only when S > 1: float32 [Bt][H][(S-1)K][P][N], the state each piece of
  * the first S-1 segments produces from a zero state, then float32
  * [Bt][H][(S-1)K], each piece's total log2-decay (sum of dt*A over the piece,
- * times log2(e)); with S == 1 no workspace is needed (NULL is accepted). On
+ * times log2(e)); when (S-1)K > 4 a chain pass then overwrites the slot of
+ * the last piece of each segment s-1 with the state entering segment s (the
+ * initial state carried through every earlier piece). With S == 1 no
+ * workspace is needed
+ * (NULL is accepted). On
  * the stage path it holds, at 256-byte aligned offsets in this order (with
  * N = kernel_dstate):
  *   dA_cumsum   float32 [Bt][H][nC*Q]      within-chunk prefix sums of dt*A

@@ -22,8 +22,9 @@
 // is cut into segments of whole blocks, one workgroup per (batch, head,
 // segment). A segment-state kernel first computes, for pieces of the earlier
 // segments, the state each piece produces from zero and its total decay; a
-// segment's workgroup starts from the initial state brought through those
-// pieces (H <- exp(d) H + H_piece: the same recurrence at a coarser grain).
+// chain kernel folds them (H <- exp(d) H + H_piece: the same recurrence at a
+// coarser grain) into the state entering each segment, from which that
+// segment's workgroup starts.
 // Packed sequences (VL) mask rows, pairs and the state update by each
 // token's first token of its sequence, and take each sequence's final state
 // at its last token.
@@ -191,7 +192,14 @@ struct OnepassSegs {
     int nseg, len, npc, kpc;
     float *state;  // float32 [Bt][H][npc][P][N]
     float *ld;     // float32 [Bt][H][npc]
+    int chained;   // the chain kernel has left each segment's entering state in
+                   // the slot of the last piece before it (else the single-pass
+                   // kernel folds the pieces itself)
 };
+
+// The chain kernel runs when the last segment would have more than this many
+// pieces to fold; below it the single-pass kernel folds them (one batch of loads).
+constexpr int kChainPieces = 4;
 
 // Packed sequences: the tokens' int4 (see VlTab) and each sequence's final
 // state, float32 [nseq][H][P][N].
@@ -330,24 +338,49 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
 #pragma unroll
     for (int nt = 0; nt < NTH; ++nt) {
         hreg[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-        if (init) {
+        if (init && (seg == 0 || !sg.chained)) {
             const float4 v =
                 *reinterpret_cast<const float4 *>(init + bh * P * N + hoff + 16 * nt);
             hreg[nt] = floatx4{v.x, v.y, v.z, v.w};
         }
     }
-    // H <- exp(d_j) H + H_j over the pieces j before this segment (the
-    // chunk-to-chunk recurrence at piece granularity, float32)
-    for (int j = 0; j < seg * sg.kpc; ++j) {  // uniform
-        const float f = __builtin_amdgcn_exp2f(sg.ld[bh * sg.npc + j]);
-        const float *sj = sg.state + (bh * sg.npc + j) * P * N + hoff;
+    // a later segment starts from the state the pieces before it pass on:
+    // left by the chain kernel in the slot of the last of those pieces, or
+    // (a few pieces) folded here, H <- exp(d_j) H + H_j, their loads issued
+    // together
+    if (seg > 0 && sg.chained) {  // uniform
+        const float *sj = sg.state + (bh * sg.npc + seg * sg.kpc - 1) * P * N + hoff;
 #pragma unroll
         for (int nt = 0; nt < NTH; ++nt) {
             const float4 v = *reinterpret_cast<const float4 *>(sj + 16 * nt);
-            hreg[nt][0] = hreg[nt][0] * f + v.x;
-            hreg[nt][1] = hreg[nt][1] * f + v.y;
-            hreg[nt][2] = hreg[nt][2] * f + v.z;
-            hreg[nt][3] = hreg[nt][3] * f + v.w;
+            hreg[nt] = floatx4{v.x, v.y, v.z, v.w};
+        }
+    } else if (seg > 0) {
+        const int nj = seg * sg.kpc;  // uniform, at most kChainPieces
+        float4 v[kChainPieces][NTH];
+        float f[kChainPieces];
+#pragma unroll
+        for (int j = 0; j < kChainPieces; ++j) {
+            if (j < nj) {
+                const float *sj = sg.state + (bh * sg.npc + j) * P * N + hoff;
+                f[j] = sg.ld[bh * sg.npc + j];
+#pragma unroll
+                for (int nt = 0; nt < NTH; ++nt)
+                    v[j][nt] = *reinterpret_cast<const float4 *>(sj + 16 * nt);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kChainPieces; ++j) {
+            if (j < nj) {
+                const float a = __builtin_amdgcn_exp2f(f[j]);
+#pragma unroll
+                for (int nt = 0; nt < NTH; ++nt) {
+                    hreg[nt][0] = hreg[nt][0] * a + v[j][nt].x;
+                    hreg[nt][1] = hreg[nt][1] * a + v[j][nt].y;
+                    hreg[nt][2] = hreg[nt][2] * a + v[j][nt].z;
+                    hreg[nt][3] = hreg[nt][3] * a + v[j][nt].w;
+                }
+            }
         }
     }
 
@@ -738,33 +771,51 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
 // For each piece of the first S-1 segments of a (batch, head): the state the
 // piece produces from a zero state, H = sum_t exp(s_end - s_t) w_t x_t B_t^T
 // (the single-pass kernel's state update, block by block), and the piece's
-// total log2-decay. Only x, B and dt are read. Every block's inputs are loaded
-// a whole block ahead into double buffers, issued as the block before starts,
-// so one barrier per block suffices (the single-pass kernel, short of LDS,
-// single-buffers B and issues it mid-block).
+// total log2-decay. Only x, B and dt are read. The blocks here are 32 tokens
+// (the pieces still hold whole 64-token blocks of the single-pass kernel): the
+// small LDS footprint fits five to six workgroups per compute unit, enough
+// for the loads of one to hide behind the others' work. Every block's inputs
+// are loaded a whole block ahead into double buffers, issued as the block
+// before starts, so one barrier per block suffices.
+// Tokens per block of the segment-state kernel: 32 where that lets five or
+// more workgroups share a compute unit; at N 256 (eight wavefronts, B rows of
+// 512 bytes) 64, one workgroup per compute unit.
+template <int N>
+constexpr int seg_states_block() {
+    return N == 256 ? 64 : 32;
+}
+
 template <int N, bool VL>
 struct SegStateLds {
-    __bf16 xb[2][kOpT * 64];
-    __bf16 bb[2][kOpT * N];
-    __bf16 dts[2][kOpT * 8];
+    static constexpr int TS = seg_states_block<N>();
+    __bf16 xb[2][TS * 64];
+    __bf16 bb[2][TS * N];
+    __bf16 dts[2][kOpT * 8];  // one 16-byte dt piece per lane (lanes past the block repeat its last)
     struct {
-        float wp[kOpT];
+        float wp[TS];
         float dec, ld;  // the state's decay across the block and its log2 (-inf: a reset)
     } tab[2];
     int4 mts[VL ? 2 : 1][VL ? kOpT : 1];  // packed sequences: the tokens' int4 of blocks k, k+1
 };
 
+// Workgroups per compute unit of the segment-state kernel (its launch bounds
+// and the plan's count of how many fill the GPU).
+template <int N>
+constexpr int seg_states_per_cu() {
+    return N == 64 ? 7 : N == 128 ? 5 : 1;
+}
+
 template <int N, bool VL>
-__global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 4 : N == 128 ? 3 : 1) void ssd_segment_states_kernel(
+__global__ __launch_bounds__(N == 256 ? 512 : 256, seg_states_per_cu<N>()) void ssd_segment_states_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ dt, const float *__restrict__ A,
     const bf16_t *__restrict__ B, DtOpts o, int batch, int L, int H, int G, int per,
     OnepassSegs sg, OnepassVl vl) {
-    constexpr int P = 64, T = kOpT;
+    constexpr int P = 64, T = seg_states_block<N>();
     constexpr int PPR = N / 8, NT = N / 16;
     // N 256: eight wavefronts, w and w + 4 with halves of the state's n
     constexpr bool HALVES = N == 256;
     constexpr int NWV = HALVES ? 8 : 4, NTH = HALVES ? NT / 2 : NT;
-    static_assert(N % 32 == 0 && T * PPR >= 256, "state size");
+    static_assert(N % 32 == 0 && T * PPR >= 64 && T * 8 % 64 == 0, "state size");
     __shared__ __attribute__((aligned(16))) SegStateLds<N, VL> sm;
 
     // workgroup -> (batch, piece, head), XCD-aware as in the single-pass kernel
@@ -799,7 +850,7 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 4 : N == 128 ? 3 : 
         if (w == 0 && k + 1 < nblk) issue_dt(k + 1);
         const bf16_t *xk = xh + (size_t)t0 * xrow, *bk = bg + (size_t)t0 * brow;
 #pragma unroll
-        for (int i = w; i < 8; i += NWV) {
+        for (int i = w; i < T * 8 / 64; i += NWV) {
             const int s = i * 64 + l, r = s >> 3, q = (s & 7) ^ (r & 7);
             dma16_sv(xk, (uint32_t)min(r, len - 1) * xrb + q * 16, sm.xb[k & 1] + i * 512);
         }
@@ -809,7 +860,8 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 4 : N == 128 ? 3 : 
             dma16_sv(bk, (uint32_t)min(r, len - 1) * brb + q * 16, sm.bb[k & 1] + i * 512);
         }
     };
-    // block k's prefix sums and state weights (wavefront 0; lane j is token t0 + j)
+    // block k's prefix sums and state weights (wavefront 0; lane j is token
+    // t0 + j, lanes past the block add zero terms)
     auto make_tables = [&](int k) {
         const int len = min(T, Lw - k * T);
         const bool valid = l < len;
@@ -826,7 +878,7 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 4 : N == 128 ? 3 : 
             if (l < fsl) wp = 0.0f;
             reset = fsl >= 0;
         }
-        sm.tab[k & 1].wp[l] = wp;
+        if (l < T) sm.tab[k & 1].wp[l] = wp;
         if (l == 0) {
             sm.tab[k & 1].dec = reset ? 0.0f : __builtin_amdgcn_exp2f(sle);
             sm.tab[k & 1].ld = reset ? -__builtin_inff() : sle;
@@ -839,6 +891,7 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 4 : N == 128 ? 3 : 
     float ld = 0.0f;  // the piece's log2-decay so far
     int xo[4];
     x_colfrag_offsets(xo, l);
+    const int jb = 4 * g4;
 
     if (w == 0) issue_dt(0);
     issue(0);
@@ -857,18 +910,18 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 4 : N == 128 ? 3 : 
         ld += sm.tab[k & 1].ld;
 
         // H^T = exp(s_end) H^T + sum_j B_j (exp(s_end - s_j) w_j x_j)^T, p tile w
-        Frag<bf16_t> xr[2];
+        Frag<bf16_t> xr[T / 32];
         x_colfrag<0>(xr[0], xs, xo[wr]);
-        x_colfrag<1>(xr[1], xs, xo[wr]);
+        if constexpr (T == 64) x_colfrag<1>(xr[T / 32 - 1], xs, xo[wr]);
 #pragma unroll
         for (int nt = 0; nt < NTH; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) hreg[nt][r] *= dec;
 #pragma unroll
-        for (int js = 0; js < 2; ++js) {
-            const int jb = 32 * js + 4 * g4;
-            const floatx4 p0 = *reinterpret_cast<const floatx4 *>(twp + jb);
-            const floatx4 p1 = *reinterpret_cast<const floatx4 *>(twp + jb + 16);
+        for (int js = 0; js < T / 32; ++js) {
+            const int jj = 32 * js + jb;
+            const floatx4 p0 = *reinterpret_cast<const floatx4 *>(twp + jj);
+            const floatx4 p1 = *reinterpret_cast<const floatx4 *>(twp + jj + 16);
             float v[8];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -880,7 +933,7 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 4 : N == 128 ? 3 : 
 #pragma unroll
             for (int nt = 0; nt < NTH; ++nt) {
                 Frag<bf16_t> bf;
-                colfrag_swz<PPR>(bf, bs_, jb, jb + 16, (nh * NTH + nt) * 16);
+                colfrag_swz<PPR>(bf, bs_, jj, jj + 16, (nh * NTH + nt) * 16);
                 mma(hreg[nt], bf, xw);
             }
         }
@@ -895,6 +948,53 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 4 : N == 128 ? 3 : 
         *reinterpret_cast<float4 *>(sj + 16 * nt) =
             make_float4(hreg[nt][0], hreg[nt][1], hreg[nt][2], hreg[nt][3]);
     if (w == 0 && l == 0) sg.ld[bh * sg.npc + pc] = ld;
+}
+
+// ---- the chain over the pieces
+//
+// For every (batch, head) and segment s = 1 .. S-1: the state entering the
+// segment, E_s = fold over the pieces j < s k of E <- exp2(ld_j) E + H_j,
+// from the initial state (or zero): the chunk-to-chunk recurrence at piece
+// granularity, float32, each thread one float4 of one (batch, head)'s state.
+// E_s overwrites the slot of piece s k - 1, which this thread has read by
+// then; the single-pass kernel reads it from there.
+__global__ __launch_bounds__(256) void ssd_segment_chain_kernel(const float *__restrict__ init,
+                                                                OnepassSegs sg, int units, int PN) {
+    const int q4 = PN / 4;
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)units * q4) return;
+    const size_t u = idx / q4, e = idx - u * q4;
+    floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (init) {
+        const float4 v = reinterpret_cast<const float4 *>(init + u * PN)[e];
+        acc = floatx4{v.x, v.y, v.z, v.w};
+    }
+    float4 *st = reinterpret_cast<float4 *>(sg.state + u * sg.npc * PN) + e;
+    const float *ld = sg.ld + u * sg.npc;
+    const int np = (sg.nseg - 1) * sg.kpc;
+    // pieces in batches of eight: their loads issued together, then folded in order
+    for (int j0 = 0; j0 < np; j0 += 8) {
+        float4 v[8];
+        float f[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            if (j0 + q < np) {
+                v[q] = st[(size_t)(j0 + q) * q4];
+                f[q] = ld[j0 + q];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int j = j0 + q;
+            if (j < np) {
+                const float a = __builtin_amdgcn_exp2f(f[q]);
+                acc = floatx4{acc[0] * a + v[q].x, acc[1] * a + v[q].y, acc[2] * a + v[q].z,
+                              acc[3] * a + v[q].w};
+                if ((j + 1) % sg.kpc == 0)  // the last piece of a segment
+                    st[(size_t)j * q4] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            }
+        }
+    }
 }
 
 bool forward_onepass_ok(int batch, int nheads, int dstate, bool bf16, const void *dt) {
@@ -923,7 +1023,10 @@ size_t piece_bytes(int dstate) { return (64 * (size_t)dstate + 1) * sizeof(float
 // what that needs lowers k, then gives up the segments.
 OnepassPlan forward_onepass_plan(int batch, int seqlen, int nheads, int dstate, size_t cap) {
     const int slots = (dstate == 64 ? 3 : dstate == 128 ? 2 : 1) * 256,
-              so_slots = (dstate == 64 ? 4 : dstate == 128 ? 3 : 1) * 256;
+              so_slots = (dstate == 64    ? seg_states_per_cu<64>()
+                          : dstate == 128 ? seg_states_per_cu<128>()
+                                          : seg_states_per_cu<256>()) *
+                         256;
     const size_t units = (size_t)batch * nheads;
     const int blocks = (seqlen + kOpT - 1) / kOpT;
     const OnepassPlan one{1, 0, blocks, blocks, 0};
@@ -932,7 +1035,13 @@ OnepassPlan forward_onepass_plan(int batch, int seqlen, int nheads, int dstate, 
     if (S0 <= 1) return one;
     const int per = (blocks + S0 - 1) / S0;
     const size_t max_pieces = cap / piece_bytes(dstate);
-    int k = std::max(1, std::min((int)(so_slots / (units * (S0 - 1))), per / 2));
+    const int kmax = std::max(1, std::min((int)(so_slots / (units * (S0 - 1))), per / 2));
+    // the k <= kmax that pads the segments least (k * ceil(per / k) blocks),
+    // the largest of those: pieces of equal length, segments as even as the
+    // sequence allows
+    int k = 1;
+    for (int kk = 1; kk <= kmax; ++kk)
+        if (kk * ((per + kk - 1) / kk) <= k * ((per + k - 1) / k)) k = kk;
     for (;;) {
         const int psub = (per + k - 1) / k, per_seg = k * psub;
         const int S = (blocks + per_seg - 1) / per_seg;  // the last segment is not empty
@@ -957,17 +1066,25 @@ static hipError_t launch_onepass_n(const void *x, const void *dt, const float *A
     const auto Cb = static_cast<const bf16_t *>(C);
     const int npc = pl.S > 1 ? (pl.S - 1) * pl.k : 0;
     float *ld = npc ? scratch + (size_t)batch * nheads * npc * 64 * N : nullptr;
+    const int chained = npc > kChainPieces;  // the last segment folds npc pieces
     if (pl.S > 1) {
-        const OnepassSegs pieces{npc, pl.psub * kOpT, npc, 0, scratch, ld};
+        const OnepassSegs pieces{npc, pl.psub * kOpT, npc, 0, scratch, ld, 0};
         const int units = batch * nheads * npc;
         const int per = (units + 7) / 8;
         ssd_segment_states_kernel<N, VL><<<per * 8, N == 256 ? 512 : 256, 0, stream>>>(
             xb, dtb, A, Bb, opts, batch, seqlen, nheads, ngroups, per, pieces, vl);
         hipError_t e = hipGetLastError();
+        if (e == hipSuccess && chained) {
+            const OnepassSegs chain{pl.S, 0, npc, pl.k, scratch, ld, 1};
+            const size_t threads = (size_t)batch * nheads * 64 * N / 4;
+            ssd_segment_chain_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(
+                init, chain, batch * nheads, 64 * N);
+            e = hipGetLastError();
+        }
         if (e == hipSuccess && between) e = hipEventRecord(between, stream);
         if (e != hipSuccess) return e;
     }
-    const OnepassSegs segs{pl.S, pl.per_seg * kOpT, npc, pl.k, scratch, ld};
+    const OnepassSegs segs{pl.S, pl.per_seg * kOpT, npc, pl.k, scratch, ld, chained};
     const int units = batch * nheads * pl.S;
     const int per = (units + 7) / 8;
     ssd_forward_onepass_kernel<N, VL><<<per * 8, N == 256 ? 512 : 256, 0, stream>>>(
