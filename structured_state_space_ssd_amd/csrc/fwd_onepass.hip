@@ -118,6 +118,7 @@ struct OnepassLds {
     // N 256: the second half-N wavefront of each tile pair hands its partial
     // outputs over here ([row tile][head-dim tile][lane])
     floatx4 xch[N == 256 ? 16 : 1][N == 256 ? 64 : 1];
+    int touch[64];  // written by the L2 touches of B and C, never read
 };
 
 // One 16-byte-per-lane global-to-LDS load from the wave-uniform base `sbase`
@@ -128,6 +129,16 @@ __device__ __forceinline__ void dma16_sv(const void *sbase, uint32_t voff, const
     const uint32_t a =
         __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)lds_base);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(a)
+                 : "memory", "m0");
+}
+
+// The same with 4 bytes per lane (lane l's word lands at lds_base + 4 l).
+__device__ __forceinline__ void dma4_sv(const void *sbase, uint32_t voff, const void *lds_base) {
+    const uint32_t a =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)lds_base);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                  :
                  : "v"(voff), "s"(sbase), "s"(a)
                  : "memory", "m0");
@@ -450,6 +461,17 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
         } else {
             wait_barrier<0>();
             if (k + 1 < nblk) issue_x(k + 1);
+        }
+        // B and C rows two blocks ahead are touched (one 4-byte direct load
+        // per 128-byte line into a scratch LDS word, wavefronts 1 and 2 of
+        // every eighth head of a group) so that their loads a block later
+        // find them in L2
+        if ((w == 1 || w == 2) && k + 2 < nblk && ((h % (H / G)) & 7) == 0) {  // uniform
+            const int tp = t0 + 2 * T, lenp = min(T, Lw - tp);
+            const bf16_t *src = (w == 1 ? bg : cg) + (size_t)tp * brow;
+            const uint32_t off = (uint32_t)min(l, lenp - 1) * brb;
+#pragma unroll
+            for (int q = 0; q < N / 64; ++q) dma4_sv(src + 64 * q, off, sm.touch);
         }
         const __bf16 *xs = sm.xb[k % NXB];
         if (k == 0) {  // later blocks' tables are made during the block before
