@@ -668,7 +668,7 @@ UTIL_CMDS = ('rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil --output-format csv -d "
              '-- python bench.py --counters --workload $WL')
 # kernel-name fragment -> kernel, first match wins (the fused stage-2+3 kernel
 # fills the chunk_state interval of the forward)
-KERNEL_OF = {"segment_states_kernel": "segment_states",
+KERNEL_OF = {"segment_states_kernel": "segment_states", "segment_chain_kernel": "segment_chain",
              "ssd_forward_onepass": "forward_onepass", "onepass_varlen_prep": "packed: token int4s",
              "chunk_cumsum_kernel": "chunk_cumsum", "chunk_state_passing": "chunk_state",
              "state_passing_kernel": "state_passing", "chunk_state": "chunk_state",
