@@ -804,7 +804,7 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
 // 512 bytes) 64, one workgroup per compute unit.
 template <int N>
 constexpr int seg_states_block() {
-    return N == 256 ? 64 : 32;
+    return N == 128 ? 32 : 64;
 }
 
 template <int N, bool VL>
@@ -824,7 +824,7 @@ struct SegStateLds {
 // and the plan's count of how many fill the GPU).
 template <int N>
 constexpr int seg_states_per_cu() {
-    return N == 64 ? 7 : N == 128 ? 5 : 1;
+    return N == 64 ? 4 : N == 128 ? 5 : 1;
 }
 
 template <int N, bool VL>

@@ -229,10 +229,13 @@ def test_errors_raise_before_launch():
     B = torch.zeros((1, 10, 2, 64), dtype=torch.bfloat16, device="cuda")  # 3 heads, 2 groups
     with pytest.raises(ssd.SSDError):
         ssd.forward(x, dt, A, B, B.clone(), chunk=64)
-    B1 = torch.zeros((1, 10, 1, 48), dtype=torch.bfloat16, device="cuda")  # unsupported N
+    B1 = torch.zeros((1, 10, 1, 40), dtype=torch.bfloat16, device="cuda")  # N not a multiple of 16
     with pytest.raises(ssd.SSDError):
         ssd.forward(x, dt, A, B1, B1.clone(), chunk=64)
     with pytest.raises(ssd.SSDError):
         ssd.forward(x, dt, A, B1[..., :32].contiguous(), B1[..., :32].contiguous(), chunk=96)
+    B2 = torch.zeros((1, 10, 1, 272), dtype=torch.bfloat16, device="cuda")  # N above 256
+    with pytest.raises(ssd.SSDError):
+        ssd.forward(x, dt, A, B2, B2.clone(), chunk=64)
     with pytest.raises(TypeError):
         ssd.forward(x.half(), dt.half(), A, B1, B1, chunk=64)
