@@ -60,12 +60,12 @@
 //   C B^T     the row tile's causal tiles (slices j <= i), decayed by
 //             exp(s_i - s_j) w_j (below the diagonal as exp(s_i - s_31) times
 //             a per-token column factor), masked, kept in registers as the
-//             B operand of Y^T += X^T M^T over every head-dim tile; D x as
-//             X^T diag(D) (D split into two bf16 parts) on the diagonal slice;
+//             B operand of Y^T += X^T M^T over every head-dim tile;
 //   state     H^T = exp(s_end) H^T + B^T (w' o x) on MFMA for the
 //             wavefront's columns;
 //   -- barrier: B, C, dt buffers free; next loads issued; H to LDS in bf16 --
-//   outputs   this wavefront's 16 rows staged in the block's x buffer and
+//   outputs   this wavefront's 16 rows, D x added in float32 from the x
+//             elements they overwrite, staged in the block's x buffer and
 //             read back as whole 128-byte rows by the same wavefront (no
 //             barrier), stored (non-temporal) during the next block.
 #include <algorithm>
@@ -404,32 +404,6 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
     x_colfrag_offsets(xo, l);
     const int i = 16 * wr + cc;  // this lane's output token: row tile wr is rows 16wr..16wr+15
 
-    // D x on MFMA: Y^T += X^T diag(D) over the slice holding the row tile's
-    // diagonal, with D split as D_hi + D_lo (bf16 each, 16 mantissa bits in
-    // all; both products exact in float32). B-operand lane (g4, cc) is column
-    // i; its element e is token 32 js + 4 g4 + e (e < 4) or 32 js + 16 + 4 g4
-    // + e - 4, which is i for element cc - 4 g4 (w even) or 4 + cc - 4 g4
-    // (w odd) when 0 <= cc - 4 g4 < 4.
-    Frag<bf16_t> dfr[2];  // hi, lo
-    bf16x4 dfr4[2];       // N 256: the same for the k = 16 half holding the diagonal
-    {
-        const __bf16 dhi = static_cast<__bf16>(Dh);
-        const __bf16 dlo = static_cast<__bf16>(Dh - static_cast<float>(dhi));
-        const int e0 = cc - 4 * g4;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const bool on = e == ((wr & 1) ? 4 + e0 : e0) && e0 >= 0 && e0 < 4;
-            dfr[0].v[e] = on ? dhi : static_cast<__bf16>(0.0f);
-            dfr[1].v[e] = on ? dlo : static_cast<__bf16>(0.0f);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bool on = e == e0;
-            dfr4[0][e] = on ? dhi : static_cast<__bf16>(0.0f);
-            dfr4[1][e] = on ? dlo : static_cast<__bf16>(0.0f);
-        }
-    }
-
     // the state (bf16) into LDS for the next state-to-output product: this
     // wavefront's columns p = 16 w + cc, 4 consecutive n per accumulator tile
     auto put_h = [&]() {
@@ -576,10 +550,6 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
                 for (int pt = 0; pt < 4; ++pt) {
                     const bf16x4 xf = x_colfrag_half(xsl, xo[pt]);
                     mma16(acc[pt], xf, mf);
-                    if (diag && D && nh == (wr & 1)) {  // uniform: the half holding i
-                        mma16(acc[pt], xf, dfr4[0]);
-                        mma16(acc[pt], xf, dfr4[1]);
-                    }
                 }
                 continue;
             }
@@ -628,17 +598,13 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
             }
             Frag<bf16_t> mf;
             pack8(mf, v);
-            // Y^T[p][i] += sum_j x_j[p] M[i][j] (and D x on the diagonal slice)
+            // Y^T[p][i] += sum_j x_j[p] M[i][j]
             const __bf16 *xsl = xs + js * 2048;
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) {
                 Frag<bf16_t> xf;
                 x_colfrag<0>(xf, xsl, xo[pt]);
                 mma(acc[pt], xf, mf);
-                if (diag && D) {  // uniform
-                    mma(acc[pt], xf, dfr[0]);
-                    mma(acc[pt], xf, dfr[1]);
-                }
             }
         }
 
@@ -756,11 +722,19 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
                 for (int r = 0; r < 4; ++r) acc[pt][r] += o[r];
             }
         }
-        // ---- the outputs: this wavefront's rows, every column, into the x buffer
+        // ---- the outputs: this wavefront's rows, every column, into the x
+        // buffer, each over the x element of its own (token, column), which
+        // gives D x first (float32)
         __bf16 *xw_ = sm.xb[k % NXB];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
             const int off = x_at(i, 16 * pt + 4 * g4);
+            if (D) {  // uniform
+                const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xw_ + off);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[pt][r] = __builtin_fmaf(Dh, static_cast<float>(xv[r]), acc[pt][r]);
+            }
             const bf16x2 lo = __builtin_convertvector(floatx2{acc[pt][0], acc[pt][1]}, bf16x2);
             const bf16x2 hi = __builtin_convertvector(floatx2{acc[pt][2], acc[pt][3]}, bf16x2);
             *reinterpret_cast<bf16x4 *>(xw_ + off) = bf16x4{lo[0], lo[1], hi[0], hi[1]};
