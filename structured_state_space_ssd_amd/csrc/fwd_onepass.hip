@@ -60,12 +60,12 @@
 //   C B^T     the row tile's causal tiles (slices j <= i), decayed by
 //             exp(s_i - s_j) w_j (below the diagonal as exp(s_i - s_31) times
 //             a per-token column factor), masked, kept in registers as the
-//             B operand of Y^T += X^T M^T over every head-dim tile;
+//             B operand of Y^T += X^T M^T over every head-dim tile; D added
+//             to M on the diagonal (j = i), so that the product carries D x;
 //   state     H^T = exp(s_end) H^T + B^T (w' o x) on MFMA for the
 //             wavefront's columns;
 //   -- barrier: B, C, dt buffers free; next loads issued; H to LDS in bf16 --
-//   outputs   this wavefront's 16 rows, D x added in float32 from the x
-//             elements they overwrite, staged in the block's x buffer and
+//   outputs   this wavefront's 16 rows staged in the block's x buffer and
 //             read back as whole 128-byte rows by the same wavefront (no
 //             barrier), stored (non-temporal) during the next block.
 #include <algorithm>
@@ -404,6 +404,28 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
     x_colfrag_offsets(xo, l);
     const int i = 16 * wr + cc;  // this lane's output token: row tile wr is rows 16wr..16wr+15
 
+    // D on the diagonal slice (js = wr / 2) where j = i, added to M there so
+    // that M x carries D x: lane (g4, cc) holds the slice's elements j = 32 js
+    // + 4 g4 + e (e < 4) and 32 js + 12 + 4 g4 + e (e >= 4) of column i (N
+    // 256: the wavefront's half nh of the slice, elements 4 nh + r)
+    float dval[HALVES ? 4 : 8];
+#pragma unroll
+    for (int e = 0; e < (HALVES ? 4 : 8); ++e) {
+        const int ee = HALVES ? 4 * nh + e : e;
+        const int j = 32 * (wr >> 1) + 4 * g4 + (ee < 4 ? ee : 12 + ee);
+        dval[e] = j == i ? Dh : 0.0f;
+    }
+    // this lane's two 16-byte pieces of its rows' outputs: byte offsets from
+    // the block's first output row
+    uint32_t yoff[2];
+    int yrow[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int s = 128 * wr + 64 * m + l, r = s >> 3, q = (s & 7) ^ (r & 7);
+        yrow[m] = r;
+        yoff[m] = (uint32_t)((r * xrow + q * 8) * 2);
+    }
+
     // the state (bf16) into LDS for the next state-to-output product: this
     // wavefront's columns p = 16 w + cc, 4 consecutive n per accumulator tile
     auto put_h = [&]() {
@@ -498,11 +520,9 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
         // ---- the previous block's outputs leave here, between compute phases
         // (a full block: every row is in range)
         if (k > 0 && nh == 0) {
+            char *yb = reinterpret_cast<char *>(yh + (size_t)(t0 - T) * xrow);
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int s = 128 * wr + 64 * m + l, r = s >> 3, q = (s & 7) ^ (r & 7);
-                store_nt16(yh + (size_t)(t0 - T + r) * xrow + q * 8, ystage[m]);
-            }
+            for (int m = 0; m < 2; ++m) store_nt16(yb + yoff[m], ystage[m]);
         }
 
         // ---- the row tile's causal C B^T tiles (slices js <= w / 2), kept in
@@ -532,8 +552,10 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
                     const floatx4 w0 = *reinterpret_cast<const floatx4 *>(twt + jh);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float a0 = m[r] * (__builtin_amdgcn_exp2f(si - s0[r]) * w0[r]);
-                        v[r] = jh + r <= i && (!VL || jh + r >= fsi) ? a0 : 0.0f;
+                        const float a0 = __builtin_fmaf(
+                            m[r], __builtin_amdgcn_exp2f(si - s0[r]) * w0[r], dval[r]);
+                        const bool on = jh + r <= i && (!VL || jh + r >= fsi);
+                        v[r] = on ? a0 : 0.0f;
                     }
                 } else {
                     const float rowf = __builtin_amdgcn_exp2f(si - s31);
@@ -568,17 +590,21 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
             // lane (g4, cc): rows j = 32 js + 16 half + 4 g4 + r of column i
             float v[8];
             if (diag) {
-                // holds the diagonal: exp per element, causal mask
+                // holds the diagonal: exp per element, causal mask, D on j = i
                 const floatx4 s0 = *reinterpret_cast<const floatx4 *>(tsl + j0);
                 const floatx4 s1 = *reinterpret_cast<const floatx4 *>(tsl + j0 + 16);
                 const floatx4 w0 = *reinterpret_cast<const floatx4 *>(twt + j0);
                 const floatx4 w1 = *reinterpret_cast<const floatx4 *>(twt + j0 + 16);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float a0 = m[0][r] * (__builtin_amdgcn_exp2f(si - s0[r]) * w0[r]);
-                    const float a1 = m[1][r] * (__builtin_amdgcn_exp2f(si - s1[r]) * w1[r]);
-                    v[r] = j0 + r <= i && (!VL || j0 + r >= fsi) ? a0 : 0.0f;
-                    v[4 + r] = j0 + 16 + r <= i && (!VL || j0 + 16 + r >= fsi) ? a1 : 0.0f;
+                    const float a0 = __builtin_fmaf(
+                        m[0][r], __builtin_amdgcn_exp2f(si - s0[r]) * w0[r], dval[r]);
+                    const float a1 = __builtin_fmaf(
+                        m[1][r], __builtin_amdgcn_exp2f(si - s1[r]) * w1[r], dval[4 + r]);
+                    const bool on0 = j0 + r <= i && (!VL || j0 + r >= fsi);
+                    const bool on1 = j0 + 16 + r <= i && (!VL || j0 + 16 + r >= fsi);
+                    v[r] = on0 ? a0 : 0.0f;
+                    v[4 + r] = on1 ? a1 : 0.0f;
                 }
             } else {
                 // wholly below it (i >= 32 > j): exp(s_i - s_31) exp(s_31 - s_j) w_j,
@@ -722,19 +748,11 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
                 for (int r = 0; r < 4; ++r) acc[pt][r] += o[r];
             }
         }
-        // ---- the outputs: this wavefront's rows, every column, into the x
-        // buffer, each over the x element of its own (token, column), which
-        // gives D x first (float32)
+        // ---- the outputs: this wavefront's rows, every column, into the x buffer
         __bf16 *xw_ = sm.xb[k % NXB];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
             const int off = x_at(i, 16 * pt + 4 * g4);
-            if (D) {  // uniform
-                const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(xw_ + off);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[pt][r] = __builtin_fmaf(Dh, static_cast<float>(xv[r]), acc[pt][r]);
-            }
             const bf16x2 lo = __builtin_convertvector(floatx2{acc[pt][0], acc[pt][1]}, bf16x2);
             const bf16x2 hi = __builtin_convertvector(floatx2{acc[pt][2], acc[pt][3]}, bf16x2);
             *reinterpret_cast<bf16x4 *>(xw_ + off) = bf16x4{lo[0], lo[1], hi[0], hi[1]};
@@ -747,11 +765,10 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
     }
     if (nh == 0) {  // the last block's outputs (possibly a partial block)
         const int t0 = (nblk - 1) * T, len = Lw - t0;
+        char *yb = reinterpret_cast<char *>(yh + (size_t)t0 * xrow);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int s = 128 * wr + 64 * m + l, r = s >> 3, q = (s & 7) ^ (r & 7);
-            if (r < len) store_nt16(yh + (size_t)(t0 + r) * xrow + q * 8, ystage[m]);
-        }
+        for (int m = 0; m < 2; ++m)
+            if (yrow[m] < len) store_nt16(yb + yoff[m], ystage[m]);
     }
 
     if (final_state && seg == nseg - 1) {
@@ -994,10 +1011,11 @@ __global__ __launch_bounds__(256) void ssd_segment_chain_kernel(const float *__r
 }
 
 bool forward_onepass_ok(int batch, int nheads, int dstate, bool bf16, const void *dt) {
-    // dt is read as 16-byte pieces of 8 heads
+    // dt is read as 16-byte pieces of 8 heads; a block's byte offsets into x
+    // and y (64 rows of nheads * 64 bf16) are 32-bit
     (void)batch;
     return bf16 && (dstate == 64 || dstate == 128 || dstate == 256) && nheads % 8 == 0 &&
-           (reinterpret_cast<uintptr_t>(dt) & 15u) == 0;
+           nheads < (1 << 19) && (reinterpret_cast<uintptr_t>(dt) & 15u) == 0;
 }
 
 namespace {
