@@ -97,7 +97,7 @@ struct BwdLds {
     static constexpr int LDB = colfrag_stride(N, sizeof(E));
     static constexpr size_t kBytes =
         sizeof(E) * ((size_t)2 * Q * LDX + (size_t)2 * Q * LDB + (size_t)2 * P * LDB) +
-        2 * Q * sizeof(float) + 16;
+        4 * Q * sizeof(float) + 16;
 };
 
 template <typename T, int N, int Q>
@@ -124,6 +124,11 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
     __shared__ __attribute__((aligned(32))) E gs[P * LDB];
     __shared__ __attribute__((aligned(16))) float slt[Q];  // s * log2(e)
     __shared__ __attribute__((aligned(16))) float wt[Q];   // input weights (0 past the end)
+    // per token t, within its 32-token slice [r, e]: exp(s_t - s_r) and
+    // exp(s_e - s_t) w_t (both <= 1), the column and row factors of the decay
+    // between tokens of different slices
+    __shared__ __attribute__((aligned(16))) float p1t[Q];
+    __shared__ __attribute__((aligned(16))) float p2t[Q];
     __shared__ float red[4];
 
     const int kb = blockIdx.x % nblk, u = blockIdx.x / nblk;
@@ -211,9 +216,13 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
                 *reinterpret_cast<uint4 *>(gs + p * LDB + q * EPP) = pg[i];
             }
         }
-        if (tid < Q) {
-            slt[tid] = ps * kLog2e;
+        if (tid < Q) {  // whole wavefronts; a slice's tokens share one
+            const float sl = ps * kLog2e;
+            slt[tid] = sl;
             wt[tid] = pw;
+            const float sr = __shfl(sl, l & ~31), se = __shfl(sl, l | 31);
+            p1t[tid] = __builtin_amdgcn_exp2f(sl - sr);
+            p2t[tid] = __builtin_amdgcn_exp2f(se - sl) * pw;
         }
         const float Dh = pD;
         const size_t srow = ((size_t)b * H + h) * (size_t)nC * Q + (size_t)c * Q;
@@ -264,8 +273,9 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) dxT[pt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
         float cin = 0.0f, cex = 0.0f;  // column sums of e^{s_i-s_j} CB DX (with / without i = j)
-        for (int sl = w / 2; sl < Q / 32; ++sl) {
-            floatx4 dxo[2], cbo[2];
+        float cfar = 0.0f;             // the part of both from slices after tok's
+        // a slice's dy_i.x_j and C_i.B_j blocks, rows i of the slice, column tok
+        auto p1_blocks = [&](int sl, floatx4 (&dxo)[2], floatx4 (&cbo)[2]) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int ir = 32 * sl + 16 * half + c16;  // A-operand row (token i)
@@ -285,6 +295,25 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
                     mma(cbo[half], fa, own_b(kk));
                 }
             }
+        };
+        auto p1_products = [&](int sl, const Frag<T> &mf, const Frag<T> &ef) {
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                Frag<T> fa;  // dy^T: rows p = 16pt + c16, contraction over the slice's tokens
+                lds_colfrag(fa, dys, LDX, 32 * sl + 4 * g4, 32 * sl + 16 + 4 * g4, pt * 16);
+                mma(dxT[pt], fa, mf);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                Frag<T> fa;  // C^T: rows n = 16nt + c16
+                lds_colfrag(fa, cs, LDB, 32 * sl + 4 * g4, 32 * sl + 16 + 4 * g4, nt * 16);
+                mma(dBT[nt], fa, ef);
+            }
+        };
+        {  // the slice holding tok: exp per element, mask i >= tok
+            const int sl = w / 2;
+            floatx4 dxo[2], cbo[2];
+            p1_blocks(sl, dxo, cbo);
             // element (half, e): token i = 32 sl + 16 half + 4 g4 + e, column j = tok
             Frag<T> mf, ef;
 #pragma unroll
@@ -303,18 +332,29 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
                     ef.set(4 * half + e, lij * dxo[half][e] * w_t);
                 }
             }
+            p1_products(sl, mf, ef);
+        }
+        for (int sl = w / 2 + 1; sl < Q / 32; ++sl) {
+            // every i > tok: e^{s_i - s_tok} = e^{s_i - s_r} e^{s_r - s_tok}, r = 32 sl,
+            // both factors <= 1
+            floatx4 dxo[2], cbo[2];
+            p1_blocks(sl, dxo, cbo);
+            const float fr = __builtin_amdgcn_exp2f(slt[32 * sl] - sl_t);
+            Frag<T> mf, ef;
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) {
-                Frag<T> fa;  // dy^T: rows p = 16pt + c16, contraction over the slice's tokens
-                lds_colfrag(fa, dys, LDX, 32 * sl + 4 * g4, 32 * sl + 16 + 4 * g4, pt * 16);
-                mma(dxT[pt], fa, mf);
-            }
+            for (int half = 0; half < 2; ++half) {
+                const int i0 = 32 * sl + 16 * half + 4 * g4;
+                const floatx4 c4 = *reinterpret_cast<const floatx4 *>(p1t + i0);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                Frag<T> fa;  // C^T: rows n = 16nt + c16
-                lds_colfrag(fa, cs, LDB, 32 * sl + 4 * g4, 32 * sl + 16 + 4 * g4, nt * 16);
-                mma(dBT[nt], fa, ef);
+                for (int e = 0; e < 4; ++e) {
+                    const float lij = c4[e] * fr;
+                    const float lcb = lij * cbo[half][e];
+                    cfar = __builtin_fmaf(lcb, dxo[half][e], cfar);
+                    mf.set(4 * half + e, lcb * w_t);
+                    ef.set(4 * half + e, (lij * w_t) * dxo[half][e]);
+                }
             }
+            p1_products(sl, mf, ef);
         }
         // ---- the state leaving the chunk: U = G B_j^T, V = G^T x_j
         float xu = 0.0f;  // x_j . (G B_j), partial over this lane's p
@@ -357,8 +397,8 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
 #pragma unroll
             for (int pt = 0; pt < 4; ++pt) store4_global_nt<T>(dxr + pt * 16 + 4 * g4, dxT[pt]);
         }
-        cin = xor_sum_groups(cin);
-        cex = xor_sum_groups(cex);
+        cin = xor_sum_groups(cin + cfar);
+        cex = xor_sum_groups(cex + cfar);
         xu = xor_sum_groups(xu);
         const float dw_t = cin + f_t * xu;
         float ds_t = -w_t * cex - wf * xu;
@@ -369,8 +409,8 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
 
         // ================= pass 2: tok as row i, slices of columns j <= i
         float rs = 0.0f;  // row sum of T over j < i
-        for (int sl = 0; sl <= w / 2; ++sl) {
-            floatx4 dxo[2], cbo[2];
+        // a slice's x_j.dy_i and B_j.C_i blocks, rows j of the slice, column tok
+        auto p2_blocks = [&](int sl, floatx4 (&dxo)[2], floatx4 (&cbo)[2]) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int jr = 32 * sl + 16 * half + c16;  // A-operand row (token j)
@@ -390,7 +430,40 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
                     mma(cbo[half], fa, own_c(kk));
                 }
             }
+        };
+        auto p2_products = [&](int sl, const Frag<T> &wfr) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                Frag<T> fa;  // B^T: rows n = 16nt + c16, contraction over the slice's tokens
+                lds_colfrag(fa, bs, LDB, 32 * sl + 4 * g4, 32 * sl + 16 + 4 * g4, nt * 16);
+                mma(dCT[nt], fa, wfr);
+            }
+        };
+        for (int sl = 0; sl < w / 2; ++sl) {
+            // every j < tok: e^{s_tok - s_j} w_j = e^{s_tok - s_e} (e^{s_e - s_j} w_j),
+            // e = 32 sl + 31, both factors <= 1
+            floatx4 dxo[2], cbo[2];
+            p2_blocks(sl, dxo, cbo);
+            const float fe = __builtin_amdgcn_exp2f(sl_t - slt[32 * sl + 31]);
             Frag<T> wfr;  // e^{s_i-s_j} w_j (dy_i.x_j), rows j of the slice
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int j0 = 32 * sl + 16 * half + 4 * g4;
+                const floatx4 c4 = *reinterpret_cast<const floatx4 *>(p2t + j0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = (c4[e] * fe) * dxo[half][e];
+                    wfr.set(4 * half + e, v);
+                    rs = __builtin_fmaf(v, cbo[half][e], rs);
+                }
+            }
+            p2_products(sl, wfr);
+        }
+        {  // the slice holding tok: exp per element, mask j <= tok
+            const int sl = w / 2;
+            floatx4 dxo[2], cbo[2];
+            p2_blocks(sl, dxo, cbo);
+            Frag<T> wfr;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int j0 = 32 * sl + 16 * half + 4 * g4;
@@ -405,12 +478,7 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
                     rs += j < tok ? v * cbo[half][e] : 0.0f;
                 }
             }
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                Frag<T> fa;  // B^T: rows n = 16nt + c16, contraction over the slice's tokens
-                lds_colfrag(fa, bs, LDB, 32 * sl + 4 * g4, 32 * sl + 16 + 4 * g4, nt * 16);
-                mma(dCT[nt], fa, wfr);
-            }
+            p2_products(sl, wfr);
         }
         // ---- the state entering the chunk: H^T dy_i and H C_i
 #pragma unroll
