@@ -133,6 +133,15 @@ def test_backward_fused_adjoint_single_chunk():
     check_backward(w, batches=[0, 7])
 
 
+@pytest.mark.parametrize("N", [32, 128, 256])
+def test_backward_fused_state_sizes(N):
+    # Bt*H >= 512: the recompute and the adjoint pass as one kernel per (b, h)
+    # at the other state sizes (phases of 32 tokens at N >= 128, two or three
+    # load buffers), several chunks and a ragged end
+    w = W.small(f"bwd_fused_N{N}", 8, 301, 64, 64, 4, N, 64, "bf16", seed=945 + N, init_std=0.2)
+    check_backward(w, batches=[2, 7])
+
+
 def test_backward_strong_decay():
     w = W.small("bwd_strong", 1, 500, 4, 64, 1, 32, 64, "f32", seed=950, dt_lo=0.3, dt_hi=2.0)
     check_backward(w)
