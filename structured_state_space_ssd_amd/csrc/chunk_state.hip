@@ -314,7 +314,7 @@ __global__ __launch_bounds__(512) void chunk_state_bf16_kernel(
 // receives G_{c+1} (the gradient of the state leaving chunk c) and
 // final_state G_0 (the initial state's gradient).
 template <int N, int Q, bool REV>
-__global__ __launch_bounds__(512) void chunk_state_passing_bf16_kernel(
+__global__ __launch_bounds__(512, 4) void chunk_state_passing_bf16_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ B,
     const float *__restrict__ dA_cumsum, const float *__restrict__ delta,
     const float *__restrict__ init, int L, int H, int G, int nC, __bf16 *__restrict__ chunk_init,
@@ -334,6 +334,10 @@ __global__ __launch_bounds__(512) void chunk_state_passing_bf16_kernel(
     __shared__ __attribute__((aligned(16))) __bf16 bs1[TP * N];
     __shared__ __attribute__((aligned(16))) float sv0[SQ], sv1[SQ], dv0[SQ], dv1[SQ];
     __shared__ __attribute__((aligned(16))) float wj[Q];
+    // a chunk state on its way out, bf16 rows of N (padded to shift the rows'
+    // banks; 16-byte aligned)
+    constexpr int HRS = N + 8;
+    __shared__ __attribute__((aligned(16))) __bf16 hst[P * HRS];
 
     const int h = blockIdx.x, b = blockIdx.y;
     const int g = h / (H / G);
@@ -385,17 +389,27 @@ __global__ __launch_bounds__(512) void chunk_state_passing_bf16_kernel(
             hreg[i] = floatx4{v.x, v.y, v.z, v.w};
         }
     }
-    // H_0 -> chunk_init[b][0][h]
+    // H_c -> chunk_init[b][c][h]: through LDS, so that each store is a 16-byte
+    // piece of a row and consecutive lanes write whole 128-byte lines (the
+    // accumulator layout would write 8 bytes per lane, 32-byte pieces of
+    // sixteen rows per instruction: partial lines that cost the memory more
+    // than the whole stream of x and B). Every wavefront takes part.
     auto put_init = [&](int c) {
-        __bf16 *dst = chunk_init + (((size_t)b * nC + c) * H + h) * (size_t)(P * N);
 #pragma unroll
         for (int i = 0; i < NTW; ++i) {
             const int nt = w / 4 + 2 * i;
             if (nt < N / 16) {
                 const bf16x4 v{static_cast<__bf16>(hreg[i][0]), static_cast<__bf16>(hreg[i][1]),
                                static_cast<__bf16>(hreg[i][2]), static_cast<__bf16>(hreg[i][3])};
-                *reinterpret_cast<bf16x4 *>(dst + (size_t)(pt * 16 + cc) * N + nt * 16 + 4 * g4) = v;
+                *reinterpret_cast<bf16x4 *>(hst + (pt * 16 + cc) * HRS + nt * 16 + 4 * g4) = v;
             }
+        }
+        barrier_lds();
+        __bf16 *dst = chunk_init + (((size_t)b * nC + c) * H + h) * (size_t)(P * N);
+        for (int idx = tid; idx < P * N / 8; idx += 512) {
+            const int p = idx / (N / 8), q = idx % (N / 8);
+            *reinterpret_cast<uint4 *>(dst + (size_t)p * N + q * 8) =
+                *reinterpret_cast<const uint4 *>(hst + p * HRS + q * 8);
         }
     };
     put_init(REV ? nC - 1 : 0);
