@@ -553,12 +553,17 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
     }
 }
 
-// dB, dC (input dtype) = the sum of the head blocks' float32 partial sums.
+// dB, dC (input dtype) = the sums of the head blocks' float32 partial sums,
+// both in one launch: blockIdx.y picks the array.
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *__restrict__ part, int nblk,
-                                                         size_t n4, T *__restrict__ out) {
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float *__restrict__ part0,
+                                                         const float *__restrict__ part1, int nblk,
+                                                         size_t n4, T *__restrict__ out0,
+                                                         T *__restrict__ out1) {
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n4) return;
+    const float *part = blockIdx.y ? part1 : part0;
+    T *out = blockIdx.y ? out1 : out0;
     floatx4 acc = reinterpret_cast<const floatx4 *>(part)[i];
     for (int k = 1; k < nblk; ++k) {
         const floatx4 v = reinterpret_cast<const floatx4 *>(part)[(size_t)k * n4 + i];
@@ -650,11 +655,17 @@ __global__ __launch_bounds__(1024) void bwd_dt_kernel(
     }
 }
 
-// Per-head totals of the (batch, chunk) partial sums: one workgroup per head.
-__global__ __launch_bounds__(256) void bwd_head_sum_kernel(const float *__restrict__ part, int nbc,
-                                                           int H, float *__restrict__ out) {
+// Per-head totals of the (batch, chunk) partial sums: one workgroup per head
+// and array (blockIdx.y; up to three arrays in one launch).
+struct HeadSums {
+    const float *part[3];
+    float *out[3];
+};
+__global__ __launch_bounds__(256) void bwd_head_sum_kernel(HeadSums hs, int nbc, int H) {
     __shared__ float red[4];
     const int h = blockIdx.x;
+    const float *part = hs.part[blockIdx.y];
+    float *out = hs.out[blockIdx.y];
     float v = 0.0f;
     for (int i = threadIdx.x; i < nbc; i += 256) v += part[(size_t)i * H + h];
 #pragma unroll
@@ -751,12 +762,19 @@ hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t stream) {
     return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_reduce(const float *part, int nblk, size_t count, bool bf16, void *out,
-                             hipStream_t stream) {
+hipError_t launch_bwd_reduce(const float *part0, const float *part1, int nblk, size_t count,
+                             bool bf16, void *out0, void *out1, hipStream_t stream) {
     const size_t n4 = count / 4;
-    const unsigned blocks = (unsigned)((n4 + 255) / 256);
-    if (bf16) bwd_reduce_kernel<bf16_t><<<blocks, 256, 0, stream>>>(part, nblk, n4, static_cast<bf16_t *>(out));
-    else bwd_reduce_kernel<float><<<blocks, 256, 0, stream>>>(part, nblk, n4, static_cast<float *>(out));
+    const dim3 grid((unsigned)((n4 + 255) / 256), 2);
+    if (n4 == 0) return hipSuccess;
+    if (bf16)
+        bwd_reduce_kernel<bf16_t><<<grid, 256, 0, stream>>>(part0, part1, nblk, n4,
+                                                            static_cast<bf16_t *>(out0),
+                                                            static_cast<bf16_t *>(out1));
+    else
+        bwd_reduce_kernel<float><<<grid, 256, 0, stream>>>(part0, part1, nblk, n4,
+                                                           static_cast<float *>(out0),
+                                                           static_cast<float *>(out1));
     return hipGetLastError();
 }
 
@@ -785,9 +803,18 @@ hipError_t launch_bwd_dt(const void *dt, const float *A, const float *ds, const 
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_head_sum(const float *part, int nbc, int nheads, float *out,
-                               hipStream_t stream) {
-    bwd_head_sum_kernel<<<nheads, 256, 0, stream>>>(part, nbc, nheads, out);
+hipError_t launch_bwd_head_sum(const float *const *part, float *const *out, int n, int nbc,
+                               int nheads, hipStream_t stream) {
+    HeadSums hs{};
+    int k = 0;
+    for (int i = 0; i < n; ++i)
+        if (out[i]) {
+            hs.part[k] = part[i];
+            hs.out[k] = out[i];
+            ++k;
+        }
+    if (k == 0) return hipSuccess;
+    bwd_head_sum_kernel<<<dim3(nheads, k), 256, 0, stream>>>(hs, nbc, nheads);
     return hipGetLastError();
 }
 

@@ -692,17 +692,18 @@ hipError_t backward_run(const BwdWorkspace &ws, const void *x, const void *dt, c
     if (e == hipSuccess) e = ssd::launch_chunk_bwd(a, st);
     if (e == hipSuccess) e = mark(3);
     const size_t bc = static_cast<size_t>(batch) * seqlen * ngroups * dstate;
-    if (e == hipSuccess) e = ssd::launch_bwd_reduce(a.dB_part, ws.nblk, bc, bf16, dB, st);
-    if (e == hipSuccess) e = ssd::launch_bwd_reduce(a.dC_part, ws.nblk, bc, bf16, dC, st);
+    if (e == hipSuccess)
+        e = ssd::launch_bwd_reduce(a.dB_part, a.dC_part, ws.nblk, bc, bf16, dB, dC, st);
     // stage 1: dt, A, dt bias
     if (e == hipSuccess)
         e = ssd::launch_bwd_dt(dt, A, a.ds, a.dw, batch, seqlen, nheads, Q, bf16, o, ddt,
                                f32(ws.dA_off), f32(ws.dbias_off), st);
     const int nbc = batch * nC;
-    if (e == hipSuccess) e = ssd::launch_bwd_head_sum(f32(ws.dA_off), nbc, nheads, dA, st);
-    if (e == hipSuccess && ddt_bias)
-        e = ssd::launch_bwd_head_sum(f32(ws.dbias_off), nbc, nheads, ddt_bias, st);
-    if (e == hipSuccess && dD) e = ssd::launch_bwd_head_sum(a.dD_part, nbc, nheads, dD, st);
+    if (e == hipSuccess) {
+        const float *parts[3] = {f32(ws.dA_off), f32(ws.dbias_off), a.dD_part};
+        float *outs[3] = {dA, ddt_bias, dD};
+        e = ssd::launch_bwd_head_sum(parts, outs, 3, nbc, nheads, st);
+    }
     if (e == hipSuccess) e = mark(4);
     return e;
 }

@@ -135,16 +135,18 @@ struct BwdArgs {
     float *dD_part;                 // [Bt][nC][H]
 };
 hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t stream);
-// out (input dtype, count elements) = sum over nblk of part[k][count]
-hipError_t launch_bwd_reduce(const float *part, int nblk, size_t count, bool bf16, void *out,
-                             hipStream_t stream);
+// out0, out1 (input dtype, count elements each, count a multiple of 4) = the
+// sums over nblk of part0[k][count], part1[k][count], in one launch
+hipError_t launch_bwd_reduce(const float *part0, const float *part1, int nblk, size_t count,
+                             bool bf16, void *out0, void *out1, hipStream_t stream);
 hipError_t launch_bwd_dt(const void *dt, const float *A, const float *ds, const float *dw,
                          int batch, int seqlen, int nheads, int chunk, bool bf16,
                          const DtOpts &opts, void *ddt, float *dA_part, float *dbias_part,
                          hipStream_t stream);
-// out[h] = sum_i part[i][h], i < nbc
-hipError_t launch_bwd_head_sum(const float *part, int nbc, int nheads, float *out,
-                               hipStream_t stream);
+// out[j][h] = sum_i part[j][i][h], i < nbc, for the j < n (at most 3) whose out[j] is
+// not NULL, in one launch
+hipError_t launch_bwd_head_sum(const float *const *part, float *const *out, int n, int nbc,
+                               int nheads, hipStream_t stream);
 
 // State-size padding (pad.hip): the N the kernels run with for dstate (the
 // smallest of 16, 32, 64, 128, 256 not below it; 0 above 256), and a copy of
