@@ -61,20 +61,6 @@ __device__ __forceinline__ void store4_global<float>(float *p, const floatx4 &v)
     *reinterpret_cast<floatx4 *>(p) = v;
 }
 
-// Non-temporal variants, for dx (never read again on the GPU).
-template <typename T>
-__device__ __forceinline__ void store4_global_nt(T *p, const floatx4 &v);
-template <>
-__device__ __forceinline__ void store4_global_nt<bf16_t>(bf16_t *p, const floatx4 &v) {
-    const bf16x4 b = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]),
-                      static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
-    __builtin_nontemporal_store(b, reinterpret_cast<bf16x4 *>(p));
-}
-template <>
-__device__ __forceinline__ void store4_global_nt<float>(float *p, const floatx4 &v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<floatx4 *>(p));
-}
-
 // Four consecutive LDS elements as floats (8- or 16-byte aligned).
 __device__ __forceinline__ void read4(float (&v)[4], const __bf16 *p) {
     const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p);
@@ -392,10 +378,14 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) dBT[nt][e] += wf * vo[e];
         }
+        // ordinary stores: each instruction writes a quarter of every row, and
+        // the four quarters meet in L2 as whole lines before they go to memory
+        // (as non-temporal stores they reached memory as partial lines, which
+        // cost half as many bytes again as dx itself)
         if (tok < len) {
             T *dxr = dx + ((size_t)b * L + t0 + tok) * xrow + (size_t)h * P;
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt) store4_global_nt<T>(dxr + pt * 16 + 4 * g4, dxT[pt]);
+            for (int pt = 0; pt < 4; ++pt) store4_global<T>(dxr + pt * 16 + 4 * g4, dxT[pt]);
         }
         cin = xor_sum_groups(cin + cfar);
         cex = xor_sum_groups(cex + cfar);
