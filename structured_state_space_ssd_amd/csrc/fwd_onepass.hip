@@ -134,6 +134,17 @@ __device__ __forceinline__ void dma16_sv(const void *sbase, uint32_t voff, const
                  : "memory", "m0");
 }
 
+// The same, marked non-temporal (streamed past the caches' retention).
+__device__ __forceinline__ void dma16_sv_nt(const void *sbase, uint32_t voff,
+                                            const void *lds_base) {
+    const uint32_t a =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)lds_base);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(a)
+                 : "memory", "m0");
+}
+
 // The same with 4 bytes per lane (lane l's word lands at lds_base + 4 l).
 __device__ __forceinline__ void dma4_sv(const void *sbase, uint32_t voff, const void *lds_base) {
     const uint32_t a =
@@ -206,7 +217,14 @@ struct OnepassSegs {
     int chained;   // the chain kernel has left each segment's entering state in
                    // the slot of the last piece before it (else the single-pass
                    // kernel folds the pieces itself)
+    int xnt;       // x loads non-temporal (see kStreamXBytes)
 };
+
+// x larger than this (the 256 MB last-level cache) is loaded with non-temporal
+// loads: it cannot stay cached for a later reader anyway, and streaming it
+// leaves the cache to B and C, which every head of a group reads. Smaller x is
+// loaded normally, so that back-to-back calls find it still cached.
+constexpr size_t kStreamXBytes = (size_t)256 << 20;
 
 // The chain kernel runs when the last segment would have more than this many
 // pieces to fold; below it the single-pass kernel folds them (one batch of loads).
@@ -302,8 +320,15 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
     auto issue_x = [&](int k) {
         const int t0 = k * T, len = min(T, Lw - t0);
         const bf16_t *base = xh + (size_t)t0 * xrow;
+        if (sg.xnt) {
 #pragma unroll
-        for (int i = w; i < 8; i += NWV) dma16_sv(base, x_off(i, len), sm.xb[k % NXB] + i * 512);
+            for (int i = w; i < 8; i += NWV)
+                dma16_sv_nt(base, x_off(i, len), sm.xb[k % NXB] + i * 512);
+        } else {
+#pragma unroll
+            for (int i = w; i < 8; i += NWV)
+                dma16_sv(base, x_off(i, len), sm.xb[k % NXB] + i * 512);
+        }
     };
     auto issue_dt = [&](int k) {  // wavefront 0 only
         const int t0 = k * T, len = min(T, Lw - t0);
@@ -865,7 +890,9 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, seg_states_per_cu<N>()) void 
 #pragma unroll
         for (int i = w; i < T * 8 / 64; i += NWV) {
             const int s = i * 64 + l, r = s >> 3, q = (s & 7) ^ (r & 7);
-            dma16_sv(xk, (uint32_t)min(r, len - 1) * xrb + q * 16, sm.xb[k & 1] + i * 512);
+            const uint32_t off = (uint32_t)min(r, len - 1) * xrb + q * 16;
+            if (sg.xnt) dma16_sv_nt(xk, off, sm.xb[k & 1] + i * 512);
+            else dma16_sv(xk, off, sm.xb[k & 1] + i * 512);
         }
 #pragma unroll
         for (int i = w; i < T * PPR / 64; i += NWV) {
@@ -1081,15 +1108,16 @@ static hipError_t launch_onepass_n(const void *x, const void *dt, const float *A
     const int npc = pl.S > 1 ? (pl.S - 1) * pl.k : 0;
     float *ld = npc ? scratch + (size_t)batch * nheads * npc * 64 * N : nullptr;
     const int chained = npc > kChainPieces;  // the last segment folds npc pieces
+    const int xnt = (size_t)batch * seqlen * nheads * 64 * sizeof(bf16_t) > kStreamXBytes;
     if (pl.S > 1) {
-        const OnepassSegs pieces{npc, pl.psub * kOpT, npc, 0, scratch, ld, 0};
+        const OnepassSegs pieces{npc, pl.psub * kOpT, npc, 0, scratch, ld, 0, xnt};
         const int units = batch * nheads * npc;
         const int per = (units + 7) / 8;
         ssd_segment_states_kernel<N, VL><<<per * 8, N == 256 ? 512 : 256, 0, stream>>>(
             xb, dtb, A, Bb, opts, batch, seqlen, nheads, ngroups, per, pieces, vl);
         hipError_t e = hipGetLastError();
         if (e == hipSuccess && chained) {
-            const OnepassSegs chain{pl.S, 0, npc, pl.k, scratch, ld, 1};
+            const OnepassSegs chain{pl.S, 0, npc, pl.k, scratch, ld, 1, 0};
             const size_t threads = (size_t)batch * nheads * 64 * N / 4;
             ssd_segment_chain_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(
                 init, chain, batch * nheads, 64 * N);
@@ -1098,7 +1126,7 @@ static hipError_t launch_onepass_n(const void *x, const void *dt, const float *A
         if (e == hipSuccess && between) e = hipEventRecord(between, stream);
         if (e != hipSuccess) return e;
     }
-    const OnepassSegs segs{pl.S, pl.per_seg * kOpT, npc, pl.k, scratch, ld, chained};
+    const OnepassSegs segs{pl.S, pl.per_seg * kOpT, npc, pl.k, scratch, ld, chained, xnt};
     const int units = batch * nheads * pl.S;
     const int per = (units + 7) / 8;
     ssd_forward_onepass_kernel<N, VL><<<per * 8, N == 256 ? 512 : 256, 0, stream>>>(
