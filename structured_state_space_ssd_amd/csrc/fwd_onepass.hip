@@ -815,6 +815,11 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
 // for the loads of one to hide behind the others' work. Every block's inputs
 // are loaded a whole block ahead into double buffers, issued as the block
 // before starts, so one barrier per block suffices.
+// At N 128, where a group has an even number of heads, a workgroup takes two
+// heads of one group (HP = 2, four wavefronts each): they share the block's B
+// rows (and dt piece), so B, two thirds of the bytes the kernel reads per
+// head, crosses the texture path once per two heads. (At N 64, where B is a
+// third of them, the pairs were slower.)
 // Tokens per block of the segment-state kernel: 32 where that lets five or
 // more workgroups share a compute unit; at N 256 (eight wavefronts, B rows of
 // 512 bytes) 64, one workgroup per compute unit.
@@ -823,28 +828,38 @@ constexpr int seg_states_block() {
     return N == 128 ? 32 : 64;
 }
 
-template <int N, bool VL>
+template <int N, bool VL, int HP>
 struct SegStateLds {
     static constexpr int TS = seg_states_block<N>();
-    __bf16 xb[2][TS * 64];
+    __bf16 xb[HP][2][TS * 64];
     __bf16 bb[2][TS * N];
     __bf16 dts[2][kOpT * 8];  // one 16-byte dt piece per lane (lanes past the block repeat its last)
     struct {
         float wp[TS];
         float dec, ld;  // the state's decay across the block and its log2 (-inf: a reset)
-    } tab[2];
+    } tab[HP][2];
     int4 mts[VL ? 2 : 1][VL ? kOpT : 1];  // packed sequences: the tokens' int4 of blocks k, k+1
 };
 
-// Workgroups per compute unit of the segment-state kernel (its launch bounds
-// and the plan's count of how many fill the GPU).
+// Workgroups per compute unit of the segment-state kernel (its launch bounds).
+template <int N, int HP>
+constexpr int seg_states_wgs_per_cu() {
+    return HP == 2 ? 3 : N == 64 ? 4 : N == 128 ? 5 : 1;
+}
+// Heads per compute unit, as the plan counts them (with two heads per
+// workgroup at N 128 the GPU holds six).
 template <int N>
 constexpr int seg_states_per_cu() {
     return N == 64 ? 4 : N == 128 ? 5 : 1;
 }
+// Two heads per workgroup of the segment-state kernel: N 128 and an even
+// number of heads per group.
+constexpr bool seg_states_pairs(int N, int H, int G) {
+    return N == 128 && (H / G) % 2 == 0;
+}
 
-template <int N, bool VL>
-__global__ __launch_bounds__(N == 256 ? 512 : 256, seg_states_per_cu<N>()) void ssd_segment_states_kernel(
+template <int N, bool VL, int HP>
+__global__ __launch_bounds__(N == 256 ? 512 : 256 * HP, (seg_states_wgs_per_cu<N, HP>())) void ssd_segment_states_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ dt, const float *__restrict__ A,
     const bf16_t *__restrict__ B, DtOpts o, int batch, int L, int H, int G, int per,
     OnepassSegs sg, OnepassVl vl) {
@@ -852,18 +867,23 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, seg_states_per_cu<N>()) void 
     constexpr int PPR = N / 8, NT = N / 16;
     // N 256: eight wavefronts, w and w + 4 with halves of the state's n
     constexpr bool HALVES = N == 256;
-    constexpr int NWV = HALVES ? 8 : 4, NTH = HALVES ? NT / 2 : NT;
+    constexpr int NWV = HALVES ? 8 : 4, NTH = HALVES ? NT / 2 : NT;  // NWV: per head
     static_assert(N % 32 == 0 && T * PPR >= 64 && T * 8 % 64 == 0, "state size");
-    __shared__ __attribute__((aligned(16))) SegStateLds<N, VL> sm;
+    static_assert(HP == 1 || (HP == 2 && N == 128), "head pairs at N 128 only");
+    __shared__ __attribute__((aligned(16))) SegStateLds<N, VL, HP> sm;
 
-    // workgroup -> (batch, piece, head), XCD-aware as in the single-pass kernel
+    // workgroup -> (batch, piece, head pair or head), XCD-aware as in the
+    // single-pass kernel; wavefronts NWV e .. NWV e + NWV - 1 take head HP hu + e
     const int id = blockIdx.x;
     const int lin = (id & 7) * per + (id >> 3);
-    if (lin >= batch * sg.nseg * H) return;  // whole workgroup
-    const int h = lin % H, bs = lin / H, pc = bs % sg.nseg, b = bs / sg.nseg, g = h / (H / G);
+    const int HU = H / HP;  // head units (the host launches HP = 2 only where HP divides H / G)
+    if (lin >= batch * sg.nseg * HU) return;  // whole workgroup
+    const int wa = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wavefront in the workgroup
+    const int e = wa / NWV, w = wa % NWV;  // this wavefront's head of the unit, its index there
+    const int hu = lin % HU, bs = lin / HU, pc = bs % sg.nseg, b = bs / sg.nseg;
+    const int h = hu * HP + e, g = h / (H / G);
     const int tb = pc * sg.len, Lw = min(sg.len, L - tb);
     const size_t bh = (size_t)b * H + h;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wr = HALVES ? (w & 3) : w, nh = HALVES ? (w >> 2) : 0;  // head-dim tile, n half
     const int l = lane_id(), g4 = l >> 4, cc = l & 15;
     const int nblk = (Lw + T - 1) / T;
@@ -876,26 +896,29 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, seg_states_per_cu<N>()) void 
     const float bias = o.bias ? o.bias[h] : 0.0f;
     const uint32_t xrb = (uint32_t)(xrow * 2), brb = (uint32_t)(brow * 2), drb = (uint32_t)H * 2;
 
-    auto issue_dt = [&](int k) {  // wavefront 0 only
+    // (the unit's heads share the dt piece: HP hu and HP hu + 1 lie in one
+    // aligned group of 8)
+    auto issue_dt = [&](int k) {  // wavefront 0 of the workgroup only
         const int t0 = k * T, len = min(T, Lw - t0);
         dma16_sv(dth + (size_t)t0 * H, (uint32_t)min(l, len - 1) * drb, sm.dts[k & 1]);
         if constexpr (VL)
             dma16_sv(vl.meta + row0 + t0, (uint32_t)min(l, len - 1) * 16, sm.mts[k & 1]);
     };
-    // block k's x and B, and (wavefront 0) the dt of block k + 1
+    // block k's x (each head's own wavefronts) and B (every wavefront of the
+    // workgroup), and (wavefront 0) the dt of block k + 1
     auto issue = [&](int k) {
         const int t0 = k * T, len = min(T, Lw - t0);
-        if (w == 0 && k + 1 < nblk) issue_dt(k + 1);
+        if (wa == 0 && k + 1 < nblk) issue_dt(k + 1);
         const bf16_t *xk = xh + (size_t)t0 * xrow, *bk = bg + (size_t)t0 * brow;
 #pragma unroll
         for (int i = w; i < T * 8 / 64; i += NWV) {
             const int s = i * 64 + l, r = s >> 3, q = (s & 7) ^ (r & 7);
             const uint32_t off = (uint32_t)min(r, len - 1) * xrb + q * 16;
-            if (sg.xnt) dma16_sv_nt(xk, off, sm.xb[k & 1] + i * 512);
-            else dma16_sv(xk, off, sm.xb[k & 1] + i * 512);
+            if (sg.xnt) dma16_sv_nt(xk, off, sm.xb[e][k & 1] + i * 512);
+            else dma16_sv(xk, off, sm.xb[e][k & 1] + i * 512);
         }
 #pragma unroll
-        for (int i = w; i < T * PPR / 64; i += NWV) {
+        for (int i = wa; i < T * PPR / 64; i += HP * NWV) {
             const int s = i * 64 + l, r = s / PPR, q = (s % PPR) ^ tr_swz<PPR>(r);
             dma16_sv(bk, (uint32_t)min(r, len - 1) * brb + q * 16, sm.bb[k & 1] + i * 512);
         }
@@ -918,10 +941,10 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, seg_states_per_cu<N>()) void 
             if (l < fsl) wp = 0.0f;
             reset = fsl >= 0;
         }
-        if (l < T) sm.tab[k & 1].wp[l] = wp;
+        if (l < T) sm.tab[e][k & 1].wp[l] = wp;
         if (l == 0) {
-            sm.tab[k & 1].dec = reset ? 0.0f : __builtin_amdgcn_exp2f(sle);
-            sm.tab[k & 1].ld = reset ? -__builtin_inff() : sle;
+            sm.tab[e][k & 1].dec = reset ? 0.0f : __builtin_amdgcn_exp2f(sle);
+            sm.tab[e][k & 1].ld = reset ? -__builtin_inff() : sle;
         }
     };
 
@@ -933,7 +956,7 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, seg_states_per_cu<N>()) void 
     x_colfrag_offsets(xo, l);
     const int jb = 4 * g4;
 
-    if (w == 0) issue_dt(0);
+    if (wa == 0) issue_dt(0);
     issue(0);
     for (int k = 0; k < nblk; ++k) {
         // block k's inputs (and the dt of block k + 1) have landed; every
@@ -944,10 +967,10 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, seg_states_per_cu<N>()) void 
             barrier_lds();
         }
         if (k + 1 < nblk) issue(k + 1);
-        const __bf16 *xs = sm.xb[k & 1], *bs_ = sm.bb[k & 1];
-        const float *twp = sm.tab[k & 1].wp;
-        const float dec = sm.tab[k & 1].dec;
-        ld += sm.tab[k & 1].ld;
+        const __bf16 *xs = sm.xb[e][k & 1], *bs_ = sm.bb[k & 1];
+        const float *twp = sm.tab[e][k & 1].wp;
+        const float dec = sm.tab[e][k & 1].dec;
+        ld += sm.tab[e][k & 1].ld;
 
         // H^T = exp(s_end) H^T + sum_j B_j (exp(s_end - s_j) w_j x_j)^T, p tile w
         Frag<bf16_t> xr[T / 32];
@@ -1111,10 +1134,19 @@ static hipError_t launch_onepass_n(const void *x, const void *dt, const float *A
     const int xnt = (size_t)batch * seqlen * nheads * 64 * sizeof(bf16_t) > kStreamXBytes;
     if (pl.S > 1) {
         const OnepassSegs pieces{npc, pl.psub * kOpT, npc, 0, scratch, ld, 0, xnt};
-        const int units = batch * nheads * npc;
-        const int per = (units + 7) / 8;
-        ssd_segment_states_kernel<N, VL><<<per * 8, N == 256 ? 512 : 256, 0, stream>>>(
-            xb, dtb, A, Bb, opts, batch, seqlen, nheads, ngroups, per, pieces, vl);
+        bool pairs = false;
+        if constexpr (N == 128) pairs = seg_states_pairs(N, nheads, ngroups);
+        if (pairs) {
+            if constexpr (N == 128) {
+                const int per = (batch * nheads / 2 * npc + 7) / 8;
+                ssd_segment_states_kernel<N, VL, 2><<<per * 8, 512, 0, stream>>>(
+                    xb, dtb, A, Bb, opts, batch, seqlen, nheads, ngroups, per, pieces, vl);
+            }
+        } else {
+            const int per = (batch * nheads * npc + 7) / 8;
+            ssd_segment_states_kernel<N, VL, 1><<<per * 8, N == 256 ? 512 : 256, 0, stream>>>(
+                xb, dtb, A, Bb, opts, batch, seqlen, nheads, ngroups, per, pieces, vl);
+        }
         hipError_t e = hipGetLastError();
         if (e == hipSuccess && chained) {
             const OnepassSegs chain{pl.S, 0, npc, pl.k, scratch, ld, 1, 0};

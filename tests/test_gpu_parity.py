@@ -323,6 +323,18 @@ def test_segments_strong_decay():
     check_forward(w, both_D=False)
 
 
+@pytest.mark.parametrize("N", [64, 128])
+@pytest.mark.parametrize("G", [8, 3])
+def test_segments_heads_per_group(N, G):
+    # the segment-state kernel takes two heads of a group per workgroup where a
+    # group has an even number of heads (G 3: eight per group), one otherwise
+    # (G 8: three per group)
+    w = W.small(f"seg_hpg_N{N}_G{G}", 1, 1500, 24, 64, G, N, 256, "bf16", seed=940 + N + G,
+                init_std=0.2)
+    assert plan(w) > 1
+    check_forward(w)
+
+
 @pytest.mark.parametrize("L", [1, 100, 255])
 def test_segments_too_short_to_cut(L):
     w = W.small(f"seg_short_L{L}", 1, L, 8, 64, 1, 128, 64, "bf16", seed=960 + L, init_std=0.2)
