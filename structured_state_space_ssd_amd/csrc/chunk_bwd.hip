@@ -513,11 +513,18 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
             const float part = xor_sum_16(g4 == 0 ? dd : 0.0f);
             if (l == 0) atomicAdd(&red[2], part);
         }
-        {  // <G, H>, spread over the workgroup
+        {  // <G, H>, spread over the workgroup: eight consecutive n per thread
             float gh = 0.0f;
-            for (int idx = tid; idx < P * N; idx += NTHR) {
-                const int p = idx / N, n = idx % N;
-                gh += static_cast<float>(gs[p * LDB + n]) * static_cast<float>(hs[p * LDB + n]);
+            for (int idx = tid; idx < P * N / 8; idx += NTHR) {
+                const int o = idx / (N / 8) * LDB + idx % (N / 8) * 8;
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    float gv[4], hv[4];
+                    read4(gv, gs + o + 4 * hf);
+                    read4(hv, hs + o + 4 * hf);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) gh = __builtin_fmaf(gv[e], hv[e], gh);
+                }
             }
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) gh += __shfl_xor(gh, o);
