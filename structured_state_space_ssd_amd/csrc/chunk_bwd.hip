@@ -84,7 +84,29 @@ struct BwdLds {
     static constexpr size_t kBytes =
         sizeof(E) * ((size_t)2 * Q * LDX + (size_t)2 * Q * LDB + (size_t)2 * P * LDB) +
         4 * Q * sizeof(float) + 16;
+    // The chunk's C_i . B_j in 16x16 blocks (row block bi of tokens i, column
+    // block bj of tokens j), float32, kept for all heads of the workgroup where
+    // LDS allows: the blocks with bi >= 2 floor(bj / 2), those the first pass
+    // of wavefront bj reads (the second pass reads the same blocks transposed).
+    static constexpr int QB = Q / 16;
+    static constexpr int kCbBlocks = [] {
+        int n = 0;
+        for (int bj = 0; bj < QB; ++bj) n += QB - 2 * (bj / 2);
+        return n;
+    }();
+    static constexpr bool kCbCache = kBytes + (size_t)kCbBlocks * 1024 <= 160 * 1024;
 };
+
+// Index of block (bi, bj) in the C . B^T cache (bi >= 2 floor(bj / 2)).
+template <int QB>
+__device__ __forceinline__ int cb_block(int bi, int bj) {
+    const int pj = bj >> 1;
+    return pj * (2 * QB - 2 * pj + 2) + (bj & 1) * (QB - 2 * pj) + bi - 2 * pj;
+}
+// Lane l's 16-byte slot within a cached block: swizzled so that both the
+// first pass's 16-byte reads (lane l, its own slot) and the second pass's
+// 4-byte transposed reads hit distinct banks.
+__device__ __forceinline__ int cb_slot(int l) { return l ^ ((l >> 4) & 3); }
 
 template <typename T, int N, int Q>
 __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
@@ -116,6 +138,7 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
     __shared__ __attribute__((aligned(16))) float p1t[Q];
     __shared__ __attribute__((aligned(16))) float p2t[Q];
     __shared__ float red[4];
+    __shared__ __attribute__((aligned(16))) floatx4 cbc[S::kCbCache ? S::kCbBlocks * 64 : 1];
 
     const int kb = blockIdx.x % nblk, u = blockIdx.x / nblk;
     const int hpg = H / G;
@@ -139,6 +162,32 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
         }
         *reinterpret_cast<uint4 *>(bs + j * LDB + q * EPP) = vb;
         *reinterpret_cast<uint4 *>(cs + j * LDB + q * EPP) = vc;
+    }
+    if constexpr (S::kCbCache) {
+        // wavefront w forms blocks (bi, w), bi >= 2 floor(w / 2): rows i = 16 bi +
+        // 4 g4 + e, column j = tok (its first pass's C . B blocks), once for every
+        // head of the workgroup; the head loop's first barrier publishes them
+        __syncthreads();  // B and C rows in LDS
+        Frag<T> ob[NK];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+            const int n0 = kk * 32 + 8 * g4;
+            if (n0 < N) lds_frag8(ob[kk], bs + tok * LDB + n0);
+            else ob[kk].zero();
+        }
+        for (int bi = 2 * (w / 2); bi < Q / 16; ++bi) {  // wave-uniform trip count
+            const int ir = 16 * bi + c16;  // A-operand row (token i)
+            floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                const int n0 = kk * 32 + 8 * g4;
+                Frag<T> fa;
+                if (n0 < N) lds_frag8(fa, cs + ir * LDB + n0);
+                else fa.zero();
+                mma(acc, fa, ob[kk]);
+            }
+            cbc[cb_block<Q / 16>(bi, w) * 64 + cb_slot(l)] = acc;
+        }
     }
 
     floatx4 dBT[NT], dCT[NT];  // lane (g4, c16): rows n = 16nt + 4g4 + e, column token tok
@@ -272,13 +321,17 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
                     lds_frag8(fa, dys + ir * LDX + kk * 32 + 8 * g4);
                     mma(dxo[half], fa, tx[kk]);
                 }
+                if constexpr (S::kCbCache) {
+                    cbo[half] = cbc[cb_block<Q / 16>(2 * sl + half, w) * 64 + cb_slot(l)];
+                } else {
 #pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    const int n0 = kk * 32 + 8 * g4;
-                    Frag<T> fa;
-                    if (n0 < N) lds_frag8(fa, cs + ir * LDB + n0);
-                    else fa.zero();
-                    mma(cbo[half], fa, own_b(kk));
+                    for (int kk = 0; kk < NK; ++kk) {
+                        const int n0 = kk * 32 + 8 * g4;
+                        Frag<T> fa;
+                        if (n0 < N) lds_frag8(fa, cs + ir * LDB + n0);
+                        else fa.zero();
+                        mma(cbo[half], fa, own_b(kk));
+                    }
                 }
             }
         };
@@ -411,13 +464,23 @@ __global__ __launch_bounds__(Q * 4) void chunk_bwd_kernel(
                     lds_frag8(fa, xs + jr * LDX + kk * 32 + 8 * g4);
                     mma(dxo[half], fa, tdy[kk]);
                 }
+                if constexpr (S::kCbCache) {
+                    // element e: C_tok . B_j, j = 16 bj + 4 g4 + e, held in block
+                    // (w, bj) by lane 16 (c16 / 4) + 4 g4 + e as its element c16 % 4
+                    const float *blk = reinterpret_cast<const float *>(
+                        cbc + cb_block<Q / 16>(w, 2 * sl + half) * 64);
 #pragma unroll
-                for (int kk = 0; kk < NK; ++kk) {
-                    const int n0 = kk * 32 + 8 * g4;
-                    Frag<T> fa;
-                    if (n0 < N) lds_frag8(fa, bs + jr * LDB + n0);
-                    else fa.zero();
-                    mma(cbo[half], fa, own_c(kk));
+                    for (int e = 0; e < 4; ++e)
+                        cbo[half][e] = blk[cb_slot(16 * (c16 >> 2) + 4 * g4 + e) * 4 + (c16 & 3)];
+                } else {
+#pragma unroll
+                    for (int kk = 0; kk < NK; ++kk) {
+                        const int n0 = kk * 32 + 8 * g4;
+                        Frag<T> fa;
+                        if (n0 < N) lds_frag8(fa, bs + jr * LDB + n0);
+                        else fa.zero();
+                        mma(cbo[half], fa, own_c(kk));
+                    }
                 }
             }
         };
