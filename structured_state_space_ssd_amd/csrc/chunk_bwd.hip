@@ -25,9 +25,11 @@
 // i >= j of every 32-token slice, dx, dB, dw and the column sums of T) and as
 // the row index i (second pass: slices j <= i, dC and the row sums of T), so
 // the causal work is the same for every wavefront. Every 16x16 block of
-// dy.x and C.B is formed on MFMA in the orientation the next product needs
-// (its rows the contraction index, split over the two halves of a slice),
-// decayed and masked in fp32, rounded to the operand type and multiplied.
+// dy.x is formed on MFMA in the orientation the next product needs (its rows
+// the contraction index, split over the two halves of a slice); the C.B
+// blocks, the same for every head of the workgroup, are formed once and kept
+// in LDS in float32 (read in either orientation) where LDS allows. Blocks
+// are decayed and masked in fp32, rounded to the operand type and multiplied.
 // dB and dC accumulate over the block's heads in registers and leave as
 // float32 partial sums per head block (reduced by bwd_reduce_kernel).
 #include "ssd_common.h"
