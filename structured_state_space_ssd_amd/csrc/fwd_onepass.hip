@@ -809,10 +809,9 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
 // For each piece of the first S-1 segments of a (batch, head): the state the
 // piece produces from a zero state, H = sum_t exp(s_end - s_t) w_t x_t B_t^T
 // (the single-pass kernel's state update, block by block), and the piece's
-// total log2-decay. Only x, B and dt are read. The blocks here are 32 tokens
-// (the pieces still hold whole 64-token blocks of the single-pass kernel): the
-// small LDS footprint fits five to six workgroups per compute unit, enough
-// for the loads of one to hide behind the others' work. Every block's inputs
+// total log2-decay. Only x, B and dt are read. Small LDS footprints let
+// several workgroups share a compute unit, enough for the loads of one to
+// hide behind the others' work. Every block's inputs
 // are loaded a whole block ahead into double buffers, issued as the block
 // before starts, so one barrier per block suffices.
 // At N 128, where a group has an even number of heads, a workgroup takes two
@@ -820,9 +819,10 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
 // rows (and dt piece), so B, two thirds of the bytes the kernel reads per
 // head, crosses the texture path once per two heads. (At N 64, where B is a
 // third of them, the pairs were slower.)
-// Tokens per block of the segment-state kernel: 32 where that lets five or
-// more workgroups share a compute unit; at N 256 (eight wavefronts, B rows of
-// 512 bytes) 64, one workgroup per compute unit.
+// Tokens per block of the segment-state kernel (the pieces still hold whole
+// 64-token blocks of the single-pass kernel): 32 at N 128 (five workgroups per
+// compute unit, three of head pairs); 64 at N 64 (four) and at N 256 (eight
+// wavefronts, B rows of 512 bytes, one).
 template <int N>
 constexpr int seg_states_block() {
     return N == 128 ? 32 : 64;
