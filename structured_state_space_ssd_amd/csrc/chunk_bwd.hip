@@ -654,13 +654,25 @@ __global__ __launch_bounds__(1024) void bwd_dt_kernel(
     const int hc = min(h, H - 1);
     const int t0 = c * Q + k * R;
     const size_t row = ((size_t)b * H + hc) * (size_t)nC * Q + t0;
+    static_assert(R % 4 == 0, "runs of whole float4s");
     float dsv[R], dwv[R], raw[R];
+    // (a lane's R tokens are consecutive in its ds / dw row: 16-byte loads)
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        dsv[r] = h < H ? ds[row + r] : 0.0f;
-        dwv[r] = h < H ? dw[row + r] : 0.0f;
-        raw[r] = to_f32(dt[((size_t)b * L + min(t0 + r, L - 1)) * H + hc]);
+    for (int r = 0; r < R; r += 4) {
+        const float4 s4 = *reinterpret_cast<const float4 *>(ds + row + r);
+        const float4 w4 = *reinterpret_cast<const float4 *>(dw + row + r);
+        const bool on = h < H;
+        dsv[r] = on ? s4.x : 0.0f;
+        dsv[r + 1] = on ? s4.y : 0.0f;
+        dsv[r + 2] = on ? s4.z : 0.0f;
+        dsv[r + 3] = on ? s4.w : 0.0f;
+        dwv[r] = on ? w4.x : 0.0f;
+        dwv[r + 1] = on ? w4.y : 0.0f;
+        dwv[r + 2] = on ? w4.z : 0.0f;
+        dwv[r + 3] = on ? w4.w : 0.0f;
     }
+#pragma unroll
+    for (int r = 0; r < R; ++r) raw[r] = to_f32(dt[((size_t)b * L + min(t0 + r, L - 1)) * H + hc]);
     // suffix sums within the run, then across runs
 #pragma unroll
     for (int r = R - 2; r >= 0; --r) dsv[r] += dsv[r + 1];
