@@ -33,10 +33,14 @@
 // (Y^T tiles for every head-dim column) and the head-dim columns
 // 16w..16w+15 of the state H^T (float32 registers, MFMA accumulator layout).
 // At N 256 (one workgroup per compute unit) 8 wavefronts: w and w + 4 share
-// tile w, each holding half of the state's n and forming its half of the
-// sums over n (C H, C B^T, the update); the second hands its partial outputs
-// to the first through LDS at the middle barrier, and the first stages and
-// stores them.
+// tile w: each holds half of the state's n (its half of the update), forms
+// C H over the whole of N for two of the four head-dim tiles and C B^T over
+// the whole of N for half of each slice's columns; the second hands its
+// partial outputs to the first through LDS at the middle barrier, and the
+// first stages and stores them. With one workgroup per compute unit nothing
+// else hides LDS latency, so each product chain's operands are read before
+// its products (the two C H chains interleaved, the C B^T slice's B and x
+// operands ahead of a scheduling barrier).
 // The block's x rows (three buffers where LDS allows, else two), B and C rows
 // (single-buffered: they are shared by all heads of a group and come from
 // L2), and the 8-head piece of dt holding this head's values arrive by direct
@@ -427,6 +431,12 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
 
     int xo[4];
     x_colfrag_offsets(xo, l);
+    // the output accumulators acc[q] hold p tile q ^ pflip: N 256, each half's
+    // own two tiles first (the first half, which stages the rows, in order)
+    const int pflip = HALVES ? 2 * nh : 0;
+    int xol[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xol[q] = pflip ? xo[q ^ 2] : xo[q];
     const int i = 16 * wr + cc;  // this lane's output token: row tile wr is rows 16wr..16wr+15
 
     // D on the diagonal slice (js = wr / 2) where j = i, added to M there so
@@ -518,28 +528,47 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
         for (int kq = 0; kq < NK; ++kq)
             lds_frag8(cfr[kq], sm.cs + i * N + (((4 * kq + g4) ^ tr_swz<PPR>(i)) << 3));
 
-        // ---- state to output: Y^T[p][i] = exp(s_i) sum_n H[p][n] C_i[n], every p tile
-        // (N 256: the wavefront of half nh takes p tiles 2 nh, 2 nh + 1)
+        // ---- state to output: Y^T[p][i] = exp(s_i) sum_n H[p][n] C_i[n], every p
+        // tile; acc[q] holds p tile q ^ pflip. N 256: the wavefront of half nh
+        // takes its own p tiles 2 nh, 2 nh + 1 (acc[0], acc[1]), every H
+        // fragment read before the two product chains, which run interleaved
         floatx4 acc[4];
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-            const int pp = 16 * pt + cc;
-            acc[pt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-            if (HALVES && (pt >> 1) != nh) continue;  // uniform
+        for (int q = 0; q < 4; ++q) acc[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (HALVES) {
+            static_assert(HSW == 15, "rows pa and pa + 16 share their swizzle");
+            const int pa = 32 * nh + cc;  // p tile 2 nh's row of this lane; 2 nh + 1: 16 rows on
+            Frag<bf16_t> h0[NK], h1[NK];
 #pragma unroll
             for (int kq = 0; kq < NK; ++kq) {
-                Frag<bf16_t> hf;
-                lds_frag8(hf, sm.hb + pp * N + (((4 * kq + g4) ^ (pp & HSW)) << 3));
-                mma(acc[pt], hf, cfr[kq]);
+                const __bf16 *hp = sm.hb + pa * N + (((4 * kq + g4) ^ (pa & HSW)) << 3);
+                lds_frag8(h0[kq], hp);
+                lds_frag8(h1[kq], hp + 16 * N);
+            }
+#pragma unroll
+            for (int kq = 0; kq < NK; ++kq) {
+                mma(acc[0], h0[kq], cfr[kq]);
+                mma(acc[1], h1[kq], cfr[kq]);
+            }
+        } else {
+#pragma unroll
+            for (int pt = 0; pt < 4; ++pt) {
+                const int pp = 16 * pt + cc;
+#pragma unroll
+                for (int kq = 0; kq < NK; ++kq) {
+                    Frag<bf16_t> hf;
+                    lds_frag8(hf, sm.hb + pp * N + (((4 * kq + g4) ^ (pp & HSW)) << 3));
+                    mma(acc[pt], hf, cfr[kq]);
+                }
             }
         }
         {
             float e = __builtin_amdgcn_exp2f(si);
             if constexpr (VL) e = fsi < 0 ? e : 0.0f;  // H belongs to row i's sequence
 #pragma unroll
-            for (int pt = 0; pt < 4; ++pt)
+            for (int q = 0; q < (HALVES ? 2 : 4); ++q)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[pt][r] *= e;
+                for (int r = 0; r < 4; ++r) acc[q][r] *= e;
         }
 
         // ---- the previous block's outputs leave here, between compute phases
@@ -561,14 +590,27 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
                 // 32 js + 16 nh + 0..15 of the slice, each C_i . B_j summed over
                 // the whole of N in float32 (rounded to bf16 once, after the
                 // decay), and their part of Y^T += X^T M^T as k = 16 products
-                floatx4 m = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+                // (every B fragment read first; two chains, even and odd k)
                 const int jn = 32 * js + 16 * nh + cc;
+                Frag<bf16_t> bfr[NK];
 #pragma unroll
-                for (int kq = 0; kq < NK; ++kq) {
-                    Frag<bf16_t> bf;
-                    lds_frag8(bf, sm.bb + jn * N + (((4 * kq + g4) ^ tr_swz<PPR>(jn)) << 3));
-                    mma(m, bf, cfr[kq]);
+                for (int kq = 0; kq < NK; ++kq)
+                    lds_frag8(bfr[kq], sm.bb + jn * N + (((4 * kq + g4) ^ tr_swz<PPR>(jn)) << 3));
+                // the x operands of this slice's part of Y^T += X^T M^T, read
+                // with the B rows, ahead of the products
+                const __bf16 *xsl = xs + js * 2048 + nh * 1024;
+                bf16x4 xq[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xq[q] = x_colfrag_half(xsl, xol[q]);
+                __builtin_amdgcn_sched_barrier(0);  // the reads stay ahead of the products
+                floatx4 m = floatx4{0.0f, 0.0f, 0.0f, 0.0f}, m1 = m;
+#pragma unroll
+                for (int kq = 0; kq < NK; kq += 2) {
+                    mma(m, bfr[kq], cfr[kq]);
+                    mma(m1, bfr[kq + 1], cfr[kq + 1]);
                 }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m[r] += m1[r];
                 // lane (g4, cc): rows j = jh + r of column i
                 const int jh = j0 + 16 * nh;
                 float v[4];
@@ -592,12 +634,8 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
                     }
                 }
                 const bf16x4 mf = pack4(v);
-                const __bf16 *xsl = xs + js * 2048 + nh * 1024;
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt) {
-                    const bf16x4 xf = x_colfrag_half(xsl, xo[pt]);
-                    mma16(acc[pt], xf, mf);
-                }
+                for (int q = 0; q < 4; ++q) mma16(acc[q], xq[q], mf);
                 continue;
             }
             floatx4 m[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
@@ -726,11 +764,20 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
             }
             Frag<bf16_t> xw;
             pack8(xw, v);
+            if constexpr (HALVES) {  // every B^T fragment read before the products
+                Frag<bf16_t> bv[NTH];
 #pragma unroll
-            for (int nt = 0; nt < NTH; ++nt) {
-                Frag<bf16_t> bf;
-                colfrag_swz<PPR>(bf, sm.bb, jb, jb + 16, (nh * NTH + nt) * 16);
-                mma(hreg[nt], bf, xw);
+                for (int nt = 0; nt < NTH; ++nt)
+                    colfrag_swz<PPR>(bv[nt], sm.bb, jb, jb + 16, (nh * NTH + nt) * 16);
+#pragma unroll
+                for (int nt = 0; nt < NTH; ++nt) mma(hreg[nt], bv[nt], xw);
+            } else {
+#pragma unroll
+                for (int nt = 0; nt < NTH; ++nt) {
+                    Frag<bf16_t> bf;
+                    colfrag_swz<PPR>(bf, sm.bb, jb, jb + 16, (nh * NTH + nt) * 16);
+                    mma(hreg[nt], bf, xw);
+                }
             }
         }
         if constexpr (VL) {
@@ -752,7 +799,7 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
         if constexpr (HALVES) {  // the second half's partial outputs to the first
             if (nh == 1) {
 #pragma unroll
-                for (int pt = 0; pt < 4; ++pt) sm.xch[4 * wr + pt][l] = acc[pt];
+                for (int q = 0; q < 4; ++q) sm.xch[4 * wr + (q ^ pflip)][l] = acc[q];
             }
         }
 
