@@ -125,13 +125,20 @@ struct OnepassLds {
     int touch[64];  // written by the L2 touches of B and C, never read
 };
 
+// The LDS byte address of a generic pointer into LDS: the low 32 bits of its
+// flat address (what the address-space cast yields for a non-null pointer,
+// without the cast's null test, which the backend cannot always encode for a
+// pointer at LDS offset 0), made wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr32(const void *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
 // One 16-byte-per-lane global-to-LDS load from the wave-uniform base `sbase`
 // plus this lane's byte offset `voff` (lane l's 16 bytes land at lds_base +
 // 16 l): the scalar-base form, so a block's loads cost no per-lane 64-bit
 // address arithmetic.
 __device__ __forceinline__ void dma16_sv(const void *sbase, uint32_t voff, const void *lds_base) {
-    const uint32_t a =
-        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)lds_base);
+    const uint32_t a = lds_addr32(lds_base);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(voff), "s"(sbase), "s"(a)
@@ -141,8 +148,7 @@ __device__ __forceinline__ void dma16_sv(const void *sbase, uint32_t voff, const
 // The same, marked non-temporal (streamed past the caches' retention).
 __device__ __forceinline__ void dma16_sv_nt(const void *sbase, uint32_t voff,
                                             const void *lds_base) {
-    const uint32_t a =
-        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)lds_base);
+    const uint32_t a = lds_addr32(lds_base);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                  :
                  : "v"(voff), "s"(sbase), "s"(a)
@@ -151,8 +157,7 @@ __device__ __forceinline__ void dma16_sv_nt(const void *sbase, uint32_t voff,
 
 // The same with 4 bytes per lane (lane l's word lands at lds_base + 4 l).
 __device__ __forceinline__ void dma4_sv(const void *sbase, uint32_t voff, const void *lds_base) {
-    const uint32_t a =
-        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)lds_base);
+    const uint32_t a = lds_addr32(lds_base);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                  :
                  : "v"(voff), "s"(sbase), "s"(a)
@@ -367,6 +372,7 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
         t.wt[l] = wgt;
         t.wp[l] = wp;
         if (l < 32) t.cf[l] = __builtin_amdgcn_exp2f(s31 - sl) * wgt;
+
     };
 
     // the state H^T: lane (g4, cc) of wavefront w holds rows n = 16 nt + 4 g4 + r
@@ -639,15 +645,32 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
                 continue;
             }
             floatx4 m[2] = {floatx4{0.0f, 0.0f, 0.0f, 0.0f}, floatx4{0.0f, 0.0f, 0.0f, 0.0f}};
+            // the diagonal slice of an even row tile: its second half lies above
+            // the diagonal (j >= 32 js + 16 > i) and stays zero (packed sequences
+            // take the general path)
+            const bool zh1 = !VL && diag && !(wr & 1);  // uniform
+            auto cb_half = [&](int half) {
 #pragma unroll
-            for (int kq = 0; kq < NK; ++kq) {
-                const int q = 4 * kq + g4;
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
+                for (int kq = 0; kq < NK; ++kq) {
                     const int j = 32 * js + 16 * half + cc;
                     Frag<bf16_t> bf;
-                    lds_frag8(bf, sm.bb + j * N + ((q ^ tr_swz<PPR>(j)) << 3));
+                    lds_frag8(bf, sm.bb + j * N + (((4 * kq + g4) ^ tr_swz<PPR>(j)) << 3));
                     mma(m[half], bf, cfr[kq]);
+                }
+            };
+            if (zh1) {
+                cb_half(0);
+            } else {
+#pragma unroll
+                for (int kq = 0; kq < NK; ++kq) {
+                    const int q = 4 * kq + g4;
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const int j = 32 * js + 16 * half + cc;
+                        Frag<bf16_t> bf;
+                        lds_frag8(bf, sm.bb + j * N + ((q ^ tr_swz<PPR>(j)) << 3));
+                        mma(m[half], bf, cfr[kq]);
+                    }
                 }
             }
             // lane (g4, cc): rows j = 32 js + 16 half + 4 g4 + r of column i
@@ -658,16 +681,41 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
                 const floatx4 s1 = *reinterpret_cast<const floatx4 *>(tsl + j0 + 16);
                 const floatx4 w0 = *reinterpret_cast<const floatx4 *>(twt + j0);
                 const floatx4 w1 = *reinterpret_cast<const floatx4 *>(twt + j0 + 16);
+                if (!VL && (wr & 1)) {
+                    // odd row tile (i >= 32 js + 16): the first half lies wholly
+                    // below the diagonal (no mask, no D; its decays exp(s_i - s_b)
+                    // exp(s_b - s_j) w_j through the slice's 16th token b, both
+                    // factors <= 1), the second holds the diagonal 16 x 16 block
+                    // (j <= i: 4 g4 + r <= cc)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float a0 = __builtin_fmaf(
-                        m[0][r], __builtin_amdgcn_exp2f(si - s0[r]) * w0[r], dval[r]);
-                    const float a1 = __builtin_fmaf(
-                        m[1][r], __builtin_amdgcn_exp2f(si - s1[r]) * w1[r], dval[4 + r]);
-                    const bool on0 = j0 + r <= i && (!VL || j0 + r >= fsi);
-                    const bool on1 = j0 + 16 + r <= i && (!VL || j0 + 16 + r >= fsi);
-                    v[r] = on0 ? a0 : 0.0f;
-                    v[4 + r] = on1 ? a1 : 0.0f;
+                    for (int r = 0; r < 4; ++r) {
+                        v[r] = m[0][r] * (__builtin_amdgcn_exp2f(si - s0[r]) * w0[r]);
+                        const float a1 = __builtin_fmaf(
+                            m[1][r], __builtin_amdgcn_exp2f(si - s1[r]) * w1[r], dval[4 + r]);
+                        v[4 + r] = 4 * g4 + r <= cc ? a1 : 0.0f;
+                    }
+                } else if (!VL) {
+                    // even row tile: the first half holds the diagonal block, the
+                    // second is zero
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float a0 = __builtin_fmaf(
+                            m[0][r], __builtin_amdgcn_exp2f(si - s0[r]) * w0[r], dval[r]);
+                        v[r] = 4 * g4 + r <= cc ? a0 : 0.0f;
+                        v[4 + r] = 0.0f;
+                    }
+                } else {  // packed sequences: masks of causality and of each row's sequence
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float a0 = __builtin_fmaf(
+                            m[0][r], __builtin_amdgcn_exp2f(si - s0[r]) * w0[r], dval[r]);
+                        const float a1 = __builtin_fmaf(
+                            m[1][r], __builtin_amdgcn_exp2f(si - s1[r]) * w1[r], dval[4 + r]);
+                        const bool on0 = j0 + r <= i && j0 + r >= fsi;
+                        const bool on1 = j0 + 16 + r <= i && j0 + 16 + r >= fsi;
+                        v[r] = on0 ? a0 : 0.0f;
+                        v[4 + r] = on1 ? a1 : 0.0f;
+                    }
                 }
             } else {
                 // wholly below it (i >= 32 > j): exp(s_i - s_31) exp(s_31 - s_j) w_j,
