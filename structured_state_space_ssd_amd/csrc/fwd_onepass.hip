@@ -125,14 +125,6 @@ struct OnepassLds {
     int touch[64];  // written by the L2 touches of B and C, never read
 };
 
-// The LDS byte address of a generic pointer into LDS: the low 32 bits of its
-// flat address (what the address-space cast yields for a non-null pointer,
-// without the cast's null test, which the backend cannot always encode for a
-// pointer at LDS offset 0), made wave-uniform.
-__device__ __forceinline__ uint32_t lds_addr32(const void *p) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
-
 // One 16-byte-per-lane global-to-LDS load from the wave-uniform base `sbase`
 // plus this lane's byte offset `voff` (lane l's 16 bytes land at lds_base +
 // 16 l): the scalar-base form, so a block's loads cost no per-lane 64-bit

@@ -250,13 +250,20 @@ __host__ __device__ constexpr int colfrag_stride(int cols, int bytes) {
 //
 typedef __attribute__((address_space(3))) void lds_void;
 
+// The LDS byte address of a generic pointer into LDS: the low 32 bits of its
+// flat address (what the address-space cast yields for a non-null pointer,
+// without the cast's null test, which the backend cannot always encode for a
+// pointer at LDS offset 0), made wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr32(const void *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
 // One 16-byte-per-lane global-to-LDS load: lane l's 16 bytes from `src` land
 // at byte lds_base + 16*l (lds_base is the same for the whole wavefront). In
 // inline assembly so that the compiler does not hold later reads of other LDS
 // buffers behind it; completion is awaited explicitly (wait_barrier).
 __device__ __forceinline__ void dma16(const void *src, const void *lds_base) {
-    const uint32_t a =
-        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)lds_base);
+    const uint32_t a = lds_addr32(lds_base);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(src), "s"(a)
