@@ -652,6 +652,22 @@ __global__ __launch_bounds__(N == 256 ? 512 : 256, N == 64 ? 3 : N == 128 ? 2 : 
             };
             if (zh1) {
                 cb_half(0);
+            } else if (N == 128) {
+                // (two workgroups per compute unit: both halves' B fragments
+                // read before the products, which then wait on no LDS read)
+                Frag<bf16_t> bq[2][NK];
+#pragma unroll
+                for (int kq = 0; kq < NK; ++kq)
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const int j = 32 * js + 16 * half + cc;
+                        lds_frag8(bq[half][kq], sm.bb + j * N + (((4 * kq + g4) ^ tr_swz<PPR>(j)) << 3));
+                    }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kq = 0; kq < NK; ++kq)
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) mma(m[half], bq[half][kq], cfr[kq]);
             } else {
 #pragma unroll
                 for (int kq = 0; kq < NK; ++kq) {
