@@ -216,11 +216,13 @@ def test_fused_state_path_single_chunk_short():
 # One workgroup per (batch, head) walks the sequence in 64-token blocks with
 # the state in registers (these cases have enough (batch, head) pairs for one
 # segment; the segmented form follows further down). Cases: a single token, one partial block, exactly
-# one block, one block plus one token, several blocks with a ragged end; an
+# one block, one block plus one token, several blocks with a ragged end (the
+# last block ending inside an even 16-token row tile, and inside an odd one:
+# 84 and 247, where an odd tile's diagonal slice takes its unmasked path); an
 # initial state; several groups; every chunk argument (it does not change the
 # kernel's blocks, only the rounding order against the oracle).
 
-@pytest.mark.parametrize("L", [1, 37, 64, 65, 200, 1000])
+@pytest.mark.parametrize("L", [1, 37, 64, 65, 84, 200, 247, 1000])
 def test_onepass_lengths(L):
     w = W.small(f"onepass_L{L}", 8, L, 64, 64, 4, 64, 256, "bf16", seed=800 + L, init_std=0.2)
     assert w.batch * w.nheads >= 512
